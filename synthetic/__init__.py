@@ -1,0 +1,81 @@
+"""Seeded synthetic inputs for the small-M 8-bit GEMM.
+
+Shared by the tests, the benchmark and the smoke check, on both sides of every
+parity comparison.  This module holds none of the method's arithmetic: it only
+draws random numbers and rounds fp32 samples to bf16 (the activation dtype).
+Quantization of activations and weights is done separately by each side.
+
+Workload recipe (stand-in for decode-time linear layers under serving, which
+the pages benchmark on ShareGPT with Qwen3 models; neither is used here):
+  - activations X: bf16, N(0, 1) samples rounded to nearest-even bf16, [M, K];
+  - W8A8_INT8 weights: int8 codes uniform in [-127, 127], [N, K], with
+    per-output-channel fp32 scales uniform in [0.001, 0.01);
+  - FP8_Dynamic weights: fp32 N(0, 0.02) samples, [N, K], quantized per row;
+  - Block_FP8 weights: fp32 N(0, 1) samples, [N, K], quantized per 128x128 block.
+Inputs are dense; no outlier channels are modelled.
+Seeds: crc32 of "fmt|M|N|K|tensor", numpy PCG64.
+"""
+import zlib
+
+import numpy as np
+import torch
+
+FORMAT_NAMES = ("FP8_Dynamic", "W8A8_INT8", "Block_FP8")
+WEIGHT_SIGMA = {"FP8_Dynamic": 0.02, "Block_FP8": 1.0}
+
+
+def seed_for(fmt: str, M: int, N: int, K: int, tensor: str) -> int:
+    return zlib.crc32(f"{fmt}|{M}|{N}|{K}|{tensor}".encode())
+
+
+def rng(fmt: str, M: int, N: int, K: int, tensor: str) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed_for(fmt, M, N, K, tensor)))
+
+
+def fp32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 to the nearest-even bf16 (torch's CPU conversion); uint16 bits."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_bits_to_fp32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def activations(fmt: str, M: int, N: int, K: int) -> np.ndarray:
+    """bf16 X [M, K] as uint16 bits, from N(0, 1)."""
+    x = rng(fmt, M, N, K, "x").standard_normal((M, K), dtype=np.float32)
+    return fp32_to_bf16_bits(x)
+
+
+def int8_weights(fmt: str, M: int, N: int, K: int):
+    """int8 codes [N, K] uniform in [-127, 127] and fp32 scales [N] in U(0.001, 0.01)."""
+    wq = rng(fmt, M, N, K, "w").integers(-127, 128, size=(N, K), dtype=np.int8)
+    sw = rng(fmt, M, N, K, "sw").uniform(0.001, 0.01, size=(N,)).astype(np.float32)
+    return wq, sw
+
+
+def fp32_weights(fmt: str, M: int, N: int, K: int) -> np.ndarray:
+    """fp32 W [N, K] from N(0, sigma), sigma 0.02 (FP8_Dynamic) or 1 (Block_FP8)."""
+    sigma = WEIGHT_SIGMA[fmt]
+    w = rng(fmt, M, N, K, "w").standard_normal((N, K), dtype=np.float32)
+    return (w * np.float32(sigma)).astype(np.float32)
+
+
+# The shape sweep: the (N, K) pairs of the FlashInfer mm_fp4 tuning table
+# (flashinfer PR 3948, "Performance Data measured on B200", tuning testlist)
+# that fall on the N x K grid {512, 896, 1792, 3584, 4608, 5120} x
+# {640, 1024, 2048, 5120, 7168, 8192}, each at the page's M values, plus
+# M = 32 (the top of the small-M window) for the three pairs that have
+# M in {1, 4, 16} rows.
+SWEEP = (
+    (1, 512, 7168), (4, 512, 7168), (16, 512, 7168), (32, 512, 7168),
+    (1, 896, 1024), (4, 896, 1024), (16, 896, 1024), (32, 896, 1024),
+    (1, 4608, 7168), (4, 4608, 7168), (16, 4608, 7168), (32, 4608, 7168),
+    (1, 896, 5120), (8, 896, 5120),
+    (1, 1792, 5120), (8, 1792, 5120),
+    (1, 3584, 5120), (8, 3584, 5120),
+    (1, 5120, 640), (8, 5120, 640),
+    (1, 5120, 2048), (8, 5120, 2048),
+    (1, 5120, 8192), (8, 5120, 8192),
+)
