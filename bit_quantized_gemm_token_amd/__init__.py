@@ -1,0 +1,325 @@
+"""Small-M 8-bit quantized linear-layer GEMM for MI355X (gfx950).
+
+    Y[M, N] = dequant(Xq) . dequant(Wq)^T,  1 <= M <= 32,
+    formats FP8_Dynamic, W8A8_INT8 and Block_FP8.
+
+Python face of the C-ABI in include/w8gemm.h (libw8gemm.so, built in-tree).
+This module only marshals arguments: it takes torch tensors for device memory
+and the current HIP stream, checks dtypes and layouts, and calls the library;
+every step of the computation runs in the library's HIP kernels.  Importing it
+fails when the library is not built.
+
+Method: ai-radar.it, "Helion nel backend vLLM: un solo GEMM, tuning per forma e
+guadagni fino al 10%" -- paragraph 1 (formats), 2-3 (Standard, Split-K,
+Swap-AB as tunables of one GEMM; split_k a power of two up to 256),
+4 (M <= 32 under graph replay), 6-7 (per-shape config table with a default).
+"""
+import ctypes
+import os
+
+import torch
+
+from . import _capi
+from ._capi import (ABI_VERSION, FORMATS, FORMAT_NAMES, GROUP, MAX_M, MAX_SPLIT_K, Config,
+                    TuneOpts, TuneStats)
+
+_lib = _capi.load()
+LIB_PATH = _capi.LIB_PATH
+DEFAULT_TABLE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "configs", "gfx950.tbl")
+
+__all__ = ["Config", "W8Error", "UnsupportedShape", "Workspace", "quantize_act",
+           "quantize_weight", "gemm_w8a8", "gemm_w8a8_acc", "linear", "workspace_size",
+           "validate_config", "default_config", "resolve_config", "lookup_config",
+           "set_config", "load_config_table", "save_config_table", "clear_config_table",
+           "config_table_size", "config_table_foreign", "tune_shape", "FORMATS", "MAX_M",
+           "MAX_SPLIT_K", "GROUP", "ABI_VERSION"]
+
+
+class W8Error(RuntimeError):
+    def __init__(self, status, message):
+        self.status = status
+        self.status_name = _capi.STATUS.get(status, str(status))
+        super().__init__(f"{self.status_name}: {message}")
+
+
+class UnsupportedShape(W8Error):
+    """M is outside the small-M window; the caller should use another backend."""
+
+
+def _check(status):
+    if status != 0:
+        msg = _lib.w8_last_error().decode(errors="replace")
+        if status == 2:
+            raise UnsupportedShape(status, msg)
+        raise W8Error(status, msg)
+
+
+def _fmt(fmt):
+    if isinstance(fmt, str):
+        if fmt not in FORMATS:
+            raise ValueError(f"unknown format {fmt!r}; expected one of {list(FORMATS)}")
+        return FORMATS[fmt]
+    return int(fmt)
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev_ptr(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _row_major(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit inner stride")
+    return t.stride(0)
+
+
+def _cfg_ptr(cfg):
+    if cfg is None:
+        return None
+    if isinstance(cfg, dict):
+        cfg = Config.make(**cfg)
+    return ctypes.byref(cfg)
+
+
+def _codes_dtype(fmt):
+    return torch.int8 if _fmt(fmt) == FORMATS["W8A8_INT8"] else torch.float8_e4m3fn
+
+
+# ----------------------------------------------------------------- quantize --
+def quantize_act(fmt, x, xq=None, sx=None, stream=None):
+    """Dynamic activation quantization of bf16 x [M, K] on the GPU.
+
+    Returns (xq, sx): codes [M, K] (float8_e4m3fn or int8) and fp32 scales,
+    [M] for the per-token formats or [M, K/128] for Block_FP8.
+    """
+    f = _fmt(fmt)
+    ldx = _row_major(x, "x")
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=_codes_dtype(f), device=x.device)
+    if sx is None:
+        shape = (M, K // GROUP) if f == FORMATS["Block_FP8"] else (M,)
+        sx = torch.empty(shape, dtype=torch.float32, device=x.device)
+    ldq = _row_major(xq, "xq")
+    _check(_lib.w8_quantize_act(f, M, K, _dev_ptr(x, "x", torch.bfloat16), ldx,
+                                _dev_ptr(xq, "xq"), ldq * xq.element_size(),
+                                _dev_ptr(sx, "sx", torch.float32), _stream(stream, x.device)))
+    return xq, sx
+
+
+def quantize_weight(fmt, w, wq=None, sw=None, stream=None):
+    """Offline E4M3FN quantization of fp32 weights w [N, K] on the GPU.
+
+    FP8_Dynamic: sw [N]; Block_FP8: sw [ceil(N/128), ceil(K/128)].
+    """
+    f = _fmt(fmt)
+    ldw = _row_major(w, "w")
+    N, K = w.shape
+    if wq is None:
+        wq = torch.empty((N, K), dtype=torch.float8_e4m3fn, device=w.device)
+    if sw is None:
+        shape = ((N + GROUP - 1) // GROUP, (K + GROUP - 1) // GROUP) \
+            if f == FORMATS["Block_FP8"] else (N,)
+        sw = torch.empty(shape, dtype=torch.float32, device=w.device)
+    ldq = _row_major(wq, "wq")
+    _check(_lib.w8_quantize_weight(f, N, K, _dev_ptr(w, "w", torch.float32), ldw,
+                                   _dev_ptr(wq, "wq"), ldq * wq.element_size(),
+                                   _dev_ptr(sw, "sw", torch.float32), _stream(stream, w.device)))
+    return wq, sw
+
+
+# --------------------------------------------------------------------- GEMM --
+def workspace_size(fmt, M, N, K, cfg=None):
+    n = ctypes.c_size_t(0)
+    _check(_lib.w8_workspace_size(_fmt(fmt), M, N, K, _cfg_ptr(cfg), ctypes.byref(n)))
+    return n.value
+
+
+class Workspace:
+    """Device workspace for split-K, zero-filled once when (re)allocated.
+
+    The GEMM leaves its counters at zero after each call, so one Workspace can
+    serve any sequence of calls on one stream (not concurrent calls).
+    """
+
+    def __init__(self, device=None, nbytes=0):
+        self.device = torch.device(device or "cuda")
+        self.buf = None
+        if nbytes:
+            self.reserve(nbytes)
+
+    def reserve(self, nbytes):
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+    def for_call(self, fmt, M, N, K, cfg=None):
+        need = workspace_size(fmt, M, N, K, cfg)
+        if need == 0:
+            return None, 0
+        buf = self.reserve(need)
+        return ctypes.c_void_p(buf.data_ptr()), buf.numel()
+
+
+def _gemm(entry, fmt, xq, sx, wq, sw, out, cfg, workspace, stream):
+    f = _fmt(fmt)
+    ldq = _row_major(xq, "xq") * xq.element_size()
+    ldw = _row_major(wq, "wq") * wq.element_size()
+    ldo = _row_major(out, "out")
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError(f"K mismatch: xq {tuple(xq.shape)} vs wq {tuple(wq.shape)}")
+    if xq.element_size() != 1 or wq.element_size() != 1:
+        raise TypeError("xq and wq must hold 1-byte codes")
+    if workspace is None:
+        workspace = _default_workspace(xq.device)
+    ws_ptr, ws_bytes = workspace.for_call(f, M, N, K, cfg)
+    _check(entry(f, M, N, K, _dev_ptr(xq, "xq"), ldq, _dev_ptr(sx, "sx", torch.float32),
+                 _dev_ptr(wq, "wq"), ldw, _dev_ptr(sw, "sw", torch.float32),
+                 _dev_ptr(out, "out"), ldo, _cfg_ptr(cfg), ws_ptr, ws_bytes,
+                 _stream(stream, xq.device)))
+    return out
+
+
+_workspaces = {}
+
+
+def _default_workspace(device):
+    key = str(device)
+    if key not in _workspaces:
+        _workspaces[key] = Workspace(device)
+    return _workspaces[key]
+
+
+def gemm_w8a8(fmt, xq, sx, wq, sw, cfg=None, y=None, workspace=None, stream=None):
+    """Y = dequant(xq) . dequant(wq)^T as bf16 [M, N].
+
+    cfg: a Config (or dict of its fields); None uses the config table entry
+    for the shape, else the default config.
+    """
+    M, N = xq.shape[0], wq.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    elif y.dtype != torch.bfloat16:
+        raise TypeError("y must be bfloat16")
+    return _gemm(_lib.w8_gemm_w8a8, fmt, xq, sx, wq, sw, y, cfg, workspace, stream)
+
+
+def gemm_w8a8_acc(fmt, xq, sx, wq, sw, cfg=None, out=None, workspace=None, stream=None):
+    """Test hook: raw accumulators [M, N] (int32 for W8A8_INT8, else fp32)."""
+    M, N = xq.shape[0], wq.shape[0]
+    dt = torch.int32 if _fmt(fmt) == FORMATS["W8A8_INT8"] else torch.float32
+    if out is None:
+        out = torch.empty((M, N), dtype=dt, device=xq.device)
+    elif out.dtype != dt:
+        raise TypeError(f"out must be {dt}")
+    return _gemm(_lib.w8_gemm_w8a8_acc, fmt, xq, sx, wq, sw, out, cfg, workspace, stream)
+
+
+def linear(fmt, x, wq, sw, cfg=None, y=None, workspace=None, stream=None):
+    """The whole hot path: quantize bf16 activations, then the GEMM."""
+    xq, sx = quantize_act(fmt, x, stream=stream)
+    return gemm_w8a8(fmt, xq, sx, wq, sw, cfg=cfg, y=y, workspace=workspace, stream=stream)
+
+
+# ------------------------------------------------------------------- config --
+def validate_config(fmt, M, N, K, cfg):
+    _check(_lib.w8_validate_config(_fmt(fmt), M, N, K, _cfg_ptr(cfg)))
+
+
+def default_config(fmt, M, N, K):
+    c = Config()
+    _check(_lib.w8_default_config(_fmt(fmt), M, N, K, ctypes.byref(c)))
+    return c
+
+
+def resolve_config(fmt, M, N, K):
+    """(Config, from_table) that gemm_w8a8 uses when cfg is None."""
+    c = Config()
+    hit = ctypes.c_int(0)
+    _check(_lib.w8_resolve_config(_fmt(fmt), M, N, K, ctypes.byref(c), ctypes.byref(hit)))
+    return c, bool(hit.value)
+
+
+def lookup_config(fmt, M, N, K):
+    """Exact table entry for the shape, or None."""
+    c = Config()
+    st = _lib.w8_lookup_config(_fmt(fmt), M, N, K, ctypes.byref(c))
+    if st == 8:
+        return None
+    _check(st)
+    return c
+
+
+def set_config(fmt, M, N, K, cfg, us_per_gemm=0.0):
+    if isinstance(cfg, dict):
+        cfg = Config.make(**cfg)
+    _check(_lib.w8_set_config(_fmt(fmt), M, N, K, ctypes.byref(cfg), float(us_per_gemm)))
+
+
+def load_config_table(path):
+    _check(_lib.w8_load_config_table(os.fsencode(path)))
+
+
+def save_config_table(path):
+    _check(_lib.w8_save_config_table(os.fsencode(path)))
+
+
+def clear_config_table():
+    _lib.w8_clear_config_table()
+
+
+def config_table_size():
+    return _lib.w8_config_table_size()
+
+
+def config_table_foreign():
+    return _lib.w8_config_table_foreign()
+
+
+def load_default_table():
+    """Load the shipped gfx950 table if present; returns True if loaded."""
+    if os.path.exists(DEFAULT_TABLE):
+        load_config_table(DEFAULT_TABLE)
+        return True
+    return False
+
+
+# -------------------------------------------------------------------- tuner --
+def tune_shape(fmt, M, N, K, warmup=3, replays=10, bank2_top=6, rotate_bytes=1 << 30,
+               max_split_k=MAX_SPLIT_K, insert=True, fail_candidate=-1):
+    """Ahead-of-time tuning of one shape on the current device.
+
+    Returns (Config, stats dict).  Synchronizes the device.
+    """
+    o = TuneOpts()
+    _lib.w8_tune_default_opts(ctypes.byref(o))
+    o.warmup, o.replays, o.bank2_top = warmup, replays, bank2_top
+    o.rotate_bytes, o.max_split_k = rotate_bytes, max_split_k
+    o.insert, o.fail_candidate = int(bool(insert)), fail_candidate
+    best = Config()
+    stats = TuneStats()
+    _check(_lib.w8_tune_shape(_fmt(fmt), M, N, K, ctypes.byref(o), ctypes.byref(best),
+                              ctypes.byref(stats)))
+    return best, stats.as_dict()
+
+
+def algorithmic_bytes(fmt, M, N, K):
+    """Bytes the GEMM must move: weights, activations, scales and bf16 output."""
+    if _fmt(fmt) == FORMATS["Block_FP8"]:
+        G = (K + GROUP - 1) // GROUP
+        return N * K + M * K + 2 * M * N + 4 * ((N + GROUP - 1) // GROUP) * G + 4 * M * G
+    return N * K + M * K + 2 * M * N + 4 * N + 4 * M
+
+
+load_default_table()

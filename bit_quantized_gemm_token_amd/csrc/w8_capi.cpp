@@ -1,0 +1,356 @@
+// C-ABI of the w8gemm library: argument validation, config resolution and
+// kernel dispatch.  Nothing here allocates, frees or synchronizes on the
+// quantize / GEMM path, so both can be captured into a HIP graph.
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "w8_internal.hpp"
+
+namespace w8 {
+
+namespace {
+thread_local std::string g_err;
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int kMaxK = 1 << 22;
+constexpr int kMaxN = 1 << 24;
+
+int wn_index(int wn) { return wn == 1 ? 0 : wn == 2 ? 1 : wn == 4 ? 2 : -1; }
+int wk_index(int wk) { return wk == 1 ? 0 : wk == 2 ? 1 : wk == 4 ? 2 : wk == 8 ? 3 : -1; }
+int u_index(int u) { return u == 1 ? 0 : u == 2 ? 1 : u == 4 ? 2 : -1; }
+
+// [fmt][mb-1][wn][wk][unroll][swap] -> launcher
+struct InstanceIndex {
+  GemmLaunchFn fn[3][2][3][4][3][2] = {};
+  InstanceIndex() {
+    int n = 0;
+    const GemmInstance* p = gemm_instances(&n);
+    for (int i = 0; i < n; ++i) {
+      const GemmInstance& g = p[i];
+      fn[g.fmt][g.mb - 1][wn_index(g.wn)][wk_index(g.wk)][u_index(g.unroll)][g.swap] = g.fn;
+    }
+  }
+};
+
+const InstanceIndex& instance_index() {
+  static const InstanceIndex idx;
+  return idx;
+}
+}  // namespace
+
+w8_status fail(w8_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+w8_status ok() {
+  g_err.clear();
+  return W8_OK;
+}
+
+std::string hip_msg(const char* what, hipError_t e) {
+  return std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
+}
+
+const char* fmt_name(int fmt) {
+  switch (fmt) {
+    case W8_FP8_DYNAMIC: return "FP8_Dynamic";
+    case W8_W8A8_INT8: return "W8A8_INT8";
+    case W8_BLOCK_FP8: return "Block_FP8";
+  }
+  return "?";
+}
+
+int fmt_from_name(const std::string& s) {
+  for (int f = 0; f < 3; ++f)
+    if (s == fmt_name(f)) return f;
+  return -1;
+}
+
+int ksteps_of(int fmt, int K) { return (K + kstep_of(fmt) - 1) / kstep_of(fmt); }
+
+w8_status check_gemm_shape(int fmt, int M, int N, int K) {
+  if (fmt < 0 || fmt > 2) return fail(W8_E_INVALID, "unknown format " + std::to_string(fmt));
+  if (M < 1 || N < 1 || K < 1)
+    return fail(W8_E_INVALID, "M, N and K must be positive (M=" + std::to_string(M) +
+                                  ", N=" + std::to_string(N) + ", K=" + std::to_string(K) + ")");
+  if (M > W8_MAX_M)
+    return fail(W8_E_UNSUPPORTED, "M=" + std::to_string(M) + " is above the small-M window (" +
+                                      std::to_string(W8_MAX_M) + "); use another backend");
+  if (K % 16) return fail(W8_E_INVALID, "K must be a multiple of 16");
+  if (fmt == W8_BLOCK_FP8 && K % W8_GROUP) return fail(W8_E_INVALID, "Block_FP8 needs K % 128 == 0");
+  if (K > kMaxK) return fail(W8_E_INVALID, "K above 2^22");
+  if (N > kMaxN) return fail(W8_E_INVALID, "N above 2^24");
+  return W8_OK;
+}
+
+w8_status check_cfg(int fmt, int M, int N, int K, const w8_cfg& c) {
+  (void)fmt, (void)M, (void)K;
+  if (c.abi_version != W8_ABI_VERSION)
+    return fail(W8_E_INVALID, "cfg.abi_version " + std::to_string(c.abi_version) + " != " +
+                                  std::to_string(W8_ABI_VERSION));
+  if (c.reserved[0] || c.reserved[1]) return fail(W8_E_INVALID, "cfg.reserved must be zero");
+  if (c.tile_n != 16 && c.tile_n != 32 && c.tile_n != 64)
+    return fail(W8_E_INVALID, "cfg.tile_n must be 16, 32 or 64");
+  if (wk_index(c.waves_k) < 0) return fail(W8_E_INVALID, "cfg.waves_k must be 1, 2, 4 or 8");
+  if ((c.tile_n / 16) * c.waves_k > 8) return fail(W8_E_INVALID, "cfg: tile_n/16 * waves_k > 8");
+  if (u_index(c.unroll) < 0) return fail(W8_E_INVALID, "cfg.unroll must be 1, 2 or 4");
+  if (!is_pow2(c.split_k) || c.split_k > W8_MAX_SPLIT_K)
+    return fail(W8_E_INVALID, "cfg.split_k must be a power of two in [1, 256], got " +
+                                  std::to_string(c.split_k));
+  if (c.swap_ab != 0 && c.swap_ab != 1) return fail(W8_E_INVALID, "cfg.swap_ab must be 0 or 1");
+  if (c.split_k > 1 && (N + c.tile_n - 1) / c.tile_n > kSplitKMaxTiles)
+    return fail(W8_E_INVALID, "split_k > 1 supports at most " + std::to_string(kSplitKMaxTiles) +
+                                  " output tiles (N <= " +
+                                  std::to_string(kSplitKMaxTiles * c.tile_n) + ")");
+  return W8_OK;
+}
+
+size_t workspace_bytes(int fmt, int M, int N, const w8_cfg& c) {
+  (void)fmt;
+  if (c.split_k <= 1) return 0;
+  const int ntiles = (N + c.tile_n - 1) / c.tile_n;
+  const int mb = (M + 15) / 16;
+  return ws_counter_bytes(ntiles) + ws_partial_bytes(ntiles, c.split_k, c.tile_n / 16, mb);
+}
+
+// Default config (used when the table has no entry for the shape).  It
+// follows the rule of thumb the page quotes for vLLM's Block_FP8 backend --
+// Swap-AB below 32 tokens -- for every format, and picks the smallest
+// split_k that gives at least two workgroups per compute unit while every
+// wave keeps at least one full stage of K-steps.
+w8_cfg make_default_cfg(int fmt, int M, int N, int K) {
+  w8_cfg c;
+  std::memset(&c, 0, sizeof c);
+  c.abi_version = W8_ABI_VERSION;
+  c.tile_n = 16;
+  c.waves_k = 4;
+  c.unroll = 2;
+  c.swap_ab = M < 32 ? 1 : 0;
+  const int ntiles = (N + 15) / 16;
+  const int T = ksteps_of(fmt, K);
+  int s = 1;
+  while (s < W8_MAX_SPLIT_K && (long long)ntiles * s < 512 &&
+         T / (2 * s) >= c.waves_k * c.unroll)
+    s *= 2;
+  c.split_k = s;
+  return c;
+}
+
+w8_status check_device() {
+  static std::atomic<int> state[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("hipGetDevice", e));
+  if (dev < 0 || dev >= 64) return fail(W8_E_UNSUPPORTED, "device index out of range");
+  int st = state[dev].load();
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("hipGetDeviceProperties", e));
+    st = std::strncmp(prop.gcnArchName, kArch, std::strlen(kArch)) == 0 ? 1 : 2;
+    state[dev].store(st);
+  }
+  if (st != 1) return fail(W8_E_UNSUPPORTED, "this library is built for gfx950 only");
+  return W8_OK;
+}
+
+w8_status launch_gemm_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
+  const int mb = (g.M + 15) / 16;
+  const int wn = c.tile_n / 16;
+  GemmLaunchFn fn = instance_index().fn[g.fmt][mb - 1][wn_index(wn)][wk_index(c.waves_k)]
+                                         [u_index(c.unroll)][c.swap_ab];
+  if (!fn) return fail(W8_E_INVALID, "no compiled kernel for this config");
+  const int ntiles = (g.N + c.tile_n - 1) / c.tile_n;
+  GemmArgs a;
+  a.xq = static_cast<const uint8_t*>(g.xq);
+  a.sx = g.sx;
+  a.wq = static_cast<const uint8_t*>(g.wq);
+  a.sw = g.sw;
+  a.out = g.out;
+  a.ldq = g.ldq;
+  a.ldw = g.ldw;
+  a.ldo = g.ldo;
+  a.M = g.M;
+  a.N = g.N;
+  a.K = g.K;
+  a.ksteps = ksteps_of(g.fmt, g.K);
+  a.kfull = g.K / kstep_of(g.fmt);
+  a.split_k = c.split_k;
+  a.ntiles = ntiles;
+  a.sgroups = g.fmt == W8_BLOCK_FP8 ? g.K / W8_GROUP : 0;
+  a.out_mode = g.out_mode;
+  a.counters = nullptr;
+  a.part = nullptr;
+  if (c.split_k > 1) {
+    a.counters = static_cast<unsigned int*>(g.ws);
+    a.part = static_cast<char*>(g.ws) + ws_counter_bytes(ntiles);
+  }
+  hipError_t e = fn(a, dim3(ntiles, c.split_k), dim3(64 * wn * c.waves_k), s);
+  if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("GEMM launch", e));
+  return W8_OK;
+}
+
+}  // namespace w8
+
+using namespace w8;
+
+namespace {
+
+w8_status gemm_entry(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ldq,
+                     const float* sx, const void* wq, int64_t ldw, const float* sw, void* out,
+                     int64_t ldo, const w8_cfg* cfg, void* ws, size_t ws_bytes,
+                     w8_stream stream, int out_mode) {
+  w8_status st = check_gemm_shape(fmt, M, N, K);
+  if (st) return st;
+  if (!xq || !sx || !wq || !sw || !out) return fail(W8_E_INVALID, "null device pointer");
+  if (!aligned(xq, 16) || !aligned(wq, 16))
+    return fail(W8_E_INVALID, "xq and wq must be 16-byte aligned");
+  if (ldq < K || ldw < K || ldq % 16 || ldw % 16)
+    return fail(W8_E_INVALID, "ldq and ldw must be >= K and multiples of 16");
+  if (ldo < N) return fail(W8_E_INVALID, "output leading dimension must be >= N");
+  if (!aligned(sx, 4) || !aligned(sw, 4) || !aligned(out, out_mode ? 4 : 2))
+    return fail(W8_E_INVALID, "misaligned scale or output pointer");
+  w8_cfg c;
+  if (cfg) {
+    c = *cfg;
+    st = check_cfg(fmt, M, N, K, c);
+    if (st) return st;
+  } else {
+    c = resolve_cfg(fmt, M, N, K, nullptr);
+  }
+  const size_t need = workspace_bytes(fmt, M, N, c);
+  if (need > 0) {
+    if (!ws || ws_bytes < need)
+      return fail(W8_E_WORKSPACE, "workspace of " + std::to_string(need) + " bytes needed, got " +
+                                      std::to_string(ws ? ws_bytes : 0));
+    if (!aligned(ws, 16)) return fail(W8_E_INVALID, "workspace must be 16-byte aligned");
+  }
+  st = check_device();
+  if (st) return st;
+  GemmCall g{fmt, M, N, K, xq, ldq, sx, wq, ldw, sw, out, ldo, out_mode, ws, ws_bytes};
+  st = launch_gemm_call(g, c, static_cast<hipStream_t>(stream));
+  if (st) return st;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int w8_abi_version(void) { return W8_ABI_VERSION; }
+
+const char* w8_status_string(w8_status s) {
+  switch (s) {
+    case W8_OK: return "W8_OK";
+    case W8_E_INVALID: return "W8_E_INVALID";
+    case W8_E_UNSUPPORTED: return "W8_E_UNSUPPORTED";
+    case W8_E_WORKSPACE: return "W8_E_WORKSPACE";
+    case W8_E_TABLE_FORMAT: return "W8_E_TABLE_FORMAT";
+    case W8_E_IO: return "W8_E_IO";
+    case W8_E_HIP: return "W8_E_HIP";
+    case W8_E_VALIDATION: return "W8_E_VALIDATION";
+    case W8_E_NOT_FOUND: return "W8_E_NOT_FOUND";
+  }
+  return "W8_E_UNKNOWN";
+}
+
+const char* w8_last_error(void) { return g_err.c_str(); }
+
+w8_status w8_quantize_act(w8_fmt fmt, int M, int K, const void* x, int64_t ldx, void* xq,
+                          int64_t ldq, float* sx, w8_stream stream) {
+  w8_status st = check_gemm_shape(fmt, M, 1, K);
+  if (st) return st;
+  if (!x || !xq || !sx) return fail(W8_E_INVALID, "null device pointer");
+  if (!aligned(x, 16) || ldx % 8 || ldx < K)
+    return fail(W8_E_INVALID, "x must be 16-byte aligned with ldx >= K and ldx % 8 == 0");
+  if (!aligned(xq, 16) || ldq % 16 || ldq < K)
+    return fail(W8_E_INVALID, "xq must be 16-byte aligned with ldq >= K and ldq % 16 == 0");
+  if (!aligned(sx, 4)) return fail(W8_E_INVALID, "sx must be 4-byte aligned");
+  st = check_device();
+  if (st) return st;
+  QuantActArgs a{static_cast<const uint16_t*>(x), static_cast<uint8_t*>(xq), sx, ldx, ldq, M, K};
+  hipError_t e = launch_quantize_act(fmt, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("quantize_act launch", e));
+  return ok();
+}
+
+w8_status w8_quantize_weight(w8_fmt fmt, int N, int K, const float* w, int64_t ldw, void* wq,
+                             int64_t ldq, float* sw, w8_stream stream) {
+  if (fmt != W8_FP8_DYNAMIC && fmt != W8_BLOCK_FP8)
+    return fail(W8_E_INVALID, "weight quantization is defined for FP8_Dynamic and Block_FP8");
+  if (N < 1 || K < 1 || N > kMaxN || K > kMaxK) return fail(W8_E_INVALID, "bad N or K");
+  if (!w || !wq || !sw) return fail(W8_E_INVALID, "null device pointer");
+  if (ldw < K || ldq < K) return fail(W8_E_INVALID, "leading dimensions must be >= K");
+  if (!aligned(w, 4) || !aligned(sw, 4)) return fail(W8_E_INVALID, "misaligned w or sw");
+  w8_status st = check_device();
+  if (st) return st;
+  QuantWeightArgs a{w, static_cast<uint8_t*>(wq), sw, ldw, ldq, N, K};
+  hipError_t e = launch_quantize_weight(fmt, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("quantize_weight launch", e));
+  return ok();
+}
+
+w8_status w8_workspace_size(w8_fmt fmt, int M, int N, int K, const w8_cfg* cfg, size_t* bytes) {
+  w8_status st = check_gemm_shape(fmt, M, N, K);
+  if (st) return st;
+  if (!bytes) return fail(W8_E_INVALID, "null output pointer");
+  w8_cfg c;
+  if (cfg) {
+    c = *cfg;
+    st = check_cfg(fmt, M, N, K, c);
+    if (st) return st;
+  } else {
+    c = resolve_cfg(fmt, M, N, K, nullptr);
+  }
+  *bytes = workspace_bytes(fmt, M, N, c);
+  return ok();
+}
+
+w8_status w8_gemm_w8a8(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ldq,
+                       const float* sx, const void* wq, int64_t ldw, const float* sw, void* y,
+                       int64_t ldy, const w8_cfg* cfg, void* ws, size_t ws_bytes,
+                       w8_stream stream) {
+  return gemm_entry(fmt, M, N, K, xq, ldq, sx, wq, ldw, sw, y, ldy, cfg, ws, ws_bytes, stream, 0);
+}
+
+w8_status w8_gemm_w8a8_acc(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ldq,
+                           const float* sx, const void* wq, int64_t ldw, const float* sw,
+                           void* acc, int64_t ldacc, const w8_cfg* cfg, void* ws,
+                           size_t ws_bytes, w8_stream stream) {
+  return gemm_entry(fmt, M, N, K, xq, ldq, sx, wq, ldw, sw, acc, ldacc, cfg, ws, ws_bytes, stream,
+                    1);
+}
+
+w8_status w8_validate_config(w8_fmt fmt, int M, int N, int K, const w8_cfg* cfg) {
+  w8_status st = check_gemm_shape(fmt, M, N, K);
+  if (st) return st;
+  if (!cfg) return fail(W8_E_INVALID, "null cfg");
+  st = check_cfg(fmt, M, N, K, *cfg);
+  if (st) return st;
+  return ok();
+}
+
+w8_status w8_default_config(w8_fmt fmt, int M, int N, int K, w8_cfg* out) {
+  w8_status st = check_gemm_shape(fmt, M, N, K);
+  if (st) return st;
+  if (!out) return fail(W8_E_INVALID, "null output pointer");
+  *out = make_default_cfg(fmt, M, N, K);
+  return ok();
+}
+
+w8_status w8_resolve_config(w8_fmt fmt, int M, int N, int K, w8_cfg* out, int* from_table) {
+  w8_status st = check_gemm_shape(fmt, M, N, K);
+  if (st) return st;
+  if (!out) return fail(W8_E_INVALID, "null output pointer");
+  int hit = 0;
+  *out = resolve_cfg(fmt, M, N, K, &hit);
+  if (from_table) *from_table = hit;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Device-side helpers for gfx950: vector types, 8-bit encoders, bf16
+// rounding, wavefront reductions and the two MFMA forms the GEMM uses.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+enum Fmt { FP8_DYNAMIC = 0, W8A8_INT8 = 1, BLOCK_FP8 = 2 };
+
+constexpr float kQmaxE4M3 = 448.0f;  // largest finite OCP E4M3FN magnitude
+constexpr float kQmaxInt8 = 127.0f;  // symmetric int8 range [-127, 127]
+constexpr int kGroup = 128;          // Block_FP8 group / block edge
+
+// ---------------------------------------------------------------- codecs --
+// Saturating E4M3FN encode of four floats, packed little-endian into a dword.
+// v_cvt_pk_fp8_f32 rounds to nearest even in the OCP E4M3FN format on gfx950;
+// the explicit clamp to +-448 gives saturation (the sign of zero is kept by
+// v_max/v_min, so -0 and negative underflow encode as 0x80).
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -kQmaxE4M3), kQmaxE4M3);
+  b = fminf(fmaxf(b, -kQmaxE4M3), kQmaxE4M3);
+  c = fminf(fmaxf(c, -kQmaxE4M3), kQmaxE4M3);
+  d = fminf(fmaxf(d, -kQmaxE4M3), kQmaxE4M3);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// int8 encode: round to nearest even, clamp to [-127, 127].
+__device__ __forceinline__ uint32_t i8_byte(float v) {
+  float r = fminf(fmaxf(__builtin_rintf(v), -kQmaxInt8), kQmaxInt8);
+  return (uint32_t)((int)r) & 0xFFu;
+}
+
+__device__ __forceinline__ uint32_t i8_pack4(float a, float b, float c, float d) {
+  return i8_byte(a) | (i8_byte(b) << 8) | (i8_byte(c) << 16) | (i8_byte(d) << 24);
+}
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ------------------------------------------------------------- reductions --
+// Max over the 64 lanes of a wavefront (every lane gets the result).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Max over aligned segments of 16 lanes.
+__device__ __forceinline__ float seg16_max(float v) {
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// ------------------------------------------------------------------- MFMA --
+// 16x16 output tile; lane l holds column l%16, rows 4*(l/16) .. 4*(l/16)+3.
+// A and B operands: lane l supplies row (A) / column (B) l%16 and one slice
+// of K selected by l/16; both operands use the same lane->K assignment, so
+// loading the same K bytes of an activation row and a weight row into the
+// same lane slot pairs them correctly whatever the in-register K order is.
+
+// int8 x int8 -> int32, K = 64 (16 bytes per lane per operand).
+__device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// E4M3FN x E4M3FN -> fp32, K = 128 (32 bytes per lane per operand).  Format
+// selectors 0/0 pick FP8 E4M3 for both operands; zero scale operands select
+// the unscaled v_mfma_f32_16x16x128_f8f6f4.
+__device__ __forceinline__ v4f mfma_f8(v8i a, v8i b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+}  // namespace w8

@@ -1,0 +1,53 @@
+// Host-side internals shared by the C-ABI, the config table and the tuner.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "../../include/w8gemm.h"
+#include "w8_launch.hpp"
+
+namespace w8 {
+
+// Thread-local error text behind w8_last_error().
+w8_status fail(w8_status s, const std::string& msg);
+w8_status ok();
+std::string hip_msg(const char* what, hipError_t e);
+
+const char* fmt_name(int fmt);
+int fmt_from_name(const std::string& s);  // -1 if unknown
+
+// Shape checks shared by the GEMM, the quantizer and the tuner.
+w8_status check_gemm_shape(int fmt, int M, int N, int K);
+// Config checks (shape-independent and shape-dependent).
+w8_status check_cfg(int fmt, int M, int N, int K, const w8_cfg& c);
+w8_cfg make_default_cfg(int fmt, int M, int N, int K);
+size_t workspace_bytes(int fmt, int M, int N, const w8_cfg& c);
+int ksteps_of(int fmt, int K);
+
+// Resolve cfg == NULL through the table, else the default.
+w8_cfg resolve_cfg(int fmt, int M, int N, int K, int* from_table);
+
+// The device must be gfx950 (checked once per device).
+w8_status check_device();
+
+// Launch one GEMM (arguments already validated).
+struct GemmCall {
+  int fmt, M, N, K;
+  const void* xq;
+  long long ldq;
+  const float* sx;
+  const void* wq;
+  long long ldw;
+  const float* sw;
+  void* out;
+  long long ldo;
+  int out_mode;
+  void* ws;
+  size_t ws_bytes;
+};
+w8_status launch_gemm_call(const GemmCall& call, const w8_cfg& c, hipStream_t s);
+
+constexpr const char* kArch = "gfx950";
+
+}  // namespace w8

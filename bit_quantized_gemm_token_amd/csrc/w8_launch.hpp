@@ -1,0 +1,80 @@
+// Host-side declarations shared by the kernel translation units and the
+// C-ABI: kernel argument blocks, launchers and the GEMM instance registry.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w8 {
+
+// ------------------------------------------------------------- quantizer --
+struct QuantActArgs {
+  const uint16_t* x;  // bf16 [M, K]
+  uint8_t* xq;        // codes [M, K]
+  float* sx;          // [M] or [M, K/128]
+  long long ldx;      // elements
+  long long ldq;      // bytes
+  int M, K;
+};
+
+hipError_t launch_quantize_act(int fmt, const QuantActArgs& a, hipStream_t s);
+
+struct QuantWeightArgs {
+  const float* w;  // fp32 [N, K]
+  uint8_t* wq;     // codes [N, K]
+  float* sw;       // [N] or [ceil(N/128), ceil(K/128)]
+  long long ldw;   // elements
+  long long ldq;   // bytes
+  int N, K;
+};
+
+hipError_t launch_quantize_weight(int fmt, const QuantWeightArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------------ GEMM --
+struct GemmArgs {
+  const uint8_t* xq;       // activation codes [M, K], row stride ldq bytes
+  const float* sx;         // activation scales
+  const uint8_t* wq;       // weight codes [N, K], row stride ldw bytes
+  const float* sw;         // weight scales
+  void* out;               // bf16 Y [M, N] or 4-byte accumulators, stride ldo elements
+  void* part;              // split-K partials (workspace), 16-byte aligned
+  unsigned int* counters;  // split-K arrival counters, one per output tile
+  long long ldq, ldw, ldo;
+  int M, N, K;
+  int ksteps;    // K-steps in total: ceil(K / KSTEP)
+  int kfull;     // K-steps with no ragged tail: K / KSTEP
+  int split_k;
+  int ntiles;    // output tiles along N
+  int sgroups;   // Block_FP8: K / 128 (row stride of sx and sw)
+  int out_mode;  // 0: bf16 Y; 1: raw accumulators
+};
+
+typedef hipError_t (*GemmLaunchFn)(const GemmArgs&, dim3 grid, dim3 block, hipStream_t);
+
+struct GemmInstance {
+  int fmt, mb, wn, wk, unroll, swap;
+  GemmLaunchFn fn;
+};
+
+// Every compiled instance, gathered from the per-format translation units.
+const GemmInstance* gemm_instances(int* count);
+
+// K-step (bytes of K per MFMA) of each format.
+inline int kstep_of(int fmt) { return fmt == 1 ? 64 : 128; }
+
+// Workspace layout: a fixed 64 KiB counter region (one 4-byte arrival counter
+// per output tile, at most kSplitKMaxTiles tiles), then the partials: one
+// 1 KiB fragment (64 lanes x 16 bytes) per (tile, split, wave along N,
+// 16-row block of M).  The counter region has the same size for every shape,
+// so the partials of one call never overlap the counters of another call
+// that shares the workspace: counters left at zero stay zero.
+constexpr int kSplitKMaxTiles = 16384;
+inline size_t ws_counter_bytes(int ntiles) {
+  (void)ntiles;
+  return (size_t)kSplitKMaxTiles * 4;
+}
+inline size_t ws_partial_bytes(int ntiles, int split_k, int wn, int mb) {
+  return (size_t)ntiles * split_k * wn * mb * 1024;
+}
+
+}  // namespace w8

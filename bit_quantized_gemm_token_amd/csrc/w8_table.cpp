@@ -1,0 +1,262 @@
+// Per-shape config table (ai-radar.it, "Helion nel backend vLLM", paragraphs
+// 6-7: tuned configs are shipped per shape, with a default config for shapes
+// that have none).  Lookup is exact on (arch, abi, fmt, M, N, K); a miss, or
+// an entry written for another arch or ABI, falls back to the default config
+// (the hard-fallback cases of TensorRT-LLM issue 16363, "Suggested
+// direction", that apply to a table: cache miss and backend identity
+// mismatch).
+#include <cerrno>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <map>
+#include <mutex>
+#include <sstream>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "w8_internal.hpp"
+
+namespace w8 {
+namespace {
+
+struct Entry {
+  w8_cfg cfg;
+  double us;
+};
+
+typedef std::tuple<int, int, int, int> Key;  // fmt, M, N, K
+
+struct Table {
+  std::mutex mu;
+  std::map<Key, Entry> native;
+  std::vector<std::string> foreign;  // lines for another arch / abi, kept verbatim
+  int foreign_count = 0;
+  bool env_checked = false;
+};
+
+Table& table() {
+  static Table t;
+  return t;
+}
+
+bool parse_int(const std::string& s, int* out) {
+  if (s.empty()) return false;
+  char* end = nullptr;
+  errno = 0;
+  long v = std::strtol(s.c_str(), &end, 10);
+  if (errno || *end != '\0' || v < -2147483647L || v > 2147483647L) return false;
+  *out = (int)v;
+  return true;
+}
+
+bool parse_double(const std::string& s, double* out) {
+  if (s.empty()) return false;
+  char* end = nullptr;
+  errno = 0;
+  double v = std::strtod(s.c_str(), &end);
+  if (errno || *end != '\0') return false;
+  *out = v;
+  return true;
+}
+
+// Parses `text`; on success fills native/foreign, else returns the failing
+// line number and a reason.
+w8_status parse_table(const std::string& text, std::map<Key, Entry>* native,
+                      std::vector<std::string>* foreign) {
+  std::istringstream in(text);
+  std::string line;
+  int lineno = 0;
+  while (std::getline(in, line)) {
+    ++lineno;
+    const size_t hash = line.find('#');
+    const std::string body = hash == std::string::npos ? line : line.substr(0, hash);
+    std::istringstream ls(body);
+    std::vector<std::string> tok;
+    std::string t;
+    while (ls >> t) tok.push_back(t);
+    if (tok.empty()) continue;
+    const std::string where = "config table line " + std::to_string(lineno) + ": ";
+    if (tok.size() != 12)
+      return fail(W8_E_TABLE_FORMAT, where + "expected 12 fields, got " + std::to_string(tok.size()));
+    int abi = 0;
+    if (!parse_int(tok[1], &abi)) return fail(W8_E_TABLE_FORMAT, where + "bad abi field");
+    const int fmt = fmt_from_name(tok[2]);
+    if (fmt < 0) return fail(W8_E_TABLE_FORMAT, where + "unknown format '" + tok[2] + "'");
+    int v[8];
+    for (int i = 0; i < 8; ++i)
+      if (!parse_int(tok[3 + i], &v[i]))
+        return fail(W8_E_TABLE_FORMAT, where + "bad integer '" + tok[3 + i] + "'");
+    double us = 0;
+    if (!parse_double(tok[11], &us)) return fail(W8_E_TABLE_FORMAT, where + "bad time field");
+    if (tok[0] != kArch || abi != W8_ABI_VERSION) {
+      foreign->push_back(line);
+      continue;
+    }
+    w8_cfg c;
+    std::memset(&c, 0, sizeof c);
+    c.abi_version = abi;
+    c.tile_n = v[3];
+    c.waves_k = v[4];
+    c.unroll = v[5];
+    c.split_k = v[6];
+    c.swap_ab = v[7];
+    if (check_gemm_shape(fmt, v[0], v[1], v[2]) != W8_OK || check_cfg(fmt, v[0], v[1], v[2], c) != W8_OK)
+      return fail(W8_E_TABLE_FORMAT, where + "invalid entry (" + std::string(w8_last_error()) + ")");
+    (*native)[Key(fmt, v[0], v[1], v[2])] = Entry{c, us};
+  }
+  return W8_OK;
+}
+
+w8_status load_file(const char* path) {
+  std::ifstream f(path, std::ios::binary);
+  if (!f) return fail(W8_E_IO, std::string("cannot open ") + path);
+  std::stringstream ss;
+  ss << f.rdbuf();
+  if (f.bad()) return fail(W8_E_IO, std::string("cannot read ") + path);
+  std::map<Key, Entry> native;
+  std::vector<std::string> foreign;
+  w8_status st = parse_table(ss.str(), &native, &foreign);
+  if (st) return st;
+  Table& t = table();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.native.swap(native);
+  t.foreign.swap(foreign);
+  t.foreign_count = (int)t.foreign.size();
+  t.env_checked = true;
+  return ok();
+}
+
+void maybe_load_env(Table& t) {
+  // called with t.mu held
+  if (t.env_checked) return;
+  t.env_checked = true;
+  const char* p = std::getenv("W8_CONFIG_TABLE");
+  if (!p || !*p) return;
+  std::ifstream f(p, std::ios::binary);
+  if (!f) return;
+  std::stringstream ss;
+  ss << f.rdbuf();
+  std::map<Key, Entry> native;
+  std::vector<std::string> foreign;
+  if (parse_table(ss.str(), &native, &foreign) == W8_OK) {
+    t.native.swap(native);
+    t.foreign.swap(foreign);
+    t.foreign_count = (int)t.foreign.size();
+  } else if (std::getenv("W8_LOG")) {
+    std::fprintf(stderr, "w8gemm: W8_CONFIG_TABLE not loaded: %s\n", w8_last_error());
+  }
+}
+
+}  // namespace
+
+w8_cfg resolve_cfg(int fmt, int M, int N, int K, int* from_table) {
+  Table& t = table();
+  {
+    std::lock_guard<std::mutex> lk(t.mu);
+    maybe_load_env(t);
+    auto it = t.native.find(Key(fmt, M, N, K));
+    if (it != t.native.end()) {
+      if (from_table) *from_table = 1;
+      return it->second.cfg;
+    }
+  }
+  if (from_table) *from_table = 0;
+  return make_default_cfg(fmt, M, N, K);
+}
+
+}  // namespace w8
+
+using namespace w8;
+
+extern "C" {
+
+w8_status w8_load_config_table(const char* path) {
+  if (!path) return fail(W8_E_INVALID, "null path");
+  return load_file(path);
+}
+
+w8_status w8_save_config_table(const char* path) {
+  if (!path) return fail(W8_E_INVALID, "null path");
+  std::ostringstream out;
+  {
+    Table& t = table();
+    std::lock_guard<std::mutex> lk(t.mu);
+    maybe_load_env(t);
+    out << "# w8gemm per-shape config table\n"
+        << "# arch abi fmt M N K tile_n waves_k unroll split_k swap_ab us_per_gemm\n";
+    for (const auto& kv : t.native) {
+      const Entry& e = kv.second;
+      char buf[256];
+      std::snprintf(buf, sizeof buf, "%s %d %s %d %d %d %d %d %d %d %d %.4f\n", kArch,
+                    W8_ABI_VERSION, fmt_name(std::get<0>(kv.first)), std::get<1>(kv.first),
+                    std::get<2>(kv.first), std::get<3>(kv.first), e.cfg.tile_n, e.cfg.waves_k,
+                    e.cfg.unroll, e.cfg.split_k, e.cfg.swap_ab, e.us);
+      out << buf;
+    }
+    for (const auto& l : t.foreign) out << l << "\n";
+  }
+  // write-then-rename so a crash never leaves a truncated table behind
+  const std::string tmp = std::string(path) + ".tmp";
+  {
+    std::ofstream f(tmp, std::ios::binary | std::ios::trunc);
+    if (!f) return fail(W8_E_IO, "cannot write " + tmp);
+    f << out.str();
+    f.flush();
+    if (!f) return fail(W8_E_IO, "write failed: " + tmp);
+  }
+  if (std::rename(tmp.c_str(), path) != 0) return fail(W8_E_IO, std::string("cannot rename to ") + path);
+  return ok();
+}
+
+void w8_clear_config_table(void) {
+  Table& t = table();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.native.clear();
+  t.foreign.clear();
+  t.foreign_count = 0;
+  t.env_checked = true;
+}
+
+int w8_config_table_size(void) {
+  Table& t = table();
+  std::lock_guard<std::mutex> lk(t.mu);
+  maybe_load_env(t);
+  return (int)t.native.size();
+}
+
+int w8_config_table_foreign(void) {
+  Table& t = table();
+  std::lock_guard<std::mutex> lk(t.mu);
+  return t.foreign_count;
+}
+
+w8_status w8_set_config(w8_fmt fmt, int M, int N, int K, const w8_cfg* cfg, double us_per_gemm) {
+  w8_status st = check_gemm_shape(fmt, M, N, K);
+  if (st) return st;
+  if (!cfg) return fail(W8_E_INVALID, "null cfg");
+  st = check_cfg(fmt, M, N, K, *cfg);
+  if (st) return st;
+  Table& t = table();
+  std::lock_guard<std::mutex> lk(t.mu);
+  maybe_load_env(t);
+  t.native[Key(fmt, M, N, K)] = Entry{*cfg, us_per_gemm};
+  return ok();
+}
+
+w8_status w8_lookup_config(w8_fmt fmt, int M, int N, int K, w8_cfg* out) {
+  w8_status st = check_gemm_shape(fmt, M, N, K);
+  if (st) return st;
+  if (!out) return fail(W8_E_INVALID, "null output pointer");
+  Table& t = table();
+  std::lock_guard<std::mutex> lk(t.mu);
+  maybe_load_env(t);
+  auto it = t.native.find(Key(fmt, M, N, K));
+  if (it == t.native.end()) return fail(W8_E_NOT_FOUND, "no table entry for this shape");
+  *out = it->second.cfg;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,350 @@
+// Ahead-of-time per-shape tuner (ai-radar.it, "Helion nel backend vLLM",
+// paragraph 3: the autotuner compares the combinations of the tunable
+// parameters -- split_k a power of two up to 256, swap_ab -- and keeps the
+// best per workload).
+//
+// Timing harness: every candidate runs as a HIP graph of R back-to-back
+// GEMMs, each on its own copy of the weights, R copies spanning at least
+// `rotate_bytes` so weight reads come from HBM and not from the last-level
+// cache; the graph is the way the tuned kernels are deployed (paragraph 4:
+// small-M shapes run under graph replay).  Candidates are picked on timing
+// bank 1 and the best few re-timed on a fresh bank 2, whose figures are the
+// ones reported (heliostune audit: select on one timing bank, score on
+// another).  Every candidate is first checked against the default config's
+// output on the same inputs; a mismatch removes it (TensorRT-LLM issue
+// 16363, "Suggested direction": select only after validation).
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "w8_device.hpp"
+#include "w8_internal.hpp"
+
+namespace w8 {
+namespace {
+
+__device__ __forceinline__ uint32_t hash32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  return x;
+}
+
+// Random 8-bit codes: int8 in [-127, 127], or E4M3FN with the NaN codes
+// replaced.
+__global__ void fill_codes_kernel(uint8_t* p, size_t n, uint32_t seed, int int8) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    uint32_t h = hash32((uint32_t)i * 2654435761U ^ seed ^ (uint32_t)(i >> 32));
+    uint8_t c = (uint8_t)h;
+    if (int8) {
+      if (c == 0x80) c = 0x81;
+    } else if ((c & 0x7F) == 0x7F) {
+      c = 0x38;
+    }
+    p[i] = c;
+  }
+}
+
+__global__ void fill_scales_kernel(float* p, size_t n, uint32_t seed, float lo, float hi) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const uint32_t h = hash32((uint32_t)i ^ seed);
+    p[i] = lo + (hi - lo) * ((h >> 8) * (1.0f / 16777216.0f));
+  }
+}
+
+struct Buffers {
+  uint8_t* wpool = nullptr;
+  uint8_t* xq = nullptr;
+  float* sx = nullptr;
+  float* sw = nullptr;
+  uint16_t* y = nullptr;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  ~Buffers() {
+    hipFree(wpool);
+    hipFree(xq);
+    hipFree(sx);
+    hipFree(sw);
+    hipFree(y);
+    hipFree(ws);
+  }
+};
+
+float bf16_to_float(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+struct Cand {
+  w8_cfg cfg;
+  int index;
+  double us1 = 1e30, us2 = 1e30;
+  bool valid = false;
+};
+
+#define TRY_HIP(expr)                                                       \
+  do {                                                                      \
+    hipError_t e_ = (expr);                                                 \
+    if (e_ != hipSuccess) return fail(W8_E_HIP, hip_msg(#expr, e_));        \
+  } while (0)
+
+}  // namespace
+}  // namespace w8
+
+using namespace w8;
+
+extern "C" void w8_tune_default_opts(w8_tune_opts* o) {
+  if (!o) return;
+  std::memset(o, 0, sizeof *o);
+  o->abi_version = W8_ABI_VERSION;
+  o->warmup = 3;
+  o->replays = 10;
+  o->bank2_top = 6;
+  o->rotate_bytes = (int64_t)1 << 30;
+  o->max_split_k = W8_MAX_SPLIT_K;
+  o->insert = 1;
+  o->fail_candidate = -1;
+}
+
+extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tune_opts* opts,
+                                   w8_cfg* best, w8_tune_stats* stats) {
+  const auto t_start = std::chrono::steady_clock::now();
+  w8_status st = check_gemm_shape(fmt, M, N, K);
+  if (st) return st;
+  if (!best) return fail(W8_E_INVALID, "null best");
+  w8_tune_opts o;
+  w8_tune_default_opts(&o);
+  if (opts) {
+    if (opts->abi_version != W8_ABI_VERSION) return fail(W8_E_INVALID, "opts.abi_version mismatch");
+    o = *opts;
+  }
+  if (o.warmup < 0 || o.replays < 1 || o.bank2_top < 1 || o.rotate_bytes < 0 ||
+      o.max_split_k < 1 || o.max_split_k > W8_MAX_SPLIT_K)
+    return fail(W8_E_INVALID, "bad tuner options");
+  st = check_device();
+  if (st) return st;
+
+  const long long ld = (K + 15) / 16 * 16;
+  const size_t wbytes = (size_t)N * ld;
+  size_t R = wbytes ? (size_t)((o.rotate_bytes + (long long)wbytes - 1) / (long long)wbytes) : 1;
+  R = std::max<size_t>(R, 2);
+  R = std::min<size_t>(R, 4096);
+  const bool block = fmt == W8_BLOCK_FP8;
+  const int G = K / W8_GROUP;
+  const size_t nsx = block ? (size_t)M * G : (size_t)M;
+  const size_t nsw = block ? (size_t)((N + 127) / 128) * G : (size_t)N;
+
+  // Candidates: every config of the family (with split_k up to max_split_k),
+  // minus those that cannot pay off: split_k above the number of K-steps
+  // (only empty splits added) and split-K partial traffic above twice the
+  // weight bytes.
+  std::vector<Cand> cands;
+  const int T = ksteps_of(fmt, K);
+  const int tiles_n[] = {16, 32, 64};
+  const int waves[] = {1, 2, 4, 8};
+  const int unrolls[] = {1, 2, 4};
+  size_t max_ws = 0;
+  for (int tn : tiles_n)
+    for (int wk : waves)
+      for (int u : unrolls)
+        for (int s = 1; s <= o.max_split_k; s *= 2)
+          for (int sw = 0; sw < 2; ++sw) {
+            w8_cfg c;
+            std::memset(&c, 0, sizeof c);
+            c.abi_version = W8_ABI_VERSION;
+            c.tile_n = tn;
+            c.waves_k = wk;
+            c.unroll = u;
+            c.split_k = s;
+            c.swap_ab = sw;
+            if (check_cfg(fmt, M, N, K, c) != W8_OK) continue;
+            if (s > T) continue;
+            const size_t wsb = workspace_bytes(fmt, M, N, c);
+            if (wsb > 2 * wbytes + 65536) continue;
+            max_ws = std::max(max_ws, wsb);
+            Cand cd;
+            cd.cfg = c;
+            cd.index = (int)cands.size();
+            cands.push_back(cd);
+          }
+  const w8_cfg dflt = make_default_cfg(fmt, M, N, K);
+  max_ws = std::max(max_ws, workspace_bytes(fmt, M, N, dflt));
+
+  Buffers b;
+  hipStream_t stream = nullptr;
+  TRY_HIP(hipStreamCreate(&stream));
+  struct StreamGuard {
+    hipStream_t s;
+    ~StreamGuard() { hipStreamDestroy(s); }
+  } sguard{stream};
+  TRY_HIP(hipMalloc(&b.wpool, wbytes * R));
+  TRY_HIP(hipMalloc(&b.xq, (size_t)M * ld));
+  TRY_HIP(hipMalloc(&b.sx, nsx * 4));
+  TRY_HIP(hipMalloc(&b.sw, nsw * 4));
+  TRY_HIP(hipMalloc(&b.y, (size_t)M * N * 2));
+  b.ws_bytes = max_ws;
+  if (max_ws) {
+    TRY_HIP(hipMalloc(&b.ws, max_ws));
+    TRY_HIP(hipMemsetAsync(b.ws, 0, max_ws, stream));
+  }
+  const int is_int8 = fmt == W8_W8A8_INT8;
+  hipLaunchKernelGGL(fill_codes_kernel, dim3(4096), dim3(256), 0, stream, b.wpool, wbytes * R,
+                     0x1234u, is_int8);
+  hipLaunchKernelGGL(fill_codes_kernel, dim3(64), dim3(256), 0, stream, b.xq, (size_t)M * ld,
+                     0x9876u, is_int8);
+  hipLaunchKernelGGL(fill_scales_kernel, dim3(64), dim3(256), 0, stream, b.sx, nsx, 0x55u, 0.01f,
+                     0.1f);
+  hipLaunchKernelGGL(fill_scales_kernel, dim3(64), dim3(256), 0, stream, b.sw, nsw, 0x77u, 0.001f,
+                     0.01f);
+  TRY_HIP(hipGetLastError());
+  TRY_HIP(hipStreamSynchronize(stream));
+
+  GemmCall call{fmt, M, N, K, b.xq, ld, b.sx, b.wpool, ld, b.sw, b.y, N, 0, b.ws, b.ws_bytes};
+
+  // Reference output: the default config on weight copy 0.
+  std::vector<uint16_t> yref((size_t)M * N), ycur((size_t)M * N);
+  st = launch_gemm_call(call, dflt, stream);
+  if (st) return st;
+  TRY_HIP(hipStreamSynchronize(stream));
+  TRY_HIP(hipMemcpy(yref.data(), b.y, yref.size() * 2, hipMemcpyDeviceToHost));
+  float ref_max = 0.0f;
+  for (uint16_t v : yref) ref_max = std::max(ref_max, std::fabs(bf16_to_float(v)));
+
+  auto validate = [&](const w8_cfg& c, bool* good) -> w8_status {
+    w8_status s2 = launch_gemm_call(call, c, stream);
+    if (s2) return s2;
+    TRY_HIP(hipStreamSynchronize(stream));
+    TRY_HIP(hipMemcpy(ycur.data(), b.y, ycur.size() * 2, hipMemcpyDeviceToHost));
+    *good = true;
+    for (size_t i = 0; i < ycur.size() && *good; ++i) {
+      if (is_int8) {
+        *good = ycur[i] == yref[i];
+      } else {
+        const float a = bf16_to_float(ycur[i]), r = bf16_to_float(yref[i]);
+        // fp32 sums in another order: relative 1e-2, plus a floor tied to the
+        // output's scale for entries that cancel to near zero
+        *good = std::fabs(a - r) <= 1e-2f * (1.0f + std::fabs(r)) + 1e-3f * ref_max;
+      }
+    }
+    return W8_OK;
+  };
+
+  // Median us per GEMM of the graph of R GEMMs over rotating weight copies.
+  auto time_cfg = [&](const w8_cfg& c, double* us) -> w8_status {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    TRY_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal));
+    w8_status s2 = W8_OK;
+    for (size_t r = 0; r < R && s2 == W8_OK; ++r) {
+      GemmCall cr = call;
+      cr.wq = b.wpool + r * wbytes;
+      s2 = launch_gemm_call(cr, c, stream);
+    }
+    hipError_t e = hipStreamEndCapture(stream, &graph);
+    if (s2) {
+      if (graph) hipGraphDestroy(graph);
+      return s2;
+    }
+    if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("hipStreamEndCapture", e));
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("hipGraphInstantiate", e));
+    hipEvent_t e0, e1;
+    hipEventCreate(&e0);
+    hipEventCreate(&e1);
+    std::vector<float> ms;
+    for (int i = 0; i < o.warmup + o.replays && e == hipSuccess; ++i) {
+      e = hipEventRecord(e0, stream);
+      if (e == hipSuccess) e = hipGraphLaunch(exec, stream);
+      if (e == hipSuccess) e = hipEventRecord(e1, stream);
+      if (e == hipSuccess) e = hipEventSynchronize(e1);
+      float t = 0;
+      if (e == hipSuccess) e = hipEventElapsedTime(&t, e0, e1);
+      if (i >= o.warmup) ms.push_back(t);
+    }
+    hipEventDestroy(e0);
+    hipEventDestroy(e1);
+    hipGraphExecDestroy(exec);
+    if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("timing replay", e));
+    std::sort(ms.begin(), ms.end());
+    *us = ms[ms.size() / 2] * 1000.0 / (double)R;
+    return W8_OK;
+  };
+
+  int nvalid = 0, nrej = 0;
+  for (Cand& cd : cands) {
+    bool good = false;
+    st = validate(cd.cfg, &good);
+    if (st) return st;
+    if (cd.index == o.fail_candidate) good = false;
+    if (!good) {
+      ++nrej;
+      continue;
+    }
+    cd.valid = true;
+    ++nvalid;
+    st = time_cfg(cd.cfg, &cd.us1);
+    if (st) return st;
+  }
+  if (nvalid == 0) return fail(W8_E_VALIDATION, "no candidate passed validation");
+
+  std::vector<Cand*> order;
+  for (Cand& cd : cands)
+    if (cd.valid) order.push_back(&cd);
+  std::sort(order.begin(), order.end(), [](const Cand* a, const Cand* c) { return a->us1 < c->us1; });
+  const size_t top = std::min<size_t>(order.size(), (size_t)o.bank2_top);
+  for (size_t i = 0; i < top; ++i) {
+    st = time_cfg(order[i]->cfg, &order[i]->us2);
+    if (st) return st;
+  }
+  double dflt_us2 = 0;
+  st = time_cfg(dflt, &dflt_us2);
+  if (st) return st;
+
+  // Bank-2 winner; within 1% prefer split_k = 1, then swap_ab = 0, then fewer waves.
+  Cand* win = order[0];
+  for (size_t i = 1; i < top; ++i) {
+    Cand* c = order[i];
+    const double a = c->us2, w = win->us2;
+    if (a < w * 0.99) {
+      win = c;
+    } else if (a <= w * 1.01) {
+      const auto rank = [](const w8_cfg& x) {
+        return std::make_tuple(x.split_k == 1 ? 0 : 1, x.swap_ab, x.waves_k * (x.tile_n / 16));
+      };
+      if (rank(c->cfg) < rank(win->cfg)) win = c;
+    }
+  }
+  *best = win->cfg;
+  if (o.insert) {
+    st = w8_set_config(fmt, M, N, K, &win->cfg, win->us2);
+    if (st) return st;
+  }
+  if (stats) {
+    std::memset(stats, 0, sizeof *stats);
+    stats->candidates = (int)cands.size();
+    stats->validated = nvalid;
+    stats->rejected = nrej;
+    stats->best_index = win->index;
+    stats->best_us_bank1 = win->us1;
+    stats->best_us_bank2 = win->us2;
+    stats->default_us_bank2 = dflt_us2;
+    const double bytes = block ? (double)N * K + (double)M * K + 2.0 * M * N +
+                                     4.0 * ((N + 127) / 128) * G + 4.0 * M * G
+                               : (double)N * K + (double)M * K + 2.0 * M * N + 4.0 * N + 4.0 * M;
+    stats->best_gbps = bytes / (win->us2 * 1e3);
+    stats->tune_seconds =
+        std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
+  }
+  return ok();
+}

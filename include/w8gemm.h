@@ -1,0 +1,263 @@
+/*
+ * w8gemm: small-M 8-bit quantized linear-layer GEMM for MI355X (gfx950).
+ *
+ *     Y[M, N] = dequant(Xq)[M, K] . dequant(Wq)[N, K]^T,   1 <= M <= 32
+ *
+ * The method: ai-radar.it, "Helion nel backend vLLM: un solo GEMM, tuning per
+ * forma e guadagni fino al 10%".
+ *   - paragraph 1: the three 8-bit formats FP8_Dynamic, W8A8_INT8, Block_FP8;
+ *   - paragraph 2: Standard, Split-K and Swap-AB computed by one GEMM family;
+ *   - paragraph 3: split_k and swap_ab are tunables, split_k a power of two
+ *     up to 256, chosen per shape by an ahead-of-time tuner;
+ *   - paragraph 4: the tuned kernels serve token counts up to 32 under graph
+ *     replay; larger M goes to another backend;
+ *   - paragraphs 6-7: per-shape config files, with a default config when no
+ *     tuned entry exists;
+ *   - paragraph 8: quantization is an auxiliary kernel beside the GEMM.
+ * The page defines none of the formats; this library uses:
+ *   FP8_Dynamic  activations: per-token (row) OCP E4M3FN codes, fp32 sx[M];
+ *                weights: E4M3FN codes, fp32 sw[N] (one per output channel);
+ *                fp32 accumulation.
+ *   W8A8_INT8    activations: per-token int8 codes, fp32 sx[M];
+ *                weights: int8 codes, fp32 sw[N]; exact int32 accumulation.
+ *   Block_FP8    activations: E4M3FN, fp32 sx[M, K/128] (1x128 groups);
+ *                weights: E4M3FN, fp32 sw[ceil(N/128), K/128] (128x128
+ *                blocks); each 128-wide K group's partial dot product is
+ *                multiplied by sx[m, g] * sw[n/128, g] before the groups are
+ *                summed in fp32.
+ * Scales are dequantization multipliers (x ~= code * s).  Quantization uses
+ * s = amax / Qmax (Qmax 448 for E4M3FN, 127 for int8; s = 1 for an all-zero
+ * group), codes = round-to-nearest-even(x / s) with saturation to +-Qmax.
+ * Output Y is bf16 (round to nearest even), row-major.
+ *
+ * Layouts: every matrix is row-major with an explicit leading dimension.
+ * Wq is [N, K] with K contiguous (the usual linear-layer weight layout).
+ *
+ * Ownership: the caller owns every device buffer.  w8_quantize_act,
+ * w8_gemm_w8a8 and w8_gemm_w8a8_acc never allocate, free or synchronize; they
+ * only enqueue kernels on the caller's stream, so they can be captured into a
+ * HIP graph.  The config table is owned by the library (process-global,
+ * guarded by a mutex).  w8_tune_shape allocates, synchronizes and must not be
+ * called while the stream is capturing.
+ *
+ * Errors: every entry point returns a w8_status.  All argument checks run
+ * before anything is enqueued, and nothing throws or aborts across the ABI.
+ * A kernel launch failure returns W8_E_HIP; asynchronous device faults show
+ * up at the caller's next synchronization.  w8_last_error() gives a
+ * thread-local message for the last failing call.
+ *
+ * Streams: w8_stream is a hipStream_t passed as a plain pointer (NULL is the
+ * default stream).  Device pointers are HIP device (or managed) addresses.
+ */
+#ifndef W8GEMM_H
+#define W8GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W8_ABI_VERSION 1
+#define W8_MAX_M 32         /* token-count window of the tuned path (paragraph 4) */
+#define W8_MAX_SPLIT_K 256  /* split_k is a power of two up to 256 (paragraph 3) */
+#define W8_GROUP 128        /* Block_FP8 group / block edge */
+
+typedef void *w8_stream; /* hipStream_t */
+
+typedef enum {
+    W8_FP8_DYNAMIC = 0,
+    W8_W8A8_INT8 = 1,
+    W8_BLOCK_FP8 = 2
+} w8_fmt;
+
+typedef enum {
+    W8_OK = 0,
+    W8_E_INVALID = 1,      /* bad argument, alignment or config */
+    W8_E_UNSUPPORTED = 2,  /* outside the method's window (M > 32): caller falls back */
+    W8_E_WORKSPACE = 3,    /* workspace missing or too small */
+    W8_E_TABLE_FORMAT = 4, /* config-table file malformed; the old table is kept */
+    W8_E_IO = 5,           /* file could not be read or written */
+    W8_E_HIP = 6,          /* a HIP runtime call failed */
+    W8_E_VALIDATION = 7,   /* tuner: no candidate passed validation */
+    W8_E_NOT_FOUND = 8     /* lookup miss */
+} w8_status;
+
+/* One kernel configuration of the GEMM family (paragraph 2-3 of the page:
+ * the algorithmic variants are parameters, not separate kernels).
+ *   tile_n   output columns (= weight rows) per workgroup: 16, 32 or 64.
+ *   waves_k  wavefronts inside one workgroup that split its K range and are
+ *            reduced through LDS: 1, 2, 4 or 8 (tile_n/16 * waves_k <= 8).
+ *   unroll   MFMA K-steps each wave keeps in flight per loop iteration:
+ *            1, 2 or 4.
+ *   split_k  workgroups splitting K, reduced in fixed order by the last one
+ *            to finish: 1, 2, 4, ..., 256 (Split-K; 1 = Standard).
+ *   swap_ab  0: MFMA A operand = activations, B = weights^T.
+ *            1: Swap-AB, Y^T = Wq . Xq^T: A = weights, B = activations^T.
+ * Set abi_version to W8_ABI_VERSION and reserved[] to 0.                    */
+typedef struct {
+    int32_t abi_version;
+    int32_t tile_n;
+    int32_t waves_k;
+    int32_t unroll;
+    int32_t split_k;
+    int32_t swap_ab;
+    int32_t reserved[2];
+} w8_cfg;
+
+/* Options of the ahead-of-time tuner (paragraph 3 and 6 of the page). */
+typedef struct {
+    int32_t abi_version;      /* W8_ABI_VERSION */
+    int32_t warmup;           /* untimed graph replays per candidate (default 3) */
+    int32_t replays;          /* timed graph replays per candidate and bank (default 10) */
+    int32_t bank2_top;        /* best bank-1 candidates re-timed on bank 2 (default 6) */
+    int64_t rotate_bytes;     /* weight bytes cycled through per graph, >= the last-level
+                                 cache so reads come from HBM (default 1 GiB) */
+    int32_t max_split_k;      /* largest split_k tried (default 256) */
+    int32_t insert;           /* 1: insert the winner into the config table */
+    int32_t fail_candidate;   /* test hook: candidate with this index fails validation
+                                 (-1 = none) */
+    int32_t reserved[3];
+} w8_tune_opts;
+
+typedef struct {
+    int32_t candidates;       /* feasible candidates enumerated */
+    int32_t validated;        /* of which passed validation against the default config */
+    int32_t rejected;         /* of which failed validation */
+    int32_t best_index;       /* index of the winner in enumeration order */
+    double best_us_bank1;     /* winner, median us per GEMM on timing bank 1 */
+    double best_us_bank2;     /* winner, median us per GEMM on bank 2 (reported figure) */
+    double default_us_bank2;  /* default config on bank 2 */
+    double best_gbps;         /* algorithmic bytes / best_us_bank2 */
+    double tune_seconds;      /* wall-clock time of the whole tuning call */
+} w8_tune_stats;
+
+/* ---------------------------------------------------------------- info -- */
+int w8_abi_version(void);
+const char *w8_status_string(w8_status s);
+const char *w8_last_error(void); /* thread-local; "" when the last call succeeded */
+
+/* --------------------------------------------------------- quantization -- */
+/* Dynamic activation quantization (paragraph 1's formats, paragraph 8's
+ * auxiliary quantization kernel).  One kernel launch on `stream`.
+ *   x    bf16 [M, K], row stride ldx elements (device)
+ *   xq   1-byte codes [M, K], row stride ldq bytes (device): E4M3FN for the
+ *        FP8 formats, int8 for W8A8_INT8
+ *   sx   fp32 scales (device): [M] (FP8_Dynamic, W8A8_INT8) or [M, K/128]
+ *        row-major (Block_FP8)
+ * Requires 1 <= M <= 32 (else W8_E_UNSUPPORTED), K >= 16, K % 16 == 0
+ * (Block_FP8: K % 128 == 0), ldx >= K, ldq >= K, x 16-byte aligned with
+ * ldx % 8 == 0, xq 16-byte aligned with ldq % 16 == 0.  Inputs must be finite. */
+w8_status w8_quantize_act(w8_fmt fmt, int M, int K, const void *x, int64_t ldx,
+                          void *xq, int64_t ldq, float *sx, w8_stream stream);
+
+/* Offline weight quantization to E4M3FN (FP8_Dynamic: one scale per row,
+ * sw[N]; Block_FP8: one scale per 128x128 block, sw[ceil(N/128), ceil(K/128)]
+ * row-major, edge blocks may be partial).  W8A8_INT8 weights are supplied as
+ * codes and scales and are rejected here (W8_E_INVALID).
+ *   w    fp32 [N, K], row stride ldw elements (device)
+ *   wq   1-byte codes [N, K], row stride ldq bytes (device)
+ * Requires N >= 1, K >= 1, ldw >= K, ldq >= K.  Inputs must be finite.       */
+w8_status w8_quantize_weight(w8_fmt fmt, int N, int K, const float *w, int64_t ldw,
+                             void *wq, int64_t ldq, float *sw, w8_stream stream);
+
+/* ------------------------------------------------------------------ GEMM -- */
+/* Bytes of device workspace the GEMM needs for (fmt, M, N, K) under cfg
+ * (cfg NULL: the config w8_resolve_config picks).  0 when split_k == 1.
+ * Layout: a fixed 64 KiB region of arrival counters, then the split-K
+ * partials; split_k > 1 therefore supports at most 16384 output tiles
+ * (N <= 16384 * tile_n).                                                    */
+w8_status w8_workspace_size(w8_fmt fmt, int M, int N, int K, const w8_cfg *cfg,
+                            size_t *bytes);
+
+/* The quantized GEMM.  One kernel launch on `stream` (the split-K reduction
+ * runs inside it: the last workgroup of each output tile to finish sums the
+ * partials in split order, so results are run-to-run deterministic).
+ *   xq, sx  activations as written by w8_quantize_act
+ *   wq, sw  weights: codes [N, K] with row stride ldw bytes and scales in the
+ *           layout given above for fmt
+ *   y       bf16 [M, N], row stride ldy elements (device)
+ *   cfg     kernel configuration; NULL = the config table entry for
+ *           (fmt, M, N, K) on this device, else the default config
+ *   ws      workspace of at least w8_workspace_size() bytes, zero-filled
+ *           before its first use; every completed call leaves its counters
+ *           at zero again.  May be NULL when the size is 0.  Calls that share
+ *           a workspace must not run concurrently.
+ * Requires 1 <= M <= 32 (else W8_E_UNSUPPORTED), N >= 1, K >= 16,
+ * K % 16 == 0 (Block_FP8: K % 128 == 0), ldq >= K, ldw >= K, ldy >= N,
+ * xq/wq 16-byte aligned with ldq % 16 == 0 and ldw % 16 == 0, finite codes
+ * (no E4M3FN NaN codes).                                                     */
+w8_status w8_gemm_w8a8(w8_fmt fmt, int M, int N, int K,
+                       const void *xq, int64_t ldq, const float *sx,
+                       const void *wq, int64_t ldw, const float *sw,
+                       void *y, int64_t ldy, const w8_cfg *cfg,
+                       void *ws, size_t ws_bytes, w8_stream stream);
+
+/* Test hook: the same GEMM with the accumulators written raw instead of the
+ * bf16 output.  acc is [M, N] 4-byte elements with row stride ldacc:
+ *   W8A8_INT8    int32  sum_k xq*wq               (exact)
+ *   FP8_Dynamic  fp32   sum_k dec(xq)*dec(wq)     (scales not applied)
+ *   Block_FP8    fp32   sum_g sx*sw*partial_g     (the value before bf16)  */
+w8_status w8_gemm_w8a8_acc(w8_fmt fmt, int M, int N, int K,
+                           const void *xq, int64_t ldq, const float *sx,
+                           const void *wq, int64_t ldw, const float *sw,
+                           void *acc, int64_t ldacc, const w8_cfg *cfg,
+                           void *ws, size_t ws_bytes, w8_stream stream);
+
+/* ---------------------------------------------------------------- config -- */
+/* W8_OK if cfg is a valid configuration for (fmt, M, N, K), else
+ * W8_E_INVALID (with the reason in w8_last_error()).                        */
+w8_status w8_validate_config(w8_fmt fmt, int M, int N, int K, const w8_cfg *cfg);
+
+/* The built-in default configuration for (fmt, M, N, K) (paragraph 7 of the
+ * page: a default config serves untuned shapes).                           */
+w8_status w8_default_config(w8_fmt fmt, int M, int N, int K, w8_cfg *out);
+
+/* The config the GEMM uses when called with cfg == NULL: the table entry for
+ * (this device's arch, W8_ABI_VERSION, fmt, M, N, K) if present, else the
+ * default.  *from_table is set to 1 on a table hit, 0 otherwise.            */
+w8_status w8_resolve_config(w8_fmt fmt, int M, int N, int K, w8_cfg *out,
+                            int *from_table);
+
+/* ----------------------------------------------------------- config table -- */
+/* Per-shape config table (paragraphs 6-7 of the page).  Text format, one entry
+ * per line:
+ *   arch abi fmt M N K tile_n waves_k unroll split_k swap_ab us_per_gemm
+ * '#' starts a comment.  Entries whose arch or abi differ from this build and
+ * device are kept in the file but never used.
+ * w8_load_config_table replaces the in-memory table atomically: on any parse
+ * error it returns W8_E_TABLE_FORMAT (line number in w8_last_error()) and
+ * keeps the old table.  If the environment variable W8_CONFIG_TABLE names a
+ * file, it is loaded at the first config lookup.                           */
+w8_status w8_load_config_table(const char *path);
+w8_status w8_save_config_table(const char *path);
+void w8_clear_config_table(void);
+int w8_config_table_size(void);
+/* Entries of the last load that were skipped for a foreign arch or abi. */
+int w8_config_table_foreign(void);
+/* Insert or replace one entry for this device (validated first). */
+w8_status w8_set_config(w8_fmt fmt, int M, int N, int K, const w8_cfg *cfg,
+                        double us_per_gemm);
+/* Exact-shape lookup for this device: W8_OK on a hit, W8_E_NOT_FOUND on a miss. */
+w8_status w8_lookup_config(w8_fmt fmt, int M, int N, int K, w8_cfg *out);
+
+/* ------------------------------------------------------------------ tuner -- */
+/* Ahead-of-time per-shape tuner (paragraph 3 of the page: the autotuner
+ * compares configurations and keeps the best for each shape).  Allocates its
+ * own inputs (random codes and scales), enumerates every feasible config
+ * (tile_n x waves_k x unroll x split_k in {1, 2, ..., max_split_k} x
+ * swap_ab), checks each against the default config's output (bit-equal for
+ * W8A8_INT8, within 1e-2 relative for the FP8 formats) and times it as HIP
+ * graph replays over rotating weight copies; the best on timing bank 1 is
+ * re-timed with the runners-up on bank 2, and the bank-2 winner is returned
+ * (and inserted into the table when opts->insert).  opts NULL = defaults.
+ * Synchronizes the device; not callable during stream capture.            */
+w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tune_opts *opts,
+                        w8_cfg *best, w8_tune_stats *stats);
+void w8_tune_default_opts(w8_tune_opts *opts);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W8GEMM_H */

@@ -240,21 +240,25 @@ int or_quantize_act(int fmt, int M, int K, const uint16_t *x, int64_t ldx,
 int or_quantize_weight(int fmt, int N, int K, const float *w, int64_t ldw,
                        uint8_t *wq, int64_t ldq, float *sw)
 {
-    int n, rc;
+    int n;
     if (N <= 0 || K <= 0 || ldw < K || ldq < K)
         return OR_E_ARG;
     if (fmt == OR_FP8_DYNAMIC) {
-        for (n = 0; n < N; ++n) {
-            rc = quantize_group(w + (int64_t)n * ldw, K, 1, 0, wq + (int64_t)n * ldq, 1, &sw[n]);
-            if (rc)
-                return rc;
-        }
-        return OR_OK;
+        int bad = 0;
+        /* rows are independent groups; running them on several threads
+         * changes no arithmetic */
+#pragma omp parallel for schedule(static) reduction(| : bad)
+        for (n = 0; n < N; ++n)
+            bad |= quantize_group(w + (int64_t)n * ldw, K, 1, 0, wq + (int64_t)n * ldq, 1, &sw[n]);
+        return bad ? OR_E_NONFINITE : OR_OK;
     }
     if (fmt == OR_BLOCK_FP8) {
         int NB = (N + OR_GROUP - 1) / OR_GROUP, KB = (K + OR_GROUP - 1) / OR_GROUP;
-        int bn, bk;
-        for (bn = 0; bn < NB; ++bn)
+        int bn, bad = 0;
+        /* blocks are independent groups (see above) */
+#pragma omp parallel for schedule(static) reduction(| : bad)
+        for (bn = 0; bn < NB; ++bn) {
+            int bk;
             for (bk = 0; bk < KB; ++bk) {
                 int n0 = bn * OR_GROUP, k0 = bk * OR_GROUP;
                 int nr = (N - n0 < OR_GROUP) ? N - n0 : OR_GROUP;
@@ -265,8 +269,8 @@ int or_quantize_weight(int fmt, int N, int K, const float *w, int64_t ldw,
                     for (j = 0; j < kc; ++j) {
                         float a = fabsf(w[(int64_t)(n0 + i) * ldw + k0 + j]);
                         if (!isfinite(a))
-                            return OR_E_NONFINITE;
-                        if (a > amax)
+                            bad = 1;
+                        else if (a > amax)
                             amax = a;
                     }
                 scale = (amax == 0.0f) ? 1.0f : amax / 448.0f;
@@ -276,7 +280,8 @@ int or_quantize_weight(int fmt, int N, int K, const float *w, int64_t ldw,
                             or_e4m3_encode(w[(int64_t)(n0 + i) * ldw + k0 + j] / scale);
                 sw[(int64_t)bn * KB + bk] = scale;
             }
-        return OR_OK;
+        }
+        return bad ? OR_E_NONFINITE : OR_OK;
     }
     return OR_E_ARG;
 }

@@ -1,0 +1,236 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, rejects bad arguments before touching the device, and its
+config table parses, saves, reloads and falls back as documented."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w8gemm.h")
+
+
+@pytest.fixture(scope="module")
+def w8():
+    import bit_quantized_gemm_token_amd as mod
+    return mod
+
+
+@pytest.fixture(scope="module")
+def lib(w8):
+    return w8._lib
+
+
+@pytest.fixture(autouse=True)
+def _clean_table(w8):
+    w8.clear_config_table()
+    yield
+    w8.clear_config_table()
+
+
+def test_exports_every_declared_symbol(lib):
+    text = open(HEADER).read()
+    declared = sorted(set(re.findall(r"\b(w8_[a-z0-9_]+)\s*\(", text)))
+    assert len(declared) >= 20
+    from bit_quantized_gemm_token_amd import _capi
+    assert sorted(_capi.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _capi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(set(re.findall(r" T (\w+)", out)))
+    assert exported == declared          # nothing else leaks out of the library
+
+
+def test_abi_and_status_strings(lib):
+    assert lib.w8_abi_version() == 1
+    assert lib.w8_status_string(2) == b"W8_E_UNSUPPORTED"
+    assert lib.w8_status_string(99) == b"W8_E_UNKNOWN"
+
+
+def test_pages_constants_match_library(w8):
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_constants.json")))
+    assert list(w8.FORMATS) == g["formats"]["value"]
+    assert w8.MAX_M == g["max_tokens"]["value"]
+    allowed = [s for s in range(1, 513)
+               if _valid(w8, "W8A8_INT8", 16, 512, 1024, w8.Config.make(split_k=s))]
+    assert allowed == g["split_k_values"]["value"]
+    # M window: 32 accepted, 33 refused as unsupported (caller falls back)
+    w8.default_config("FP8_Dynamic", g["max_tokens"]["value"], 256, 256)
+    with pytest.raises(w8.UnsupportedShape):
+        w8.default_config("FP8_Dynamic", g["max_tokens"]["value"] + 1, 256, 256)
+
+
+def _valid(w8, fmt, M, N, K, cfg):
+    try:
+        w8.validate_config(fmt, M, N, K, cfg)
+        return True
+    except w8.W8Error:
+        return False
+
+
+@pytest.mark.parametrize("field,value", [("tile_n", 8), ("tile_n", 128), ("waves_k", 3),
+                                         ("waves_k", 16), ("unroll", 3), ("split_k", 0),
+                                         ("split_k", 3), ("split_k", 512), ("swap_ab", 2)])
+def test_config_rejects(w8, field, value):
+    cfg = w8.Config.make()
+    setattr(cfg, field, value)
+    assert not _valid(w8, "FP8_Dynamic", 4, 512, 1024, cfg)
+
+
+def test_config_rejects_abi_and_reserved(w8):
+    cfg = w8.Config.make()
+    cfg.abi_version = 2
+    assert not _valid(w8, "FP8_Dynamic", 4, 512, 1024, cfg)
+    cfg = w8.Config.make()
+    cfg.reserved[1] = 7
+    assert not _valid(w8, "FP8_Dynamic", 4, 512, 1024, cfg)
+    cfg = w8.Config.make(tile_n=64, waves_k=4)   # 4 x 4 = 16 waves > 8
+    assert not _valid(w8, "FP8_Dynamic", 4, 512, 1024, cfg)
+
+
+def test_default_config_is_valid_everywhere(w8):
+    import synthetic
+    for fmt in w8.FORMATS:
+        for (M, N, K) in synthetic.SWEEP + ((2, 512, 7168), (32, 4096, 4096)):
+            c = w8.default_config(fmt, M, N, K)
+            w8.validate_config(fmt, M, N, K, c)
+            assert c.swap_ab == (1 if M < 32 else 0)
+
+
+FAKE = ctypes.c_void_p(0x100000)   # 16-byte aligned, never dereferenced
+
+
+def _gemm(lib, fmt=0, M=4, N=64, K=256, xq=FAKE, ldq=256, sx=FAKE, wq=FAKE, ldw=256, sw=FAKE,
+          y=FAKE, ldy=64, cfg=None, ws=None, wsb=0):
+    return lib.w8_gemm_w8a8(fmt, M, N, K, xq, ldq, sx, wq, ldw, sw, y, ldy, cfg, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=0), 1), (dict(M=33), 2), (dict(N=0), 1), (dict(K=0), 1), (dict(K=200), 1),
+    (dict(fmt=2, K=272, ldq=272, ldw=272), 1), (dict(fmt=7), 1),
+    (dict(xq=None), 1), (dict(sw=None), 1), (dict(y=None), 1),
+    (dict(xq=ctypes.c_void_p(0x100008)), 1), (dict(ldq=255), 1), (dict(ldw=248), 1),
+    (dict(ldy=63), 1), (dict(sx=ctypes.c_void_p(0x100002)), 1)])
+def test_gemm_argument_errors(lib, kw, status):
+    assert _gemm(lib, **kw) == status
+    assert lib.w8_last_error() != b""
+
+
+def test_gemm_workspace_errors(w8, lib):
+    cfg = w8.Config.make(split_k=8)
+    need = w8.workspace_size("FP8_Dynamic", 4, 64, 1024, cfg)
+    assert need > 0
+    assert _gemm(lib, K=1024, ldq=1024, ldw=1024, cfg=ctypes.byref(cfg)) == 3
+    assert _gemm(lib, K=1024, ldq=1024, ldw=1024, cfg=ctypes.byref(cfg), ws=FAKE, wsb=need - 1) == 3
+    assert b"workspace" in lib.w8_last_error()
+    assert w8.workspace_size("FP8_Dynamic", 4, 64, 1024, w8.Config.make(split_k=1)) == 0
+
+
+def test_quantize_argument_errors(lib):
+    q = lib.w8_quantize_act
+    assert q(0, 33, 256, FAKE, 256, FAKE, 256, FAKE, None) == 2
+    assert q(0, 4, 100, FAKE, 256, FAKE, 256, FAKE, None) == 1
+    assert q(2, 4, 192, FAKE, 256, FAKE, 256, FAKE, None) == 1
+    assert q(0, 4, 256, FAKE, 252, FAKE, 256, FAKE, None) == 1
+    assert q(0, 4, 256, FAKE, 256, FAKE, 264, FAKE, None) == 1
+    assert q(0, 4, 256, None, 256, FAKE, 256, FAKE, None) == 1
+    w = lib.w8_quantize_weight
+    assert w(1, 4, 256, FAKE, 256, FAKE, 256, FAKE, None) == 1   # int8 weights are given
+    assert w(0, 0, 256, FAKE, 256, FAKE, 256, FAKE, None) == 1
+
+
+def test_table_roundtrip_and_lookup(w8, tmp_path):
+    c1 = w8.Config.make(tile_n=32, waves_k=2, unroll=4, split_k=16, swap_ab=1)
+    c2 = w8.Config.make(tile_n=16, waves_k=8, unroll=1, split_k=1, swap_ab=0)
+    w8.set_config("FP8_Dynamic", 4, 4096, 4096, c1, 3.25)
+    w8.set_config("Block_FP8", 32, 4608, 7168, c2, 5.5)
+    assert w8.config_table_size() == 2
+    assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096) == c1
+    assert w8.lookup_config("FP8_Dynamic", 5, 4096, 4096) is None
+    got, hit = w8.resolve_config("Block_FP8", 32, 4608, 7168)
+    assert hit and got == c2
+    got, hit = w8.resolve_config("Block_FP8", 16, 4608, 7168)       # miss -> default
+    assert not hit and got == w8.default_config("Block_FP8", 16, 4608, 7168)
+    p = tmp_path / "t.tbl"
+    w8.save_config_table(str(p))
+    w8.clear_config_table()
+    assert w8.config_table_size() == 0
+    w8.load_config_table(str(p))
+    assert w8.config_table_size() == 2
+    assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096) == c1
+    assert w8.lookup_config("Block_FP8", 32, 4608, 7168) == c2
+
+
+def test_table_malformed_keeps_old_table(w8, tmp_path):
+    w8.set_config("W8A8_INT8", 16, 896, 1024, w8.Config.make(), 1.0)
+    bad_files = [
+        "gfx950 1 W8A8_INT8 16 896 1024 16 4 2 1\n",                        # too few fields
+        "gfx950 1 INT4 16 896 1024 16 4 2 1 0 1.0\n",                       # unknown format
+        "gfx950 1 W8A8_INT8 16 896 1024 16 4 2 3 0 1.0\n",                  # split_k 3
+        "gfx950 1 W8A8_INT8 40 896 1024 16 4 2 1 0 1.0\n",                  # M above 32
+        "gfx950 1 W8A8_INT8 16 896 1024 16 4 x 1 0 1.0\n",                  # not an integer
+        "gfx950 1 W8A8_INT8 16 896 1024 16 4 2 1 0 fast\n",                 # bad time
+    ]
+    for i, text in enumerate(bad_files):
+        p = tmp_path / f"bad{i}.tbl"
+        p.write_text("# header\n" + text)
+        with pytest.raises(w8.W8Error) as e:
+            w8.load_config_table(str(p))
+        assert e.value.status == 4 and "line 2" in str(e.value)
+        assert w8.config_table_size() == 1          # old table kept
+    with pytest.raises(w8.W8Error) as e:
+        w8.load_config_table(str(tmp_path / "missing.tbl"))
+    assert e.value.status == 5
+
+
+def test_table_foreign_entries_ignored_and_kept(w8, tmp_path):
+    p = tmp_path / "mixed.tbl"
+    p.write_text("gfx942 1 FP8_Dynamic 4 4096 4096 64 2 4 1 1 2.0\n"
+                 "gfx950 9 FP8_Dynamic 4 4096 4096 64 2 4 1 1 2.0\n"
+                 "gfx950 1 FP8_Dynamic 4 4096 4096 32 2 4 4 0 2.5  # native\n")
+    w8.load_config_table(str(p))
+    assert w8.config_table_size() == 1 and w8.config_table_foreign() == 2
+    assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096) == \
+        w8.Config.make(tile_n=32, waves_k=2, unroll=4, split_k=4, swap_ab=0)
+    q = tmp_path / "out.tbl"
+    w8.save_config_table(str(q))
+    text = q.read_text()
+    assert "gfx942 1 FP8_Dynamic" in text and "gfx950 9 FP8_Dynamic" in text
+
+
+def test_table_from_environment(tmp_path):
+    p = tmp_path / "env.tbl"
+    p.write_text("gfx950 1 W8A8_INT8 16 896 1024 32 2 4 8 1 0.5\n")
+    code = ("import bit_quantized_gemm_token_amd as w8;"
+            "c = w8.lookup_config('W8A8_INT8', 16, 896, 1024);"
+            "print(c.as_dict() if c else None)")
+    env = dict(os.environ, W8_CONFIG_TABLE=str(p))
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                         text=True, check=True).stdout
+    # the shipped default table is loaded at import and replaces the env table,
+    # unless there is none
+    from bit_quantized_gemm_token_amd import DEFAULT_TABLE
+    if not os.path.exists(DEFAULT_TABLE):
+        assert "'split_k': 8" in out and "'tile_n': 32" in out
+
+
+def test_env_table_loaded_by_the_c_library_alone(tmp_path):
+    p = tmp_path / "env.tbl"
+    p.write_text("gfx950 1 W8A8_INT8 16 896 1024 32 2 4 8 1 0.5\n")
+    from bit_quantized_gemm_token_amd import _capi
+    code = (
+        "import ctypes, sys\n"
+        f"sys.path.insert(0, {ROOT!r})\n"
+        "from bit_quantized_gemm_token_amd import _capi\n"
+        "lib = _capi.load()\n"
+        "c = _capi.Config()\n"
+        "print(lib.w8_lookup_config(1, 16, 896, 1024, ctypes.byref(c)), c.split_k, c.tile_n)\n")
+    env = dict(os.environ, W8_CONFIG_TABLE=str(p))
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                         check=True).stdout.split()
+    assert out == ["0", "8", "32"]

@@ -1,0 +1,214 @@
+"""GPU GEMM against the oracle.
+
+- int32 accumulators (W8A8_INT8) bit-identical to the oracle's exact sums;
+- fp32 accumulators (FP8 formats) within the fp32 summation bound of the
+  oracle's exact sums;
+- bf16 outputs of the whole path (GPU quantize + GPU GEMM, GPU-quantized
+  weights) within atol = rtol = 1e-2 of the oracle's fp64 result;
+- Standard / Split-K / Swap-AB and every tile choice give the same answer;
+- split-K is deterministic, leaves its counters at zero and survives graph
+  capture and replay.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from tests.gpu_cases import DEV, Case, assert_bf16_close, u8
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def w8():
+    import bit_quantized_gemm_token_amd as mod
+    return mod
+
+
+def C(w8, **kw):
+    return w8.Config.make(**kw)
+
+
+_cases = {}
+
+
+def case(fmt, M, N, K):
+    key = (fmt, M, N, K)
+    if key not in _cases:
+        _cases.clear()                       # keep one case resident at a time
+        _cases[key] = Case(fmt, M, N, K)
+    return _cases[key]
+
+
+def acc_check(w8, cs, xq, sx, cfg, what=""):
+    """Accumulator parity: int32 bit-exact, fp32 within the summation bound."""
+    acc = w8.gemm_w8a8_acc(cs.fmt, xq, sx, cs.wq, cs.sw, cfg=cfg)
+    torch.cuda.synchronize()
+    got = acc.cpu().numpy()
+    ref = cs.acc_ref()
+    if cs.fmt == "W8A8_INT8":
+        assert np.array_equal(got.astype(np.int64), ref), f"{what}: int32 accumulators differ"
+    else:
+        bad = np.argwhere(np.abs(got - ref) > cs.acc_bound())
+        assert bad.size == 0, f"{what}: {len(bad)} fp32 accumulators off, first {bad[:3]}"
+    return acc
+
+
+def full_path(w8, cs, cfg=None):
+    y = w8.linear(cs.fmt, cs.x, cs.wq, cs.sw, cfg=cfg)
+    torch.cuda.synchronize()
+    return y
+
+
+# -------------------------------------------------- the configurations --
+def test_int8_standard_16x896x1024(w8):
+    """W8A8_INT8, M=16, N=896, K=1024: Standard variant, split_k=1, swap_ab=0."""
+    cs = case("W8A8_INT8", 16, 896, 1024)
+    cfg = C(w8, tile_n=16, waves_k=4, unroll=2, split_k=1, swap_ab=0)
+    xq, sx = cs.gpu_act()
+    assert np.array_equal(u8(xq), cs.xq_ref)
+    acc_check(w8, cs, xq, sx, cfg, "int8 standard")
+    assert_bf16_close(full_path(w8, cs, cfg), cs.Y, "int8 standard")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 32])
+def test_fp8_dynamic_4096(w8, M):
+    """FP8_Dynamic, N=K=4096: default config, resolved (table) config and a spread of others."""
+    cs = case("FP8_Dynamic", M, 4096, 4096)
+    xq, sx = cs.gpu_act()
+    cfgs = [None, w8.default_config("FP8_Dynamic", M, 4096, 4096),
+            C(w8, tile_n=64, waves_k=2, unroll=4, split_k=4, swap_ab=0),
+            C(w8, tile_n=32, waves_k=1, unroll=1, split_k=32, swap_ab=1),
+            C(w8, tile_n=16, waves_k=8, unroll=2, split_k=1, swap_ab=1)]
+    for cfg in cfgs:
+        acc_check(w8, cs, xq, sx, cfg, f"fp8 M={M} {cfg}")
+        assert_bf16_close(full_path(w8, cs, cfg), cs.Y, f"fp8 M={M} {cfg}")
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_block_fp8_swap_on_and_off(w8, M):
+    """Block_FP8, N=4608, K=7168: swap_ab forced to 0 and 1, both against the
+    oracle and against each other."""
+    cs = case("Block_FP8", M, 4608, 7168)
+    xq, sx = cs.gpu_act()
+    assert np.array_equal(u8(xq), cs.xq_ref)
+    outs = []
+    for swap in (0, 1):
+        cfg = C(w8, tile_n=16, waves_k=4, unroll=2, split_k=2, swap_ab=swap)
+        acc_check(w8, cs, xq, sx, cfg, f"block swap={swap}")
+        y = full_path(w8, cs, cfg)
+        assert_bf16_close(y, cs.Y, f"block M={M} swap={swap}")
+        outs.append(y.float().cpu().numpy())
+    np.testing.assert_allclose(outs[0], outs[1], rtol=1e-2, atol=1e-2)
+
+
+@pytest.mark.parametrize("fmt", ["W8A8_INT8", "FP8_Dynamic"])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 32])
+def test_split_k_sweep_512x7168(w8, fmt, M):
+    """N=512, K=7168: every split_k in 1..256 against the oracle; int8
+    accumulators are bit-identical for every setting."""
+    cs = case(fmt, M, 512, 7168)
+    xq, sx = cs.gpu_act()
+    for s in [1 << i for i in range(9)]:
+        for swap in (0, 1):
+            cfg = C(w8, tile_n=16, waves_k=2, unroll=2, split_k=s, swap_ab=swap)
+            acc_check(w8, cs, xq, sx, cfg, f"{fmt} M={M} split_k={s} swap={swap}")
+            assert_bf16_close(full_path(w8, cs, cfg), cs.Y, f"{fmt} M={M} split_k={s}")
+
+
+@pytest.mark.parametrize("fmt", ["W8A8_INT8", "FP8_Dynamic", "Block_FP8"])
+def test_every_tile_config(w8, fmt):
+    """Every (tile_n, waves_k, unroll, swap_ab) instance at one ragged shape."""
+    M, N, K = (17, 200, 1280)
+    cs = case(fmt, M, N, K)
+    xq, sx = cs.gpu_act()
+    n = 0
+    for tn, wk, u, swap, s in itertools.product((16, 32, 64), (1, 2, 4, 8), (1, 2, 4), (0, 1),
+                                                (1, 4)):
+        if (tn // 16) * wk > 8:
+            continue
+        cfg = C(w8, tile_n=tn, waves_k=wk, unroll=u, split_k=s, swap_ab=swap)
+        acc_check(w8, cs, xq, sx, cfg, f"{fmt} {cfg}")
+        n += 1
+    assert n == 2 * 2 * 3 * 9
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [
+    ("W8A8_INT8", 1, 16, 16), ("W8A8_INT8", 5, 200, 208), ("W8A8_INT8", 32, 1000, 1040),
+    ("W8A8_INT8", 17, 33, 80), ("FP8_Dynamic", 1, 16, 16), ("FP8_Dynamic", 5, 200, 208),
+    ("FP8_Dynamic", 32, 1000, 1040), ("FP8_Dynamic", 31, 77, 336), ("Block_FP8", 1, 16, 128),
+    ("Block_FP8", 5, 200, 384), ("Block_FP8", 32, 1000, 1024), ("Block_FP8", 20, 130, 256)])
+def test_ragged_shapes(w8, fmt, M, N, K):
+    """Ragged M (tile padding), N (partial tile) and K (masked tail step)."""
+    cs = case(fmt, M, N, K)
+    xq, sx = cs.gpu_act()
+    assert np.array_equal(u8(xq), cs.xq_ref)
+    for cfg in (None, C(w8, tile_n=32, waves_k=2, unroll=4, split_k=8, swap_ab=0),
+                C(w8, tile_n=64, waves_k=1, unroll=1, split_k=2, swap_ab=1)):
+        acc_check(w8, cs, xq, sx, cfg, f"ragged {cfg}")
+        assert_bf16_close(full_path(w8, cs, cfg), cs.Y, f"ragged {fmt} {cfg}")
+
+
+@pytest.mark.parametrize("fmt", ["W8A8_INT8", "FP8_Dynamic", "Block_FP8"])
+@pytest.mark.parametrize("M,N,K", synthetic.SWEEP)
+def test_sweep_shapes_resolved_config(w8, fmt, M, N, K):
+    """The 24-shape sweep with the config the library resolves (table or default)."""
+    cs = case(fmt, M, N, K)
+    assert_bf16_close(full_path(w8, cs), cs.Y, f"sweep {fmt} {M}x{N}x{K}")
+
+
+# ------------------------------------------------ properties of the path --
+def test_split_k_deterministic_and_counters_reset(w8):
+    cs = case("FP8_Dynamic", 8, 1024, 4096)
+    xq, sx = cs.gpu_act()
+    cfg = C(w8, tile_n=16, waves_k=2, unroll=2, split_k=16, swap_ab=1)
+    ws = w8.Workspace(DEV)
+    need = w8.workspace_size("FP8_Dynamic", 8, 1024, 4096, cfg)
+    ys = [w8.gemm_w8a8("FP8_Dynamic", xq, sx, cs.wq, cs.sw, cfg=cfg, workspace=ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+    ntiles = 1024 // 16
+    assert need > ntiles * 4
+    assert (ws.buf[:ntiles * 4].cpu() == 0).all()
+
+
+def test_unsupported_m_raises(w8):
+    x = torch.zeros((33, 256), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(w8.UnsupportedShape):
+        w8.quantize_act("FP8_Dynamic", x)
+    xq = torch.zeros((33, 256), dtype=torch.uint8, device=DEV)
+    wq = torch.zeros((64, 256), dtype=torch.uint8, device=DEV)
+    with pytest.raises(w8.UnsupportedShape):
+        w8.gemm_w8a8("FP8_Dynamic", xq, torch.ones(33, device=DEV), wq, torch.ones(64, device=DEV))
+
+
+def test_graph_capture_replay(w8):
+    """quantize + GEMM (split-K) captured once, replayed with eager work in
+    between; every replay equals the eager result bit for bit."""
+    cs = case("Block_FP8", 8, 4608, 7168)
+    cfg = C(w8, tile_n=16, waves_k=4, unroll=2, split_k=8, swap_ab=1)
+    ws = w8.Workspace(DEV, w8.workspace_size("Block_FP8", 8, 4608, 7168, cfg))
+    eager = w8.linear("Block_FP8", cs.x, cs.wq, cs.sw, cfg=cfg, workspace=ws).clone()
+    x_static = cs.x.clone()
+    y_static = torch.empty_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        w8.linear("Block_FP8", x_static, cs.wq, cs.sw, cfg=cfg, y=y_static, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w8.linear("Block_FP8", x_static, cs.wq, cs.sw, cfg=cfg, y=y_static, workspace=ws)
+    for i in range(4):
+        y_static.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_static.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+        junk = torch.randn(1024, 1024, device=DEV) @ torch.randn(1024, 1024, device=DEV)
+        del junk
+    assert_bf16_close(y_static, cs.Y, "graph replay")

@@ -1,0 +1,60 @@
+"""The ahead-of-time tuner on the GPU: its winner is a valid, validated config
+that is no slower than the default on the second timing bank, it lands in the
+config table, survives a save/load round trip and is what the GEMM resolves;
+an injected validation failure removes a candidate."""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_cases import Case, assert_bf16_close
+
+pytestmark = pytest.mark.gpu
+
+SMALL = dict(warmup=1, replays=3, bank2_top=3, rotate_bytes=64 << 20, max_split_k=8)
+
+
+@pytest.fixture(scope="module")
+def w8():
+    import bit_quantized_gemm_token_amd as mod
+    return mod
+
+
+@pytest.fixture(autouse=True)
+def _restore_table(w8):
+    yield
+    w8.clear_config_table()
+    w8.load_default_table()
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [("W8A8_INT8", 16, 896, 1024), ("FP8_Dynamic", 4, 512, 2048),
+                                       ("Block_FP8", 8, 512, 1024)])
+def test_tune_shape(w8, fmt, M, N, K, tmp_path):
+    print(f"[tune] {fmt} M={M} N={N} K={K}", flush=True)
+    w8.clear_config_table()
+    best, st = w8.tune_shape(fmt, M, N, K, **SMALL)
+    print(f"[tune] best {best} stats {st}", flush=True)
+    w8.validate_config(fmt, M, N, K, best)
+    assert st["candidates"] > 50 and st["validated"] == st["candidates"] and st["rejected"] == 0
+    assert best.split_k <= 8
+    assert st["best_us_bank2"] > 0 and st["best_gbps"] > 0
+    assert st["best_us_bank2"] <= st["default_us_bank2"] * 1.10
+    assert w8.lookup_config(fmt, M, N, K) == best
+    cfg, hit = w8.resolve_config(fmt, M, N, K)
+    assert hit and cfg == best
+    p = tmp_path / "tuned.tbl"
+    w8.save_config_table(str(p))
+    w8.clear_config_table()
+    w8.load_config_table(str(p))
+    assert w8.lookup_config(fmt, M, N, K) == best
+    cs = Case(fmt, M, N, K)
+    y = w8.linear(fmt, cs.x, cs.wq, cs.sw)            # resolves the tuned entry
+    torch.cuda.synchronize()
+    assert_bf16_close(y, cs.Y, f"tuned {fmt}")
+
+
+def test_tune_rejects_injected_failure(w8):
+    w8.clear_config_table()
+    best, st = w8.tune_shape("W8A8_INT8", 4, 256, 512, insert=False, fail_candidate=0, **SMALL)
+    assert st["rejected"] == 1 and st["validated"] == st["candidates"] - 1
+    assert st["best_index"] != 0
+    assert w8.config_table_size() == 0                # insert=False
