@@ -296,7 +296,7 @@ def load_default_table():
 
 
 # -------------------------------------------------------------------- tuner --
-def tune_shape(fmt, M, N, K, warmup=3, replays=10, bank2_top=6, rotate_bytes=1 << 30,
+def tune_shape(fmt, M, N, K, warmup=2, replays=5, bank2_top=5, rotate_bytes=512 << 20,
                max_split_k=MAX_SPLIT_K, insert=True, fail_candidate=-1):
     """Ahead-of-time tuning of one shape on the current device.
 

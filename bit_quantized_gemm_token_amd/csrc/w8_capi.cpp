@@ -20,12 +20,14 @@ constexpr int kMaxK = 1 << 22;
 constexpr int kMaxN = 1 << 24;
 
 int wn_index(int wn) { return wn == 1 ? 0 : wn == 2 ? 1 : wn == 4 ? 2 : -1; }
-int wk_index(int wk) { return wk == 1 ? 0 : wk == 2 ? 1 : wk == 4 ? 2 : wk == 8 ? 3 : -1; }
+int wk_index(int wk) {
+  return wk == 1 ? 0 : wk == 2 ? 1 : wk == 4 ? 2 : wk == 8 ? 3 : wk == 16 ? 4 : -1;
+}
 int u_index(int u) { return u == 1 ? 0 : u == 2 ? 1 : u == 4 ? 2 : -1; }
 
 // [fmt][mb-1][wn][wk][unroll][swap] -> launcher
 struct InstanceIndex {
-  GemmLaunchFn fn[3][2][3][4][3][2] = {};
+  GemmLaunchFn fn[3][2][3][5][3][2] = {};
   InstanceIndex() {
     int n = 0;
     const GemmInstance* p = gemm_instances(&n);
@@ -96,8 +98,8 @@ w8_status check_cfg(int fmt, int M, int N, int K, const w8_cfg& c) {
   if (c.reserved[0] || c.reserved[1]) return fail(W8_E_INVALID, "cfg.reserved must be zero");
   if (c.tile_n != 16 && c.tile_n != 32 && c.tile_n != 64)
     return fail(W8_E_INVALID, "cfg.tile_n must be 16, 32 or 64");
-  if (wk_index(c.waves_k) < 0) return fail(W8_E_INVALID, "cfg.waves_k must be 1, 2, 4 or 8");
-  if ((c.tile_n / 16) * c.waves_k > 8) return fail(W8_E_INVALID, "cfg: tile_n/16 * waves_k > 8");
+  if (wk_index(c.waves_k) < 0) return fail(W8_E_INVALID, "cfg.waves_k must be 1, 2, 4, 8 or 16");
+  if ((c.tile_n / 16) * c.waves_k > 16) return fail(W8_E_INVALID, "cfg: tile_n/16 * waves_k > 16");
   if (u_index(c.unroll) < 0) return fail(W8_E_INVALID, "cfg.unroll must be 1, 2 or 4");
   if (!is_pow2(c.split_k) || c.split_k > W8_MAX_SPLIT_K)
     return fail(W8_E_INVALID, "cfg.split_k must be a power of two in [1, 256], got " +

@@ -35,6 +35,8 @@
 // tile) read a clamped valid row; their outputs are never stored.  A ragged
 // K tail (K % KSTEP != 0, K % 16 == 0) is one masked K-step.
 #pragma once
+#include <type_traits>
+
 #include "w8_device.hpp"
 #include "w8_launch.hpp"
 
@@ -121,18 +123,34 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(GemmArgs a) {
   for (int b = 0; b < MB; ++b) xrow[b] = a.xq + (long long)min(16 * b + r, a.M - 1) * a.ldq + 16 * g;
 
   // Block_FP8 scale pointers for this lane: sw row of the 128-row block, and
-  // the sx rows of the accumulator elements the lane holds.
+  // the sx rows of the accumulator elements the lane holds (SWAP: one m per
+  // lane; standard: four).
+  constexpr int SXN = SWAP ? 1 : 4;
   const float* swrow = nullptr;
-  const float* sxrow[MB][4];
+  const float* sxrow[MB][SXN];
   if constexpr (BLOCK) {
     swrow = a.sw + (long long)(min(n0, a.N - 1) / kGroup) * a.sgroups;
 #pragma unroll
     for (int b = 0; b < MB; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < SXN; ++i) {
         const int m = SWAP ? 16 * b + r : 16 * b + 4 * g + i;
         sxrow[b][i] = a.sx + (long long)min(m, a.M - 1) * a.sgroups;
       }
+  }
+
+  // Epilogue scales of the per-token formats, loaded now so their latency
+  // hides under the K loop instead of adding a round trip at the end.
+  float ep_sx[MB][SXN], ep_sw[4 / SXN];
+  if constexpr (!BLOCK) {
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int i = 0; i < SXN; ++i)
+        ep_sx[b][i] = a.sx[min(SWAP ? 16 * b + r : 16 * b + 4 * g + i, a.M - 1)];
+#pragma unroll
+    for (int i = 0; i < 4 / SXN; ++i)
+      ep_sw[i] = a.sw[min(SWAP ? n0 + 4 * g + i : n0 + r, a.N - 1)];
   }
 
   // K-steps of this split, then of this wave.
@@ -147,75 +165,92 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int b = 0; b < MB; ++b) acc[b] = Acc{0, 0, 0, 0};
 
-  // One K-step: MFMA, and for Block_FP8 the group rescale.
-  auto step = [&](const Frag& wf, const Frag (&xf)[MB], int kk) {
-    if constexpr (BLOCK) {
-      const float swv = swrow[kk];
-#pragma unroll
-      for (int b = 0; b < MB; ++b) {
-        const Acc p = mma<FMT, SWAP>(wf, xf[b], Acc{0, 0, 0, 0});
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[b][i] += p[i] * (sxrow[b][i][kk] * swv);
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < MB; ++b) acc[b] = mma<FMT, SWAP>(wf, xf[b], acc[b]);
-    }
+  // A stage is U consecutive K-steps.  The wave's full K-steps [la, lfull)
+  // are covered by ns whole stages ending at lfull; the first stage may
+  // start before la, and its steps below la load a clamped (valid) address
+  // and are zeroed before their MFMA, so every load of a stage is issued at
+  // once and no K-step is ever processed alone.
+  struct Stage {
+    Frag w[U];
+    Frag x[U][MB];
+    float sw[BLOCK ? U : 1];
+    float sx[BLOCK ? U : 1][MB][SXN];
   };
-
-  // Main loop: stages of U K-steps, ping-ponged between two register sets so
-  // that the next stage's loads are in flight while the current one feeds
-  // the MFMAs (loads inside the loop are unconditional, which lets the
-  // compiler wait only for the stage it is about to use).
-  auto load_stage = [&](Frag (&w)[U], Frag (&x)[U][MB], int k0) {
+  auto load_stage = [&](Stage& st, int k0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      w[u] = load_frag<FMT>(wrow, k0 + u);
+      const int k = max(k0 + u, la);
+      st.w[u] = load_frag<FMT>(wrow, k);
 #pragma unroll
-      for (int b = 0; b < MB; ++b) x[u][b] = load_frag<FMT>(xrow[b], k0 + u);
+      for (int b = 0; b < MB; ++b) st.x[u][b] = load_frag<FMT>(xrow[b], k);
+      if constexpr (BLOCK) {
+        st.sw[u] = swrow[k];
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+          for (int i = 0; i < SXN; ++i) st.sx[u][b][i] = sxrow[b][i][k];
+      }
     }
   };
-  auto run_stage = [&](const Frag (&w)[U], const Frag (&x)[U][MB], int k0) {
+  // MASK: the first stage, whose steps below la are zeroed.
+  auto run_stage = [&](const Stage& st, int k0, auto mask) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) step(w[u], x[u], k0 + u);
+    for (int u = 0; u < U; ++u) {
+      const Frag zero = {};
+      const Frag w = (decltype(mask)::value && k0 + u < la) ? zero : st.w[u];
+      if constexpr (BLOCK) {
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+          const Acc p = mma<FMT, SWAP>(w, st.x[u][b], Acc{0, 0, 0, 0});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[b][i] += p[i] * (st.sx[u][b][SWAP ? 0 : i] * st.sw[u]);
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < MB; ++b) acc[b] = mma<FMT, SWAP>(w, st.x[u][b], acc[b]);
+      }
+    }
   };
+  const std::true_type masked;
+  const std::false_type whole;
 
-  int kk = la;
-  const int nit = max(lfull - la, 0) / U;
-  if (nit > 0) {
-    Frag wA[U], xA[U][MB], wB[U], xB[U][MB];
-    load_stage(wA, xA, kk);
-    int it = 0;
-    for (; it + 2 < nit; it += 2) {
-      load_stage(wB, xB, kk + U);
-      run_stage(wA, xA, kk);
-      load_stage(wA, xA, kk + 2 * U);
-      run_stage(wB, xB, kk + U);
-      kk += 2 * U;
-    }
-    if (nit - it == 2) {
-      load_stage(wB, xB, kk + U);
-      run_stage(wA, xA, kk);
-      run_stage(wB, xB, kk + U);
-      kk += 2 * U;
+  // Stages alternate between register sets A and B: the loads of stage s+1
+  // are issued before stage s feeds the MFMAs.
+  const int ns = (max(lfull - la, 0) + U - 1) / U;
+  if (ns > 0) {
+    const int k0 = lfull - ns * U;
+    Stage A, B;
+    load_stage(A, k0);
+    if (ns == 1) {
+      run_stage(A, k0, masked);
     } else {
-      run_stage(wA, xA, kk);
-      kk += U;
+      load_stage(B, k0 + U);
+      run_stage(A, k0, masked);
+      int s = 1;  // B holds stage s
+      for (; s + 2 <= ns - 1; s += 2) {
+        load_stage(A, k0 + (s + 1) * U);
+        run_stage(B, k0 + s * U, whole);
+        load_stage(B, k0 + (s + 2) * U);
+        run_stage(A, k0 + (s + 1) * U, whole);
+      }
+      if (s + 1 <= ns - 1) {
+        load_stage(A, k0 + (s + 1) * U);
+        run_stage(B, k0 + s * U, whole);
+        run_stage(A, k0 + (s + 1) * U, whole);
+      } else {
+        run_stage(B, k0 + s * U, whole);
+      }
     }
   }
-  for (; kk < lfull; ++kk) {
-    Frag xs[MB];
-    const Frag ws = load_frag<FMT>(wrow, kk);
-#pragma unroll
-    for (int b = 0; b < MB; ++b) xs[b] = load_frag<FMT>(xrow[b], kk);
-    step(ws, xs, kk);
-  }
-  if (lb > a.kfull && la < lb) {  // the ragged K tail belongs to this wave
+  // The ragged K tail (K % KSTEP != 0; never for Block_FP8, whose K is a
+  // multiple of its 128-byte K-step) belongs to the wave that owns step kfull.
+  if (!BLOCK && lb > a.kfull && la < lb) {
     Frag xs[MB];
     const Frag ws = load_frag_tail<FMT>(wrow, a.kfull, 16 * g, a.K);
 #pragma unroll
     for (int b = 0; b < MB; ++b) xs[b] = load_frag_tail<FMT>(xrow[b], a.kfull, 16 * g, a.K);
-    step(ws, xs, a.kfull);
+#pragma unroll
+    for (int b = 0; b < MB; ++b) acc[b] = mma<FMT, SWAP>(ws, xs[b], acc[b]);
   }
 
   // Sum the WK waves of each wn through LDS, in wave order.
@@ -234,31 +269,52 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(GemmArgs a) {
   }
 
   // Split-K: publish the partial; the last workgroup of the tile reduces.
+  // Protocol (no L2 writeback or invalidate): the partials are written with
+  // agent-scope atomic stores, which write through this XCD's L2 to the
+  // device-coherent level; s_waitcnt waits until every one of them is
+  // acknowledged before the workgroup counts itself in; the last workgroup
+  // to arrive reads the partials with agent-scope atomic loads, which are
+  // served from the device-coherent level, so it sees every split's data.
+  // Partial layout: fragment f = ((tile*S + split)*WN + wn)*MB + b holds
+  // 4 x 64 words, word (f*4 + i)*64 + lane, so each of the four stores of a
+  // wave writes 256 contiguous bytes.
   if (a.split_k > 1) {
-    Acc* part = reinterpret_cast<Acc*>(a.part);
-    const long long frag = (long long)tile * a.split_k;
+    typedef decltype(acc[0][0]) Elem;
+    typedef typename std::remove_cv<typename std::remove_reference<Elem>::type>::type Word;
+    Word* part = reinterpret_cast<Word*>(a.part);
+    const long long frag0 = (long long)tile * a.split_k;
     if (wk == 0) {
 #pragma unroll
-      for (int b = 0; b < MB; ++b) part[(((frag + split) * WN + wn) * MB + b) * 64 + lane] = acc[b];
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __hip_atomic_store(part + ((((frag0 + split) * WN + wn) * MB + b) * 4 + i) * 64 + lane,
+                             acc[b][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     __shared__ int is_last;
     if (threadIdx.x == 0) {
-      const unsigned prev = atomicAdd(&a.counters[tile], 1u);
+      const unsigned prev = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
       is_last = (prev == (unsigned)(a.split_k - 1));
     }
     __syncthreads();
     if (!is_last) return;
-    __threadfence();
     if (wk == 0) {
 #pragma unroll
       for (int b = 0; b < MB; ++b) acc[b] = Acc{0, 0, 0, 0};
       for (int s = 0; s < a.split_k; ++s)
 #pragma unroll
-        for (int b = 0; b < MB; ++b) acc[b] += part[(((frag + s) * WN + wn) * MB + b) * 64 + lane];
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[b][i] += __hip_atomic_load(
+                part + ((((frag0 + s) * WN + wn) * MB + b) * 4 + i) * 64 + lane, __ATOMIC_RELAXED,
+                __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (threadIdx.x == 0) atomicExch(&a.counters[tile], 0u);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   if (wk != 0) return;
@@ -279,12 +335,15 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(GemmArgs a) {
             reinterpret_cast<float*>(a.out)[o] = acc[b][i];
         } else {
           float y;
-          if constexpr (FMT == W8A8_INT8)
-            y = (float)acc[b][i] * a.sx[m] * a.sw[n];
-          else if constexpr (FMT == FP8_DYNAMIC)
-            y = acc[b][i] * a.sx[m] * a.sw[n];
-          else
+          if constexpr (BLOCK) {
             y = acc[b][i];
+          } else {
+            const float sxm = ep_sx[b][SWAP ? 0 : i], swn = ep_sw[SWAP ? i : 0];
+            if constexpr (FMT == W8A8_INT8)
+              y = (float)acc[b][i] * sxm * swn;
+            else
+              y = acc[b][i] * sxm * swn;
+          }
           reinterpret_cast<uint16_t*>(a.out)[o] = bf16_rne(y);
         }
       }

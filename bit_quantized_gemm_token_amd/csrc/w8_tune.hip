@@ -107,10 +107,10 @@ extern "C" void w8_tune_default_opts(w8_tune_opts* o) {
   if (!o) return;
   std::memset(o, 0, sizeof *o);
   o->abi_version = W8_ABI_VERSION;
-  o->warmup = 3;
-  o->replays = 10;
-  o->bank2_top = 6;
-  o->rotate_bytes = (int64_t)1 << 30;
+  o->warmup = 2;
+  o->replays = 5;
+  o->bank2_top = 5;
+  o->rotate_bytes = (int64_t)512 << 20;
   o->max_split_k = W8_MAX_SPLIT_K;
   o->insert = 1;
   o->fail_candidate = -1;
@@ -144,16 +144,24 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   const size_t nsx = block ? (size_t)M * G : (size_t)M;
   const size_t nsw = block ? (size_t)((N + 127) / 128) * G : (size_t)N;
 
-  // Candidates: every config of the family (with split_k up to max_split_k),
-  // minus those that cannot pay off: split_k above the number of K-steps
-  // (only empty splits added) and split-K partial traffic above twice the
-  // weight bytes.
+  // Candidates: every config of the family with split_k up to max_split_k,
+  // minus those that cannot pay off or cannot differ from another one:
+  //   - split_k above the number of K-steps (only empty splits added);
+  //   - unroll above the K-steps each wave owns (the loop would never run a
+  //     full stage, so the candidate equals the one with a smaller unroll);
+  //   - split-K partial traffic above twice the weight bytes;
+  //   - fewer waves in total than min(256, the most any candidate has): a
+  //     stream this narrow leaves most of the 256 compute units idle.
   std::vector<Cand> cands;
   const int T = ksteps_of(fmt, K);
   const int tiles_n[] = {16, 32, 64};
-  const int waves[] = {1, 2, 4, 8};
+  const int waves[] = {1, 2, 4, 8, 16};
   const int unrolls[] = {1, 2, 4};
-  size_t max_ws = 0;
+  auto total_waves = [&](const w8_cfg& c) {
+    return (long long)((N + c.tile_n - 1) / c.tile_n) * (c.tile_n / 16) * c.waves_k * c.split_k;
+  };
+  std::vector<w8_cfg> all;
+  long long most_waves = 0;
   for (int tn : tiles_n)
     for (int wk : waves)
       for (int u : unrolls)
@@ -169,14 +177,22 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
             c.swap_ab = sw;
             if (check_cfg(fmt, M, N, K, c) != W8_OK) continue;
             if (s > T) continue;
-            const size_t wsb = workspace_bytes(fmt, M, N, c);
-            if (wsb > 2 * wbytes + 65536) continue;
-            max_ws = std::max(max_ws, wsb);
-            Cand cd;
-            cd.cfg = c;
-            cd.index = (int)cands.size();
-            cands.push_back(cd);
+            if (u > 1 && T / (s * wk) < u) continue;
+            if (workspace_bytes(fmt, M, N, c) > 2 * wbytes + 65536 + (size_t)kSplitKMaxTiles * 4)
+              continue;
+            all.push_back(c);
+            most_waves = std::max(most_waves, total_waves(c));
           }
+  const long long min_waves = std::min<long long>(256, most_waves);
+  size_t max_ws = 0;
+  for (const w8_cfg& c : all) {
+    if (total_waves(c) < min_waves) continue;
+    max_ws = std::max(max_ws, workspace_bytes(fmt, M, N, c));
+    Cand cd;
+    cd.cfg = c;
+    cd.index = (int)cands.size();
+    cands.push_back(cd);
+  }
   const w8_cfg dflt = make_default_cfg(fmt, M, N, K);
   max_ws = std::max(max_ws, workspace_bytes(fmt, M, N, dflt));
 

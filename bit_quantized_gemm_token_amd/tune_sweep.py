@@ -1,0 +1,84 @@
+"""Ahead-of-time tuning of a list of shapes into a config table file.
+
+    python -m bit_quantized_gemm_token_amd.tune_sweep --out TABLE [--formats ...]
+           [--shapes M,N,K;M,N,K...] [--no-resume] [--max-split-k 256]
+
+Default shapes: the 24-shape M <= 32 sweep of synthetic.SWEEP plus the shapes
+the tests and benchmarks name (N=K=4096 at M in {1, 4, 16, 32}; N=4608,
+K=7168 at M in {1, 8, 32}; N=512, K=7168 at M in {1, 2, 4, 8, 16, 32};
+16 x 896 x 1024).
+
+Tuning is the expensive offline step the page describes (ai-radar.it,
+"Helion nel backend vLLM", paragraph 6: ahead-of-time tuning can take hours
+and its config files must be managed), so this tool is resumable: entries
+already in TABLE for this arch and ABI are kept and skipped, and the table is
+rewritten (write-then-rename, by the library) after every tuned shape.
+"""
+import argparse
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+EXTRA_SHAPES = ((1, 4096, 4096), (4, 4096, 4096), (16, 4096, 4096), (32, 4096, 4096),
+                (1, 4608, 7168), (8, 4608, 7168), (32, 4608, 7168),
+                (1, 512, 7168), (2, 512, 7168), (4, 512, 7168), (8, 512, 7168),
+                (16, 512, 7168), (32, 512, 7168), (16, 896, 1024))
+
+
+def default_shapes():
+    sys.path.insert(0, ROOT)
+    from synthetic import SWEEP
+    out = []
+    for s in tuple(SWEEP) + EXTRA_SHAPES:
+        if s not in out:
+            out.append(s)
+    return out
+
+
+def main(argv=None):
+    import bit_quantized_gemm_token_amd as w8
+    p = argparse.ArgumentParser()
+    p.add_argument("--out", required=True)
+    p.add_argument("--formats", default="FP8_Dynamic,W8A8_INT8,Block_FP8")
+    p.add_argument("--shapes", default=None)
+    p.add_argument("--no-resume", action="store_true")
+    p.add_argument("--max-split-k", type=int, default=w8.MAX_SPLIT_K)
+    p.add_argument("--rotate-mib", type=int, default=512)
+    p.add_argument("--replays", type=int, default=5)
+    p.add_argument("--time-budget-s", type=float, default=0.0,
+                   help="stop starting new shapes after this many seconds (0 = no limit)")
+    a = p.parse_args(argv)
+    if a.shapes:
+        shapes = [tuple(int(v) for v in s.split(",")) for s in a.shapes.split(";") if s]
+    else:
+        shapes = default_shapes()
+    w8.clear_config_table()
+    if not a.no_resume and os.path.exists(a.out):
+        w8.load_config_table(a.out)
+    t0 = time.time()
+    done = skipped = 0
+    for fmt in a.formats.split(","):
+        for (M, N, K) in shapes:
+            if w8.lookup_config(fmt, M, N, K) is not None:
+                skipped += 1
+                continue
+            if a.time_budget_s and time.time() - t0 > a.time_budget_s:
+                print(f"[tune] time budget reached after {done} shapes", flush=True)
+                print(f"[tune] tuned {done}, kept {skipped}, table {a.out}", flush=True)
+                return 0
+            best, st = w8.tune_shape(fmt, M, N, K, rotate_bytes=a.rotate_mib << 20,
+                                     replays=a.replays, max_split_k=a.max_split_k, insert=True)
+            w8.save_config_table(a.out)
+            done += 1
+            print(f"[tune] {fmt} {M}x{N}x{K}: {best} {st['best_us_bank2']:.3f} us "
+                  f"({st['best_gbps']:.0f} GB/s; default {st['default_us_bank2']:.3f} us; "
+                  f"{st['validated']}/{st['candidates']} validated; {st['tune_seconds']:.1f} s)",
+                  flush=True)
+    print(f"[tune] tuned {done}, kept {skipped}, table {a.out}", flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

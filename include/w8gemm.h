@@ -88,7 +88,8 @@ typedef enum {
  * the algorithmic variants are parameters, not separate kernels).
  *   tile_n   output columns (= weight rows) per workgroup: 16, 32 or 64.
  *   waves_k  wavefronts inside one workgroup that split its K range and are
- *            reduced through LDS: 1, 2, 4 or 8 (tile_n/16 * waves_k <= 8).
+ *            reduced through LDS: 1, 2, 4, 8 or 16 (tile_n/16 * waves_k
+ *            <= 16, i.e. at most 1024 threads).
  *   unroll   MFMA K-steps each wave keeps in flight per loop iteration:
  *            1, 2 or 4.
  *   split_k  workgroups splitting K, reduced in fixed order by the last one
@@ -109,11 +110,11 @@ typedef struct {
 /* Options of the ahead-of-time tuner (paragraph 3 and 6 of the page). */
 typedef struct {
     int32_t abi_version;      /* W8_ABI_VERSION */
-    int32_t warmup;           /* untimed graph replays per candidate (default 3) */
-    int32_t replays;          /* timed graph replays per candidate and bank (default 10) */
-    int32_t bank2_top;        /* best bank-1 candidates re-timed on bank 2 (default 6) */
+    int32_t warmup;           /* untimed graph replays per candidate (default 2) */
+    int32_t replays;          /* timed graph replays per candidate and bank (default 5) */
+    int32_t bank2_top;        /* best bank-1 candidates re-timed on bank 2 (default 5) */
     int64_t rotate_bytes;     /* weight bytes cycled through per graph, >= the last-level
-                                 cache so reads come from HBM (default 1 GiB) */
+                                 cache so reads come from HBM (default 512 MiB) */
     int32_t max_split_k;      /* largest split_k tried (default 256) */
     int32_t insert;           /* 1: insert the winner into the config table */
     int32_t fail_candidate;   /* test hook: candidate with this index fails validation
@@ -245,14 +246,17 @@ w8_status w8_lookup_config(w8_fmt fmt, int M, int N, int K, w8_cfg *out);
 /* ------------------------------------------------------------------ tuner -- */
 /* Ahead-of-time per-shape tuner (paragraph 3 of the page: the autotuner
  * compares configurations and keeps the best for each shape).  Allocates its
- * own inputs (random codes and scales), enumerates every feasible config
+ * own inputs (random codes and scales), enumerates the configs of the family
  * (tile_n x waves_k x unroll x split_k in {1, 2, ..., max_split_k} x
- * swap_ab), checks each against the default config's output (bit-equal for
- * W8A8_INT8, within 1e-2 relative for the FP8 formats) and times it as HIP
- * graph replays over rotating weight copies; the best on timing bank 1 is
- * re-timed with the runners-up on bank 2, and the bank-2 winner is returned
- * (and inserted into the table when opts->insert).  opts NULL = defaults.
- * Synchronizes the device; not callable during stream capture.            */
+ * swap_ab) minus those that cannot pay off or duplicate another (split_k
+ * above the K-steps, unroll above the K-steps per wave, partials above twice
+ * the weight bytes, fewer than min(256, most possible) waves), checks each
+ * against the default config's output (bit-equal for W8A8_INT8, within 1e-2
+ * relative for the FP8 formats) and times it as HIP graph replays over
+ * rotating weight copies; the best on timing bank 1 are re-timed on bank 2,
+ * and the bank-2 winner is returned (and inserted into the table when
+ * opts->insert).  opts NULL = defaults.  Synchronizes the device; not
+ * callable during stream capture.                                          */
 w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tune_opts *opts,
                         w8_cfg *best, w8_tune_stats *stats);
 void w8_tune_default_opts(w8_tune_opts *opts);

@@ -126,14 +126,14 @@ def test_every_tile_config(w8, fmt):
     cs = case(fmt, M, N, K)
     xq, sx = cs.gpu_act()
     n = 0
-    for tn, wk, u, swap, s in itertools.product((16, 32, 64), (1, 2, 4, 8), (1, 2, 4), (0, 1),
-                                                (1, 4)):
-        if (tn // 16) * wk > 8:
+    for tn, wk, u, swap, s in itertools.product((16, 32, 64), (1, 2, 4, 8, 16), (1, 2, 4),
+                                                (0, 1), (1, 4)):
+        if (tn // 16) * wk > 16:
             continue
         cfg = C(w8, tile_n=tn, waves_k=wk, unroll=u, split_k=s, swap_ab=swap)
         acc_check(w8, cs, xq, sx, cfg, f"{fmt} {cfg}")
         n += 1
-    assert n == 2 * 2 * 3 * 9
+    assert n == 2 * 2 * 3 * 12
 
 
 @pytest.mark.parametrize("fmt,M,N,K", [
