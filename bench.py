@@ -66,7 +66,9 @@ def log(*a):
 class Problem:
     def __init__(self, w8, fmt, M, N, K, rotate_bytes, dev):
         self.fmt, self.M, self.N, self.K = fmt, M, N, K
-        self.cfg, self.from_table = w8.resolve_config(fmt, M, N, K)
+        # the weight layout the table times best for this shape (row-major if none)
+        self.packed = w8.best_layout(fmt, M, N, K)
+        self.cfg, self.from_table = w8.resolve_config(fmt, M, N, K, packed=self.packed)
         self.bytes = w8.algorithmic_bytes(fmt, M, N, K)
         x_bits = synthetic.activations(fmt, M, N, K)
         self.x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -79,28 +81,35 @@ class Problem:
             wq, self.sw = w8.quantize_weight(fmt, w)
             del w
         self.R = max(2, math.ceil(rotate_bytes / (N * K)))
-        self.pool = torch.empty((self.R, N, K), dtype=wq.dtype, device=dev)
-        self.pool.copy_(wq.unsqueeze(0).expand(self.R, N, K))
-        self.wq = self.pool[0]
+        if self.packed:
+            pk = w8.pack_weight(fmt, wq)
+            self.pool = torch.empty((self.R, pk.data.numel()), dtype=torch.uint8, device=dev)
+            self.pool.copy_(pk.data.unsqueeze(0).expand(self.R, -1))
+            self.weights = [w8.PackedWeight(fmt, N, K, self.pool[r]) for r in range(self.R)]
+        else:
+            self.pool = torch.empty((self.R, N, K), dtype=wq.dtype, device=dev)
+            self.pool.copy_(wq.unsqueeze(0).expand(self.R, N, K))
+            self.weights = [self.pool[r] for r in range(self.R)]
+        self.wq = self.weights[0]
         self.xq, self.sx = w8.quantize_act(fmt, self.x)
         self.y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         self.ws = w8.Workspace(dev, max(w8.workspace_size(fmt, M, N, K, self.cfg), 256))
         mb = (M + 15) // 16
         c = self.cfg
         self.kernel = (f"gemm_kernel<{w8.FORMATS[fmt]}, {mb}, {c.tile_n // 16}, {c.waves_k}, "
-                       f"{c.unroll}, {c.swap_ab}>")
+                       f"{c.unroll}, {c.swap_ab}, {int(self.packed)}>")
 
     def capture(self, w8, stream):
         self.g_gemm = torch.cuda.CUDAGraph()
         self.g_path = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.g_gemm, stream=stream):
             for r in range(self.R):
-                w8.gemm_w8a8(self.fmt, self.xq, self.sx, self.pool[r], self.sw, cfg=self.cfg,
+                w8.gemm_w8a8(self.fmt, self.xq, self.sx, self.weights[r], self.sw, cfg=self.cfg,
                              y=self.y, workspace=self.ws)
         with torch.cuda.graph(self.g_path, stream=stream):
             for r in range(self.R):
                 xq, sx = w8.quantize_act(self.fmt, self.x, xq=self.xq, sx=self.sx)
-                w8.gemm_w8a8(self.fmt, xq, sx, self.pool[r], self.sw, cfg=self.cfg, y=self.y,
+                w8.gemm_w8a8(self.fmt, xq, sx, self.weights[r], self.sw, cfg=self.cfg, y=self.y,
                              workspace=self.ws)
 
 
@@ -267,7 +276,8 @@ def main():
                                "= 72 GEMMs, per-shape table configs, HIP graph replay over "
                                f"{args.rotate_mib} MiB of rotating weights per problem",
                    "problems": len(problems),
-                   "table_hits": sum(p.from_table for p in problems)},
+                   "table_hits": sum(p.from_table for p in problems),
+                   "packed_layout": sum(bool(p.packed) for p in problems)},
         "geomean_us_per_gemm": round(geomean([p.us_gemm for p in problems]), 4),
         "geomean_us_quant_plus_gemm": round(geomean([p.us_path for p in problems]), 4),
         "geomean_gbps_quant_plus_gemm": round(geomean([p.gbps_path for p in problems]), 2),
@@ -279,6 +289,7 @@ def main():
     }
     if args.report:
         rows = [{"fmt": p.fmt, "M": p.M, "N": p.N, "K": p.K, "cfg": p.cfg.as_dict(),
+                 "layout": "packed" if p.packed else "row",
                  "from_table": p.from_table, "R": p.R, "bytes": p.bytes,
                  "us_gemm": round(p.us_gemm, 4), "us_gemm_min": round(p.us_gemm_min, 4),
                  "us_gemm_p90": round(p.us_gemm_p90, 4), "us_quant_plus_gemm": round(p.us_path, 4),

@@ -27,8 +27,9 @@ _lib = _capi.load()
 LIB_PATH = _capi.LIB_PATH
 DEFAULT_TABLE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "configs", "gfx950.tbl")
 
-__all__ = ["Config", "W8Error", "UnsupportedShape", "Workspace", "quantize_act",
-           "quantize_weight", "gemm_w8a8", "gemm_w8a8_acc", "linear", "workspace_size",
+__all__ = ["Config", "W8Error", "UnsupportedShape", "Workspace", "PackedWeight", "quantize_act",
+           "quantize_weight", "pack_weight", "gemm_w8a8", "gemm_w8a8_acc", "linear",
+           "workspace_size",
            "validate_config", "default_config", "resolve_config", "lookup_config",
            "set_config", "load_config_table", "save_config_table", "clear_config_table",
            "config_table_size", "config_table_foreign", "tune_shape", "FORMATS", "MAX_M",
@@ -137,10 +138,42 @@ def quantize_weight(fmt, w, wq=None, sw=None, stream=None):
     return wq, sw
 
 
-# --------------------------------------------------------------------- GEMM --
-def workspace_size(fmt, M, N, K, cfg=None):
+# ------------------------------------------------------------- weight layout --
+class PackedWeight:
+    """Weight codes in the GEMM's packed (MFMA-native) layout.
+
+    Produced by pack_weight(); pass it to gemm_w8a8() in place of the
+    row-major [N, K] code tensor.  `data` is the 1-D uint8 device buffer.
+    """
+
+    def __init__(self, fmt, N, K, data):
+        self.fmt, self.N, self.K, self.data = _fmt(fmt), int(N), int(K), data
+        self.shape = (self.N, self.K)
+        self.device = data.device
+
+
+def packed_weight_size(fmt, N, K):
     n = ctypes.c_size_t(0)
-    _check(_lib.w8_workspace_size(_fmt(fmt), M, N, K, _cfg_ptr(cfg), ctypes.byref(n)))
+    _check(_lib.w8_packed_weight_size(_fmt(fmt), N, K, ctypes.byref(n)))
+    return n.value
+
+
+def pack_weight(fmt, wq, stream=None):
+    """Pack row-major codes [N, K] into the packed layout (offline, on the GPU)."""
+    f = _fmt(fmt)
+    ldw = _row_major(wq, "wq") * wq.element_size()
+    N, K = wq.shape
+    out = torch.empty(packed_weight_size(f, N, K), dtype=torch.uint8, device=wq.device)
+    _check(_lib.w8_pack_weight(f, N, K, _dev_ptr(wq, "wq"), ldw, _dev_ptr(out, "out"),
+                               _stream(stream, wq.device)))
+    return PackedWeight(f, N, K, out)
+
+
+# --------------------------------------------------------------------- GEMM --
+def workspace_size(fmt, M, N, K, cfg=None, packed=False):
+    n = ctypes.c_size_t(0)
+    _check(_lib.w8_workspace_size(_fmt(fmt), M, N, K, int(bool(packed)), _cfg_ptr(cfg),
+                                  ctypes.byref(n)))
     return n.value
 
 
@@ -162,8 +195,8 @@ class Workspace:
             self.buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
         return self.buf
 
-    def for_call(self, fmt, M, N, K, cfg=None):
-        need = workspace_size(fmt, M, N, K, cfg)
+    def for_call(self, fmt, M, N, K, cfg=None, packed=False):
+        need = workspace_size(fmt, M, N, K, cfg, packed)
         if need == 0:
             return None, 0
         buf = self.reserve(need)
@@ -173,19 +206,26 @@ class Workspace:
 def _gemm(entry, fmt, xq, sx, wq, sw, out, cfg, workspace, stream):
     f = _fmt(fmt)
     ldq = _row_major(xq, "xq") * xq.element_size()
-    ldw = _row_major(wq, "wq") * wq.element_size()
     ldo = _row_major(out, "out")
     M, K = xq.shape
-    N = wq.shape[0]
-    if wq.shape[1] != K:
-        raise ValueError(f"K mismatch: xq {tuple(xq.shape)} vs wq {tuple(wq.shape)}")
-    if xq.element_size() != 1 or wq.element_size() != 1:
-        raise TypeError("xq and wq must hold 1-byte codes")
+    if isinstance(wq, PackedWeight):
+        if wq.fmt != f:
+            raise ValueError("packed weights were packed for another format")
+        N, wk, ldw, wptr, packed = wq.N, wq.K, 0, _dev_ptr(wq.data, "wq"), True
+    else:
+        N, wk = wq.shape
+        ldw, wptr, packed = _row_major(wq, "wq") * wq.element_size(), _dev_ptr(wq, "wq"), False
+        if wq.element_size() != 1:
+            raise TypeError("wq must hold 1-byte codes")
+    if wk != K:
+        raise ValueError(f"K mismatch: xq {tuple(xq.shape)} vs weights {(N, wk)}")
+    if xq.element_size() != 1:
+        raise TypeError("xq must hold 1-byte codes")
     if workspace is None:
         workspace = _default_workspace(xq.device)
-    ws_ptr, ws_bytes = workspace.for_call(f, M, N, K, cfg)
+    ws_ptr, ws_bytes = workspace.for_call(f, M, N, K, cfg, packed)
     _check(entry(f, M, N, K, _dev_ptr(xq, "xq"), ldq, _dev_ptr(sx, "sx", torch.float32),
-                 _dev_ptr(wq, "wq"), ldw, _dev_ptr(sw, "sw", torch.float32),
+                 wptr, ldw, _dev_ptr(sw, "sw", torch.float32),
                  _dev_ptr(out, "out"), ldo, _cfg_ptr(cfg), ws_ptr, ws_bytes,
                  _stream(stream, xq.device)))
     return out
@@ -204,8 +244,9 @@ def _default_workspace(device):
 def gemm_w8a8(fmt, xq, sx, wq, sw, cfg=None, y=None, workspace=None, stream=None):
     """Y = dequant(xq) . dequant(wq)^T as bf16 [M, N].
 
-    cfg: a Config (or dict of its fields); None uses the config table entry
-    for the shape, else the default config.
+    wq: row-major codes [N, K] or a PackedWeight.  cfg: a Config (or dict of
+    its fields); None uses the config table entry for the shape and weight
+    layout, else the default config.
     """
     M, N = xq.shape[0], wq.shape[0]
     if y is None:
@@ -227,7 +268,9 @@ def gemm_w8a8_acc(fmt, xq, sx, wq, sw, cfg=None, out=None, workspace=None, strea
 
 
 def linear(fmt, x, wq, sw, cfg=None, y=None, workspace=None, stream=None):
-    """The whole hot path: quantize bf16 activations, then the GEMM."""
+    """The whole hot path: quantize bf16 activations, then the GEMM.
+
+    wq: row-major codes [N, K] or a PackedWeight."""
     xq, sx = quantize_act(fmt, x, stream=stream)
     return gemm_w8a8(fmt, xq, sx, wq, sw, cfg=cfg, y=y, workspace=workspace, stream=stream)
 
@@ -243,28 +286,44 @@ def default_config(fmt, M, N, K):
     return c
 
 
-def resolve_config(fmt, M, N, K):
+def resolve_config(fmt, M, N, K, packed=False):
     """(Config, from_table) that gemm_w8a8 uses when cfg is None."""
     c = Config()
     hit = ctypes.c_int(0)
-    _check(_lib.w8_resolve_config(_fmt(fmt), M, N, K, ctypes.byref(c), ctypes.byref(hit)))
+    _check(_lib.w8_resolve_config(_fmt(fmt), M, N, K, int(bool(packed)), ctypes.byref(c),
+                                  ctypes.byref(hit)))
     return c, bool(hit.value)
 
 
-def lookup_config(fmt, M, N, K):
-    """Exact table entry for the shape, or None."""
+def lookup_config(fmt, M, N, K, packed=False, with_time=False):
+    """Exact table entry for the shape and weight layout, or None.
+
+    with_time=True returns (Config, us_per_gemm) instead of the Config.
+    """
     c = Config()
-    st = _lib.w8_lookup_config(_fmt(fmt), M, N, K, ctypes.byref(c))
+    us = ctypes.c_double(0.0)
+    st = _lib.w8_lookup_config(_fmt(fmt), M, N, K, int(bool(packed)), ctypes.byref(c),
+                               ctypes.byref(us))
     if st == 8:
         return None
     _check(st)
-    return c
+    return (c, us.value) if with_time else c
 
 
-def set_config(fmt, M, N, K, cfg, us_per_gemm=0.0):
+def best_layout(fmt, M, N, K):
+    """True if the table says packed weights are faster for this shape."""
+    row = lookup_config(fmt, M, N, K, packed=False, with_time=True)
+    pk = lookup_config(fmt, M, N, K, packed=True, with_time=True)
+    if pk is None:
+        return False
+    return row is None or pk[1] < row[1]
+
+
+def set_config(fmt, M, N, K, cfg, us_per_gemm=0.0, packed=False):
     if isinstance(cfg, dict):
         cfg = Config.make(**cfg)
-    _check(_lib.w8_set_config(_fmt(fmt), M, N, K, ctypes.byref(cfg), float(us_per_gemm)))
+    _check(_lib.w8_set_config(_fmt(fmt), M, N, K, int(bool(packed)), ctypes.byref(cfg),
+                              float(us_per_gemm)))
 
 
 def load_config_table(path):
@@ -297,8 +356,8 @@ def load_default_table():
 
 # -------------------------------------------------------------------- tuner --
 def tune_shape(fmt, M, N, K, warmup=2, replays=5, bank2_top=5, rotate_bytes=512 << 20,
-               max_split_k=MAX_SPLIT_K, insert=True, fail_candidate=-1):
-    """Ahead-of-time tuning of one shape on the current device.
+               max_split_k=MAX_SPLIT_K, insert=True, fail_candidate=-1, packed=False):
+    """Ahead-of-time tuning of one shape and weight layout on the current device.
 
     Returns (Config, stats dict).  Synchronizes the device.
     """
@@ -307,6 +366,7 @@ def tune_shape(fmt, M, N, K, warmup=2, replays=5, bank2_top=5, rotate_bytes=512 
     o.warmup, o.replays, o.bank2_top = warmup, replays, bank2_top
     o.rotate_bytes, o.max_split_k = rotate_bytes, max_split_k
     o.insert, o.fail_candidate = int(bool(insert)), fail_candidate
+    o.packed = int(bool(packed))
     best = Config()
     stats = TuneStats()
     _check(_lib.w8_tune_shape(_fmt(fmt), M, N, K, ctypes.byref(o), ctypes.byref(best),

@@ -19,21 +19,22 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 constexpr int kMaxK = 1 << 22;
 constexpr int kMaxN = 1 << 24;
 
-int wn_index(int wn) { return wn == 1 ? 0 : wn == 2 ? 1 : wn == 4 ? 2 : -1; }
+int nb_index(int nb) { return nb == 1 ? 0 : nb == 2 ? 1 : nb == 4 ? 2 : -1; }
 int wk_index(int wk) {
   return wk == 1 ? 0 : wk == 2 ? 1 : wk == 4 ? 2 : wk == 8 ? 3 : wk == 16 ? 4 : -1;
 }
 int u_index(int u) { return u == 1 ? 0 : u == 2 ? 1 : u == 4 ? 2 : -1; }
 
-// [fmt][mb-1][wn][wk][unroll][swap] -> launcher
+// [fmt][mb-1][nb][wk][unroll][swap][packed] -> launcher
 struct InstanceIndex {
-  GemmLaunchFn fn[3][2][3][5][3][2] = {};
+  GemmLaunchFn fn[3][2][3][5][3][2][2] = {};
   InstanceIndex() {
     int n = 0;
     const GemmInstance* p = gemm_instances(&n);
     for (int i = 0; i < n; ++i) {
       const GemmInstance& g = p[i];
-      fn[g.fmt][g.mb - 1][wn_index(g.wn)][wk_index(g.wk)][u_index(g.unroll)][g.swap] = g.fn;
+      fn[g.fmt][g.mb - 1][nb_index(g.nb)][wk_index(g.wk)][u_index(g.unroll)][g.swap][g.packed] =
+          g.fn;
     }
   }
 };
@@ -96,11 +97,12 @@ w8_status check_cfg(int fmt, int M, int N, int K, const w8_cfg& c) {
     return fail(W8_E_INVALID, "cfg.abi_version " + std::to_string(c.abi_version) + " != " +
                                   std::to_string(W8_ABI_VERSION));
   if (c.reserved[0] || c.reserved[1]) return fail(W8_E_INVALID, "cfg.reserved must be zero");
-  if (c.tile_n != 16 && c.tile_n != 32 && c.tile_n != 64)
+  if (nb_index(c.tile_n / 16) < 0 || c.tile_n % 16)
     return fail(W8_E_INVALID, "cfg.tile_n must be 16, 32 or 64");
   if (wk_index(c.waves_k) < 0) return fail(W8_E_INVALID, "cfg.waves_k must be 1, 2, 4, 8 or 16");
-  if ((c.tile_n / 16) * c.waves_k > 16) return fail(W8_E_INVALID, "cfg: tile_n/16 * waves_k > 16");
   if (u_index(c.unroll) < 0) return fail(W8_E_INVALID, "cfg.unroll must be 1, 2 or 4");
+  if ((c.tile_n / 16) * c.unroll > 4)
+    return fail(W8_E_INVALID, "cfg: tile_n/16 * unroll must be at most 4");
   if (!is_pow2(c.split_k) || c.split_k > W8_MAX_SPLIT_K)
     return fail(W8_E_INVALID, "cfg.split_k must be a power of two in [1, 256], got " +
                                   std::to_string(c.split_k));
@@ -163,9 +165,9 @@ w8_status check_device() {
 
 w8_status launch_gemm_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
   const int mb = (g.M + 15) / 16;
-  const int wn = c.tile_n / 16;
-  GemmLaunchFn fn = instance_index().fn[g.fmt][mb - 1][wn_index(wn)][wk_index(c.waves_k)]
-                                         [u_index(c.unroll)][c.swap_ab];
+  const int nb = c.tile_n / 16;
+  GemmLaunchFn fn = instance_index().fn[g.fmt][mb - 1][nb_index(nb)][wk_index(c.waves_k)]
+                                         [u_index(c.unroll)][c.swap_ab][g.packed ? 1 : 0];
   if (!fn) return fail(W8_E_INVALID, "no compiled kernel for this config");
   const int ntiles = (g.N + c.tile_n - 1) / c.tile_n;
   GemmArgs a;
@@ -192,7 +194,7 @@ w8_status launch_gemm_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
     a.counters = static_cast<unsigned int*>(g.ws);
     a.part = static_cast<char*>(g.ws) + ws_counter_bytes(ntiles);
   }
-  hipError_t e = fn(a, dim3(ntiles, c.split_k), dim3(64 * wn * c.waves_k), s);
+  hipError_t e = fn(a, dim3(ntiles, c.split_k), dim3(64 * c.waves_k), s);
   if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("GEMM launch", e));
   return W8_OK;
 }
@@ -212,8 +214,11 @@ w8_status gemm_entry(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ld
   if (!xq || !sx || !wq || !sw || !out) return fail(W8_E_INVALID, "null device pointer");
   if (!aligned(xq, 16) || !aligned(wq, 16))
     return fail(W8_E_INVALID, "xq and wq must be 16-byte aligned");
-  if (ldq < K || ldw < K || ldq % 16 || ldw % 16)
-    return fail(W8_E_INVALID, "ldq and ldw must be >= K and multiples of 16");
+  const int packed = ldw == 0;  // ldw == 0: weights in the packed layout
+  if (ldq < K || ldq % 16 || (!packed && (ldw < K || ldw % 16)))
+    return fail(W8_E_INVALID,
+                "ldq must be >= K and a multiple of 16; ldw must be 0 (packed weights) or "
+                ">= K and a multiple of 16");
   if (ldo < N) return fail(W8_E_INVALID, "output leading dimension must be >= N");
   if (!aligned(sx, 4) || !aligned(sw, 4) || !aligned(out, out_mode ? 4 : 2))
     return fail(W8_E_INVALID, "misaligned scale or output pointer");
@@ -223,7 +228,7 @@ w8_status gemm_entry(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ld
     st = check_cfg(fmt, M, N, K, c);
     if (st) return st;
   } else {
-    c = resolve_cfg(fmt, M, N, K, nullptr);
+    c = resolve_cfg(fmt, M, N, K, packed, nullptr);
   }
   const size_t need = workspace_bytes(fmt, M, N, c);
   if (need > 0) {
@@ -234,7 +239,7 @@ w8_status gemm_entry(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ld
   }
   st = check_device();
   if (st) return st;
-  GemmCall g{fmt, M, N, K, xq, ldq, sx, wq, ldw, sw, out, ldo, out_mode, ws, ws_bytes};
+  GemmCall g{fmt, M, N, K, xq, ldq, sx, wq, ldw, sw, out, ldo, out_mode, ws, ws_bytes, packed};
   st = launch_gemm_call(g, c, static_cast<hipStream_t>(stream));
   if (st) return st;
   return ok();
@@ -297,7 +302,8 @@ w8_status w8_quantize_weight(w8_fmt fmt, int N, int K, const float* w, int64_t l
   return ok();
 }
 
-w8_status w8_workspace_size(w8_fmt fmt, int M, int N, int K, const w8_cfg* cfg, size_t* bytes) {
+w8_status w8_workspace_size(w8_fmt fmt, int M, int N, int K, int packed, const w8_cfg* cfg,
+                            size_t* bytes) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!bytes) return fail(W8_E_INVALID, "null output pointer");
@@ -307,9 +313,32 @@ w8_status w8_workspace_size(w8_fmt fmt, int M, int N, int K, const w8_cfg* cfg, 
     st = check_cfg(fmt, M, N, K, c);
     if (st) return st;
   } else {
-    c = resolve_cfg(fmt, M, N, K, nullptr);
+    c = resolve_cfg(fmt, M, N, K, packed != 0, nullptr);
   }
   *bytes = workspace_bytes(fmt, M, N, c);
+  return ok();
+}
+
+w8_status w8_packed_weight_size(w8_fmt fmt, int N, int K, size_t* bytes) {
+  w8_status st = check_gemm_shape(fmt, 1, N, K);
+  if (st) return st;
+  if (!bytes) return fail(W8_E_INVALID, "null output pointer");
+  *bytes = packed_weight_bytes(fmt, N, K);
+  return ok();
+}
+
+w8_status w8_pack_weight(w8_fmt fmt, int N, int K, const void* wq, int64_t ldw, void* wp,
+                         w8_stream stream) {
+  w8_status st = check_gemm_shape(fmt, 1, N, K);
+  if (st) return st;
+  if (!wq || !wp) return fail(W8_E_INVALID, "null device pointer");
+  if (!aligned(wq, 16) || !aligned(wp, 16) || ldw < K || ldw % 16)
+    return fail(W8_E_INVALID, "wq and wp must be 16-byte aligned, ldw >= K and ldw % 16 == 0");
+  st = check_device();
+  if (st) return st;
+  hipError_t e = launch_pack_weight(fmt, static_cast<const uint8_t*>(wq), ldw, N, K,
+                                    static_cast<uint8_t*>(wp), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("pack_weight launch", e));
   return ok();
 }
 
@@ -345,12 +374,13 @@ w8_status w8_default_config(w8_fmt fmt, int M, int N, int K, w8_cfg* out) {
   return ok();
 }
 
-w8_status w8_resolve_config(w8_fmt fmt, int M, int N, int K, w8_cfg* out, int* from_table) {
+w8_status w8_resolve_config(w8_fmt fmt, int M, int N, int K, int packed, w8_cfg* out,
+                            int* from_table) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!out) return fail(W8_E_INVALID, "null output pointer");
   int hit = 0;
-  *out = resolve_cfg(fmt, M, N, K, &hit);
+  *out = resolve_cfg(fmt, M, N, K, packed != 0, &hit);
   if (from_table) *from_table = hit;
   return ok();
 }

@@ -25,8 +25,9 @@ w8_cfg make_default_cfg(int fmt, int M, int N, int K);
 size_t workspace_bytes(int fmt, int M, int N, const w8_cfg& c);
 int ksteps_of(int fmt, int K);
 
-// Resolve cfg == NULL through the table, else the default.
-w8_cfg resolve_cfg(int fmt, int M, int N, int K, int* from_table);
+// Resolve cfg == NULL through the table (entries are per weight layout),
+// else the default.
+w8_cfg resolve_cfg(int fmt, int M, int N, int K, int packed, int* from_table);
 
 // The device must be gfx950 (checked once per device).
 w8_status check_device();
@@ -45,6 +46,7 @@ struct GemmCall {
   int out_mode;
   void* ws;
   size_t ws_bytes;
+  int packed;  // weights in the packed (MFMA-native) layout
 };
 w8_status launch_gemm_call(const GemmCall& call, const w8_cfg& c, hipStream_t s);
 

@@ -52,9 +52,17 @@ struct GemmArgs {
 typedef hipError_t (*GemmLaunchFn)(const GemmArgs&, dim3 grid, dim3 block, hipStream_t);
 
 struct GemmInstance {
-  int fmt, mb, wn, wk, unroll, swap;
+  int fmt, mb, nb, wk, unroll, swap, packed;
   GemmLaunchFn fn;
 };
+
+// Packs row-major weight codes into the MFMA-native layout of fmt.
+hipError_t launch_pack_weight(int fmt, const uint8_t* w, long long ldw, int N, int K,
+                              uint8_t* out, hipStream_t s);
+inline size_t packed_weight_bytes(int fmt, int N, int K) {
+  const int kstep = fmt == 1 ? 64 : 128;
+  return (size_t)((N + 15) / 16) * ((K + kstep - 1) / kstep) * 16 * kstep;
+}
 
 // Every compiled instance, gathered from the per-format translation units.
 const GemmInstance* gemm_instances(int* count);
@@ -64,7 +72,7 @@ inline int kstep_of(int fmt) { return fmt == 1 ? 64 : 128; }
 
 // Workspace layout: a fixed 64 KiB counter region (one 4-byte arrival counter
 // per output tile, at most kSplitKMaxTiles tiles), then the partials: one
-// 1 KiB fragment (64 lanes x 16 bytes) per (tile, split, wave along N,
+// 1 KiB fragment (64 lanes x 16 bytes) per (tile, split, 16-row block of N,
 // 16-row block of M).  The counter region has the same size for every shape,
 // so the partials of one call never overlap the counters of another call
 // that shares the workspace: counters left at zero stay zero.
@@ -73,8 +81,8 @@ inline size_t ws_counter_bytes(int ntiles) {
   (void)ntiles;
   return (size_t)kSplitKMaxTiles * 4;
 }
-inline size_t ws_partial_bytes(int ntiles, int split_k, int wn, int mb) {
-  return (size_t)ntiles * split_k * wn * mb * 1024;
+inline size_t ws_partial_bytes(int ntiles, int split_k, int nb, int mb) {
+  return (size_t)ntiles * split_k * nb * mb * 1024;
 }
 
 }  // namespace w8

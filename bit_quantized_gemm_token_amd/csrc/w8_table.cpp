@@ -1,6 +1,7 @@
 // Per-shape config table (ai-radar.it, "Helion nel backend vLLM", paragraphs
 // 6-7: tuned configs are shipped per shape, with a default config for shapes
-// that have none).  Lookup is exact on (arch, abi, fmt, M, N, K); a miss, or
+// that have none).  Lookup is exact on (arch, abi, fmt, weight layout, M, N,
+// K); a miss, or
 // an entry written for another arch or ABI, falls back to the default config
 // (the hard-fallback cases of TensorRT-LLM issue 16363, "Suggested
 // direction", that apply to a table: cache miss and backend identity
@@ -27,7 +28,9 @@ struct Entry {
   double us;
 };
 
-typedef std::tuple<int, int, int, int> Key;  // fmt, M, N, K
+typedef std::tuple<int, int, int, int, int> Key;  // fmt, packed, M, N, K
+
+const char* layout_name(int packed) { return packed ? "packed" : "row"; }
 
 struct Table {
   std::mutex mu;
@@ -79,18 +82,22 @@ w8_status parse_table(const std::string& text, std::map<Key, Entry>* native,
     while (ls >> t) tok.push_back(t);
     if (tok.empty()) continue;
     const std::string where = "config table line " + std::to_string(lineno) + ": ";
-    if (tok.size() != 12)
-      return fail(W8_E_TABLE_FORMAT, where + "expected 12 fields, got " + std::to_string(tok.size()));
+    if (tok.size() != 13)
+      return fail(W8_E_TABLE_FORMAT, where + "expected 13 fields, got " + std::to_string(tok.size()));
     int abi = 0;
     if (!parse_int(tok[1], &abi)) return fail(W8_E_TABLE_FORMAT, where + "bad abi field");
     const int fmt = fmt_from_name(tok[2]);
     if (fmt < 0) return fail(W8_E_TABLE_FORMAT, where + "unknown format '" + tok[2] + "'");
+    int packed = -1;
+    if (tok[3] == "row") packed = 0;
+    if (tok[3] == "packed") packed = 1;
+    if (packed < 0) return fail(W8_E_TABLE_FORMAT, where + "layout must be row or packed");
     int v[8];
     for (int i = 0; i < 8; ++i)
-      if (!parse_int(tok[3 + i], &v[i]))
-        return fail(W8_E_TABLE_FORMAT, where + "bad integer '" + tok[3 + i] + "'");
+      if (!parse_int(tok[4 + i], &v[i]))
+        return fail(W8_E_TABLE_FORMAT, where + "bad integer '" + tok[4 + i] + "'");
     double us = 0;
-    if (!parse_double(tok[11], &us)) return fail(W8_E_TABLE_FORMAT, where + "bad time field");
+    if (!parse_double(tok[12], &us)) return fail(W8_E_TABLE_FORMAT, where + "bad time field");
     if (tok[0] != kArch || abi != W8_ABI_VERSION) {
       foreign->push_back(line);
       continue;
@@ -105,7 +112,7 @@ w8_status parse_table(const std::string& text, std::map<Key, Entry>* native,
     c.swap_ab = v[7];
     if (check_gemm_shape(fmt, v[0], v[1], v[2]) != W8_OK || check_cfg(fmt, v[0], v[1], v[2], c) != W8_OK)
       return fail(W8_E_TABLE_FORMAT, where + "invalid entry (" + std::string(w8_last_error()) + ")");
-    (*native)[Key(fmt, v[0], v[1], v[2])] = Entry{c, us};
+    (*native)[Key(fmt, packed, v[0], v[1], v[2])] = Entry{c, us};
   }
   return W8_OK;
 }
@@ -152,12 +159,12 @@ void maybe_load_env(Table& t) {
 
 }  // namespace
 
-w8_cfg resolve_cfg(int fmt, int M, int N, int K, int* from_table) {
+w8_cfg resolve_cfg(int fmt, int M, int N, int K, int packed, int* from_table) {
   Table& t = table();
   {
     std::lock_guard<std::mutex> lk(t.mu);
     maybe_load_env(t);
-    auto it = t.native.find(Key(fmt, M, N, K));
+    auto it = t.native.find(Key(fmt, packed ? 1 : 0, M, N, K));
     if (it != t.native.end()) {
       if (from_table) *from_table = 1;
       return it->second.cfg;
@@ -186,13 +193,14 @@ w8_status w8_save_config_table(const char* path) {
     std::lock_guard<std::mutex> lk(t.mu);
     maybe_load_env(t);
     out << "# w8gemm per-shape config table\n"
-        << "# arch abi fmt M N K tile_n waves_k unroll split_k swap_ab us_per_gemm\n";
+        << "# arch abi fmt layout M N K tile_n waves_k unroll split_k swap_ab us_per_gemm\n";
     for (const auto& kv : t.native) {
       const Entry& e = kv.second;
       char buf[256];
-      std::snprintf(buf, sizeof buf, "%s %d %s %d %d %d %d %d %d %d %d %.4f\n", kArch,
-                    W8_ABI_VERSION, fmt_name(std::get<0>(kv.first)), std::get<1>(kv.first),
-                    std::get<2>(kv.first), std::get<3>(kv.first), e.cfg.tile_n, e.cfg.waves_k,
+      std::snprintf(buf, sizeof buf, "%s %d %s %s %d %d %d %d %d %d %d %d %.4f\n", kArch,
+                    W8_ABI_VERSION, fmt_name(std::get<0>(kv.first)),
+                    layout_name(std::get<1>(kv.first)), std::get<2>(kv.first),
+                    std::get<3>(kv.first), std::get<4>(kv.first), e.cfg.tile_n, e.cfg.waves_k,
                     e.cfg.unroll, e.cfg.split_k, e.cfg.swap_ab, e.us);
       out << buf;
     }
@@ -233,7 +241,8 @@ int w8_config_table_foreign(void) {
   return t.foreign_count;
 }
 
-w8_status w8_set_config(w8_fmt fmt, int M, int N, int K, const w8_cfg* cfg, double us_per_gemm) {
+w8_status w8_set_config(w8_fmt fmt, int M, int N, int K, int packed, const w8_cfg* cfg,
+                        double us_per_gemm) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!cfg) return fail(W8_E_INVALID, "null cfg");
@@ -242,20 +251,22 @@ w8_status w8_set_config(w8_fmt fmt, int M, int N, int K, const w8_cfg* cfg, doub
   Table& t = table();
   std::lock_guard<std::mutex> lk(t.mu);
   maybe_load_env(t);
-  t.native[Key(fmt, M, N, K)] = Entry{*cfg, us_per_gemm};
+  t.native[Key(fmt, packed ? 1 : 0, M, N, K)] = Entry{*cfg, us_per_gemm};
   return ok();
 }
 
-w8_status w8_lookup_config(w8_fmt fmt, int M, int N, int K, w8_cfg* out) {
+w8_status w8_lookup_config(w8_fmt fmt, int M, int N, int K, int packed, w8_cfg* out,
+                           double* us_per_gemm) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!out) return fail(W8_E_INVALID, "null output pointer");
   Table& t = table();
   std::lock_guard<std::mutex> lk(t.mu);
   maybe_load_env(t);
-  auto it = t.native.find(Key(fmt, M, N, K));
-  if (it == t.native.end()) return fail(W8_E_NOT_FOUND, "no table entry for this shape");
+  auto it = t.native.find(Key(fmt, packed ? 1 : 0, M, N, K));
+  if (it == t.native.end()) return fail(W8_E_NOT_FOUND, "no table entry for this shape and layout");
   *out = it->second.cfg;
+  if (us_per_gemm) *us_per_gemm = it->second.us;
   return ok();
 }
 

@@ -61,7 +61,8 @@ __global__ void fill_scales_kernel(float* p, size_t n, uint32_t seed, float lo, 
 }
 
 struct Buffers {
-  uint8_t* wpool = nullptr;
+  uint8_t* wrow = nullptr;   // row-major weights of copy 0 (validation reference)
+  uint8_t* wpool = nullptr;  // R weight copies in the tuned layout
   uint8_t* xq = nullptr;
   float* sx = nullptr;
   float* sw = nullptr;
@@ -69,6 +70,7 @@ struct Buffers {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   ~Buffers() {
+    hipFree(wrow);
     hipFree(wpool);
     hipFree(xq);
     hipFree(sx);
@@ -114,6 +116,7 @@ extern "C" void w8_tune_default_opts(w8_tune_opts* o) {
   o->max_split_k = W8_MAX_SPLIT_K;
   o->insert = 1;
   o->fail_candidate = -1;
+  o->packed = 0;
 }
 
 extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tune_opts* opts,
@@ -134,8 +137,10 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   st = check_device();
   if (st) return st;
 
+  const int packed = o.packed ? 1 : 0;
   const long long ld = (K + 15) / 16 * 16;
-  const size_t wbytes = (size_t)N * ld;
+  const size_t wrow_bytes = (size_t)N * ld;
+  const size_t wbytes = packed ? packed_weight_bytes(fmt, N, K) : wrow_bytes;
   size_t R = wbytes ? (size_t)((o.rotate_bytes + (long long)wbytes - 1) / (long long)wbytes) : 1;
   R = std::max<size_t>(R, 2);
   R = std::min<size_t>(R, 4096);
@@ -158,7 +163,7 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   const int waves[] = {1, 2, 4, 8, 16};
   const int unrolls[] = {1, 2, 4};
   auto total_waves = [&](const w8_cfg& c) {
-    return (long long)((N + c.tile_n - 1) / c.tile_n) * (c.tile_n / 16) * c.waves_k * c.split_k;
+    return (long long)((N + c.tile_n - 1) / c.tile_n) * c.waves_k * c.split_k;
   };
   std::vector<w8_cfg> all;
   long long most_waves = 0;
@@ -203,6 +208,7 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
     hipStream_t s;
     ~StreamGuard() { hipStreamDestroy(s); }
   } sguard{stream};
+  TRY_HIP(hipMalloc(&b.wrow, wrow_bytes));
   TRY_HIP(hipMalloc(&b.wpool, wbytes * R));
   TRY_HIP(hipMalloc(&b.xq, (size_t)M * ld));
   TRY_HIP(hipMalloc(&b.sx, nsx * 4));
@@ -216,6 +222,14 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   const int is_int8 = fmt == W8_W8A8_INT8;
   hipLaunchKernelGGL(fill_codes_kernel, dim3(4096), dim3(256), 0, stream, b.wpool, wbytes * R,
                      0x1234u, is_int8);
+  hipLaunchKernelGGL(fill_codes_kernel, dim3(1024), dim3(256), 0, stream, b.wrow, wrow_bytes,
+                     0x4321u, is_int8);
+  // copy 0 of the pool holds the same weights as the reference, in the tuned layout
+  if (packed) {
+    TRY_HIP(launch_pack_weight(fmt, b.wrow, ld, N, K, b.wpool, stream));
+  } else {
+    TRY_HIP(hipMemcpyAsync(b.wpool, b.wrow, wrow_bytes, hipMemcpyDeviceToDevice, stream));
+  }
   hipLaunchKernelGGL(fill_codes_kernel, dim3(64), dim3(256), 0, stream, b.xq, (size_t)M * ld,
                      0x9876u, is_int8);
   hipLaunchKernelGGL(fill_scales_kernel, dim3(64), dim3(256), 0, stream, b.sx, nsx, 0x55u, 0.01f,
@@ -225,11 +239,16 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   TRY_HIP(hipGetLastError());
   TRY_HIP(hipStreamSynchronize(stream));
 
-  GemmCall call{fmt, M, N, K, b.xq, ld, b.sx, b.wpool, ld, b.sw, b.y, N, 0, b.ws, b.ws_bytes};
+  GemmCall call{fmt, M,     N, K,     b.xq, ld, b.sx,      b.wpool, packed ? 0 : ld,
+                b.sw, b.y, N, 0, b.ws, b.ws_bytes, packed};
 
-  // Reference output: the default config on weight copy 0.
+  // Reference output: the default config on the row-major weights of copy 0.
   std::vector<uint16_t> yref((size_t)M * N), ycur((size_t)M * N);
-  st = launch_gemm_call(call, dflt, stream);
+  GemmCall ref = call;
+  ref.wq = b.wrow;
+  ref.ldw = ld;
+  ref.packed = 0;
+  st = launch_gemm_call(ref, dflt, stream);
   if (st) return st;
   TRY_HIP(hipStreamSynchronize(stream));
   TRY_HIP(hipMemcpy(yref.data(), b.y, yref.size() * 2, hipMemcpyDeviceToHost));
@@ -257,6 +276,7 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
 
   // Median us per GEMM of the graph of R GEMMs over rotating weight copies.
   auto time_cfg = [&](const w8_cfg& c, double* us) -> w8_status {
+    // (every GEMM of the graph reads its own copy of the weights)
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     TRY_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal));
@@ -324,7 +344,7 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
     if (st) return st;
   }
   double dflt_us2 = 0;
-  st = time_cfg(dflt, &dflt_us2);
+  st = time_cfg(dflt, &dflt_us2);  // the default config on the tuned layout
   if (st) return st;
 
   // Bank-2 winner; within 1% prefer split_k = 1, then swap_ab = 0, then fewer waves.
@@ -336,14 +356,14 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
       win = c;
     } else if (a <= w * 1.01) {
       const auto rank = [](const w8_cfg& x) {
-        return std::make_tuple(x.split_k == 1 ? 0 : 1, x.swap_ab, x.waves_k * (x.tile_n / 16));
+        return std::make_tuple(x.split_k == 1 ? 0 : 1, x.swap_ab, x.waves_k);
       };
       if (rank(c->cfg) < rank(win->cfg)) win = c;
     }
   }
   *best = win->cfg;
   if (o.insert) {
-    st = w8_set_config(fmt, M, N, K, &win->cfg, win->us2);
+    st = w8_set_config(fmt, M, N, K, packed, &win->cfg, win->us2);
     if (st) return st;
   }
   if (stats) {

@@ -42,6 +42,7 @@ def main(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--out", required=True)
     p.add_argument("--formats", default="FP8_Dynamic,W8A8_INT8,Block_FP8")
+    p.add_argument("--layouts", default="row,packed")
     p.add_argument("--shapes", default=None)
     p.add_argument("--no-resume", action="store_true")
     p.add_argument("--max-split-k", type=int, default=w8.MAX_SPLIT_K)
@@ -59,23 +60,27 @@ def main(argv=None):
         w8.load_config_table(a.out)
     t0 = time.time()
     done = skipped = 0
+    layouts = [{"row": False, "packed": True}[v] for v in a.layouts.split(",")]
     for fmt in a.formats.split(","):
         for (M, N, K) in shapes:
-            if w8.lookup_config(fmt, M, N, K) is not None:
-                skipped += 1
-                continue
-            if a.time_budget_s and time.time() - t0 > a.time_budget_s:
-                print(f"[tune] time budget reached after {done} shapes", flush=True)
-                print(f"[tune] tuned {done}, kept {skipped}, table {a.out}", flush=True)
-                return 0
-            best, st = w8.tune_shape(fmt, M, N, K, rotate_bytes=a.rotate_mib << 20,
-                                     replays=a.replays, max_split_k=a.max_split_k, insert=True)
-            w8.save_config_table(a.out)
-            done += 1
-            print(f"[tune] {fmt} {M}x{N}x{K}: {best} {st['best_us_bank2']:.3f} us "
-                  f"({st['best_gbps']:.0f} GB/s; default {st['default_us_bank2']:.3f} us; "
-                  f"{st['validated']}/{st['candidates']} validated; {st['tune_seconds']:.1f} s)",
-                  flush=True)
+            for packed in layouts:
+                if w8.lookup_config(fmt, M, N, K, packed=packed) is not None:
+                    skipped += 1
+                    continue
+                if a.time_budget_s and time.time() - t0 > a.time_budget_s:
+                    print(f"[tune] time budget reached after {done} shapes", flush=True)
+                    print(f"[tune] tuned {done}, kept {skipped}, table {a.out}", flush=True)
+                    return 0
+                best, st = w8.tune_shape(fmt, M, N, K, rotate_bytes=a.rotate_mib << 20,
+                                         replays=a.replays, max_split_k=a.max_split_k, insert=True,
+                                         packed=packed)
+                w8.save_config_table(a.out)
+                done += 1
+                print(f"[tune] {fmt} {'packed' if packed else 'row'} {M}x{N}x{K}: {best} "
+                      f"{st['best_us_bank2']:.3f} us "
+                      f"({st['best_gbps']:.0f} GB/s; default {st['default_us_bank2']:.3f} us; "
+                      f"{st['validated']}/{st['candidates']} validated; {st['tune_seconds']:.1f} s)",
+                      flush=True)
     print(f"[tune] tuned {done}, kept {skipped}, table {a.out}", flush=True)
     return 0
 

@@ -84,19 +84,22 @@ typedef enum {
     W8_E_NOT_FOUND = 8     /* lookup miss */
 } w8_status;
 
-/* One kernel configuration of the GEMM family (paragraph 2-3 of the page:
+/* One kernel configuration of the GEMM family (paragraphs 2-3 of the page:
  * the algorithmic variants are parameters, not separate kernels).
- *   tile_n   output columns (= weight rows) per workgroup: 16, 32 or 64.
+ *   tile_n   output columns (= weight rows) per workgroup, all owned by every
+ *            wave of it: 16, 32 or 64 (one activation fragment feeds
+ *            tile_n/16 MFMAs per K-step).
  *   waves_k  wavefronts inside one workgroup that split its K range and are
- *            reduced through LDS: 1, 2, 4, 8 or 16 (tile_n/16 * waves_k
- *            <= 16, i.e. at most 1024 threads).
- *   unroll   MFMA K-steps each wave keeps in flight per loop iteration:
- *            1, 2 or 4.
+ *            reduced through LDS: 1, 2, 4, 8 or 16 (at most 1024 threads).
+ *   unroll   K-steps each wave loads per stage (two stages in flight):
+ *            1, 2 or 4, with tile_n/16 * unroll <= 4.
  *   split_k  workgroups splitting K, reduced in fixed order by the last one
  *            to finish: 1, 2, 4, ..., 256 (Split-K; 1 = Standard).
  *   swap_ab  0: MFMA A operand = activations, B = weights^T.
  *            1: Swap-AB, Y^T = Wq . Xq^T: A = weights, B = activations^T.
- * Set abi_version to W8_ABI_VERSION and reserved[] to 0.                    */
+ * Set abi_version to W8_ABI_VERSION and reserved[] to 0.  The weight layout
+ * (row-major or packed, below) is a property of the weight buffer, not of
+ * the config: it is given by the ldw argument of the GEMM.                 */
 typedef struct {
     int32_t abi_version;
     int32_t tile_n;
@@ -119,7 +122,8 @@ typedef struct {
     int32_t insert;           /* 1: insert the winner into the config table */
     int32_t fail_candidate;   /* test hook: candidate with this index fails validation
                                  (-1 = none) */
-    int32_t reserved[3];
+    int32_t packed;           /* weight layout tuned: 0 row-major, 1 packed */
+    int32_t reserved[2];
 } w8_tune_opts;
 
 typedef struct {
@@ -164,31 +168,50 @@ w8_status w8_quantize_weight(w8_fmt fmt, int N, int K, const float *w, int64_t l
                              void *wq, int64_t ldq, float *sw, w8_stream stream);
 
 /* ------------------------------------------------------------------ GEMM -- */
+/* Weight layouts.  Row-major: codes [N, K], row stride ldw bytes (ldw >= K,
+ * ldw % 16 == 0).  Packed: the MFMA-native layout written by w8_pack_weight
+ * (the "memory layout" choice the page puts in the tuner's search space,
+ * paragraph 3): for each block of 16 rows and each K-step (64 bytes of K for
+ * W8A8_INT8, 128 for the FP8 formats), the 16 x K-step bytes are stored in
+ * the order the kernel's lanes load them, so every load instruction reads
+ * 1 KiB contiguous; rows and K are zero-padded to whole fragments.  A GEMM
+ * call passes ldw = 0 for packed weights.  Configs are tuned per layout.     */
+
+/* Bytes of the packed layout for an N x K weight of fmt. */
+w8_status w8_packed_weight_size(w8_fmt fmt, int N, int K, size_t *bytes);
+
+/* Packs row-major codes (device, 16-byte aligned, ldw >= K, ldw % 16 == 0)
+ * into wp (device, 16-byte aligned, w8_packed_weight_size bytes).  Offline;
+ * one kernel launch on stream.  Same preconditions on N and K as the GEMM. */
+w8_status w8_pack_weight(w8_fmt fmt, int N, int K, const void *wq, int64_t ldw, void *wp,
+                         w8_stream stream);
+
 /* Bytes of device workspace the GEMM needs for (fmt, M, N, K) under cfg
- * (cfg NULL: the config w8_resolve_config picks).  0 when split_k == 1.
+ * (cfg NULL: the config w8_resolve_config picks for that weight layout;
+ * packed = 1 for packed weights).  0 when split_k == 1.
  * Layout: a fixed 64 KiB region of arrival counters, then the split-K
  * partials; split_k > 1 therefore supports at most 16384 output tiles
  * (N <= 16384 * tile_n).                                                    */
-w8_status w8_workspace_size(w8_fmt fmt, int M, int N, int K, const w8_cfg *cfg,
+w8_status w8_workspace_size(w8_fmt fmt, int M, int N, int K, int packed, const w8_cfg *cfg,
                             size_t *bytes);
 
 /* The quantized GEMM.  One kernel launch on `stream` (the split-K reduction
  * runs inside it: the last workgroup of each output tile to finish sums the
  * partials in split order, so results are run-to-run deterministic).
  *   xq, sx  activations as written by w8_quantize_act
- *   wq, sw  weights: codes [N, K] with row stride ldw bytes and scales in the
- *           layout given above for fmt
+ *   wq, sw  weights: codes in the row-major layout (row stride ldw bytes) or,
+ *           with ldw = 0, in the packed layout; scales in the layout given
+ *           above for fmt
  *   y       bf16 [M, N], row stride ldy elements (device)
  *   cfg     kernel configuration; NULL = the config table entry for
- *           (fmt, M, N, K) on this device, else the default config
+ *           (fmt, weight layout, M, N, K) on this device, else the default
  *   ws      workspace of at least w8_workspace_size() bytes, zero-filled
  *           before its first use; every completed call leaves its counters
  *           at zero again.  May be NULL when the size is 0.  Calls that share
  *           a workspace must not run concurrently.
  * Requires 1 <= M <= 32 (else W8_E_UNSUPPORTED), N >= 1, K >= 16,
- * K % 16 == 0 (Block_FP8: K % 128 == 0), ldq >= K, ldw >= K, ldy >= N,
- * xq/wq 16-byte aligned with ldq % 16 == 0 and ldw % 16 == 0, finite codes
- * (no E4M3FN NaN codes).                                                     */
+ * K % 16 == 0 (Block_FP8: K % 128 == 0), ldq >= K, ldy >= N, xq/wq 16-byte
+ * aligned with ldq % 16 == 0, finite codes (no E4M3FN NaN codes).          */
 w8_status w8_gemm_w8a8(w8_fmt fmt, int M, int N, int K,
                        const void *xq, int64_t ldq, const float *sx,
                        const void *wq, int64_t ldw, const float *sw,
@@ -215,18 +238,19 @@ w8_status w8_validate_config(w8_fmt fmt, int M, int N, int K, const w8_cfg *cfg)
  * page: a default config serves untuned shapes).                           */
 w8_status w8_default_config(w8_fmt fmt, int M, int N, int K, w8_cfg *out);
 
-/* The config the GEMM uses when called with cfg == NULL: the table entry for
- * (this device's arch, W8_ABI_VERSION, fmt, M, N, K) if present, else the
- * default.  *from_table is set to 1 on a table hit, 0 otherwise.            */
-w8_status w8_resolve_config(w8_fmt fmt, int M, int N, int K, w8_cfg *out,
+/* The config the GEMM uses when called with cfg == NULL for weights in the
+ * given layout (packed = 0 row-major, 1 packed): the table entry for
+ * (this device's arch, W8_ABI_VERSION, fmt, layout, M, N, K) if present,
+ * else the default.  *from_table is set to 1 on a table hit, 0 otherwise.   */
+w8_status w8_resolve_config(w8_fmt fmt, int M, int N, int K, int packed, w8_cfg *out,
                             int *from_table);
 
 /* ----------------------------------------------------------- config table -- */
 /* Per-shape config table (paragraphs 6-7 of the page).  Text format, one entry
  * per line:
- *   arch abi fmt M N K tile_n waves_k unroll split_k swap_ab us_per_gemm
- * '#' starts a comment.  Entries whose arch or abi differ from this build and
- * device are kept in the file but never used.
+ *   arch abi fmt layout M N K tile_n waves_k unroll split_k swap_ab us_per_gemm
+ * with layout "row" or "packed"; '#' starts a comment.  Entries whose arch or
+ * abi differ from this build and device are kept in the file but never used.
  * w8_load_config_table replaces the in-memory table atomically: on any parse
  * error it returns W8_E_TABLE_FORMAT (line number in w8_last_error()) and
  * keeps the old table.  If the environment variable W8_CONFIG_TABLE names a
@@ -238,15 +262,19 @@ int w8_config_table_size(void);
 /* Entries of the last load that were skipped for a foreign arch or abi. */
 int w8_config_table_foreign(void);
 /* Insert or replace one entry for this device (validated first). */
-w8_status w8_set_config(w8_fmt fmt, int M, int N, int K, const w8_cfg *cfg,
+w8_status w8_set_config(w8_fmt fmt, int M, int N, int K, int packed, const w8_cfg *cfg,
                         double us_per_gemm);
-/* Exact-shape lookup for this device: W8_OK on a hit, W8_E_NOT_FOUND on a miss. */
-w8_status w8_lookup_config(w8_fmt fmt, int M, int N, int K, w8_cfg *out);
+/* Exact lookup for this device: W8_OK on a hit (with the entry's time per
+ * GEMM in *us_per_gemm when not NULL), W8_E_NOT_FOUND on a miss.  Comparing
+ * the two layouts' times tells a caller which layout to store its weights in. */
+w8_status w8_lookup_config(w8_fmt fmt, int M, int N, int K, int packed, w8_cfg *out,
+                           double *us_per_gemm);
 
 /* ------------------------------------------------------------------ tuner -- */
 /* Ahead-of-time per-shape tuner (paragraph 3 of the page: the autotuner
- * compares configurations and keeps the best for each shape).  Allocates its
- * own inputs (random codes and scales), enumerates the configs of the family
+ * compares configurations and keeps the best for each shape).  Tunes one
+ * weight layout (opts->packed).  Allocates its own inputs (random codes and
+ * scales), enumerates the configs of the family
  * (tile_n x waves_k x unroll x split_k in {1, 2, ..., max_split_k} x
  * swap_ab) minus those that cannot pay off or duplicate another (split_k
  * above the K-steps, unroll above the K-steps per wave, partials above twice

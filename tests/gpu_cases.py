@@ -87,6 +87,14 @@ class Case:
             return out
         return self.memo("bound", lambda: 2.0 ** -14 * mag() + 1e-30)
 
+    def packed(self):
+        """The GPU weights in the packed layout (packed on the GPU)."""
+        import bit_quantized_gemm_token_amd as w8
+        return self.memo("packed", lambda: w8.pack_weight(self.fmt, self.wq))
+
+    def weights(self, packed):
+        return self.packed() if packed else self.wq
+
     def gpu_act(self):
         import bit_quantized_gemm_token_amd as w8
         return w8.quantize_act(self.fmt, self.x)

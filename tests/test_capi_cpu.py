@@ -89,8 +89,11 @@ def test_config_rejects_abi_and_reserved(w8):
     cfg = w8.Config.make()
     cfg.reserved[1] = 7
     assert not _valid(w8, "FP8_Dynamic", 4, 512, 1024, cfg)
-    cfg = w8.Config.make(tile_n=64, waves_k=8)   # 4 x 8 = 32 waves > 16
+    cfg = w8.Config.make(tile_n=64, unroll=2)    # 4 row blocks x unroll 2 > 4 registers sets
     assert not _valid(w8, "FP8_Dynamic", 4, 512, 1024, cfg)
+    cfg = w8.Config.make(tile_n=32, unroll=4)
+    assert not _valid(w8, "FP8_Dynamic", 4, 512, 1024, cfg)
+    assert _valid(w8, "FP8_Dynamic", 4, 512, 1024, w8.Config.make(tile_n=64, unroll=1, waves_k=16))
 
 
 def test_default_config_is_valid_everywhere(w8):
@@ -115,6 +118,7 @@ def _gemm(lib, fmt=0, M=4, N=64, K=256, xq=FAKE, ldq=256, sx=FAKE, wq=FAKE, ldw=
     (dict(fmt=2, K=272, ldq=272, ldw=272), 1), (dict(fmt=7), 1),
     (dict(xq=None), 1), (dict(sw=None), 1), (dict(y=None), 1),
     (dict(xq=ctypes.c_void_p(0x100008)), 1), (dict(ldq=255), 1), (dict(ldw=248), 1),
+    (dict(ldw=-16), 1), (dict(wq=ctypes.c_void_p(0x100004), ldw=0), 1),
     (dict(ldy=63), 1), (dict(sx=ctypes.c_void_p(0x100002)), 1)])
 def test_gemm_argument_errors(lib, kw, status):
     assert _gemm(lib, **kw) == status
@@ -129,6 +133,25 @@ def test_gemm_workspace_errors(w8, lib):
     assert _gemm(lib, K=1024, ldq=1024, ldw=1024, cfg=ctypes.byref(cfg), ws=FAKE, wsb=need - 1) == 3
     assert b"workspace" in lib.w8_last_error()
     assert w8.workspace_size("FP8_Dynamic", 4, 64, 1024, w8.Config.make(split_k=1)) == 0
+    # counters (64 KiB) + one 1 KiB fragment per (tile, split, row block, M block)
+    assert need == 65536 + 4 * 8 * 1 * 1 * 1024
+    assert w8.workspace_size("FP8_Dynamic", 20, 64, 1024, w8.Config.make(tile_n=32, unroll=2,
+                                                                         split_k=8)) == \
+        65536 + 2 * 8 * 2 * 2 * 1024
+
+
+def test_pack_argument_errors(w8, lib):
+    # every call here fails validation before anything touches a device
+    p = lib.w8_pack_weight
+    assert p(0, 64, 256, FAKE, 248, FAKE, None) == 1            # ldw < K
+    assert p(0, 64, 200, FAKE, 256, FAKE, None) == 1            # K % 16
+    assert p(2, 64, 192, FAKE, 256, FAKE, None) == 1            # Block_FP8 K % 128
+    assert p(0, 64, 256, None, 256, FAKE, None) == 1
+    assert p(0, 64, 256, FAKE, 256, ctypes.c_void_p(0x100008), None) == 1
+    # 16-row blocks x K-steps x (16 x K-step) bytes, zero padded
+    assert w8.packed_weight_size("W8A8_INT8", 17, 80) == 2 * 2 * 16 * 64
+    assert w8.packed_weight_size("FP8_Dynamic", 200, 208) == 13 * 2 * 16 * 128
+    assert w8.packed_weight_size("Block_FP8", 4608, 7168) == 4608 * 7168
 
 
 def test_quantize_argument_errors(lib):
@@ -145,17 +168,23 @@ def test_quantize_argument_errors(lib):
 
 
 def test_table_roundtrip_and_lookup(w8, tmp_path):
-    c1 = w8.Config.make(tile_n=32, waves_k=2, unroll=4, split_k=16, swap_ab=1)
+    c1 = w8.Config.make(tile_n=32, waves_k=2, unroll=2, split_k=16, swap_ab=1)
     c2 = w8.Config.make(tile_n=16, waves_k=8, unroll=1, split_k=1, swap_ab=0)
     w8.set_config("FP8_Dynamic", 4, 4096, 4096, c1, 3.25)
-    w8.set_config("Block_FP8", 32, 4608, 7168, c2, 5.5)
+    w8.set_config("Block_FP8", 32, 4608, 7168, c2, 5.5, packed=True)
     assert w8.config_table_size() == 2
     assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096) == c1
+    assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096, packed=True) is None
     assert w8.lookup_config("FP8_Dynamic", 5, 4096, 4096) is None
-    got, hit = w8.resolve_config("Block_FP8", 32, 4608, 7168)
+    assert w8.lookup_config("Block_FP8", 32, 4608, 7168, packed=True, with_time=True) == (c2, 5.5)
+    got, hit = w8.resolve_config("Block_FP8", 32, 4608, 7168, packed=True)
     assert hit and got == c2
+    got, hit = w8.resolve_config("Block_FP8", 32, 4608, 7168)       # other layout -> default
+    assert not hit and got == w8.default_config("Block_FP8", 32, 4608, 7168)
     got, hit = w8.resolve_config("Block_FP8", 16, 4608, 7168)       # miss -> default
     assert not hit and got == w8.default_config("Block_FP8", 16, 4608, 7168)
+    assert w8.best_layout("Block_FP8", 32, 4608, 7168) is True
+    assert w8.best_layout("FP8_Dynamic", 4, 4096, 4096) is False
     p = tmp_path / "t.tbl"
     w8.save_config_table(str(p))
     w8.clear_config_table()
@@ -163,18 +192,20 @@ def test_table_roundtrip_and_lookup(w8, tmp_path):
     w8.load_config_table(str(p))
     assert w8.config_table_size() == 2
     assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096) == c1
-    assert w8.lookup_config("Block_FP8", 32, 4608, 7168) == c2
+    assert w8.lookup_config("Block_FP8", 32, 4608, 7168, packed=True) == c2
 
 
 def test_table_malformed_keeps_old_table(w8, tmp_path):
     w8.set_config("W8A8_INT8", 16, 896, 1024, w8.Config.make(), 1.0)
     bad_files = [
-        "gfx950 1 W8A8_INT8 16 896 1024 16 4 2 1\n",                        # too few fields
-        "gfx950 1 INT4 16 896 1024 16 4 2 1 0 1.0\n",                       # unknown format
-        "gfx950 1 W8A8_INT8 16 896 1024 16 4 2 3 0 1.0\n",                  # split_k 3
-        "gfx950 1 W8A8_INT8 40 896 1024 16 4 2 1 0 1.0\n",                  # M above 32
-        "gfx950 1 W8A8_INT8 16 896 1024 16 4 x 1 0 1.0\n",                  # not an integer
-        "gfx950 1 W8A8_INT8 16 896 1024 16 4 2 1 0 fast\n",                 # bad time
+        "gfx950 1 W8A8_INT8 row 16 896 1024 16 4 2 1\n",                    # too few fields
+        "gfx950 1 INT4 row 16 896 1024 16 4 2 1 0 1.0\n",                   # unknown format
+        "gfx950 1 W8A8_INT8 tiled 16 896 1024 16 4 2 1 0 1.0\n",            # unknown layout
+        "gfx950 1 W8A8_INT8 row 16 896 1024 16 4 2 3 0 1.0\n",              # split_k 3
+        "gfx950 1 W8A8_INT8 row 40 896 1024 16 4 2 1 0 1.0\n",              # M above 32
+        "gfx950 1 W8A8_INT8 row 16 896 1024 16 4 x 1 0 1.0\n",              # not an integer
+        "gfx950 1 W8A8_INT8 row 16 896 1024 16 4 2 1 0 fast\n",             # bad time
+        "gfx950 1 W8A8_INT8 row 16 896 1024 64 4 2 1 0 1.0\n",              # tile 64 x unroll 2
     ]
     for i, text in enumerate(bad_files):
         p = tmp_path / f"bad{i}.tbl"
@@ -190,22 +221,22 @@ def test_table_malformed_keeps_old_table(w8, tmp_path):
 
 def test_table_foreign_entries_ignored_and_kept(w8, tmp_path):
     p = tmp_path / "mixed.tbl"
-    p.write_text("gfx942 1 FP8_Dynamic 4 4096 4096 64 2 4 1 1 2.0\n"
-                 "gfx950 9 FP8_Dynamic 4 4096 4096 64 2 4 1 1 2.0\n"
-                 "gfx950 1 FP8_Dynamic 4 4096 4096 32 2 4 4 0 2.5  # native\n")
+    p.write_text("gfx942 1 FP8_Dynamic row 4 4096 4096 64 2 4 1 1 2.0\n"
+                 "gfx950 9 FP8_Dynamic row 4 4096 4096 64 2 4 1 1 2.0\n"
+                 "gfx950 1 FP8_Dynamic row 4 4096 4096 32 2 2 4 0 2.5  # native\n")
     w8.load_config_table(str(p))
     assert w8.config_table_size() == 1 and w8.config_table_foreign() == 2
     assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096) == \
-        w8.Config.make(tile_n=32, waves_k=2, unroll=4, split_k=4, swap_ab=0)
+        w8.Config.make(tile_n=32, waves_k=2, unroll=2, split_k=4, swap_ab=0)
     q = tmp_path / "out.tbl"
     w8.save_config_table(str(q))
     text = q.read_text()
-    assert "gfx942 1 FP8_Dynamic" in text and "gfx950 9 FP8_Dynamic" in text
+    assert "gfx942 1 FP8_Dynamic row" in text and "gfx950 9 FP8_Dynamic row" in text
 
 
 def test_table_from_environment(tmp_path):
     p = tmp_path / "env.tbl"
-    p.write_text("gfx950 1 W8A8_INT8 16 896 1024 32 2 4 8 1 0.5\n")
+    p.write_text("gfx950 1 W8A8_INT8 row 16 896 1024 32 2 2 8 1 0.5\n")
     code = ("import bit_quantized_gemm_token_amd as w8;"
             "c = w8.lookup_config('W8A8_INT8', 16, 896, 1024);"
             "print(c.as_dict() if c else None)")
@@ -221,7 +252,7 @@ def test_table_from_environment(tmp_path):
 
 def test_env_table_loaded_by_the_c_library_alone(tmp_path):
     p = tmp_path / "env.tbl"
-    p.write_text("gfx950 1 W8A8_INT8 16 896 1024 32 2 4 8 1 0.5\n")
+    p.write_text("gfx950 1 W8A8_INT8 row 16 896 1024 32 2 2 8 1 0.5\n")
     from bit_quantized_gemm_token_amd import _capi
     # load _capi.py on its own (the package __init__ would load the shipped table)
     code = (
@@ -231,7 +262,7 @@ def test_env_table_loaded_by_the_c_library_alone(tmp_path):
         "spec.loader.exec_module(_capi)\n"
         "lib = _capi.load()\n"
         "c = _capi.Config()\n"
-        "print(lib.w8_lookup_config(1, 16, 896, 1024, ctypes.byref(c)), c.split_k, c.tile_n)\n")
+        "print(lib.w8_lookup_config(1, 16, 896, 1024, 0, ctypes.byref(c), None), c.split_k, c.tile_n)\n")
     env = dict(os.environ, W8_CONFIG_TABLE=str(p))
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                          check=True).stdout.split()

@@ -43,9 +43,9 @@ def case(fmt, M, N, K):
     return _cases[key]
 
 
-def acc_check(w8, cs, xq, sx, cfg, what=""):
+def acc_check(w8, cs, xq, sx, cfg, what="", packed=False):
     """Accumulator parity: int32 bit-exact, fp32 within the summation bound."""
-    acc = w8.gemm_w8a8_acc(cs.fmt, xq, sx, cs.wq, cs.sw, cfg=cfg)
+    acc = w8.gemm_w8a8_acc(cs.fmt, xq, sx, cs.weights(packed), cs.sw, cfg=cfg)
     torch.cuda.synchronize()
     got = acc.cpu().numpy()
     ref = cs.acc_ref()
@@ -57,8 +57,8 @@ def acc_check(w8, cs, xq, sx, cfg, what=""):
     return acc
 
 
-def full_path(w8, cs, cfg=None):
-    y = w8.linear(cs.fmt, cs.x, cs.wq, cs.sw, cfg=cfg)
+def full_path(w8, cs, cfg=None, packed=False):
+    y = w8.linear(cs.fmt, cs.x, cs.weights(packed), cs.sw, cfg=cfg)
     torch.cuda.synchronize()
     return y
 
@@ -80,12 +80,13 @@ def test_fp8_dynamic_4096(w8, M):
     cs = case("FP8_Dynamic", M, 4096, 4096)
     xq, sx = cs.gpu_act()
     cfgs = [None, w8.default_config("FP8_Dynamic", M, 4096, 4096),
-            C(w8, tile_n=64, waves_k=2, unroll=4, split_k=4, swap_ab=0),
-            C(w8, tile_n=32, waves_k=1, unroll=1, split_k=32, swap_ab=1),
-            C(w8, tile_n=16, waves_k=8, unroll=2, split_k=1, swap_ab=1)]
-    for cfg in cfgs:
-        acc_check(w8, cs, xq, sx, cfg, f"fp8 M={M} {cfg}")
-        assert_bf16_close(full_path(w8, cs, cfg), cs.Y, f"fp8 M={M} {cfg}")
+            C(w8, tile_n=64, waves_k=2, unroll=1, split_k=4, swap_ab=0),
+            C(w8, tile_n=32, waves_k=1, unroll=2, split_k=32, swap_ab=1),
+            C(w8, tile_n=16, waves_k=8, unroll=4, split_k=1, swap_ab=1)]
+    for packed in (False, True):
+        for cfg in cfgs:
+            acc_check(w8, cs, xq, sx, cfg, f"fp8 M={M} {cfg} packed={packed}", packed)
+            assert_bf16_close(full_path(w8, cs, cfg, packed), cs.Y, f"fp8 M={M} {cfg}")
 
 
 @pytest.mark.parametrize("M", [1, 8, 32])
@@ -99,6 +100,7 @@ def test_block_fp8_swap_on_and_off(w8, M):
     for swap in (0, 1):
         cfg = C(w8, tile_n=16, waves_k=4, unroll=2, split_k=2, swap_ab=swap)
         acc_check(w8, cs, xq, sx, cfg, f"block swap={swap}")
+        acc_check(w8, cs, xq, sx, cfg, f"block swap={swap} packed", packed=True)
         y = full_path(w8, cs, cfg)
         assert_bf16_close(y, cs.Y, f"block M={M} swap={swap}")
         outs.append(y.float().cpu().numpy())
@@ -116,24 +118,26 @@ def test_split_k_sweep_512x7168(w8, fmt, M):
         for swap in (0, 1):
             cfg = C(w8, tile_n=16, waves_k=2, unroll=2, split_k=s, swap_ab=swap)
             acc_check(w8, cs, xq, sx, cfg, f"{fmt} M={M} split_k={s} swap={swap}")
+            acc_check(w8, cs, xq, sx, cfg, f"{fmt} M={M} split_k={s} swap={swap} packed", True)
             assert_bf16_close(full_path(w8, cs, cfg), cs.Y, f"{fmt} M={M} split_k={s}")
 
 
 @pytest.mark.parametrize("fmt", ["W8A8_INT8", "FP8_Dynamic", "Block_FP8"])
 def test_every_tile_config(w8, fmt):
-    """Every (tile_n, waves_k, unroll, swap_ab) instance at one ragged shape."""
+    """Every (tile_n, waves_k, unroll, swap_ab, layout) instance at one ragged
+    shape (M = 17 needs both 16-row blocks of M), with and without split-K."""
     M, N, K = (17, 200, 1280)
     cs = case(fmt, M, N, K)
     xq, sx = cs.gpu_act()
     n = 0
-    for tn, wk, u, swap, s in itertools.product((16, 32, 64), (1, 2, 4, 8, 16), (1, 2, 4),
-                                                (0, 1), (1, 4)):
-        if (tn // 16) * wk > 16:
+    for tn, wk, u, swap, s, packed in itertools.product((16, 32, 64), (1, 2, 4, 8, 16),
+                                                        (1, 2, 4), (0, 1), (1, 4), (0, 1)):
+        if (tn // 16) * u > 4:
             continue
         cfg = C(w8, tile_n=tn, waves_k=wk, unroll=u, split_k=s, swap_ab=swap)
-        acc_check(w8, cs, xq, sx, cfg, f"{fmt} {cfg}")
+        acc_check(w8, cs, xq, sx, cfg, f"{fmt} {cfg} packed={packed}", bool(packed))
         n += 1
-    assert n == 2 * 2 * 3 * 12
+    assert n == 6 * 5 * 2 * 2 * 2
 
 
 @pytest.mark.parametrize("fmt,M,N,K", [
@@ -146,18 +150,50 @@ def test_ragged_shapes(w8, fmt, M, N, K):
     cs = case(fmt, M, N, K)
     xq, sx = cs.gpu_act()
     assert np.array_equal(u8(xq), cs.xq_ref)
-    for cfg in (None, C(w8, tile_n=32, waves_k=2, unroll=4, split_k=8, swap_ab=0),
-                C(w8, tile_n=64, waves_k=1, unroll=1, split_k=2, swap_ab=1)):
-        acc_check(w8, cs, xq, sx, cfg, f"ragged {cfg}")
-        assert_bf16_close(full_path(w8, cs, cfg), cs.Y, f"ragged {fmt} {cfg}")
+    for packed in (False, True):
+        for cfg in (None, C(w8, tile_n=32, waves_k=2, unroll=2, split_k=8, swap_ab=0),
+                    C(w8, tile_n=64, waves_k=1, unroll=1, split_k=2, swap_ab=1)):
+            acc_check(w8, cs, xq, sx, cfg, f"ragged {cfg} packed={packed}", packed)
+            assert_bf16_close(full_path(w8, cs, cfg, packed), cs.Y, f"ragged {fmt} {cfg}")
 
 
 @pytest.mark.parametrize("fmt", ["W8A8_INT8", "FP8_Dynamic", "Block_FP8"])
 @pytest.mark.parametrize("M,N,K", synthetic.SWEEP)
 def test_sweep_shapes_resolved_config(w8, fmt, M, N, K):
-    """The 24-shape sweep with the config the library resolves (table or default)."""
+    """The 24-shape sweep with the config the library resolves (table or
+    default), in both weight layouts."""
     cs = case(fmt, M, N, K)
     assert_bf16_close(full_path(w8, cs), cs.Y, f"sweep {fmt} {M}x{N}x{K}")
+    assert_bf16_close(full_path(w8, cs, packed=True), cs.Y, f"sweep packed {fmt} {M}x{N}x{K}")
+
+
+def _pack_reference(codes, kstep):
+    """The packed layout written out with numpy: fragment (row block, K-step)
+    of 16 x kstep bytes, load instruction jj at jj*1024, lane l's 16 bytes at
+    16*l = row 16*nb + l%16, bytes kstep*kk + 64*jj + 16*(l//16) .. +16."""
+    N, K = codes.shape
+    nblk, ks = -(-N // 16), -(-K // kstep)
+    padded = np.zeros((nblk * 16, ks * kstep), np.uint8)
+    padded[:N, :K] = codes
+    out = np.zeros((nblk, ks, kstep // 64, 64, 16), np.uint8)
+    for l in range(64):
+        r, g = l % 16, l // 16
+        for jj in range(kstep // 64):
+            cols = np.arange(ks)[:, None] * kstep + 64 * jj + 16 * g + np.arange(16)[None, :]
+            out[:, :, jj, l, :] = padded.reshape(nblk, 16, -1)[:, r, :][:, cols]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("fmt,N,K", [("W8A8_INT8", 200, 208), ("FP8_Dynamic", 37, 400),
+                                     ("Block_FP8", 130, 384), ("W8A8_INT8", 512, 7168)])
+def test_pack_weight_layout(w8, fmt, N, K):
+    rng = np.random.default_rng(N + K)
+    codes = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    got = w8.pack_weight(fmt, torch.from_numpy(codes).to(DEV)).data.cpu().numpy()
+    kstep = 64 if fmt == "W8A8_INT8" else 128
+    assert got.size == w8.packed_weight_size(fmt, N, K)
+    assert np.array_equal(got, _pack_reference(codes, kstep))
 
 
 # ------------------------------------------------ properties of the path --
@@ -168,12 +204,14 @@ def test_split_k_deterministic_and_counters_reset(w8):
     ws = w8.Workspace(DEV)
     need = w8.workspace_size("FP8_Dynamic", 8, 1024, 4096, cfg)
     ys = [w8.gemm_w8a8("FP8_Dynamic", xq, sx, cs.wq, cs.sw, cfg=cfg, workspace=ws) for _ in range(3)]
+    ys += [w8.gemm_w8a8("FP8_Dynamic", xq, sx, cs.packed(), cs.sw, cfg=cfg, workspace=ws)
+           for _ in range(2)]
     torch.cuda.synchronize()
     for y in ys[1:]:
         assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
     ntiles = 1024 // 16
-    assert need > ntiles * 4
-    assert (ws.buf[:ntiles * 4].cpu() == 0).all()
+    assert need > 65536
+    assert (ws.buf[:65536].cpu() == 0).all()
 
 
 def test_unsupported_m_raises(w8):
@@ -192,18 +230,19 @@ def test_graph_capture_replay(w8):
     cs = case("Block_FP8", 8, 4608, 7168)
     cfg = C(w8, tile_n=16, waves_k=4, unroll=2, split_k=8, swap_ab=1)
     ws = w8.Workspace(DEV, w8.workspace_size("Block_FP8", 8, 4608, 7168, cfg))
-    eager = w8.linear("Block_FP8", cs.x, cs.wq, cs.sw, cfg=cfg, workspace=ws).clone()
+    wp = cs.packed()
+    eager = w8.linear("Block_FP8", cs.x, wp, cs.sw, cfg=cfg, workspace=ws).clone()
     x_static = cs.x.clone()
     y_static = torch.empty_like(eager)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        w8.linear("Block_FP8", x_static, cs.wq, cs.sw, cfg=cfg, y=y_static, workspace=ws)
+        w8.linear("Block_FP8", x_static, wp, cs.sw, cfg=cfg, y=y_static, workspace=ws)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        w8.linear("Block_FP8", x_static, cs.wq, cs.sw, cfg=cfg, y=y_static, workspace=ws)
+        w8.linear("Block_FP8", x_static, wp, cs.sw, cfg=cfg, y=y_static, workspace=ws)
     for i in range(4):
         y_static.zero_()
         g.replay()

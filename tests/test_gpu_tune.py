@@ -26,28 +26,31 @@ def _restore_table(w8):
     w8.load_default_table()
 
 
-@pytest.mark.parametrize("fmt,M,N,K", [("W8A8_INT8", 16, 896, 1024), ("FP8_Dynamic", 4, 512, 2048),
-                                       ("Block_FP8", 8, 512, 1024)])
-def test_tune_shape(w8, fmt, M, N, K, tmp_path):
-    print(f"[tune] {fmt} M={M} N={N} K={K}", flush=True)
+@pytest.mark.parametrize("fmt,M,N,K,packed", [("W8A8_INT8", 16, 896, 1024, False),
+                                              ("FP8_Dynamic", 4, 512, 2048, True),
+                                              ("Block_FP8", 8, 512, 1024, False),
+                                              ("Block_FP8", 8, 512, 1024, True)])
+def test_tune_shape(w8, fmt, M, N, K, packed, tmp_path):
+    print(f"[tune] {fmt} M={M} N={N} K={K} packed={packed}", flush=True)
     w8.clear_config_table()
-    best, st = w8.tune_shape(fmt, M, N, K, **SMALL)
+    best, st = w8.tune_shape(fmt, M, N, K, packed=packed, **SMALL)
     print(f"[tune] best {best} stats {st}", flush=True)
     w8.validate_config(fmt, M, N, K, best)
     assert st["candidates"] > 50 and st["validated"] == st["candidates"] and st["rejected"] == 0
     assert best.split_k <= 8
     assert st["best_us_bank2"] > 0 and st["best_gbps"] > 0
     assert st["best_us_bank2"] <= st["default_us_bank2"] * 1.10
-    assert w8.lookup_config(fmt, M, N, K) == best
-    cfg, hit = w8.resolve_config(fmt, M, N, K)
+    assert w8.lookup_config(fmt, M, N, K, packed=packed) == best
+    assert w8.lookup_config(fmt, M, N, K, packed=not packed) is None
+    cfg, hit = w8.resolve_config(fmt, M, N, K, packed=packed)
     assert hit and cfg == best
     p = tmp_path / "tuned.tbl"
     w8.save_config_table(str(p))
     w8.clear_config_table()
     w8.load_config_table(str(p))
-    assert w8.lookup_config(fmt, M, N, K) == best
+    assert w8.lookup_config(fmt, M, N, K, packed=packed) == best
     cs = Case(fmt, M, N, K)
-    y = w8.linear(fmt, cs.x, cs.wq, cs.sw)            # resolves the tuned entry
+    y = w8.linear(fmt, cs.x, cs.weights(packed), cs.sw)   # resolves the tuned entry
     torch.cuda.synchronize()
     assert_bf16_close(y, cs.Y, f"tuned {fmt}")
 
