@@ -43,6 +43,127 @@ sys.path.insert(0, ROOT)
 import synthetic  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+PMC_FILE = os.path.join(ROOT, "profiles", "gemm_sweep72_hbm_counters.json")
+KERNEL_SOURCES = ("w8_gemm.hpp", "w8_device.hpp", "w8_gemm_inst.hip", "w8_launch.hpp")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bit_quantized_gemm_token_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, problems):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    runs (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, each scaled by what
+    the same counter reads for a plain copy of known size), weighted over
+    `problems` like the achieved rate.  None when the counter file is missing,
+    was taken from other kernel sources, or lacks any of these problems with
+    the same config and layout."""
+    try:
+        with open(PMC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    rows = {(r["fmt"], r["M"], r["N"], r["K"], r["layout"], json.dumps(r["cfg"], sort_keys=True)): r
+            for r in d.get("problems", [])}
+    total = launches = 0.0
+    for p in problems:
+        r = rows.get((p.fmt, p.M, p.N, p.K, "packed" if p.packed else "row",
+                      json.dumps(p.cfg.as_dict(), sort_keys=True)))
+        if r is None or r.get("kernel") != kernel:
+            return None
+        total += (r["fetch_kib"] * d["fetch_scale"] + r["write_kib"] * d["write_scale"]) * 1024 * p.R
+        launches += p.R
+    return round(total / launches) if launches else None
+
+
+def counter_pass(problems, w8, manifest_path, copy_mib, launches=2):
+    """Launches for a rocprofv3 --pmc run: each problem's GEMM `launches` times,
+    each on another weight copy, then a plain device copy of `copy_mib` MiB
+    (float32 negation: it reads and writes exactly that many bytes) three
+    times; every launch is followed by a device synchronization, so dispatches
+    never queue up under the profiler.  The dispatch order is written to
+    `manifest_path` for ingest_counters()."""
+    order = []
+    for i, p in enumerate(problems):
+        for r in range(launches):
+            w8.gemm_w8a8(p.fmt, p.xq, p.sx, p.weights[r % p.R], p.sw, cfg=p.cfg, y=p.y,
+                         workspace=p.ws)
+            torch.cuda.synchronize()
+            order.append(i)
+    n = (copy_mib << 20) // 4
+    src = torch.zeros(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+    manifest = {"problems": [{"fmt": p.fmt, "M": p.M, "N": p.N, "K": p.K,
+                              "layout": "packed" if p.packed else "row", "cfg": p.cfg.as_dict(),
+                              "kernel": p.kernel} for p in problems],
+                "gemm_dispatch_order": order, "copy_bytes_read": n * 4, "copy_bytes_written": n * 4,
+                "copies": 3, "source_hash": kernel_source_hash()}
+    with open(manifest_path, "w") as f:
+        json.dump(manifest, f)
+    log(f"[bench] counter pass: {len(order)} GEMM dispatches, 3 copies of {copy_mib} MiB; "
+        f"manifest {manifest_path}")
+
+
+def _read_counter_csv(path, counter):
+    """Per-dispatch values of `counter` from a rocprofv3 counter-collection
+    CSV, in dispatch order: [(kernel_name, value)]."""
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") != counter:
+                continue
+            rows.append((int(r.get("Dispatch_Id") or r.get("Correlation_Id") or 0),
+                         r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort(key=lambda t: t[0])
+    return [(k, v) for _, k, v in rows]
+
+
+def ingest_counters(manifest_path, fetch_csv, write_csv, out_path, command):
+    """Turns the two counter runs into the per-problem HBM traffic file read
+    by measured_traffic()."""
+    with open(manifest_path) as f:
+        man = json.load(f)
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _read_counter_csv(path, counter)
+        gemm = [v for k, v in rows if "gemm_kernel<" in k]
+        copy = [v for k, v in rows if "neg" in k]
+        if len(gemm) != len(man["gemm_dispatch_order"]) or len(copy) != man["copies"]:
+            raise SystemExit(f"{path}: {len(gemm)} GEMM and {len(copy)} copy dispatches, expected "
+                             f"{len(man['gemm_dispatch_order'])} and {man['copies']}")
+        per = {}
+        for i, v in zip(man["gemm_dispatch_order"], gemm):
+            per.setdefault(i, []).append(v)
+        nbytes = man["copy_bytes_read"] if counter == "FETCH_SIZE" else man["copy_bytes_written"]
+        copy_kib = sorted(copy)[len(copy) // 2]
+        res[counter] = (per, nbytes / (copy_kib * 1024), copy_kib)
+    fetch, fscale, fcopy = res["FETCH_SIZE"]
+    write, wscale, wcopy = res["WRITE_SIZE"]
+    probs = []
+    for i, p in enumerate(man["problems"]):
+        row = dict(p)
+        row["fetch_kib"] = round(sum(fetch[i]) / len(fetch[i]), 3)
+        row["write_kib"] = round(sum(write[i]) / len(write[i]), 3)
+        probs.append(row)
+    out = {"source_hash": man["source_hash"], "fetch_scale": round(fscale, 5),
+           "write_scale": round(wscale, 5), "copy_fetch_kib": fcopy, "copy_write_kib": wcopy,
+           "copy_bytes": man["copy_bytes_read"], "command": command, "problems": probs}
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    log(f"[bench] wrote {out_path}: fetch scale {fscale:.4f}, write scale {wscale:.4f}, "
+        f"{len(probs)} problems")
 
 
 def parse():
@@ -56,6 +177,17 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--table", default=None, help="config table to load instead of the shipped one")
     p.add_argument("--report", default=None, help="write per-problem results (JSON) here")
+    p.add_argument("--counter-pass", default=None, metavar="MANIFEST",
+                   help="instead of timing, make the launches for a rocprofv3 --pmc run and "
+                        "write their order to MANIFEST")
+    p.add_argument("--copy-calibration-mib", type=int, default=256,
+                   help="size of the plain device copy in a counter pass")
+    p.add_argument("--ingest-counters", nargs=3, default=None,
+                   metavar=("MANIFEST", "FETCH_CSV", "WRITE_CSV"),
+                   help="write the HBM counter file from a counter pass's manifest and the "
+                        "FETCH_SIZE and WRITE_SIZE counter-collection CSVs, then exit")
+    p.add_argument("--ingest-command", default="",
+                   help="the commands that made the counter runs, recorded with them")
     return p.parse_args()
 
 
@@ -99,18 +231,24 @@ class Problem:
         self.kernel = (f"gemm_kernel<{w8.FORMATS[fmt]}, {mb}, {c.tile_n // 16}, {c.waves_k}, "
                        f"{c.unroll}, {c.swap_ab}, {int(self.packed)}>")
 
+    def run_gemm(self, w8):
+        for r in range(self.R):
+            w8.gemm_w8a8(self.fmt, self.xq, self.sx, self.weights[r], self.sw, cfg=self.cfg,
+                         y=self.y, workspace=self.ws)
+
+    def run_path(self, w8):
+        for r in range(self.R):
+            xq, sx = w8.quantize_act(self.fmt, self.x, xq=self.xq, sx=self.sx)
+            w8.gemm_w8a8(self.fmt, xq, sx, self.weights[r], self.sw, cfg=self.cfg, y=self.y,
+                         workspace=self.ws)
+
     def capture(self, w8, stream):
         self.g_gemm = torch.cuda.CUDAGraph()
         self.g_path = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.g_gemm, stream=stream):
-            for r in range(self.R):
-                w8.gemm_w8a8(self.fmt, self.xq, self.sx, self.weights[r], self.sw, cfg=self.cfg,
-                             y=self.y, workspace=self.ws)
+            self.run_gemm(w8)
         with torch.cuda.graph(self.g_path, stream=stream):
-            for r in range(self.R):
-                xq, sx = w8.quantize_act(self.fmt, self.x, xq=self.xq, sx=self.sx)
-                w8.gemm_w8a8(self.fmt, xq, sx, self.weights[r], self.sw, cfg=self.cfg, y=self.y,
-                             workspace=self.ws)
+            self.run_path(w8)
 
 
 def geomean(v):
@@ -119,41 +257,56 @@ def geomean(v):
 
 
 def cpu_baseline(problems, budget_s):
-    """The oracle on a bounded sample of the problems, timed on the host."""
+    """The oracle, timed on the host: passes over the problems (quantize + GEMM
+    of each) until `budget_s` seconds of oracle time are spent; per problem the
+    fastest run counts."""
     import oracle
     oracle._load()
-    gbps, done, t_total = [], [], 0.0
+    inputs = []
     for p in problems:
-        if t_total >= budget_s:
-            break
         x_bits = synthetic.activations(p.fmt, p.M, p.N, p.K)
         if p.fmt == "W8A8_INT8":
             wq, sw = synthetic.int8_weights(p.fmt, p.M, p.N, p.K)
             wq = wq.view(np.uint8)
         else:
             wq, sw = oracle.quantize_weight(p.fmt, synthetic.fp32_weights(p.fmt, p.M, p.N, p.K))
-        t0 = time.perf_counter()
-        Y, _, _ = oracle.forward(p.fmt, x_bits, wq, sw)
-        dt = time.perf_counter() - t0
-        t_total += dt
-        gbps.append(p.bytes / (dt * 1e9))
-        # refcheck: the GPU output of this problem against the oracle
-        got = p.y_check.float().cpu().numpy().astype(np.float64)
-        p.refcheck = bool((np.abs(got - Y) <= 1e-2 + 1e-2 * np.abs(Y)).all())
-        done.append(p)
+        inputs.append((x_bits, wq, sw))
+    best = [math.inf] * len(problems)
+    done, t_total, passes = set(), 0.0, 0
+    while t_total < budget_s and (passes == 0 or len(done) == len(problems)):
+        for i, (p, (x_bits, wq, sw)) in enumerate(zip(problems, inputs)):
+            if t_total >= budget_s and passes > 0:
+                break
+            t0 = time.perf_counter()
+            Y, _, _ = oracle.forward(p.fmt, x_bits, wq, sw)
+            dt = time.perf_counter() - t0
+            t_total += dt
+            best[i] = min(best[i], dt)
+            if i not in done:
+                # refcheck: the GPU output of this problem against the oracle
+                got = p.y_check.float().cpu().numpy().astype(np.float64)
+                p.refcheck = bool((np.abs(got - Y) <= 1e-2 + 1e-2 * np.abs(Y)).all())
+                done.add(i)
+        passes += 1
+    checked = [problems[i] for i in sorted(done)]
+    gbps = [problems[i].bytes / (best[i] * 1e9) for i in sorted(done)]
     return {
         "value": round(geomean(gbps), 4),
         "unit": "GB/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": (f"{len(done)} of {len(problems)} problems in sweep order "
-                   f"({', '.join(sorted(set(p.fmt for p in done)))}), quantize + GEMM, one run "
-                   f"each, {t_total:.1f} s of CPU work; geomean of algorithmic bytes / time"),
-    }, done
+        "sample": (f"{len(checked)} of {len(problems)} problems "
+                   f"({', '.join(sorted(set(p.fmt for p in checked)))}), quantize + GEMM, "
+                   f"{passes} passes in {t_total:.1f} s of CPU work, fastest run per problem; "
+                   f"geomean of algorithmic bytes / time"),
+    }, checked
 
 
 def main():
     args = parse()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters, PMC_FILE, args.ingest_command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested). Run with --gpus 1.", file=sys.stderr)
@@ -175,6 +328,9 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] {len(problems)} problems set up in {time.time() - t0:.1f} s "
         f"({sum(p.from_table for p in problems)} configs from the table)")
+    if args.counter_pass:
+        counter_pass(problems, w8, args.counter_pass, args.copy_calibration_mib)
+        return
     stream = torch.cuda.Stream(dev)
     t0 = time.time()
     for p in problems:
@@ -228,7 +384,8 @@ def main():
     by_kernel = {}
     for p in problems:
         by_kernel.setdefault(p.kernel, []).append(p)
-    dom = max(by_kernel, key=lambda k: sum(p.us_gemm for p in by_kernel[k]))
+    # the instance with the largest share of the timed GEMM work (launches x time)
+    dom = max(by_kernel, key=lambda k: sum(p.us_gemm * p.R for p in by_kernel[k]))
     dp = by_kernel[dom]
     launches = sum(p.R for p in dp)
     achieved = sum(p.bytes * p.R for p in dp) / sum(p.us_gemm * 1e3 * p.R for p in dp)
@@ -242,7 +399,7 @@ def main():
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
         "avg_launch_us": round(sum(p.us_gemm * p.R for p in dp) / launches, 4),
         "bytes_per_launch": round(sum(p.bytes * p.R for p in dp) / launches),
-        "traffic": None,
+        "traffic": measured_traffic(dom, dp),
     }
 
     cpu = None
