@@ -111,6 +111,10 @@ w8_status check_cfg(int fmt, int M, int N, int K, const w8_cfg& c) {
     return fail(W8_E_INVALID, "split_k > 1 supports at most " + std::to_string(kSplitKMaxTiles) +
                                   " output tiles (N <= " +
                                   std::to_string(kSplitKMaxTiles * c.tile_n) + ")");
+  // one-dimensional grid: the launch's total thread count must fit in 32 bits
+  const long long threads = (long long)((N + c.tile_n - 1) / c.tile_n) * c.split_k * 64 * c.waves_k;
+  if (threads > 0xFFFFFFFFLL)
+    return fail(W8_E_INVALID, "cfg: (tiles x split_k x waves_k x 64) threads exceed 2^32 - 1");
   return W8_OK;
 }
 
@@ -185,6 +189,7 @@ w8_status launch_gemm_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
   a.ksteps = ksteps_of(g.fmt, g.K);
   a.kfull = g.K / kstep_of(g.fmt);
   a.split_k = c.split_k;
+  a.split_shift = __builtin_ctz((unsigned)c.split_k);
   a.ntiles = ntiles;
   a.sgroups = g.fmt == W8_BLOCK_FP8 ? g.K / W8_GROUP : 0;
   a.out_mode = g.out_mode;
@@ -194,7 +199,7 @@ w8_status launch_gemm_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
     a.counters = static_cast<unsigned int*>(g.ws);
     a.part = static_cast<char*>(g.ws) + ws_counter_bytes(ntiles);
   }
-  hipError_t e = fn(a, dim3(ntiles, c.split_k), dim3(64 * c.waves_k), s);
+  hipError_t e = fn(a, dim3(ntiles * c.split_k), dim3(64 * c.waves_k), s);
   if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("GEMM launch", e));
   return W8_OK;
 }

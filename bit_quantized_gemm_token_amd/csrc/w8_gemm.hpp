@@ -6,7 +6,11 @@
 // to 256; the search also covers memory layout.  Here they are template and
 // launch parameters of one kernel:
 //
-//   grid   (ceil(N / (16*NB)), split_k); block 64*WK threads.
+//   grid   ceil(N / (16*NB)) * split_k workgroups of 64*WK threads; the
+//          split index varies fastest.  Workgroups are dealt round-robin to
+//          the 8 XCDs, each with its own L2, so with split_k a power of two
+//          an XCD sees only split_k/8 K ranges (split_k >= 8) or one (split_k
+//          < 8), and fetches only those activation columns instead of all K.
 //   wave   wk owns the workgroup's NB blocks of 16 weight rows
 //          (n0 = tile*16*NB) over the wk-th slice of the workgroup's K range.
 //   K loop one MFMA per K-step and row block (64 bytes of K for int8, 128 for
@@ -139,7 +143,8 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(GemmArgs a) {
   const int lane = threadIdx.x & 63;
   const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
-  const int tile = blockIdx.x, split = blockIdx.y;
+  const int split = (int)(blockIdx.x & (unsigned)(a.split_k - 1));
+  const int tile = (int)(blockIdx.x >> a.split_shift);
   const int n0 = tile * 16 * NB;
 
   // Weight pointers of the NB row blocks (clamped for the ragged N tile).

@@ -44,6 +44,7 @@ struct GemmArgs {
   int ksteps;    // K-steps in total: ceil(K / KSTEP)
   int kfull;     // K-steps with no ragged tail: K / KSTEP
   int split_k;
+  int split_shift;  // log2(split_k)
   int ntiles;    // output tiles along N
   int sgroups;   // Block_FP8: K / 128 (row stride of sx and sw)
   int out_mode;  // 0: bf16 Y; 1: raw accumulators

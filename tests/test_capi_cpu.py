@@ -96,6 +96,16 @@ def test_config_rejects_abi_and_reserved(w8):
     assert _valid(w8, "FP8_Dynamic", 4, 512, 1024, w8.Config.make(tile_n=64, unroll=1, waves_k=16))
 
 
+def test_config_rejects_grid_overflow(w8):
+    # 16384 tiles x 256 splits x 16 waves x 64 lanes = 2^32 threads: one more
+    # than a launch can hold; half the waves fit
+    big = w8.Config.make(tile_n=64, unroll=1, waves_k=16, split_k=256)
+    with pytest.raises(w8.W8Error, match="2\\^32"):
+        w8.validate_config("FP8_Dynamic", 1, 16384 * 64, 1 << 20, big)
+    assert _valid(w8, "FP8_Dynamic", 1, 16384 * 64, 1 << 20,
+                  w8.Config.make(tile_n=64, unroll=1, waves_k=8, split_k=256))
+
+
 def test_default_config_is_valid_everywhere(w8):
     import synthetic
     for fmt in w8.FORMATS:
