@@ -229,7 +229,7 @@ class Problem:
         mb = (M + 15) // 16
         c = self.cfg
         self.kernel = (f"gemm_kernel<{w8.FORMATS[fmt]}, {mb}, {c.tile_n // 16}, {c.waves_k}, "
-                       f"{c.unroll}, {c.swap_ab}, {int(self.packed)}>")
+                       f"{c.waves_n}, {c.unroll}, {c.swap_ab}, {int(self.packed)}, {c.x_lds}>")
 
     def run_gemm(self, w8):
         for r in range(self.R):

@@ -5,7 +5,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw8gemm.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 MAX_M = 32
 MAX_SPLIT_K = 256
 GROUP = 128
@@ -30,15 +30,20 @@ EXPORTS = ("w8_abi_version", "w8_status_string", "w8_last_error", "w8_quantize_a
 class Config(ctypes.Structure):
     """w8_cfg: one configuration of the GEMM family."""
     _fields_ = [("abi_version", ctypes.c_int32), ("tile_n", ctypes.c_int32),
-                ("waves_k", ctypes.c_int32), ("unroll", ctypes.c_int32),
-                ("split_k", ctypes.c_int32), ("swap_ab", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 2)]
+                ("waves_k", ctypes.c_int32), ("waves_n", ctypes.c_int32),
+                ("unroll", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("grid", ctypes.c_int32), ("swap_ab", ctypes.c_int32),
+                ("x_lds", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
 
-    KEYS = ("tile_n", "waves_k", "unroll", "split_k", "swap_ab")
+    KEYS = ("tile_n", "waves_k", "waves_n", "unroll", "split_k", "grid", "swap_ab", "x_lds")
 
     @classmethod
-    def make(cls, tile_n=16, waves_k=4, unroll=2, split_k=1, swap_ab=0):
-        return cls(ABI_VERSION, tile_n, waves_k, unroll, split_k, int(swap_ab))
+    def make(cls, tile_n=16, waves_k=4, unroll=2, split_k=1, swap_ab=0, waves_n=1, grid=0,
+             x_lds=None):
+        if x_lds is None:
+            x_lds = 1 if waves_n > 1 else 0
+        return cls(ABI_VERSION, tile_n, waves_k, waves_n, unroll, split_k, grid, int(swap_ab),
+                   int(x_lds))
 
     def as_dict(self):
         return {k: int(getattr(self, k)) for k in self.KEYS}

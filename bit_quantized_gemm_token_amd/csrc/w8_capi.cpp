@@ -1,6 +1,7 @@
 // C-ABI of the w8gemm library: argument validation, config resolution and
 // kernel dispatch.  Nothing here allocates, frees or synchronizes on the
 // quantize / GEMM path, so both can be captured into a HIP graph.
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -23,18 +24,19 @@ int nb_index(int nb) { return nb == 1 ? 0 : nb == 2 ? 1 : nb == 4 ? 2 : -1; }
 int wk_index(int wk) {
   return wk == 1 ? 0 : wk == 2 ? 1 : wk == 4 ? 2 : wk == 8 ? 3 : wk == 16 ? 4 : -1;
 }
+int wn_index(int wn) { return wn == 1 ? 0 : wn == 2 ? 1 : wn == 4 ? 2 : wn == 8 ? 3 : -1; }
 int u_index(int u) { return u == 1 ? 0 : u == 2 ? 1 : u == 4 ? 2 : -1; }
 
-// [fmt][mb-1][nb][wk][unroll][swap][packed] -> launcher
+// [fmt][mb-1][nb][wk][wn][unroll][swap][packed][xl] -> launcher
 struct InstanceIndex {
-  GemmLaunchFn fn[3][2][3][5][3][2][2] = {};
+  GemmLaunchFn fn[3][2][3][5][4][3][2][2][2] = {};
   InstanceIndex() {
     int n = 0;
     const GemmInstance* p = gemm_instances(&n);
     for (int i = 0; i < n; ++i) {
       const GemmInstance& g = p[i];
-      fn[g.fmt][g.mb - 1][nb_index(g.nb)][wk_index(g.wk)][u_index(g.unroll)][g.swap][g.packed] =
-          g.fn;
+      fn[g.fmt][g.mb - 1][nb_index(g.nb)][wk_index(g.wk)][wn_index(g.wn)][u_index(g.unroll)]
+        [g.swap][g.packed][g.xl] = g.fn;
     }
   }
 };
@@ -100,6 +102,12 @@ w8_status check_cfg(int fmt, int M, int N, int K, const w8_cfg& c) {
   if (nb_index(c.tile_n / 16) < 0 || c.tile_n % 16)
     return fail(W8_E_INVALID, "cfg.tile_n must be 16, 32 or 64");
   if (wk_index(c.waves_k) < 0) return fail(W8_E_INVALID, "cfg.waves_k must be 1, 2, 4, 8 or 16");
+  if (wn_index(c.waves_n) < 0) return fail(W8_E_INVALID, "cfg.waves_n must be 1, 2, 4 or 8");
+  if (c.waves_n > 1 && c.waves_k != 1)
+    return fail(W8_E_INVALID, "cfg: waves_n > 1 needs waves_k == 1");
+  if (c.x_lds != 0 && c.x_lds != 1) return fail(W8_E_INVALID, "cfg.x_lds must be 0 or 1");
+  if (c.waves_n > 1 && !c.x_lds) return fail(W8_E_INVALID, "cfg: waves_n > 1 needs x_lds == 1");
+  if (c.x_lds && c.waves_k > 8) return fail(W8_E_INVALID, "cfg: x_lds needs waves_k <= 8");
   if (u_index(c.unroll) < 0) return fail(W8_E_INVALID, "cfg.unroll must be 1, 2 or 4");
   if ((c.tile_n / 16) * c.unroll > 4)
     return fail(W8_E_INVALID, "cfg: tile_n/16 * unroll must be at most 4");
@@ -107,23 +115,54 @@ w8_status check_cfg(int fmt, int M, int N, int K, const w8_cfg& c) {
     return fail(W8_E_INVALID, "cfg.split_k must be a power of two in [1, 256], got " +
                                   std::to_string(c.split_k));
   if (c.swap_ab != 0 && c.swap_ab != 1) return fail(W8_E_INVALID, "cfg.swap_ab must be 0 or 1");
-  if (c.split_k > 1 && (N + c.tile_n - 1) / c.tile_n > kSplitKMaxTiles)
-    return fail(W8_E_INVALID, "split_k > 1 supports at most " + std::to_string(kSplitKMaxTiles) +
-                                  " output tiles (N <= " +
-                                  std::to_string(kSplitKMaxTiles * c.tile_n) + ")");
+  const long long ntiles = tiles_of(N, c);
+  const long long iters = ntiles * ksteps_of(fmt, K);
+  if (c.grid < 0) return fail(W8_E_INVALID, "cfg.grid must be >= 0");
+  if (c.grid > 0) {
+    if (c.split_k != 1) return fail(W8_E_INVALID, "cfg: stream-K (grid > 0) needs split_k == 1");
+    if (c.grid > iters)
+      return fail(W8_E_INVALID, "cfg.grid " + std::to_string(c.grid) +
+                                    " exceeds the (tile, K-step) iterations (" +
+                                    std::to_string(iters) + ")");
+  }
+  if (c.x_lds) {
+    const long long ks = ksteps_of(fmt, K);
+    const long long seg = c.grid > 0 ? std::min(ks, (iters + c.grid - 1) / c.grid)
+                                     : (ks + c.split_k - 1) / c.split_k;
+    const long long chunks = seg * ((M + 15) / 16) * (kstep_of(fmt) / 64);
+    if (chunks > kXlChunks)
+      return fail(W8_E_INVALID, "cfg: x_lds needs the activations of a workgroup's K range in "
+                                "64 KiB (" + std::to_string(chunks) + " KiB here)");
+  }
+  if ((c.split_k > 1 || c.grid > 0) && ntiles > kSplitKMaxTiles)
+    return fail(W8_E_INVALID, "split_k > 1 and grid > 0 support at most " +
+                                  std::to_string(kSplitKMaxTiles) + " output tiles (N <= " +
+                                  std::to_string((long long)kSplitKMaxTiles * c.tile_n * c.waves_n) +
+                                  ")");
   // one-dimensional grid: the launch's total thread count must fit in 32 bits
-  const long long threads = (long long)((N + c.tile_n - 1) / c.tile_n) * c.split_k * 64 * c.waves_k;
+  const long long wgs = c.grid > 0 ? c.grid : ntiles * c.split_k;
+  const long long threads = wgs * 64 * c.waves_k * c.waves_n;
   if (threads > 0xFFFFFFFFLL)
-    return fail(W8_E_INVALID, "cfg: (tiles x split_k x waves_k x 64) threads exceed 2^32 - 1");
+    return fail(W8_E_INVALID, "cfg: (workgroups x waves x 64) threads exceed 2^32 - 1");
   return W8_OK;
 }
 
-size_t workspace_bytes(int fmt, int M, int N, const w8_cfg& c) {
-  (void)fmt;
-  if (c.split_k <= 1) return 0;
-  const int ntiles = (N + c.tile_n - 1) / c.tile_n;
+int tiles_of(int N, const w8_cfg& c) {
+  const int cols = c.tile_n * c.waves_n;
+  return (N + cols - 1) / cols;
+}
+
+int partial_slots(int fmt, int N, int K, const w8_cfg& c) {
+  if (c.grid > 0) return stream_k_slots(tiles_of(N, c), ksteps_of(fmt, K), c.grid);
+  return c.split_k;
+}
+
+size_t workspace_bytes(int fmt, int M, int N, int K, const w8_cfg& c) {
+  if (c.split_k <= 1 && c.grid <= 0) return 0;
+  const int ntiles = tiles_of(N, c);
   const int mb = (M + 15) / 16;
-  return ws_counter_bytes(ntiles) + ws_partial_bytes(ntiles, c.split_k, c.tile_n / 16, mb);
+  return ws_counter_bytes(ntiles) + ws_partial_bytes(ntiles, partial_slots(fmt, N, K, c),
+                                                     c.waves_n * c.tile_n / 16, mb);
 }
 
 // Default config (used when the table has no entry for the shape).  It
@@ -137,6 +176,7 @@ w8_cfg make_default_cfg(int fmt, int M, int N, int K) {
   c.abi_version = W8_ABI_VERSION;
   c.tile_n = 16;
   c.waves_k = 4;
+  c.waves_n = 1;
   c.unroll = 2;
   c.swap_ab = M < 32 ? 1 : 0;
   const int ntiles = (N + 15) / 16;
@@ -170,10 +210,11 @@ w8_status check_device() {
 w8_status launch_gemm_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
   const int mb = (g.M + 15) / 16;
   const int nb = c.tile_n / 16;
-  GemmLaunchFn fn = instance_index().fn[g.fmt][mb - 1][nb_index(nb)][wk_index(c.waves_k)]
-                                         [u_index(c.unroll)][c.swap_ab][g.packed ? 1 : 0];
+  GemmLaunchFn fn =
+      instance_index().fn[g.fmt][mb - 1][nb_index(nb)][wk_index(c.waves_k)][wn_index(c.waves_n)]
+                         [u_index(c.unroll)][c.swap_ab][g.packed ? 1 : 0][c.x_lds];
   if (!fn) return fail(W8_E_INVALID, "no compiled kernel for this config");
-  const int ntiles = (g.N + c.tile_n - 1) / c.tile_n;
+  const int ntiles = tiles_of(g.N, c);
   GemmArgs a;
   a.xq = static_cast<const uint8_t*>(g.xq);
   a.sx = g.sx;
@@ -190,16 +231,19 @@ w8_status launch_gemm_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
   a.kfull = g.K / kstep_of(g.fmt);
   a.split_k = c.split_k;
   a.split_shift = __builtin_ctz((unsigned)c.split_k);
+  a.grid = c.grid;
+  a.slots = partial_slots(g.fmt, g.N, g.K, c);
   a.ntiles = ntiles;
   a.sgroups = g.fmt == W8_BLOCK_FP8 ? g.K / W8_GROUP : 0;
   a.out_mode = g.out_mode;
   a.counters = nullptr;
   a.part = nullptr;
-  if (c.split_k > 1) {
+  if (c.split_k > 1 || c.grid > 0) {
     a.counters = static_cast<unsigned int*>(g.ws);
     a.part = static_cast<char*>(g.ws) + ws_counter_bytes(ntiles);
   }
-  hipError_t e = fn(a, dim3(ntiles * c.split_k), dim3(64 * c.waves_k), s);
+  const unsigned wgs = c.grid > 0 ? (unsigned)c.grid : (unsigned)(ntiles * c.split_k);
+  hipError_t e = fn(a, dim3(wgs), dim3(64 * c.waves_k * c.waves_n), s);
   if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("GEMM launch", e));
   return W8_OK;
 }
@@ -235,7 +279,7 @@ w8_status gemm_entry(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ld
   } else {
     c = resolve_cfg(fmt, M, N, K, packed, nullptr);
   }
-  const size_t need = workspace_bytes(fmt, M, N, c);
+  const size_t need = workspace_bytes(fmt, M, N, K, c);
   if (need > 0) {
     if (!ws || ws_bytes < need)
       return fail(W8_E_WORKSPACE, "workspace of " + std::to_string(need) + " bytes needed, got " +
@@ -320,7 +364,7 @@ w8_status w8_workspace_size(w8_fmt fmt, int M, int N, int K, int packed, const w
   } else {
     c = resolve_cfg(fmt, M, N, K, packed != 0, nullptr);
   }
-  *bytes = workspace_bytes(fmt, M, N, c);
+  *bytes = workspace_bytes(fmt, M, N, K, c);
   return ok();
 }
 

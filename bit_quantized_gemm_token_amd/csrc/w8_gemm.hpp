@@ -6,20 +6,36 @@
 // to 256; the search also covers memory layout.  Here they are template and
 // launch parameters of one kernel:
 //
-//   grid   ceil(N / (16*NB)) * split_k workgroups of 64*WK threads; the
-//          split index varies fastest.  Workgroups are dealt round-robin to
+//   wave   owns NB blocks of 16 weight rows; a workgroup has WK x WN waves:
+//          WK waves split the workgroup's K range (summed through LDS in
+//          wave order), WN waves sit side by side along N (tile = WN*NB row
+//          blocks) and share the activations staged in LDS (one of WK, WN is
+//          1; WN > 1 needs XL).
+//   grid   grid == 0: ntiles * split_k workgroups, one per (tile, split), the
+//          split index varying fastest.  Workgroups are dealt round-robin to
 //          the 8 XCDs, each with its own L2, so with split_k a power of two
 //          an XCD sees only split_k/8 K ranges (split_k >= 8) or one (split_k
 //          < 8), and fetches only those activation columns instead of all K.
-//   wave   wk owns the workgroup's NB blocks of 16 weight rows
-//          (n0 = tile*16*NB) over the wk-th slice of the workgroup's K range.
-//   K loop one MFMA per K-step and row block (64 bytes of K for int8, 128 for
-//          E4M3FN); each lane streams its weight bytes straight from HBM into
-//          MFMA operand registers with 16-byte loads (no LDS for weights:
-//          every weight byte meets at most 32 tokens, so there is nothing to
-//          reuse), U K-steps per stage, two stages in flight.  The activation
-//          fragment of a K-step is loaded once and reused by the NB row
-//          blocks (activations are tiny and stay in L2).
+//          grid > 0 (stream-K): exactly `grid` workgroups share the ntiles x
+//          ksteps (tile, K-step) iterations in equal contiguous ranges, so the
+//          weight stream is spread evenly over the compute units whatever the
+//          tile count; a tile split between workgroups is summed like a
+//          split-K tile.
+//   K loop one MFMA per K-step, row block and 16-row block of M (64 bytes of K
+//          for int8, 128 for E4M3FN); each lane streams its weight bytes
+//          straight from HBM into MFMA operand registers with 16-byte loads
+//          (no LDS for weights: every weight byte meets at most 32 tokens, so
+//          there is nothing to reuse), U K-steps per stage, two stages in
+//          flight.  XL == 0: the wave loads its own activation fragments in
+//          each stage (reused by its NB row blocks).  XL == 1: before the K
+//          loop the workgroup copies the activation fragments of its K range
+//          into LDS with direct-to-LDS loads, each wave a share of them, and
+//          the K loop reads them from LDS: the loop's vector-memory pipe then
+//          carries only weights, and with WN > 1 every activation byte is
+//          fetched once per workgroup instead of once per wave.  (A compute
+//          unit moves about 20 bytes per clock through its vector-memory
+//          path whether a load hits or misses; at M = 32 the activation
+//          fragments are as many bytes as the weights.)
 //   layout PACKED=0: Wq row-major [N, K] (row stride ldw); a load instruction
 //          reads 64 contiguous bytes of 16 rows.  PACKED=1: the MFMA-native
 //          layout written by the weight packer: the 16 x KSTEP bytes of one
@@ -31,13 +47,12 @@
 //          SWAP=1: A = weights, B = activations^T, C[n][m] = (Wq . Xq^T)^T.
 //          The MFMA work is identical (square 16x16 tiles); what changes is
 //          the accumulator-to-lane map and so the epilogue's store pattern.
-//   WK     waves splitting K inside the workgroup are summed through LDS in
-//          fixed wave order.
-//   Split-K  each workgroup writes its partial tile to the workspace; the
-//          last workgroup of a tile to arrive (arrival counter) sums the
-//          partials in split order, runs the epilogue and resets the counter.
-//          The fixed order makes results run-to-run deterministic; empty
-//          splits (split_k > number of K-steps) contribute zeros.
+//   Split-K / shared tiles  each contributing workgroup writes its partial
+//          tile to the workspace; the last one of the tile to arrive (arrival
+//          counter) sums the partials in K order, runs the epilogue and
+//          resets the counter.  The fixed order makes results run-to-run
+//          deterministic; empty splits (split_k > number of K-steps)
+//          contribute zeros.
 //   Block_FP8  K-step = one 128-wide group: each group's MFMA starts from
 //          zero and is added into the fp32 accumulator times
 //          sx[m, g] * sw[n / 128, g].
@@ -133,158 +148,208 @@ __device__ __forceinline__ typename Traits<FMT>::Acc mma(typename Traits<FMT>::F
   }
 }
 
-template <int FMT, int MB, int NB, int WK, int U, int SWAP, int PACKED>
-__global__ __launch_bounds__(64 * WK) void gemm_kernel(GemmArgs a) {
+template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL>
+__global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
   typedef typename Traits<FMT>::Frag Frag;
   typedef typename Traits<FMT>::Acc Acc;
   constexpr int KSTEP = Traits<FMT>::KSTEP;
   constexpr bool BLOCK = (FMT == BLOCK_FP8);
+  static_assert(WN == 1 || WK == 1, "the waves of a workgroup split either K or N");
+  static_assert(WN == 1 || XL, "waves side by side along N share activations through LDS");
+  // XL: the segment's activation fragments are copied into LDS up front,
+  // one 1 KiB chunk (16 bytes per lane) per (K-step, M block, 16-byte
+  // load): chunk ((k - ka) * MB + b) * CH + jj.
+  constexpr int CH = KSTEP / 64;
 
   const int lane = threadIdx.x & 63;
-  const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wk = wave % WK, wn = wave / WK;
   const int r = lane & 15, g = lane >> 4;
-  const int split = (int)(blockIdx.x & (unsigned)(a.split_k - 1));
-  const int tile = (int)(blockIdx.x >> a.split_shift);
-  const int n0 = tile * 16 * NB;
 
-  // Weight pointers of the NB row blocks (clamped for the ragged N tile).
-  const uint8_t* wptr[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    if constexpr (PACKED) {
-      const int nb = min(tile * NB + j, (a.N + 15) / 16 - 1);
-      wptr[j] = a.wq + (long long)nb * a.ksteps * (16 * KSTEP) + 16 * lane;
-    } else {
-      wptr[j] = a.wq + (long long)min(n0 + 16 * j + r, a.N - 1) * a.ldw + 16 * g;
-    }
-  }
+  // Activation rows of this lane (padding rows of the 16-row MFMA tile read
+  // a clamped valid row; their outputs are never stored).
   const uint8_t* xrow[MB];
 #pragma unroll
   for (int b = 0; b < MB; ++b) xrow[b] = a.xq + (long long)min(16 * b + r, a.M - 1) * a.ldq + 16 * g;
 
-  auto load_w = [&](int j, int kk) -> Frag {
-    if constexpr (PACKED)
-      return load_packed<FMT>(wptr[j], kk);
-    else
-      return load_frag<FMT>(wptr[j], kk);
-  };
-
-  // Block_FP8 scale pointers for this lane: sw row of the 128-row block (the
-  // 16*NB rows of a tile never straddle two blocks), and the sx rows of the
-  // accumulator elements the lane holds (SWAP: one m per lane; else four).
+  // Block_FP8 sx rows of the accumulator elements this lane holds (SWAP: one
+  // m per lane; else four), and the per-token formats' epilogue sx, loaded
+  // now so their latency hides under the K loop.
   constexpr int SXN = SWAP ? 1 : 4;
-  const float* swrow = nullptr;
   const float* sxrow[MB][SXN];
-  if constexpr (BLOCK) {
-    swrow = a.sw + (long long)(min(n0, a.N - 1) / kGroup) * a.sgroups;
-#pragma unroll
-    for (int b = 0; b < MB; ++b)
-#pragma unroll
-      for (int i = 0; i < SXN; ++i) {
-        const int m = SWAP ? 16 * b + r : 16 * b + 4 * g + i;
-        sxrow[b][i] = a.sx + (long long)min(m, a.M - 1) * a.sgroups;
-      }
-  }
-
-  // Epilogue scales of the per-token formats, loaded now so their latency
-  // hides under the K loop instead of adding a round trip at the end.
-  float ep_sx[MB][SXN], ep_sw[NB][4 / SXN];
-  if constexpr (!BLOCK) {
-#pragma unroll
-    for (int b = 0; b < MB; ++b)
-#pragma unroll
-      for (int i = 0; i < SXN; ++i)
-        ep_sx[b][i] = a.sx[min(SWAP ? 16 * b + r : 16 * b + 4 * g + i, a.M - 1)];
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int i = 0; i < 4 / SXN; ++i)
-        ep_sw[j][i] = a.sw[min(SWAP ? n0 + 16 * j + 4 * g + i : n0 + 16 * j + r, a.N - 1)];
-  }
-
-  // K-steps of this split, then of this wave.
-  // (32-bit: the host guarantees split_k * ksteps < 2^31.)
-  const int ka = (int)((unsigned)(split * a.ksteps) / (unsigned)a.split_k);
-  const int kb = (int)((unsigned)((split + 1) * a.ksteps) / (unsigned)a.split_k);
-  const int la = ka + (kb - ka) * wk / WK;
-  const int lb = ka + (kb - ka) * (wk + 1) / WK;
-  const int lfull = min(lb, a.kfull);
-
-  Acc acc[MB][NB];
+  float ep_sx[MB][SXN];
 #pragma unroll
   for (int b = 0; b < MB; ++b)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[b][j] = Acc{0, 0, 0, 0};
-
-  // A stage is U consecutive K-steps.  The wave's full K-steps [la, lfull)
-  // are covered by ns whole stages ending at lfull; the first stage may
-  // start before la, and its steps below la load a clamped (valid) address
-  // and are zeroed before their MFMA, so every load of a stage is issued at
-  // once and no K-step is ever processed alone.
-  struct Stage {
-    Frag w[U][NB];
-    Frag x[U][MB];
-    float sw[BLOCK ? U : 1];
-    float sx[BLOCK ? U : 1][MB][SXN];
-  };
-  auto load_stage = [&](Stage& st, int k0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = max(k0 + u, la);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) st.w[u][j] = load_w(j, k);
-#pragma unroll
-      for (int b = 0; b < MB; ++b) st.x[u][b] = load_frag<FMT>(xrow[b], k);
+    for (int i = 0; i < SXN; ++i) {
+      const int m = min(SWAP ? 16 * b + r : 16 * b + 4 * g + i, a.M - 1);
       if constexpr (BLOCK) {
-        st.sw[u] = swrow[k];
-#pragma unroll
-        for (int b = 0; b < MB; ++b)
-#pragma unroll
-          for (int i = 0; i < SXN; ++i) st.sx[u][b][i] = sxrow[b][i][k];
+        sxrow[b][i] = a.sx + (long long)m * a.sgroups;
+        ep_sx[b][i] = 0.0f;
+      } else {
+        sxrow[b][i] = nullptr;
+        ep_sx[b][i] = a.sx[m];
       }
     }
-  };
-  auto step = [&](const Frag (&w)[NB], const Frag (&x)[MB], float sw, const float (&sx)[MB][SXN]) {
+
+  __shared__ Acc red[WK > 1 ? (WK - 1) * MB * NB * 64 : 1];
+  __shared__ v4i xl[XL ? kXlChunks * 64 : 1];
+  __shared__ int is_last;
+
+  // One segment: K-steps [ka, kb) of output tile `tile` (WN*NB blocks of 16
+  // weight rows).  The segment is contributor `slot` of the `count`
+  // workgroups that cover the tile; count == 1 writes Y directly.
+  auto segment = [&](int tile, int ka, int kb, int slot, int count) {
+    const int n0 = (tile * WN + wn) * 16 * NB;  // first weight row of this wave
+
+    const uint8_t* wptr[NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+    for (int j = 0; j < NB; ++j) {
+      if constexpr (PACKED) {
+        const int nb = min((tile * WN + wn) * NB + j, (a.N + 15) / 16 - 1);
+        wptr[j] = a.wq + (long long)nb * a.ksteps * (16 * KSTEP) + 16 * lane;
+      } else {
+        wptr[j] = a.wq + (long long)min(n0 + 16 * j + r, a.N - 1) * a.ldw + 16 * g;
+      }
+    }
+    auto load_w = [&](int j, int kk) -> Frag {
+      if constexpr (PACKED)
+        return load_packed<FMT>(wptr[j], kk);
+      else
+        return load_frag<FMT>(wptr[j], kk);
+    };
+    // Block_FP8 sw row of the wave's 128-row block (its 16*NB rows never
+    // straddle two blocks); the per-token formats' epilogue sw.
+    const float* swrow = nullptr;
+    float ep_sw[NB][4 / SXN];
+    if constexpr (BLOCK) {
+      swrow = a.sw + (long long)(min(n0, a.N - 1) / kGroup) * a.sgroups;
+    } else {
 #pragma unroll
-      for (int b = 0; b < MB; ++b) {
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4 / SXN; ++i)
+          ep_sw[j][i] = a.sw[min(SWAP ? n0 + 16 * j + 4 * g + i : n0 + 16 * j + r, a.N - 1)];
+    }
+
+    // K-steps of this wave: its WK-th of the segment.
+    const int la = ka + (kb - ka) * wk / WK;
+    const int lb = ka + (kb - ka) * (wk + 1) / WK;
+    const int lfull = min(lb, a.kfull);
+
+    Acc acc[MB][NB];
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[b][j] = Acc{0, 0, 0, 0};
+
+    // A stage is U consecutive K-steps.  The wave's full K-steps [la, lfull)
+    // are covered by ns whole stages ending at lfull; the first stage may
+    // start before la, and its steps below la load a clamped (valid) address
+    // and are zeroed before their MFMA, so every load of a stage is issued
+    // at once and no K-step is ever processed alone.
+    struct Stage {
+      Frag w[U][NB];
+      Frag x[XL ? 1 : U][MB];  // !XL: the wave's own activation fragments
+      float sw[BLOCK ? U : 1];
+      float sx[BLOCK ? U : 1][MB][SXN];
+    };
+    auto load_stage = [&](Stage& st, int k0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = max(k0 + u, la);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) st.w[u][j] = load_w(j, k);
+        if constexpr (!XL) {
+#pragma unroll
+          for (int b = 0; b < MB; ++b) st.x[u][b] = load_frag<FMT>(xrow[b], k);
+        }
         if constexpr (BLOCK) {
-          const Acc p = mma<FMT, SWAP>(w[j], x[b], Acc{0, 0, 0, 0});
+          st.sw[u] = swrow[k];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[b][j][i] += p[i] * (sx[b][SWAP ? 0 : i] * sw);
-        } else {
-          acc[b][j] = mma<FMT, SWAP>(w[j], x[b], acc[b][j]);
+          for (int b = 0; b < MB; ++b)
+#pragma unroll
+            for (int i = 0; i < SXN; ++i) st.sx[u][b][i] = sxrow[b][i][k];
         }
       }
-  };
-  // MASK: the first stage, whose steps below la are zeroed.
-  auto run_stage = [&](const Stage& st, int k0, auto mask) {
+    };
+    auto step = [&](const Frag (&w)[NB], const Frag (&x)[MB], float sw,
+                    const float (&sx)[MB][SXN]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      Frag w[NB];
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const Frag zero = {};
-        w[j] = (decltype(mask)::value && k0 + u < la) ? zero : st.w[u][j];
+        for (int b = 0; b < MB; ++b) {
+          if constexpr (BLOCK) {
+            const Acc p = mma<FMT, SWAP>(w[j], x[b], Acc{0, 0, 0, 0});
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[b][j][i] += p[i] * (sx[b][SWAP ? 0 : i] * sw);
+          } else {
+            acc[b][j] = mma<FMT, SWAP>(w[j], x[b], acc[b][j]);
+          }
+        }
+    };
+    // MASK: the first stage, whose steps below la are zeroed.
+    auto run_stage = [&](const Stage& st, int k0, auto mask) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        Frag w[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const Frag zero = {};
+          w[j] = (decltype(mask)::value && k0 + u < la) ? zero : st.w[u][j];
+        }
+        if constexpr (XL) {
+          const int k = max(k0 + u, la);
+          Frag x[MB];
+#pragma unroll
+          for (int b = 0; b < MB; ++b) {
+            const int c = ((k - ka) * MB + b) * CH;
+            if constexpr (FMT == W8A8_INT8) {
+              x[b] = xl[c * 64 + lane];
+            } else {
+              const v4i lo = xl[c * 64 + lane];
+              const v4i hi = xl[(c + 1) * 64 + lane];
+              x[b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+          }
+          step(w, x, st.sw[BLOCK ? u : 0], st.sx[BLOCK ? u : 0]);
+        } else {
+          step(w, st.x[u], st.sw[BLOCK ? u : 0], st.sx[BLOCK ? u : 0]);
+        }
       }
-      step(w, st.x[u], st.sw[BLOCK ? u : 0], st.sx[BLOCK ? u : 0]);
-    }
-  };
-  const std::true_type masked;
-  const std::false_type whole;
+    };
+    const std::true_type masked;
+    const std::false_type whole;
 
-  // Stages alternate between register sets A and B: the loads of stage s+1
-  // are issued before stage s feeds the MFMAs.
-  const int ns = (max(lfull - la, 0) + U - 1) / U;
-  if (ns > 0) {
+    // XL: every wave of the workgroup copies its share of the segment's
+    // full K-steps [ka, min(kb, kfull)) of activations into LDS with
+    // direct-to-LDS loads (no registers), issued before the weight loads.
+    if constexpr (XL) {
+      const int nchunks = (min(kb, a.kfull) - ka) * MB * CH;
+      for (int c = wave; c < nchunks; c += WK * WN) {
+        const int kk = c / (MB * CH), b = (c / CH) % MB, jj = c % CH;
+        const uint8_t* src = a.xq + (long long)min(16 * b + r, a.M - 1) * a.ldq + 16 * g +
+                             (long long)(ka + kk) * KSTEP + 64 * jj;
+        __builtin_amdgcn_global_load_lds(
+            src, (__attribute__((address_space(3))) void*)(xl + c * 64), 16, 0, 0);
+      }
+    }
+
+    // Stages alternate between register sets A and B: the loads of stage s+1
+    // are issued before stage s feeds the MFMAs.
+    const int ns = (max(lfull - la, 0) + U - 1) / U;
     const int k0 = lfull - ns * U;
     Stage A, B;
-    load_stage(A, k0);
+    if (ns > 0) load_stage(A, k0);
+    if (ns > 1) load_stage(B, k0 + U);
+    if constexpr (XL) {
+      // the copies (and the first weight stages) have landed in every wave
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
     if (ns == 1) {
       run_stage(A, k0, masked);
-    } else {
-      load_stage(B, k0 + U);
+    } else if (ns > 1) {
       run_stage(A, k0, masked);
       int s = 1;  // B holds stage s
       for (; s + 2 <= ns - 1; s += 2) {
@@ -301,135 +366,172 @@ __global__ __launch_bounds__(64 * WK) void gemm_kernel(GemmArgs a) {
         run_stage(B, k0 + s * U, whole);
       }
     }
-  }
-  // The ragged K tail (K % KSTEP != 0; never for Block_FP8, whose K is a
-  // multiple of its 128-byte K-step) belongs to the wave that owns step
-  // kfull.  Packed weights are zero-padded there; activations are masked.
-  if constexpr (!BLOCK) {
-    if (lb > a.kfull && la < lb) {
-      Frag wt[NB], xt[MB];
+    // The ragged K tail (K % KSTEP != 0; never for Block_FP8, whose K is a
+    // multiple of its 128-byte K-step) belongs to the wave that owns step
+    // kfull.  Packed weights are zero-padded there; activations are masked.
+    if constexpr (!BLOCK) {
+      if (lb > a.kfull && la < lb) {
+        Frag wt[NB], xt[MB];
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        wt[j] = PACKED ? load_w(j, a.kfull) : load_frag_tail<FMT>(wptr[j], a.kfull, 16 * g, a.K);
+        for (int j = 0; j < NB; ++j)
+          wt[j] = PACKED ? load_w(j, a.kfull) : load_frag_tail<FMT>(wptr[j], a.kfull, 16 * g, a.K);
 #pragma unroll
-      for (int b = 0; b < MB; ++b) xt[b] = load_frag_tail<FMT>(xrow[b], a.kfull, 16 * g, a.K);
-      const float no_sx[MB][SXN] = {};
-      step(wt, xt, 0.0f, no_sx);
+        for (int b = 0; b < MB; ++b) xt[b] = load_frag_tail<FMT>(xrow[b], a.kfull, 16 * g, a.K);
+        const float no_sx[MB][SXN] = {};
+        step(wt, xt, 0.0f, no_sx);
+      }
     }
-  }
 
-  // Sum the WK waves through LDS, in wave order.
-  if constexpr (WK > 1) {
-    __shared__ Acc red[(WK - 1) * MB * NB * 64];
-    if (wk > 0) {
-#pragma unroll
-      for (int b = 0; b < MB; ++b)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) red[(((wk - 1) * MB + b) * NB + j) * 64 + lane] = acc[b][j];
-    }
-    __syncthreads();
-    if (wk == 0) {
-      for (int q = 1; q < WK; ++q)
+    // Sum the WK waves through LDS, in wave order.
+    if constexpr (WK > 1) {
+      if (wk > 0) {
 #pragma unroll
         for (int b = 0; b < MB; ++b)
 #pragma unroll
-          for (int j = 0; j < NB; ++j) acc[b][j] += red[(((q - 1) * MB + b) * NB + j) * 64 + lane];
+          for (int j = 0; j < NB; ++j) red[(((wk - 1) * MB + b) * NB + j) * 64 + lane] = acc[b][j];
+      }
+      __syncthreads();
+      if (wk == 0) {
+        for (int q = 1; q < WK; ++q)
+#pragma unroll
+          for (int b = 0; b < MB; ++b)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[b][j] += red[(((q - 1) * MB + b) * NB + j) * 64 + lane];
+      }
     }
-  }
 
-  // Split-K: publish the partial; the last workgroup of the tile reduces.
-  // Protocol (no L2 writeback or invalidate): the partials are written with
-  // agent-scope atomic stores, which write through this XCD's L2 to the
-  // device-coherent level; s_waitcnt waits until every one of them is
-  // acknowledged before the workgroup counts itself in; the last workgroup
-  // to arrive reads the partials with agent-scope atomic loads, which are
-  // served from the device-coherent level, so it sees every split's data.
-  // Partial layout: fragment f = ((tile*S + split)*NB + j)*MB + b holds
-  // 4 x 64 words, word (f*4 + i)*64 + lane, so each of the four stores of a
-  // wave writes 256 contiguous bytes.
-  if (a.split_k > 1) {
-    typedef decltype(acc[0][0][0]) Elem;
-    typedef typename std::remove_cv<typename std::remove_reference<Elem>::type>::type Word;
-    Word* part = reinterpret_cast<Word*>(a.part);
-    const long long frag0 = (long long)tile * a.split_k;
-    if (wk == 0) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int b = 0; b < MB; ++b)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            __hip_atomic_store(part + ((((frag0 + split) * NB + j) * MB + b) * 4 + i) * 64 + lane,
-                               acc[b][j][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    __shared__ int is_last;
-    if (threadIdx.x == 0) {
-      const unsigned prev = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-      is_last = (prev == (unsigned)(a.split_k - 1));
-    }
-    __syncthreads();
-    if (!is_last) return;
-    if (wk == 0) {
-#pragma unroll
-      for (int b = 0; b < MB; ++b)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[b][j] = Acc{0, 0, 0, 0};
-      for (int s = 0; s < a.split_k; ++s)
+    // Several workgroups cover this tile: publish the partial; the last
+    // workgroup to arrive sums them in slot (= K) order.
+    // Protocol (no L2 writeback or invalidate): the partials are written with
+    // agent-scope atomic stores, which write through this XCD's L2 to the
+    // device-coherent level; s_waitcnt waits until every one of them is
+    // acknowledged before the workgroup counts itself in; the last workgroup
+    // to arrive reads the partials with agent-scope atomic loads, which are
+    // served from the device-coherent level, so it sees every slot's data.
+    // Partial layout: fragment f = ((tile*slots + slot)*WN*NB + wn*NB + j)*MB
+    // + b holds 4 x 64 words, word (f*4 + i)*64 + lane, so each of the four
+    // stores of a wave writes 256 contiguous bytes.
+    bool store = true;
+    if (count > 1) {
+      typedef decltype(acc[0][0][0]) Elem;
+      typedef typename std::remove_cv<typename std::remove_reference<Elem>::type>::type Word;
+      Word* part = reinterpret_cast<Word*>(a.part);
+      const long long f0 = ((long long)tile * a.slots * WN + wn) * NB;  // + slot*WN*NB + j
+      if (wk == 0) {
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
           for (int b = 0; b < MB; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              acc[b][j][i] += __hip_atomic_load(
-                  part + ((((frag0 + s) * NB + j) * MB + b) * 4 + i) * 64 + lane,
-                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              __hip_atomic_store(
+                  part + (((f0 + (long long)slot * WN * NB + j) * MB + b) * 4 + i) * 64 + lane,
+                  acc[b][j][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        is_last = (prev == (unsigned)(count - 1));
+      }
+      __syncthreads();
+      store = is_last;
+      if (store) {
+        if (wk == 0) {
+#pragma unroll
+          for (int b = 0; b < MB; ++b)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[b][j] = Acc{0, 0, 0, 0};
+          for (int s = 0; s < count; ++s)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+              for (int b = 0; b < MB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  acc[b][j][i] += __hip_atomic_load(
+                      part + (((f0 + (long long)s * WN * NB + j) * MB + b) * 4 + i) * 64 + lane,
+                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (threadIdx.x == 0)
+          __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
-    if (threadIdx.x == 0)
-      __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+    if (!store || wk != 0) return;
 
-  if (wk != 0) return;
-
-  // Epilogue.
+    // Epilogue.
 #pragma unroll
-  for (int b = 0; b < MB; ++b)
+    for (int b = 0; b < MB; ++b)
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = SWAP ? 16 * b + r : 16 * b + 4 * g + i;
-        const int n = SWAP ? n0 + 16 * j + 4 * g + i : n0 + 16 * j + r;
-        if (m < a.M && n < a.N) {
-          const long long o = (long long)m * a.ldo + n;
-          if (a.out_mode) {
-            if constexpr (FMT == W8A8_INT8)
-              reinterpret_cast<int*>(a.out)[o] = acc[b][j][i];
-            else
-              reinterpret_cast<float*>(a.out)[o] = acc[b][j][i];
-          } else {
-            float y;
-            if constexpr (BLOCK) {
-              y = acc[b][j][i];
-            } else {
-              const float sxm = ep_sx[b][SWAP ? 0 : i], swn = ep_sw[j][SWAP ? i : 0];
+        for (int i = 0; i < 4; ++i) {
+          // MFMA 16x16 C layout: lane holds column lane%16, rows 4*(lane/16)+i.
+          // SWAP=0: C[m][n]: m = 16b + 4g + i, n = n0 + 16j + r.
+          // SWAP=1: C[n][m]: n = n0 + 16j + 4g + i, m = 16b + r.
+          const int m = SWAP ? 16 * b + r : 16 * b + 4 * g + i;
+          const int n = SWAP ? n0 + 16 * j + 4 * g + i : n0 + 16 * j + r;
+          if (m < a.M && n < a.N) {
+            const long long o = (long long)m * a.ldo + n;
+            if (a.out_mode) {
               if constexpr (FMT == W8A8_INT8)
-                y = (float)acc[b][j][i] * sxm * swn;
+                reinterpret_cast<int*>(a.out)[o] = acc[b][j][i];
               else
-                y = acc[b][j][i] * sxm * swn;
+                reinterpret_cast<float*>(a.out)[o] = acc[b][j][i];
+            } else {
+              float y;
+              if constexpr (BLOCK) {
+                y = acc[b][j][i];
+              } else {
+                const float sxm = ep_sx[b][SWAP ? 0 : i], swn = ep_sw[j][SWAP ? i : 0];
+                if constexpr (FMT == W8A8_INT8)
+                  y = (float)acc[b][j][i] * sxm * swn;
+                else
+                  y = acc[b][j][i] * sxm * swn;
+              }
+              reinterpret_cast<uint16_t*>(a.out)[o] = bf16_rne(y);
             }
-            reinterpret_cast<uint16_t*>(a.out)[o] = bf16_rne(y);
           }
         }
-      }
+  };
+
+  if (a.grid == 0) {
+    // One workgroup per (tile, split); the split index varies fastest.
+    const int split = (int)(blockIdx.x & (unsigned)(a.split_k - 1));
+    const int tile = (int)(blockIdx.x >> a.split_shift);
+    // (32-bit: the host guarantees split_k * ksteps < 2^31.)
+    const int ka = (int)((unsigned)(split * a.ksteps) / (unsigned)a.split_k);
+    const int kb = (int)((unsigned)((split + 1) * a.ksteps) / (unsigned)a.split_k);
+    segment(tile, ka, kb, split, a.split_k);
+  } else {
+    // Stream-K: the ntiles * ksteps (tile, K-step) iterations, tile-major,
+    // are dealt out in grid contiguous ranges, workgroup w taking
+    // [w*I/grid, (w+1)*I/grid); the host guarantees grid <= I, so no range
+    // is empty.  The workgroup holding iteration i is ((i+1)*grid - 1) / I,
+    // which gives each tile's first contributor and contributor count.
+    const unsigned long long I = (unsigned long long)a.ntiles * (unsigned)a.ksteps;
+    const unsigned long long G = (unsigned)a.grid, w = blockIdx.x;
+    const unsigned long long KS = (unsigned)a.ksteps;
+    unsigned long long i0 = w * I / G;
+    const unsigned long long i1 = (w + 1) * I / G;
+    while (i0 < i1) {
+      const unsigned long long t = i0 / KS;
+      const int ka = (int)(i0 - t * KS);
+      const unsigned long long kend = (unsigned long long)ka + (i1 - i0);
+      const int kb = (int)(kend < KS ? kend : KS);
+      const unsigned long long first = ((t * KS + 1) * G - 1) / I;
+      const unsigned long long last = (((t + 1) * KS) * G - 1) / I;
+      segment((int)t, ka, kb, (int)(w - first), (int)(last - first + 1));
+      i0 += (unsigned long long)(kb - ka);
+      if (i0 < i1) __syncthreads();  // LDS and is_last are reused by the next segment
+    }
+  }
 }
 
-template <int FMT, int MB, int NB, int WK, int U, int SWAP, int PACKED>
+template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL>
 hipError_t launch_gemm(const GemmArgs& a, dim3 grid, dim3 block, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, WK, U, SWAP, PACKED>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, WK, WN, U, SWAP, PACKED, XL>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

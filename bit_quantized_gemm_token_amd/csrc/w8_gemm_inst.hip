@@ -14,16 +14,20 @@
 #define W8_CAT(a, b, c) W8_CAT2(a, b, c)
 #define W8_TABLE_FN W8_CAT(gemm_instances_f, W8_FMT, W8_SWAP)
 
-// One entry per (MB, NB, WK, UNROLL, PACKED): MB in {1, 2}; (NB, UNROLL) with
-// NB * UNROLL <= 4 (the weight registers of one stage); WK in {1, ..., 16};
-// PACKED in {0, 1}.
-#define W8_I(MB, NB, WK, U, P) \
-  {W8_FMT, MB, NB, WK, U, W8_SWAP, P, &launch_gemm<W8_FMT, MB, NB, WK, U, W8_SWAP, P>},
-#define W8_P(MB, NB, WK, U) W8_I(MB, NB, WK, U, 0) W8_I(MB, NB, WK, U, 1)
-#define W8_U(MB, WK)                                                                   \
-  W8_P(MB, 1, WK, 1) W8_P(MB, 1, WK, 2) W8_P(MB, 1, WK, 4) W8_P(MB, 2, WK, 1)         \
-  W8_P(MB, 2, WK, 2) W8_P(MB, 4, WK, 1)
-#define W8_W(MB) W8_U(MB, 1) W8_U(MB, 2) W8_U(MB, 4) W8_U(MB, 8) W8_U(MB, 16)
+// One entry per (MB, NB, WK, WN, UNROLL, PACKED, XL): MB in {1, 2}; (NB,
+// UNROLL) with NB * UNROLL <= 4 (the weight registers of one stage);
+// (WK, WN, XL) in {(1..16, 1, 0), (1..8, 1, 1), (1, 2..8, 1)}; PACKED in {0, 1}.
+#define W8_I(MB, NB, WK, WN, U, P, XL)                                       \
+  {W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL,                                 \
+   &launch_gemm<W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL>},
+#define W8_P(MB, NB, WK, WN, U, XL) W8_I(MB, NB, WK, WN, U, 0, XL) W8_I(MB, NB, WK, WN, U, 1, XL)
+#define W8_U(MB, WK, WN, XL)                                                           \
+  W8_P(MB, 1, WK, WN, 1, XL) W8_P(MB, 1, WK, WN, 2, XL) W8_P(MB, 1, WK, WN, 4, XL)    \
+  W8_P(MB, 2, WK, WN, 1, XL) W8_P(MB, 2, WK, WN, 2, XL) W8_P(MB, 4, WK, WN, 1, XL)
+#define W8_W(MB)                                                                       \
+  W8_U(MB, 1, 1, 0) W8_U(MB, 2, 1, 0) W8_U(MB, 4, 1, 0) W8_U(MB, 8, 1, 0)             \
+  W8_U(MB, 16, 1, 0) W8_U(MB, 1, 1, 1) W8_U(MB, 2, 1, 1) W8_U(MB, 4, 1, 1)            \
+  W8_U(MB, 8, 1, 1) W8_U(MB, 1, 2, 1) W8_U(MB, 1, 4, 1) W8_U(MB, 1, 8, 1)
 
 namespace w8 {
 

@@ -22,7 +22,9 @@ w8_status check_gemm_shape(int fmt, int M, int N, int K);
 // Config checks (shape-independent and shape-dependent).
 w8_status check_cfg(int fmt, int M, int N, int K, const w8_cfg& c);
 w8_cfg make_default_cfg(int fmt, int M, int N, int K);
-size_t workspace_bytes(int fmt, int M, int N, const w8_cfg& c);
+size_t workspace_bytes(int fmt, int M, int N, int K, const w8_cfg& c);
+int tiles_of(int N, const w8_cfg& c);                       // output tiles along N
+int partial_slots(int fmt, int N, int K, const w8_cfg& c);  // workspace slots per tile
 int ksteps_of(int fmt, int K);
 
 // Resolve cfg == NULL through the table (entries are per weight layout),

@@ -37,15 +37,17 @@ struct GemmArgs {
   const uint8_t* wq;       // weight codes [N, K], row stride ldw bytes
   const float* sw;         // weight scales
   void* out;               // bf16 Y [M, N] or 4-byte accumulators, stride ldo elements
-  void* part;              // split-K partials (workspace), 16-byte aligned
-  unsigned int* counters;  // split-K arrival counters, one per output tile
+  void* part;              // partials of shared tiles (workspace), 16-byte aligned
+  unsigned int* counters;  // arrival counters, one per output tile
   long long ldq, ldw, ldo;
   int M, N, K;
   int ksteps;    // K-steps in total: ceil(K / KSTEP)
   int kfull;     // K-steps with no ragged tail: K / KSTEP
   int split_k;
   int split_shift;  // log2(split_k)
-  int ntiles;    // output tiles along N
+  int grid;      // 0: one workgroup per (tile, split); > 0: stream-K over this many
+  int slots;     // partial slots per tile in the workspace
+  int ntiles;    // output tiles along N (WN * NB row blocks each)
   int sgroups;   // Block_FP8: K / 128 (row stride of sx and sw)
   int out_mode;  // 0: bf16 Y; 1: raw accumulators
 };
@@ -53,7 +55,7 @@ struct GemmArgs {
 typedef hipError_t (*GemmLaunchFn)(const GemmArgs&, dim3 grid, dim3 block, hipStream_t);
 
 struct GemmInstance {
-  int fmt, mb, nb, wk, unroll, swap, packed;
+  int fmt, mb, nb, wk, wn, unroll, swap, packed, xl;
   GemmLaunchFn fn;
 };
 
@@ -71,19 +73,35 @@ const GemmInstance* gemm_instances(int* count);
 // K-step (bytes of K per MFMA) of each format.
 inline int kstep_of(int fmt) { return fmt == 1 ? 64 : 128; }
 
+// Activations staged in LDS (cfg.x_lds): at most this many 1 KiB chunks (one
+// per K-step, 16-row block of M and 64 bytes of K-step) per workgroup
+// segment, 64 KiB, so two workgroups fit in a compute unit's 160 KiB.
+constexpr int kXlChunks = 64;
+
 // Workspace layout: a fixed 64 KiB counter region (one 4-byte arrival counter
 // per output tile, at most kSplitKMaxTiles tiles), then the partials: one
-// 1 KiB fragment (64 lanes x 16 bytes) per (tile, split, 16-row block of N,
-// 16-row block of M).  The counter region has the same size for every shape,
-// so the partials of one call never overlap the counters of another call
-// that shares the workspace: counters left at zero stay zero.
+// 1 KiB fragment (64 lanes x 16 bytes) per (tile, slot, 16-row block of N,
+// 16-row block of M), with split_k slots per tile for Split-K and
+// stream_k_slots() for stream-K.  The counter region has the same size for
+// every shape, so the partials of one call never overlap the counters of
+// another call that shares the workspace: counters left at zero stay zero.
 constexpr int kSplitKMaxTiles = 16384;
 inline size_t ws_counter_bytes(int ntiles) {
   (void)ntiles;
   return (size_t)kSplitKMaxTiles * 4;
 }
-inline size_t ws_partial_bytes(int ntiles, int split_k, int nb, int mb) {
-  return (size_t)ntiles * split_k * nb * mb * 1024;
+inline size_t ws_partial_bytes(int ntiles, int slots, int row_blocks, int mb) {
+  return (size_t)ntiles * slots * row_blocks * mb * 1024;
+}
+// Stream-K: an upper bound on the workgroups that share one tile of ks
+// K-steps when I = ntiles * ks iterations are dealt to grid workgroups in
+// ranges of at least floor(I / grid) >= 1: the first and last contributors
+// hold at least one iteration each, every other one at least floor(I/grid).
+inline int stream_k_slots(long long ntiles, int ks, int grid) {
+  const long long I = ntiles * ks;
+  const long long lmin = I / grid;
+  if (ks <= 1) return 1;
+  return (int)((ks - 2) / lmin) + 2;
 }
 
 }  // namespace w8

@@ -1,8 +1,8 @@
 // Per-shape config table (ai-radar.it, "Helion nel backend vLLM", paragraphs
 // 6-7: tuned configs are shipped per shape, with a default config for shapes
 // that have none).  Lookup is exact on (arch, abi, fmt, weight layout, M, N,
-// K); a miss, or
-// an entry written for another arch or ABI, falls back to the default config
+// K); a miss, or an entry written for another arch or ABI (kept in the file,
+// never used), falls back to the default config
 // (the hard-fallback cases of TensorRT-LLM issue 16363, "Suggested
 // direction", that apply to a table: cache miss and backend identity
 // mismatch).
@@ -82,34 +82,39 @@ w8_status parse_table(const std::string& text, std::map<Key, Entry>* native,
     while (ls >> t) tok.push_back(t);
     if (tok.empty()) continue;
     const std::string where = "config table line " + std::to_string(lineno) + ": ";
-    if (tok.size() != 13)
-      return fail(W8_E_TABLE_FORMAT, where + "expected 13 fields, got " + std::to_string(tok.size()));
     int abi = 0;
-    if (!parse_int(tok[1], &abi)) return fail(W8_E_TABLE_FORMAT, where + "bad abi field");
+    if (tok.size() < 2 || !parse_int(tok[1], &abi))
+      return fail(W8_E_TABLE_FORMAT, where + "expected arch and abi fields");
+    // An entry for another arch or ABI (whose fields may differ) is kept verbatim.
+    if (tok[0] != kArch || abi != W8_ABI_VERSION) {
+      foreign->push_back(line);
+      continue;
+    }
+    if (tok.size() != 16)
+      return fail(W8_E_TABLE_FORMAT, where + "expected 16 fields, got " + std::to_string(tok.size()));
     const int fmt = fmt_from_name(tok[2]);
     if (fmt < 0) return fail(W8_E_TABLE_FORMAT, where + "unknown format '" + tok[2] + "'");
     int packed = -1;
     if (tok[3] == "row") packed = 0;
     if (tok[3] == "packed") packed = 1;
     if (packed < 0) return fail(W8_E_TABLE_FORMAT, where + "layout must be row or packed");
-    int v[8];
-    for (int i = 0; i < 8; ++i)
+    int v[11];  // M N K tile_n waves_k waves_n unroll split_k grid swap_ab x_lds
+    for (int i = 0; i < 11; ++i)
       if (!parse_int(tok[4 + i], &v[i]))
         return fail(W8_E_TABLE_FORMAT, where + "bad integer '" + tok[4 + i] + "'");
     double us = 0;
-    if (!parse_double(tok[12], &us)) return fail(W8_E_TABLE_FORMAT, where + "bad time field");
-    if (tok[0] != kArch || abi != W8_ABI_VERSION) {
-      foreign->push_back(line);
-      continue;
-    }
+    if (!parse_double(tok[15], &us)) return fail(W8_E_TABLE_FORMAT, where + "bad time field");
     w8_cfg c;
     std::memset(&c, 0, sizeof c);
     c.abi_version = abi;
     c.tile_n = v[3];
     c.waves_k = v[4];
-    c.unroll = v[5];
-    c.split_k = v[6];
-    c.swap_ab = v[7];
+    c.waves_n = v[5];
+    c.unroll = v[6];
+    c.split_k = v[7];
+    c.grid = v[8];
+    c.swap_ab = v[9];
+    c.x_lds = v[10];
     if (check_gemm_shape(fmt, v[0], v[1], v[2]) != W8_OK || check_cfg(fmt, v[0], v[1], v[2], c) != W8_OK)
       return fail(W8_E_TABLE_FORMAT, where + "invalid entry (" + std::string(w8_last_error()) + ")");
     (*native)[Key(fmt, packed, v[0], v[1], v[2])] = Entry{c, us};
@@ -193,15 +198,17 @@ w8_status w8_save_config_table(const char* path) {
     std::lock_guard<std::mutex> lk(t.mu);
     maybe_load_env(t);
     out << "# w8gemm per-shape config table\n"
-        << "# arch abi fmt layout M N K tile_n waves_k unroll split_k swap_ab us_per_gemm\n";
+        << "# arch abi fmt layout M N K tile_n waves_k waves_n unroll split_k grid swap_ab "
+           "x_lds us_per_gemm\n";
     for (const auto& kv : t.native) {
       const Entry& e = kv.second;
       char buf[256];
-      std::snprintf(buf, sizeof buf, "%s %d %s %s %d %d %d %d %d %d %d %d %.4f\n", kArch,
+      std::snprintf(buf, sizeof buf, "%s %d %s %s %d %d %d %d %d %d %d %d %d %d %d %.4f\n", kArch,
                     W8_ABI_VERSION, fmt_name(std::get<0>(kv.first)),
                     layout_name(std::get<1>(kv.first)), std::get<2>(kv.first),
                     std::get<3>(kv.first), std::get<4>(kv.first), e.cfg.tile_n, e.cfg.waves_k,
-                    e.cfg.unroll, e.cfg.split_k, e.cfg.swap_ab, e.us);
+                    e.cfg.waves_n, e.cfg.unroll, e.cfg.split_k, e.cfg.grid, e.cfg.swap_ab,
+                    e.cfg.x_lds, e.us);
       out << buf;
     }
     for (const auto& l : t.foreign) out << l << "\n";

@@ -149,57 +149,79 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   const size_t nsx = block ? (size_t)M * G : (size_t)M;
   const size_t nsw = block ? (size_t)((N + 127) / 128) * G : (size_t)N;
 
-  // Candidates: every config of the family with split_k up to max_split_k,
-  // minus those that cannot pay off or cannot differ from another one:
+  // Candidates: every config of the family -- (waves_k, waves_n, x_lds) in
+  // {(1..16, 1, 0), (1..8, 1, 1), (1, 2..8, 1)}, each with split_k up to
+  // max_split_k or with a
+  // stream-K grid of 256, 512 or 1024 workgroups (1, 2 or 4 per compute
+  // unit) -- minus those that cannot pay off or cannot differ from another:
   //   - split_k above the number of K-steps (only empty splits added);
   //   - unroll above the K-steps each wave owns (the loop would never run a
   //     full stage, so the candidate equals the one with a smaller unroll);
-  //   - split-K partial traffic above twice the weight bytes;
+  //   - partial traffic above twice the weight bytes;
   //   - fewer waves in total than min(256, the most any candidate has): a
   //     stream this narrow leaves most of the 256 compute units idle.
   std::vector<Cand> cands;
   const int T = ksteps_of(fmt, K);
   const int tiles_n[] = {16, 32, 64};
-  const int waves[] = {1, 2, 4, 8, 16};
+  // (waves_k, waves_n, x_lds)
+  const int wave_shapes[][3] = {{1, 1, 0}, {2, 1, 0}, {4, 1, 0}, {8, 1, 0}, {16, 1, 0},
+                                {1, 1, 1}, {2, 1, 1}, {4, 1, 1}, {8, 1, 1},
+                                {1, 2, 1}, {1, 4, 1}, {1, 8, 1}};
   const int unrolls[] = {1, 2, 4};
+  const int grids[] = {256, 512, 1024};
   auto total_waves = [&](const w8_cfg& c) {
-    return (long long)((N + c.tile_n - 1) / c.tile_n) * c.waves_k * c.split_k;
+    const long long wgs = c.grid > 0 ? c.grid : (long long)tiles_of(N, c) * c.split_k;
+    return wgs * c.waves_k * c.waves_n;
   };
   std::vector<w8_cfg> all;
   long long most_waves = 0;
+  auto consider = [&](const w8_cfg& c) {
+    if (check_cfg(fmt, M, N, K, c) != W8_OK) return;
+    // K-steps per wave
+    const long long per_wave = c.grid > 0 ? (long long)tiles_of(N, c) * T / (c.grid * c.waves_k)
+                                          : (long long)T / (c.split_k * c.waves_k);
+    if (c.grid == 0 && c.split_k > T) return;
+    if (c.unroll > 1 && per_wave < c.unroll) return;
+    if (workspace_bytes(fmt, M, N, K, c) > 2 * wbytes + 65536 + (size_t)kSplitKMaxTiles * 4) return;
+    all.push_back(c);
+    most_waves = std::max(most_waves, total_waves(c));
+  };
   for (int tn : tiles_n)
-    for (int wk : waves)
+    for (const auto& ws : wave_shapes)
       for (int u : unrolls)
-        for (int s = 1; s <= o.max_split_k; s *= 2)
-          for (int sw = 0; sw < 2; ++sw) {
-            w8_cfg c;
-            std::memset(&c, 0, sizeof c);
-            c.abi_version = W8_ABI_VERSION;
-            c.tile_n = tn;
-            c.waves_k = wk;
-            c.unroll = u;
+        for (int sw = 0; sw < 2; ++sw) {
+          w8_cfg c;
+          std::memset(&c, 0, sizeof c);
+          c.abi_version = W8_ABI_VERSION;
+          c.tile_n = tn;
+          c.waves_k = ws[0];
+          c.waves_n = ws[1];
+          c.x_lds = ws[2];
+          c.unroll = u;
+          c.swap_ab = sw;
+          for (int s = 1; s <= o.max_split_k; s *= 2) {
             c.split_k = s;
-            c.swap_ab = sw;
-            if (check_cfg(fmt, M, N, K, c) != W8_OK) continue;
-            if (s > T) continue;
-            if (u > 1 && T / (s * wk) < u) continue;
-            if (workspace_bytes(fmt, M, N, c) > 2 * wbytes + 65536 + (size_t)kSplitKMaxTiles * 4)
-              continue;
-            all.push_back(c);
-            most_waves = std::max(most_waves, total_waves(c));
+            c.grid = 0;
+            consider(c);
           }
+          for (int gr : grids) {
+            c.split_k = 1;
+            c.grid = gr;
+            consider(c);
+          }
+        }
   const long long min_waves = std::min<long long>(256, most_waves);
   size_t max_ws = 0;
   for (const w8_cfg& c : all) {
     if (total_waves(c) < min_waves) continue;
-    max_ws = std::max(max_ws, workspace_bytes(fmt, M, N, c));
+    max_ws = std::max(max_ws, workspace_bytes(fmt, M, N, K, c));
     Cand cd;
     cd.cfg = c;
     cd.index = (int)cands.size();
     cands.push_back(cd);
   }
   const w8_cfg dflt = make_default_cfg(fmt, M, N, K);
-  max_ws = std::max(max_ws, workspace_bytes(fmt, M, N, dflt));
+  max_ws = std::max(max_ws, workspace_bytes(fmt, M, N, K, dflt));
 
   Buffers b;
   hipStream_t stream = nullptr;
@@ -347,7 +369,8 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   st = time_cfg(dflt, &dflt_us2);  // the default config on the tuned layout
   if (st) return st;
 
-  // Bank-2 winner; within 1% prefer split_k = 1, then swap_ab = 0, then fewer waves.
+  // Bank-2 winner; within 1% prefer no shared tiles (split_k = 1, grid = 0),
+  // then swap_ab = 0, then fewer waves per workgroup.
   Cand* win = order[0];
   for (size_t i = 1; i < top; ++i) {
     Cand* c = order[i];
@@ -356,7 +379,8 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
       win = c;
     } else if (a <= w * 1.01) {
       const auto rank = [](const w8_cfg& x) {
-        return std::make_tuple(x.split_k == 1 ? 0 : 1, x.swap_ab, x.waves_k);
+        return std::make_tuple(x.split_k == 1 && x.grid == 0 ? 0 : 1, x.swap_ab,
+                               x.waves_k * x.waves_n);
       };
       if (rank(c->cfg) < rank(win->cfg)) win = c;
     }

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define W8_ABI_VERSION 1
+#define W8_ABI_VERSION 2
 #define W8_MAX_M 32         /* token-count window of the tuned path (paragraph 4) */
 #define W8_MAX_SPLIT_K 256  /* split_k is a power of two up to 256 (paragraph 3) */
 #define W8_GROUP 128        /* Block_FP8 group / block edge */
@@ -86,15 +86,31 @@ typedef enum {
 
 /* One kernel configuration of the GEMM family (paragraphs 2-3 of the page:
  * the algorithmic variants are parameters, not separate kernels).
- *   tile_n   output columns (= weight rows) per workgroup, all owned by every
- *            wave of it: 16, 32 or 64 (one activation fragment feeds
- *            tile_n/16 MFMAs per K-step).
- *   waves_k  wavefronts inside one workgroup that split its K range and are
- *            reduced through LDS: 1, 2, 4, 8 or 16 (at most 1024 threads).
+ *   tile_n   output columns (= weight rows) each wave owns: 16, 32 or 64
+ *            (one activation fragment feeds tile_n/16 MFMAs per K-step).
+ *   waves_k  wavefronts of a workgroup that split its K range and are
+ *            reduced through LDS: 1, 2, 4, 8 or 16.
+ *   waves_n  wavefronts of a workgroup side by side along N, which share
+ *            the activations staged in LDS: 1, 2, 4 or 8; a workgroup covers
+ *            tile_n * waves_n columns.  waves_n > 1 needs waves_k == 1 and
+ *            x_lds == 1.
+ *   x_lds    0: each wave loads its activation fragments from memory inside
+ *            the K loop.  1: the workgroup first copies the activations of
+ *            its K range into LDS and the K loop reads them there; needs
+ *            waves_k <= 8 and at most 64 KiB per workgroup:
+ *            ceil(M/16) x (K-steps per workgroup) x (K-step bytes / 64) <= 64,
+ *            with K-steps per workgroup = ceil(K-steps / split_k), or for
+ *            stream-K min(K-steps, ceil(tiles x K-steps / grid)).
  *   unroll   K-steps each wave loads per stage (two stages in flight):
  *            1, 2 or 4, with tile_n/16 * unroll <= 4.
  *   split_k  workgroups splitting K, reduced in fixed order by the last one
  *            to finish: 1, 2, 4, ..., 256 (Split-K; 1 = Standard).
+ *   grid     0: one workgroup per (output tile, split).  > 0: stream-K, a
+ *            decomposition for a GPU with many compute units and few tiles:
+ *            exactly `grid` workgroups share the (tile, K-step) iterations
+ *            in equal contiguous ranges; a tile split between workgroups is
+ *            reduced like a split-K tile.  Needs split_k == 1 and grid at
+ *            most tiles x K-steps.
  *   swap_ab  0: MFMA A operand = activations, B = weights^T.
  *            1: Swap-AB, Y^T = Wq . Xq^T: A = weights, B = activations^T.
  * Set abi_version to W8_ABI_VERSION and reserved[] to 0.  The weight layout
@@ -104,9 +120,12 @@ typedef struct {
     int32_t abi_version;
     int32_t tile_n;
     int32_t waves_k;
+    int32_t waves_n;
     int32_t unroll;
     int32_t split_k;
+    int32_t grid;
     int32_t swap_ab;
+    int32_t x_lds;
     int32_t reserved[2];
 } w8_cfg;
 
@@ -188,10 +207,11 @@ w8_status w8_pack_weight(w8_fmt fmt, int N, int K, const void *wq, int64_t ldw, 
 
 /* Bytes of device workspace the GEMM needs for (fmt, M, N, K) under cfg
  * (cfg NULL: the config w8_resolve_config picks for that weight layout;
- * packed = 1 for packed weights).  0 when split_k == 1.
- * Layout: a fixed 64 KiB region of arrival counters, then the split-K
- * partials; split_k > 1 therefore supports at most 16384 output tiles
- * (N <= 16384 * tile_n).                                                    */
+ * packed = 1 for packed weights).  0 when no tile is shared between
+ * workgroups (split_k == 1 and grid == 0).
+ * Layout: a fixed 64 KiB region of arrival counters, then the partials of
+ * shared tiles; split_k > 1 and grid > 0 therefore support at most 16384
+ * output tiles (N <= 16384 * tile_n * waves_n).                             */
 w8_status w8_workspace_size(w8_fmt fmt, int M, int N, int K, int packed, const w8_cfg *cfg,
                             size_t *bytes);
 
@@ -248,7 +268,8 @@ w8_status w8_resolve_config(w8_fmt fmt, int M, int N, int K, int packed, w8_cfg 
 /* ----------------------------------------------------------- config table -- */
 /* Per-shape config table (paragraphs 6-7 of the page).  Text format, one entry
  * per line:
- *   arch abi fmt layout M N K tile_n waves_k unroll split_k swap_ab us_per_gemm
+ *   arch abi fmt layout M N K tile_n waves_k waves_n unroll split_k grid swap_ab
+ *   x_lds us_per_gemm
  * with layout "row" or "packed"; '#' starts a comment.  Entries whose arch or
  * abi differ from this build and device are kept in the file but never used.
  * w8_load_config_table replaces the in-memory table atomically: on any parse
@@ -275,10 +296,11 @@ w8_status w8_lookup_config(w8_fmt fmt, int M, int N, int K, int packed, w8_cfg *
  * compares configurations and keeps the best for each shape).  Tunes one
  * weight layout (opts->packed).  Allocates its own inputs (random codes and
  * scales), enumerates the configs of the family
- * (tile_n x waves_k x unroll x split_k in {1, 2, ..., max_split_k} x
- * swap_ab) minus those that cannot pay off or duplicate another (split_k
- * above the K-steps, unroll above the K-steps per wave, partials above twice
- * the weight bytes, fewer than min(256, most possible) waves), checks each
+ * (tile_n x (waves_k or waves_n) x x_lds x unroll x (split_k in {1, 2, ...,
+ * max_split_k} or stream-K grid in {256, 512, 1024}) x swap_ab) minus those
+ * that cannot pay off or duplicate another (split_k above the K-steps,
+ * unroll above the K-steps per wave, partials above twice the weight bytes,
+ * fewer than min(256, most possible) waves), checks each
  * against the default config's output (bit-equal for W8A8_INT8, within 1e-2
  * relative for the FP8 formats) and times it as HIP graph replays over
  * rotating weight copies; the best on timing bank 1 are re-timed on bank 2,

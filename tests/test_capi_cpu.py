@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_and_status_strings(lib):
-    assert lib.w8_abi_version() == 1
+    assert lib.w8_abi_version() == 2
     assert lib.w8_status_string(2) == b"W8_E_UNSUPPORTED"
     assert lib.w8_status_string(99) == b"W8_E_UNKNOWN"
 
@@ -84,7 +84,7 @@ def test_config_rejects(w8, field, value):
 
 def test_config_rejects_abi_and_reserved(w8):
     cfg = w8.Config.make()
-    cfg.abi_version = 2
+    cfg.abi_version = 1
     assert not _valid(w8, "FP8_Dynamic", 4, 512, 1024, cfg)
     cfg = w8.Config.make()
     cfg.reserved[1] = 7
@@ -94,6 +94,56 @@ def test_config_rejects_abi_and_reserved(w8):
     cfg = w8.Config.make(tile_n=32, unroll=4)
     assert not _valid(w8, "FP8_Dynamic", 4, 512, 1024, cfg)
     assert _valid(w8, "FP8_Dynamic", 4, 512, 1024, w8.Config.make(tile_n=64, unroll=1, waves_k=16))
+
+
+def test_config_rejects_wave_shapes_and_grids(w8):
+    M, N, K = 4, 512, 1024                       # FP8: 8 K-steps
+    ok = w8.Config.make(tile_n=16, waves_k=1, waves_n=8, unroll=2)
+    assert _valid(w8, "FP8_Dynamic", M, N, K, ok)
+    for kw in (dict(waves_n=3), dict(waves_n=16), dict(waves_n=0),
+               dict(waves_n=2, waves_k=2),       # waves split either K or N
+               dict(grid=-1), dict(grid=256, split_k=2),
+               dict(waves_n=2, x_lds=0),         # side by side along N shares through LDS
+               dict(waves_k=16, x_lds=1), dict(x_lds=2)):
+        cfg = w8.Config.make(**dict(dict(tile_n=16, waves_k=1, unroll=2), **kw))
+        assert not _valid(w8, "FP8_Dynamic", M, N, K, cfg), kw
+    # stream-K: at most one workgroup per (tile, K-step) iteration
+    iters = (N // (16 * 4)) * (K // 128)         # 8 tiles of 4 waves x 8 K-steps = 64
+    assert _valid(w8, "FP8_Dynamic", M, N, K, w8.Config.make(tile_n=16, waves_k=1, waves_n=4,
+                                                              grid=iters))
+    assert not _valid(w8, "FP8_Dynamic", M, N, K, w8.Config.make(tile_n=16, waves_k=1,
+                                                                  waves_n=4, grid=iters + 1))
+    # x_lds: the workgroup's K range of activations must fit in 64 KiB
+    # (ceil(M/16) x K-steps x K-step/64 chunks of 1 KiB)
+    K2 = 7168                                    # FP8: 56 K-steps, 2 chunks each
+    assert _valid(w8, "FP8_Dynamic", 16, N, K2, w8.Config.make(waves_k=1, x_lds=1, split_k=2))
+    assert not _valid(w8, "FP8_Dynamic", 16, N, K2, w8.Config.make(waves_k=1, x_lds=1))
+    assert not _valid(w8, "FP8_Dynamic", 32, N, K2, w8.Config.make(waves_k=1, x_lds=1,
+                                                                   split_k=2))
+    assert _valid(w8, "FP8_Dynamic", 32, N, K2, w8.Config.make(waves_k=1, x_lds=1, split_k=4))
+
+
+def _max_contributors(I, G, KS, T):
+    # by definition: workgroup g owns iterations [g*I//G, (g+1)*I//G)
+    starts = [g * I // G for g in range(G + 1)]
+    most = 0
+    for t in range(T):
+        lo, hi = t * KS, (t + 1) * KS
+        most = max(most, sum(1 for g in range(G) if starts[g] < hi and starts[g + 1] > lo))
+    return most
+
+
+@pytest.mark.parametrize("N,K,grid", [(512, 7168, 256), (4608, 7168, 256), (4608, 7168, 1024),
+                                      (896, 1024, 256), (896, 1024, 448), (5120, 640, 512),
+                                      (272, 640, 7), (80, 256, 3)])
+def test_stream_k_workspace_covers_every_tile(w8, N, K, grid):
+    cfg = w8.Config.make(tile_n=32, waves_k=1, waves_n=1, unroll=1, grid=grid)
+    KS = K // 64                                 # W8A8_INT8 K-steps
+    T = -(-N // 32)
+    need = w8.workspace_size("W8A8_INT8", 20, N, K, cfg)
+    slots = (need - 65536) // (T * 2 * 2 * 1024)  # 2 row blocks per tile, 2 blocks of M
+    assert need == 65536 + T * slots * 2 * 2 * 1024
+    assert slots >= _max_contributors(T * KS, grid, KS, T)
 
 
 def test_config_rejects_grid_overflow(w8):
@@ -208,14 +258,18 @@ def test_table_roundtrip_and_lookup(w8, tmp_path):
 def test_table_malformed_keeps_old_table(w8, tmp_path):
     w8.set_config("W8A8_INT8", 16, 896, 1024, w8.Config.make(), 1.0)
     bad_files = [
-        "gfx950 1 W8A8_INT8 row 16 896 1024 16 4 2 1\n",                    # too few fields
-        "gfx950 1 INT4 row 16 896 1024 16 4 2 1 0 1.0\n",                   # unknown format
-        "gfx950 1 W8A8_INT8 tiled 16 896 1024 16 4 2 1 0 1.0\n",            # unknown layout
-        "gfx950 1 W8A8_INT8 row 16 896 1024 16 4 2 3 0 1.0\n",              # split_k 3
-        "gfx950 1 W8A8_INT8 row 40 896 1024 16 4 2 1 0 1.0\n",              # M above 32
-        "gfx950 1 W8A8_INT8 row 16 896 1024 16 4 x 1 0 1.0\n",              # not an integer
-        "gfx950 1 W8A8_INT8 row 16 896 1024 16 4 2 1 0 fast\n",             # bad time
-        "gfx950 1 W8A8_INT8 row 16 896 1024 64 4 2 1 0 1.0\n",              # tile 64 x unroll 2
+        "gfx950 2 W8A8_INT8 row 16 896 1024 16 4 1 2 1 0\n",                # too few fields
+        "gfx950 2 INT4 row 16 896 1024 16 4 1 2 1 0 0 0 1.0\n",               # unknown format
+        "gfx950 2 W8A8_INT8 tiled 16 896 1024 16 4 1 2 1 0 0 0 1.0\n",        # unknown layout
+        "gfx950 2 W8A8_INT8 row 16 896 1024 16 4 1 2 3 0 0 0 1.0\n",          # split_k 3
+        "gfx950 2 W8A8_INT8 row 40 896 1024 16 4 1 2 1 0 0 0 1.0\n",          # M above 32
+        "gfx950 2 W8A8_INT8 row 16 896 1024 16 4 1 x 1 0 0 0 1.0\n",          # not an integer
+        "gfx950 2 W8A8_INT8 row 16 896 1024 16 4 1 2 1 0 0 0 fast\n",         # bad time
+        "gfx950 2 W8A8_INT8 row 16 896 1024 64 4 1 2 1 0 0 0 1.0\n",          # tile 64 x unroll 2
+        "gfx950 2 W8A8_INT8 row 16 896 1024 16 2 2 2 1 0 0 0 1.0\n",          # waves_k and waves_n
+        "gfx950 2 W8A8_INT8 row 16 896 1024 16 1 1 2 2 256 0 0 1.0\n",        # grid with split_k
+        "gfx950 2 W8A8_INT8 row 16 896 1024 16 1 1 2 1 100000 0 0 1.0\n",     # grid > iterations
+        "gfx950 2 W8A8_INT8 row 16 896 1024 16 16 1 2 1 0 0 1 1.0\n",        # x_lds, 16 waves
     ]
     for i, text in enumerate(bad_files):
         p = tmp_path / f"bad{i}.tbl"
@@ -231,22 +285,24 @@ def test_table_malformed_keeps_old_table(w8, tmp_path):
 
 def test_table_foreign_entries_ignored_and_kept(w8, tmp_path):
     p = tmp_path / "mixed.tbl"
-    p.write_text("gfx942 1 FP8_Dynamic row 4 4096 4096 64 2 4 1 1 2.0\n"
-                 "gfx950 9 FP8_Dynamic row 4 4096 4096 64 2 4 1 1 2.0\n"
-                 "gfx950 1 FP8_Dynamic row 4 4096 4096 32 2 2 4 0 2.5  # native\n")
+    p.write_text("gfx942 2 FP8_Dynamic row 4 4096 4096 64 2 1 4 1 0 1 0 2.0\n"
+                 "gfx950 9 FP8_Dynamic row 4 4096 4096 64 2 1 4 1 0 1 2.0\n"
+                 "gfx950 1 FP8_Dynamic row 4 4096 4096 32 2 2 4 0 2.5\n"
+                 "gfx950 2 FP8_Dynamic row 4 4096 4096 32 2 1 2 4 0 0 0 2.5  # native\n")
     w8.load_config_table(str(p))
-    assert w8.config_table_size() == 1 and w8.config_table_foreign() == 2
+    assert w8.config_table_size() == 1 and w8.config_table_foreign() == 3
     assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096) == \
         w8.Config.make(tile_n=32, waves_k=2, unroll=2, split_k=4, swap_ab=0)
     q = tmp_path / "out.tbl"
     w8.save_config_table(str(q))
     text = q.read_text()
-    assert "gfx942 1 FP8_Dynamic row" in text and "gfx950 9 FP8_Dynamic row" in text
+    assert "gfx942 2 FP8_Dynamic row" in text and "gfx950 9 FP8_Dynamic row" in text
+    assert "gfx950 1 FP8_Dynamic row 4 4096 4096 32 2 2 4 0 2.5" in text   # older ABI, kept
 
 
 def test_table_from_environment(tmp_path):
     p = tmp_path / "env.tbl"
-    p.write_text("gfx950 1 W8A8_INT8 row 16 896 1024 32 2 2 8 1 0.5\n")
+    p.write_text("gfx950 2 W8A8_INT8 row 16 896 1024 32 2 1 2 8 0 1 0 0.5\n")
     code = ("import bit_quantized_gemm_token_amd as w8;"
             "c = w8.lookup_config('W8A8_INT8', 16, 896, 1024);"
             "print(c.as_dict() if c else None)")
@@ -262,7 +318,7 @@ def test_table_from_environment(tmp_path):
 
 def test_env_table_loaded_by_the_c_library_alone(tmp_path):
     p = tmp_path / "env.tbl"
-    p.write_text("gfx950 1 W8A8_INT8 row 16 896 1024 32 2 2 8 1 0.5\n")
+    p.write_text("gfx950 2 W8A8_INT8 row 16 896 1024 32 2 1 2 8 0 1 0 0.5\n")
     from bit_quantized_gemm_token_amd import _capi
     # load _capi.py on its own (the package __init__ would load the shipped table)
     code = (

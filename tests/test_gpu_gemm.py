@@ -122,22 +122,50 @@ def test_split_k_sweep_512x7168(w8, fmt, M):
             assert_bf16_close(full_path(w8, cs, cfg), cs.Y, f"{fmt} M={M} split_k={s}")
 
 
+# (waves_k, waves_n, x_lds)
+WAVE_SHAPES = ((1, 1, 0), (2, 1, 0), (4, 1, 0), (8, 1, 0), (16, 1, 0), (1, 1, 1), (2, 1, 1),
+               (4, 1, 1), (8, 1, 1), (1, 2, 1), (1, 4, 1), (1, 8, 1))
+
+
 @pytest.mark.parametrize("fmt", ["W8A8_INT8", "FP8_Dynamic", "Block_FP8"])
 def test_every_tile_config(w8, fmt):
-    """Every (tile_n, waves_k, unroll, swap_ab, layout) instance at one ragged
-    shape (M = 17 needs both 16-row blocks of M), with and without split-K."""
+    """Every (tile_n, waves_k x waves_n, x_lds, unroll, swap_ab, layout)
+    instance at one ragged shape (M = 17 needs both 16-row blocks of M),
+    whole tiles, split-K and stream-K (3 and 7 workgroups: several tiles and
+    partial tiles per workgroup)."""
     M, N, K = (17, 200, 1280)
     cs = case(fmt, M, N, K)
     xq, sx = cs.gpu_act()
     n = 0
-    for tn, wk, u, swap, s, packed in itertools.product((16, 32, 64), (1, 2, 4, 8, 16),
-                                                        (1, 2, 4), (0, 1), (1, 4), (0, 1)):
+    for tn, (wk, wn, xl), u, swap, (s, grid), packed in itertools.product(
+            (16, 32, 64), WAVE_SHAPES, (1, 2, 4), (0, 1), ((1, 0), (4, 0), (1, 3), (1, 7)),
+            (0, 1)):
         if (tn // 16) * u > 4:
             continue
-        cfg = C(w8, tile_n=tn, waves_k=wk, unroll=u, split_k=s, swap_ab=swap)
+        cfg = C(w8, tile_n=tn, waves_k=wk, waves_n=wn, unroll=u, split_k=s, grid=grid,
+                swap_ab=swap, x_lds=xl)
         acc_check(w8, cs, xq, sx, cfg, f"{fmt} {cfg} packed={packed}", bool(packed))
         n += 1
-    assert n == 6 * 5 * 2 * 2 * 2
+    assert n == 6 * 12 * 2 * 4 * 2
+
+
+@pytest.mark.parametrize("fmt,M", [("W8A8_INT8", 32), ("FP8_Dynamic", 16), ("Block_FP8", 1),
+                                   ("Block_FP8", 32)])
+def test_stream_k_and_shared_activations_large(w8, fmt, M):
+    """Stream-K grids of 256/512/1024 workgroups, activations staged in LDS
+    and waves side by side along N at a large shape (288 row blocks, 56 or
+    112 K-steps: tiles shared by up to several workgroups), accumulators
+    against the oracle."""
+    cs = case(fmt, M, 4608, 7168)
+    xq, sx = cs.gpu_act()
+    for tn, wk, wn, u, s, grid, swap, xl in (
+            (16, 1, 8, 2, 1, 256, 0, 1), (16, 1, 4, 1, 1, 512, 1, 1), (32, 2, 1, 2, 1, 1024, 0, 0),
+            (16, 1, 2, 4, 1, 1024, 1, 1), (64, 1, 8, 1, 4, 0, 0, 1), (16, 4, 1, 2, 1, 512, 1, 0),
+            (16, 2, 1, 2, 4, 0, 0, 1), (32, 1, 1, 1, 8, 0, 1, 1)):
+        cfg = C(w8, tile_n=tn, waves_k=wk, waves_n=wn, unroll=u, split_k=s, grid=grid,
+                swap_ab=swap, x_lds=xl)
+        acc_check(w8, cs, xq, sx, cfg, f"{fmt} M={M} {cfg} packed", True)
+    assert_bf16_close(full_path(w8, cs, cfg, True), cs.Y, f"{fmt} M={M} stream-K path")
 
 
 @pytest.mark.parametrize("fmt,M,N,K", [
@@ -152,7 +180,11 @@ def test_ragged_shapes(w8, fmt, M, N, K):
     assert np.array_equal(u8(xq), cs.xq_ref)
     for packed in (False, True):
         for cfg in (None, C(w8, tile_n=32, waves_k=2, unroll=2, split_k=8, swap_ab=0),
-                    C(w8, tile_n=64, waves_k=1, unroll=1, split_k=2, swap_ab=1)):
+                    C(w8, tile_n=64, waves_k=1, unroll=1, split_k=2, swap_ab=1),
+                    C(w8, tile_n=16, waves_k=1, waves_n=4, unroll=2,
+                      grid=min(5, -(-N // 64) * -(-K // (64 if fmt == "W8A8_INT8" else 128))),
+                      swap_ab=0),
+                    C(w8, tile_n=16, waves_k=1, waves_n=8, unroll=1, split_k=2, swap_ab=1)):
             acc_check(w8, cs, xq, sx, cfg, f"ragged {cfg} packed={packed}", packed)
             assert_bf16_close(full_path(w8, cs, cfg, packed), cs.Y, f"ragged {fmt} {cfg}")
 
@@ -209,9 +241,18 @@ def test_split_k_deterministic_and_counters_reset(w8):
     torch.cuda.synchronize()
     for y in ys[1:]:
         assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
-    ntiles = 1024 // 16
     assert need > 65536
     assert (ws.buf[:65536].cpu() == 0).all()
+    # stream-K with shared activations: same properties
+    cfg = C(w8, tile_n=16, waves_k=1, waves_n=4, unroll=2, grid=96, swap_ab=0)
+    ws2 = w8.Workspace(DEV, w8.workspace_size("FP8_Dynamic", 8, 1024, 4096, cfg, packed=True))
+    zs = [w8.gemm_w8a8("FP8_Dynamic", xq, sx, cs.packed(), cs.sw, cfg=cfg, workspace=ws2)
+          for _ in range(3)]
+    torch.cuda.synchronize()
+    for z in zs[1:]:
+        assert torch.equal(z.view(torch.int16), zs[0].view(torch.int16))
+    assert (ws2.buf[:65536].cpu() == 0).all()
+    assert_bf16_close(zs[0], cs.Y, "stream-K")
 
 
 def test_unsupported_m_raises(w8):
@@ -224,12 +265,17 @@ def test_unsupported_m_raises(w8):
         w8.gemm_w8a8("FP8_Dynamic", xq, torch.ones(33, device=DEV), wq, torch.ones(64, device=DEV))
 
 
-def test_graph_capture_replay(w8):
-    """quantize + GEMM (split-K) captured once, replayed with eager work in
-    between; every replay equals the eager result bit for bit."""
+@pytest.mark.parametrize("kind", ["split_k", "stream_k"])
+def test_graph_capture_replay(w8, kind):
+    """quantize + GEMM (split-K, or stream-K with shared activations) captured
+    once, replayed with eager work in between; every replay equals the eager
+    result bit for bit."""
     cs = case("Block_FP8", 8, 4608, 7168)
-    cfg = C(w8, tile_n=16, waves_k=4, unroll=2, split_k=8, swap_ab=1)
-    ws = w8.Workspace(DEV, w8.workspace_size("Block_FP8", 8, 4608, 7168, cfg))
+    if kind == "split_k":
+        cfg = C(w8, tile_n=16, waves_k=4, unroll=2, split_k=8, swap_ab=1)
+    else:
+        cfg = C(w8, tile_n=16, waves_k=1, waves_n=8, unroll=2, grid=512, swap_ab=1)
+    ws = w8.Workspace(DEV, w8.workspace_size("Block_FP8", 8, 4608, 7168, cfg, packed=True))
     wp = cs.packed()
     eager = w8.linear("Block_FP8", cs.x, wp, cs.sw, cfg=cfg, workspace=ws).clone()
     x_static = cs.x.clone()
