@@ -356,7 +356,8 @@ def load_default_table():
 
 # -------------------------------------------------------------------- tuner --
 def tune_shape(fmt, M, N, K, warmup=2, replays=5, bank2_top=5, rotate_bytes=512 << 20,
-               max_split_k=MAX_SPLIT_K, insert=True, fail_candidate=-1, packed=False):
+               max_split_k=MAX_SPLIT_K, insert=True, fail_candidate=-1, packed=False,
+               stream_k=False):
     """Ahead-of-time tuning of one shape and weight layout on the current device.
 
     Returns (Config, stats dict).  Synchronizes the device.
@@ -367,6 +368,7 @@ def tune_shape(fmt, M, N, K, warmup=2, replays=5, bank2_top=5, rotate_bytes=512 
     o.rotate_bytes, o.max_split_k = rotate_bytes, max_split_k
     o.insert, o.fail_candidate = int(bool(insert)), fail_candidate
     o.packed = int(bool(packed))
+    o.stream_k = int(bool(stream_k))
     best = Config()
     stats = TuneStats()
     _check(_lib.w8_tune_shape(_fmt(fmt), M, N, K, ctypes.byref(o), ctypes.byref(best),

@@ -60,7 +60,8 @@ class TuneOpts(ctypes.Structure):
                 ("replays", ctypes.c_int32), ("bank2_top", ctypes.c_int32),
                 ("rotate_bytes", ctypes.c_int64), ("max_split_k", ctypes.c_int32),
                 ("insert", ctypes.c_int32), ("fail_candidate", ctypes.c_int32),
-                ("packed", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
+                ("packed", ctypes.c_int32), ("stream_k", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 1)]
 
 
 class TuneStats(ctypes.Structure):

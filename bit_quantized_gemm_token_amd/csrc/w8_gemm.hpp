@@ -431,8 +431,8 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (threadIdx.x == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned prev = __hip_atomic_fetch_add(&a.counters[tile * kCounterWords], 1u,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         is_last = (prev == (unsigned)(count - 1));
       }
       __syncthreads();
@@ -443,19 +443,40 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
           for (int b = 0; b < MB; ++b)
 #pragma unroll
             for (int j = 0; j < NB; ++j) acc[b][j] = Acc{0, 0, 0, 0};
-          for (int s = 0; s < count; ++s)
+          // Slots are read in batches of Q, all loads of a batch in flight
+          // at once (a slot past the end rereads the last one and adds 0),
+          // then added in slot order.
+          constexpr int Q = (NB * MB >= 8) ? 1 : 8 / (NB * MB);
+          for (int s0 = 0; s0 < count; s0 += Q) {
+            Word v[Q][NB][MB][4];
 #pragma unroll
-            for (int j = 0; j < NB; ++j)
+            for (int q = 0; q < Q; ++q) {
+              const long long sl = min(s0 + q, count - 1);
 #pragma unroll
-              for (int b = 0; b < MB; ++b)
+              for (int j = 0; j < NB; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  acc[b][j][i] += __hip_atomic_load(
-                      part + (((f0 + (long long)s * WN * NB + j) * MB + b) * 4 + i) * 64 + lane,
-                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int b = 0; b < MB; ++b)
+#pragma unroll
+                  for (int i = 0; i < 4; ++i)
+                    v[q][j][b][i] = __hip_atomic_load(
+                        part + (((f0 + sl * WN * NB + j) * MB + b) * 4 + i) * 64 + lane,
+                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+              const bool in = s0 + q < count;
+#pragma unroll
+              for (int j = 0; j < NB; ++j)
+#pragma unroll
+                for (int b = 0; b < MB; ++b)
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) acc[b][j][i] += in ? v[q][j][b][i] : Word(0);
+            }
+          }
         }
         if (threadIdx.x == 0)
-          __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&a.counters[tile * kCounterWords], 0u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     if (!store || wk != 0) return;

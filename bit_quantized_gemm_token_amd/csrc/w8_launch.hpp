@@ -78,17 +78,20 @@ inline int kstep_of(int fmt) { return fmt == 1 ? 64 : 128; }
 // segment, 64 KiB, so two workgroups fit in a compute unit's 160 KiB.
 constexpr int kXlChunks = 64;
 
-// Workspace layout: a fixed 64 KiB counter region (one 4-byte arrival counter
-// per output tile, at most kSplitKMaxTiles tiles), then the partials: one
-// 1 KiB fragment (64 lanes x 16 bytes) per (tile, slot, 16-row block of N,
-// 16-row block of M), with split_k slots per tile for Split-K and
-// stream_k_slots() for stream-K.  The counter region has the same size for
-// every shape, so the partials of one call never overlap the counters of
-// another call that shares the workspace: counters left at zero stay zero.
+// Workspace layout: a fixed 2 MiB counter region (one 4-byte arrival counter
+// per output tile in its own 128-byte cache line -- counters of neighbouring
+// tiles sharing a line serialize their device-scope atomics -- for at most
+// kSplitKMaxTiles tiles), then the partials: one 1 KiB fragment (64 lanes x
+// 16 bytes) per (tile, slot, 16-row block of N, 16-row block of M), with
+// split_k slots per tile for Split-K and stream_k_slots() for stream-K.  The
+// counter region has the same size for every shape, so the partials of one
+// call never overlap the counters of another call that shares the
+// workspace: counters left at zero stay zero.
 constexpr int kSplitKMaxTiles = 16384;
+constexpr int kCounterWords = 32;  // counter stride, 128 bytes
 inline size_t ws_counter_bytes(int ntiles) {
   (void)ntiles;
-  return (size_t)kSplitKMaxTiles * 4;
+  return (size_t)kSplitKMaxTiles * kCounterWords * 4;
 }
 inline size_t ws_partial_bytes(int ntiles, int slots, int row_blocks, int mb) {
   return (size_t)ntiles * slots * row_blocks * mb * 1024;

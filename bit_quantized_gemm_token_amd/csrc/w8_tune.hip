@@ -117,6 +117,7 @@ extern "C" void w8_tune_default_opts(w8_tune_opts* o) {
   o->insert = 1;
   o->fail_candidate = -1;
   o->packed = 0;
+  o->stream_k = 0;
 }
 
 extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tune_opts* opts,
@@ -151,10 +152,10 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
 
   // Candidates: every config of the family -- (waves_k, waves_n, x_lds) in
   // {(1..16, 1, 0), (1..8, 1, 1), (1, 2..8, 1)}, each with split_k up to
-  // max_split_k or with a
+  // max_split_k or (opts.stream_k) with a
   // stream-K grid of 256, 512 or 1024 workgroups (1, 2 or 4 per compute
   // unit) -- minus those that cannot pay off or cannot differ from another:
-  //   - split_k above the number of K-steps (only empty splits added);
+  //   - fewer than one K-step per wave (only empty splits or waves added);
   //   - unroll above the K-steps each wave owns (the loop would never run a
   //     full stage, so the candidate equals the one with a smaller unroll);
   //   - partial traffic above twice the weight bytes;
@@ -180,9 +181,9 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
     // K-steps per wave
     const long long per_wave = c.grid > 0 ? (long long)tiles_of(N, c) * T / (c.grid * c.waves_k)
                                           : (long long)T / (c.split_k * c.waves_k);
-    if (c.grid == 0 && c.split_k > T) return;
+    if (per_wave < 1) return;
     if (c.unroll > 1 && per_wave < c.unroll) return;
-    if (workspace_bytes(fmt, M, N, K, c) > 2 * wbytes + 65536 + (size_t)kSplitKMaxTiles * 4) return;
+    if (workspace_bytes(fmt, M, N, K, c) > 2 * wbytes + ws_counter_bytes(0)) return;
     all.push_back(c);
     most_waves = std::max(most_waves, total_waves(c));
   };
@@ -205,6 +206,7 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
             consider(c);
           }
           for (int gr : grids) {
+            if (!o.stream_k) break;
             c.split_k = 1;
             c.grid = gr;
             consider(c);

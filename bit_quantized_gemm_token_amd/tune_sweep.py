@@ -48,6 +48,7 @@ def main(argv=None):
     p.add_argument("--max-split-k", type=int, default=w8.MAX_SPLIT_K)
     p.add_argument("--rotate-mib", type=int, default=512)
     p.add_argument("--replays", type=int, default=5)
+    p.add_argument("--stream-k", action="store_true", help="also try stream-K grids")
     p.add_argument("--time-budget-s", type=float, default=0.0,
                    help="stop starting new shapes after this many seconds (0 = no limit)")
     a = p.parse_args(argv)
@@ -73,7 +74,7 @@ def main(argv=None):
                     return 0
                 best, st = w8.tune_shape(fmt, M, N, K, rotate_bytes=a.rotate_mib << 20,
                                          replays=a.replays, max_split_k=a.max_split_k, insert=True,
-                                         packed=packed)
+                                         packed=packed, stream_k=a.stream_k)
                 w8.save_config_table(a.out)
                 done += 1
                 print(f"[tune] {fmt} {'packed' if packed else 'row'} {M}x{N}x{K}: {best} "

@@ -142,7 +142,9 @@ typedef struct {
     int32_t fail_candidate;   /* test hook: candidate with this index fails validation
                                  (-1 = none) */
     int32_t packed;           /* weight layout tuned: 0 row-major, 1 packed */
-    int32_t reserved[2];
+    int32_t stream_k;         /* 1: also try stream-K grids (default 0: on the
+                                 shapes measured so far they never won) */
+    int32_t reserved[1];
 } w8_tune_opts;
 
 typedef struct {
@@ -209,7 +211,7 @@ w8_status w8_pack_weight(w8_fmt fmt, int N, int K, const void *wq, int64_t ldw, 
  * (cfg NULL: the config w8_resolve_config picks for that weight layout;
  * packed = 1 for packed weights).  0 when no tile is shared between
  * workgroups (split_k == 1 and grid == 0).
- * Layout: a fixed 64 KiB region of arrival counters, then the partials of
+ * Layout: a fixed 2 MiB region of arrival counters, then the partials of
  * shared tiles; split_k > 1 and grid > 0 therefore support at most 16384
  * output tiles (N <= 16384 * tile_n * waves_n).                             */
 w8_status w8_workspace_size(w8_fmt fmt, int M, int N, int K, int packed, const w8_cfg *cfg,
@@ -297,10 +299,11 @@ w8_status w8_lookup_config(w8_fmt fmt, int M, int N, int K, int packed, w8_cfg *
  * weight layout (opts->packed).  Allocates its own inputs (random codes and
  * scales), enumerates the configs of the family
  * (tile_n x (waves_k or waves_n) x x_lds x unroll x (split_k in {1, 2, ...,
- * max_split_k} or stream-K grid in {256, 512, 1024}) x swap_ab) minus those
- * that cannot pay off or duplicate another (split_k above the K-steps,
- * unroll above the K-steps per wave, partials above twice the weight bytes,
- * fewer than min(256, most possible) waves), checks each
+ * max_split_k}, or with opts->stream_k a stream-K grid in {256, 512, 1024})
+ * x swap_ab) minus those that cannot pay off or duplicate another (fewer
+ * than one K-step per wave, unroll above the K-steps per wave, partials
+ * above twice the weight bytes, fewer than min(256, most possible) waves),
+ * checks each
  * against the default config's output (bit-equal for W8A8_INT8, within 1e-2
  * relative for the FP8 formats) and times it as HIP graph replays over
  * rotating weight copies; the best on timing bank 1 are re-timed on bank 2,

@@ -141,8 +141,8 @@ def test_stream_k_workspace_covers_every_tile(w8, N, K, grid):
     KS = K // 64                                 # W8A8_INT8 K-steps
     T = -(-N // 32)
     need = w8.workspace_size("W8A8_INT8", 20, N, K, cfg)
-    slots = (need - 65536) // (T * 2 * 2 * 1024)  # 2 row blocks per tile, 2 blocks of M
-    assert need == 65536 + T * slots * 2 * 2 * 1024
+    slots = (need - COUNTERS) // (T * 2 * 2 * 1024)  # 2 row blocks per tile, 2 blocks of M
+    assert need == COUNTERS + T * slots * 2 * 2 * 1024
     assert slots >= _max_contributors(T * KS, grid, KS, T)
 
 
@@ -166,6 +166,7 @@ def test_default_config_is_valid_everywhere(w8):
 
 
 FAKE = ctypes.c_void_p(0x100000)   # 16-byte aligned, never dereferenced
+COUNTERS = 16384 * 128              # workspace arrival-counter region
 
 
 def _gemm(lib, fmt=0, M=4, N=64, K=256, xq=FAKE, ldq=256, sx=FAKE, wq=FAKE, ldw=256, sw=FAKE,
@@ -193,11 +194,12 @@ def test_gemm_workspace_errors(w8, lib):
     assert _gemm(lib, K=1024, ldq=1024, ldw=1024, cfg=ctypes.byref(cfg), ws=FAKE, wsb=need - 1) == 3
     assert b"workspace" in lib.w8_last_error()
     assert w8.workspace_size("FP8_Dynamic", 4, 64, 1024, w8.Config.make(split_k=1)) == 0
-    # counters (64 KiB) + one 1 KiB fragment per (tile, split, row block, M block)
-    assert need == 65536 + 4 * 8 * 1 * 1 * 1024
+    # counters (one per 128-byte line, 16384 tiles: 2 MiB) + one 1 KiB fragment
+    # per (tile, split, row block, M block)
+    assert need == COUNTERS + 4 * 8 * 1 * 1 * 1024
     assert w8.workspace_size("FP8_Dynamic", 20, 64, 1024, w8.Config.make(tile_n=32, unroll=2,
                                                                          split_k=8)) == \
-        65536 + 2 * 8 * 2 * 2 * 1024
+        COUNTERS + 2 * 8 * 2 * 2 * 1024
 
 
 def test_pack_argument_errors(w8, lib):

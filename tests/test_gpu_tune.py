@@ -26,14 +26,14 @@ def _restore_table(w8):
     w8.load_default_table()
 
 
-@pytest.mark.parametrize("fmt,M,N,K,packed", [("W8A8_INT8", 16, 896, 1024, False),
-                                              ("FP8_Dynamic", 4, 512, 2048, True),
-                                              ("Block_FP8", 8, 512, 1024, False),
-                                              ("Block_FP8", 8, 512, 1024, True)])
-def test_tune_shape(w8, fmt, M, N, K, packed, tmp_path):
-    print(f"[tune] {fmt} M={M} N={N} K={K} packed={packed}", flush=True)
+@pytest.mark.parametrize("fmt,M,N,K,packed,stream_k", [("W8A8_INT8", 16, 896, 1024, False, False),
+                                                       ("FP8_Dynamic", 4, 512, 2048, True, True),
+                                                       ("Block_FP8", 8, 512, 1024, False, False),
+                                                       ("Block_FP8", 32, 512, 1024, True, False)])
+def test_tune_shape(w8, fmt, M, N, K, packed, stream_k, tmp_path):
+    print(f"[tune] {fmt} M={M} N={N} K={K} packed={packed} stream_k={stream_k}", flush=True)
     w8.clear_config_table()
-    best, st = w8.tune_shape(fmt, M, N, K, packed=packed, **SMALL)
+    best, st = w8.tune_shape(fmt, M, N, K, packed=packed, stream_k=stream_k, **SMALL)
     print(f"[tune] best {best} stats {st}", flush=True)
     w8.validate_config(fmt, M, N, K, best)
     assert st["candidates"] > 50 and st["validated"] == st["candidates"] and st["rejected"] == 0
