@@ -20,7 +20,7 @@ import os
 import torch
 
 from . import _capi
-from ._capi import (ABI_VERSION, FORMATS, FORMAT_NAMES, GROUP, MAX_M, MAX_SPLIT_K, Config,
+from ._capi import (ABI_VERSION, FORMATS, FORMAT_NAMES, GROUP, MAX_M, MAX_SPLIT_K, OPS, Config,
                     TuneOpts, TuneStats)
 
 _lib = _capi.load()
@@ -89,6 +89,14 @@ def _cfg_ptr(cfg):
     if isinstance(cfg, dict):
         cfg = Config.make(**cfg)
     return ctypes.byref(cfg)
+
+
+def _op(op):
+    if isinstance(op, str):
+        if op not in OPS:
+            raise ValueError(f"unknown op {op!r}; expected one of {list(OPS)}")
+        return OPS[op]
+    return int(op)
 
 
 def _codes_dtype(fmt):
@@ -170,9 +178,9 @@ def pack_weight(fmt, wq, stream=None):
 
 
 # --------------------------------------------------------------------- GEMM --
-def workspace_size(fmt, M, N, K, cfg=None, packed=False):
+def workspace_size(fmt, M, N, K, cfg=None, packed=False, op="gemm"):
     n = ctypes.c_size_t(0)
-    _check(_lib.w8_workspace_size(_fmt(fmt), M, N, K, int(bool(packed)), _cfg_ptr(cfg),
+    _check(_lib.w8_workspace_size(_fmt(fmt), _op(op), M, N, K, int(bool(packed)), _cfg_ptr(cfg),
                                   ctypes.byref(n)))
     return n.value
 
@@ -195,12 +203,24 @@ class Workspace:
             self.buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
         return self.buf
 
-    def for_call(self, fmt, M, N, K, cfg=None, packed=False):
-        need = workspace_size(fmt, M, N, K, cfg, packed)
+    def for_call(self, fmt, M, N, K, cfg=None, packed=False, op="gemm"):
+        need = workspace_size(fmt, M, N, K, cfg, packed, op)
         if need == 0:
             return None, 0
         buf = self.reserve(need)
         return ctypes.c_void_p(buf.data_ptr()), buf.numel()
+
+
+def _weights(f, wq):
+    """(N, K, ldw, pointer, packed) of row-major codes or a PackedWeight."""
+    if isinstance(wq, PackedWeight):
+        if wq.fmt != f:
+            raise ValueError("packed weights were packed for another format")
+        return wq.N, wq.K, 0, _dev_ptr(wq.data, "wq"), True
+    if wq.element_size() != 1:
+        raise TypeError("wq must hold 1-byte codes")
+    N, wk = wq.shape
+    return N, wk, _row_major(wq, "wq") * wq.element_size(), _dev_ptr(wq, "wq"), False
 
 
 def _gemm(entry, fmt, xq, sx, wq, sw, out, cfg, workspace, stream):
@@ -208,22 +228,14 @@ def _gemm(entry, fmt, xq, sx, wq, sw, out, cfg, workspace, stream):
     ldq = _row_major(xq, "xq") * xq.element_size()
     ldo = _row_major(out, "out")
     M, K = xq.shape
-    if isinstance(wq, PackedWeight):
-        if wq.fmt != f:
-            raise ValueError("packed weights were packed for another format")
-        N, wk, ldw, wptr, packed = wq.N, wq.K, 0, _dev_ptr(wq.data, "wq"), True
-    else:
-        N, wk = wq.shape
-        ldw, wptr, packed = _row_major(wq, "wq") * wq.element_size(), _dev_ptr(wq, "wq"), False
-        if wq.element_size() != 1:
-            raise TypeError("wq must hold 1-byte codes")
+    N, wk, ldw, wptr, packed = _weights(f, wq)
     if wk != K:
         raise ValueError(f"K mismatch: xq {tuple(xq.shape)} vs weights {(N, wk)}")
     if xq.element_size() != 1:
         raise TypeError("xq must hold 1-byte codes")
     if workspace is None:
         workspace = _default_workspace(xq.device)
-    ws_ptr, ws_bytes = workspace.for_call(f, M, N, K, cfg, packed)
+    ws_ptr, ws_bytes = workspace.for_call(f, M, N, K, cfg, packed, "gemm")
     _check(entry(f, M, N, K, _dev_ptr(xq, "xq"), ldq, _dev_ptr(sx, "sx", torch.float32),
                  wptr, ldw, _dev_ptr(sw, "sw", torch.float32),
                  _dev_ptr(out, "out"), ldo, _cfg_ptr(cfg), ws_ptr, ws_bytes,
@@ -267,42 +279,67 @@ def gemm_w8a8_acc(fmt, xq, sx, wq, sw, cfg=None, out=None, workspace=None, strea
     return _gemm(_lib.w8_gemm_w8a8_acc, fmt, xq, sx, wq, sw, out, cfg, workspace, stream)
 
 
-def linear(fmt, x, wq, sw, cfg=None, y=None, workspace=None, stream=None):
-    """The whole hot path: quantize bf16 activations, then the GEMM.
+def linear(fmt, x, wq, sw, cfg=None, y=None, workspace=None, stream=None, fused=False):
+    """The whole hot path on bf16 activations x [M, K].
 
-    wq: row-major codes [N, K] or a PackedWeight."""
-    xq, sx = quantize_act(fmt, x, stream=stream)
-    return gemm_w8a8(fmt, xq, sx, wq, sw, cfg=cfg, y=y, workspace=workspace, stream=stream)
+    fused=False: quantize_act, then gemm_w8a8 (two launches; cfg is the GEMM
+    config).  fused=True: w8_linear, quantization fused into the GEMM (one
+    launch; cfg must have x_lds=1, None = the table's "linear" entry).  Both
+    give the same Y for the same cfg.  wq: row-major codes [N, K] or a
+    PackedWeight."""
+    if not fused:
+        xq, sx = quantize_act(fmt, x, stream=stream)
+        return gemm_w8a8(fmt, xq, sx, wq, sw, cfg=cfg, y=y, workspace=workspace, stream=stream)
+    f = _fmt(fmt)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    ldx = _row_major(x, "x")
+    M, K = x.shape
+    N, wk, ldw, wptr, packed = _weights(f, wq)
+    if wk != K:
+        raise ValueError(f"K mismatch: x {tuple(x.shape)} vs weights {(N, wk)}")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    elif y.dtype != torch.bfloat16:
+        raise TypeError("y must be bfloat16")
+    if workspace is None:
+        workspace = _default_workspace(x.device)
+    ws_ptr, ws_bytes = workspace.for_call(f, M, N, K, cfg, packed, "linear")
+    _check(_lib.w8_linear(f, M, N, K, _dev_ptr(x, "x"), ldx, wptr, ldw,
+                          _dev_ptr(sw, "sw", torch.float32), _dev_ptr(y, "y"), _row_major(y, "y"),
+                          _cfg_ptr(cfg), ws_ptr, ws_bytes, _stream(stream, x.device)))
+    return y
 
 
 # ------------------------------------------------------------------- config --
-def validate_config(fmt, M, N, K, cfg):
-    _check(_lib.w8_validate_config(_fmt(fmt), M, N, K, _cfg_ptr(cfg)))
+# op: "gemm" (gemm_w8a8) or "linear" (linear(..., fused=True)).
+def validate_config(fmt, M, N, K, cfg, op="gemm"):
+    _check(_lib.w8_validate_config(_fmt(fmt), _op(op), M, N, K, _cfg_ptr(cfg)))
 
 
-def default_config(fmt, M, N, K):
+def default_config(fmt, M, N, K, op="gemm"):
     c = Config()
-    _check(_lib.w8_default_config(_fmt(fmt), M, N, K, ctypes.byref(c)))
+    _check(_lib.w8_default_config(_fmt(fmt), _op(op), M, N, K, ctypes.byref(c)))
     return c
 
 
-def resolve_config(fmt, M, N, K, packed=False):
-    """(Config, from_table) that gemm_w8a8 uses when cfg is None."""
+def resolve_config(fmt, M, N, K, packed=False, op="gemm"):
+    """(Config, from_table) that the op uses when cfg is None."""
     c = Config()
     hit = ctypes.c_int(0)
-    _check(_lib.w8_resolve_config(_fmt(fmt), M, N, K, int(bool(packed)), ctypes.byref(c),
-                                  ctypes.byref(hit)))
+    _check(_lib.w8_resolve_config(_fmt(fmt), _op(op), M, N, K, int(bool(packed)),
+                                  ctypes.byref(c), ctypes.byref(hit)))
     return c, bool(hit.value)
 
 
-def lookup_config(fmt, M, N, K, packed=False, with_time=False):
-    """Exact table entry for the shape and weight layout, or None.
+def lookup_config(fmt, M, N, K, packed=False, with_time=False, op="gemm"):
+    """Exact table entry for the op, shape and weight layout, or None.
 
-    with_time=True returns (Config, us_per_gemm) instead of the Config.
+    with_time=True returns (Config, us_per_call) instead of the Config.
     """
     c = Config()
     us = ctypes.c_double(0.0)
-    st = _lib.w8_lookup_config(_fmt(fmt), M, N, K, int(bool(packed)), ctypes.byref(c),
+    st = _lib.w8_lookup_config(_fmt(fmt), _op(op), M, N, K, int(bool(packed)), ctypes.byref(c),
                                ctypes.byref(us))
     if st == 8:
         return None
@@ -310,19 +347,19 @@ def lookup_config(fmt, M, N, K, packed=False, with_time=False):
     return (c, us.value) if with_time else c
 
 
-def best_layout(fmt, M, N, K):
+def best_layout(fmt, M, N, K, op="gemm"):
     """True if the table says packed weights are faster for this shape."""
-    row = lookup_config(fmt, M, N, K, packed=False, with_time=True)
-    pk = lookup_config(fmt, M, N, K, packed=True, with_time=True)
+    row = lookup_config(fmt, M, N, K, packed=False, with_time=True, op=op)
+    pk = lookup_config(fmt, M, N, K, packed=True, with_time=True, op=op)
     if pk is None:
         return False
     return row is None or pk[1] < row[1]
 
 
-def set_config(fmt, M, N, K, cfg, us_per_gemm=0.0, packed=False):
+def set_config(fmt, M, N, K, cfg, us_per_gemm=0.0, packed=False, op="gemm"):
     if isinstance(cfg, dict):
         cfg = Config.make(**cfg)
-    _check(_lib.w8_set_config(_fmt(fmt), M, N, K, int(bool(packed)), ctypes.byref(cfg),
+    _check(_lib.w8_set_config(_fmt(fmt), _op(op), M, N, K, int(bool(packed)), ctypes.byref(cfg),
                               float(us_per_gemm)))
 
 
@@ -357,7 +394,7 @@ def load_default_table():
 # -------------------------------------------------------------------- tuner --
 def tune_shape(fmt, M, N, K, warmup=2, replays=5, bank2_top=5, rotate_bytes=512 << 20,
                max_split_k=MAX_SPLIT_K, insert=True, fail_candidate=-1, packed=False,
-               stream_k=False):
+               stream_k=False, op="gemm"):
     """Ahead-of-time tuning of one shape and weight layout on the current device.
 
     Returns (Config, stats dict).  Synchronizes the device.
@@ -369,6 +406,7 @@ def tune_shape(fmt, M, N, K, warmup=2, replays=5, bank2_top=5, rotate_bytes=512 
     o.insert, o.fail_candidate = int(bool(insert)), fail_candidate
     o.packed = int(bool(packed))
     o.stream_k = int(bool(stream_k))
+    o.op = _op(op)
     best = Config()
     stats = TuneStats()
     _check(_lib.w8_tune_shape(_fmt(fmt), M, N, K, ctypes.byref(o), ctypes.byref(best),

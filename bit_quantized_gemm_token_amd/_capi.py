@@ -11,6 +11,7 @@ MAX_SPLIT_K = 256
 GROUP = 128
 
 FORMATS = {"FP8_Dynamic": 0, "W8A8_INT8": 1, "Block_FP8": 2}
+OPS = {"gemm": 0, "linear": 1}
 FORMAT_NAMES = {v: k for k, v in FORMATS.items()}
 
 STATUS = {0: "W8_OK", 1: "W8_E_INVALID", 2: "W8_E_UNSUPPORTED", 3: "W8_E_WORKSPACE",
@@ -20,7 +21,7 @@ STATUS = {0: "W8_OK", 1: "W8_E_INVALID", 2: "W8_E_UNSUPPORTED", 3: "W8_E_WORKSPA
 # Every symbol include/w8gemm.h declares.
 EXPORTS = ("w8_abi_version", "w8_status_string", "w8_last_error", "w8_quantize_act",
            "w8_quantize_weight", "w8_packed_weight_size", "w8_pack_weight",
-           "w8_workspace_size", "w8_gemm_w8a8", "w8_gemm_w8a8_acc",
+           "w8_workspace_size", "w8_gemm_w8a8", "w8_gemm_w8a8_acc", "w8_linear",
            "w8_validate_config", "w8_default_config", "w8_resolve_config",
            "w8_load_config_table", "w8_save_config_table", "w8_clear_config_table",
            "w8_config_table_size", "w8_config_table_foreign", "w8_set_config",
@@ -61,7 +62,7 @@ class TuneOpts(ctypes.Structure):
                 ("rotate_bytes", ctypes.c_int64), ("max_split_k", ctypes.c_int32),
                 ("insert", ctypes.c_int32), ("fail_candidate", ctypes.c_int32),
                 ("packed", ctypes.c_int32), ("stream_k", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 1)]
+                ("op", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
 
 
 class TuneStats(ctypes.Structure):
@@ -92,7 +93,7 @@ def load():
     lib.w8_quantize_act.restype = st
     lib.w8_quantize_weight.argtypes = [c_int, c_int, c_int, f32p, i64, vp, i64, f32p, vp]
     lib.w8_quantize_weight.restype = st
-    lib.w8_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int, cfgp,
+    lib.w8_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, cfgp,
                                       ctypes.POINTER(ctypes.c_size_t)]
     lib.w8_workspace_size.restype = st
     lib.w8_packed_weight_size.argtypes = [c_int, c_int, c_int, ctypes.POINTER(ctypes.c_size_t)]
@@ -105,11 +106,14 @@ def load():
     lib.w8_gemm_w8a8.restype = st
     lib.w8_gemm_w8a8_acc.argtypes = gemm_args
     lib.w8_gemm_w8a8_acc.restype = st
-    lib.w8_validate_config.argtypes = [c_int, c_int, c_int, c_int, cfgp]
+    lib.w8_linear.argtypes = [c_int, c_int, c_int, c_int, vp, i64, vp, i64, f32p, vp, i64, cfgp,
+                              vp, ctypes.c_size_t, vp]
+    lib.w8_linear.restype = st
+    lib.w8_validate_config.argtypes = [c_int, c_int, c_int, c_int, c_int, cfgp]
     lib.w8_validate_config.restype = st
-    lib.w8_default_config.argtypes = [c_int, c_int, c_int, c_int, cfgp]
+    lib.w8_default_config.argtypes = [c_int, c_int, c_int, c_int, c_int, cfgp]
     lib.w8_default_config.restype = st
-    lib.w8_resolve_config.argtypes = [c_int, c_int, c_int, c_int, c_int, cfgp,
+    lib.w8_resolve_config.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, cfgp,
                                       ctypes.POINTER(c_int)]
     lib.w8_resolve_config.restype = st
     lib.w8_load_config_table.argtypes = [ctypes.c_char_p]
@@ -119,9 +123,9 @@ def load():
     lib.w8_clear_config_table.restype = None
     lib.w8_config_table_size.restype = c_int
     lib.w8_config_table_foreign.restype = c_int
-    lib.w8_set_config.argtypes = [c_int, c_int, c_int, c_int, c_int, cfgp, ctypes.c_double]
+    lib.w8_set_config.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, cfgp, ctypes.c_double]
     lib.w8_set_config.restype = st
-    lib.w8_lookup_config.argtypes = [c_int, c_int, c_int, c_int, c_int, cfgp,
+    lib.w8_lookup_config.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, cfgp,
                                      ctypes.POINTER(ctypes.c_double)]
     lib.w8_lookup_config.restype = st
     lib.w8_tune_shape.argtypes = [c_int, c_int, c_int, c_int, ctypes.POINTER(TuneOpts), cfgp,

@@ -29,7 +29,7 @@ int u_index(int u) { return u == 1 ? 0 : u == 2 ? 1 : u == 4 ? 2 : -1; }
 
 // [fmt][mb-1][nb][wk][wn][unroll][swap][packed][xl] -> launcher
 struct InstanceIndex {
-  GemmLaunchFn fn[3][2][3][5][4][3][2][2][2] = {};
+  GemmLaunchFn fn[3][2][3][5][4][3][2][2][3] = {};
   InstanceIndex() {
     int n = 0;
     const GemmInstance* p = gemm_instances(&n);
@@ -93,8 +93,7 @@ w8_status check_gemm_shape(int fmt, int M, int N, int K) {
   return W8_OK;
 }
 
-w8_status check_cfg(int fmt, int M, int N, int K, const w8_cfg& c) {
-  (void)fmt, (void)M, (void)K;
+w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c) {
   if (c.abi_version != W8_ABI_VERSION)
     return fail(W8_E_INVALID, "cfg.abi_version " + std::to_string(c.abi_version) + " != " +
                                   std::to_string(W8_ABI_VERSION));
@@ -108,6 +107,9 @@ w8_status check_cfg(int fmt, int M, int N, int K, const w8_cfg& c) {
   if (c.x_lds != 0 && c.x_lds != 1) return fail(W8_E_INVALID, "cfg.x_lds must be 0 or 1");
   if (c.waves_n > 1 && !c.x_lds) return fail(W8_E_INVALID, "cfg: waves_n > 1 needs x_lds == 1");
   if (c.x_lds && c.waves_k > 8) return fail(W8_E_INVALID, "cfg: x_lds needs waves_k <= 8");
+  if (op != W8_OP_GEMM && op != W8_OP_LINEAR) return fail(W8_E_INVALID, "unknown op");
+  if (op == W8_OP_LINEAR && (!c.x_lds || c.waves_k > 4))
+    return fail(W8_E_INVALID, "cfg: the fused linear op needs x_lds == 1 and waves_k <= 4");
   if (u_index(c.unroll) < 0) return fail(W8_E_INVALID, "cfg.unroll must be 1, 2 or 4");
   if ((c.tile_n / 16) * c.unroll > 4)
     return fail(W8_E_INVALID, "cfg: tile_n/16 * unroll must be at most 4");
@@ -169,8 +171,10 @@ size_t workspace_bytes(int fmt, int M, int N, int K, const w8_cfg& c) {
 // follows the rule of thumb the page quotes for vLLM's Block_FP8 backend --
 // Swap-AB below 32 tokens -- for every format, and picks the smallest
 // split_k that gives at least two workgroups per compute unit while every
-// wave keeps at least one full stage of K-steps.
-w8_cfg make_default_cfg(int fmt, int M, int N, int K) {
+// wave keeps at least one full stage of K-steps.  The fused linear op stages
+// activations in LDS (x_lds), so it doubles split_k further until a
+// workgroup's K range of activations fits.
+w8_cfg make_default_cfg(int fmt, int op, int M, int N, int K) {
   w8_cfg c;
   std::memset(&c, 0, sizeof c);
   c.abi_version = W8_ABI_VERSION;
@@ -186,6 +190,12 @@ w8_cfg make_default_cfg(int fmt, int M, int N, int K) {
          T / (2 * s) >= c.waves_k * c.unroll)
     s *= 2;
   c.split_k = s;
+  if (op == W8_OP_LINEAR) {
+    c.x_lds = 1;
+    const long long per_step = (long long)((M + 15) / 16) * (kstep_of(fmt) / 64);
+    while (c.split_k < W8_MAX_SPLIT_K && (T + c.split_k - 1) / c.split_k * per_step > kXlChunks)
+      c.split_k *= 2;
+  }
   return c;
 }
 
@@ -212,12 +222,14 @@ w8_status launch_gemm_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
   const int nb = c.tile_n / 16;
   GemmLaunchFn fn =
       instance_index().fn[g.fmt][mb - 1][nb_index(nb)][wk_index(c.waves_k)][wn_index(c.waves_n)]
-                         [u_index(c.unroll)][c.swap_ab][g.packed ? 1 : 0][c.x_lds];
+                         [u_index(c.unroll)][c.swap_ab][g.packed ? 1 : 0][g.x ? 2 : c.x_lds];
   if (!fn) return fail(W8_E_INVALID, "no compiled kernel for this config");
   const int ntiles = tiles_of(g.N, c);
   GemmArgs a;
   a.xq = static_cast<const uint8_t*>(g.xq);
   a.sx = g.sx;
+  a.x = static_cast<const uint16_t*>(g.x);
+  a.ldx = g.ldx;
   a.wq = static_cast<const uint8_t*>(g.wq);
   a.sw = g.sw;
   a.out = g.out;
@@ -274,10 +286,10 @@ w8_status gemm_entry(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ld
   w8_cfg c;
   if (cfg) {
     c = *cfg;
-    st = check_cfg(fmt, M, N, K, c);
+    st = check_cfg(fmt, W8_OP_GEMM, M, N, K, c);
     if (st) return st;
   } else {
-    c = resolve_cfg(fmt, M, N, K, packed, nullptr);
+    c = resolve_cfg(fmt, W8_OP_GEMM, M, N, K, packed, nullptr);
   }
   const size_t need = workspace_bytes(fmt, M, N, K, c);
   if (need > 0) {
@@ -288,7 +300,8 @@ w8_status gemm_entry(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ld
   }
   st = check_device();
   if (st) return st;
-  GemmCall g{fmt, M, N, K, xq, ldq, sx, wq, ldw, sw, out, ldo, out_mode, ws, ws_bytes, packed};
+  GemmCall g{fmt, M, N, K, xq, ldq, sx, wq, ldw, sw, out, ldo, out_mode, ws, ws_bytes, packed,
+             nullptr, 0};
   st = launch_gemm_call(g, c, static_cast<hipStream_t>(stream));
   if (st) return st;
   return ok();
@@ -351,18 +364,19 @@ w8_status w8_quantize_weight(w8_fmt fmt, int N, int K, const float* w, int64_t l
   return ok();
 }
 
-w8_status w8_workspace_size(w8_fmt fmt, int M, int N, int K, int packed, const w8_cfg* cfg,
-                            size_t* bytes) {
+w8_status w8_workspace_size(w8_fmt fmt, w8_op op, int M, int N, int K, int packed,
+                            const w8_cfg* cfg, size_t* bytes) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!bytes) return fail(W8_E_INVALID, "null output pointer");
+  if (op != W8_OP_GEMM && op != W8_OP_LINEAR) return fail(W8_E_INVALID, "unknown op");
   w8_cfg c;
   if (cfg) {
     c = *cfg;
-    st = check_cfg(fmt, M, N, K, c);
+    st = check_cfg(fmt, op, M, N, K, c);
     if (st) return st;
   } else {
-    c = resolve_cfg(fmt, M, N, K, packed != 0, nullptr);
+    c = resolve_cfg(fmt, op, M, N, K, packed != 0, nullptr);
   }
   *bytes = workspace_bytes(fmt, M, N, K, c);
   return ok();
@@ -406,30 +420,70 @@ w8_status w8_gemm_w8a8_acc(w8_fmt fmt, int M, int N, int K, const void* xq, int6
                     1);
 }
 
-w8_status w8_validate_config(w8_fmt fmt, int M, int N, int K, const w8_cfg* cfg) {
+w8_status w8_linear(w8_fmt fmt, int M, int N, int K, const void* x, int64_t ldx, const void* wq,
+                    int64_t ldw, const float* sw, void* y, int64_t ldy, const w8_cfg* cfg,
+                    void* ws, size_t ws_bytes, w8_stream stream) {
+  w8_status st = check_gemm_shape(fmt, M, N, K);
+  if (st) return st;
+  if (!x || !wq || !sw || !y) return fail(W8_E_INVALID, "null device pointer");
+  if (!aligned(x, 16) || ldx % 8 || ldx < K)
+    return fail(W8_E_INVALID, "x must be 16-byte aligned with ldx >= K and ldx % 8 == 0");
+  if (!aligned(wq, 16)) return fail(W8_E_INVALID, "wq must be 16-byte aligned");
+  const int packed = ldw == 0;
+  if (!packed && (ldw < K || ldw % 16))
+    return fail(W8_E_INVALID, "ldw must be 0 (packed weights) or >= K and a multiple of 16");
+  if (ldy < N) return fail(W8_E_INVALID, "output leading dimension must be >= N");
+  if (!aligned(sw, 4) || !aligned(y, 2)) return fail(W8_E_INVALID, "misaligned sw or y");
+  w8_cfg c;
+  if (cfg) {
+    c = *cfg;
+    st = check_cfg(fmt, W8_OP_LINEAR, M, N, K, c);
+    if (st) return st;
+  } else {
+    c = resolve_cfg(fmt, W8_OP_LINEAR, M, N, K, packed, nullptr);
+  }
+  const size_t need = workspace_bytes(fmt, M, N, K, c);
+  if (need > 0) {
+    if (!ws || ws_bytes < need)
+      return fail(W8_E_WORKSPACE, "workspace of " + std::to_string(need) + " bytes needed, got " +
+                                      std::to_string(ws ? ws_bytes : 0));
+    if (!aligned(ws, 16)) return fail(W8_E_INVALID, "workspace must be 16-byte aligned");
+  }
+  st = check_device();
+  if (st) return st;
+  GemmCall g{fmt, M, N, K, nullptr, 0, nullptr, wq, ldw, sw, y, ldy, 0, ws, ws_bytes, packed,
+             x, ldx};
+  st = launch_gemm_call(g, c, static_cast<hipStream_t>(stream));
+  if (st) return st;
+  return ok();
+}
+
+w8_status w8_validate_config(w8_fmt fmt, w8_op op, int M, int N, int K, const w8_cfg* cfg) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!cfg) return fail(W8_E_INVALID, "null cfg");
-  st = check_cfg(fmt, M, N, K, *cfg);
+  st = check_cfg(fmt, op, M, N, K, *cfg);
   if (st) return st;
   return ok();
 }
 
-w8_status w8_default_config(w8_fmt fmt, int M, int N, int K, w8_cfg* out) {
+w8_status w8_default_config(w8_fmt fmt, w8_op op, int M, int N, int K, w8_cfg* out) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!out) return fail(W8_E_INVALID, "null output pointer");
-  *out = make_default_cfg(fmt, M, N, K);
+  if (op != W8_OP_GEMM && op != W8_OP_LINEAR) return fail(W8_E_INVALID, "unknown op");
+  *out = make_default_cfg(fmt, op, M, N, K);
   return ok();
 }
 
-w8_status w8_resolve_config(w8_fmt fmt, int M, int N, int K, int packed, w8_cfg* out,
+w8_status w8_resolve_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed, w8_cfg* out,
                             int* from_table) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!out) return fail(W8_E_INVALID, "null output pointer");
+  if (op != W8_OP_GEMM && op != W8_OP_LINEAR) return fail(W8_E_INVALID, "unknown op");
   int hit = 0;
-  *out = resolve_cfg(fmt, M, N, K, packed != 0, &hit);
+  *out = resolve_cfg(fmt, op, M, N, K, packed != 0, &hit);
   if (from_table) *from_table = hit;
   return ok();
 }

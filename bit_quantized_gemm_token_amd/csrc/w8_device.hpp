@@ -52,6 +52,48 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// ------------------------------------------------------ activation codes --
+// The activation quantizer's per-element steps, shared by the standalone
+// quantize kernels and the GEMM's fused-quantization staging so both give
+// the same codes: amax of eight bf16 values (one 16-byte chunk), and eight
+// bf16 values -> eight codes with code = encode(x / s) (correctly rounded
+// fp32 division: the library is built with -fhip-fp32-correctly-rounded-
+// divide-sqrt and without fast-math).
+__device__ __forceinline__ float absmax8(v4u v) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = fmaxf(m, fabsf(bf16_lo(v[i])));
+    m = fmaxf(m, fabsf(bf16_hi(v[i])));
+  }
+  return m;
+}
+
+template <bool INT8>
+__device__ __forceinline__ v2u encode8(v4u v, float s) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(v[i]) / s;
+    f[2 * i + 1] = bf16_hi(v[i]) / s;
+  }
+  v2u o;
+  if (INT8) {
+    o[0] = i8_pack4(f[0], f[1], f[2], f[3]);
+    o[1] = i8_pack4(f[4], f[5], f[6], f[7]);
+  } else {
+    o[0] = e4m3_pack4(f[0], f[1], f[2], f[3]);
+    o[1] = e4m3_pack4(f[4], f[5], f[6], f[7]);
+  }
+  return o;
+}
+
+// Scale of a group with absolute maximum amax (an all-zero group takes 1).
+template <bool INT8>
+__device__ __forceinline__ float act_scale(float amax) {
+  return (amax == 0.0f) ? 1.0f : amax / (INT8 ? kQmaxInt8 : kQmaxE4M3);
+}
+
 // ------------------------------------------------------------- reductions --
 // Max over the 64 lanes of a wavefront (every lane gets the result).
 __device__ __forceinline__ float wave_max(float v) {

@@ -156,10 +156,12 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
   constexpr bool BLOCK = (FMT == BLOCK_FP8);
   static_assert(WN == 1 || WK == 1, "the waves of a workgroup split either K or N");
   static_assert(WN == 1 || XL, "waves side by side along N share activations through LDS");
-  // XL: the segment's activation fragments are copied into LDS up front,
-  // one 1 KiB chunk (16 bytes per lane) per (K-step, M block, 16-byte
-  // load): chunk ((k - ka) * MB + b) * CH + jj.
+  // XL: the segment's activation fragments are staged in LDS up front, one
+  // 1 KiB chunk (16 bytes per lane) per (K-step, M block, 16-byte load):
+  // chunk ((k - ka) * MB + b) * CH + jj.  XL == 1 copies the codes; XL == 2
+  // (fused quantization) quantizes bf16 activations into them.
   constexpr int CH = KSTEP / 64;
+  constexpr bool INT8 = (FMT == W8A8_INT8);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -176,25 +178,45 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
   // m per lane; else four), and the per-token formats' epilogue sx, loaded
   // now so their latency hides under the K loop.
   constexpr int SXN = SWAP ? 1 : 4;
+  const int nthreads = 64 * WK * WN;
+  __shared__ Acc red[WK > 1 ? (WK - 1) * MB * NB * 64 : 1];
+  __shared__ v4i xl[XL ? kXlChunks * 64 : 1];
+  // XL == 2: activation scales computed here -- per row for the per-token
+  // formats, per (staged group, row) for Block_FP8.
+  __shared__ float sxl[XL == 2 ? (BLOCK ? kXlMaxGroups * 32 : 32) : 1];
+  __shared__ int is_last;
+
+  if constexpr (XL == 2 && !BLOCK) {
+    // Row scales over the whole of K, one wave per row (the standalone
+    // quantizer's rule, so the codes match it).
+    for (int m = wave; m < a.M; m += WK * WN) {
+      const uint16_t* xr = a.x + (long long)m * a.ldx;
+      float amax = 0.0f;
+      for (int c = lane; c < a.K / 8; c += 64)
+        amax = fmaxf(amax, absmax8(*reinterpret_cast<const v4u*>(xr + 8 * c)));
+      amax = wave_max(amax);
+      if (lane == 0) sxl[m] = act_scale<INT8>(amax);
+    }
+    __syncthreads();
+  }
+
   const float* sxrow[MB][SXN];
+  int sxm[MB][SXN];  // row of each accumulator element this lane holds (clamped)
   float ep_sx[MB][SXN];
 #pragma unroll
   for (int b = 0; b < MB; ++b)
 #pragma unroll
     for (int i = 0; i < SXN; ++i) {
       const int m = min(SWAP ? 16 * b + r : 16 * b + 4 * g + i, a.M - 1);
+      sxm[b][i] = m;
       if constexpr (BLOCK) {
-        sxrow[b][i] = a.sx + (long long)m * a.sgroups;
+        sxrow[b][i] = XL == 2 ? nullptr : a.sx + (long long)m * a.sgroups;
         ep_sx[b][i] = 0.0f;
       } else {
         sxrow[b][i] = nullptr;
-        ep_sx[b][i] = a.sx[m];
+        ep_sx[b][i] = XL == 2 ? sxl[m] : a.sx[m];
       }
     }
-
-  __shared__ Acc red[WK > 1 ? (WK - 1) * MB * NB * 64 : 1];
-  __shared__ v4i xl[XL ? kXlChunks * 64 : 1];
-  __shared__ int is_last;
 
   // One segment: K-steps [ka, kb) of output tile `tile` (WN*NB blocks of 16
   // weight rows).  The segment is contributor `slot` of the `count`
@@ -269,7 +291,8 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
 #pragma unroll
           for (int b = 0; b < MB; ++b)
 #pragma unroll
-            for (int i = 0; i < SXN; ++i) st.sx[u][b][i] = sxrow[b][i][k];
+            for (int i = 0; i < SXN; ++i)
+              st.sx[u][b][i] = XL == 2 ? sxl[(k - ka) * 32 + sxm[b][i]] : sxrow[b][i][k];
         }
       }
     };
@@ -321,10 +344,49 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
     const std::true_type masked;
     const std::false_type whole;
 
-    // XL: every wave of the workgroup copies its share of the segment's
+    // XL == 2: quantize the segment's activations into the LDS stage.  For
+    // Block_FP8 the group scales of the segment come first (16 lanes per
+    // (group, row), as in the standalone quantizer); the codes use the same
+    // encoder, so they equal the standalone quantizer's byte for byte.  The
+    // ragged K tail step is staged too, its bytes past K as zero codes.
+    if constexpr (XL == 2) {
+      if constexpr (BLOCK) {
+        const int units = (kb - ka) * a.M;  // (group, row), group-major
+        for (int base = 0; base < units; base += nthreads / 16) {
+          const int u = base + (int)(threadIdx.x >> 4), j = threadIdx.x & 15;
+          const bool act = u < units;
+          const int kk = act ? u / a.M : 0, m = act ? u % a.M : 0;
+          v4u v = v4u{0u, 0u, 0u, 0u};
+          if (act)
+            v = *reinterpret_cast<const v4u*>(a.x + (long long)m * a.ldx +
+                                              (long long)(ka + kk) * kGroup + 8 * j);
+          const float amax = seg16_max(absmax8(v));
+          if (act && j == 0) sxl[kk * 32 + m] = act_scale<false>(amax);
+        }
+        __syncthreads();
+      }
+      const int nunits = (kb - ka) * MB * CH * 64;  // (chunk, lane)
+      for (int u = threadIdx.x; u < nunits; u += nthreads) {
+        const int c = u >> 6, l = u & 63;
+        const int kk = c / (MB * CH), b = (c / CH) % MB, jj = c % CH;
+        const int row = min(16 * b + (l & 15), a.M - 1);
+        const int e = (ka + kk) * KSTEP + 64 * jj + 16 * (l >> 4);  // first element
+        v4u lo = v4u{0u, 0u, 0u, 0u}, hi = lo;
+        if (e < a.K) {  // (K % 16 == 0: the chunk is wholly inside K or past it)
+          const uint16_t* src = a.x + (long long)row * a.ldx + e;
+          lo = *reinterpret_cast<const v4u*>(src);
+          hi = *reinterpret_cast<const v4u*>(src + 8);
+        }
+        const float s = BLOCK ? sxl[kk * 32 + row] : sxl[row];
+        const v2u ql = encode8<INT8>(lo, s), qh = encode8<INT8>(hi, s);
+        xl[c * 64 + l] = v4i{(int)ql[0], (int)ql[1], (int)qh[0], (int)qh[1]};
+      }
+    }
+
+    // XL == 1: every wave of the workgroup copies its share of the segment's
     // full K-steps [ka, min(kb, kfull)) of activations into LDS with
     // direct-to-LDS loads (no registers), issued before the weight loads.
-    if constexpr (XL) {
+    if constexpr (XL == 1) {
       const int nchunks = (min(kb, a.kfull) - ka) * MB * CH;
       for (int c = wave; c < nchunks; c += WK * WN) {
         const int kk = c / (MB * CH), b = (c / CH) % MB, jj = c % CH;
@@ -376,7 +438,20 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
         for (int j = 0; j < NB; ++j)
           wt[j] = PACKED ? load_w(j, a.kfull) : load_frag_tail<FMT>(wptr[j], a.kfull, 16 * g, a.K);
 #pragma unroll
-        for (int b = 0; b < MB; ++b) xt[b] = load_frag_tail<FMT>(xrow[b], a.kfull, 16 * g, a.K);
+        for (int b = 0; b < MB; ++b) {
+          if constexpr (XL == 2) {
+            const int c = ((a.kfull - ka) * MB + b) * CH;  // staged, zero past K
+            if constexpr (FMT == W8A8_INT8) {
+              xt[b] = xl[c * 64 + lane];
+            } else {
+              const v4i lo = xl[c * 64 + lane];
+              const v4i hi = xl[(c + 1) * 64 + lane];
+              xt[b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+          } else {
+            xt[b] = load_frag_tail<FMT>(xrow[b], a.kfull, 16 * g, a.K);
+          }
+        }
         const float no_sx[MB][SXN] = {};
         step(wt, xt, 0.0f, no_sx);
       }

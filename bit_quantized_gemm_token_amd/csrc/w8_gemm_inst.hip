@@ -16,7 +16,8 @@
 
 // One entry per (MB, NB, WK, WN, UNROLL, PACKED, XL): MB in {1, 2}; (NB,
 // UNROLL) with NB * UNROLL <= 4 (the weight registers of one stage);
-// (WK, WN, XL) in {(1..16, 1, 0), (1..8, 1, 1), (1, 2..8, 1)}; PACKED in {0, 1}.
+// (WK, WN, XL) in {(1..16, 1, 0), (1..8, 1, 1), (1, 2..8, 1), (1..4, 1, 2),
+// (1, 2..8, 2)} (XL 2: fused quantization); PACKED in {0, 1}.
 #define W8_I(MB, NB, WK, WN, U, P, XL)                                       \
   {W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL,                                 \
    &launch_gemm<W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL>},
@@ -27,7 +28,9 @@
 #define W8_W(MB)                                                                       \
   W8_U(MB, 1, 1, 0) W8_U(MB, 2, 1, 0) W8_U(MB, 4, 1, 0) W8_U(MB, 8, 1, 0)             \
   W8_U(MB, 16, 1, 0) W8_U(MB, 1, 1, 1) W8_U(MB, 2, 1, 1) W8_U(MB, 4, 1, 1)            \
-  W8_U(MB, 8, 1, 1) W8_U(MB, 1, 2, 1) W8_U(MB, 1, 4, 1) W8_U(MB, 1, 8, 1)
+  W8_U(MB, 8, 1, 1) W8_U(MB, 1, 2, 1) W8_U(MB, 1, 4, 1) W8_U(MB, 1, 8, 1)             \
+  W8_U(MB, 1, 1, 2) W8_U(MB, 2, 1, 2) W8_U(MB, 4, 1, 2) W8_U(MB, 1, 2, 2)             \
+  W8_U(MB, 1, 4, 2) W8_U(MB, 1, 8, 2)
 
 namespace w8 {
 

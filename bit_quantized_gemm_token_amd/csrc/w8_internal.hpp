@@ -19,17 +19,17 @@ int fmt_from_name(const std::string& s);  // -1 if unknown
 
 // Shape checks shared by the GEMM, the quantizer and the tuner.
 w8_status check_gemm_shape(int fmt, int M, int N, int K);
-// Config checks (shape-independent and shape-dependent).
-w8_status check_cfg(int fmt, int M, int N, int K, const w8_cfg& c);
-w8_cfg make_default_cfg(int fmt, int M, int N, int K);
+// Config checks (shape-independent and shape-dependent) for operation op.
+w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c);
+w8_cfg make_default_cfg(int fmt, int op, int M, int N, int K);
 size_t workspace_bytes(int fmt, int M, int N, int K, const w8_cfg& c);
 int tiles_of(int N, const w8_cfg& c);                       // output tiles along N
 int partial_slots(int fmt, int N, int K, const w8_cfg& c);  // workspace slots per tile
 int ksteps_of(int fmt, int K);
 
-// Resolve cfg == NULL through the table (entries are per weight layout),
-// else the default.
-w8_cfg resolve_cfg(int fmt, int M, int N, int K, int packed, int* from_table);
+// Resolve cfg == NULL through the table (entries are per operation and
+// weight layout), else the default.
+w8_cfg resolve_cfg(int fmt, int op, int M, int N, int K, int packed, int* from_table);
 
 // The device must be gfx950 (checked once per device).
 w8_status check_device();
@@ -48,7 +48,9 @@ struct GemmCall {
   int out_mode;
   void* ws;
   size_t ws_bytes;
-  int packed;  // weights in the packed (MFMA-native) layout
+  int packed;         // weights in the packed (MFMA-native) layout
+  const void* x;      // fused quantization (w8_linear): bf16 activations, else null
+  long long ldx;
 };
 w8_status launch_gemm_call(const GemmCall& call, const w8_cfg& c, hipStream_t s);
 

@@ -34,6 +34,8 @@ hipError_t launch_quantize_weight(int fmt, const QuantWeightArgs& a, hipStream_t
 struct GemmArgs {
   const uint8_t* xq;       // activation codes [M, K], row stride ldq bytes
   const float* sx;         // activation scales
+  const uint16_t* x;       // fused quantization: bf16 activations [M, K], row stride ldx
+  long long ldx;           // elements
   const uint8_t* wq;       // weight codes [N, K], row stride ldw bytes
   const float* sw;         // weight scales
   void* out;               // bf16 Y [M, N] or 4-byte accumulators, stride ldo elements
@@ -77,6 +79,9 @@ inline int kstep_of(int fmt) { return fmt == 1 ? 64 : 128; }
 // per K-step, 16-row block of M and 64 bytes of K-step) per workgroup
 // segment, 64 KiB, so two workgroups fit in a compute unit's 160 KiB.
 constexpr int kXlChunks = 64;
+// Fused quantization of Block_FP8 keeps each staged group's scales in LDS:
+// at most this many K-steps per segment (kXlChunks / 2 chunks per K-step).
+constexpr int kXlMaxGroups = kXlChunks / 2;
 
 // Workspace layout: a fixed 2 MiB counter region (one 4-byte arrival counter
 // per output tile in its own 128-byte cache line -- counters of neighbouring

@@ -16,36 +16,6 @@ namespace {
 constexpr int kQuantThreads = 256;
 constexpr int kRowCache = 4;  // 16-byte chunks per thread kept in registers (K <= 8192)
 
-__device__ __forceinline__ float absmax8(v4u v) {
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m = fmaxf(m, fabsf(bf16_lo(v[i])));
-    m = fmaxf(m, fabsf(bf16_hi(v[i])));
-  }
-  return m;
-}
-
-// Eight bf16 values (one 16-byte chunk) -> eight codes (8 bytes).
-template <bool INT8>
-__device__ __forceinline__ v2u encode8(v4u v, float s) {
-  float f[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = bf16_lo(v[i]) / s;
-    f[2 * i + 1] = bf16_hi(v[i]) / s;
-  }
-  v2u o;
-  if (INT8) {
-    o[0] = i8_pack4(f[0], f[1], f[2], f[3]);
-    o[1] = i8_pack4(f[4], f[5], f[6], f[7]);
-  } else {
-    o[0] = e4m3_pack4(f[0], f[1], f[2], f[3]);
-    o[1] = e4m3_pack4(f[4], f[5], f[6], f[7]);
-  }
-  return o;
-}
-
 // Per-token quantization: one workgroup per row.
 template <bool INT8>
 __global__ __launch_bounds__(kQuantThreads) void quant_token_kernel(QuantActArgs a) {
@@ -74,7 +44,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_token_kernel(QuantActArgs
 #pragma unroll
   for (int w = 0; w < kQuantThreads / 64; ++w) amax = fmaxf(amax, red[w]);
 
-  const float s = (amax == 0.0f) ? 1.0f : amax / (INT8 ? kQmaxInt8 : kQmaxE4M3);
+  const float s = act_scale<INT8>(amax);
   if (t == 0) a.sx[m] = s;
 
 #pragma unroll
@@ -101,7 +71,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_group_kernel(QuantActArgs
   v4u v = v4u{0u, 0u, 0u, 0u};
   if (active) v = *reinterpret_cast<const v4u*>(a.x + xo);
   const float amax = seg16_max(absmax8(v));
-  const float s = (amax == 0.0f) ? 1.0f : amax / kQmaxE4M3;
+  const float s = act_scale<false>(amax);
   if (active) {
     if (j == 0) a.sx[(long long)m * G + g] = s;
     *reinterpret_cast<v2u*>(a.xq + (long long)m * a.ldq + g * kGroup + 8 * j) =

@@ -28,9 +28,10 @@ struct Entry {
   double us;
 };
 
-typedef std::tuple<int, int, int, int, int> Key;  // fmt, packed, M, N, K
+typedef std::tuple<int, int, int, int, int, int> Key;  // fmt, op, packed, M, N, K
 
 const char* layout_name(int packed) { return packed ? "packed" : "row"; }
+const char* op_name(int op) { return op == W8_OP_LINEAR ? "linear" : "gemm"; }
 
 struct Table {
   std::mutex mu;
@@ -90,20 +91,24 @@ w8_status parse_table(const std::string& text, std::map<Key, Entry>* native,
       foreign->push_back(line);
       continue;
     }
-    if (tok.size() != 16)
-      return fail(W8_E_TABLE_FORMAT, where + "expected 16 fields, got " + std::to_string(tok.size()));
+    if (tok.size() != 17)
+      return fail(W8_E_TABLE_FORMAT, where + "expected 17 fields, got " + std::to_string(tok.size()));
     const int fmt = fmt_from_name(tok[2]);
     if (fmt < 0) return fail(W8_E_TABLE_FORMAT, where + "unknown format '" + tok[2] + "'");
+    int op = -1;
+    if (tok[3] == "gemm") op = W8_OP_GEMM;
+    if (tok[3] == "linear") op = W8_OP_LINEAR;
+    if (op < 0) return fail(W8_E_TABLE_FORMAT, where + "op must be gemm or linear");
     int packed = -1;
-    if (tok[3] == "row") packed = 0;
-    if (tok[3] == "packed") packed = 1;
+    if (tok[4] == "row") packed = 0;
+    if (tok[4] == "packed") packed = 1;
     if (packed < 0) return fail(W8_E_TABLE_FORMAT, where + "layout must be row or packed");
     int v[11];  // M N K tile_n waves_k waves_n unroll split_k grid swap_ab x_lds
     for (int i = 0; i < 11; ++i)
-      if (!parse_int(tok[4 + i], &v[i]))
-        return fail(W8_E_TABLE_FORMAT, where + "bad integer '" + tok[4 + i] + "'");
+      if (!parse_int(tok[5 + i], &v[i]))
+        return fail(W8_E_TABLE_FORMAT, where + "bad integer '" + tok[5 + i] + "'");
     double us = 0;
-    if (!parse_double(tok[15], &us)) return fail(W8_E_TABLE_FORMAT, where + "bad time field");
+    if (!parse_double(tok[16], &us)) return fail(W8_E_TABLE_FORMAT, where + "bad time field");
     w8_cfg c;
     std::memset(&c, 0, sizeof c);
     c.abi_version = abi;
@@ -115,9 +120,10 @@ w8_status parse_table(const std::string& text, std::map<Key, Entry>* native,
     c.grid = v[8];
     c.swap_ab = v[9];
     c.x_lds = v[10];
-    if (check_gemm_shape(fmt, v[0], v[1], v[2]) != W8_OK || check_cfg(fmt, v[0], v[1], v[2], c) != W8_OK)
+    if (check_gemm_shape(fmt, v[0], v[1], v[2]) != W8_OK ||
+        check_cfg(fmt, op, v[0], v[1], v[2], c) != W8_OK)
       return fail(W8_E_TABLE_FORMAT, where + "invalid entry (" + std::string(w8_last_error()) + ")");
-    (*native)[Key(fmt, packed, v[0], v[1], v[2])] = Entry{c, us};
+    (*native)[Key(fmt, op, packed, v[0], v[1], v[2])] = Entry{c, us};
   }
   return W8_OK;
 }
@@ -164,19 +170,19 @@ void maybe_load_env(Table& t) {
 
 }  // namespace
 
-w8_cfg resolve_cfg(int fmt, int M, int N, int K, int packed, int* from_table) {
+w8_cfg resolve_cfg(int fmt, int op, int M, int N, int K, int packed, int* from_table) {
   Table& t = table();
   {
     std::lock_guard<std::mutex> lk(t.mu);
     maybe_load_env(t);
-    auto it = t.native.find(Key(fmt, packed ? 1 : 0, M, N, K));
+    auto it = t.native.find(Key(fmt, op, packed ? 1 : 0, M, N, K));
     if (it != t.native.end()) {
       if (from_table) *from_table = 1;
       return it->second.cfg;
     }
   }
   if (from_table) *from_table = 0;
-  return make_default_cfg(fmt, M, N, K);
+  return make_default_cfg(fmt, op, M, N, K);
 }
 
 }  // namespace w8
@@ -198,15 +204,16 @@ w8_status w8_save_config_table(const char* path) {
     std::lock_guard<std::mutex> lk(t.mu);
     maybe_load_env(t);
     out << "# w8gemm per-shape config table\n"
-        << "# arch abi fmt layout M N K tile_n waves_k waves_n unroll split_k grid swap_ab "
-           "x_lds us_per_gemm\n";
+        << "# arch abi fmt op layout M N K tile_n waves_k waves_n unroll split_k grid swap_ab "
+           "x_lds us_per_call\n";
     for (const auto& kv : t.native) {
       const Entry& e = kv.second;
       char buf[256];
-      std::snprintf(buf, sizeof buf, "%s %d %s %s %d %d %d %d %d %d %d %d %d %d %d %.4f\n", kArch,
-                    W8_ABI_VERSION, fmt_name(std::get<0>(kv.first)),
-                    layout_name(std::get<1>(kv.first)), std::get<2>(kv.first),
-                    std::get<3>(kv.first), std::get<4>(kv.first), e.cfg.tile_n, e.cfg.waves_k,
+      std::snprintf(buf, sizeof buf, "%s %d %s %s %s %d %d %d %d %d %d %d %d %d %d %d %.4f\n",
+                    kArch, W8_ABI_VERSION, fmt_name(std::get<0>(kv.first)),
+                    op_name(std::get<1>(kv.first)), layout_name(std::get<2>(kv.first)),
+                    std::get<3>(kv.first), std::get<4>(kv.first), std::get<5>(kv.first),
+                    e.cfg.tile_n, e.cfg.waves_k,
                     e.cfg.waves_n, e.cfg.unroll, e.cfg.split_k, e.cfg.grid, e.cfg.swap_ab,
                     e.cfg.x_lds, e.us);
       out << buf;
@@ -248,32 +255,33 @@ int w8_config_table_foreign(void) {
   return t.foreign_count;
 }
 
-w8_status w8_set_config(w8_fmt fmt, int M, int N, int K, int packed, const w8_cfg* cfg,
-                        double us_per_gemm) {
+w8_status w8_set_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed,
+                        const w8_cfg* cfg, double us_per_call) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!cfg) return fail(W8_E_INVALID, "null cfg");
-  st = check_cfg(fmt, M, N, K, *cfg);
+  st = check_cfg(fmt, op, M, N, K, *cfg);
   if (st) return st;
   Table& t = table();
   std::lock_guard<std::mutex> lk(t.mu);
   maybe_load_env(t);
-  t.native[Key(fmt, packed ? 1 : 0, M, N, K)] = Entry{*cfg, us_per_gemm};
+  t.native[Key(fmt, op, packed ? 1 : 0, M, N, K)] = Entry{*cfg, us_per_call};
   return ok();
 }
 
-w8_status w8_lookup_config(w8_fmt fmt, int M, int N, int K, int packed, w8_cfg* out,
-                           double* us_per_gemm) {
+w8_status w8_lookup_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed, w8_cfg* out,
+                           double* us_per_call) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!out) return fail(W8_E_INVALID, "null output pointer");
+  if (op != W8_OP_GEMM && op != W8_OP_LINEAR) return fail(W8_E_INVALID, "unknown op");
   Table& t = table();
   std::lock_guard<std::mutex> lk(t.mu);
   maybe_load_env(t);
-  auto it = t.native.find(Key(fmt, packed ? 1 : 0, M, N, K));
+  auto it = t.native.find(Key(fmt, op, packed ? 1 : 0, M, N, K));
   if (it == t.native.end()) return fail(W8_E_NOT_FOUND, "no table entry for this shape and layout");
   *out = it->second.cfg;
-  if (us_per_gemm) *us_per_gemm = it->second.us;
+  if (us_per_call) *us_per_call = it->second.us;
   return ok();
 }
 

@@ -52,6 +52,18 @@ __global__ void fill_codes_kernel(uint8_t* p, size_t n, uint32_t seed, int int8)
   }
 }
 
+// Random bf16 activations, roughly N(0, 1)-sized: uniform in (-4, 4) with a
+// few larger outliers, rounded to bf16 by truncation.
+__global__ void fill_bf16_kernel(uint16_t* p, size_t n, uint32_t seed) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const uint32_t h = hash32((uint32_t)i * 2246822519U ^ seed);
+    float v = ((h >> 8) * (1.0f / 16777216.0f) - 0.5f) * 8.0f;
+    if ((h & 0xFFu) == 0x5Au) v *= 6.0f;
+    p[i] = (uint16_t)(__float_as_uint(v) >> 16);
+  }
+}
+
 __global__ void fill_scales_kernel(float* p, size_t n, uint32_t seed, float lo, float hi) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x) {
@@ -65,6 +77,7 @@ struct Buffers {
   uint8_t* wpool = nullptr;  // R weight copies in the tuned layout
   uint8_t* xq = nullptr;
   float* sx = nullptr;
+  uint16_t* x = nullptr;     // bf16 activations (fused linear op)
   float* sw = nullptr;
   uint16_t* y = nullptr;
   void* ws = nullptr;
@@ -74,6 +87,7 @@ struct Buffers {
     hipFree(wpool);
     hipFree(xq);
     hipFree(sx);
+    hipFree(x);
     hipFree(sw);
     hipFree(y);
     hipFree(ws);
@@ -118,6 +132,7 @@ extern "C" void w8_tune_default_opts(w8_tune_opts* o) {
   o->fail_candidate = -1;
   o->packed = 0;
   o->stream_k = 0;
+  o->op = W8_OP_GEMM;
 }
 
 extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tune_opts* opts,
@@ -133,8 +148,10 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
     o = *opts;
   }
   if (o.warmup < 0 || o.replays < 1 || o.bank2_top < 1 || o.rotate_bytes < 0 ||
-      o.max_split_k < 1 || o.max_split_k > W8_MAX_SPLIT_K)
+      o.max_split_k < 1 || o.max_split_k > W8_MAX_SPLIT_K ||
+      (o.op != W8_OP_GEMM && o.op != W8_OP_LINEAR))
     return fail(W8_E_INVALID, "bad tuner options");
+  const int op = o.op;
   st = check_device();
   if (st) return st;
 
@@ -177,7 +194,7 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   std::vector<w8_cfg> all;
   long long most_waves = 0;
   auto consider = [&](const w8_cfg& c) {
-    if (check_cfg(fmt, M, N, K, c) != W8_OK) return;
+    if (check_cfg(fmt, op, M, N, K, c) != W8_OK) return;
     // K-steps per wave
     const long long per_wave = c.grid > 0 ? (long long)tiles_of(N, c) * T / (c.grid * c.waves_k)
                                           : (long long)T / (c.split_k * c.waves_k);
@@ -222,8 +239,10 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
     cd.index = (int)cands.size();
     cands.push_back(cd);
   }
-  const w8_cfg dflt = make_default_cfg(fmt, M, N, K);
+  const w8_cfg dflt = make_default_cfg(fmt, W8_OP_GEMM, M, N, K);     // reference
+  const w8_cfg dflt_op = make_default_cfg(fmt, op, M, N, K);          // reported baseline
   max_ws = std::max(max_ws, workspace_bytes(fmt, M, N, K, dflt));
+  max_ws = std::max(max_ws, workspace_bytes(fmt, M, N, K, dflt_op));
 
   Buffers b;
   hipStream_t stream = nullptr;
@@ -235,6 +254,7 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   TRY_HIP(hipMalloc(&b.wrow, wrow_bytes));
   TRY_HIP(hipMalloc(&b.wpool, wbytes * R));
   TRY_HIP(hipMalloc(&b.xq, (size_t)M * ld));
+  if (op == W8_OP_LINEAR) TRY_HIP(hipMalloc(&b.x, (size_t)M * ld * 2));
   TRY_HIP(hipMalloc(&b.sx, nsx * 4));
   TRY_HIP(hipMalloc(&b.sw, nsw * 4));
   TRY_HIP(hipMalloc(&b.y, (size_t)M * N * 2));
@@ -254,24 +274,38 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   } else {
     TRY_HIP(hipMemcpyAsync(b.wpool, b.wrow, wrow_bytes, hipMemcpyDeviceToDevice, stream));
   }
-  hipLaunchKernelGGL(fill_codes_kernel, dim3(64), dim3(256), 0, stream, b.xq, (size_t)M * ld,
-                     0x9876u, is_int8);
-  hipLaunchKernelGGL(fill_scales_kernel, dim3(64), dim3(256), 0, stream, b.sx, nsx, 0x55u, 0.01f,
-                     0.1f);
+  if (op == W8_OP_LINEAR) {
+    // bf16 activations, quantized by the standalone quantizer for the reference
+    hipLaunchKernelGGL(fill_bf16_kernel, dim3(64), dim3(256), 0, stream, b.x, (size_t)M * ld,
+                       0x9876u);
+    TRY_HIP(hipGetLastError());
+    QuantActArgs qa{b.x, b.xq, b.sx, ld, ld, M, K};
+    TRY_HIP(launch_quantize_act(fmt, qa, stream));
+  } else {
+    hipLaunchKernelGGL(fill_codes_kernel, dim3(64), dim3(256), 0, stream, b.xq, (size_t)M * ld,
+                       0x9876u, is_int8);
+    hipLaunchKernelGGL(fill_scales_kernel, dim3(64), dim3(256), 0, stream, b.sx, nsx, 0x55u,
+                       0.01f, 0.1f);
+  }
   hipLaunchKernelGGL(fill_scales_kernel, dim3(64), dim3(256), 0, stream, b.sw, nsw, 0x77u, 0.001f,
                      0.01f);
   TRY_HIP(hipGetLastError());
   TRY_HIP(hipStreamSynchronize(stream));
 
-  GemmCall call{fmt, M,     N, K,     b.xq, ld, b.sx,      b.wpool, packed ? 0 : ld,
-                b.sw, b.y, N, 0, b.ws, b.ws_bytes, packed};
+  GemmCall call{fmt,  M,   N, K, b.xq, ld,        b.sx,       b.wpool, packed ? 0 : ld,
+                b.sw, b.y, N, 0, b.ws, b.ws_bytes, packed, nullptr, 0};
+  if (op == W8_OP_LINEAR) {  // the fused op reads bf16 activations
+    call.xq = nullptr;
+    call.sx = nullptr;
+    call.x = b.x;
+    call.ldx = ld;
+  }
 
-  // Reference output: the default config on the row-major weights of copy 0.
+  // Reference output: the default GEMM config on the row-major weights of
+  // copy 0 (for the fused op, after the standalone quantizer).
   std::vector<uint16_t> yref((size_t)M * N), ycur((size_t)M * N);
-  GemmCall ref = call;
-  ref.wq = b.wrow;
-  ref.ldw = ld;
-  ref.packed = 0;
+  GemmCall ref{fmt,  M,   N, K, b.xq, ld,        b.sx,       b.wrow, ld,
+               b.sw, b.y, N, 0, b.ws, b.ws_bytes, 0,      nullptr, 0};
   st = launch_gemm_call(ref, dflt, stream);
   if (st) return st;
   TRY_HIP(hipStreamSynchronize(stream));
@@ -368,7 +402,7 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
     if (st) return st;
   }
   double dflt_us2 = 0;
-  st = time_cfg(dflt, &dflt_us2);  // the default config on the tuned layout
+  st = time_cfg(dflt_op, &dflt_us2);  // the op's default config on the tuned layout
   if (st) return st;
 
   // Bank-2 winner; within 1% prefer no shared tiles (split_k = 1, grid = 0),
@@ -389,7 +423,7 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   }
   *best = win->cfg;
   if (o.insert) {
-    st = w8_set_config(fmt, M, N, K, packed, &win->cfg, win->us2);
+    st = w8_set_config(fmt, (w8_op)op, M, N, K, packed, &win->cfg, win->us2);
     if (st) return st;
   }
   if (stats) {

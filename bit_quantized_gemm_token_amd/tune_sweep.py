@@ -1,7 +1,8 @@
 """Ahead-of-time tuning of a list of shapes into a config table file.
 
     python -m bit_quantized_gemm_token_amd.tune_sweep --out TABLE [--formats ...]
-           [--shapes M,N,K;M,N,K...] [--no-resume] [--max-split-k 256]
+           [--ops gemm,linear] [--layouts row,packed] [--shapes M,N,K;M,N,K...]
+           [--no-resume] [--max-split-k 256]
 
 Default shapes: the 24-shape M <= 32 sweep of synthetic.SWEEP plus the shapes
 the tests and benchmarks name (N=K=4096 at M in {1, 4, 16, 32}; N=4608,
@@ -43,6 +44,7 @@ def main(argv=None):
     p.add_argument("--out", required=True)
     p.add_argument("--formats", default="FP8_Dynamic,W8A8_INT8,Block_FP8")
     p.add_argument("--layouts", default="row,packed")
+    p.add_argument("--ops", default="gemm", help="gemm, linear or gemm,linear")
     p.add_argument("--shapes", default=None)
     p.add_argument("--no-resume", action="store_true")
     p.add_argument("--max-split-k", type=int, default=w8.MAX_SPLIT_K)
@@ -62,26 +64,26 @@ def main(argv=None):
     t0 = time.time()
     done = skipped = 0
     layouts = [{"row": False, "packed": True}[v] for v in a.layouts.split(",")]
-    for fmt in a.formats.split(","):
-        for (M, N, K) in shapes:
-            for packed in layouts:
-                if w8.lookup_config(fmt, M, N, K, packed=packed) is not None:
-                    skipped += 1
-                    continue
-                if a.time_budget_s and time.time() - t0 > a.time_budget_s:
-                    print(f"[tune] time budget reached after {done} shapes", flush=True)
-                    print(f"[tune] tuned {done}, kept {skipped}, table {a.out}", flush=True)
-                    return 0
-                best, st = w8.tune_shape(fmt, M, N, K, rotate_bytes=a.rotate_mib << 20,
-                                         replays=a.replays, max_split_k=a.max_split_k, insert=True,
-                                         packed=packed, stream_k=a.stream_k)
-                w8.save_config_table(a.out)
-                done += 1
-                print(f"[tune] {fmt} {'packed' if packed else 'row'} {M}x{N}x{K}: {best} "
-                      f"{st['best_us_bank2']:.3f} us "
-                      f"({st['best_gbps']:.0f} GB/s; default {st['default_us_bank2']:.3f} us; "
-                      f"{st['validated']}/{st['candidates']} validated; {st['tune_seconds']:.1f} s)",
-                      flush=True)
+    jobs = [(op, fmt, s, packed) for op in a.ops.split(",") for fmt in a.formats.split(",")
+            for s in shapes for packed in layouts]
+    for op, fmt, (M, N, K), packed in jobs:
+        if w8.lookup_config(fmt, M, N, K, packed=packed, op=op) is not None:
+            skipped += 1
+            continue
+        if a.time_budget_s and time.time() - t0 > a.time_budget_s:
+            print(f"[tune] time budget reached after {done} shapes", flush=True)
+            print(f"[tune] tuned {done}, kept {skipped}, table {a.out}", flush=True)
+            return 0
+        best, st = w8.tune_shape(fmt, M, N, K, rotate_bytes=a.rotate_mib << 20,
+                                 replays=a.replays, max_split_k=a.max_split_k, insert=True,
+                                 packed=packed, stream_k=a.stream_k, op=op)
+        w8.save_config_table(a.out)
+        done += 1
+        print(f"[tune] {op} {fmt} {'packed' if packed else 'row'} {M}x{N}x{K}: {best} "
+              f"{st['best_us_bank2']:.3f} us "
+              f"({st['best_gbps']:.0f} GB/s; default {st['default_us_bank2']:.3f} us; "
+              f"{st['validated']}/{st['candidates']} validated; {st['tune_seconds']:.1f} s)",
+              flush=True)
     print(f"[tune] tuned {done}, kept {skipped}, table {a.out}", flush=True)
     return 0
 

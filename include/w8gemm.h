@@ -13,7 +13,8 @@
  *     replay; larger M goes to another backend;
  *   - paragraphs 6-7: per-shape config files, with a default config when no
  *     tuned entry exists;
- *   - paragraph 8: quantization is an auxiliary kernel beside the GEMM.
+ *   - paragraph 8: quantization is an auxiliary kernel beside the GEMM;
+ *     w8_linear also offers it fused into the GEMM (one launch per layer).
  * The page defines none of the formats; this library uses:
  *   FP8_Dynamic  activations: per-token (row) OCP E4M3FN codes, fp32 sx[M];
  *                weights: E4M3FN codes, fp32 sw[N] (one per output channel);
@@ -65,6 +66,14 @@ extern "C" {
 #define W8_GROUP 128        /* Block_FP8 group / block edge */
 
 typedef void *w8_stream; /* hipStream_t */
+
+/* The two operations configs are tuned for: the GEMM on quantized
+ * activations (w8_gemm_w8a8), and the whole linear layer with activation
+ * quantization fused into the GEMM (w8_linear).                            */
+typedef enum {
+    W8_OP_GEMM = 0,
+    W8_OP_LINEAR = 1
+} w8_op;
 
 typedef enum {
     W8_FP8_DYNAMIC = 0,
@@ -144,6 +153,7 @@ typedef struct {
     int32_t packed;           /* weight layout tuned: 0 row-major, 1 packed */
     int32_t stream_k;         /* 1: also try stream-K grids (default 0: on the
                                  shapes measured so far they never won) */
+    int32_t op;               /* w8_op tuned (default W8_OP_GEMM) */
     int32_t reserved[1];
 } w8_tune_opts;
 
@@ -207,15 +217,15 @@ w8_status w8_packed_weight_size(w8_fmt fmt, int N, int K, size_t *bytes);
 w8_status w8_pack_weight(w8_fmt fmt, int N, int K, const void *wq, int64_t ldw, void *wp,
                          w8_stream stream);
 
-/* Bytes of device workspace the GEMM needs for (fmt, M, N, K) under cfg
- * (cfg NULL: the config w8_resolve_config picks for that weight layout;
- * packed = 1 for packed weights).  0 when no tile is shared between
+/* Bytes of device workspace operation op needs for (fmt, M, N, K) under cfg
+ * (cfg NULL: the config w8_resolve_config picks for op and that weight
+ * layout; packed = 1 for packed weights).  0 when no tile is shared between
  * workgroups (split_k == 1 and grid == 0).
  * Layout: a fixed 2 MiB region of arrival counters, then the partials of
  * shared tiles; split_k > 1 and grid > 0 therefore support at most 16384
  * output tiles (N <= 16384 * tile_n * waves_n).                             */
-w8_status w8_workspace_size(w8_fmt fmt, int M, int N, int K, int packed, const w8_cfg *cfg,
-                            size_t *bytes);
+w8_status w8_workspace_size(w8_fmt fmt, w8_op op, int M, int N, int K, int packed,
+                            const w8_cfg *cfg, size_t *bytes);
 
 /* The quantized GEMM.  One kernel launch on `stream` (the split-K reduction
  * runs inside it: the last workgroup of each output tile to finish sums the
@@ -251,28 +261,46 @@ w8_status w8_gemm_w8a8_acc(w8_fmt fmt, int M, int N, int K,
                            void *acc, int64_t ldacc, const w8_cfg *cfg,
                            void *ws, size_t ws_bytes, w8_stream stream);
 
+/* The whole linear layer in one kernel launch: activation quantization
+ * (the w8_quantize_act rules, giving the same codes and scales) fused into
+ * the GEMM.  Each workgroup quantizes the activations of its K range into
+ * LDS: per 1x128 group for Block_FP8; per token for the other formats,
+ * after a pass over the whole row for its absolute maximum.  Y equals
+ * w8_quantize_act followed by w8_gemm_w8a8 with the same cfg, bit for bit.
+ *   x       bf16 [M, K], row stride ldx elements (device), 16-byte aligned,
+ *           ldx % 8 == 0
+ *   wq, sw, y, ws, stream  as for w8_gemm_w8a8
+ *   cfg     needs x_lds == 1 and waves_k <= 4; NULL = the table entry for
+ *           (fmt, W8_OP_LINEAR, weight layout, M, N, K), else the default
+ *           linear config (w8_default_config with W8_OP_LINEAR).          */
+w8_status w8_linear(w8_fmt fmt, int M, int N, int K, const void *x, int64_t ldx,
+                    const void *wq, int64_t ldw, const float *sw,
+                    void *y, int64_t ldy, const w8_cfg *cfg,
+                    void *ws, size_t ws_bytes, w8_stream stream);
+
 /* ---------------------------------------------------------------- config -- */
-/* W8_OK if cfg is a valid configuration for (fmt, M, N, K), else
- * W8_E_INVALID (with the reason in w8_last_error()).                        */
-w8_status w8_validate_config(w8_fmt fmt, int M, int N, int K, const w8_cfg *cfg);
+/* W8_OK if cfg is a valid configuration of operation op for (fmt, M, N, K),
+ * else W8_E_INVALID (with the reason in w8_last_error()).                   */
+w8_status w8_validate_config(w8_fmt fmt, w8_op op, int M, int N, int K, const w8_cfg *cfg);
 
-/* The built-in default configuration for (fmt, M, N, K) (paragraph 7 of the
- * page: a default config serves untuned shapes).                           */
-w8_status w8_default_config(w8_fmt fmt, int M, int N, int K, w8_cfg *out);
+/* The built-in default configuration of op for (fmt, M, N, K) (paragraph 7
+ * of the page: a default config serves untuned shapes).                    */
+w8_status w8_default_config(w8_fmt fmt, w8_op op, int M, int N, int K, w8_cfg *out);
 
-/* The config the GEMM uses when called with cfg == NULL for weights in the
- * given layout (packed = 0 row-major, 1 packed): the table entry for
- * (this device's arch, W8_ABI_VERSION, fmt, layout, M, N, K) if present,
- * else the default.  *from_table is set to 1 on a table hit, 0 otherwise.   */
-w8_status w8_resolve_config(w8_fmt fmt, int M, int N, int K, int packed, w8_cfg *out,
-                            int *from_table);
+/* The config op uses when called with cfg == NULL for weights in the given
+ * layout (packed = 0 row-major, 1 packed): the table entry for (this
+ * device's arch, W8_ABI_VERSION, fmt, op, layout, M, N, K) if present, else
+ * the default.  *from_table is set to 1 on a table hit, 0 otherwise.        */
+w8_status w8_resolve_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed,
+                            w8_cfg *out, int *from_table);
 
 /* ----------------------------------------------------------- config table -- */
 /* Per-shape config table (paragraphs 6-7 of the page).  Text format, one entry
  * per line:
- *   arch abi fmt layout M N K tile_n waves_k waves_n unroll split_k grid swap_ab
- *   x_lds us_per_gemm
- * with layout "row" or "packed"; '#' starts a comment.  Entries whose arch or
+ *   arch abi fmt op layout M N K tile_n waves_k waves_n unroll split_k grid
+ *   swap_ab x_lds us_per_call
+ * with op "gemm" or "linear" and layout "row" or "packed"; '#' starts a
+ * comment.  Entries whose arch or
  * abi differ from this build and device are kept in the file but never used.
  * w8_load_config_table replaces the in-memory table atomically: on any parse
  * error it returns W8_E_TABLE_FORMAT (line number in w8_last_error()) and
@@ -285,27 +313,30 @@ int w8_config_table_size(void);
 /* Entries of the last load that were skipped for a foreign arch or abi. */
 int w8_config_table_foreign(void);
 /* Insert or replace one entry for this device (validated first). */
-w8_status w8_set_config(w8_fmt fmt, int M, int N, int K, int packed, const w8_cfg *cfg,
-                        double us_per_gemm);
+w8_status w8_set_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed,
+                        const w8_cfg *cfg, double us_per_call);
 /* Exact lookup for this device: W8_OK on a hit (with the entry's time per
- * GEMM in *us_per_gemm when not NULL), W8_E_NOT_FOUND on a miss.  Comparing
+ * call in *us_per_call when not NULL), W8_E_NOT_FOUND on a miss.  Comparing
  * the two layouts' times tells a caller which layout to store its weights in. */
-w8_status w8_lookup_config(w8_fmt fmt, int M, int N, int K, int packed, w8_cfg *out,
-                           double *us_per_gemm);
+w8_status w8_lookup_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed,
+                           w8_cfg *out, double *us_per_call);
 
 /* ------------------------------------------------------------------ tuner -- */
 /* Ahead-of-time per-shape tuner (paragraph 3 of the page: the autotuner
  * compares configurations and keeps the best for each shape).  Tunes one
- * weight layout (opts->packed).  Allocates its own inputs (random codes and
- * scales), enumerates the configs of the family
+ * operation (opts->op) for one weight layout (opts->packed).  Allocates its
+ * own inputs (random codes, bf16 activations for W8_OP_LINEAR, and scales),
+ * enumerates the configs of the family (W8_OP_LINEAR: those with x_lds and
+ * waves_k <= 4)
  * (tile_n x (waves_k or waves_n) x x_lds x unroll x (split_k in {1, 2, ...,
  * max_split_k}, or with opts->stream_k a stream-K grid in {256, 512, 1024})
  * x swap_ab) minus those that cannot pay off or duplicate another (fewer
  * than one K-step per wave, unroll above the K-steps per wave, partials
  * above twice the weight bytes, fewer than min(256, most possible) waves),
  * checks each
- * against the default config's output (bit-equal for W8A8_INT8, within 1e-2
- * relative for the FP8 formats) and times it as HIP graph replays over
+ * against the default GEMM config's output (for W8_OP_LINEAR after the
+ * standalone quantizer; bit-equal for W8A8_INT8, within 1e-2 relative for
+ * the FP8 formats) and times it as HIP graph replays over
  * rotating weight copies; the best on timing bank 1 are re-timed on bank 2,
  * and the bank-2 winner is returned (and inserted into the table when
  * opts->insert).  opts NULL = defaults.  Synchronizes the device; not

@@ -159,10 +159,33 @@ def test_config_rejects_grid_overflow(w8):
 def test_default_config_is_valid_everywhere(w8):
     import synthetic
     for fmt in w8.FORMATS:
-        for (M, N, K) in synthetic.SWEEP + ((2, 512, 7168), (32, 4096, 4096)):
+        for (M, N, K) in synthetic.SWEEP + ((2, 512, 7168), (32, 4096, 4096), (32, 5120, 8192)):
             c = w8.default_config(fmt, M, N, K)
             w8.validate_config(fmt, M, N, K, c)
             assert c.swap_ab == (1 if M < 32 else 0)
+            cl = w8.default_config(fmt, M, N, K, op="linear")
+            w8.validate_config(fmt, M, N, K, cl, op="linear")
+            assert cl.x_lds == 1
+            assert not _valid_op(w8, fmt, M, N, K, c, "linear")      # the GEMM default has no x_lds
+
+
+def _valid_op(w8, fmt, M, N, K, cfg, op):
+    try:
+        w8.validate_config(fmt, M, N, K, cfg, op=op)
+        return True
+    except w8.W8Error:
+        return False
+
+
+def test_linear_config_rules(w8):
+    ok = w8.Config.make(waves_k=4, x_lds=1, split_k=2)
+    assert _valid_op(w8, "FP8_Dynamic", 4, 512, 1024, ok, "linear")
+    assert not _valid_op(w8, "FP8_Dynamic", 4, 512, 1024, w8.Config.make(waves_k=8, x_lds=1),
+                         "linear")                                   # waves_k <= 4
+    assert _valid_op(w8, "FP8_Dynamic", 4, 512, 1024,
+                     w8.Config.make(waves_k=1, waves_n=8, x_lds=1), "linear")
+    with pytest.raises(ValueError):
+        w8.validate_config("FP8_Dynamic", 4, 512, 1024, ok, op="fused")
 
 
 FAKE = ctypes.c_void_p(0x100000)   # 16-byte aligned, never dereferenced
@@ -216,6 +239,28 @@ def test_pack_argument_errors(w8, lib):
     assert w8.packed_weight_size("Block_FP8", 4608, 7168) == 4608 * 7168
 
 
+def test_linear_argument_errors(w8, lib):
+    # every call here fails validation before anything touches a device
+    L = lib.w8_linear
+    cfg = w8.Config.make(waves_k=4, x_lds=1)
+    c = ctypes.byref(cfg)
+    assert L(0, 33, 64, 256, FAKE, 256, FAKE, 256, FAKE, FAKE, 64, c, None, 0, None) == 2
+    assert L(0, 4, 64, 200, FAKE, 256, FAKE, 256, FAKE, FAKE, 64, c, None, 0, None) == 1
+    assert L(0, 4, 64, 256, None, 256, FAKE, 256, FAKE, FAKE, 64, c, None, 0, None) == 1
+    assert L(0, 4, 64, 256, ctypes.c_void_p(0x100008), 256, FAKE, 256, FAKE, FAKE, 64, c, None, 0,
+             None) == 1                                              # x not 16-byte aligned
+    assert L(0, 4, 64, 256, FAKE, 252, FAKE, 256, FAKE, FAKE, 64, c, None, 0, None) == 1
+    assert L(0, 4, 64, 256, FAKE, 256, FAKE, 248, FAKE, FAKE, 64, c, None, 0, None) == 1
+    assert L(0, 4, 64, 256, FAKE, 256, FAKE, 256, FAKE, FAKE, 63, c, None, 0, None) == 1
+    gemm_cfg = w8.Config.make(waves_k=4)                            # no x_lds
+    assert L(0, 4, 64, 256, FAKE, 256, FAKE, 256, FAKE, FAKE, 64, ctypes.byref(gemm_cfg), None,
+             0, None) == 1
+    assert b"x_lds" in lib.w8_last_error()
+    sk = w8.Config.make(waves_k=4, x_lds=1, split_k=2)
+    assert L(0, 4, 64, 256, FAKE, 256, FAKE, 256, FAKE, FAKE, 64, ctypes.byref(sk), None, 0,
+             None) == 3                                              # workspace missing
+
+
 def test_quantize_argument_errors(lib):
     q = lib.w8_quantize_act
     assert q(0, 33, 256, FAKE, 256, FAKE, 256, FAKE, None) == 2
@@ -236,6 +281,7 @@ def test_table_roundtrip_and_lookup(w8, tmp_path):
     w8.set_config("Block_FP8", 32, 4608, 7168, c2, 5.5, packed=True)
     assert w8.config_table_size() == 2
     assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096) == c1
+    assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096, op="linear") is None
     assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096, packed=True) is None
     assert w8.lookup_config("FP8_Dynamic", 5, 4096, 4096) is None
     assert w8.lookup_config("Block_FP8", 32, 4608, 7168, packed=True, with_time=True) == (c2, 5.5)
@@ -247,31 +293,47 @@ def test_table_roundtrip_and_lookup(w8, tmp_path):
     assert not hit and got == w8.default_config("Block_FP8", 16, 4608, 7168)
     assert w8.best_layout("Block_FP8", 32, 4608, 7168) is True
     assert w8.best_layout("FP8_Dynamic", 4, 4096, 4096) is False
+    # the fused linear op has entries of its own
+    c3 = w8.Config.make(tile_n=16, waves_k=1, waves_n=8, unroll=1, split_k=4, x_lds=1)
+    w8.set_config("Block_FP8", 32, 4608, 7168, c3, 7.5, packed=True, op="linear")
+    assert w8.lookup_config("Block_FP8", 32, 4608, 7168, packed=True, op="linear") == c3
+    assert w8.lookup_config("Block_FP8", 32, 4608, 7168, packed=True) == c2
+    got, hit = w8.resolve_config("Block_FP8", 32, 4608, 7168, packed=True, op="linear")
+    assert hit and got == c3
+    got, hit = w8.resolve_config("Block_FP8", 32, 4608, 7168, op="linear")
+    assert not hit and got == w8.default_config("Block_FP8", 32, 4608, 7168, op="linear")
+    with pytest.raises(w8.W8Error):                                  # a GEMM config is no linear one
+        w8.set_config("Block_FP8", 32, 4608, 7168, c2, 5.5, packed=True, op="linear")
     p = tmp_path / "t.tbl"
     w8.save_config_table(str(p))
+    assert " linear packed 32 4608 7168 " in p.read_text()
     w8.clear_config_table()
     assert w8.config_table_size() == 0
     w8.load_config_table(str(p))
-    assert w8.config_table_size() == 2
+    assert w8.config_table_size() == 3
     assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096) == c1
     assert w8.lookup_config("Block_FP8", 32, 4608, 7168, packed=True) == c2
+    assert w8.lookup_config("Block_FP8", 32, 4608, 7168, packed=True, op="linear") == c3
 
 
 def test_table_malformed_keeps_old_table(w8, tmp_path):
     w8.set_config("W8A8_INT8", 16, 896, 1024, w8.Config.make(), 1.0)
     bad_files = [
         "gfx950 2 W8A8_INT8 row 16 896 1024 16 4 1 2 1 0\n",                # too few fields
-        "gfx950 2 INT4 row 16 896 1024 16 4 1 2 1 0 0 0 1.0\n",               # unknown format
-        "gfx950 2 W8A8_INT8 tiled 16 896 1024 16 4 1 2 1 0 0 0 1.0\n",        # unknown layout
-        "gfx950 2 W8A8_INT8 row 16 896 1024 16 4 1 2 3 0 0 0 1.0\n",          # split_k 3
-        "gfx950 2 W8A8_INT8 row 40 896 1024 16 4 1 2 1 0 0 0 1.0\n",          # M above 32
-        "gfx950 2 W8A8_INT8 row 16 896 1024 16 4 1 x 1 0 0 0 1.0\n",          # not an integer
-        "gfx950 2 W8A8_INT8 row 16 896 1024 16 4 1 2 1 0 0 0 fast\n",         # bad time
-        "gfx950 2 W8A8_INT8 row 16 896 1024 64 4 1 2 1 0 0 0 1.0\n",          # tile 64 x unroll 2
-        "gfx950 2 W8A8_INT8 row 16 896 1024 16 2 2 2 1 0 0 0 1.0\n",          # waves_k and waves_n
-        "gfx950 2 W8A8_INT8 row 16 896 1024 16 1 1 2 2 256 0 0 1.0\n",        # grid with split_k
-        "gfx950 2 W8A8_INT8 row 16 896 1024 16 1 1 2 1 100000 0 0 1.0\n",     # grid > iterations
-        "gfx950 2 W8A8_INT8 row 16 896 1024 16 16 1 2 1 0 0 1 1.0\n",        # x_lds, 16 waves
+        "gfx950 2 INT4 gemm row 16 896 1024 16 4 1 2 1 0 0 0 1.0\n",               # unknown format
+        "gfx950 2 W8A8_INT8 gemm tiled 16 896 1024 16 4 1 2 1 0 0 0 1.0\n",        # unknown layout
+        "gfx950 2 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 3 0 0 0 1.0\n",          # split_k 3
+        "gfx950 2 W8A8_INT8 gemm row 40 896 1024 16 4 1 2 1 0 0 0 1.0\n",          # M above 32
+        "gfx950 2 W8A8_INT8 gemm row 16 896 1024 16 4 1 x 1 0 0 0 1.0\n",          # not an integer
+        "gfx950 2 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 fast\n",         # bad time
+        "gfx950 2 W8A8_INT8 gemm row 16 896 1024 64 4 1 2 1 0 0 0 1.0\n",          # tile 64 x unroll 2
+        "gfx950 2 W8A8_INT8 gemm row 16 896 1024 16 2 2 2 1 0 0 0 1.0\n",          # waves_k and waves_n
+        "gfx950 2 W8A8_INT8 gemm row 16 896 1024 16 1 1 2 2 256 0 0 1.0\n",        # grid with split_k
+        "gfx950 2 W8A8_INT8 gemm row 16 896 1024 16 1 1 2 1 100000 0 0 1.0\n",     # grid > iterations
+        "gfx950 2 W8A8_INT8 gemm row 16 896 1024 16 16 1 2 1 0 0 1 1.0\n",        # x_lds, 16 waves
+        "gfx950 2 W8A8_INT8 fused row 16 896 1024 16 4 1 2 1 0 0 1 1.0\n",       # unknown op
+        "gfx950 2 W8A8_INT8 linear row 16 896 1024 16 4 1 2 1 0 0 0 1.0\n",      # linear without x_lds
+        "gfx950 2 W8A8_INT8 linear row 16 896 1024 16 8 1 2 1 0 0 1 1.0\n",      # linear, 8 waves_k
     ]
     for i, text in enumerate(bad_files):
         p = tmp_path / f"bad{i}.tbl"
@@ -287,10 +349,10 @@ def test_table_malformed_keeps_old_table(w8, tmp_path):
 
 def test_table_foreign_entries_ignored_and_kept(w8, tmp_path):
     p = tmp_path / "mixed.tbl"
-    p.write_text("gfx942 2 FP8_Dynamic row 4 4096 4096 64 2 1 4 1 0 1 0 2.0\n"
+    p.write_text("gfx942 2 FP8_Dynamic gemm row 4 4096 4096 64 2 1 4 1 0 1 0 2.0\n"
                  "gfx950 9 FP8_Dynamic row 4 4096 4096 64 2 1 4 1 0 1 2.0\n"
                  "gfx950 1 FP8_Dynamic row 4 4096 4096 32 2 2 4 0 2.5\n"
-                 "gfx950 2 FP8_Dynamic row 4 4096 4096 32 2 1 2 4 0 0 0 2.5  # native\n")
+                 "gfx950 2 FP8_Dynamic gemm row 4 4096 4096 32 2 1 2 4 0 0 0 2.5  # native\n")
     w8.load_config_table(str(p))
     assert w8.config_table_size() == 1 and w8.config_table_foreign() == 3
     assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096) == \
@@ -298,13 +360,13 @@ def test_table_foreign_entries_ignored_and_kept(w8, tmp_path):
     q = tmp_path / "out.tbl"
     w8.save_config_table(str(q))
     text = q.read_text()
-    assert "gfx942 2 FP8_Dynamic row" in text and "gfx950 9 FP8_Dynamic row" in text
+    assert "gfx942 2 FP8_Dynamic gemm row" in text and "gfx950 9 FP8_Dynamic row" in text
     assert "gfx950 1 FP8_Dynamic row 4 4096 4096 32 2 2 4 0 2.5" in text   # older ABI, kept
 
 
 def test_table_from_environment(tmp_path):
     p = tmp_path / "env.tbl"
-    p.write_text("gfx950 2 W8A8_INT8 row 16 896 1024 32 2 1 2 8 0 1 0 0.5\n")
+    p.write_text("gfx950 2 W8A8_INT8 gemm row 16 896 1024 32 2 1 2 8 0 1 0 0.5\n")
     code = ("import bit_quantized_gemm_token_amd as w8;"
             "c = w8.lookup_config('W8A8_INT8', 16, 896, 1024);"
             "print(c.as_dict() if c else None)")
@@ -320,7 +382,7 @@ def test_table_from_environment(tmp_path):
 
 def test_env_table_loaded_by_the_c_library_alone(tmp_path):
     p = tmp_path / "env.tbl"
-    p.write_text("gfx950 2 W8A8_INT8 row 16 896 1024 32 2 1 2 8 0 1 0 0.5\n")
+    p.write_text("gfx950 2 W8A8_INT8 gemm row 16 896 1024 32 2 1 2 8 0 1 0 0.5\n")
     from bit_quantized_gemm_token_amd import _capi
     # load _capi.py on its own (the package __init__ would load the shipped table)
     code = (
@@ -330,7 +392,7 @@ def test_env_table_loaded_by_the_c_library_alone(tmp_path):
         "spec.loader.exec_module(_capi)\n"
         "lib = _capi.load()\n"
         "c = _capi.Config()\n"
-        "print(lib.w8_lookup_config(1, 16, 896, 1024, 0, ctypes.byref(c), None), c.split_k, c.tile_n)\n")
+        "print(lib.w8_lookup_config(1, 0, 16, 896, 1024, 0, ctypes.byref(c), None), c.split_k, c.tile_n)\n")
     env = dict(os.environ, W8_CONFIG_TABLE=str(p))
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                          check=True).stdout.split()

@@ -1,0 +1,167 @@
+"""The fused linear layer (w8_linear: activation quantization inside the
+GEMM) on the GPU.
+
+- bf16 Y bit-identical to the two-launch path (w8_quantize_act, then
+  w8_gemm_w8a8) with the same config: the fused staging uses the standalone
+  quantizer's rules, so codes, scales and the MFMA sequence all match;
+- Y within atol = rtol = 1e-2 of the oracle's fp64 result (oracle codes
+  from the same bf16 activations);
+- every fused-quantization instance at a ragged shape, whole tiles, split-K
+  and stream-K; ragged K (masked tail step); all-zero rows; graph replay.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_cases import DEV, Case, assert_bf16_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def w8():
+    import bit_quantized_gemm_token_amd as mod
+    return mod
+
+
+_cases = {}
+
+
+def case(fmt, M, N, K):
+    key = (fmt, M, N, K)
+    if key not in _cases:
+        _cases.clear()
+        _cases[key] = Case(fmt, M, N, K)
+    return _cases[key]
+
+
+def two_launch(w8, cs, cfg, packed):
+    xq, sx = w8.quantize_act(cs.fmt, cs.x)
+    return w8.gemm_w8a8(cs.fmt, xq, sx, cs.weights(packed), cs.sw, cfg=cfg)
+
+
+def fused(w8, cs, cfg, packed, x=None):
+    return w8.linear(cs.fmt, cs.x if x is None else x, cs.weights(packed), cs.sw, cfg=cfg,
+                     fused=True)
+
+
+def same_bits(a, b):
+    return torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# (waves_k, waves_n) of the fused instances
+FUSED_WAVES = ((1, 1), (2, 1), (4, 1), (1, 2), (1, 4), (1, 8))
+
+
+@pytest.mark.parametrize("fmt", ["W8A8_INT8", "FP8_Dynamic", "Block_FP8"])
+def test_every_fused_instance(w8, fmt):
+    """Every fused-quantization instance (tile_n x waves x unroll x swap_ab x
+    layout) at M = 17 (two 16-row blocks of M), with whole tiles, split-K and
+    stream-K, against the two-launch path bit for bit."""
+    M, N, K = 17, 200, 1280
+    cs = case(fmt, M, N, K)
+    n = 0
+    for tn, (wk, wn), u, swap, (s, grid), packed in itertools.product(
+            (16, 32, 64), FUSED_WAVES, (1, 2, 4), (0, 1), ((1, 0), (4, 0), (1, 3)), (False, True)):
+        if (tn // 16) * u > 4:
+            continue
+        cfg = w8.Config.make(tile_n=tn, waves_k=wk, waves_n=wn, unroll=u, split_k=s, grid=grid,
+                             swap_ab=swap, x_lds=1)
+        y1 = fused(w8, cs, cfg, packed)
+        y2 = two_launch(w8, cs, cfg, packed)
+        torch.cuda.synchronize()
+        assert same_bits(y1, y2), f"{fmt} {cfg} packed={packed}: fused != two-launch"
+        n += 1
+    assert n == 6 * 6 * 2 * 3 * 2
+    assert_bf16_close(y1, cs.Y, f"fused {fmt}")
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [
+    ("W8A8_INT8", 1, 16, 16), ("W8A8_INT8", 5, 200, 208), ("W8A8_INT8", 32, 1000, 1040),
+    ("FP8_Dynamic", 1, 16, 16), ("FP8_Dynamic", 31, 77, 336), ("FP8_Dynamic", 32, 1000, 1040),
+    ("Block_FP8", 1, 16, 128), ("Block_FP8", 20, 130, 256), ("Block_FP8", 32, 1000, 1024)])
+def test_fused_ragged_shapes(w8, fmt, M, N, K):
+    """Ragged M, N and K (the masked tail K-step is quantized in the stage),
+    default and explicit configs, both weight layouts, against the oracle and
+    the two-launch path."""
+    cs = case(fmt, M, N, K)
+    for packed in (False, True):
+        for cfg in (None, w8.Config.make(tile_n=32, waves_k=2, unroll=2, split_k=2, x_lds=1),
+                    w8.Config.make(tile_n=16, waves_k=1, waves_n=4, unroll=1, swap_ab=1,
+                                   x_lds=1)):
+            y = fused(w8, cs, cfg, packed)
+            torch.cuda.synchronize()
+            assert_bf16_close(y, cs.Y, f"fused ragged {fmt} {cfg} packed={packed}")
+            if cfg is not None:
+                assert same_bits(y, two_launch(w8, cs, cfg, packed)), f"{fmt} {cfg}"
+
+
+@pytest.mark.parametrize("fmt,M", [("W8A8_INT8", 1), ("FP8_Dynamic", 8), ("Block_FP8", 32),
+                                   ("FP8_Dynamic", 32)])
+def test_fused_large(w8, fmt, M):
+    """4608 x 7168 (56 or 112 K-steps): per-token row scales over the whole
+    K, split-K and stream-K grids, against the oracle and the two-launch
+    path."""
+    cs = case(fmt, M, 4608, 7168)
+    for cfg in (w8.Config.make(tile_n=16, waves_k=1, waves_n=8, unroll=1, split_k=4, x_lds=1),
+                w8.Config.make(tile_n=16, waves_k=4, unroll=2, split_k=8, x_lds=1, swap_ab=1),
+                w8.Config.make(tile_n=32, waves_k=2, unroll=1, grid=512, x_lds=1)):
+        y = fused(w8, cs, cfg, True)
+        torch.cuda.synchronize()
+        assert_bf16_close(y, cs.Y, f"fused large {fmt} M={M} {cfg}")
+        assert same_bits(y, two_launch(w8, cs, cfg, True)), f"{fmt} M={M} {cfg}"
+
+
+@pytest.mark.parametrize("fmt", ["W8A8_INT8", "FP8_Dynamic", "Block_FP8"])
+def test_fused_zero_rows(w8, fmt):
+    """An all-zero row (and, for Block_FP8, all-zero groups) takes scale 1 and
+    codes 0 in the stage, like the standalone quantizer."""
+    cs = case(fmt, 8, 272, 640 if fmt != "Block_FP8" else 768)
+    x = cs.x.clone()
+    x[3] = 0
+    x[5, :128] = 0
+    cfg = w8.Config.make(tile_n=16, waves_k=2, unroll=2, split_k=2, x_lds=1)
+    y1 = fused(w8, cs, cfg, True, x=x)
+    xq, sx = w8.quantize_act(fmt, x)
+    y2 = w8.gemm_w8a8(fmt, xq, sx, cs.weights(True), cs.sw, cfg=cfg)
+    torch.cuda.synchronize()
+    assert same_bits(y1, y2)
+    assert (y1[3].float() == 0).all()
+
+
+def test_fused_graph_replay(w8):
+    cs = case("FP8_Dynamic", 4, 4096, 4096)
+    cfg = w8.Config.make(tile_n=16, waves_k=4, unroll=2, split_k=8, x_lds=1)
+    wp = cs.packed()
+    ws = w8.Workspace(DEV, w8.workspace_size("FP8_Dynamic", 4, 4096, 4096, cfg, packed=True,
+                                             op="linear"))
+    eager = w8.linear("FP8_Dynamic", cs.x, wp, cs.sw, cfg=cfg, workspace=ws, fused=True).clone()
+    x_static = cs.x.clone()
+    y_static = torch.empty_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        w8.linear("FP8_Dynamic", x_static, wp, cs.sw, cfg=cfg, y=y_static, workspace=ws,
+                  fused=True)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w8.linear("FP8_Dynamic", x_static, wp, cs.sw, cfg=cfg, y=y_static, workspace=ws,
+                  fused=True)
+    for i in range(4):
+        y_static.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert same_bits(y_static, eager), f"replay {i}"
+        junk = torch.randn(512, 512, device=DEV) @ torch.randn(512, 512, device=DEV)
+        del junk
+    assert_bf16_close(y_static, cs.Y, "fused graph replay")
+
+
+def test_fused_rejects_gemm_config(w8):
+    cs = case("W8A8_INT8", 4, 64, 256)
+    with pytest.raises(w8.W8Error, match="x_lds"):
+        fused(w8, cs, w8.Config.make(waves_k=4), False)

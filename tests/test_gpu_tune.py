@@ -26,33 +26,37 @@ def _restore_table(w8):
     w8.load_default_table()
 
 
-@pytest.mark.parametrize("fmt,M,N,K,packed,stream_k", [("W8A8_INT8", 16, 896, 1024, False, False),
-                                                       ("FP8_Dynamic", 4, 512, 2048, True, True),
-                                                       ("Block_FP8", 8, 512, 1024, False, False),
-                                                       ("Block_FP8", 32, 512, 1024, True, False)])
-def test_tune_shape(w8, fmt, M, N, K, packed, stream_k, tmp_path):
-    print(f"[tune] {fmt} M={M} N={N} K={K} packed={packed} stream_k={stream_k}", flush=True)
+@pytest.mark.parametrize("fmt,M,N,K,packed,stream_k,op", [
+    ("W8A8_INT8", 16, 896, 1024, False, False, "gemm"),
+    ("FP8_Dynamic", 4, 512, 2048, True, True, "gemm"),
+    ("Block_FP8", 8, 512, 1024, False, False, "gemm"),
+    ("Block_FP8", 32, 512, 1024, True, False, "gemm"),
+    ("FP8_Dynamic", 8, 512, 2048, True, False, "linear"),
+    ("W8A8_INT8", 1, 896, 1040, False, False, "linear")])
+def test_tune_shape(w8, fmt, M, N, K, packed, stream_k, op, tmp_path):
+    print(f"[tune] {op} {fmt} M={M} N={N} K={K} packed={packed} stream_k={stream_k}", flush=True)
     w8.clear_config_table()
-    best, st = w8.tune_shape(fmt, M, N, K, packed=packed, stream_k=stream_k, **SMALL)
+    best, st = w8.tune_shape(fmt, M, N, K, packed=packed, stream_k=stream_k, op=op, **SMALL)
     print(f"[tune] best {best} stats {st}", flush=True)
-    w8.validate_config(fmt, M, N, K, best)
-    assert st["candidates"] > 50 and st["validated"] == st["candidates"] and st["rejected"] == 0
+    w8.validate_config(fmt, M, N, K, best, op=op)
+    assert st["candidates"] > 10 and st["validated"] == st["candidates"] and st["rejected"] == 0
     assert best.split_k <= 8
     assert st["best_us_bank2"] > 0 and st["best_gbps"] > 0
     assert st["best_us_bank2"] <= st["default_us_bank2"] * 1.10
-    assert w8.lookup_config(fmt, M, N, K, packed=packed) == best
-    assert w8.lookup_config(fmt, M, N, K, packed=not packed) is None
-    cfg, hit = w8.resolve_config(fmt, M, N, K, packed=packed)
+    assert w8.lookup_config(fmt, M, N, K, packed=packed, op=op) == best
+    assert w8.lookup_config(fmt, M, N, K, packed=not packed, op=op) is None
+    cfg, hit = w8.resolve_config(fmt, M, N, K, packed=packed, op=op)
     assert hit and cfg == best
     p = tmp_path / "tuned.tbl"
     w8.save_config_table(str(p))
     w8.clear_config_table()
     w8.load_config_table(str(p))
-    assert w8.lookup_config(fmt, M, N, K, packed=packed) == best
+    assert w8.lookup_config(fmt, M, N, K, packed=packed, op=op) == best
     cs = Case(fmt, M, N, K)
-    y = w8.linear(fmt, cs.x, cs.weights(packed), cs.sw)   # resolves the tuned entry
+    # resolves the tuned entry
+    y = w8.linear(fmt, cs.x, cs.weights(packed), cs.sw, fused=(op == "linear"))
     torch.cuda.synchronize()
-    assert_bf16_close(y, cs.Y, f"tuned {fmt}")
+    assert_bf16_close(y, cs.Y, f"tuned {op} {fmt}")
 
 
 def test_tune_rejects_injected_failure(w8):
