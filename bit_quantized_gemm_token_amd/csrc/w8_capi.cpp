@@ -226,14 +226,12 @@ w8_status launch_gemm_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
   if (!fn) return fail(W8_E_INVALID, "no compiled kernel for this config");
   const int ntiles = tiles_of(g.N, c);
   GemmArgs a;
-  a.xq = static_cast<const uint8_t*>(g.xq);
+  a.xq = static_cast<const uint8_t*>(g.x ? g.x : g.xq);  // fused: bf16 activations
   a.sx = g.sx;
-  a.x = static_cast<const uint16_t*>(g.x);
-  a.ldx = g.ldx;
   a.wq = static_cast<const uint8_t*>(g.wq);
   a.sw = g.sw;
   a.out = g.out;
-  a.ldq = g.ldq;
+  a.ldq = g.x ? g.ldx : g.ldq;
   a.ldw = g.ldw;
   a.ldo = g.ldo;
   a.M = g.M;

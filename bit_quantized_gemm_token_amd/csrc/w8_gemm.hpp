@@ -190,7 +190,7 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
     // Row scales over the whole of K, one wave per row (the standalone
     // quantizer's rule, so the codes match it).
     for (int m = wave; m < a.M; m += WK * WN) {
-      const uint16_t* xr = a.x + (long long)m * a.ldx;
+      const uint16_t* xr = reinterpret_cast<const uint16_t*>(a.xq) + (long long)m * a.ldq;
       float amax = 0.0f;
       for (int c = lane; c < a.K / 8; c += 64)
         amax = fmaxf(amax, absmax8(*reinterpret_cast<const v4u*>(xr + 8 * c)));
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
           const int kk = act ? u / a.M : 0, m = act ? u % a.M : 0;
           v4u v = v4u{0u, 0u, 0u, 0u};
           if (act)
-            v = *reinterpret_cast<const v4u*>(a.x + (long long)m * a.ldx +
+            v = *reinterpret_cast<const v4u*>(reinterpret_cast<const uint16_t*>(a.xq) + (long long)m * a.ldq +
                                               (long long)(ka + kk) * kGroup + 8 * j);
           const float amax = seg16_max(absmax8(v));
           if (act && j == 0) sxl[kk * 32 + m] = act_scale<false>(amax);
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
         const int e = (ka + kk) * KSTEP + 64 * jj + 16 * (l >> 4);  // first element
         v4u lo = v4u{0u, 0u, 0u, 0u}, hi = lo;
         if (e < a.K) {  // (K % 16 == 0: the chunk is wholly inside K or past it)
-          const uint16_t* src = a.x + (long long)row * a.ldx + e;
+          const uint16_t* src = reinterpret_cast<const uint16_t*>(a.xq) + (long long)row * a.ldq + e;
           lo = *reinterpret_cast<const v4u*>(src);
           hi = *reinterpret_cast<const v4u*>(src + 8);
         }

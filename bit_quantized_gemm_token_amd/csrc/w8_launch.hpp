@@ -32,10 +32,10 @@ hipError_t launch_quantize_weight(int fmt, const QuantWeightArgs& a, hipStream_t
 
 // ------------------------------------------------------------------ GEMM --
 struct GemmArgs {
-  const uint8_t* xq;       // activation codes [M, K], row stride ldq bytes
-  const float* sx;         // activation scales
-  const uint16_t* x;       // fused quantization: bf16 activations [M, K], row stride ldx
-  long long ldx;           // elements
+  // Activation codes [M, K] (row stride ldq bytes), or for the fused
+  // quantization (XL == 2) bf16 activations [M, K] (row stride ldq elements).
+  const uint8_t* xq;
+  const float* sx;         // activation scales (unused with XL == 2)
   const uint8_t* wq;       // weight codes [N, K], row stride ldw bytes
   const float* sw;         // weight scales
   void* out;               // bf16 Y [M, N] or 4-byte accumulators, stride ldo elements
