@@ -9,7 +9,10 @@ table shipped with the package; default config on a miss).
 Per problem, three HIP graphs are captured once:
   gemm   R back-to-back GEMMs, each reading its own copy of the weights;
   path   R back-to-back (activation quantization + GEMM) pairs;
-  fused  R back-to-back fused linear layers (quantization inside the GEMM).
+  linear R back-to-back linear layers through the single entry point
+         w8_linear with its own table entry: the fused kernel (quantization
+         inside the GEMM, one launch) or, where the tuner found it faster,
+         the quantize kernel and the GEMM (quant_launch = 1).
 The R weight copies span at least --rotate-mib MiB (default 1024), more than
 the last-level cache, so every weight byte read in the timed region comes
 from HBM.  One step replays the three graphs of every problem once; W warmup steps
@@ -19,8 +22,9 @@ Per problem: us per GEMM = median over steps of (graph time / R).  The
 headline value is the geometric mean over the 72 problems of the achieved
 GB/s of the GEMM, algorithmic bytes (weights + activations + scales + bf16
 output) / us per GEMM; geomean us per GEMM is reported beside it, and so is
-the same pair for the whole path (quantize + GEMM, two launches) and the
-time of the fused linear layer (one launch).
+the same pair for the whole path (quantize + GEMM, two calls) and the time
+of the linear layer through w8_linear (with the count of problems whose
+table entry is the fused kernel).
 
 roofline: the dominant GEMM kernel instance (largest summed time over the
 problems that use it), achieved = its algorithmic bytes per launch / its
@@ -228,8 +232,8 @@ class Problem:
         self.xq, self.sx = w8.quantize_act(fmt, self.x)
         self.y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         self.ws = w8.Workspace(dev, max(w8.workspace_size(fmt, M, N, K, self.cfg), 256))
-        # the fused linear layer (quantization inside the GEMM), with its own
-        # table entry for the same weight layout
+        # the linear layer through w8_linear, with its own table entry for the
+        # same weight layout (fused kernel or quantize launch + GEMM)
         self.cfg_l, self.from_table_l = w8.resolve_config(fmt, M, N, K, packed=self.packed,
                                                           op="linear")
         self.ws_l = w8.Workspace(dev, max(w8.workspace_size(fmt, M, N, K, self.cfg_l,
@@ -250,7 +254,7 @@ class Problem:
             w8.gemm_w8a8(self.fmt, xq, sx, self.weights[r], self.sw, cfg=self.cfg, y=self.y,
                          workspace=self.ws)
 
-    def run_fused(self, w8):
+    def run_linear(self, w8):
         for r in range(self.R):
             w8.linear(self.fmt, self.x, self.weights[r], self.sw, cfg=self.cfg_l, y=self.y,
                       workspace=self.ws_l, fused=True)
@@ -258,13 +262,13 @@ class Problem:
     def capture(self, w8, stream):
         self.g_gemm = torch.cuda.CUDAGraph()
         self.g_path = torch.cuda.CUDAGraph()
-        self.g_fused = torch.cuda.CUDAGraph()
+        self.g_linear = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.g_gemm, stream=stream):
             self.run_gemm(w8)
         with torch.cuda.graph(self.g_path, stream=stream):
             self.run_path(w8)
-        with torch.cuda.graph(self.g_fused, stream=stream):
-            self.run_fused(w8)
+        with torch.cuda.graph(self.g_linear, stream=stream):
+            self.run_linear(w8)
 
 
 def geomean(v):
@@ -302,7 +306,7 @@ def cpu_baseline(problems, budget_s):
                 # refcheck: the GPU outputs of this problem (two-launch and
                 # fused paths) against the oracle
                 ok = True
-                for y in (p.y_check, p.y_check_fused):
+                for y in (p.y_check, p.y_check_linear):
                     got = y.float().cpu().numpy().astype(np.float64)
                     ok = ok and bool((np.abs(got - Y) <= 1e-2 + 1e-2 * np.abs(Y)).all())
                 p.refcheck = ok
@@ -368,13 +372,13 @@ def main():
                 ev[1].record(stream)
                 p.g_path.replay()
                 ev[2].record(stream)
-                p.g_fused.replay()
+                p.g_linear.replay()
                 ev[3].record(stream)
                 p.events.append(ev)
             else:
                 p.g_gemm.replay()
                 p.g_path.replay()
-                p.g_fused.replay()
+                p.g_linear.replay()
 
     with torch.cuda.stream(stream):
         for p in problems:
@@ -396,14 +400,14 @@ def main():
         f = sorted(e[2].elapsed_time(e[3]) for e in p.events)
         p.us_gemm = g[len(g) // 2] * 1e3 / p.R
         p.us_path = a[len(a) // 2] * 1e3 / p.R
-        p.us_fused = f[len(f) // 2] * 1e3 / p.R
+        p.us_linear = f[len(f) // 2] * 1e3 / p.R
         p.gbps = p.bytes / (p.us_gemm * 1e3)
         p.gbps_path = p.bytes / (p.us_path * 1e3)
         p.us_gemm_min = g[0] * 1e3 / p.R
         p.us_gemm_p90 = g[min(len(g) - 1, int(0.9 * len(g)))] * 1e3 / p.R
         # one eager run of each path for the refcheck
         p.y_check = w8.linear(p.fmt, p.x, p.wq, p.sw, cfg=p.cfg)
-        p.y_check_fused = w8.linear(p.fmt, p.x, p.wq, p.sw, cfg=p.cfg_l, fused=True)
+        p.y_check_linear = w8.linear(p.fmt, p.x, p.wq, p.sw, cfg=p.cfg_l, fused=True)
     torch.cuda.synchronize()
 
     # dominant kernel instance
@@ -441,7 +445,7 @@ def main():
         per_fmt[fmt] = {"geomean_us_per_gemm": round(geomean([p.us_gemm for p in ps]), 4),
                         "geomean_gbps": round(geomean([p.gbps for p in ps]), 2),
                         "geomean_us_quant_plus_gemm": round(geomean([p.us_path for p in ps]), 4),
-                        "geomean_us_fused_linear": round(geomean([p.us_fused for p in ps]), 4)}
+                        "geomean_us_linear": round(geomean([p.us_linear for p in ps]), 4)}
     value = geomean([p.gbps for p in problems])
     out = {
         "metric": "geomean us/GEMM + achieved HBM GB/s, 8-bit GEMM sweep M<=32 (1 GPU)",
@@ -465,9 +469,10 @@ def main():
         "geomean_us_per_gemm": round(geomean([p.us_gemm for p in problems]), 4),
         "geomean_us_quant_plus_gemm": round(geomean([p.us_path for p in problems]), 4),
         "geomean_gbps_quant_plus_gemm": round(geomean([p.gbps_path for p in problems]), 2),
-        "geomean_us_fused_linear": round(geomean([p.us_fused for p in problems]), 4),
-        "geomean_gbps_fused_linear": round(geomean([p.bytes / (p.us_fused * 1e3)
-                                                    for p in problems]), 2),
+        "geomean_us_linear": round(geomean([p.us_linear for p in problems]), 4),
+        "geomean_gbps_linear": round(geomean([p.bytes / (p.us_linear * 1e3)
+                                              for p in problems]), 2),
+        "linear_fused_problems": sum(p.cfg_l.quant_launch == 0 for p in problems),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "per_format": per_fmt,
         "refcheck": refcheck,
@@ -480,7 +485,7 @@ def main():
                  "from_table": p.from_table, "R": p.R, "bytes": p.bytes,
                  "us_gemm": round(p.us_gemm, 4), "us_gemm_min": round(p.us_gemm_min, 4),
                  "us_gemm_p90": round(p.us_gemm_p90, 4), "us_quant_plus_gemm": round(p.us_path, 4),
-                 "us_fused_linear": round(p.us_fused, 4), "cfg_linear": p.cfg_l.as_dict(),
+                 "us_linear": round(p.us_linear, 4), "cfg_linear": p.cfg_l.as_dict(),
                  "linear_from_table": p.from_table_l,
                  "gbps": round(p.gbps, 1), "frac": round(p.gbps / HBM_PEAK_GBPS, 4),
                  "kernel": p.kernel} for p in problems]

@@ -282,11 +282,12 @@ def gemm_w8a8_acc(fmt, xq, sx, wq, sw, cfg=None, out=None, workspace=None, strea
 def linear(fmt, x, wq, sw, cfg=None, y=None, workspace=None, stream=None, fused=False):
     """The whole hot path on bf16 activations x [M, K].
 
-    fused=False: quantize_act, then gemm_w8a8 (two launches; cfg is the GEMM
-    config).  fused=True: w8_linear, quantization fused into the GEMM (one
-    launch; cfg must have x_lds=1, None = the table's "linear" entry).  Both
-    give the same Y for the same cfg.  wq: row-major codes [N, K] or a
-    PackedWeight."""
+    fused=False: quantize_act, then gemm_w8a8 (two calls; cfg is the GEMM
+    config).  fused=True: the single entry point w8_linear with a linear-op
+    config (None = the table's "linear" entry): cfg.quant_launch = 0 fuses the
+    quantization into the GEMM (one launch; needs x_lds=1), 1 runs the
+    quantize kernel into the workspace and then the GEMM.  All give the same Y
+    for the same tile config.  wq: row-major codes [N, K] or a PackedWeight."""
     if not fused:
         xq, sx = quantize_act(fmt, x, stream=stream)
         return gemm_w8a8(fmt, xq, sx, wq, sw, cfg=cfg, y=y, workspace=workspace, stream=stream)

@@ -5,7 +5,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw8gemm.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 MAX_M = 32
 MAX_SPLIT_K = 256
 GROUP = 128
@@ -34,17 +34,19 @@ class Config(ctypes.Structure):
                 ("waves_k", ctypes.c_int32), ("waves_n", ctypes.c_int32),
                 ("unroll", ctypes.c_int32), ("split_k", ctypes.c_int32),
                 ("grid", ctypes.c_int32), ("swap_ab", ctypes.c_int32),
-                ("x_lds", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
+                ("x_lds", ctypes.c_int32), ("quant_launch", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 1)]
 
-    KEYS = ("tile_n", "waves_k", "waves_n", "unroll", "split_k", "grid", "swap_ab", "x_lds")
+    KEYS = ("tile_n", "waves_k", "waves_n", "unroll", "split_k", "grid", "swap_ab", "x_lds",
+            "quant_launch")
 
     @classmethod
     def make(cls, tile_n=16, waves_k=4, unroll=2, split_k=1, swap_ab=0, waves_n=1, grid=0,
-             x_lds=None):
+             x_lds=None, quant_launch=0):
         if x_lds is None:
             x_lds = 1 if waves_n > 1 else 0
         return cls(ABI_VERSION, tile_n, waves_k, waves_n, unroll, split_k, grid, int(swap_ab),
-                   int(x_lds))
+                   int(x_lds), int(quant_launch))
 
     def as_dict(self):
         return {k: int(getattr(self, k)) for k in self.KEYS}

@@ -97,7 +97,7 @@ w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c) {
   if (c.abi_version != W8_ABI_VERSION)
     return fail(W8_E_INVALID, "cfg.abi_version " + std::to_string(c.abi_version) + " != " +
                                   std::to_string(W8_ABI_VERSION));
-  if (c.reserved[0] || c.reserved[1]) return fail(W8_E_INVALID, "cfg.reserved must be zero");
+  if (c.reserved[0]) return fail(W8_E_INVALID, "cfg.reserved must be zero");
   if (nb_index(c.tile_n / 16) < 0 || c.tile_n % 16)
     return fail(W8_E_INVALID, "cfg.tile_n must be 16, 32 or 64");
   if (wk_index(c.waves_k) < 0) return fail(W8_E_INVALID, "cfg.waves_k must be 1, 2, 4, 8 or 16");
@@ -108,8 +108,13 @@ w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c) {
   if (c.waves_n > 1 && !c.x_lds) return fail(W8_E_INVALID, "cfg: waves_n > 1 needs x_lds == 1");
   if (c.x_lds && c.waves_k > 8) return fail(W8_E_INVALID, "cfg: x_lds needs waves_k <= 8");
   if (op != W8_OP_GEMM && op != W8_OP_LINEAR) return fail(W8_E_INVALID, "unknown op");
-  if (op == W8_OP_LINEAR && (!c.x_lds || c.waves_k > 4))
-    return fail(W8_E_INVALID, "cfg: the fused linear op needs x_lds == 1 and waves_k <= 4");
+  if (c.quant_launch != 0 && c.quant_launch != 1)
+    return fail(W8_E_INVALID, "cfg.quant_launch must be 0 or 1");
+  if (op == W8_OP_GEMM && c.quant_launch)
+    return fail(W8_E_INVALID, "cfg.quant_launch is for the linear op only");
+  if (op == W8_OP_LINEAR && !c.quant_launch && (!c.x_lds || c.waves_k > 4))
+    return fail(W8_E_INVALID,
+                "cfg: the fused linear op (quant_launch == 0) needs x_lds == 1 and waves_k <= 4");
   if (u_index(c.unroll) < 0) return fail(W8_E_INVALID, "cfg.unroll must be 1, 2 or 4");
   if ((c.tile_n / 16) * c.unroll > 4)
     return fail(W8_E_INVALID, "cfg: tile_n/16 * unroll must be at most 4");
@@ -159,12 +164,31 @@ int partial_slots(int fmt, int N, int K, const w8_cfg& c) {
   return c.split_k;
 }
 
-size_t workspace_bytes(int fmt, int M, int N, int K, const w8_cfg& c) {
+static size_t gemm_ws_bytes(int fmt, int M, int N, int K, const w8_cfg& c) {
   if (c.split_k <= 1 && c.grid <= 0) return 0;
   const int ntiles = tiles_of(N, c);
   const int mb = (M + 15) / 16;
   return ws_counter_bytes(ntiles) + ws_partial_bytes(ntiles, partial_slots(fmt, N, K, c),
                                                      c.waves_n * c.tile_n / 16, mb);
+}
+
+static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+LinearWs linear_ws(int fmt, int M, int N, int K, const w8_cfg& c) {
+  LinearWs w;
+  w.ldq = (K + 15) / 16 * 16;
+  // past the arrival counters even when this config shares no tile: another
+  // call on the same workspace may need them at zero
+  w.codes = round256(std::max(gemm_ws_bytes(fmt, M, N, K, c), ws_counter_bytes(0)));
+  w.scales = w.codes + round256((size_t)M * w.ldq);
+  const size_t nsx = fmt == W8_BLOCK_FP8 ? (size_t)M * (K / W8_GROUP) : (size_t)M;
+  w.total = w.scales + round256(nsx * 4);
+  return w;
+}
+
+size_t workspace_bytes(int fmt, int op, int M, int N, int K, const w8_cfg& c) {
+  if (op == W8_OP_LINEAR && c.quant_launch) return linear_ws(fmt, M, N, K, c).total;
+  return gemm_ws_bytes(fmt, M, N, K, c);
 }
 
 // Default config (used when the table has no entry for the shape).  It
@@ -258,6 +282,26 @@ w8_status launch_gemm_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
   return W8_OK;
 }
 
+w8_status launch_linear_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
+  if (!c.quant_launch) return launch_gemm_call(g, c, s);
+  // quantize into the workspace, then the GEMM on the codes
+  const LinearWs w = linear_ws(g.fmt, g.M, g.N, g.K, c);
+  char* base = static_cast<char*>(g.ws);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(base + w.codes);
+  float* sx = reinterpret_cast<float*>(base + w.scales);
+  QuantActArgs q{static_cast<const uint16_t*>(g.x), xq, sx, g.ldx, w.ldq, g.M, g.K};
+  hipError_t e = launch_quantize_act(g.fmt, q, s);
+  if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("quantize_act launch", e));
+  GemmCall gg = g;
+  gg.xq = xq;
+  gg.ldq = w.ldq;
+  gg.sx = sx;
+  gg.x = nullptr;
+  gg.ldx = 0;
+  gg.ws_bytes = w.codes;
+  return launch_gemm_call(gg, c, s);
+}
+
 }  // namespace w8
 
 using namespace w8;
@@ -289,7 +333,7 @@ w8_status gemm_entry(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ld
   } else {
     c = resolve_cfg(fmt, W8_OP_GEMM, M, N, K, packed, nullptr);
   }
-  const size_t need = workspace_bytes(fmt, M, N, K, c);
+  const size_t need = workspace_bytes(fmt, W8_OP_GEMM, M, N, K, c);
   if (need > 0) {
     if (!ws || ws_bytes < need)
       return fail(W8_E_WORKSPACE, "workspace of " + std::to_string(need) + " bytes needed, got " +
@@ -376,7 +420,7 @@ w8_status w8_workspace_size(w8_fmt fmt, w8_op op, int M, int N, int K, int packe
   } else {
     c = resolve_cfg(fmt, op, M, N, K, packed != 0, nullptr);
   }
-  *bytes = workspace_bytes(fmt, M, N, K, c);
+  *bytes = workspace_bytes(fmt, op, M, N, K, c);
   return ok();
 }
 
@@ -440,7 +484,7 @@ w8_status w8_linear(w8_fmt fmt, int M, int N, int K, const void* x, int64_t ldx,
   } else {
     c = resolve_cfg(fmt, W8_OP_LINEAR, M, N, K, packed, nullptr);
   }
-  const size_t need = workspace_bytes(fmt, M, N, K, c);
+  const size_t need = workspace_bytes(fmt, W8_OP_LINEAR, M, N, K, c);
   if (need > 0) {
     if (!ws || ws_bytes < need)
       return fail(W8_E_WORKSPACE, "workspace of " + std::to_string(need) + " bytes needed, got " +
@@ -451,7 +495,7 @@ w8_status w8_linear(w8_fmt fmt, int M, int N, int K, const void* x, int64_t ldx,
   if (st) return st;
   GemmCall g{fmt, M, N, K, nullptr, 0, nullptr, wq, ldw, sw, y, ldy, 0, ws, ws_bytes, packed,
              x, ldx};
-  st = launch_gemm_call(g, c, static_cast<hipStream_t>(stream));
+  st = launch_linear_call(g, c, static_cast<hipStream_t>(stream));
   if (st) return st;
   return ok();
 }

@@ -56,9 +56,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // The activation quantizer's per-element steps, shared by the standalone
 // quantize kernels and the GEMM's fused-quantization staging so both give
 // the same codes: amax of eight bf16 values (one 16-byte chunk), and eight
-// bf16 values -> eight codes with code = encode(x / s) (correctly rounded
-// fp32 division: the library is built with -fhip-fp32-correctly-rounded-
-// divide-sqrt and without fast-math).
+// bf16 values -> eight codes with code = encode(x / s).
 __device__ __forceinline__ float absmax8(v4u v) {
   float m = 0.0f;
 #pragma unroll
@@ -69,13 +67,46 @@ __device__ __forceinline__ float absmax8(v4u v) {
   return m;
 }
 
+// Scale of a group with absolute maximum amax (an all-zero group takes 1).
 template <bool INT8>
-__device__ __forceinline__ v2u encode8(v4u v, float s) {
+__device__ __forceinline__ float act_scale(float amax) {
+  return (amax == 0.0f) ? 1.0f : amax / (INT8 ? kQmaxInt8 : kQmaxE4M3);
+}
+
+// The quotient x / s is taken without a per-element division: with r the
+// correctly rounded reciprocal of s, q0 = x*r, the residual x - q0*s is
+// exact in one FMA, and q0 + residual*r is the correctly rounded quotient
+// whenever nothing underflows (Markstein's correction step).  Where x is
+// subnormal the two may differ in the last place, but for every scale
+// s >= 2^-100 and every bf16 x with |x| <= the amax behind s they give the
+// same E4M3FN and int8 code (checked exhaustively on the host).  Smaller
+// scales (act_recip returns 0) divide.  The sign is copied from x so a
+// negative zero keeps its code.  (The library is built without fast-math
+// and with -fhip-fp32-correctly-rounded-divide-sqrt, so 1/s and x/s are
+// correctly rounded.)
+__device__ __forceinline__ float act_recip(float s) { return s >= 0x1p-100f ? 1.0f / s : 0.0f; }
+
+__device__ __forceinline__ float act_quot(float x, float s, float r) {
+  const float q0 = x * r;
+  const float e = __builtin_fmaf(-q0, s, x);
+  return __builtin_copysignf(__builtin_fmaf(e, r, q0), x);
+}
+
+// Eight bf16 values -> eight codes; r = act_recip(s).
+template <bool INT8>
+__device__ __forceinline__ v2u encode8(v4u v, float s, float r) {
   float f[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    f[2 * i] = bf16_lo(v[i]) / s;
-    f[2 * i + 1] = bf16_hi(v[i]) / s;
+    f[2 * i] = bf16_lo(v[i]);
+    f[2 * i + 1] = bf16_hi(v[i]);
+  }
+  if (r != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = act_quot(f[i], s, r);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = f[i] / s;
   }
   v2u o;
   if (INT8) {
@@ -86,12 +117,6 @@ __device__ __forceinline__ v2u encode8(v4u v, float s) {
     o[1] = e4m3_pack4(f[4], f[5], f[6], f[7]);
   }
   return o;
-}
-
-// Scale of a group with absolute maximum amax (an all-zero group takes 1).
-template <bool INT8>
-__device__ __forceinline__ float act_scale(float amax) {
-  return (amax == 0.0f) ? 1.0f : amax / (INT8 ? kQmaxInt8 : kQmaxE4M3);
 }
 
 // ------------------------------------------------------------- reductions --

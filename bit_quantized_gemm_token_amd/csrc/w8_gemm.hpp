@@ -187,18 +187,11 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
   __shared__ int is_last;
 
   if constexpr (XL == 2 && !BLOCK) {
-    // Row scales over the whole of K, one wave per row (the standalone
-    // quantizer's rule, so the codes match it).
-    for (int m = wave; m < a.M; m += WK * WN) {
-      const uint16_t* xr = reinterpret_cast<const uint16_t*>(a.xq) + (long long)m * a.ldq;
-      float amax = 0.0f;
-      for (int c = lane; c < a.K / 8; c += 64)
-        amax = fmaxf(amax, absmax8(*reinterpret_cast<const v4u*>(xr + 8 * c)));
-      amax = wave_max(amax);
-      if (lane == 0) sxl[m] = act_scale<INT8>(amax);
-    }
+    // Row absolute maxima (float bits), folded in by the first segment.
+    if (threadIdx.x < 32) reinterpret_cast<unsigned*>(sxl)[threadIdx.x] = 0u;
     __syncthreads();
   }
+  bool rows_done = false;  // XL == 2, per-token formats: row scales computed
 
   const float* sxrow[MB][SXN];
   int sxm[MB][SXN];  // row of each accumulator element this lane holds (clamped)
@@ -214,7 +207,7 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
         ep_sx[b][i] = 0.0f;
       } else {
         sxrow[b][i] = nullptr;
-        ep_sx[b][i] = XL == 2 ? sxl[m] : a.sx[m];
+        ep_sx[b][i] = XL == 2 ? 0.0f : a.sx[m];  // XL == 2: set once the row scales exist
       }
     }
 
@@ -288,11 +281,12 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
         }
         if constexpr (BLOCK) {
           st.sw[u] = swrow[k];
+          if constexpr (XL != 2) {  // XL == 2: staged scales, read from LDS in run_stage
 #pragma unroll
-          for (int b = 0; b < MB; ++b)
+            for (int b = 0; b < MB; ++b)
 #pragma unroll
-            for (int i = 0; i < SXN; ++i)
-              st.sx[u][b][i] = XL == 2 ? sxl[(k - ka) * 32 + sxm[b][i]] : sxrow[b][i][k];
+              for (int i = 0; i < SXN; ++i) st.sx[u][b][i] = sxrow[b][i][k];
+          }
         }
       }
     };
@@ -335,7 +329,16 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
               x[b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
           }
-          step(w, x, st.sw[BLOCK ? u : 0], st.sx[BLOCK ? u : 0]);
+          if constexpr (XL == 2 && BLOCK) {
+            float sx[MB][SXN];
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+#pragma unroll
+              for (int i = 0; i < SXN; ++i) sx[b][i] = sxl[(k - ka) * 32 + sxm[b][i]];
+            step(w, x, st.sw[u], sx);
+          } else {
+            step(w, x, st.sw[BLOCK ? u : 0], st.sx[BLOCK ? u : 0]);
+          }
         } else {
           step(w, st.x[u], st.sw[BLOCK ? u : 0], st.sx[BLOCK ? u : 0]);
         }
@@ -343,45 +346,6 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
     };
     const std::true_type masked;
     const std::false_type whole;
-
-    // XL == 2: quantize the segment's activations into the LDS stage.  For
-    // Block_FP8 the group scales of the segment come first (16 lanes per
-    // (group, row), as in the standalone quantizer); the codes use the same
-    // encoder, so they equal the standalone quantizer's byte for byte.  The
-    // ragged K tail step is staged too, its bytes past K as zero codes.
-    if constexpr (XL == 2) {
-      if constexpr (BLOCK) {
-        const int units = (kb - ka) * a.M;  // (group, row), group-major
-        for (int base = 0; base < units; base += nthreads / 16) {
-          const int u = base + (int)(threadIdx.x >> 4), j = threadIdx.x & 15;
-          const bool act = u < units;
-          const int kk = act ? u / a.M : 0, m = act ? u % a.M : 0;
-          v4u v = v4u{0u, 0u, 0u, 0u};
-          if (act)
-            v = *reinterpret_cast<const v4u*>(reinterpret_cast<const uint16_t*>(a.xq) + (long long)m * a.ldq +
-                                              (long long)(ka + kk) * kGroup + 8 * j);
-          const float amax = seg16_max(absmax8(v));
-          if (act && j == 0) sxl[kk * 32 + m] = act_scale<false>(amax);
-        }
-        __syncthreads();
-      }
-      const int nunits = (kb - ka) * MB * CH * 64;  // (chunk, lane)
-      for (int u = threadIdx.x; u < nunits; u += nthreads) {
-        const int c = u >> 6, l = u & 63;
-        const int kk = c / (MB * CH), b = (c / CH) % MB, jj = c % CH;
-        const int row = min(16 * b + (l & 15), a.M - 1);
-        const int e = (ka + kk) * KSTEP + 64 * jj + 16 * (l >> 4);  // first element
-        v4u lo = v4u{0u, 0u, 0u, 0u}, hi = lo;
-        if (e < a.K) {  // (K % 16 == 0: the chunk is wholly inside K or past it)
-          const uint16_t* src = reinterpret_cast<const uint16_t*>(a.xq) + (long long)row * a.ldq + e;
-          lo = *reinterpret_cast<const v4u*>(src);
-          hi = *reinterpret_cast<const v4u*>(src + 8);
-        }
-        const float s = BLOCK ? sxl[kk * 32 + row] : sxl[row];
-        const v2u ql = encode8<INT8>(lo, s), qh = encode8<INT8>(hi, s);
-        xl[c * 64 + l] = v4i{(int)ql[0], (int)ql[1], (int)qh[0], (int)qh[1]};
-      }
-    }
 
     // XL == 1: every wave of the workgroup copies its share of the segment's
     // full K-steps [ka, min(kb, kfull)) of activations into LDS with
@@ -404,6 +368,119 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
     Stage A, B;
     if (ns > 0) load_stage(A, k0);
     if (ns > 1) load_stage(B, k0 + U);
+    // XL == 2: quantize the segment's activations into the LDS stage.  The
+    // raw bf16 slice is fetched while the first weight stages are in flight
+    // (and, for the per-token formats, together with the row pass), so one
+    // memory latency covers all of them.  Scales and codes follow the
+    // standalone quantizer (per-token formats: the row's absolute maximum
+    // over the whole of K, computed in the first segment; Block_FP8: each
+    // staged 1x128 group), with the same encoder, so the codes equal its
+    // codes byte for byte.  A unit is (K-step, row block, lane): the CH
+    // 16-byte chunks lane l of that MFMA operand reads; a wave's 64 units
+    // share one K-step and row block, so the four lanes l, l^16, l^32, l^48
+    // hold one row's whole K-step, a Block_FP8 group.  The ragged K tail step
+    // is staged too, its bytes past K as zero codes.
+    if constexpr (XL == 2) {
+      const uint16_t* xb = reinterpret_cast<const uint16_t*>(a.xq);
+      constexpr int QB = WK * WN >= 8 ? 1 : 2;  // units per thread per batch (registers)
+      const int nunits = (kb - ka) * MB * 64;
+      v4u raw[QB][CH][2];
+      auto fetch = [&](int u0) {
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+          const int u = u0 + q * nthreads;
+          const int kk = u / (MB * 64), b = (u >> 6) % MB;
+          const int row = min(16 * b + (lane & 15), a.M - 1);
+#pragma unroll
+          for (int jj = 0; jj < CH; ++jj) {
+            const int e = (ka + kk) * KSTEP + 64 * jj + 16 * (lane >> 4);  // first element
+            raw[q][jj][0] = raw[q][jj][1] = v4u{0u, 0u, 0u, 0u};
+            if (u < nunits && e < a.K) {  // (K % 16 == 0: a chunk is wholly inside K or past it)
+              const uint16_t* src = xb + (long long)row * a.ldq + e;
+              raw[q][jj][0] = *reinterpret_cast<const v4u*>(src);
+              raw[q][jj][1] = *reinterpret_cast<const v4u*>(src + 8);
+            }
+          }
+        }
+      };
+      auto put = [&](int u0) {
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+          const int u = u0 + q * nthreads;  // wave-uniform validity (nunits % 64 == 0)
+          const int kk = u / (MB * 64), b = (u >> 6) % MB;
+          const int row = min(16 * b + (lane & 15), a.M - 1);
+          float s;
+          if constexpr (BLOCK) {
+            float gm = 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < CH; ++jj)
+              gm = fmaxf(gm, fmaxf(absmax8(raw[q][jj][0]), absmax8(raw[q][jj][1])));
+            gm = fmaxf(gm, __shfl_xor(gm, 16, 64));
+            gm = fmaxf(gm, __shfl_xor(gm, 32, 64));
+            s = act_scale<false>(gm);
+            if (u < nunits && lane < 16 && 16 * b + lane < a.M) sxl[kk * 32 + 16 * b + lane] = s;
+          } else {
+            s = act_scale<INT8>(__uint_as_float(reinterpret_cast<const unsigned*>(sxl)[row]));
+          }
+          if (u < nunits) {
+            const float rs = act_recip(s);
+#pragma unroll
+            for (int jj = 0; jj < CH; ++jj) {
+              const v2u ql = encode8<INT8>(raw[q][jj][0], s, rs),
+                        qh = encode8<INT8>(raw[q][jj][1], s, rs);
+              xl[((kk * MB + b) * CH + jj) * 64 + lane] =
+                  v4i{(int)ql[0], (int)ql[1], (int)qh[0], (int)qh[1]};
+            }
+          }
+        }
+      };
+      fetch(threadIdx.x);
+      if constexpr (!BLOCK) {
+        if (!rows_done) {
+          // Row absolute maxima over the whole of K: each row is split over
+          // max(1, waves / M) waves, each lane keeps a running maximum of its
+          // chunks (two or four loads in flight), one wave reduction per (row,
+          // part), folded into the row's word (|x| >= 0: its float bits
+          // order as unsigned integers).
+          unsigned* amx = reinterpret_cast<unsigned*>(sxl);
+          const int nw = WK * WN;
+          const int wpr = max(1, nw / a.M);  // waves per row
+          const int cpr = a.K / 8;           // 16-byte chunks per row
+          const int step = 64 * wpr;
+          for (int slot = wave; slot < a.M * wpr; slot += nw) {
+            const int m = slot / wpr, part = slot - m * wpr;
+            const uint16_t* rowp = xb + (long long)m * a.ldq;
+            float mx = 0.0f;
+            constexpr int QA = WK * WN >= 8 ? 2 : 4;  // loads in flight per lane (registers)
+            for (int c0 = part * 64 + lane; c0 < cpr; c0 += QA * step) {
+              v4u v[QA];
+#pragma unroll
+              for (int q = 0; q < QA; ++q) {
+                const int c = c0 + q * step;
+                v[q] = v4u{0u, 0u, 0u, 0u};
+                if (c < cpr) v[q] = *reinterpret_cast<const v4u*>(rowp + 8 * c);
+              }
+#pragma unroll
+              for (int q = 0; q < QA; ++q) mx = fmaxf(mx, absmax8(v[q]));
+            }
+            mx = wave_max(mx);
+            if (lane == 0) atomicMax(&amx[m], __float_as_uint(mx));
+          }
+          __syncthreads();
+#pragma unroll
+          for (int b = 0; b < MB; ++b)
+#pragma unroll
+            for (int i = 0; i < SXN; ++i)
+              ep_sx[b][i] = act_scale<INT8>(__uint_as_float(amx[sxm[b][i]]));
+          rows_done = true;
+        }
+      }
+      put(threadIdx.x);
+      for (int u0 = threadIdx.x + QB * nthreads; u0 < nunits; u0 += QB * nthreads) {
+        fetch(u0);
+        put(u0);
+      }
+    }
     if constexpr (XL) {
       // the copies (and the first weight stages) have landed in every wave
       __builtin_amdgcn_s_waitcnt(0);

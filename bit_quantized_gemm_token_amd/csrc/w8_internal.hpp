@@ -22,7 +22,14 @@ w8_status check_gemm_shape(int fmt, int M, int N, int K);
 // Config checks (shape-independent and shape-dependent) for operation op.
 w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c);
 w8_cfg make_default_cfg(int fmt, int op, int M, int N, int K);
-size_t workspace_bytes(int fmt, int M, int N, int K, const w8_cfg& c);
+size_t workspace_bytes(int fmt, int op, int M, int N, int K, const w8_cfg& c);
+// Workspace regions of the linear op with quant_launch == 1 (byte offsets):
+// the GEMM's part at 0, the activation codes (row stride ldq) and scales.
+struct LinearWs {
+  size_t codes, scales, total;
+  long long ldq;
+};
+LinearWs linear_ws(int fmt, int M, int N, int K, const w8_cfg& c);
 int tiles_of(int N, const w8_cfg& c);                       // output tiles along N
 int partial_slots(int fmt, int N, int K, const w8_cfg& c);  // workspace slots per tile
 int ksteps_of(int fmt, int K);
@@ -53,6 +60,9 @@ struct GemmCall {
   long long ldx;
 };
 w8_status launch_gemm_call(const GemmCall& call, const w8_cfg& c, hipStream_t s);
+// The linear op (call.x set): the fused GEMM, or with c.quant_launch the
+// quantize kernel into the workspace and then the GEMM.
+w8_status launch_linear_call(const GemmCall& call, const w8_cfg& c, hipStream_t s);
 
 constexpr const char* kArch = "gfx950";
 

@@ -45,16 +45,17 @@ __global__ __launch_bounds__(kQuantThreads) void quant_token_kernel(QuantActArgs
   for (int w = 0; w < kQuantThreads / 64; ++w) amax = fmaxf(amax, red[w]);
 
   const float s = act_scale<INT8>(amax);
+  const float rs = act_recip(s);
   if (t == 0) a.sx[m] = s;
 
 #pragma unroll
   for (int i = 0; i < kRowCache; ++i) {
     const int c = t + i * kQuantThreads;
-    if (c < nch) *reinterpret_cast<v2u*>(qr + 8 * c) = encode8<INT8>(cache[i], s);
+    if (c < nch) *reinterpret_cast<v2u*>(qr + 8 * c) = encode8<INT8>(cache[i], s, rs);
   }
   for (int c = t + kRowCache * kQuantThreads; c < nch; c += kQuantThreads)
     *reinterpret_cast<v2u*>(qr + 8 * c) =
-        encode8<INT8>(*reinterpret_cast<const v4u*>(xr + 8 * c), s);
+        encode8<INT8>(*reinterpret_cast<const v4u*>(xr + 8 * c), s, rs);
 }
 
 // Per-group (1 x 128) E4M3FN quantization: 16 lanes per group, each lane one
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_group_kernel(QuantActArgs
   if (active) {
     if (j == 0) a.sx[(long long)m * G + g] = s;
     *reinterpret_cast<v2u*>(a.xq + (long long)m * a.ldq + g * kGroup + 8 * j) =
-        encode8<false>(v, s);
+        encode8<false>(v, s, act_recip(s));
   }
 }
 

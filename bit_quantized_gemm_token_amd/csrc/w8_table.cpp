@@ -91,8 +91,8 @@ w8_status parse_table(const std::string& text, std::map<Key, Entry>* native,
       foreign->push_back(line);
       continue;
     }
-    if (tok.size() != 17)
-      return fail(W8_E_TABLE_FORMAT, where + "expected 17 fields, got " + std::to_string(tok.size()));
+    if (tok.size() != 18)
+      return fail(W8_E_TABLE_FORMAT, where + "expected 18 fields, got " + std::to_string(tok.size()));
     const int fmt = fmt_from_name(tok[2]);
     if (fmt < 0) return fail(W8_E_TABLE_FORMAT, where + "unknown format '" + tok[2] + "'");
     int op = -1;
@@ -103,12 +103,12 @@ w8_status parse_table(const std::string& text, std::map<Key, Entry>* native,
     if (tok[4] == "row") packed = 0;
     if (tok[4] == "packed") packed = 1;
     if (packed < 0) return fail(W8_E_TABLE_FORMAT, where + "layout must be row or packed");
-    int v[11];  // M N K tile_n waves_k waves_n unroll split_k grid swap_ab x_lds
-    for (int i = 0; i < 11; ++i)
+    int v[12];  // M N K tile_n waves_k waves_n unroll split_k grid swap_ab x_lds quant_launch
+    for (int i = 0; i < 12; ++i)
       if (!parse_int(tok[5 + i], &v[i]))
         return fail(W8_E_TABLE_FORMAT, where + "bad integer '" + tok[5 + i] + "'");
     double us = 0;
-    if (!parse_double(tok[16], &us)) return fail(W8_E_TABLE_FORMAT, where + "bad time field");
+    if (!parse_double(tok[17], &us)) return fail(W8_E_TABLE_FORMAT, where + "bad time field");
     w8_cfg c;
     std::memset(&c, 0, sizeof c);
     c.abi_version = abi;
@@ -120,6 +120,7 @@ w8_status parse_table(const std::string& text, std::map<Key, Entry>* native,
     c.grid = v[8];
     c.swap_ab = v[9];
     c.x_lds = v[10];
+    c.quant_launch = v[11];
     if (check_gemm_shape(fmt, v[0], v[1], v[2]) != W8_OK ||
         check_cfg(fmt, op, v[0], v[1], v[2], c) != W8_OK)
       return fail(W8_E_TABLE_FORMAT, where + "invalid entry (" + std::string(w8_last_error()) + ")");
@@ -205,17 +206,17 @@ w8_status w8_save_config_table(const char* path) {
     maybe_load_env(t);
     out << "# w8gemm per-shape config table\n"
         << "# arch abi fmt op layout M N K tile_n waves_k waves_n unroll split_k grid swap_ab "
-           "x_lds us_per_call\n";
+           "x_lds quant_launch us_per_call\n";
     for (const auto& kv : t.native) {
       const Entry& e = kv.second;
       char buf[256];
-      std::snprintf(buf, sizeof buf, "%s %d %s %s %s %d %d %d %d %d %d %d %d %d %d %d %.4f\n",
+      std::snprintf(buf, sizeof buf, "%s %d %s %s %s %d %d %d %d %d %d %d %d %d %d %d %d %.4f\n",
                     kArch, W8_ABI_VERSION, fmt_name(std::get<0>(kv.first)),
                     op_name(std::get<1>(kv.first)), layout_name(std::get<2>(kv.first)),
                     std::get<3>(kv.first), std::get<4>(kv.first), std::get<5>(kv.first),
                     e.cfg.tile_n, e.cfg.waves_k,
                     e.cfg.waves_n, e.cfg.unroll, e.cfg.split_k, e.cfg.grid, e.cfg.swap_ab,
-                    e.cfg.x_lds, e.us);
+                    e.cfg.x_lds, e.cfg.quant_launch, e.us);
       out << buf;
     }
     for (const auto& l : t.foreign) out << l << "\n";

@@ -167,7 +167,8 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   const size_t nsx = block ? (size_t)M * G : (size_t)M;
   const size_t nsw = block ? (size_t)((N + 127) / 128) * G : (size_t)N;
 
-  // Candidates: every config of the family -- (waves_k, waves_n, x_lds) in
+  // Candidates: every config of the family valid for the op -- (waves_k,
+  // waves_n, x_lds) in
   // {(1..16, 1, 0), (1..8, 1, 1), (1, 2..8, 1)}, each with split_k up to
   // max_split_k or (opts.stream_k) with a
   // stream-K grid of 256, 512 or 1024 workgroups (1, 2 or 4 per compute
@@ -200,7 +201,7 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
                                           : (long long)T / (c.split_k * c.waves_k);
     if (per_wave < 1) return;
     if (c.unroll > 1 && per_wave < c.unroll) return;
-    if (workspace_bytes(fmt, M, N, K, c) > 2 * wbytes + ws_counter_bytes(0)) return;
+    if (workspace_bytes(fmt, op, M, N, K, c) > 2 * wbytes + ws_counter_bytes(0)) return;
     all.push_back(c);
     most_waves = std::max(most_waves, total_waves(c));
   };
@@ -230,19 +231,38 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
           }
         }
   const long long min_waves = std::min<long long>(256, most_waves);
-  size_t max_ws = 0;
   for (const w8_cfg& c : all) {
     if (total_waves(c) < min_waves) continue;
-    max_ws = std::max(max_ws, workspace_bytes(fmt, M, N, K, c));
     Cand cd;
     cd.cfg = c;
     cd.index = (int)cands.size();
     cands.push_back(cd);
   }
+  // The linear op also competes with a quantize launch of its own followed
+  // by the GEMM: with the GEMM's table entry for this shape and layout (tune
+  // the GEMM first) and with the GEMM's default config.
+  if (op == W8_OP_LINEAR) {
+    int hit = 0;
+    std::vector<w8_cfg> gemm_cfgs = {resolve_cfg(fmt, W8_OP_GEMM, M, N, K, packed, &hit)};
+    if (hit) gemm_cfgs.push_back(make_default_cfg(fmt, W8_OP_GEMM, M, N, K));
+    for (w8_cfg c : gemm_cfgs) {
+      c.quant_launch = 1;
+      if (check_cfg(fmt, op, M, N, K, c) != W8_OK) continue;
+      bool dup = false;
+      for (const Cand& e : cands) dup = dup || std::memcmp(&e.cfg, &c, sizeof c) == 0;
+      if (dup) continue;
+      Cand cd;
+      cd.cfg = c;
+      cd.index = (int)cands.size();
+      cands.push_back(cd);
+    }
+  }
+  size_t max_ws = 0;
+  for (const Cand& cd : cands) max_ws = std::max(max_ws, workspace_bytes(fmt, op, M, N, K, cd.cfg));
   const w8_cfg dflt = make_default_cfg(fmt, W8_OP_GEMM, M, N, K);     // reference
   const w8_cfg dflt_op = make_default_cfg(fmt, op, M, N, K);          // reported baseline
-  max_ws = std::max(max_ws, workspace_bytes(fmt, M, N, K, dflt));
-  max_ws = std::max(max_ws, workspace_bytes(fmt, M, N, K, dflt_op));
+  max_ws = std::max(max_ws, workspace_bytes(fmt, W8_OP_GEMM, M, N, K, dflt));
+  max_ws = std::max(max_ws, workspace_bytes(fmt, op, M, N, K, dflt_op));
 
   Buffers b;
   hipStream_t stream = nullptr;
@@ -313,8 +333,11 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   float ref_max = 0.0f;
   for (uint16_t v : yref) ref_max = std::max(ref_max, std::fabs(bf16_to_float(v)));
 
+  auto launch = [&](const GemmCall& g, const w8_cfg& c) {
+    return op == W8_OP_LINEAR ? launch_linear_call(g, c, stream) : launch_gemm_call(g, c, stream);
+  };
   auto validate = [&](const w8_cfg& c, bool* good) -> w8_status {
-    w8_status s2 = launch_gemm_call(call, c, stream);
+    w8_status s2 = launch(call, c);
     if (s2) return s2;
     TRY_HIP(hipStreamSynchronize(stream));
     TRY_HIP(hipMemcpy(ycur.data(), b.y, ycur.size() * 2, hipMemcpyDeviceToHost));
@@ -342,7 +365,7 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
     for (size_t r = 0; r < R && s2 == W8_OK; ++r) {
       GemmCall cr = call;
       cr.wq = b.wpool + r * wbytes;
-      s2 = launch_gemm_call(cr, c, stream);
+      s2 = launch(cr, c);
     }
     hipError_t e = hipStreamEndCapture(stream, &graph);
     if (s2) {

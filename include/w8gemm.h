@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define W8_ABI_VERSION 2
+#define W8_ABI_VERSION 3
 #define W8_MAX_M 32         /* token-count window of the tuned path (paragraph 4) */
 #define W8_MAX_SPLIT_K 256  /* split_k is a power of two up to 256 (paragraph 3) */
 #define W8_GROUP 128        /* Block_FP8 group / block edge */
@@ -122,6 +122,12 @@ typedef enum {
  *            most tiles x K-steps.
  *   swap_ab  0: MFMA A operand = activations, B = weights^T.
  *            1: Swap-AB, Y^T = Wq . Xq^T: A = weights, B = activations^T.
+ *   quant_launch  W8_OP_LINEAR only (0 for W8_OP_GEMM).  0: the activations
+ *            are quantized inside the GEMM (needs x_lds == 1 and
+ *            waves_k <= 4).  1: they are quantized by a launch of their own
+ *            (w8_quantize_act's kernel) into the workspace, and the GEMM
+ *            runs with this config under the W8_OP_GEMM rules.  The tuner
+ *            tries both for the linear op and keeps the faster.
  * Set abi_version to W8_ABI_VERSION and reserved[] to 0.  The weight layout
  * (row-major or packed, below) is a property of the weight buffer, not of
  * the config: it is given by the ldw argument of the GEMM.                 */
@@ -135,7 +141,8 @@ typedef struct {
     int32_t grid;
     int32_t swap_ab;
     int32_t x_lds;
-    int32_t reserved[2];
+    int32_t quant_launch;
+    int32_t reserved[1];
 } w8_cfg;
 
 /* Options of the ahead-of-time tuner (paragraph 3 and 6 of the page). */
@@ -219,11 +226,15 @@ w8_status w8_pack_weight(w8_fmt fmt, int N, int K, const void *wq, int64_t ldw, 
 
 /* Bytes of device workspace operation op needs for (fmt, M, N, K) under cfg
  * (cfg NULL: the config w8_resolve_config picks for op and that weight
- * layout; packed = 1 for packed weights).  0 when no tile is shared between
- * workgroups (split_k == 1 and grid == 0).
- * Layout: a fixed 2 MiB region of arrival counters, then the partials of
- * shared tiles; split_k > 1 and grid > 0 therefore support at most 16384
- * output tiles (N <= 16384 * tile_n * waves_n).                             */
+ * layout; packed = 1 for packed weights).  The GEMM needs none when no tile
+ * is shared between workgroups (split_k == 1 and grid == 0); otherwise a
+ * fixed 2 MiB region of arrival counters, then the partials of shared
+ * tiles, so split_k > 1 and grid > 0 support at most 16384 output tiles
+ * (N <= 16384 * tile_n * waves_n).  The linear op with quant_launch == 1
+ * adds, after the GEMM's part and never below the 2 MiB counter region (so a
+ * workspace shared by any sequence of calls keeps its counters at zero),
+ * the codes (M rows of K rounded up to 16 bytes) and the scales of the
+ * activations, each region 256-byte aligned.                               */
 w8_status w8_workspace_size(w8_fmt fmt, w8_op op, int M, int N, int K, int packed,
                             const w8_cfg *cfg, size_t *bytes);
 
@@ -261,18 +272,21 @@ w8_status w8_gemm_w8a8_acc(w8_fmt fmt, int M, int N, int K,
                            void *acc, int64_t ldacc, const w8_cfg *cfg,
                            void *ws, size_t ws_bytes, w8_stream stream);
 
-/* The whole linear layer in one kernel launch: activation quantization
- * (the w8_quantize_act rules, giving the same codes and scales) fused into
- * the GEMM.  Each workgroup quantizes the activations of its K range into
- * LDS: per 1x128 group for Block_FP8; per token for the other formats,
- * after a pass over the whole row for its absolute maximum.  Y equals
- * w8_quantize_act followed by w8_gemm_w8a8 with the same cfg, bit for bit.
+/* The whole linear layer on bf16 activations.  With quant_launch == 0, one
+ * kernel launch: activation quantization (the w8_quantize_act rules, giving
+ * the same codes and scales) fused into the GEMM.  Each workgroup quantizes
+ * the activations of its K range into LDS: per 1x128 group for Block_FP8;
+ * per token for the other formats, after a pass over the whole row for its
+ * absolute maximum.  Either way Y equals w8_quantize_act followed by
+ * w8_gemm_w8a8 with the same tile config, bit for bit.
  *   x       bf16 [M, K], row stride ldx elements (device), 16-byte aligned,
  *           ldx % 8 == 0
  *   wq, sw, y, ws, stream  as for w8_gemm_w8a8
- *   cfg     needs x_lds == 1 and waves_k <= 4; NULL = the table entry for
- *           (fmt, W8_OP_LINEAR, weight layout, M, N, K), else the default
- *           linear config (w8_default_config with W8_OP_LINEAR).          */
+ *   cfg     NULL = the table entry for (fmt, W8_OP_LINEAR, weight layout,
+ *           M, N, K), else the default linear config (w8_default_config
+ *           with W8_OP_LINEAR).  With quant_launch == 1 the call makes two
+ *           launches instead: w8_quantize_act's kernel into the workspace,
+ *           then the GEMM (same Y).  Both forms allocate nothing.          */
 w8_status w8_linear(w8_fmt fmt, int M, int N, int K, const void *x, int64_t ldx,
                     const void *wq, int64_t ldw, const float *sw,
                     void *y, int64_t ldy, const w8_cfg *cfg,
@@ -298,7 +312,7 @@ w8_status w8_resolve_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packe
 /* Per-shape config table (paragraphs 6-7 of the page).  Text format, one entry
  * per line:
  *   arch abi fmt op layout M N K tile_n waves_k waves_n unroll split_k grid
- *   swap_ab x_lds us_per_call
+ *   swap_ab x_lds quant_launch us_per_call
  * with op "gemm" or "linear" and layout "row" or "packed"; '#' starts a
  * comment.  Entries whose arch or
  * abi differ from this build and device are kept in the file but never used.

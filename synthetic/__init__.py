@@ -79,3 +79,23 @@ SWEEP = (
     (1, 5120, 2048), (8, 5120, 2048),
     (1, 5120, 8192), (8, 5120, 8192),
 )
+
+
+def activations_extreme(fmt: str, M: int, K: int) -> np.ndarray:
+    """bf16 X [M, K] whose rows span the magnitudes an activation quantizer
+    meets at the edges of bf16: row r is N(0, 1) scaled by 2^e with e cycling
+    through -124, -96, -90, -86, 0, 60, 120, and every third row (from row 1) has a
+    quarter of its entries replaced by subnormal bf16 values (down to 2^-133)
+    and an eighth by negative zeros."""
+    g = rng(fmt, M, 0, K, "x_extreme")
+    exps = (-124, -96, -90, -86, 0, 60, 120)
+    x = g.standard_normal((M, K)).astype(np.float64)
+    for r in range(M):
+        x[r] *= 2.0 ** exps[r % len(exps)]
+        if r % 3 == 1:
+            idx = g.permutation(K)
+            sub = idx[:K // 4]
+            x[r, sub] = g.uniform(-1, 1, len(sub)) * 2.0 ** -126
+            x[r, idx[K // 4:K // 4 + K // 8]] = -0.0
+    bits = fp32_to_bf16_bits(x.astype(np.float32))
+    return bits

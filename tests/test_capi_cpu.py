@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_and_status_strings(lib):
-    assert lib.w8_abi_version() == 2
+    assert lib.w8_abi_version() == 3
     assert lib.w8_status_string(2) == b"W8_E_UNSUPPORTED"
     assert lib.w8_status_string(99) == b"W8_E_UNKNOWN"
 
@@ -87,7 +87,7 @@ def test_config_rejects_abi_and_reserved(w8):
     cfg.abi_version = 1
     assert not _valid(w8, "FP8_Dynamic", 4, 512, 1024, cfg)
     cfg = w8.Config.make()
-    cfg.reserved[1] = 7
+    cfg.reserved[0] = 7
     assert not _valid(w8, "FP8_Dynamic", 4, 512, 1024, cfg)
     cfg = w8.Config.make(tile_n=64, unroll=2)    # 4 row blocks x unroll 2 > 4 registers sets
     assert not _valid(w8, "FP8_Dynamic", 4, 512, 1024, cfg)
@@ -188,6 +188,36 @@ def test_linear_config_rules(w8):
         w8.validate_config("FP8_Dynamic", 4, 512, 1024, ok, op="fused")
 
 
+def test_quant_launch_rules_and_workspace(w8):
+    """quant_launch = 1: the linear op quantizes in a launch of its own into
+    the workspace and runs the GEMM under the GEMM's rules."""
+    g = w8.Config.make(waves_k=8, split_k=4)                         # a GEMM config, no x_lds
+    ql = w8.Config.make(waves_k=8, split_k=4, quant_launch=1)
+    assert not _valid_op(w8, "FP8_Dynamic", 4, 512, 1024, g, "linear")
+    assert _valid_op(w8, "FP8_Dynamic", 4, 512, 1024, ql, "linear")
+    assert not _valid_op(w8, "FP8_Dynamic", 4, 512, 1024, ql, "gemm")  # linear only
+    bad = w8.Config.make(waves_k=8, quant_launch=2)
+    assert not _valid_op(w8, "FP8_Dynamic", 4, 512, 1024, bad, "linear")
+    assert not _valid_op(w8, "FP8_Dynamic", 4, 512, 1024,
+                         w8.Config.make(waves_k=16, x_lds=1, quant_launch=1), "linear")
+
+    def r256(b):
+        return (b + 255) // 256 * 256
+
+    for fmt, M, N, K in (("FP8_Dynamic", 4, 512, 1024), ("Block_FP8", 17, 300, 1152),
+                         ("W8A8_INT8", 32, 64, 208)):
+        gemm_ws = w8.workspace_size(fmt, M, N, K, g)
+        nsx = M * (K // 128) if fmt == "Block_FP8" else M
+        assert gemm_ws > COUNTERS
+        want = r256(gemm_ws) + r256(M * ((K + 15) // 16 * 16)) + r256(4 * nsx)
+        assert w8.workspace_size(fmt, M, N, K, ql, op="linear") == want
+        # no shared tiles: the codes still start past the counter region
+        one = w8.Config.make(waves_k=8, quant_launch=1)
+        assert w8.workspace_size(fmt, M, N, K, one, op="linear") == \
+            COUNTERS + r256(M * ((K + 15) // 16 * 16)) + r256(4 * nsx)
+        assert w8.workspace_size(fmt, M, N, K, w8.Config.make(waves_k=8)) == 0
+
+
 FAKE = ctypes.c_void_p(0x100000)   # 16-byte aligned, never dereferenced
 COUNTERS = 16384 * 128              # workspace arrival-counter region
 
@@ -259,6 +289,11 @@ def test_linear_argument_errors(w8, lib):
     sk = w8.Config.make(waves_k=4, x_lds=1, split_k=2)
     assert L(0, 4, 64, 256, FAKE, 256, FAKE, 256, FAKE, FAKE, 64, ctypes.byref(sk), None, 0,
              None) == 3                                              # workspace missing
+    ql = w8.Config.make(waves_k=4, quant_launch=1)                    # codes live in the workspace
+    assert L(0, 4, 64, 256, FAKE, 256, FAKE, 256, FAKE, FAKE, 64, ctypes.byref(ql), None, 0,
+             None) == 3
+    assert L(0, 4, 64, 256, FAKE, 256, FAKE, 256, FAKE, FAKE, 64, ctypes.byref(ql), FAKE,
+             COUNTERS + 1279, None) == 3                             # counters, codes, scales - 1
 
 
 def test_quantize_argument_errors(lib):
@@ -319,21 +354,23 @@ def test_table_roundtrip_and_lookup(w8, tmp_path):
 def test_table_malformed_keeps_old_table(w8, tmp_path):
     w8.set_config("W8A8_INT8", 16, 896, 1024, w8.Config.make(), 1.0)
     bad_files = [
-        "gfx950 2 W8A8_INT8 row 16 896 1024 16 4 1 2 1 0\n",                # too few fields
-        "gfx950 2 INT4 gemm row 16 896 1024 16 4 1 2 1 0 0 0 1.0\n",               # unknown format
-        "gfx950 2 W8A8_INT8 gemm tiled 16 896 1024 16 4 1 2 1 0 0 0 1.0\n",        # unknown layout
-        "gfx950 2 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 3 0 0 0 1.0\n",          # split_k 3
-        "gfx950 2 W8A8_INT8 gemm row 40 896 1024 16 4 1 2 1 0 0 0 1.0\n",          # M above 32
-        "gfx950 2 W8A8_INT8 gemm row 16 896 1024 16 4 1 x 1 0 0 0 1.0\n",          # not an integer
-        "gfx950 2 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 fast\n",         # bad time
-        "gfx950 2 W8A8_INT8 gemm row 16 896 1024 64 4 1 2 1 0 0 0 1.0\n",          # tile 64 x unroll 2
-        "gfx950 2 W8A8_INT8 gemm row 16 896 1024 16 2 2 2 1 0 0 0 1.0\n",          # waves_k and waves_n
-        "gfx950 2 W8A8_INT8 gemm row 16 896 1024 16 1 1 2 2 256 0 0 1.0\n",        # grid with split_k
-        "gfx950 2 W8A8_INT8 gemm row 16 896 1024 16 1 1 2 1 100000 0 0 1.0\n",     # grid > iterations
-        "gfx950 2 W8A8_INT8 gemm row 16 896 1024 16 16 1 2 1 0 0 1 1.0\n",        # x_lds, 16 waves
-        "gfx950 2 W8A8_INT8 fused row 16 896 1024 16 4 1 2 1 0 0 1 1.0\n",       # unknown op
-        "gfx950 2 W8A8_INT8 linear row 16 896 1024 16 4 1 2 1 0 0 0 1.0\n",      # linear without x_lds
-        "gfx950 2 W8A8_INT8 linear row 16 896 1024 16 8 1 2 1 0 0 1 1.0\n",      # linear, 8 waves_k
+        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 1.0\n",          # too few fields
+        "gfx950 3 INT4 gemm row 16 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",               # unknown format
+        "gfx950 3 W8A8_INT8 gemm tiled 16 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",        # unknown layout
+        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 3 0 0 0 0 1.0\n",          # split_k 3
+        "gfx950 3 W8A8_INT8 gemm row 40 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",          # M above 32
+        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 4 1 x 1 0 0 0 0 1.0\n",          # not an integer
+        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 0 fast\n",         # bad time
+        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 64 4 1 2 1 0 0 0 0 1.0\n",          # tile 64 x unroll 2
+        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 2 2 2 1 0 0 0 0 1.0\n",          # waves_k and waves_n
+        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 1 1 2 2 256 0 0 0 1.0\n",        # grid with split_k
+        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 1 1 2 1 100000 0 0 0 1.0\n",     # grid > iterations
+        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 16 1 2 1 0 0 1 0 1.0\n",        # x_lds, 16 waves
+        "gfx950 3 W8A8_INT8 fused row 16 896 1024 16 4 1 2 1 0 0 1 0 1.0\n",       # unknown op
+        "gfx950 3 W8A8_INT8 linear row 16 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",      # linear without x_lds
+        "gfx950 3 W8A8_INT8 linear row 16 896 1024 16 8 1 2 1 0 0 1 0 1.0\n",      # linear, 8 waves_k
+        "gfx950 3 W8A8_INT8 linear row 16 896 1024 16 8 1 2 1 0 0 1 2 1.0\n",      # quant_launch 2
+        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 1 1.0\n",        # gemm, quant_launch
     ]
     for i, text in enumerate(bad_files):
         p = tmp_path / f"bad{i}.tbl"
@@ -352,9 +389,10 @@ def test_table_foreign_entries_ignored_and_kept(w8, tmp_path):
     p.write_text("gfx942 2 FP8_Dynamic gemm row 4 4096 4096 64 2 1 4 1 0 1 0 2.0\n"
                  "gfx950 9 FP8_Dynamic row 4 4096 4096 64 2 1 4 1 0 1 2.0\n"
                  "gfx950 1 FP8_Dynamic row 4 4096 4096 32 2 2 4 0 2.5\n"
-                 "gfx950 2 FP8_Dynamic gemm row 4 4096 4096 32 2 1 2 4 0 0 0 2.5  # native\n")
+                 "gfx950 2 FP8_Dynamic gemm row 4 4096 4096 32 2 1 2 4 0 0 0 2.5\n"
+                 "gfx950 3 FP8_Dynamic gemm row 4 4096 4096 32 2 1 2 4 0 0 0 0 2.5  # native\n")
     w8.load_config_table(str(p))
-    assert w8.config_table_size() == 1 and w8.config_table_foreign() == 3
+    assert w8.config_table_size() == 1 and w8.config_table_foreign() == 4
     assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096) == \
         w8.Config.make(tile_n=32, waves_k=2, unroll=2, split_k=4, swap_ab=0)
     q = tmp_path / "out.tbl"
@@ -366,7 +404,7 @@ def test_table_foreign_entries_ignored_and_kept(w8, tmp_path):
 
 def test_table_from_environment(tmp_path):
     p = tmp_path / "env.tbl"
-    p.write_text("gfx950 2 W8A8_INT8 gemm row 16 896 1024 32 2 1 2 8 0 1 0 0.5\n")
+    p.write_text("gfx950 3 W8A8_INT8 gemm row 16 896 1024 32 2 1 2 8 0 1 0 0 0.5\n")
     code = ("import bit_quantized_gemm_token_amd as w8;"
             "c = w8.lookup_config('W8A8_INT8', 16, 896, 1024);"
             "print(c.as_dict() if c else None)")
@@ -382,7 +420,7 @@ def test_table_from_environment(tmp_path):
 
 def test_env_table_loaded_by_the_c_library_alone(tmp_path):
     p = tmp_path / "env.tbl"
-    p.write_text("gfx950 2 W8A8_INT8 gemm row 16 896 1024 32 2 1 2 8 0 1 0 0.5\n")
+    p.write_text("gfx950 3 W8A8_INT8 gemm row 16 896 1024 32 2 1 2 8 0 1 0 0 0.5\n")
     from bit_quantized_gemm_token_amd import _capi
     # load _capi.py on its own (the package __init__ would load the shipped table)
     code = (

@@ -131,6 +131,26 @@ def test_fused_zero_rows(w8, fmt):
     assert (y1[3].float() == 0).all()
 
 
+@pytest.mark.parametrize("fmt", ["W8A8_INT8", "FP8_Dynamic", "Block_FP8"])
+def test_fused_extreme_magnitudes(w8, fmt):
+    """Rows scaled by 2^-124 .. 2^120 with subnormal entries and negative
+    zeros: the staged codes and scales equal the standalone quantizer's (its
+    own parity with the oracle on these rows is a quantizer test), so Y is
+    bit-identical to the two-launch path."""
+    import synthetic
+    from tests.gpu_cases import to_bf16_tensor
+    M, N, K = 14, 272, 1024
+    cs = case(fmt, M, N, K)
+    x = to_bf16_tensor(synthetic.activations_extreme(fmt, M, K))
+    for cfg in (w8.Config.make(tile_n=16, waves_k=2, unroll=2, split_k=2, x_lds=1),
+                w8.Config.make(tile_n=32, waves_k=1, waves_n=4, unroll=1, x_lds=1)):
+        y1 = fused(w8, cs, cfg, True, x=x)
+        xq, sx = w8.quantize_act(fmt, x)
+        y2 = w8.gemm_w8a8(fmt, xq, sx, cs.weights(True), cs.sw, cfg=cfg)
+        torch.cuda.synchronize()
+        assert same_bits(y1, y2), f"{fmt} {cfg}"
+
+
 def test_fused_graph_replay(w8):
     cs = case("FP8_Dynamic", 4, 4096, 4096)
     cfg = w8.Config.make(tile_n=16, waves_k=4, unroll=2, split_k=8, x_lds=1)
@@ -159,6 +179,79 @@ def test_fused_graph_replay(w8):
         junk = torch.randn(512, 512, device=DEV) @ torch.randn(512, 512, device=DEV)
         del junk
     assert_bf16_close(y_static, cs.Y, "fused graph replay")
+
+
+QL_CFGS = (dict(tile_n=16, waves_k=4, unroll=2, split_k=1),
+           dict(tile_n=32, waves_k=16, unroll=1, split_k=8),
+           dict(tile_n=16, waves_k=1, waves_n=8, unroll=1, split_k=4, x_lds=1),
+           dict(tile_n=64, waves_k=2, unroll=1, split_k=1, swap_ab=1),
+           dict(tile_n=16, waves_k=2, unroll=2, grid=300))
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [("W8A8_INT8", 7, 300, 1040), ("FP8_Dynamic", 32, 1000, 2048),
+                                       ("Block_FP8", 17, 520, 1152), ("FP8_Dynamic", 1, 64, 16)])
+def test_quant_launch(w8, fmt, M, N, K):
+    """quant_launch = 1: w8_linear quantizes in a launch of its own into the
+    workspace, then runs the GEMM with the config's GEMM part: Y bit for bit
+    the two-call path's, both layouts, split-K, stream-K and x_lds 0/1."""
+    cs = case(fmt, M, N, K)
+    for kw in QL_CFGS:
+        if kw.get("grid", 0) > (N + 15) // 16 * ((K + 127) // 128):
+            continue
+        g = w8.Config.make(**kw)
+        q = w8.Config.make(quant_launch=1, **kw)
+        for packed in (False, True):
+            y1 = fused(w8, cs, q, packed)
+            y2 = two_launch(w8, cs, g, packed)
+            torch.cuda.synchronize()
+            assert same_bits(y1, y2), f"{fmt} {kw} packed={packed}"
+    assert_bf16_close(y1, cs.Y, f"quant_launch {fmt}")
+
+
+def test_quant_launch_shares_workspace_with_split_k(w8):
+    """A workspace used by a quant_launch call and by split-K GEMMs in turn:
+    the codes never land on the arrival counters, so every call stays right,
+    also under graph replay."""
+    fmt, M, N, K = "FP8_Dynamic", 8, 4096, 4096
+    cs = case(fmt, M, N, K)
+    wp = cs.packed()
+    q = w8.Config.make(tile_n=16, waves_k=4, unroll=2, quant_launch=1)            # no split
+    sk = w8.Config.make(tile_n=16, waves_k=4, unroll=2, split_k=16)
+    qsk = w8.Config.make(tile_n=16, waves_k=4, unroll=2, split_k=16, quant_launch=1)
+    ws = w8.Workspace(DEV, max(w8.workspace_size(fmt, M, N, K, c, packed=True, op=op)
+                               for c, op in ((q, "linear"), (sk, "gemm"), (qsk, "linear"))))
+    xq, sx = w8.quantize_act(fmt, cs.x)
+    ref = w8.gemm_w8a8(fmt, xq, sx, wp, cs.sw, cfg=sk, workspace=ws).clone()
+    x_static = cs.x.clone()
+    y = [torch.empty_like(ref) for _ in range(3)]
+
+    def calls():
+        w8.linear(fmt, x_static, wp, cs.sw, cfg=q, y=y[0], workspace=ws, fused=True)
+        w8.gemm_w8a8(fmt, xq, sx, wp, cs.sw, cfg=sk, y=y[1], workspace=ws)
+        w8.linear(fmt, x_static, wp, cs.sw, cfg=qsk, y=y[2], workspace=ws, fused=True)
+
+    for _ in range(3):
+        calls()
+        torch.cuda.synchronize()
+        for t in y:
+            assert same_bits(t, ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for i in range(4):
+        for t in y:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for t in y:
+            assert same_bits(t, ref), f"replay {i}"
+    assert_bf16_close(ref, cs.Y, "shared workspace")
 
 
 def test_fused_rejects_gemm_config(w8):

@@ -56,6 +56,15 @@ def test_quantize_act_zero_rows_and_groups(w8, fmt):
     _act_case(w8, fmt, 6, 512, bits)
 
 
+@pytest.mark.parametrize("fmt", ["FP8_Dynamic", "W8A8_INT8", "Block_FP8"])
+def test_quantize_act_extreme_magnitudes(w8, fmt):
+    """Rows scaled by 2^-124 .. 2^120, with subnormal entries and negative
+    zeros: scales below 2^-100 (divided), just above it (reciprocal with an
+    FMA correction, subnormal x), and near the top of the bf16 range."""
+    M, K = 21, 1024
+    _act_case(w8, fmt, M, K, synthetic.activations_extreme(fmt, M, K))
+
+
 def test_int8_round_ties(w8):
     # amax 127 gives s = 1, so x / s = x: every k + 0.5 is an exact tie
     vals = np.concatenate([[127.0], np.arange(-126.5, 127.0, 1.0), [-0.0, 0.5, -0.5]])

@@ -59,6 +59,27 @@ def test_tune_shape(w8, fmt, M, N, K, packed, stream_k, op, tmp_path):
     assert_bf16_close(y, cs.Y, f"tuned {op} {fmt}")
 
 
+def test_tune_linear_picks_quant_launch_where_it_wins(w8):
+    """Per-token FP8 at M = 32, K = 7168: every workgroup of the fused kernel
+    reads all 32 x 7168 bf16 activations for the row maxima, so a quantize
+    launch of its own plus the tuned GEMM is about twice as fast; the linear
+    tuner, run after the GEMM's, must pick it, and w8_linear must run it."""
+    fmt, M, N, K = "FP8_Dynamic", 32, 512, 7168
+    w8.clear_config_table()
+    g, _ = w8.tune_shape(fmt, M, N, K, packed=True, op="gemm", **SMALL)
+    best, st = w8.tune_shape(fmt, M, N, K, packed=True, op="linear", **SMALL)
+    print(f"[tune] linear best {best} stats {st}", flush=True)
+    assert best.quant_launch == 1
+    gq = w8.Config.make(**{k: v for k, v in g.as_dict().items() if k != "quant_launch"},
+                        quant_launch=1)
+    assert best in (gq, w8.Config.make(**{k: v for k, v in w8.default_config(
+        fmt, M, N, K).as_dict().items() if k != "quant_launch"}, quant_launch=1))
+    cs = Case(fmt, M, N, K)
+    y = w8.linear(fmt, cs.x, cs.weights(True), cs.sw, fused=True)   # table entry
+    torch.cuda.synchronize()
+    assert_bf16_close(y, cs.Y, "tuned linear, quant_launch")
+
+
 def test_tune_rejects_injected_failure(w8):
     w8.clear_config_table()
     best, st = w8.tune_shape("W8A8_INT8", 4, 256, 512, insert=False, fail_candidate=0, **SMALL)
