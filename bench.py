@@ -182,6 +182,8 @@ def parse():
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--table", default=None, help="config table to load instead of the shipped one")
+    p.add_argument("--layout", choices=("table", "row", "packed"), default="table",
+                   help="weight layout: the faster one per the table (default), or forced")
     p.add_argument("--report", default=None, help="write per-problem results (JSON) here")
     p.add_argument("--counter-pass", default=None, metavar="MANIFEST",
                    help="instead of timing, make the launches for a rocprofv3 --pmc run and "
@@ -202,10 +204,10 @@ def log(*a):
 
 
 class Problem:
-    def __init__(self, w8, fmt, M, N, K, rotate_bytes, dev):
+    def __init__(self, w8, fmt, M, N, K, rotate_bytes, dev, layout="table"):
         self.fmt, self.M, self.N, self.K = fmt, M, N, K
         # the weight layout the table times best for this shape (row-major if none)
-        self.packed = w8.best_layout(fmt, M, N, K)
+        self.packed = w8.best_layout(fmt, M, N, K) if layout == "table" else layout == "packed"
         self.cfg, self.from_table = w8.resolve_config(fmt, M, N, K, packed=self.packed)
         self.bytes = w8.algorithmic_bytes(fmt, M, N, K)
         x_bits = synthetic.activations(fmt, M, N, K)
@@ -348,10 +350,10 @@ def main():
     t0 = time.time()
     for fmt in fmts:
         for (M, N, K) in synthetic.SWEEP:
-            problems.append(Problem(w8, fmt, M, N, K, rotate, dev))
+            problems.append(Problem(w8, fmt, M, N, K, rotate, dev, args.layout))
     torch.cuda.synchronize()
     log(f"[bench] {len(problems)} problems set up in {time.time() - t0:.1f} s "
-        f"({sum(p.from_table for p in problems)} configs from the table)")
+        f"({sum(p.from_table == 1 for p in problems)} configs from the table)")
     if args.counter_pass:
         counter_pass(problems, w8, args.counter_pass, args.copy_calibration_mib)
         return
@@ -464,7 +466,8 @@ def main():
                                "= 72 GEMMs, per-shape table configs, HIP graph replay over "
                                f"{args.rotate_mib} MiB of rotating weights per problem",
                    "problems": len(problems),
-                   "table_hits": sum(p.from_table for p in problems),
+                   "table_hits": sum(p.from_table == 1 for p in problems),
+                   "bucket_hits": sum(p.from_table == 2 for p in problems),
                    "packed_layout": sum(bool(p.packed) for p in problems)},
         "geomean_us_per_gemm": round(geomean([p.us_gemm for p in problems]), 4),
         "geomean_us_quant_plus_gemm": round(geomean([p.us_path for p in problems]), 4),

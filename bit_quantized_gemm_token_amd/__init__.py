@@ -32,7 +32,8 @@ __all__ = ["Config", "W8Error", "UnsupportedShape", "Workspace", "PackedWeight",
            "workspace_size",
            "validate_config", "default_config", "resolve_config", "lookup_config",
            "set_config", "load_config_table", "save_config_table", "clear_config_table",
-           "config_table_size", "config_table_foreign", "tune_shape", "FORMATS", "MAX_M",
+           "config_table_size", "config_table_foreign", "tune_shape", "rank_configs",
+           "profile_configs", "model_config", "FORMATS", "MAX_M",
            "MAX_SPLIT_K", "GROUP", "ABI_VERSION"]
 
 
@@ -325,12 +326,21 @@ def default_config(fmt, M, N, K, op="gemm"):
 
 
 def resolve_config(fmt, M, N, K, packed=False, op="gemm"):
-    """(Config, from_table) that the op uses when cfg is None."""
+    """(Config, source) that the op uses when cfg is None; source is 1 for
+    the table entry of the shape, 2 for an entry of the same N, K and
+    floor(log2 M) bucket, 0 for the cost model's pick."""
     c = Config()
     hit = ctypes.c_int(0)
     _check(_lib.w8_resolve_config(_fmt(fmt), _op(op), M, N, K, int(bool(packed)),
                                   ctypes.byref(c), ctypes.byref(hit)))
-    return c, bool(hit.value)
+    return c, hit.value
+
+
+def model_config(fmt, M, N, K, packed=False, op="gemm"):
+    """The cost model's top-1 config (what an untuned shape runs)."""
+    c = Config()
+    _check(_lib.w8_model_config(_fmt(fmt), _op(op), M, N, K, int(bool(packed)), ctypes.byref(c)))
+    return c
 
 
 def lookup_config(fmt, M, N, K, packed=False, with_time=False, op="gemm"):
@@ -393,13 +403,9 @@ def load_default_table():
 
 
 # -------------------------------------------------------------------- tuner --
-def tune_shape(fmt, M, N, K, warmup=2, replays=5, bank2_top=5, rotate_bytes=512 << 20,
+def _tune_opts(warmup=2, replays=5, bank2_top=5, rotate_bytes=512 << 20,
                max_split_k=MAX_SPLIT_K, insert=True, fail_candidate=-1, packed=False,
-               stream_k=False, op="gemm"):
-    """Ahead-of-time tuning of one shape and weight layout on the current device.
-
-    Returns (Config, stats dict).  Synchronizes the device.
-    """
+               stream_k=False, op="gemm", top_n=0):
     o = TuneOpts()
     _lib.w8_tune_default_opts(ctypes.byref(o))
     o.warmup, o.replays, o.bank2_top = warmup, replays, bank2_top
@@ -408,6 +414,49 @@ def tune_shape(fmt, M, N, K, warmup=2, replays=5, bank2_top=5, rotate_bytes=512 
     o.packed = int(bool(packed))
     o.stream_k = int(bool(stream_k))
     o.op = _op(op)
+    o.top_n = int(top_n)
+    return o
+
+
+def rank_configs(fmt, M, N, K, packed=False, op="gemm", max_split_k=MAX_SPLIT_K,
+                 stream_k=False):
+    """The tuner's candidate set ranked by the cost model: [(predicted_us, Config)],
+    fastest first.  Host only."""
+    o = _tune_opts(packed=packed, op=op, max_split_k=max_split_k, stream_k=stream_k)
+    n = ctypes.c_int(0)
+    _check(_lib.w8_rank_configs(_fmt(fmt), M, N, K, ctypes.byref(o), None, None, 0,
+                                ctypes.byref(n)))
+    cfgs = (Config * max(n.value, 1))()
+    us = (ctypes.c_double * max(n.value, 1))()
+    _check(_lib.w8_rank_configs(_fmt(fmt), M, N, K, ctypes.byref(o), cfgs, us, n.value,
+                                ctypes.byref(n)))
+    return [(us[i], cfgs[i]) for i in range(n.value)]
+
+
+def profile_configs(fmt, M, N, K, cfgs, packed=False, op="gemm", warmup=2, replays=5,
+                    rotate_bytes=512 << 20):
+    """Times configs with the tuner's harness (bank 1, no table insert):
+    [us or None when the config's output failed validation].  Synchronizes."""
+    o = _tune_opts(warmup=warmup, replays=replays, rotate_bytes=rotate_bytes, packed=packed,
+                   op=op, insert=False)
+    n = len(cfgs)
+    arr = (Config * max(n, 1))(*cfgs)
+    us = (ctypes.c_double * max(n, 1))()
+    valid = (ctypes.c_int * max(n, 1))()
+    _check(_lib.w8_profile_configs(_fmt(fmt), M, N, K, ctypes.byref(o), arr, n, us, valid))
+    return [us[i] if valid[i] else None for i in range(n)]
+
+
+def tune_shape(fmt, M, N, K, warmup=2, replays=5, bank2_top=5, rotate_bytes=512 << 20,
+               max_split_k=MAX_SPLIT_K, insert=True, fail_candidate=-1, packed=False,
+               stream_k=False, op="gemm", top_n=0):
+    """Ahead-of-time tuning of one shape and weight layout on the current device
+    (top_n > 0: only the cost model's top_n candidates are timed).
+
+    Returns (Config, stats dict).  Synchronizes the device.
+    """
+    o = _tune_opts(warmup, replays, bank2_top, rotate_bytes, max_split_k, insert,
+                   fail_candidate, packed, stream_k, op, top_n)
     best = Config()
     stats = TuneStats()
     _check(_lib.w8_tune_shape(_fmt(fmt), M, N, K, ctypes.byref(o), ctypes.byref(best),

@@ -25,7 +25,8 @@ EXPORTS = ("w8_abi_version", "w8_status_string", "w8_last_error", "w8_quantize_a
            "w8_validate_config", "w8_default_config", "w8_resolve_config",
            "w8_load_config_table", "w8_save_config_table", "w8_clear_config_table",
            "w8_config_table_size", "w8_config_table_foreign", "w8_set_config",
-           "w8_lookup_config", "w8_tune_shape", "w8_tune_default_opts")
+           "w8_lookup_config", "w8_tune_shape", "w8_tune_default_opts", "w8_model_config",
+           "w8_rank_configs", "w8_profile_configs")
 
 
 class Config(ctypes.Structure):
@@ -64,7 +65,7 @@ class TuneOpts(ctypes.Structure):
                 ("rotate_bytes", ctypes.c_int64), ("max_split_k", ctypes.c_int32),
                 ("insert", ctypes.c_int32), ("fail_candidate", ctypes.c_int32),
                 ("packed", ctypes.c_int32), ("stream_k", ctypes.c_int32),
-                ("op", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
+                ("op", ctypes.c_int32), ("top_n", ctypes.c_int32)]
 
 
 class TuneStats(ctypes.Structure):
@@ -135,4 +136,13 @@ def load():
     lib.w8_tune_shape.restype = st
     lib.w8_tune_default_opts.argtypes = [ctypes.POINTER(TuneOpts)]
     lib.w8_tune_default_opts.restype = None
+    lib.w8_model_config.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, cfgp]
+    lib.w8_model_config.restype = st
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.w8_rank_configs.argtypes = [c_int, c_int, c_int, c_int, ctypes.POINTER(TuneOpts), cfgp,
+                                    dp, c_int, ctypes.POINTER(c_int)]
+    lib.w8_rank_configs.restype = st
+    lib.w8_profile_configs.argtypes = [c_int, c_int, c_int, c_int, ctypes.POINTER(TuneOpts),
+                                       cfgp, c_int, dp, ctypes.POINTER(c_int)]
+    lib.w8_profile_configs.restype = st
     return lib

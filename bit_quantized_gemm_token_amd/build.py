@@ -36,6 +36,7 @@ def _units():
              ("w8_tune.hip", [], "w8_tune.o"),
              ("w8_capi.cpp", ["-x", "hip"], "w8_capi.o"),
              ("w8_table.cpp", ["-x", "hip"], "w8_table.o"),
+             ("w8_model.cpp", ["-x", "hip"], "w8_model.o"),
              ("w8_registry.cpp", ["-x", "hip"], "w8_registry.o")]
     for fmt in (0, 1, 2):
         for swap in (0, 1):

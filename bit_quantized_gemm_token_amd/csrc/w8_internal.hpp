@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "../../include/w8gemm.h"
 #include "w8_launch.hpp"
@@ -34,9 +36,21 @@ int tiles_of(int N, const w8_cfg& c);                       // output tiles alon
 int partial_slots(int fmt, int N, int K, const w8_cfg& c);  // workspace slots per tile
 int ksteps_of(int fmt, int K);
 
-// Resolve cfg == NULL through the table (entries are per operation and
-// weight layout), else the default.
+// Resolve cfg == NULL: the table entry for the shape (*from_table = 1), else
+// one for the same N, K and an M of the same floor(log2 M) bucket that is
+// valid for this M (2), else the cost model's pick (0).
 w8_cfg resolve_cfg(int fmt, int op, int M, int N, int K, int packed, int* from_table);
+
+// The config family's feasible set for the tuner (its pruning rules, and for
+// the linear op the quantize-launch variants), the cost model's predicted
+// time per call of a config, the set ranked by it (ascending), and the
+// model's top-1 pick.
+std::vector<w8_cfg> enumerate_configs(int fmt, int op, int M, int N, int K, int packed,
+                                      int max_split_k, int stream_k);
+double predict_us(int fmt, int op, int M, int N, int K, const w8_cfg& c);
+std::vector<std::pair<double, w8_cfg>> rank_configs(int fmt, int op, int M, int N, int K,
+                                                    int packed, int max_split_k, int stream_k);
+w8_cfg model_cfg(int fmt, int op, int M, int N, int K, int packed);
 
 // The device must be gfx950 (checked once per device).
 w8_status check_device();

@@ -171,19 +171,45 @@ void maybe_load_env(Table& t) {
 
 }  // namespace
 
+static int m_bucket(int M) { return 31 - __builtin_clz((unsigned)M); }  // floor(log2 M)
+
 w8_cfg resolve_cfg(int fmt, int op, int M, int N, int K, int packed, int* from_table) {
   Table& t = table();
   {
     std::lock_guard<std::mutex> lk(t.mu);
     maybe_load_env(t);
-    auto it = t.native.find(Key(fmt, op, packed ? 1 : 0, M, N, K));
+    const int pk = packed ? 1 : 0;
+    auto it = t.native.find(Key(fmt, op, pk, M, N, K));
     if (it != t.native.end()) {
       if (from_table) *from_table = 1;
       return it->second.cfg;
     }
+    // M-bucket fallback (flashinfer-ai/flashinfer pull 3948: the pick is
+    // made per floor(log2 M)): the entry of the nearest M in the bucket,
+    // the larger on a tie, if its config is valid for this M.
+    const int bucket = m_bucket(M);
+    const w8_cfg* pick = nullptr;
+    int pick_dist = 1 << 30, pick_m = 0;
+    for (int m = 1 << bucket; m < (2 << bucket) && m <= W8_MAX_M; ++m) {
+      if (m == M) continue;
+      auto e = t.native.find(Key(fmt, op, pk, m, N, K));
+      if (e == t.native.end()) continue;
+      const int d = m > M ? m - M : M - m;
+      if (d < pick_dist || (d == pick_dist && m > pick_m)) {
+        w8_cfg c = e->second.cfg;
+        if (check_cfg(fmt, op, M, N, K, c) != W8_OK) continue;
+        pick = &e->second.cfg;
+        pick_dist = d;
+        pick_m = m;
+      }
+    }
+    if (pick) {
+      if (from_table) *from_table = 2;
+      return *pick;
+    }
   }
   if (from_table) *from_table = 0;
-  return make_default_cfg(fmt, op, M, N, K);
+  return model_cfg(fmt, op, M, N, K, packed ? 1 : 0);
 }
 
 }  // namespace w8

@@ -114,229 +114,111 @@ struct Cand {
     if (e_ != hipSuccess) return fail(W8_E_HIP, hip_msg(#expr, e_));        \
   } while (0)
 
-}  // namespace
-}  // namespace w8
-
-using namespace w8;
-
-extern "C" void w8_tune_default_opts(w8_tune_opts* o) {
-  if (!o) return;
-  std::memset(o, 0, sizeof *o);
-  o->abi_version = W8_ABI_VERSION;
-  o->warmup = 2;
-  o->replays = 5;
-  o->bank2_top = 5;
-  o->rotate_bytes = (int64_t)512 << 20;
-  o->max_split_k = W8_MAX_SPLIT_K;
-  o->insert = 1;
-  o->fail_candidate = -1;
-  o->packed = 0;
-  o->stream_k = 0;
-  o->op = W8_OP_GEMM;
-}
-
-extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tune_opts* opts,
-                                   w8_cfg* best, w8_tune_stats* stats) {
-  const auto t_start = std::chrono::steady_clock::now();
-  w8_status st = check_gemm_shape(fmt, M, N, K);
-  if (st) return st;
-  if (!best) return fail(W8_E_INVALID, "null best");
+// The timing and validation harness shared by the tuner and the profiler:
+// device buffers for (fmt, M, N, K) and one op and weight layout, the
+// reference output of the default GEMM config, and graph timing over R
+// rotating weight copies.
+struct Harness {
+  int fmt, op, M, N, K, packed;
   w8_tune_opts o;
-  w8_tune_default_opts(&o);
-  if (opts) {
-    if (opts->abi_version != W8_ABI_VERSION) return fail(W8_E_INVALID, "opts.abi_version mismatch");
-    o = *opts;
-  }
-  if (o.warmup < 0 || o.replays < 1 || o.bank2_top < 1 || o.rotate_bytes < 0 ||
-      o.max_split_k < 1 || o.max_split_k > W8_MAX_SPLIT_K ||
-      (o.op != W8_OP_GEMM && o.op != W8_OP_LINEAR))
-    return fail(W8_E_INVALID, "bad tuner options");
-  const int op = o.op;
-  st = check_device();
-  if (st) return st;
-
-  const int packed = o.packed ? 1 : 0;
-  const long long ld = (K + 15) / 16 * 16;
-  const size_t wrow_bytes = (size_t)N * ld;
-  const size_t wbytes = packed ? packed_weight_bytes(fmt, N, K) : wrow_bytes;
-  size_t R = wbytes ? (size_t)((o.rotate_bytes + (long long)wbytes - 1) / (long long)wbytes) : 1;
-  R = std::max<size_t>(R, 2);
-  R = std::min<size_t>(R, 4096);
-  const bool block = fmt == W8_BLOCK_FP8;
-  const int G = K / W8_GROUP;
-  const size_t nsx = block ? (size_t)M * G : (size_t)M;
-  const size_t nsw = block ? (size_t)((N + 127) / 128) * G : (size_t)N;
-
-  // Candidates: every config of the family valid for the op -- (waves_k,
-  // waves_n, x_lds) in
-  // {(1..16, 1, 0), (1..8, 1, 1), (1, 2..8, 1)}, each with split_k up to
-  // max_split_k or (opts.stream_k) with a
-  // stream-K grid of 256, 512 or 1024 workgroups (1, 2 or 4 per compute
-  // unit) -- minus those that cannot pay off or cannot differ from another:
-  //   - fewer than one K-step per wave (only empty splits or waves added);
-  //   - unroll above the K-steps each wave owns (the loop would never run a
-  //     full stage, so the candidate equals the one with a smaller unroll);
-  //   - partial traffic above twice the weight bytes;
-  //   - fewer waves in total than min(256, the most any candidate has): a
-  //     stream this narrow leaves most of the 256 compute units idle.
-  std::vector<Cand> cands;
-  const int T = ksteps_of(fmt, K);
-  const int tiles_n[] = {16, 32, 64};
-  // (waves_k, waves_n, x_lds)
-  const int wave_shapes[][3] = {{1, 1, 0}, {2, 1, 0}, {4, 1, 0}, {8, 1, 0}, {16, 1, 0},
-                                {1, 1, 1}, {2, 1, 1}, {4, 1, 1}, {8, 1, 1},
-                                {1, 2, 1}, {1, 4, 1}, {1, 8, 1}};
-  const int unrolls[] = {1, 2, 4};
-  const int grids[] = {256, 512, 1024};
-  auto total_waves = [&](const w8_cfg& c) {
-    const long long wgs = c.grid > 0 ? c.grid : (long long)tiles_of(N, c) * c.split_k;
-    return wgs * c.waves_k * c.waves_n;
-  };
-  std::vector<w8_cfg> all;
-  long long most_waves = 0;
-  auto consider = [&](const w8_cfg& c) {
-    if (check_cfg(fmt, op, M, N, K, c) != W8_OK) return;
-    // K-steps per wave
-    const long long per_wave = c.grid > 0 ? (long long)tiles_of(N, c) * T / (c.grid * c.waves_k)
-                                          : (long long)T / (c.split_k * c.waves_k);
-    if (per_wave < 1) return;
-    if (c.unroll > 1 && per_wave < c.unroll) return;
-    if (workspace_bytes(fmt, op, M, N, K, c) > 2 * wbytes + ws_counter_bytes(0)) return;
-    all.push_back(c);
-    most_waves = std::max(most_waves, total_waves(c));
-  };
-  for (int tn : tiles_n)
-    for (const auto& ws : wave_shapes)
-      for (int u : unrolls)
-        for (int sw = 0; sw < 2; ++sw) {
-          w8_cfg c;
-          std::memset(&c, 0, sizeof c);
-          c.abi_version = W8_ABI_VERSION;
-          c.tile_n = tn;
-          c.waves_k = ws[0];
-          c.waves_n = ws[1];
-          c.x_lds = ws[2];
-          c.unroll = u;
-          c.swap_ab = sw;
-          for (int s = 1; s <= o.max_split_k; s *= 2) {
-            c.split_k = s;
-            c.grid = 0;
-            consider(c);
-          }
-          for (int gr : grids) {
-            if (!o.stream_k) break;
-            c.split_k = 1;
-            c.grid = gr;
-            consider(c);
-          }
-        }
-  const long long min_waves = std::min<long long>(256, most_waves);
-  for (const w8_cfg& c : all) {
-    if (total_waves(c) < min_waves) continue;
-    Cand cd;
-    cd.cfg = c;
-    cd.index = (int)cands.size();
-    cands.push_back(cd);
-  }
-  // The linear op also competes with a quantize launch of its own followed
-  // by the GEMM: with the GEMM's table entry for this shape and layout (tune
-  // the GEMM first) and with the GEMM's default config.
-  if (op == W8_OP_LINEAR) {
-    int hit = 0;
-    std::vector<w8_cfg> gemm_cfgs = {resolve_cfg(fmt, W8_OP_GEMM, M, N, K, packed, &hit)};
-    if (hit) gemm_cfgs.push_back(make_default_cfg(fmt, W8_OP_GEMM, M, N, K));
-    for (w8_cfg c : gemm_cfgs) {
-      c.quant_launch = 1;
-      if (check_cfg(fmt, op, M, N, K, c) != W8_OK) continue;
-      bool dup = false;
-      for (const Cand& e : cands) dup = dup || std::memcmp(&e.cfg, &c, sizeof c) == 0;
-      if (dup) continue;
-      Cand cd;
-      cd.cfg = c;
-      cd.index = (int)cands.size();
-      cands.push_back(cd);
-    }
-  }
-  size_t max_ws = 0;
-  for (const Cand& cd : cands) max_ws = std::max(max_ws, workspace_bytes(fmt, op, M, N, K, cd.cfg));
-  const w8_cfg dflt = make_default_cfg(fmt, W8_OP_GEMM, M, N, K);     // reference
-  const w8_cfg dflt_op = make_default_cfg(fmt, op, M, N, K);          // reported baseline
-  max_ws = std::max(max_ws, workspace_bytes(fmt, W8_OP_GEMM, M, N, K, dflt));
-  max_ws = std::max(max_ws, workspace_bytes(fmt, op, M, N, K, dflt_op));
-
+  long long ld = 0;
+  size_t wbytes = 0, wrow_bytes = 0, R = 0, nsx = 0, nsw = 0;
+  bool block = false;
+  int is_int8 = 0;
   Buffers b;
   hipStream_t stream = nullptr;
-  TRY_HIP(hipStreamCreate(&stream));
-  struct StreamGuard {
-    hipStream_t s;
-    ~StreamGuard() { hipStreamDestroy(s); }
-  } sguard{stream};
-  TRY_HIP(hipMalloc(&b.wrow, wrow_bytes));
-  TRY_HIP(hipMalloc(&b.wpool, wbytes * R));
-  TRY_HIP(hipMalloc(&b.xq, (size_t)M * ld));
-  if (op == W8_OP_LINEAR) TRY_HIP(hipMalloc(&b.x, (size_t)M * ld * 2));
-  TRY_HIP(hipMalloc(&b.sx, nsx * 4));
-  TRY_HIP(hipMalloc(&b.sw, nsw * 4));
-  TRY_HIP(hipMalloc(&b.y, (size_t)M * N * 2));
-  b.ws_bytes = max_ws;
-  if (max_ws) {
-    TRY_HIP(hipMalloc(&b.ws, max_ws));
-    TRY_HIP(hipMemsetAsync(b.ws, 0, max_ws, stream));
-  }
-  const int is_int8 = fmt == W8_W8A8_INT8;
-  hipLaunchKernelGGL(fill_codes_kernel, dim3(4096), dim3(256), 0, stream, b.wpool, wbytes * R,
-                     0x1234u, is_int8);
-  hipLaunchKernelGGL(fill_codes_kernel, dim3(1024), dim3(256), 0, stream, b.wrow, wrow_bytes,
-                     0x4321u, is_int8);
-  // copy 0 of the pool holds the same weights as the reference, in the tuned layout
-  if (packed) {
-    TRY_HIP(launch_pack_weight(fmt, b.wrow, ld, N, K, b.wpool, stream));
-  } else {
-    TRY_HIP(hipMemcpyAsync(b.wpool, b.wrow, wrow_bytes, hipMemcpyDeviceToDevice, stream));
-  }
-  if (op == W8_OP_LINEAR) {
-    // bf16 activations, quantized by the standalone quantizer for the reference
-    hipLaunchKernelGGL(fill_bf16_kernel, dim3(64), dim3(256), 0, stream, b.x, (size_t)M * ld,
-                       0x9876u);
-    TRY_HIP(hipGetLastError());
-    QuantActArgs qa{b.x, b.xq, b.sx, ld, ld, M, K};
-    TRY_HIP(launch_quantize_act(fmt, qa, stream));
-  } else {
-    hipLaunchKernelGGL(fill_codes_kernel, dim3(64), dim3(256), 0, stream, b.xq, (size_t)M * ld,
-                       0x9876u, is_int8);
-    hipLaunchKernelGGL(fill_scales_kernel, dim3(64), dim3(256), 0, stream, b.sx, nsx, 0x55u,
-                       0.01f, 0.1f);
-  }
-  hipLaunchKernelGGL(fill_scales_kernel, dim3(64), dim3(256), 0, stream, b.sw, nsw, 0x77u, 0.001f,
-                     0.01f);
-  TRY_HIP(hipGetLastError());
-  TRY_HIP(hipStreamSynchronize(stream));
-
-  GemmCall call{fmt,  M,   N, K, b.xq, ld,        b.sx,       b.wpool, packed ? 0 : ld,
-                b.sw, b.y, N, 0, b.ws, b.ws_bytes, packed, nullptr, 0};
-  if (op == W8_OP_LINEAR) {  // the fused op reads bf16 activations
-    call.xq = nullptr;
-    call.sx = nullptr;
-    call.x = b.x;
-    call.ldx = ld;
-  }
-
-  // Reference output: the default GEMM config on the row-major weights of
-  // copy 0 (for the fused op, after the standalone quantizer).
-  std::vector<uint16_t> yref((size_t)M * N), ycur((size_t)M * N);
-  GemmCall ref{fmt,  M,   N, K, b.xq, ld,        b.sx,       b.wrow, ld,
-               b.sw, b.y, N, 0, b.ws, b.ws_bytes, 0,      nullptr, 0};
-  st = launch_gemm_call(ref, dflt, stream);
-  if (st) return st;
-  TRY_HIP(hipStreamSynchronize(stream));
-  TRY_HIP(hipMemcpy(yref.data(), b.y, yref.size() * 2, hipMemcpyDeviceToHost));
+  GemmCall call{};
+  std::vector<uint16_t> yref, ycur;
   float ref_max = 0.0f;
-  for (uint16_t v : yref) ref_max = std::max(ref_max, std::fabs(bf16_to_float(v)));
 
-  auto launch = [&](const GemmCall& g, const w8_cfg& c) {
+  ~Harness() {
+    if (stream) hipStreamDestroy(stream);
+  }
+
+  w8_status launch(const GemmCall& g, const w8_cfg& c) {
     return op == W8_OP_LINEAR ? launch_linear_call(g, c, stream) : launch_gemm_call(g, c, stream);
-  };
-  auto validate = [&](const w8_cfg& c, bool* good) -> w8_status {
+  }
+
+  // Allocates and fills the inputs; max_ws: largest workspace of any config
+  // that will run.
+  w8_status setup(size_t max_ws) {
+    ld = (K + 15) / 16 * 16;
+    wrow_bytes = (size_t)N * ld;
+    wbytes = packed ? packed_weight_bytes(fmt, N, K) : wrow_bytes;
+    R = wbytes ? (size_t)((o.rotate_bytes + (long long)wbytes - 1) / (long long)wbytes) : 1;
+    R = std::max<size_t>(R, 2);
+    R = std::min<size_t>(R, 4096);
+    block = fmt == W8_BLOCK_FP8;
+    const int G = K / W8_GROUP;
+    nsx = block ? (size_t)M * G : (size_t)M;
+    nsw = block ? (size_t)((N + 127) / 128) * G : (size_t)N;
+    const w8_cfg dflt = make_default_cfg(fmt, W8_OP_GEMM, M, N, K);  // reference
+    max_ws = std::max(max_ws, workspace_bytes(fmt, W8_OP_GEMM, M, N, K, dflt));
+    TRY_HIP(hipStreamCreate(&stream));
+    TRY_HIP(hipMalloc(&b.wrow, wrow_bytes));
+    TRY_HIP(hipMalloc(&b.wpool, wbytes * R));
+    TRY_HIP(hipMalloc(&b.xq, (size_t)M * ld));
+    if (op == W8_OP_LINEAR) TRY_HIP(hipMalloc(&b.x, (size_t)M * ld * 2));
+    TRY_HIP(hipMalloc(&b.sx, nsx * 4));
+    TRY_HIP(hipMalloc(&b.sw, nsw * 4));
+    TRY_HIP(hipMalloc(&b.y, (size_t)M * N * 2));
+    b.ws_bytes = max_ws;
+    if (max_ws) {
+      TRY_HIP(hipMalloc(&b.ws, max_ws));
+      TRY_HIP(hipMemsetAsync(b.ws, 0, max_ws, stream));
+    }
+    is_int8 = fmt == W8_W8A8_INT8;
+    hipLaunchKernelGGL(fill_codes_kernel, dim3(4096), dim3(256), 0, stream, b.wpool, wbytes * R,
+                       0x1234u, is_int8);
+    hipLaunchKernelGGL(fill_codes_kernel, dim3(1024), dim3(256), 0, stream, b.wrow, wrow_bytes,
+                       0x4321u, is_int8);
+    // copy 0 of the pool holds the same weights as the reference, in the tuned layout
+    if (packed) {
+      TRY_HIP(launch_pack_weight(fmt, b.wrow, ld, N, K, b.wpool, stream));
+    } else {
+      TRY_HIP(hipMemcpyAsync(b.wpool, b.wrow, wrow_bytes, hipMemcpyDeviceToDevice, stream));
+    }
+    if (op == W8_OP_LINEAR) {
+      // bf16 activations, quantized by the standalone quantizer for the reference
+      hipLaunchKernelGGL(fill_bf16_kernel, dim3(64), dim3(256), 0, stream, b.x, (size_t)M * ld,
+                         0x9876u);
+      TRY_HIP(hipGetLastError());
+      QuantActArgs qa{b.x, b.xq, b.sx, ld, ld, M, K};
+      TRY_HIP(launch_quantize_act(fmt, qa, stream));
+    } else {
+      hipLaunchKernelGGL(fill_codes_kernel, dim3(64), dim3(256), 0, stream, b.xq, (size_t)M * ld,
+                         0x9876u, is_int8);
+      hipLaunchKernelGGL(fill_scales_kernel, dim3(64), dim3(256), 0, stream, b.sx, nsx, 0x55u,
+                         0.01f, 0.1f);
+    }
+    hipLaunchKernelGGL(fill_scales_kernel, dim3(64), dim3(256), 0, stream, b.sw, nsw, 0x77u,
+                       0.001f, 0.01f);
+    TRY_HIP(hipGetLastError());
+    TRY_HIP(hipStreamSynchronize(stream));
+
+    call = GemmCall{fmt,  M,   N, K, b.xq, ld,        b.sx,   b.wpool, packed ? 0 : ld,
+                    b.sw, b.y, N, 0, b.ws, b.ws_bytes, packed, nullptr, 0};
+    if (op == W8_OP_LINEAR) {  // the linear op reads bf16 activations
+      call.xq = nullptr;
+      call.sx = nullptr;
+      call.x = b.x;
+      call.ldx = ld;
+    }
+    // Reference output: the default GEMM config on the row-major weights of
+    // copy 0 (for the linear op, after the standalone quantizer).
+    yref.resize((size_t)M * N);
+    ycur.resize((size_t)M * N);
+    GemmCall ref{fmt,  M,   N, K, b.xq, ld,        b.sx, b.wrow,  ld,
+                 b.sw, b.y, N, 0, b.ws, b.ws_bytes, 0,    nullptr, 0};
+    w8_status st = launch_gemm_call(ref, dflt, stream);
+    if (st) return st;
+    TRY_HIP(hipStreamSynchronize(stream));
+    TRY_HIP(hipMemcpy(yref.data(), b.y, yref.size() * 2, hipMemcpyDeviceToHost));
+    for (uint16_t v : yref) ref_max = std::max(ref_max, std::fabs(bf16_to_float(v)));
+    return W8_OK;
+  }
+
+  w8_status validate(const w8_cfg& c, bool* good) {
     w8_status s2 = launch(call, c);
     if (s2) return s2;
     TRY_HIP(hipStreamSynchronize(stream));
@@ -353,11 +235,11 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
       }
     }
     return W8_OK;
-  };
+  }
 
-  // Median us per GEMM of the graph of R GEMMs over rotating weight copies.
-  auto time_cfg = [&](const w8_cfg& c, double* us) -> w8_status {
-    // (every GEMM of the graph reads its own copy of the weights)
+  // Median us per call of the graph of R calls over rotating weight copies
+  // (every call of the graph reads its own copy of the weights).
+  w8_status time(const w8_cfg& c, double* us) {
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     TRY_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal));
@@ -396,12 +278,152 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
     std::sort(ms.begin(), ms.end());
     *us = ms[ms.size() / 2] * 1000.0 / (double)R;
     return W8_OK;
-  };
+  }
+};
+
+w8_status read_opts(const w8_tune_opts* opts, w8_tune_opts* o) {
+  w8_tune_default_opts(o);
+  if (opts) {
+    if (opts->abi_version != W8_ABI_VERSION) return fail(W8_E_INVALID, "opts.abi_version mismatch");
+    *o = *opts;
+  }
+  if (o->warmup < 0 || o->replays < 1 || o->bank2_top < 1 || o->rotate_bytes < 0 ||
+      o->max_split_k < 1 || o->max_split_k > W8_MAX_SPLIT_K || o->top_n < 0 ||
+      (o->op != W8_OP_GEMM && o->op != W8_OP_LINEAR))
+    return fail(W8_E_INVALID, "bad tuner options");
+  return W8_OK;
+}
+
+}  // namespace
+}  // namespace w8
+
+using namespace w8;
+
+extern "C" void w8_tune_default_opts(w8_tune_opts* o) {
+  if (!o) return;
+  std::memset(o, 0, sizeof *o);
+  o->abi_version = W8_ABI_VERSION;
+  o->warmup = 2;
+  o->replays = 5;
+  o->bank2_top = 5;
+  o->rotate_bytes = (int64_t)512 << 20;
+  o->max_split_k = W8_MAX_SPLIT_K;
+  o->insert = 1;
+  o->fail_candidate = -1;
+  o->packed = 0;
+  o->stream_k = 0;
+  o->op = W8_OP_GEMM;
+  o->top_n = 0;
+}
+
+extern "C" w8_status w8_rank_configs(w8_fmt fmt, int M, int N, int K, const w8_tune_opts* opts,
+                                     w8_cfg* out, double* predicted_us, int cap, int* count) {
+  w8_status st = check_gemm_shape(fmt, M, N, K);
+  if (st) return st;
+  if (!count || cap < 0 || (cap > 0 && !out)) return fail(W8_E_INVALID, "bad output arguments");
+  w8_tune_opts o;
+  st = read_opts(opts, &o);
+  if (st) return st;
+  const auto r = rank_configs(fmt, o.op, M, N, K, o.packed ? 1 : 0, o.max_split_k, o.stream_k);
+  *count = (int)r.size();
+  for (int i = 0; i < cap && i < (int)r.size(); ++i) {
+    out[i] = r[i].second;
+    if (predicted_us) predicted_us[i] = r[i].first;
+  }
+  return ok();
+}
+
+extern "C" w8_status w8_profile_configs(w8_fmt fmt, int M, int N, int K,
+                                        const w8_tune_opts* opts, const w8_cfg* cfgs, int n,
+                                        double* us, int* valid) {
+  w8_status st = check_gemm_shape(fmt, M, N, K);
+  if (st) return st;
+  if (n < 0 || (n > 0 && (!cfgs || !us || !valid))) return fail(W8_E_INVALID, "bad arguments");
+  w8_tune_opts o;
+  st = read_opts(opts, &o);
+  if (st) return st;
+  for (int i = 0; i < n; ++i) {
+    st = check_cfg(fmt, o.op, M, N, K, cfgs[i]);
+    if (st) return st;
+  }
+  st = check_device();
+  if (st) return st;
+  Harness h;
+  h.fmt = fmt;
+  h.op = o.op;
+  h.M = M;
+  h.N = N;
+  h.K = K;
+  h.packed = o.packed ? 1 : 0;
+  h.o = o;
+  size_t max_ws = 0;
+  for (int i = 0; i < n; ++i) max_ws = std::max(max_ws, workspace_bytes(fmt, o.op, M, N, K, cfgs[i]));
+  st = h.setup(max_ws);
+  if (st) return st;
+  for (int i = 0; i < n; ++i) {
+    bool good = false;
+    st = h.validate(cfgs[i], &good);
+    if (st) return st;
+    valid[i] = good ? 1 : 0;
+    us[i] = 0.0;
+    if (!good) continue;
+    st = h.time(cfgs[i], &us[i]);
+    if (st) return st;
+  }
+  return ok();
+}
+
+extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tune_opts* opts,
+                                   w8_cfg* best, w8_tune_stats* stats) {
+  const auto t_start = std::chrono::steady_clock::now();
+  w8_status st = check_gemm_shape(fmt, M, N, K);
+  if (st) return st;
+  if (!best) return fail(W8_E_INVALID, "null best");
+  w8_tune_opts o;
+  st = read_opts(opts, &o);
+  if (st) return st;
+  const int op = o.op;
+  st = check_device();
+  if (st) return st;
+  const int packed = o.packed ? 1 : 0;
+
+  // Candidates: the feasible set of the family (enumerate_configs), in
+  // enumeration order, or with top_n > 0 the top_n of the cost model's
+  // ranking.
+  std::vector<Cand> cands;
+  std::vector<w8_cfg> list;
+  if (o.top_n > 0) {
+    const auto r = rank_configs(fmt, op, M, N, K, packed, o.max_split_k, o.stream_k);
+    for (size_t i = 0; i < r.size() && (int)i < o.top_n; ++i) list.push_back(r[i].second);
+  } else {
+    list = enumerate_configs(fmt, op, M, N, K, packed, o.max_split_k, o.stream_k);
+  }
+  if (list.empty()) return fail(W8_E_VALIDATION, "no feasible candidate");
+  for (const w8_cfg& c : list) {
+    Cand cd;
+    cd.cfg = c;
+    cd.index = (int)cands.size();
+    cands.push_back(cd);
+  }
+  const w8_cfg dflt_op = make_default_cfg(fmt, op, M, N, K);  // reported baseline
+  size_t max_ws = workspace_bytes(fmt, op, M, N, K, dflt_op);
+  for (const Cand& cd : cands) max_ws = std::max(max_ws, workspace_bytes(fmt, op, M, N, K, cd.cfg));
+
+  Harness h;
+  h.fmt = fmt;
+  h.op = op;
+  h.M = M;
+  h.N = N;
+  h.K = K;
+  h.packed = packed;
+  h.o = o;
+  st = h.setup(max_ws);
+  if (st) return st;
 
   int nvalid = 0, nrej = 0;
   for (Cand& cd : cands) {
     bool good = false;
-    st = validate(cd.cfg, &good);
+    st = h.validate(cd.cfg, &good);
     if (st) return st;
     if (cd.index == o.fail_candidate) good = false;
     if (!good) {
@@ -410,7 +432,7 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
     }
     cd.valid = true;
     ++nvalid;
-    st = time_cfg(cd.cfg, &cd.us1);
+    st = h.time(cd.cfg, &cd.us1);
     if (st) return st;
   }
   if (nvalid == 0) return fail(W8_E_VALIDATION, "no candidate passed validation");
@@ -421,11 +443,11 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   std::sort(order.begin(), order.end(), [](const Cand* a, const Cand* c) { return a->us1 < c->us1; });
   const size_t top = std::min<size_t>(order.size(), (size_t)o.bank2_top);
   for (size_t i = 0; i < top; ++i) {
-    st = time_cfg(order[i]->cfg, &order[i]->us2);
+    st = h.time(order[i]->cfg, &order[i]->us2);
     if (st) return st;
   }
   double dflt_us2 = 0;
-  st = time_cfg(dflt_op, &dflt_us2);  // the op's default config on the tuned layout
+  st = h.time(dflt_op, &dflt_us2);  // the op's default config on the tuned layout
   if (st) return st;
 
   // Bank-2 winner; within 1% prefer no shared tiles (split_k = 1, grid = 0),
@@ -458,6 +480,8 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
     stats->best_us_bank1 = win->us1;
     stats->best_us_bank2 = win->us2;
     stats->default_us_bank2 = dflt_us2;
+    const int G = K / W8_GROUP;
+    const bool block = fmt == W8_BLOCK_FP8;
     const double bytes = block ? (double)N * K + (double)M * K + 2.0 * M * N +
                                      4.0 * ((N + 127) / 128) * G + 4.0 * M * G
                                : (double)N * K + (double)M * K + 2.0 * M * N + 4.0 * N + 4.0 * M;

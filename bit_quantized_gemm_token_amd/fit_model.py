@@ -1,0 +1,315 @@
+"""Measured data for the config cost model, and the fit of its constants.
+
+    python -m bit_quantized_gemm_token_amd.fit_model collect --out CSV
+           [--formats ...] [--layouts packed] [--ops gemm] [--shapes M,N,K;...]
+           [--replays 3] [--rotate-mib 256] [--time-budget-s 0]
+    python -m bit_quantized_gemm_token_amd.fit_model fit CSV [--top-n 16] [--params a,b]
+    python -m bit_quantized_gemm_token_amd.fit_model bucket-eval --shapes M,N,K;...
+
+collect (GPU): for every shape, layout and op, times every candidate of the
+tuner's feasible set with the tuner's own harness (w8_profile_configs: graph
+replays over rotating weight copies) and appends one CSV row per candidate:
+fmt, op, layout, M, N, K, the config fields, the measured us (empty when the
+config failed validation) and the model's current prediction.
+
+fit (CPU): fits the constants of the model in csrc/w8_model.cpp to those
+timings (a ranking loss plus a weighted log-time error, Nelder-Mead over the
+constants, which enter the model non-linearly) and reports how good the model's
+top-1 and the best of its top-N are against the measured best -- the two
+quantities the flashinfer-ai/flashinfer pull 3948 discussion weighs (top-1
+geomean, and the loss of autotuning only a top-N ranked list).  The Python
+model below mirrors predict_us() in w8_model.cpp term by term; the printed
+constants go into kParams there.
+
+bucket-eval (GPU): for shapes whose M has no table entry but whose
+floor(log2 M) bucket has one, times the bucket entry's config, the model's
+pick and the tuned best (packed weights) and reports the ratios.
+"""
+import argparse
+import csv
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CFG_KEYS = ("tile_n", "waves_k", "waves_n", "unroll", "split_k", "grid", "swap_ab", "x_lds",
+            "quant_launch")
+PARAM_NAMES = ("t0", "cu_bw", "latency", "hbm_bw", "slots", "sk_base", "sk_slot", "xl_stage",
+               "wg_cost", "mfma", "reduce", "q_launch", "q_row_bw")
+
+
+def collect(a):
+    import bit_quantized_gemm_token_amd as w8
+    from bit_quantized_gemm_token_amd.tune_sweep import default_shapes
+    if a.shapes:
+        shapes = [tuple(int(v) for v in s.split(",")) for s in a.shapes.split(";") if s]
+    else:
+        shapes = default_shapes()
+    new = not os.path.exists(a.out)
+    t0 = time.time()
+    with open(a.out, "a", newline="") as f:
+        wr = csv.writer(f)
+        if new:
+            wr.writerow(("fmt", "op", "layout", "M", "N", "K") + CFG_KEYS + ("us", "pred"))
+        for op in a.ops.split(","):
+            for fmt in a.formats.split(","):
+                for packed in [{"row": False, "packed": True}[v] for v in a.layouts.split(",")]:
+                    for (M, N, K) in shapes:
+                        if a.time_budget_s and time.time() - t0 > a.time_budget_s:
+                            print("[collect] time budget reached", flush=True)
+                            return 0
+                        ranked = w8.rank_configs(fmt, M, N, K, packed=packed, op=op)
+                        cfgs = [c for _, c in ranked]
+                        us = w8.profile_configs(fmt, M, N, K, cfgs, packed=packed, op=op,
+                                                warmup=1, replays=a.replays,
+                                                rotate_bytes=a.rotate_mib << 20)
+                        layout = "packed" if packed else "row"
+                        for (pred, c), u in zip(ranked, us):
+                            d = c.as_dict()
+                            wr.writerow((fmt, op, layout, M, N, K) + tuple(d[k] for k in CFG_KEYS)
+                                        + ("" if u is None else f"{u:.4f}", f"{pred:.4f}"))
+                        f.flush()
+                        good = [u for u in us if u is not None]
+                        print(f"[collect] {op} {fmt} {layout} {M}x{N}x{K}: {len(cfgs)} configs, "
+                              f"best {min(good):.3f} us, model top-1 {us[0]} us", flush=True)
+    return 0
+
+
+# ------------------------------------------------------------------ model --
+def ksteps(fmt, K):
+    ks = 64 if fmt == "W8A8_INT8" else 128
+    return (K + ks - 1) // ks, ks
+
+
+def partial_slots(fmt, N, K, c, ntiles):
+    if c["grid"] > 0:
+        T, _ = ksteps(fmt, K)
+        I = ntiles * T
+        lmin = I // c["grid"]
+        return 1 if T <= 1 else (T - 2) // lmin + 2
+    return c["split_k"]
+
+
+def predict(p, fmt, op, M, N, K, c):
+    """predict_us() of csrc/w8_model.cpp."""
+    (t0, cu_bw, lat, hbm_bw, slots, sk_base, sk_slot, xl_stage, wg_cost, mfma, reduce,
+     q_launch, q_row_bw) = p
+    T, KS = ksteps(fmt, K)
+    MB, NB, W = (M + 15) // 16, c["tile_n"] // 16, c["waves_k"] * c["waves_n"]
+    cols = c["tile_n"] * c["waves_n"]
+    ntiles = (N + cols - 1) // cols
+    G = c["grid"] if c["grid"] > 0 else ntiles * c["split_k"]
+    seg = math.ceil(ntiles * T / c["grid"]) if c["grid"] > 0 else math.ceil(T / c["split_k"])
+    fused = op == "linear" and not c["quant_launch"]
+    wbytes = 16.0 * NB * c["waves_n"] * seg * KS
+    abytes = (1.0 if c["x_lds"] else c["waves_n"]) * 16.0 * MB * seg * KS
+    if fused:
+        abytes *= 2.0
+    shared = c["split_k"] > 1 or c["grid"] > 0
+    pbytes = 16.0 * NB * c["waves_n"] * 16.0 * MB * 4.0 if shared else 0.0
+    per_wg = wbytes + abytes + pbytes
+    per_cu_wgs = math.ceil(G / 256.0)
+    resident = min(per_cu_wgs, slots)
+    frag = 64.0 * 16.0 * (KS / 64.0)
+    inflight = resident * W * 2.0 * c["unroll"] * (NB + (0.0 if c["x_lds"] else MB)) * frag
+    rate = min(cu_bw, inflight / lat)
+    t_cu = per_cu_wgs * per_wg / rate
+    t_hbm = N * K / hbm_bw
+    t = t0 + max(t_cu, t_hbm)
+    t += per_cu_wgs * wg_cost
+    t += mfma * per_cu_wgs * seg * NB * MB * (KS / 64.0) / max(1, min(W, 4))
+    t += reduce * (c["waves_k"] - 1) * NB * MB
+    if shared:
+        ns = partial_slots(fmt, N, K, c, ntiles)
+        t += sk_base + sk_slot * ns * 16.0 * NB * c["waves_n"] * 16.0 * MB * 4.0 / cu_bw
+    if c["x_lds"]:
+        t += xl_stage
+    if fused and fmt != "Block_FP8":
+        t += 2.0 * M * K / q_row_bw
+    if op == "linear" and c["quant_launch"]:
+        t += q_launch
+    return t
+
+
+# the constants compiled into csrc/w8_model.cpp (kParams); the fit starts here
+CURRENT = (1.6537, 56705.2, 1.0003, 4.54169e6, 2.608, 1.2018, 1.5197, 0.43, 0.1419, 0.0146,
+           0.051, 0.225973, 20816.5)
+
+
+def load(path):
+    """Timed rows of a collect CSV as numpy arrays, grouped by problem."""
+    import numpy as np
+    with open(path) as f:
+        rows = [r for r in csv.DictReader(f) if r["us"]]
+    d = {k: np.array([int(r[k]) for r in rows]) for k in ("M", "N", "K") + CFG_KEYS}
+    d["fmt"] = np.array([r["fmt"] for r in rows])
+    d["op"] = np.array([r["op"] for r in rows])
+    d["us"] = np.array([float(r["us"]) for r in rows])
+    key = np.array([f"{r['fmt']} {r['op']} {r['layout']} {r['M']}x{r['N']}x{r['K']}"
+                    for r in rows])
+    d["keys"], d["group"] = np.unique(key, return_inverse=True)
+    return d
+
+
+def predict_arrays(p, d):
+    """predict() over the arrays of load()."""
+    import numpy as np
+    (t0, cu_bw, lat, hbm_bw, slots, sk_base, sk_slot, xl_stage, wg_cost, mfma, reduce,
+     q_launch, q_row_bw) = p
+    KS = np.where(d["fmt"] == "W8A8_INT8", 64.0, 128.0)
+    T = np.ceil(d["K"] / KS)
+    MB, NB = (d["M"] + 15) // 16, d["tile_n"] // 16
+    wk, wn, S, grid, xl, ql = (d[k] for k in ("waves_k", "waves_n", "split_k", "grid", "x_lds",
+                                             "quant_launch"))
+    W = wk * wn
+    ntiles = np.ceil(d["N"] / (d["tile_n"] * wn))
+    G = np.where(grid > 0, grid, ntiles * S)
+    seg = np.where(grid > 0, np.ceil(ntiles * T / np.maximum(grid, 1)), np.ceil(T / S))
+    fused = (d["op"] == "linear") & (ql == 0)
+    abytes = np.where(xl > 0, 1.0, wn) * 16.0 * MB * seg * KS * np.where(fused, 2.0, 1.0)
+    shared = (S > 1) | (grid > 0)
+    tile_p = 16.0 * NB * wn * 16.0 * MB * 4.0
+    per_wg = 16.0 * NB * wn * seg * KS + abytes + np.where(shared, tile_p, 0.0)
+    pcw = np.ceil(G / 256.0)
+    inflight = (np.minimum(pcw, slots) * W * 2.0 * d["unroll"] *
+                (NB + np.where(xl > 0, 0.0, MB)) * 64.0 * 16.0 * (KS / 64.0))
+    t_cu = pcw * per_wg / np.minimum(cu_bw, inflight / lat)
+    t = t0 + np.maximum(t_cu, d["N"] * d["K"] / hbm_bw)
+    t = t + pcw * wg_cost + mfma * pcw * seg * NB * MB * (KS / 64.0) / np.clip(W, 1, 4)
+    t = t + reduce * (wk - 1) * NB * MB
+    lmin = np.maximum(ntiles * T // np.maximum(grid, 1), 1)
+    slots_n = np.where(grid > 0, np.where(T <= 1, 1, (T - 2) // lmin + 2), S)
+    t = t + np.where(shared, sk_base + sk_slot * slots_n * tile_p / cu_bw, 0.0)
+    t = t + np.where(xl > 0, xl_stage, 0.0)
+    t = t + np.where(fused & (d["fmt"] != "Block_FP8"), 2.0 * d["M"] * d["K"] / q_row_bw, 0.0)
+    t = t + np.where((d["op"] == "linear") & (ql > 0), q_launch, 0.0)
+    return t
+
+
+def evaluate(p, d, top_n):
+    """(geomean top-1 / best, geomean best-of-top-n / best, worst of the latter)."""
+    import numpy as np
+    pr = predict_arrays(p, d)
+    l1 = ln = 0.0
+    worst = 1.0
+    for g in range(len(d["keys"])):
+        ix = np.where(d["group"] == g)[0]
+        best = d["us"][ix].min()
+        o = ix[np.argsort(pr[ix], kind="stable")]
+        l1 += math.log(d["us"][o[0]] / best)
+        r = d["us"][o[:top_n]].min() / best
+        ln += math.log(r)
+        worst = max(worst, r)
+    n = len(d["keys"])
+    return math.exp(l1 / n), math.exp(ln / n), worst
+
+
+def fit(a):
+    """Nelder-Mead over the logs of the constants (all positive) from CURRENT,
+    minimizing the ranking loss -- log(top-1 / best) plus half of
+    log(best of the top 4 / best), averaged over problems -- plus 0.3 x the
+    squared log error of the predictions, weighted by (best / us)^4 so the
+    configs near the top of each problem count most."""
+    import numpy as np
+    from scipy.optimize import minimize
+    d = load(a.csv)
+    print(f"[fit] {len(d['keys'])} problems, {len(d['us'])} timed configs", flush=True)
+    groups = [np.where(d["group"] == g)[0] for g in range(len(d["keys"]))]
+    best = np.zeros(len(d["us"]))
+    for ix in groups:
+        best[ix] = d["us"][ix].min()
+    wt = (best / d["us"]) ** 4
+    free = [PARAM_NAMES.index(n) for n in (a.params.split(",") if a.params else PARAM_NAMES)]
+    base = np.log(np.array(CURRENT, dtype=float))
+
+    def unpack(x):
+        v = base.copy()
+        v[free] = x
+        return np.exp(v)
+
+    def objective(x):
+        p = unpack(x)
+        pr = predict_arrays(p, d)
+        reg = np.sum(wt * (np.log(pr) - np.log(d["us"])) ** 2) / np.sum(wt)
+        rank = 0.0
+        for ix in groups:
+            o = ix[np.argsort(pr[ix], kind="stable")[:4]]
+            b = d["us"][ix].min()
+            rank += math.log(d["us"][o[0]] / b) + 0.5 * math.log(d["us"][o].min() / b)
+        return rank / len(groups) + 0.3 * reg
+
+    x0 = base[free]
+    print(f"[fit] start: objective {objective(x0):.4f}; top-1, top-{a.top_n}, worst: "
+          f"{evaluate(unpack(x0), d, a.top_n)}", flush=True)
+    res = minimize(objective, x0, method="Nelder-Mead",
+                   options={"maxiter": a.maxiter, "xatol": 1e-4, "fatol": 1e-7})
+    p = unpack(res.x)
+    top1, topn, worst = evaluate(p, d, a.top_n)
+    print(f"[fit] objective {res.fun:.4f} after {res.nit} iterations", flush=True)
+    print(f"[fit] model top-1 vs measured best: geomean x{top1:.4f}; best of top-{a.top_n}: "
+          f"geomean x{topn:.4f}, worst x{worst:.4f}", flush=True)
+    print("constexpr ModelParams kParams = {" + ", ".join(f"{v:.6g}" for v in p) + "};",
+          flush=True)
+    return 0
+
+
+def bucket_eval(a):
+    """For shapes whose M has no table entry but whose floor(log2 M) bucket
+    has one: time the bucket's config, the model's pick and the tuned best."""
+    import bit_quantized_gemm_token_amd as w8
+    shapes = [tuple(int(v) for v in s.split(",")) for s in a.shapes.split(";") if s]
+    ratios = {"bucket": [], "model": []}
+    for fmt in a.formats.split(","):
+        for (M, N, K) in shapes:
+            cfg_b, src = w8.resolve_config(fmt, M, N, K, packed=True)
+            if src != 2:
+                print(f"[bucket] {fmt} {M}x{N}x{K}: no bucket entry, skipped", flush=True)
+                continue
+            cfg_m = w8.model_config(fmt, M, N, K, packed=True)
+            t_b, t_m = w8.profile_configs(fmt, M, N, K, [cfg_b, cfg_m], packed=True)
+            best, st = w8.tune_shape(fmt, M, N, K, packed=True, insert=False)
+            (t_t,) = w8.profile_configs(fmt, M, N, K, [best], packed=True)
+            ratios["bucket"].append(t_b / t_t)
+            ratios["model"].append(t_m / t_t)
+            print(f"[bucket] {fmt} {M}x{N}x{K}: bucket {t_b:.3f} us, model {t_m:.3f} us, "
+                  f"tuned {t_t:.3f} us", flush=True)
+    for k, v in ratios.items():
+        if v:
+            print(f"[bucket] {k} / tuned: geomean x{math.exp(sum(map(math.log, v)) / len(v)):.4f}"
+                  f", worst x{max(v):.4f} over {len(v)} shapes", flush=True)
+    return 0
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser()
+    sub = p.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("collect")
+    c.add_argument("--out", required=True)
+    c.add_argument("--formats", default="FP8_Dynamic,W8A8_INT8,Block_FP8")
+    c.add_argument("--layouts", default="packed")
+    c.add_argument("--ops", default="gemm")
+    c.add_argument("--shapes", default=None)
+    c.add_argument("--replays", type=int, default=3)
+    c.add_argument("--rotate-mib", type=int, default=256)
+    c.add_argument("--time-budget-s", type=float, default=0.0)
+    f = sub.add_parser("fit")
+    f.add_argument("csv")
+    f.add_argument("--top-n", type=int, default=16)
+    f.add_argument("--maxiter", type=int, default=3000)
+    f.add_argument("--params", default=None,
+                   help="comma-separated constants to fit (default: all)")
+    b = sub.add_parser("bucket-eval")
+    b.add_argument("--formats", default="FP8_Dynamic,W8A8_INT8,Block_FP8")
+    b.add_argument("--shapes", required=True)
+    a = p.parse_args(argv)
+    if a.cmd == "collect":
+        sys.path.insert(0, ROOT)
+        return collect(a)
+    if a.cmd == "bucket-eval":
+        return bucket_eval(a)
+    return fit(a)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -2,7 +2,7 @@
 
     python -m bit_quantized_gemm_token_amd.tune_sweep --out TABLE [--formats ...]
            [--ops gemm,linear] [--layouts row,packed] [--shapes M,N,K;M,N,K...]
-           [--no-resume] [--max-split-k 256]
+           [--no-resume] [--max-split-k 256] [--top-n N]
 
 Default shapes: the 24-shape M <= 32 sweep of synthetic.SWEEP plus the shapes
 the tests and benchmarks name (N=K=4096 at M in {1, 4, 16, 32}; N=4608,
@@ -51,6 +51,8 @@ def main(argv=None):
     p.add_argument("--rotate-mib", type=int, default=512)
     p.add_argument("--replays", type=int, default=5)
     p.add_argument("--stream-k", action="store_true", help="also try stream-K grids")
+    p.add_argument("--top-n", type=int, default=0,
+                   help="time only the cost model's top N candidates (0 = all)")
     p.add_argument("--time-budget-s", type=float, default=0.0,
                    help="stop starting new shapes after this many seconds (0 = no limit)")
     a = p.parse_args(argv)
@@ -76,7 +78,7 @@ def main(argv=None):
             return 0
         best, st = w8.tune_shape(fmt, M, N, K, rotate_bytes=a.rotate_mib << 20,
                                  replays=a.replays, max_split_k=a.max_split_k, insert=True,
-                                 packed=packed, stream_k=a.stream_k, op=op)
+                                 packed=packed, stream_k=a.stream_k, op=op, top_n=a.top_n)
         w8.save_config_table(a.out)
         done += 1
         print(f"[tune] {op} {fmt} {'packed' if packed else 'row'} {M}x{N}x{K}: {best} "

@@ -161,7 +161,8 @@ typedef struct {
     int32_t stream_k;         /* 1: also try stream-K grids (default 0: on the
                                  shapes measured so far they never won) */
     int32_t op;               /* w8_op tuned (default W8_OP_GEMM) */
-    int32_t reserved[1];
+    int32_t top_n;            /* > 0: time only the top_n candidates of the cost
+                                 model's ranking (w8_rank_configs); 0: all */
 } w8_tune_opts;
 
 typedef struct {
@@ -246,8 +247,9 @@ w8_status w8_workspace_size(w8_fmt fmt, w8_op op, int M, int N, int K, int packe
  *           with ldw = 0, in the packed layout; scales in the layout given
  *           above for fmt
  *   y       bf16 [M, N], row stride ldy elements (device)
- *   cfg     kernel configuration; NULL = the config table entry for
- *           (fmt, weight layout, M, N, K) on this device, else the default
+ *   cfg     kernel configuration; NULL = w8_resolve_config's pick for
+ *           (fmt, weight layout, M, N, K): table entry, M-bucket entry or
+ *           the cost model's pick
  *   ws      workspace of at least w8_workspace_size() bytes, zero-filled
  *           before its first use; every completed call leaves its counters
  *           at zero again.  May be NULL when the size is 0.  Calls that share
@@ -282,9 +284,8 @@ w8_status w8_gemm_w8a8_acc(w8_fmt fmt, int M, int N, int K,
  *   x       bf16 [M, K], row stride ldx elements (device), 16-byte aligned,
  *           ldx % 8 == 0
  *   wq, sw, y, ws, stream  as for w8_gemm_w8a8
- *   cfg     NULL = the table entry for (fmt, W8_OP_LINEAR, weight layout,
- *           M, N, K), else the default linear config (w8_default_config
- *           with W8_OP_LINEAR).  With quant_launch == 1 the call makes two
+ *   cfg     NULL = w8_resolve_config's pick for (fmt, W8_OP_LINEAR, weight
+ *           layout, M, N, K).  With quant_launch == 1 the call makes two
  *           launches instead: w8_quantize_act's kernel into the workspace,
  *           then the GEMM (same Y).  Both forms allocate nothing.          */
 w8_status w8_linear(w8_fmt fmt, int M, int N, int K, const void *x, int64_t ldx,
@@ -297,14 +298,24 @@ w8_status w8_linear(w8_fmt fmt, int M, int N, int K, const void *x, int64_t ldx,
  * else W8_E_INVALID (with the reason in w8_last_error()).                   */
 w8_status w8_validate_config(w8_fmt fmt, w8_op op, int M, int N, int K, const w8_cfg *cfg);
 
-/* The built-in default configuration of op for (fmt, M, N, K) (paragraph 7
- * of the page: a default config serves untuned shapes).                    */
+/* The built-in rule-of-thumb configuration of op for (fmt, M, N, K): fixed
+ * tile and waves, Swap-AB below 32 tokens, the smallest split_k that fills
+ * the machine (paragraph 7 of the page: a default config serves untuned
+ * shapes).  The tuner validates every candidate against its output.       */
 w8_status w8_default_config(w8_fmt fmt, w8_op op, int M, int N, int K, w8_cfg *out);
 
+/* The cost model's pick (the top-1 of w8_rank_configs with the default
+ * options for op and layout): what an untuned shape runs
+ * (flashinfer-ai/flashinfer pull 3948: a heuristic top-1 without tuning). */
+w8_status w8_model_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed, w8_cfg *out);
+
 /* The config op uses when called with cfg == NULL for weights in the given
- * layout (packed = 0 row-major, 1 packed): the table entry for (this
- * device's arch, W8_ABI_VERSION, fmt, op, layout, M, N, K) if present, else
- * the default.  *from_table is set to 1 on a table hit, 0 otherwise.        */
+ * layout (packed = 0 row-major, 1 packed), looked up for this device's arch
+ * and W8_ABI_VERSION: the table entry for (fmt, op, layout, M, N, K)
+ * (*from_table = 1); else the entry for the same (fmt, op, layout, N, K)
+ * whose M is nearest in the same floor(log2 M) bucket (the larger on a tie)
+ * and whose config is valid for M (*from_table = 2); else the cost model's
+ * pick, w8_model_config (*from_table = 0).                                 */
 w8_status w8_resolve_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed,
                             w8_cfg *out, int *from_table);
 
@@ -340,14 +351,17 @@ w8_status w8_lookup_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed
  * compares configurations and keeps the best for each shape).  Tunes one
  * operation (opts->op) for one weight layout (opts->packed).  Allocates its
  * own inputs (random codes, bf16 activations for W8_OP_LINEAR, and scales),
- * enumerates the configs of the family (W8_OP_LINEAR: those with x_lds and
- * waves_k <= 4)
+ * enumerates the configs of the family (W8_OP_LINEAR: the fused ones, with
+ * x_lds and waves_k <= 4, plus quant_launch = 1 with the GEMM's config for
+ * the shape and layout -- table entry or model pick -- and with the GEMM's
+ * default, so tune the GEMM first)
  * (tile_n x (waves_k or waves_n) x x_lds x unroll x (split_k in {1, 2, ...,
  * max_split_k}, or with opts->stream_k a stream-K grid in {256, 512, 1024})
  * x swap_ab) minus those that cannot pay off or duplicate another (fewer
  * than one K-step per wave, unroll above the K-steps per wave, partials
- * above twice the weight bytes, fewer than min(256, most possible) waves),
- * checks each
+ * above twice the weight bytes, fewer than min(256, most possible) waves);
+ * with opts->top_n > 0 only the top_n of the cost model's ranking remain
+ * (w8_rank_configs).  It checks each
  * against the default GEMM config's output (for W8_OP_LINEAR after the
  * standalone quantizer; bit-equal for W8A8_INT8, within 1e-2 relative for
  * the FP8 formats) and times it as HIP graph replays over
@@ -358,6 +372,28 @@ w8_status w8_lookup_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed
 w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tune_opts *opts,
                         w8_cfg *best, w8_tune_stats *stats);
 void w8_tune_default_opts(w8_tune_opts *opts);
+
+/* The tuner's candidate set for (fmt, M, N, K) under opts (op, packed,
+ * max_split_k, stream_k; top_n is ignored), ranked by the cost model's
+ * predicted us per call, ascending.  The model (flashinfer-ai/flashinfer
+ * pull 3948: score every feasible tactic, profile only the top-N) charges a
+ * fixed launch cost, the busiest compute unit's vector-memory bytes at a
+ * Little's-law rate (bytes in flight over load latency, capped), the HBM
+ * time of the weights (overlapped), and the reduction chain, LDS staging and
+ * quantization costs, with constants fitted to measured timings.  Writes up
+ * to cap configs (and their predictions when predicted_us is not NULL) and
+ * the set's size in *count.  Host only: no device call.                    */
+w8_status w8_rank_configs(w8_fmt fmt, int M, int N, int K, const w8_tune_opts *opts,
+                          w8_cfg *out, double *predicted_us, int cap, int *count);
+
+/* Times n configs of opts->op with the tuner's harness (same inputs,
+ * validation against the default GEMM config, median us per call of graph
+ * replays over rotating weight copies; bank 1 only, nothing inserted):
+ * valid[i] = 1 and us[i] the time, or valid[i] = 0 and us[i] = 0 for a
+ * config whose output failed validation.  Allocates and synchronizes, like
+ * w8_tune_shape.                                                           */
+w8_status w8_profile_configs(w8_fmt fmt, int M, int N, int K, const w8_tune_opts *opts,
+                             const w8_cfg *cfgs, int n, double *us, int *valid);
 
 #ifdef __cplusplus
 }

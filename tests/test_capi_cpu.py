@@ -322,10 +322,10 @@ def test_table_roundtrip_and_lookup(w8, tmp_path):
     assert w8.lookup_config("Block_FP8", 32, 4608, 7168, packed=True, with_time=True) == (c2, 5.5)
     got, hit = w8.resolve_config("Block_FP8", 32, 4608, 7168, packed=True)
     assert hit and got == c2
-    got, hit = w8.resolve_config("Block_FP8", 32, 4608, 7168)       # other layout -> default
-    assert not hit and got == w8.default_config("Block_FP8", 32, 4608, 7168)
-    got, hit = w8.resolve_config("Block_FP8", 16, 4608, 7168)       # miss -> default
-    assert not hit and got == w8.default_config("Block_FP8", 16, 4608, 7168)
+    got, hit = w8.resolve_config("Block_FP8", 32, 4608, 7168)       # other layout -> model
+    assert hit == 0 and got == w8.model_config("Block_FP8", 32, 4608, 7168)
+    got, hit = w8.resolve_config("Block_FP8", 16, 4608, 7168)       # other bucket -> model
+    assert hit == 0 and got == w8.model_config("Block_FP8", 16, 4608, 7168)
     assert w8.best_layout("Block_FP8", 32, 4608, 7168) is True
     assert w8.best_layout("FP8_Dynamic", 4, 4096, 4096) is False
     # the fused linear op has entries of its own
@@ -334,9 +334,9 @@ def test_table_roundtrip_and_lookup(w8, tmp_path):
     assert w8.lookup_config("Block_FP8", 32, 4608, 7168, packed=True, op="linear") == c3
     assert w8.lookup_config("Block_FP8", 32, 4608, 7168, packed=True) == c2
     got, hit = w8.resolve_config("Block_FP8", 32, 4608, 7168, packed=True, op="linear")
-    assert hit and got == c3
+    assert hit == 1 and got == c3
     got, hit = w8.resolve_config("Block_FP8", 32, 4608, 7168, op="linear")
-    assert not hit and got == w8.default_config("Block_FP8", 32, 4608, 7168, op="linear")
+    assert hit == 0 and got == w8.model_config("Block_FP8", 32, 4608, 7168, op="linear")
     with pytest.raises(w8.W8Error):                                  # a GEMM config is no linear one
         w8.set_config("Block_FP8", 32, 4608, 7168, c2, 5.5, packed=True, op="linear")
     p = tmp_path / "t.tbl"
@@ -349,6 +349,55 @@ def test_table_roundtrip_and_lookup(w8, tmp_path):
     assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096) == c1
     assert w8.lookup_config("Block_FP8", 32, 4608, 7168, packed=True) == c2
     assert w8.lookup_config("Block_FP8", 32, 4608, 7168, packed=True, op="linear") == c3
+
+
+def test_m_bucket_fallback(w8):
+    """A miss takes the entry of the nearest M in the same floor(log2 M)
+    bucket (the larger on a tie) if its config is valid for this M, else the
+    cost model's pick."""
+    N, K = 4096, 4096
+    c4 = w8.Config.make(tile_n=32, waves_k=2, unroll=2, split_k=4, swap_ab=1)
+    c6 = w8.Config.make(tile_n=16, waves_k=8, unroll=1, split_k=2)
+    c16 = w8.Config.make(tile_n=16, waves_k=1, waves_n=8, unroll=1, split_k=2, x_lds=1)
+    w8.set_config("FP8_Dynamic", 4, N, K, c4, 3.0)
+    w8.set_config("FP8_Dynamic", 6, N, K, c6, 3.0)
+    w8.set_config("FP8_Dynamic", 16, N, K, c16, 3.0)
+    assert w8.resolve_config("FP8_Dynamic", 5, N, K) == (c6, 2)    # 5: 4 and 6 tie, larger wins
+    assert w8.resolve_config("FP8_Dynamic", 7, N, K) == (c6, 2)
+    assert w8.resolve_config("FP8_Dynamic", 4, N, K) == (c4, 1)
+    assert w8.resolve_config("FP8_Dynamic", 31, N, K) == (c16, 2)  # bucket 16..31
+    assert w8.resolve_config("FP8_Dynamic", 8, N, K) == (w8.model_config("FP8_Dynamic", 8, N, K), 0)
+    assert w8.resolve_config("FP8_Dynamic", 32, N, K)[1] == 0      # 32 is a bucket of its own
+    assert w8.resolve_config("FP8_Dynamic", 5, N, K, packed=True)[1] == 0
+    assert w8.resolve_config("FP8_Dynamic", 5, N, K, op="linear")[1] == 0
+    # an entry whose config does not fit this M is skipped: x_lds with the
+    # whole K = 4096 of one 16-row block (64 KiB) in LDS fits M = 16; two
+    # blocks (M = 17) do not
+    big = w8.Config.make(tile_n=16, waves_k=1, waves_n=2, unroll=1, split_k=1, x_lds=1)
+    w8.set_config("W8A8_INT8", 16, 512, 4096, big, 2.0)
+    w8.validate_config("W8A8_INT8", 16, 512, 4096, big)
+    assert not _valid(w8, "W8A8_INT8", 17, 512, 4096, big)
+    assert w8.resolve_config("W8A8_INT8", 17, 512, 4096)[1] == 0
+
+
+def test_model_ranking(w8):
+    """The ranked list is the tuner's candidate set, sorted by predicted
+    time; its head is the model's pick; every entry is valid; top_n prunes."""
+    for fmt, M, N, K, op in (("FP8_Dynamic", 1, 4096, 4096, "gemm"),
+                             ("Block_FP8", 32, 4608, 7168, "gemm"),
+                             ("W8A8_INT8", 16, 896, 1024, "linear")):
+        r = w8.rank_configs(fmt, M, N, K, op=op)
+        assert len(r) > 20
+        us = [u for u, _ in r]
+        assert us == sorted(us) and us[0] > 0
+        for _, c in r[:50]:
+            w8.validate_config(fmt, M, N, K, c, op=op)
+        assert r[0][1] == w8.model_config(fmt, M, N, K, op=op)
+        if op == "linear":
+            assert any(c.quant_launch == 1 for _, c in r)
+            assert any(c.quant_launch == 0 for _, c in r)
+        else:
+            assert all(c.quant_launch == 0 for _, c in r)
 
 
 def test_table_malformed_keeps_old_table(w8, tmp_path):
@@ -435,3 +484,16 @@ def test_env_table_loaded_by_the_c_library_alone(tmp_path):
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                          check=True).stdout.split()
     assert out == ["0", "8", "32"]
+
+
+def test_model_mirror_matches_library(w8):
+    """fit_model.predict with the compiled constants reproduces the library's
+    predictions term by term (the fit tunes the same model it ships)."""
+    from bit_quantized_gemm_token_amd import fit_model as fm
+    for fmt, M, N, K, op in (("FP8_Dynamic", 1, 4096, 4096, "gemm"),
+                             ("W8A8_INT8", 32, 896, 1040, "gemm"),
+                             ("Block_FP8", 17, 4608, 7168, "linear"),
+                             ("FP8_Dynamic", 8, 512, 7168, "linear")):
+        for us, c in w8.rank_configs(fmt, M, N, K, op=op, stream_k=True):
+            want = fm.predict(fm.CURRENT, fmt, op, M, N, K, c.as_dict())
+            assert abs(us - want) <= 1e-9 * want, (fmt, M, N, K, op, c, us, want)
