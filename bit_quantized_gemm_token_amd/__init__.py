@@ -33,7 +33,8 @@ __all__ = ["Config", "W8Error", "UnsupportedShape", "Workspace", "PackedWeight",
            "validate_config", "default_config", "resolve_config", "lookup_config",
            "set_config", "load_config_table", "save_config_table", "clear_config_table",
            "config_table_size", "config_table_foreign", "tune_shape", "rank_configs",
-           "profile_configs", "model_config", "FORMATS", "MAX_M",
+           "profile_configs", "model_config", "moe_gemm", "moe_config", "moe_workspace_size",
+           "pack_experts", "PackedExperts", "FORMATS", "MAX_M",
            "MAX_SPLIT_K", "GROUP", "ABI_VERSION"]
 
 
@@ -310,6 +311,94 @@ def linear(fmt, x, wq, sw, cfg=None, y=None, workspace=None, stream=None, fused=
     _check(_lib.w8_linear(f, M, N, K, _dev_ptr(x, "x"), ldx, wptr, ldw,
                           _dev_ptr(sw, "sw", torch.float32), _dev_ptr(y, "y"), _row_major(y, "y"),
                           _cfg_ptr(cfg), ws_ptr, ws_bytes, _stream(stream, x.device)))
+    return y
+
+
+# ---------------------------------------------------------------------- MoE --
+class PackedExperts:
+    """Every expert's weight codes in the packed layout, one expert per row of
+    the 2-D uint8 device buffer `data` [E, packed_weight_size(fmt, N, K)]."""
+
+    def __init__(self, fmt, N, K, data):
+        self.fmt, self.N, self.K, self.data = _fmt(fmt), int(N), int(K), data
+        self.E = data.shape[0]
+        self.device = data.device
+
+
+def pack_experts(fmt, wq, stream=None):
+    """Pack row-major expert codes [E, N, K] (offline, on the GPU)."""
+    f = _fmt(fmt)
+    E, N, K = wq.shape
+    out = torch.empty((E, packed_weight_size(f, N, K)), dtype=torch.uint8, device=wq.device)
+    for e in range(E):
+        w = wq[e]
+        _check(_lib.w8_pack_weight(f, N, K, _dev_ptr(w, "wq"), _row_major(w, "wq"),
+                                   _dev_ptr(out[e], "out"), _stream(stream, wq.device)))
+    return PackedExperts(f, N, K, out)
+
+
+def _experts(f, wq):
+    """(E, N, K, ldw, w_stride, pointer, packed) of [E, N, K] codes or PackedExperts."""
+    if isinstance(wq, PackedExperts):
+        if wq.fmt != f:
+            raise ValueError("experts were packed for another format")
+        return wq.E, wq.N, wq.K, 0, wq.data.stride(0), _dev_ptr(wq.data, "wq"), True
+    if wq.dim() != 3 or wq.element_size() != 1 or wq.stride(2) != 1:
+        raise ValueError("wq must be [E, N, K] 1-byte codes with unit inner stride")
+    E, N, K = wq.shape
+    return E, N, K, wq.stride(1), wq.stride(0), _dev_ptr(wq, "wq"), False
+
+
+def moe_config(fmt, E, T, N, K, max_m=32, packed=False):
+    """The config moe_gemm uses when cfg is None."""
+    c = Config()
+    _check(_lib.w8_moe_config(_fmt(fmt), E, T, N, K, max_m, int(bool(packed)), ctypes.byref(c)))
+    return c
+
+
+def moe_workspace_size(fmt, E, T, N, K, max_m=32, cfg=None, packed=False):
+    n = ctypes.c_size_t(0)
+    _check(_lib.w8_moe_workspace_size(_fmt(fmt), E, T, N, K, max_m, int(bool(packed)),
+                                      _cfg_ptr(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def moe_gemm(fmt, xq, sx, offsets, rows, wq, sw, max_m=32, cfg=None, y=None, workspace=None,
+             stream=None):
+    """MoE grouped GEMM: for routed entry i of expert e (offsets[e] <= i <
+    offsets[e+1]), Y[i] = dequant(xq[rows[i]]) . dequant(Wq_e)^T, bf16
+    [len(rows), N].  xq, sx: the T quantized token rows (quantize_act);
+    offsets int32 [E + 1], rows int32 (device); wq: [E, N, K] codes or
+    PackedExperts; sw: [E, ...] scales in the format's per-expert layout;
+    every expert's count <= max_m <= 32.  One launch, no host sync."""
+    f = _fmt(fmt)
+    ldq = _row_major(xq, "xq") * xq.element_size()
+    T, K = xq.shape
+    E, N, wk, ldw, w_stride, wptr, packed = _experts(f, wq)
+    if wk != K:
+        raise ValueError(f"K mismatch: xq {tuple(xq.shape)} vs experts' K {wk}")
+    if offsets.numel() != E + 1:
+        raise ValueError("offsets must hold E + 1 entries")
+    if sw.shape[0] != E or not sw.is_contiguous():
+        raise ValueError("sw must be a contiguous [E, ...] tensor")
+    if y is None:
+        y = torch.empty((rows.numel(), N), dtype=torch.bfloat16, device=xq.device)
+    elif y.dtype != torch.bfloat16:
+        raise TypeError("y must be bfloat16")
+    if workspace is None:
+        workspace = _default_workspace(xq.device)
+    need = moe_workspace_size(f, E, T, N, K, max_m, cfg, packed)
+    ws_ptr, ws_bytes = (None, 0)
+    if need:
+        buf = workspace.reserve(need)
+        ws_ptr, ws_bytes = ctypes.c_void_p(buf.data_ptr()), buf.numel()
+    _check(_lib.w8_moe_gemm(f, E, T, N, K, max_m, _dev_ptr(xq, "xq"), ldq,
+                            _dev_ptr(sx, "sx", torch.float32),
+                            _dev_ptr(offsets, "offsets", torch.int32),
+                            _dev_ptr(rows, "rows", torch.int32), wptr, ldw, w_stride,
+                            _dev_ptr(sw, "sw", torch.float32), sw.stride(0),
+                            _dev_ptr(y, "y"), _row_major(y, "y"), _cfg_ptr(cfg), ws_ptr, ws_bytes,
+                            _stream(stream, xq.device)))
     return y
 
 

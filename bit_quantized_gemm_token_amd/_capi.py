@@ -26,7 +26,8 @@ EXPORTS = ("w8_abi_version", "w8_status_string", "w8_last_error", "w8_quantize_a
            "w8_load_config_table", "w8_save_config_table", "w8_clear_config_table",
            "w8_config_table_size", "w8_config_table_foreign", "w8_set_config",
            "w8_lookup_config", "w8_tune_shape", "w8_tune_default_opts", "w8_model_config",
-           "w8_rank_configs", "w8_profile_configs")
+           "w8_rank_configs", "w8_profile_configs", "w8_moe_gemm", "w8_moe_workspace_size",
+           "w8_moe_validate_config", "w8_moe_config")
 
 
 class Config(ctypes.Structure):
@@ -145,4 +146,14 @@ def load():
     lib.w8_profile_configs.argtypes = [c_int, c_int, c_int, c_int, ctypes.POINTER(TuneOpts),
                                        cfgp, c_int, dp, ctypes.POINTER(c_int)]
     lib.w8_profile_configs.restype = st
+    lib.w8_moe_gemm.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, vp, i64, f32p, vp, vp,
+                                vp, i64, i64, f32p, i64, vp, i64, cfgp, vp, ctypes.c_size_t, vp]
+    lib.w8_moe_gemm.restype = st
+    lib.w8_moe_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, cfgp,
+                                          ctypes.POINTER(ctypes.c_size_t)]
+    lib.w8_moe_workspace_size.restype = st
+    lib.w8_moe_validate_config.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, cfgp]
+    lib.w8_moe_validate_config.restype = st
+    lib.w8_moe_config.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, cfgp]
+    lib.w8_moe_config.restype = st
     return lib

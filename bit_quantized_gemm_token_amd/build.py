@@ -37,6 +37,7 @@ def _units():
              ("w8_capi.cpp", ["-x", "hip"], "w8_capi.o"),
              ("w8_table.cpp", ["-x", "hip"], "w8_table.o"),
              ("w8_model.cpp", ["-x", "hip"], "w8_model.o"),
+             ("w8_moe.cpp", ["-x", "hip"], "w8_moe.o"),
              ("w8_registry.cpp", ["-x", "hip"], "w8_registry.o")]
     for fmt in (0, 1, 2):
         for swap in (0, 1):

@@ -148,14 +148,27 @@ __device__ __forceinline__ typename Traits<FMT>::Acc mma(typename Traits<FMT>::F
   }
 }
 
-template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL>
-__global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
+// The body of one GEMM workgroup.  GROUPED (the MoE grouped GEMM): activation
+// row m of this call is row xrows[m] (clamped to [0, xrow_max]) of the
+// activation codes and scales; everything else is per call in `a`.
+template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL,
+          bool GROUPED>
+__device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xrows,
+                                          int xrow_max) {
   typedef typename Traits<FMT>::Frag Frag;
   typedef typename Traits<FMT>::Acc Acc;
   constexpr int KSTEP = Traits<FMT>::KSTEP;
   constexpr bool BLOCK = (FMT == BLOCK_FP8);
   static_assert(WN == 1 || WK == 1, "the waves of a workgroup split either K or N");
   static_assert(WN == 1 || XL, "waves side by side along N share activations through LDS");
+  static_assert(!GROUPED || XL != 2, "the grouped GEMM takes quantized activations");
+  // activation row (codes and scales) of row m of this call
+  auto xr = [&](int m) -> long long {
+    if constexpr (GROUPED)
+      return min(max(xrows[m], 0), xrow_max);
+    else
+      return m;
+  };
   // XL: the segment's activation fragments are staged in LDS up front, one
   // 1 KiB chunk (16 bytes per lane) per (K-step, M block, 16-byte load):
   // chunk ((k - ka) * MB + b) * CH + jj.  XL == 1 copies the codes; XL == 2
@@ -172,7 +185,7 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
   // a clamped valid row; their outputs are never stored).
   const uint8_t* xrow[MB];
 #pragma unroll
-  for (int b = 0; b < MB; ++b) xrow[b] = a.xq + (long long)min(16 * b + r, a.M - 1) * a.ldq + 16 * g;
+  for (int b = 0; b < MB; ++b) xrow[b] = a.xq + xr(min(16 * b + r, a.M - 1)) * a.ldq + 16 * g;
 
   // Block_FP8 sx rows of the accumulator elements this lane holds (SWAP: one
   // m per lane; else four), and the per-token formats' epilogue sx, loaded
@@ -203,11 +216,11 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
       const int m = min(SWAP ? 16 * b + r : 16 * b + 4 * g + i, a.M - 1);
       sxm[b][i] = m;
       if constexpr (BLOCK) {
-        sxrow[b][i] = XL == 2 ? nullptr : a.sx + (long long)m * a.sgroups;
+        sxrow[b][i] = XL == 2 ? nullptr : a.sx + xr(m) * a.sgroups;
         ep_sx[b][i] = 0.0f;
       } else {
         sxrow[b][i] = nullptr;
-        ep_sx[b][i] = XL == 2 ? 0.0f : a.sx[m];  // XL == 2: set once the row scales exist
+        ep_sx[b][i] = XL == 2 ? 0.0f : a.sx[xr(m)];  // XL == 2: set once the row scales exist
       }
     }
 
@@ -354,7 +367,7 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
       const int nchunks = (min(kb, a.kfull) - ka) * MB * CH;
       for (int c = wave; c < nchunks; c += WK * WN) {
         const int kk = c / (MB * CH), b = (c / CH) % MB, jj = c % CH;
-        const uint8_t* src = a.xq + (long long)min(16 * b + r, a.M - 1) * a.ldq + 16 * g +
+        const uint8_t* src = a.xq + xr(min(16 * b + r, a.M - 1)) * a.ldq + 16 * g +
                              (long long)(ka + kk) * KSTEP + 64 * jj;
         __builtin_amdgcn_global_load_lds(
             src, (__attribute__((address_space(3))) void*)(xl + c * 64), 16, 0, 0);
@@ -703,8 +716,42 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
 }
 
 template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL>
+__global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
+  gemm_body<FMT, MB, NB, WK, WN, U, SWAP, PACKED, XL, false>(a, nullptr, 0);
+}
+
+// MoE grouped GEMM: blockIdx.y is the expert; its rows are entries
+// [offsets[e], offsets[e+1]) of the routing (at most 16 * MB of them are
+// computed), its weights, weight scales and shared-tile workspace are at the
+// expert's strides, and its outputs are rows offsets[e].. of Y.
+template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL>
+__global__ __launch_bounds__(64 * WK * WN) void moe_gemm_kernel(GemmArgs a, MoeArgs m) {
+  const int e = blockIdx.y;
+  const int off = m.offsets[e];
+  const int rows = min(m.offsets[e + 1] - off, 16 * MB);
+  if (rows <= 0) return;  // an expert no token was routed to
+  a.M = rows;
+  a.wq += e * m.w_stride;
+  a.sw += e * m.sw_stride;
+  a.out = static_cast<char*>(a.out) + (long long)off * a.ldo * (a.out_mode ? 4 : 2);
+  if (a.counters) {
+    a.counters += (long long)e * a.ntiles * kCounterWords;
+    a.part = static_cast<char*>(a.part) + e * m.part_stride;
+  }
+  gemm_body<FMT, MB, NB, WK, WN, U, SWAP, PACKED, XL, true>(a, m.rows + off, m.xrow_max);
+}
+
+template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL>
 hipError_t launch_gemm(const GemmArgs& a, dim3 grid, dim3 block, hipStream_t s) {
   hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, WK, WN, U, SWAP, PACKED, XL>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL>
+hipError_t launch_moe_gemm(const GemmArgs& a, const MoeArgs& m, dim3 grid, dim3 block,
+                           hipStream_t s) {
+  hipLaunchKernelGGL((moe_gemm_kernel<FMT, MB, NB, WK, WN, U, SWAP, PACKED, XL>), grid, block, 0,
+                     s, a, m);
   return hipGetLastError();
 }
 

@@ -32,13 +32,33 @@
   W8_U(MB, 1, 1, 2) W8_U(MB, 2, 1, 2) W8_U(MB, 4, 1, 2) W8_U(MB, 1, 2, 2)             \
   W8_U(MB, 1, 4, 2) W8_U(MB, 1, 8, 2)
 
+// The MoE grouped GEMM: the same (MB, NB, UNROLL, PACKED) and (WK, WN, XL) in
+// {(1, 1, 0), (2, 1, 0), (4, 1, 0), (8, 1, 0), (1, 2, 1), (1, 4, 1), (1, 8, 1)}.
+#define W8_MOE_TABLE_FN W8_CAT(moe_instances_f, W8_FMT, W8_SWAP)
+#define W8_MI(MB, NB, WK, WN, U, P, XL)                                      \
+  {W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL,                                 \
+   &launch_moe_gemm<W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL>},
+#define W8_MP(MB, NB, WK, WN, U, XL) W8_MI(MB, NB, WK, WN, U, 0, XL) W8_MI(MB, NB, WK, WN, U, 1, XL)
+#define W8_MU(MB, WK, WN, XL)                                                          \
+  W8_MP(MB, 1, WK, WN, 1, XL) W8_MP(MB, 1, WK, WN, 2, XL) W8_MP(MB, 1, WK, WN, 4, XL) \
+  W8_MP(MB, 2, WK, WN, 1, XL) W8_MP(MB, 2, WK, WN, 2, XL) W8_MP(MB, 4, WK, WN, 1, XL)
+#define W8_MW(MB)                                                                      \
+  W8_MU(MB, 1, 1, 0) W8_MU(MB, 2, 1, 0) W8_MU(MB, 4, 1, 0) W8_MU(MB, 8, 1, 0)         \
+  W8_MU(MB, 1, 2, 1) W8_MU(MB, 1, 4, 1) W8_MU(MB, 1, 8, 1)
+
 namespace w8 {
 
 static const GemmInstance kInstances[] = {W8_W(1) W8_W(2)};
+static const MoeInstance kMoeInstances[] = {W8_MW(1) W8_MW(2)};
 
 const GemmInstance* W8_TABLE_FN(int* count) {
   *count = (int)(sizeof(kInstances) / sizeof(kInstances[0]));
   return kInstances;
+}
+
+const MoeInstance* W8_MOE_TABLE_FN(int* count) {
+  *count = (int)(sizeof(kMoeInstances) / sizeof(kMoeInstances[0]));
+  return kMoeInstances;
 }
 
 }  // namespace w8

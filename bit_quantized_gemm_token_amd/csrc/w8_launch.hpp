@@ -61,6 +61,24 @@ struct GemmInstance {
   GemmLaunchFn fn;
 };
 
+// MoE grouped GEMM: per-expert routing and strides (grid.y = experts).
+struct MoeArgs {
+  const int* offsets;      // [E + 1] routing offsets, ascending (device)
+  const int* rows;         // [offsets[E]] activation row of each routed entry (device)
+  long long w_stride;      // bytes between two experts' weights
+  long long sw_stride;     // floats between two experts' weight scales
+  long long part_stride;   // bytes between two experts' partials in the workspace
+  int xrow_max;            // activation rows - 1 (row ids are clamped to [0, xrow_max])
+};
+
+typedef hipError_t (*MoeLaunchFn)(const GemmArgs&, const MoeArgs&, dim3 grid, dim3 block,
+                                  hipStream_t);
+
+struct MoeInstance {
+  int fmt, mb, nb, wk, wn, unroll, swap, packed, xl;
+  MoeLaunchFn fn;
+};
+
 // Packs row-major weight codes into the MFMA-native layout of fmt.
 hipError_t launch_pack_weight(int fmt, const uint8_t* w, long long ldw, int N, int K,
                               uint8_t* out, hipStream_t s);
@@ -71,6 +89,7 @@ inline size_t packed_weight_bytes(int fmt, int N, int K) {
 
 // Every compiled instance, gathered from the per-format translation units.
 const GemmInstance* gemm_instances(int* count);
+const MoeInstance* moe_instances(int* count);
 
 // K-step (bytes of K per MFMA) of each format.
 inline int kstep_of(int fmt) { return fmt == 1 ? 64 : 128; }

@@ -1,0 +1,233 @@
+// C-ABI of the MoE grouped GEMM (ai-radar.it, "Helion nel backend vLLM",
+// paragraph 9: MoE models, whose MoE backend becomes the main optimization
+// target, are the work's next stated goal).  One launch covers every expert:
+// grid.y is the expert, and each expert runs the GEMM family's kernel on the
+// token rows routed to it (gathered through a row-index list), its own
+// weights and weight scales, and its own shared-tile workspace.
+#include <algorithm>
+#include <cstring>
+#include <string>
+
+#include "w8_internal.hpp"
+
+namespace w8 {
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+int nb_index(int nb) { return nb == 1 ? 0 : nb == 2 ? 1 : nb == 4 ? 2 : -1; }
+int wk_index(int wk) {
+  return wk == 1 ? 0 : wk == 2 ? 1 : wk == 4 ? 2 : wk == 8 ? 3 : wk == 16 ? 4 : -1;
+}
+int wn_index(int wn) { return wn == 1 ? 0 : wn == 2 ? 1 : wn == 4 ? 2 : wn == 8 ? 3 : -1; }
+int u_index(int u) { return u == 1 ? 0 : u == 2 ? 1 : u == 4 ? 2 : -1; }
+
+struct MoeIndex {
+  MoeLaunchFn fn[3][2][3][5][4][3][2][2][2] = {};
+  MoeIndex() {
+    int n = 0;
+    const MoeInstance* p = moe_instances(&n);
+    for (int i = 0; i < n; ++i) {
+      const MoeInstance& g = p[i];
+      fn[g.fmt][g.mb - 1][nb_index(g.nb)][wk_index(g.wk)][wn_index(g.wn)][u_index(g.unroll)]
+        [g.swap][g.packed][g.xl] = g.fn;
+    }
+  }
+};
+
+const MoeIndex& moe_index() {
+  static const MoeIndex idx;
+  return idx;
+}
+
+MoeLaunchFn moe_fn(int fmt, int max_m, int packed, const w8_cfg& c) {
+  if (c.x_lds > 1 || c.quant_launch) return nullptr;
+  return moe_index().fn[fmt][(max_m + 15) / 16 - 1][nb_index(c.tile_n / 16)][wk_index(c.waves_k)]
+                       [wn_index(c.waves_n)][u_index(c.unroll)][c.swap_ab][packed][c.x_lds];
+}
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Bytes between two experts' partials (0 when no tile is shared).
+size_t part_stride(int fmt, int max_m, int N, int K, const w8_cfg& c) {
+  if (c.split_k <= 1 && c.grid <= 0) return 0;
+  return round256(ws_partial_bytes(tiles_of(N, c), partial_slots(fmt, N, K, c),
+                                   c.waves_n * c.tile_n / 16, (max_m + 15) / 16));
+}
+
+// A config of the GEMM family (its rules at M = max_m) that has a compiled
+// grouped instance, and whose shared tiles fit the counter region.
+w8_status check_moe_cfg(int fmt, int E, int max_m, int N, int K, int packed, const w8_cfg& c) {
+  w8_status st = check_cfg(fmt, W8_OP_GEMM, max_m, N, K, c);
+  if (st) return st;
+  if (!moe_fn(fmt, max_m, packed, c))
+    return fail(W8_E_INVALID,
+                "cfg: the grouped GEMM is compiled for (waves_k, waves_n, x_lds) in "
+                "{(1|2|4|8, 1, 0), (1, 2|4|8, 1)}");
+  if ((c.split_k > 1 || c.grid > 0) && (long long)E * tiles_of(N, c) > kSplitKMaxTiles)
+    return fail(W8_E_INVALID, "cfg: shared tiles need experts x tiles <= " +
+                                  std::to_string(kSplitKMaxTiles));
+  return W8_OK;
+}
+
+size_t moe_ws_bytes(int fmt, int E, int max_m, int N, int K, const w8_cfg& c) {
+  const size_t stride = part_stride(fmt, max_m, N, K, c);
+  return stride ? ws_counter_bytes(0) + (size_t)E * stride : 0;
+}
+
+// Default: the cost model's fastest config with a grouped instance, for a
+// GEMM whose N spans the experts a call can reach: min(E, 8 T) of them (a
+// token is routed to at most 8 experts in the common top-k setups).
+w8_cfg moe_default_cfg(int fmt, int E, int T, int max_m, int N, int K, int packed) {
+  const long long reach = std::min<long long>(E, 8LL * T);
+  const int n_eff = (int)std::min<long long>((long long)N * reach, 1 << 24);
+  for (const auto& pc : rank_configs(fmt, W8_OP_GEMM, max_m, n_eff, K, packed, W8_MAX_SPLIT_K, 0))
+    if (check_moe_cfg(fmt, E, max_m, N, K, packed, pc.second) == W8_OK) return pc.second;
+  w8_cfg c;
+  std::memset(&c, 0, sizeof c);
+  c.abi_version = W8_ABI_VERSION;
+  c.tile_n = 16;
+  c.waves_k = 4;
+  c.waves_n = 1;
+  c.unroll = 1;
+  c.split_k = 1;
+  return c;
+}
+
+w8_status check_moe_shape(int fmt, int E, int T, int N, int K, int max_m) {
+  w8_status st = check_gemm_shape(fmt, max_m, N, K);
+  if (st) return st;
+  if (E < 1 || E > 65535) return fail(W8_E_INVALID, "E must be in [1, 65535]");
+  if (T < 1) return fail(W8_E_INVALID, "T must be positive");
+  return W8_OK;
+}
+
+w8_status resolve_moe(int fmt, int E, int T, int N, int K, int max_m, int packed,
+                      const w8_cfg* cfg, w8_cfg* out) {
+  if (cfg) {
+    w8_status st = check_moe_cfg(fmt, E, max_m, N, K, packed, *cfg);
+    if (st) return st;
+    *out = *cfg;
+  } else {
+    *out = moe_default_cfg(fmt, E, T, max_m, N, K, packed);
+  }
+  return W8_OK;
+}
+
+}  // namespace
+}  // namespace w8
+
+using namespace w8;
+
+extern "C" w8_status w8_moe_config(w8_fmt fmt, int E, int T, int N, int K, int max_m, int packed,
+                                   w8_cfg* out) {
+  w8_status st = check_moe_shape(fmt, E, T, N, K, max_m);
+  if (st) return st;
+  if (!out) return fail(W8_E_INVALID, "null output pointer");
+  *out = moe_default_cfg(fmt, E, T, max_m, N, K, packed ? 1 : 0);
+  return ok();
+}
+
+extern "C" w8_status w8_moe_validate_config(w8_fmt fmt, int E, int N, int K, int max_m,
+                                            int packed, const w8_cfg* cfg) {
+  w8_status st = check_moe_shape(fmt, E, 1, N, K, max_m);
+  if (st) return st;
+  if (!cfg) return fail(W8_E_INVALID, "null cfg");
+  st = check_moe_cfg(fmt, E, max_m, N, K, packed ? 1 : 0, *cfg);
+  if (st) return st;
+  return ok();
+}
+
+extern "C" w8_status w8_moe_workspace_size(w8_fmt fmt, int E, int T, int N, int K, int max_m,
+                                           int packed, const w8_cfg* cfg, size_t* bytes) {
+  w8_status st = check_moe_shape(fmt, E, T, N, K, max_m);
+  if (st) return st;
+  if (!bytes) return fail(W8_E_INVALID, "null output pointer");
+  w8_cfg c;
+  st = resolve_moe(fmt, E, T, N, K, max_m, packed ? 1 : 0, cfg, &c);
+  if (st) return st;
+  *bytes = moe_ws_bytes(fmt, E, max_m, N, K, c);
+  return ok();
+}
+
+extern "C" w8_status w8_moe_gemm(w8_fmt fmt, int E, int T, int N, int K, int max_m,
+                                 const void* xq, int64_t ldq, const float* sx,
+                                 const int32_t* offsets, const int32_t* rows, const void* wq,
+                                 int64_t ldw, int64_t w_stride, const float* sw,
+                                 int64_t sw_stride, void* y, int64_t ldy, const w8_cfg* cfg,
+                                 void* ws, size_t ws_bytes, w8_stream stream) {
+  w8_status st = check_moe_shape(fmt, E, T, N, K, max_m);
+  if (st) return st;
+  if (!xq || !sx || !offsets || !rows || !wq || !sw || !y)
+    return fail(W8_E_INVALID, "null device pointer");
+  const int packed = ldw == 0;
+  if (!aligned(xq, 16) || ldq < K || ldq % 16)
+    return fail(W8_E_INVALID, "xq must be 16-byte aligned with ldq >= K and ldq % 16 == 0");
+  if (!aligned(wq, 16) || w_stride % 16)
+    return fail(W8_E_INVALID, "wq and w_stride must be 16-byte aligned");
+  if (packed) {
+    if (w_stride < (int64_t)packed_weight_bytes(fmt, N, K))
+      return fail(W8_E_INVALID, "w_stride below one expert's packed weights");
+  } else {
+    if (ldw < K || ldw % 16) return fail(W8_E_INVALID, "ldw must be 0 (packed) or >= K, % 16");
+    if (w_stride < (int64_t)N * ldw) return fail(W8_E_INVALID, "w_stride below N * ldw");
+  }
+  const int64_t nsw =
+      fmt == W8_BLOCK_FP8 ? (int64_t)((N + 127) / 128) * (K / W8_GROUP) : (int64_t)N;
+  if (sw_stride < nsw) return fail(W8_E_INVALID, "sw_stride below one expert's weight scales");
+  if (ldy < N) return fail(W8_E_INVALID, "output leading dimension must be >= N");
+  if (!aligned(sx, 4) || !aligned(sw, 4) || !aligned(y, 2) || !aligned(offsets, 4) ||
+      !aligned(rows, 4))
+    return fail(W8_E_INVALID, "misaligned scale, routing or output pointer");
+  w8_cfg c;
+  st = resolve_moe(fmt, E, T, N, K, max_m, packed, cfg, &c);
+  if (st) return st;
+  const size_t need = moe_ws_bytes(fmt, E, max_m, N, K, c);
+  if (need > 0) {
+    if (!ws || ws_bytes < need)
+      return fail(W8_E_WORKSPACE, "workspace of " + std::to_string(need) + " bytes needed, got " +
+                                      std::to_string(ws ? ws_bytes : 0));
+    if (!aligned(ws, 16)) return fail(W8_E_INVALID, "workspace must be 16-byte aligned");
+  }
+  st = check_device();
+  if (st) return st;
+  const int ntiles = tiles_of(N, c);
+  GemmArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.xq = static_cast<const uint8_t*>(xq);
+  a.sx = sx;
+  a.wq = static_cast<const uint8_t*>(wq);
+  a.sw = sw;
+  a.out = y;
+  a.ldq = ldq;
+  a.ldw = ldw;
+  a.ldo = ldy;
+  a.M = max_m;  // per expert: its routed count (at most max_m rows are computed)
+  a.N = N;
+  a.K = K;
+  a.ksteps = ksteps_of(fmt, K);
+  a.kfull = K / kstep_of(fmt);
+  a.split_k = c.split_k;
+  a.split_shift = __builtin_ctz((unsigned)c.split_k);
+  a.grid = c.grid;
+  a.slots = partial_slots(fmt, N, K, c);
+  a.ntiles = ntiles;
+  a.sgroups = fmt == W8_BLOCK_FP8 ? K / W8_GROUP : 0;
+  a.out_mode = 0;
+  MoeArgs m;
+  m.offsets = offsets;
+  m.rows = rows;
+  m.w_stride = w_stride;
+  m.sw_stride = sw_stride;
+  m.part_stride = (long long)part_stride(fmt, max_m, N, K, c);
+  m.xrow_max = T - 1;
+  if (need > 0) {
+    a.counters = static_cast<unsigned int*>(ws);
+    a.part = static_cast<char*>(ws) + ws_counter_bytes(ntiles);
+  }
+  const unsigned wgs = c.grid > 0 ? (unsigned)c.grid : (unsigned)(ntiles * c.split_k);
+  hipError_t e = moe_fn(fmt, max_m, packed, c)(a, m, dim3(wgs, (unsigned)E),
+                                              dim3(64 * c.waves_k * c.waves_n),
+                                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("MoE GEMM launch", e));
+  return ok();
+}

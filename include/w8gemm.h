@@ -395,6 +395,52 @@ w8_status w8_rank_configs(w8_fmt fmt, int M, int N, int K, const w8_tune_opts *o
 w8_status w8_profile_configs(w8_fmt fmt, int M, int N, int K, const w8_tune_opts *opts,
                              const w8_cfg *cfgs, int n, double *us, int *valid);
 
+/* --------------------------------------------------------------- MoE -- */
+/* MoE grouped GEMM in the same three formats (paragraph 9 of the page: MoE
+ * models, where the MoE backend becomes the main optimization target, are
+ * the next stated goal).  E experts share (N, K).  T token rows were
+ * quantized once (w8_quantize_act: xq [T, K], sx [T] or [T, K/128]); the
+ * routing lists, per expert e, the routed entries i in [offsets[e],
+ * offsets[e+1]) and the token row rows[i] of each, and entry i's output is
+ *   Y[i, :] = dequant(xq[rows[i]]) . dequant(Wq_e)^T
+ * with expert e's weight codes Wq_e and scales sw_e in the format's
+ * layout -- the GEMM of w8_gemm_w8a8 on the gathered rows, per expert.  One
+ * kernel launch covers all experts (no host synchronization: the routing is
+ * read on the device); an expert with no entry reads no weights.
+ *   offsets  int32 [E + 1] (device), ascending, offsets[0] = 0; each
+ *            expert's count offsets[e+1] - offsets[e] must be <= max_m
+ *   rows     int32 [offsets[E]] (device), each in [0, T) (clamped if not)
+ *   max_m    bound on any expert's count, 1..32 (else W8_E_UNSUPPORTED);
+ *            kernels for ceil(max_m / 16) row blocks run
+ *   wq       expert e's codes at wq + e * w_stride bytes: row-major [N, K]
+ *            with row stride ldw, or with ldw = 0 the packed layout
+ *            (w8_pack_weight per expert); w_stride % 16 == 0
+ *   sw       expert e's scales at sw + e * sw_stride floats
+ *   y        bf16 rows offsets[0] .. offsets[E] - 1, row stride ldy (device)
+ *   cfg      a GEMM-family config valid at M = max_m whose (waves_k, waves_n,
+ *            x_lds) is one of (1|2|4|8, 1, 0) or (1, 2|4|8, 1); NULL = the
+ *            cost model's pick (w8_moe_config).  Shared tiles (split_k > 1
+ *            or grid > 0) need E x tiles <= 16384.
+ *   ws       w8_moe_workspace_size bytes: the 2 MiB counter region, then
+ *            each expert's partials; zero-filled before first use.
+ * Same allocation, ordering and error rules as w8_gemm_w8a8.               */
+w8_status w8_moe_gemm(w8_fmt fmt, int E, int T, int N, int K, int max_m,
+                      const void *xq, int64_t ldq, const float *sx,
+                      const int32_t *offsets, const int32_t *rows,
+                      const void *wq, int64_t ldw, int64_t w_stride,
+                      const float *sw, int64_t sw_stride, void *y, int64_t ldy,
+                      const w8_cfg *cfg, void *ws, size_t ws_bytes, w8_stream stream);
+w8_status w8_moe_workspace_size(w8_fmt fmt, int E, int T, int N, int K, int max_m, int packed,
+                                const w8_cfg *cfg, size_t *bytes);
+/* W8_OK if cfg is valid for w8_moe_gemm with these sizes and layout.       */
+w8_status w8_moe_validate_config(w8_fmt fmt, int E, int N, int K, int max_m, int packed,
+                                 const w8_cfg *cfg);
+/* The config w8_moe_gemm uses for cfg == NULL: the cost model's fastest
+ * valid config for a GEMM of N x min(E, 8 T) columns (the experts T tokens
+ * reach with up to 8 each).                                                 */
+w8_status w8_moe_config(w8_fmt fmt, int E, int T, int N, int K, int max_m, int packed,
+                        w8_cfg *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -228,3 +228,24 @@ def forward(fmt, x_bf16_bits, wq, sw):
     """
     xq, sx = quantize_act(fmt, x_bf16_bits)
     return gemm(fmt, xq, sx, wq, sw), xq, sx
+
+
+def moe_gemm(fmt, xq, sx, offsets, rows, wq, sw) -> np.ndarray:
+    """MoE grouped GEMM (the pages' next target: MoE models, ai-radar.it,
+    "Helion nel backend vLLM", paragraph 9).  E experts, each with its own
+    weights wq[e] [N, K] and scales sw[e]; the routed entries of expert e are
+    i in [offsets[e], offsets[e+1]), entry i reading token row rows[i] of the
+    quantized activations.  Y[i] = the GEMM of that token row with expert e's
+    weights, so Y[offsets[e]:offsets[e+1]] = gemm(fmt, xq[rows_e], sx[rows_e],
+    wq[e], sw[e]).  Returns float64 [offsets[E], N]."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    E = len(offsets) - 1
+    N = wq.shape[1]
+    Y = np.zeros((int(offsets[E]), N), dtype=np.float64)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if b > a:
+            r = rows[a:b]
+            Y[a:b] = gemm(fmt, xq[r], sx[r], wq[e], sw[e])
+    return Y

@@ -99,3 +99,34 @@ def activations_extreme(fmt: str, M: int, K: int) -> np.ndarray:
             x[r, idx[K // 4:K // 4 + K // 8]] = -0.0
     bits = fp32_to_bf16_bits(x.astype(np.float32))
     return bits
+
+
+def moe_routing(T: int, E: int, topk: int, seed: int, max_m: int = 32):
+    """Top-k routing of T tokens to E experts: each token picks topk distinct
+    experts uniformly at random (seeded), no expert takes more than max_m
+    tokens.  Returns (offsets int32 [E + 1], rows int32 [T * topk]): the
+    entries grouped by expert in expert order, tokens ascending within one."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    per = [[] for _ in range(E)]
+    for t in range(T):
+        choices = [e for e in g.permutation(E) if len(per[e]) < max_m][:topk]
+        for e in choices:
+            per[e].append(t)
+    counts = np.array([len(p) for p in per], dtype=np.int64)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    rows = np.array([t for p in per for t in p], dtype=np.int32)
+    return offsets, rows
+
+
+def moe_weights(fmt: str, E: int, N: int, K: int):
+    """Per-expert weights in the dense GEMM's distributions: W8A8_INT8 codes
+    and scales ([E, N, K], [E, N]), else fp32 weights [E, N, K] to quantize."""
+    if fmt == "W8A8_INT8":
+        g = rng(fmt, E, N, K, "moe_w")
+        wq = g.integers(-127, 128, size=(E, N, K), dtype=np.int8)
+        sw = g.uniform(0.001, 0.01, size=(E, N)).astype(np.float32)
+        return wq, sw
+    g = rng(fmt, E, N, K, "moe_w")
+    sd = 0.02 if fmt == "FP8_Dynamic" else 1.0
+    return (g.standard_normal((E, N, K)) * sd).astype(np.float32), None

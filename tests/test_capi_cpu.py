@@ -497,3 +497,51 @@ def test_model_mirror_matches_library(w8):
         for us, c in w8.rank_configs(fmt, M, N, K, op=op, stream_k=True):
             want = fm.predict(fm.CURRENT, fmt, op, M, N, K, c.as_dict())
             assert abs(us - want) <= 1e-9 * want, (fmt, M, N, K, op, c, us, want)
+
+
+def test_moe_argument_errors(w8, lib):
+    """Validation of the MoE entry point before anything touches a device."""
+    L = lib.w8_moe_gemm
+    cfg = w8.Config.make(waves_k=4, unroll=1)
+    c = ctypes.byref(cfg)
+
+    def call(fmt=0, E=8, T=16, N=64, K=256, max_m=32, xq=FAKE, ldq=256, ldw=256,
+             w_stride=64 * 256, sw_stride=64, cfgp=c, ws=None, wsb=0):
+        return L(fmt, E, T, N, K, max_m, xq, ldq, FAKE, FAKE, FAKE, FAKE, ldw, w_stride, FAKE,
+                 sw_stride, FAKE, 64, cfgp, ws, wsb, None)
+
+    assert call(max_m=33) == 2                       # outside the small-M window
+    assert call(E=0) == 1 and call(T=0) == 1
+    assert call(xq=None) == 1
+    assert call(ldq=250) == 1
+    assert call(w_stride=64 * 256 - 16) == 1         # experts overlap
+    assert call(ldw=0, w_stride=100) == 1            # packed: below one expert's packed size
+    assert call(sw_stride=63) == 1
+    assert call(fmt=2, sw_stride=1) == 1             # Block_FP8: ceil(N/128) x K/128 = 2
+    bad = w8.Config.make(waves_k=16, unroll=1)       # no grouped instance with 16 waves
+    assert call(cfgp=ctypes.byref(bad)) == 1 and b"grouped" in lib.w8_last_error()
+    sk = w8.Config.make(waves_k=4, unroll=1, split_k=4)
+    assert call(cfgp=ctypes.byref(sk)) == 3          # workspace missing
+    with pytest.raises(w8.W8Error):
+        w8.moe_workspace_size("FP8_Dynamic", 8, 16, 16384 * 16 + 16, 256, 32,
+                              w8.Config.make(waves_k=4, unroll=1, split_k=2))
+
+
+def test_moe_workspace_and_default(w8):
+    sk = w8.Config.make(tile_n=16, waves_k=4, unroll=1, split_k=4)
+    E, N, K = 8, 300, 1024
+    per = (N + 15) // 16 * 4 * 1 * 2 * 1024          # tiles x slots x N blocks x M blocks x 1 KiB
+    assert w8.moe_workspace_size("FP8_Dynamic", E, 16, N, K, 32, sk) == \
+        COUNTERS + E * ((per + 255) // 256 * 256)
+    assert w8.moe_workspace_size("FP8_Dynamic", E, 16, N, K, 32,
+                                 w8.Config.make(waves_k=4, unroll=1)) == 0
+    for fmt in w8.FORMATS:
+        for (E, T, N, K, m) in ((128, 16, 1536, 2048, 32), (8, 1, 4096, 4096, 1),
+                                (64, 32, 2048, 768, 16)):
+            c = w8.moe_config(fmt, E, T, N, K, m, packed=True)
+            assert lib_ok(w8, fmt, E, N, K, m, c)
+
+
+def lib_ok(w8, fmt, E, N, K, m, c):
+    st = w8._lib.w8_moe_validate_config(w8.FORMATS[fmt], E, N, K, m, 1, ctypes.byref(c))
+    return st == 0

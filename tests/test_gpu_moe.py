@@ -1,0 +1,159 @@
+"""The MoE grouped GEMM on the GPU against the oracle's moe_gemm, and bit for
+bit against the dense GEMM run per expert on the gathered rows with the same
+config: every format, both weight layouts, split-K, stream-K, x_lds, Swap-AB,
+empty experts, one expert holding every token, one-row tokens, and graph
+replay with a shared-tile workspace."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from tests.gpu_cases import DEV, assert_bf16_close, to_bf16_tensor
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def w8():
+    import bit_quantized_gemm_token_amd as mod
+    return mod
+
+
+class MoeCase:
+    def __init__(self, w8, fmt, T, E, N, K, topk=None, seed=0, routing=None, max_m=32):
+        print(f"[moe] {fmt} T={T} E={E} N={N} K={K} topk={topk}", flush=True)
+        self.fmt, self.T, self.E, self.N, self.K = fmt, T, E, N, K
+        bits = synthetic.activations(fmt, T, N, K)
+        self.xq, self.sx = w8.quantize_act(fmt, to_bf16_tensor(bits))
+        xq_ref, sx_ref = oracle.quantize_act(fmt, bits)
+        w, sw = synthetic.moe_weights(fmt, E, N, K)
+        if fmt == "W8A8_INT8":
+            self.wq = torch.from_numpy(w).to(DEV)
+            self.sw = torch.from_numpy(sw).to(DEV)
+            wq_ref, sw_ref = w.view(np.uint8), sw
+        else:
+            qs = [w8.quantize_weight(fmt, torch.from_numpy(w[e]).to(DEV)) for e in range(E)]
+            self.wq = torch.stack([q for q, _ in qs])
+            self.sw = torch.stack([s for _, s in qs]).contiguous()
+            rq = [oracle.quantize_weight(fmt, w[e]) for e in range(E)]
+            wq_ref = np.stack([q for q, _ in rq])
+            sw_ref = np.stack([s for _, s in rq])
+        if routing is None:
+            routing = synthetic.moe_routing(T, E, topk, seed, max_m)
+        self.offsets_np, self.rows_np = routing
+        self.offsets = torch.from_numpy(np.asarray(self.offsets_np, np.int32)).to(DEV)
+        self.rows = torch.from_numpy(np.asarray(self.rows_np, np.int32)).to(DEV)
+        self.packed = w8.pack_experts(fmt, self.wq)
+        self.Y = oracle.moe_gemm(fmt, xq_ref, sx_ref, self.offsets_np, self.rows_np, wq_ref,
+                                 sw_ref)
+
+    def weights(self, packed):
+        return self.packed if packed else self.wq
+
+    def per_expert(self, w8, cfg, packed):
+        """The dense GEMM per expert on its gathered rows."""
+        out = torch.empty((len(self.rows_np), self.N), dtype=torch.bfloat16, device=DEV)
+        for e in range(self.E):
+            a, b = int(self.offsets_np[e]), int(self.offsets_np[e + 1])
+            if b == a:
+                continue
+            r = self.rows[a:b].long()
+            xq, sx = self.xq[r].contiguous(), self.sx[r].contiguous()
+            if packed:
+                wq = w8.PackedWeight(self.fmt, self.N, self.K, self.packed.data[e])
+            else:
+                wq = self.wq[e]
+            out[a:b] = w8.gemm_w8a8(self.fmt, xq, sx, wq, self.sw[e], cfg=cfg)
+        return out
+
+
+def same_bits(a, b):
+    return torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+CFGS = (dict(tile_n=16, waves_k=4, unroll=2, split_k=1),
+        dict(tile_n=32, waves_k=2, unroll=1, split_k=4, swap_ab=1),
+        dict(tile_n=16, waves_k=1, waves_n=8, unroll=1, split_k=2, x_lds=1),
+        dict(tile_n=64, waves_k=1, unroll=1, split_k=1),
+        dict(tile_n=16, waves_k=8, unroll=1, split_k=16),
+        dict(tile_n=16, waves_k=2, unroll=2, grid=40))
+
+
+@pytest.mark.parametrize("fmt", ["W8A8_INT8", "FP8_Dynamic", "Block_FP8"])
+def test_moe_matches_oracle_and_per_expert_gemm(w8, fmt):
+    # 9 experts' routing with an empty expert inserted at index 3
+    off9, rows = synthetic.moe_routing(24, 9, 6, 5)
+    offsets = np.insert(off9, 3, off9[3]).astype(np.int32)
+    cs = MoeCase(w8, fmt, T=24, E=10, N=300, K=1024, routing=(offsets, rows))
+    counts = np.diff(cs.offsets_np)
+    assert counts.max() > 16 and counts[3] == 0
+    for packed in (False, True):
+        y = w8.moe_gemm(fmt, cs.xq, cs.sx, cs.offsets, cs.rows, cs.weights(packed), cs.sw)
+        torch.cuda.synchronize()
+        assert_bf16_close(y, cs.Y, f"moe default {fmt} packed={packed}")
+        for kw in CFGS:
+            cfg = w8.Config.make(**kw)
+            y = w8.moe_gemm(fmt, cs.xq, cs.sx, cs.offsets, cs.rows, cs.weights(packed), cs.sw,
+                            cfg=cfg)
+            ref = cs.per_expert(w8, cfg, packed)
+            torch.cuda.synchronize()
+            assert same_bits(y, ref), f"{fmt} {kw} packed={packed}"
+            assert_bf16_close(y, cs.Y, f"moe {fmt} {kw} packed={packed}")
+
+
+@pytest.mark.parametrize("fmt", ["W8A8_INT8", "Block_FP8"])
+def test_moe_edge_routings(w8, fmt):
+    T, E, N, K = 32, 4, 200, 512
+    # every token to expert 2; the others empty
+    routing = (np.array([0, 0, 0, 32, 32], np.int32), np.arange(32, dtype=np.int32))
+    cs = MoeCase(w8, fmt, T, E, N, K, routing=routing)
+    for packed in (False, True):
+        y = w8.moe_gemm(fmt, cs.xq, cs.sx, cs.offsets, cs.rows, cs.weights(packed), cs.sw,
+                        cfg=w8.Config.make(tile_n=16, waves_k=4, unroll=1, split_k=2))
+        torch.cuda.synchronize()
+        assert_bf16_close(y, cs.Y, f"moe one expert {fmt}")
+    # one token, routed to three experts out of order of their ids; max_m = 1
+    routing = (np.array([0, 1, 1, 2, 3], np.int32), np.array([0, 0, 0], np.int32))
+    cs = MoeCase(w8, fmt, 1, E, N, K, routing=routing)
+    y = w8.moe_gemm(fmt, cs.xq, cs.sx, cs.offsets, cs.rows, cs.wq, cs.sw, max_m=1)
+    torch.cuda.synchronize()
+    assert_bf16_close(y, cs.Y, f"moe one token {fmt}")
+    # E = 1, identity routing: the dense GEMM
+    routing = (np.array([0, 12], np.int32), np.arange(12, dtype=np.int32))
+    cs = MoeCase(w8, fmt, 12, 1, N, K, routing=routing)
+    cfg = w8.Config.make(tile_n=32, waves_k=2, unroll=2, split_k=2)
+    y = w8.moe_gemm(fmt, cs.xq, cs.sx, cs.offsets, cs.rows, cs.wq, cs.sw, max_m=16, cfg=cfg)
+    ref = w8.gemm_w8a8(fmt, cs.xq, cs.sx, cs.wq[0], cs.sw[0], cfg=cfg)
+    torch.cuda.synchronize()
+    assert same_bits(y, ref)
+
+
+def test_moe_many_experts_and_graph_replay(w8):
+    """128 experts (N = 512, K = 1024, top-8 of 16 tokens) under split-K,
+    eager and replayed from a HIP graph."""
+    fmt = "FP8_Dynamic"
+    cs = MoeCase(w8, fmt, T=16, E=128, N=512, K=1024, topk=8, seed=11)
+    cfg = w8.Config.make(tile_n=16, waves_k=4, unroll=1, split_k=4)
+    ws = w8.Workspace(DEV, w8.moe_workspace_size(fmt, 128, 16, 512, 1024, 32, cfg, packed=True))
+    eager = w8.moe_gemm(fmt, cs.xq, cs.sx, cs.offsets, cs.rows, cs.packed, cs.sw, cfg=cfg,
+                        workspace=ws).clone()
+    torch.cuda.synchronize()
+    assert_bf16_close(eager, cs.Y, "moe E=128")
+    y = torch.empty_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        w8.moe_gemm(fmt, cs.xq, cs.sx, cs.offsets, cs.rows, cs.packed, cs.sw, cfg=cfg, y=y,
+                    workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w8.moe_gemm(fmt, cs.xq, cs.sx, cs.offsets, cs.rows, cs.packed, cs.sw, cfg=cfg, y=y,
+                    workspace=ws)
+    for i in range(4):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert same_bits(y, eager), f"replay {i}"
