@@ -185,6 +185,7 @@ def parse():
     p.add_argument("--layout", choices=("table", "row", "packed"), default="table",
                    help="weight layout: the faster one per the table (default), or forced")
     p.add_argument("--report", default=None, help="write per-problem results (JSON) here")
+    p.add_argument("--no-moe", action="store_true", help="skip the MoE grouped GEMM measurement")
     p.add_argument("--counter-pass", default=None, metavar="MANIFEST",
                    help="instead of timing, make the launches for a rocprofv3 --pmc run and "
                         "write their order to MANIFEST")
@@ -271,6 +272,118 @@ class Problem:
             self.run_path(w8)
         with torch.cuda.graph(self.g_linear, stream=stream):
             self.run_linear(w8)
+
+
+# ------------------------------------------------------------------ MoE --
+# MoE layers of the Qwen3 family's MoE models (the pages measure Qwen3 models):
+# 128 experts, top-8 routing, hidden size 2048 and expert width 768, i.e. the
+# experts' gate/up projection (N = 1536, K = 2048) and down projection
+# (N = 2048, K = 768), at decode token counts.  Synthetic: random codes and
+# scales, seeded routing.
+MOE_E, MOE_TOPK = 128, 8
+MOE_SHAPES = (("gate_up", 1536, 2048), ("down", 2048, 768))
+MOE_TOKENS = (1, 4, 16, 32)
+
+
+def _random_codes(fmt, shape, dev, gen):
+    c = torch.randint(0, 256, shape, dtype=torch.int32, device=dev, generator=gen).to(torch.uint8)
+    if fmt == "W8A8_INT8":
+        c[c == 0x80] = 0x81
+    else:
+        c[(c & 0x7F) == 0x7F] = 0x38
+    return c
+
+
+def moe_bench(w8, dev, rotate_bytes, warmup, reps):
+    """Per (format, projection, token count): one graph of G grouped-GEMM calls,
+    call j on weight copy j % R with routing seed j, so the distinct expert
+    weights a graph reads exceed the last-level cache; beside it the same
+    calls as one dense GEMM launch per active expert (rows gathered
+    beforehand).  us per call = median graph time / G."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    rows_out = []
+    for fmt in ("FP8_Dynamic", "W8A8_INT8", "Block_FP8"):
+        for name, N, K in MOE_SHAPES:
+            pbytes = w8.packed_weight_size(fmt, N, K)
+            set_bytes = MOE_E * pbytes
+            R = max(2, math.ceil(rotate_bytes / set_bytes))
+            weights = [w8.PackedExperts(fmt, N, K, _random_codes(fmt, (MOE_E, pbytes), dev, gen))
+                       for _ in range(R)]
+            nsw = N if fmt != "Block_FP8" else ((N + 127) // 128) * (K // 128)
+            sw = (torch.rand((MOE_E, nsw), device=dev, generator=gen) * 0.01 + 0.001)
+            for T in MOE_TOKENS:
+                active = min(MOE_E, MOE_TOPK * T)
+                G = max(R, min(64, math.ceil(rotate_bytes / (active * pbytes))))
+                bits = synthetic.activations(fmt, T, N, K)
+                x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+                xq, sx = w8.quantize_act(fmt, x)
+                calls = []
+                for j in range(G):
+                    off, rows = synthetic.moe_routing(T, MOE_E, MOE_TOPK, seed=1000 * T + j)
+                    calls.append((weights[j % R], torch.from_numpy(off).to(dev),
+                                  torch.from_numpy(rows).to(dev), off, rows))
+                cfg = w8.moe_config(fmt, MOE_E, T, N, K, 32, packed=True)
+                ws = w8.Workspace(dev, max(256, w8.moe_workspace_size(fmt, MOE_E, T, N, K, 32, cfg,
+                                                                      packed=True)))
+                y = torch.empty((T * MOE_TOPK, N), dtype=torch.bfloat16, device=dev)
+                # per-expert dense launches: gathered rows and configs prepared up front
+                dense = []
+                for wt, _, _, off, rows in calls:
+                    for e in range(MOE_E):
+                        a, b = int(off[e]), int(off[e + 1])
+                        if b > a:
+                            r = torch.from_numpy(rows[a:b].astype(np.int64)).to(dev)
+                            dense.append((xq[r].contiguous(), sx[r].contiguous(),
+                                          w8.PackedWeight(fmt, N, K, wt.data[e]), sw[e],
+                                          y[a:b], w8.resolve_config(fmt, b - a, N, K,
+                                                                    packed=True)[0]))
+                wsd = w8.Workspace(dev, max([256] + [w8.workspace_size(fmt, d[0].shape[0], N, K,
+                                                                       d[5], packed=True)
+                                                     for d in dense]))
+                stream = torch.cuda.Stream(dev)
+                stream.wait_stream(torch.cuda.current_stream(dev))
+                g_moe, g_dense = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g_moe, stream=stream):
+                    for wt, offt, rowst, _, _ in calls:
+                        w8.moe_gemm(fmt, xq, sx, offt, rowst, wt, sw, cfg=cfg, y=y, workspace=ws)
+                with torch.cuda.graph(g_dense, stream=stream):
+                    for d in dense:
+                        w8.gemm_w8a8(fmt, d[0], d[1], d[2], d[3], cfg=d[5], y=d[4], workspace=wsd)
+                t = {"moe": [], "dense": []}
+                with torch.cuda.stream(stream):
+                    for i in range(warmup + reps):
+                        for key, gr in (("moe", g_moe), ("dense", g_dense)):
+                            e0 = torch.cuda.Event(enable_timing=True)
+                            e1 = torch.cuda.Event(enable_timing=True)
+                            e0.record(stream)
+                            gr.replay()
+                            e1.record(stream)
+                            e1.synchronize()
+                            if i >= warmup:
+                                t[key].append(e0.elapsed_time(e1) * 1e3 / G)
+                us = sorted(t["moe"])[len(t["moe"]) // 2]
+                us_d = sorted(t["dense"])[len(t["dense"]) // 2]
+                n_act = np.mean([int((np.diff(c[3]) > 0).sum()) for c in calls])
+                byts = n_act * (N * K + 4 * nsw) + T * K + T * MOE_TOPK * N * 2
+                rows_out.append({"fmt": fmt, "proj": name, "N": N, "K": K, "T": T,
+                                 "active_experts": float(n_act), "calls": G, "copies": R,
+                                 "cfg": cfg.as_dict(), "us": round(us, 3),
+                                 "us_per_expert_launches": round(us_d, 3),
+                                 "gbps": round(byts / (us * 1e3), 1)})
+                log(f"[moe] {fmt} {name} T={T}: {us:.2f} us ({byts / (us * 1e3):.0f} GB/s), "
+                    f"per-expert launches {us_d:.2f} us, {n_act:.0f} experts active")
+                del g_moe, g_dense, dense
+            del weights
+            torch.cuda.empty_cache()
+    return {"workload": f"{MOE_E} experts, top-{MOE_TOPK}, gate_up 1536x2048 and down 2048x768, "
+                        f"T in {list(MOE_TOKENS)}, 3 formats, packed weights",
+            "problems": len(rows_out),
+            "geomean_us": round(geomean([r["us"] for r in rows_out]), 3),
+            "geomean_gbps": round(geomean([r["gbps"] for r in rows_out]), 1),
+            "geomean_speedup_vs_per_expert_launches": round(
+                geomean([r["us_per_expert_launches"] / r["us"] for r in rows_out]), 3),
+            "rows": rows_out}
 
 
 def geomean(v):
@@ -434,6 +547,18 @@ def main():
         "traffic": measured_traffic(dom, dp),
     }
 
+    # the MoE grouped GEMM, measured after the sweep (not part of the headline)
+    moe = None
+    if not args.no_moe:
+        for p in problems:  # free the sweep's graphs and weight copies first
+            p.g_gemm = p.g_path = p.g_linear = None
+            p.pool = p.weights = p.wq = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        t0 = time.time()
+        moe = moe_bench(w8, dev, rotate, args.warmup, max(args.steps // 2, 3))
+        log(f"[bench] MoE measured in {time.time() - t0:.1f} s")
+
     cpu = None
     if not args.no_cpu:
         cpu, checked = cpu_baseline(problems, args.cpu_budget_s)
@@ -482,6 +607,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if moe is not None:
+        out["moe"] = {k: v for k, v in moe.items() if k != "rows"}
     if args.report:
         rows = [{"fmt": p.fmt, "M": p.M, "N": p.N, "K": p.K, "cfg": p.cfg.as_dict(),
                  "layout": "packed" if p.packed else "row",
@@ -493,7 +620,8 @@ def main():
                  "gbps": round(p.gbps, 1), "frac": round(p.gbps / HBM_PEAK_GBPS, 4),
                  "kernel": p.kernel} for p in problems]
         with open(args.report, "w") as f:
-            json.dump({"summary": out, "problems": rows}, f, indent=1)
+            json.dump({"summary": out, "problems": rows,
+                       "moe": moe["rows"] if moe else []}, f, indent=1)
     print(json.dumps(out), flush=True)
 
 

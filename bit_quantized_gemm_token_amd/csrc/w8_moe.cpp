@@ -74,10 +74,25 @@ size_t moe_ws_bytes(int fmt, int E, int max_m, int N, int K, const w8_cfg& c) {
   return stride ? ws_counter_bytes(0) + (size_t)E * stride : 0;
 }
 
-// Default: the cost model's fastest config with a grouped instance, for a
-// GEMM whose N spans the experts a call can reach: min(E, 8 T) of them (a
-// token is routed to at most 8 experts in the common top-k setups).
+// Default.  Measured on 128-expert top-8 layers (1536 x 2048 and 2048 x 768)
+// at 1 to 32 tokens, the fastest grouped configs are small workgroups that
+// each own 32 output columns of one expert, with no split and activations
+// loaded in the K loop: the launch has workgroups to spare across the active
+// experts, and a routed expert holds only a token or two.  Two K-waves of
+// two K-steps each help when at most 2 tokens are routed.  If that config is
+// invalid for the shape, the cost model's fastest valid config for a GEMM
+// whose N spans the experts a call can reach -- min(E, 8 T) of them -- is
+// used.
 w8_cfg moe_default_cfg(int fmt, int E, int T, int max_m, int N, int K, int packed) {
+  w8_cfg d;
+  std::memset(&d, 0, sizeof d);
+  d.abi_version = W8_ABI_VERSION;
+  d.tile_n = 32;
+  d.waves_k = T <= 2 ? 2 : 1;
+  d.waves_n = 1;
+  d.unroll = T <= 2 ? 2 : 1;
+  d.split_k = 1;
+  if (check_moe_cfg(fmt, E, max_m, N, K, packed, d) == W8_OK) return d;
   const long long reach = std::min<long long>(E, 8LL * T);
   const int n_eff = (int)std::min<long long>((long long)N * reach, 1 << 24);
   for (const auto& pc : rank_configs(fmt, W8_OP_GEMM, max_m, n_eff, K, packed, W8_MAX_SPLIT_K, 0))

@@ -435,9 +435,11 @@ w8_status w8_moe_workspace_size(w8_fmt fmt, int E, int T, int N, int K, int max_
 /* W8_OK if cfg is valid for w8_moe_gemm with these sizes and layout.       */
 w8_status w8_moe_validate_config(w8_fmt fmt, int E, int N, int K, int max_m, int packed,
                                  const w8_cfg *cfg);
-/* The config w8_moe_gemm uses for cfg == NULL: the cost model's fastest
- * valid config for a GEMM of N x min(E, 8 T) columns (the experts T tokens
- * reach with up to 8 each).                                                 */
+/* The config w8_moe_gemm uses for cfg == NULL: tile_n 32, one K-wave
+ * (two, with unroll 2, for T <= 2), no split, no x_lds -- the fastest on
+ * 128-expert top-8 layers measured at 1..32 tokens -- or, where that is
+ * invalid, the cost model's fastest valid config for a GEMM of
+ * N x min(E, 8 T) columns (the experts T tokens reach with up to 8 each).  */
 w8_status w8_moe_config(w8_fmt fmt, int E, int T, int N, int K, int max_m, int packed,
                         w8_cfg *out);
 
