@@ -385,6 +385,8 @@ def moe_gemm(fmt, xq, sx, offsets, rows, wq, sw, max_m=32, cfg=None, y=None, wor
         y = torch.empty((rows.numel(), N), dtype=torch.bfloat16, device=xq.device)
     elif y.dtype != torch.bfloat16:
         raise TypeError("y must be bfloat16")
+    elif y.shape[0] < rows.numel() or y.shape[1] != N:
+        raise ValueError(f"y must be [{rows.numel()}, {N}]")
     if workspace is None:
         workspace = _default_workspace(xq.device)
     need = moe_workspace_size(f, E, T, N, K, max_m, cfg, packed)
@@ -395,7 +397,8 @@ def moe_gemm(fmt, xq, sx, offsets, rows, wq, sw, max_m=32, cfg=None, y=None, wor
     _check(_lib.w8_moe_gemm(f, E, T, N, K, max_m, _dev_ptr(xq, "xq"), ldq,
                             _dev_ptr(sx, "sx", torch.float32),
                             _dev_ptr(offsets, "offsets", torch.int32),
-                            _dev_ptr(rows, "rows", torch.int32), wptr, ldw, w_stride,
+                            _dev_ptr(rows, "rows", torch.int32), rows.numel(), wptr, ldw,
+                            w_stride,
                             _dev_ptr(sw, "sw", torch.float32), sw.stride(0),
                             _dev_ptr(y, "y"), _row_major(y, "y"), _cfg_ptr(cfg), ws_ptr, ws_bytes,
                             _stream(stream, xq.device)))

@@ -147,7 +147,8 @@ def load():
                                        cfgp, c_int, dp, ctypes.POINTER(c_int)]
     lib.w8_profile_configs.restype = st
     lib.w8_moe_gemm.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, vp, i64, f32p, vp, vp,
-                                vp, i64, i64, f32p, i64, vp, i64, cfgp, vp, ctypes.c_size_t, vp]
+                                c_int, vp, i64, i64, f32p, i64, vp, i64, cfgp, vp,
+                                ctypes.c_size_t, vp]
     lib.w8_moe_gemm.restype = st
     lib.w8_moe_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, cfgp,
                                           ctypes.POINTER(ctypes.c_size_t)]

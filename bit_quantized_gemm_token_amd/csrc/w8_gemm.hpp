@@ -727,8 +727,10 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
 template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL>
 __global__ __launch_bounds__(64 * WK * WN) void moe_gemm_kernel(GemmArgs a, MoeArgs m) {
   const int e = blockIdx.y;
-  const int off = m.offsets[e];
-  const int rows = min(m.offsets[e + 1] - off, 16 * MB);
+  // (offsets clamped to the row list, so bad routing reads and writes nothing
+  // outside it)
+  const int off = min(max(m.offsets[e], 0), m.n_rows);
+  const int rows = min(min(m.offsets[e + 1], m.n_rows) - off, 16 * MB);
   if (rows <= 0) return;  // an expert no token was routed to
   a.M = rows;
   a.wq += e * m.w_stride;

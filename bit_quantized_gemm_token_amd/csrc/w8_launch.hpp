@@ -69,6 +69,7 @@ struct MoeArgs {
   long long sw_stride;     // floats between two experts' weight scales
   long long part_stride;   // bytes between two experts' partials in the workspace
   int xrow_max;            // activation rows - 1 (row ids are clamped to [0, xrow_max])
+  int n_rows;              // entries in `rows` (offsets are clamped to [0, n_rows])
 };
 
 typedef hipError_t (*MoeLaunchFn)(const GemmArgs&, const MoeArgs&, dim3 grid, dim3 block,

@@ -166,7 +166,8 @@ extern "C" w8_status w8_moe_workspace_size(w8_fmt fmt, int E, int T, int N, int 
 
 extern "C" w8_status w8_moe_gemm(w8_fmt fmt, int E, int T, int N, int K, int max_m,
                                  const void* xq, int64_t ldq, const float* sx,
-                                 const int32_t* offsets, const int32_t* rows, const void* wq,
+                                 const int32_t* offsets, const int32_t* rows, int n_rows,
+                                 const void* wq,
                                  int64_t ldw, int64_t w_stride, const float* sw,
                                  int64_t sw_stride, void* y, int64_t ldy, const w8_cfg* cfg,
                                  void* ws, size_t ws_bytes, w8_stream stream) {
@@ -174,6 +175,7 @@ extern "C" w8_status w8_moe_gemm(w8_fmt fmt, int E, int T, int N, int K, int max
   if (st) return st;
   if (!xq || !sx || !offsets || !rows || !wq || !sw || !y)
     return fail(W8_E_INVALID, "null device pointer");
+  if (n_rows < 0) return fail(W8_E_INVALID, "n_rows must be >= 0");
   const int packed = ldw == 0;
   if (!aligned(xq, 16) || ldq < K || ldq % 16)
     return fail(W8_E_INVALID, "xq must be 16-byte aligned with ldq >= K and ldq % 16 == 0");
@@ -235,6 +237,7 @@ extern "C" w8_status w8_moe_gemm(w8_fmt fmt, int E, int T, int N, int K, int max
   m.sw_stride = sw_stride;
   m.part_stride = (long long)part_stride(fmt, max_m, N, K, c);
   m.xrow_max = T - 1;
+  m.n_rows = n_rows;
   if (need > 0) {
     a.counters = static_cast<unsigned int*>(ws);
     a.part = static_cast<char*>(ws) + ws_counter_bytes(ntiles);

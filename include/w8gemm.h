@@ -407,16 +407,19 @@ w8_status w8_profile_configs(w8_fmt fmt, int M, int N, int K, const w8_tune_opts
  * layout -- the GEMM of w8_gemm_w8a8 on the gathered rows, per expert.  One
  * kernel launch covers all experts (no host synchronization: the routing is
  * read on the device); an expert with no entry reads no weights.
- *   offsets  int32 [E + 1] (device), ascending, offsets[0] = 0; each
- *            expert's count offsets[e+1] - offsets[e] must be <= max_m
- *   rows     int32 [offsets[E]] (device), each in [0, T) (clamped if not)
+ *   offsets  int32 [E + 1] (device), ascending, offsets[0] = 0,
+ *            offsets[E] = n_rows; each expert's count offsets[e+1] -
+ *            offsets[e] must be <= max_m (rows past 16 ceil(max_m/16) of an
+ *            expert are not computed).  Offsets are clamped to [0, n_rows],
+ *            so bad routing never reads or writes outside rows and y.
+ *   rows     int32 [n_rows] (device), each in [0, T) (clamped if not)
  *   max_m    bound on any expert's count, 1..32 (else W8_E_UNSUPPORTED);
  *            kernels for ceil(max_m / 16) row blocks run
  *   wq       expert e's codes at wq + e * w_stride bytes: row-major [N, K]
  *            with row stride ldw, or with ldw = 0 the packed layout
  *            (w8_pack_weight per expert); w_stride % 16 == 0
  *   sw       expert e's scales at sw + e * sw_stride floats
- *   y        bf16 rows offsets[0] .. offsets[E] - 1, row stride ldy (device)
+ *   y        bf16 [n_rows, N], row stride ldy (device), entry i's row i
  *   cfg      a GEMM-family config valid at M = max_m whose (waves_k, waves_n,
  *            x_lds) is one of (1|2|4|8, 1, 0) or (1, 2|4|8, 1); NULL = the
  *            cost model's pick (w8_moe_config).  Shared tiles (split_k > 1
@@ -426,7 +429,7 @@ w8_status w8_profile_configs(w8_fmt fmt, int M, int N, int K, const w8_tune_opts
  * Same allocation, ordering and error rules as w8_gemm_w8a8.               */
 w8_status w8_moe_gemm(w8_fmt fmt, int E, int T, int N, int K, int max_m,
                       const void *xq, int64_t ldq, const float *sx,
-                      const int32_t *offsets, const int32_t *rows,
+                      const int32_t *offsets, const int32_t *rows, int n_rows,
                       const void *wq, int64_t ldw, int64_t w_stride,
                       const float *sw, int64_t sw_stride, void *y, int64_t ldy,
                       const w8_cfg *cfg, void *ws, size_t ws_bytes, w8_stream stream);

@@ -506,13 +506,14 @@ def test_moe_argument_errors(w8, lib):
     c = ctypes.byref(cfg)
 
     def call(fmt=0, E=8, T=16, N=64, K=256, max_m=32, xq=FAKE, ldq=256, ldw=256,
-             w_stride=64 * 256, sw_stride=64, cfgp=c, ws=None, wsb=0):
-        return L(fmt, E, T, N, K, max_m, xq, ldq, FAKE, FAKE, FAKE, FAKE, ldw, w_stride, FAKE,
-                 sw_stride, FAKE, 64, cfgp, ws, wsb, None)
+             w_stride=64 * 256, sw_stride=64, cfgp=c, ws=None, wsb=0, n_rows=64):
+        return L(fmt, E, T, N, K, max_m, xq, ldq, FAKE, FAKE, FAKE, n_rows, FAKE, ldw, w_stride,
+                 FAKE, sw_stride, FAKE, 64, cfgp, ws, wsb, None)
 
     assert call(max_m=33) == 2                       # outside the small-M window
     assert call(E=0) == 1 and call(T=0) == 1
     assert call(xq=None) == 1
+    assert call(n_rows=-1) == 1
     assert call(ldq=250) == 1
     assert call(w_stride=64 * 256 - 16) == 1         # experts overlap
     assert call(ldw=0, w_stride=100) == 1            # packed: below one expert's packed size

@@ -129,6 +129,34 @@ def test_moe_edge_routings(w8, fmt):
     assert same_bits(y, ref)
 
 
+def test_moe_routing_is_clamped(w8):
+    """Routing that breaks the preconditions stays inside the buffers: offsets
+    beyond the row list are clamped to it, row ids beyond the tokens to the
+    last token, and an expert over max_m computes its first 16 * ceil(max_m/16)
+    rows.  The rows it does compute equal the oracle on the clamped routing."""
+    fmt, T, E, N, K = "W8A8_INT8", 8, 3, 96, 256
+    rows = np.array([0, 1, 2, 3, 4, 5, 7, 6], np.int32)
+    cs = MoeCase(w8, fmt, T, E, N, K, routing=(np.array([0, 5, 8, 8], np.int32), rows))
+    bad_off = torch.tensor([0, 5, 100, 100], dtype=torch.int32, device=DEV)
+    bad_rows = cs.rows.clone()
+    bad_rows[7] = 1000                      # clamped to token T - 1 = 7
+    y = torch.full((8, N), 7.0, dtype=torch.bfloat16, device=DEV)
+    w8.moe_gemm(fmt, cs.xq, cs.sx, bad_off, bad_rows, cs.wq, cs.sw, y=y, max_m=16)
+    want_rows = rows.copy()
+    want_rows[7] = T - 1
+    Y = oracle.moe_gemm(fmt, *[np.asarray(v) for v in (
+        oracle.quantize_act(fmt, synthetic.activations(fmt, T, N, K)))],
+        np.array([0, 5, 8, 8]), want_rows,
+        synthetic.moe_weights(fmt, E, N, K)[0].view(np.uint8), synthetic.moe_weights(fmt, E, N, K)[1])
+    torch.cuda.synchronize()
+    assert_bf16_close(y, Y, "clamped routing")
+    # an expert over max_m = 2: only its first 16 rows (one block) exist; with
+    # 5 entries and max_m 2 all 5 fit in the block, so all are computed
+    y2 = w8.moe_gemm(fmt, cs.xq, cs.sx, cs.offsets, cs.rows, cs.wq, cs.sw, max_m=2)
+    torch.cuda.synchronize()
+    assert_bf16_close(y2, cs.Y, "count above max_m within one block")
+
+
 def test_moe_many_experts_and_graph_replay(w8):
     """128 experts (N = 512, K = 1024, top-8 of 16 tokens) under split-K,
     eager and replayed from a HIP graph."""
