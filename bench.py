@@ -386,6 +386,41 @@ def moe_bench(w8, dev, rotate_bytes, warmup, reps):
             "rows": rows_out}
 
 
+def context_floors(dev, nbytes):
+    """Two device figures the small-shape results are read against: the cost
+    of one launch of a one-element kernel under graph replay, and the rate of
+    a plain device copy of `nbytes` (torch's copy_, counting the bytes read
+    and written)."""
+    s = torch.cuda.Stream(dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    t = torch.zeros(1, device=dev)
+    n = 1000
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(n):
+            t.add_(1.0)
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)  # first call outside the timing
+    launch, copy = [], []
+    with torch.cuda.stream(s):
+        for i in range(7):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(s)
+            g.replay()
+            e[1].record(s)
+            dst.copy_(src)
+            e[2].record(s)
+            e[2].synchronize()
+            if i >= 2:
+                launch.append(e[0].elapsed_time(e[1]) * 1e3 / n)
+                copy.append(2 * nbytes / (e[1].elapsed_time(e[2]) * 1e6))
+    del g, src, dst
+    return {"launch_floor_us": round(sorted(launch)[len(launch) // 2], 3),
+            "copy_gbps": round(sorted(copy)[len(copy) // 2], 1),
+            "copy_bytes": nbytes}
+
+
 def geomean(v):
     v = [x for x in v if x > 0]
     return math.exp(sum(math.log(x) for x in v) / len(v)) if v else 0.0
@@ -547,6 +582,10 @@ def main():
         "traffic": measured_traffic(dom, dp),
     }
 
+    floors = context_floors(dev, 1 << 30)
+    log(f"[bench] launch floor {floors['launch_floor_us']} us, plain copy "
+        f"{floors['copy_gbps']} GB/s")
+
     # the MoE grouped GEMM, measured after the sweep (not part of the headline)
     moe = None
     if not args.no_moe:
@@ -602,6 +641,7 @@ def main():
                                               for p in problems]), 2),
         "linear_fused_problems": sum(p.cfg_l.quant_launch == 0 for p in problems),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "context": dict(floors, frac_of_copy_bw=round(value / floors["copy_gbps"], 4)),
         "per_format": per_fmt,
         "refcheck": refcheck,
         "roofline": roofline,
