@@ -275,14 +275,11 @@ class Problem:
 
 
 # ------------------------------------------------------------------ MoE --
-# MoE layers of the Qwen3 family's MoE models (the pages measure Qwen3 models):
-# 128 experts, top-8 routing, hidden size 2048 and expert width 768, i.e. the
-# experts' gate/up projection (N = 1536, K = 2048) and down projection
-# (N = 2048, K = 768), at decode token counts.  Synthetic: random codes and
-# scales, seeded routing.
-MOE_E, MOE_TOPK = 128, 8
-MOE_SHAPES = (("gate_up", 1536, 2048), ("down", 2048, 768))
-MOE_TOKENS = (1, 4, 16, 32)
+# The MoE layers of synthetic.MOE_SHAPES (128 experts, top-8) at the token
+# counts synthetic.MOE_TOKENS.  Synthetic: random codes and scales, seeded
+# routing.
+MOE_E, MOE_TOPK = synthetic.MOE_E, synthetic.MOE_TOPK
+MOE_SHAPES, MOE_TOKENS = synthetic.MOE_SHAPES, synthetic.MOE_TOKENS
 
 
 def _random_codes(fmt, shape, dev, gen):
@@ -323,8 +320,9 @@ def moe_bench(w8, dev, rotate_bytes, warmup, reps):
                     off, rows = synthetic.moe_routing(T, MOE_E, MOE_TOPK, seed=1000 * T + j)
                     calls.append((weights[j % R], torch.from_numpy(off).to(dev),
                                   torch.from_numpy(rows).to(dev), off, rows))
-                cfg = w8.moe_config(fmt, MOE_E, T, N, K, 32, packed=True)
-                ws = w8.Workspace(dev, max(256, w8.moe_workspace_size(fmt, MOE_E, T, N, K, 32, cfg,
+                # an expert holds at most T rows (top-k picks distinct experts)
+                cfg, from_table = w8.moe_config(fmt, MOE_E, T, N, K, T, packed=True)
+                ws = w8.Workspace(dev, max(256, w8.moe_workspace_size(fmt, MOE_E, T, N, K, T, cfg,
                                                                       packed=True)))
                 y = torch.empty((T * MOE_TOPK, N), dtype=torch.bfloat16, device=dev)
                 # per-expert dense launches: gathered rows and configs prepared up front
@@ -346,7 +344,8 @@ def moe_bench(w8, dev, rotate_bytes, warmup, reps):
                 g_moe, g_dense = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g_moe, stream=stream):
                     for wt, offt, rowst, _, _ in calls:
-                        w8.moe_gemm(fmt, xq, sx, offt, rowst, wt, sw, cfg=cfg, y=y, workspace=ws)
+                        w8.moe_gemm(fmt, xq, sx, offt, rowst, wt, sw, max_m=T, cfg=cfg, y=y,
+                                    workspace=ws)
                 with torch.cuda.graph(g_dense, stream=stream):
                     for d in dense:
                         w8.gemm_w8a8(fmt, d[0], d[1], d[2], d[3], cfg=d[5], y=d[4], workspace=wsd)
@@ -368,7 +367,8 @@ def moe_bench(w8, dev, rotate_bytes, warmup, reps):
                 byts = n_act * (N * K + 4 * nsw) + T * K + T * MOE_TOPK * N * 2
                 rows_out.append({"fmt": fmt, "proj": name, "N": N, "K": K, "T": T,
                                  "active_experts": float(n_act), "calls": G, "copies": R,
-                                 "cfg": cfg.as_dict(), "us": round(us, 3),
+                                 "cfg": cfg.as_dict(), "cfg_from_table": bool(from_table),
+                                 "us": round(us, 3),
                                  "us_per_expert_launches": round(us_d, 3),
                                  "gbps": round(byts / (us * 1e3), 1)})
                 log(f"[moe] {fmt} {name} T={T}: {us:.2f} us ({byts / (us * 1e3):.0f} GB/s), "

@@ -33,7 +33,7 @@ __all__ = ["Config", "W8Error", "UnsupportedShape", "Workspace", "PackedWeight",
            "validate_config", "default_config", "resolve_config", "lookup_config",
            "set_config", "load_config_table", "save_config_table", "clear_config_table",
            "config_table_size", "config_table_foreign", "tune_shape", "rank_configs",
-           "profile_configs", "model_config", "moe_gemm", "moe_config", "moe_workspace_size",
+           "profile_configs", "model_config", "moe_gemm", "moe_config", "moe_tune", "moe_workspace_size",
            "pack_experts", "PackedExperts", "FORMATS", "MAX_M",
            "MAX_SPLIT_K", "GROUP", "ABI_VERSION"]
 
@@ -350,10 +350,28 @@ def _experts(f, wq):
 
 
 def moe_config(fmt, E, T, N, K, max_m=32, packed=False):
-    """The config moe_gemm uses when cfg is None."""
+    """(config moe_gemm uses when cfg is None, 1 if it is the table's "moe"
+    entry for (T, N, K) else 0)."""
     c = Config()
-    _check(_lib.w8_moe_config(_fmt(fmt), E, T, N, K, max_m, int(bool(packed)), ctypes.byref(c)))
-    return c
+    hit = ctypes.c_int(0)
+    _check(_lib.w8_moe_config(_fmt(fmt), E, T, N, K, max_m, int(bool(packed)), ctypes.byref(c),
+                              ctypes.byref(hit)))
+    return c, hit.value
+
+
+def moe_tune(fmt, E, T, N, K, topk, warmup=2, replays=5, bank2_top=5, rotate_bytes=512 << 20,
+             max_split_k=MAX_SPLIT_K, insert=True, fail_candidate=-1, packed=False):
+    """Ahead-of-time tuning of the grouped GEMM for E experts of (N, K) at T
+    tokens routed top-k (seeded uniform routings); the winner becomes the
+    table's "moe" entry for (T, N, K) when insert.  Returns (Config, stats
+    dict).  Synchronizes the device."""
+    o = _tune_opts(warmup, replays, bank2_top, rotate_bytes, max_split_k, insert,
+                   fail_candidate, packed, False, "gemm", 0)
+    best = Config()
+    stats = TuneStats()
+    _check(_lib.w8_moe_tune(_fmt(fmt), E, T, N, K, topk, ctypes.byref(o), ctypes.byref(best),
+                            ctypes.byref(stats)))
+    return best, stats.as_dict()
 
 
 def moe_workspace_size(fmt, E, T, N, K, max_m=32, cfg=None, packed=False):

@@ -46,7 +46,7 @@ w8_cfg resolve_cfg(int fmt, int op, int M, int N, int K, int packed, int* from_t
 // time per call of a config, the set ranked by it (ascending), and the
 // model's top-1 pick.
 std::vector<w8_cfg> enumerate_configs(int fmt, int op, int M, int N, int K, int packed,
-                                      int max_split_k, int stream_k);
+                                      int max_split_k, int stream_k, bool prune_waves = true);
 double predict_us(int fmt, int op, int M, int N, int K, const w8_cfg& c);
 std::vector<std::pair<double, w8_cfg>> rank_configs(int fmt, int op, int M, int N, int K,
                                                     int packed, int max_split_k, int stream_k);
@@ -77,6 +77,30 @@ w8_status launch_gemm_call(const GemmCall& call, const w8_cfg& c, hipStream_t s)
 // The linear op (call.x set): the fused GEMM, or with c.quant_launch the
 // quantize kernel into the workspace and then the GEMM.
 w8_status launch_linear_call(const GemmCall& call, const w8_cfg& c, hipStream_t s);
+
+// MoE grouped GEMM (w8_moe.cpp).
+struct MoeCall {
+  int fmt, E, T, N, K, max_m;
+  const void* xq;
+  long long ldq;
+  const float* sx;
+  const int* offsets;
+  const int* rows;
+  int n_rows;
+  const void* wq;
+  long long ldw;  // 0: packed
+  long long w_stride;
+  const float* sw;
+  long long sw_stride;
+  void* y;
+  long long ldy;
+  void* ws;
+  size_t ws_bytes;
+};
+w8_status check_moe_cfg(int fmt, int E, int max_m, int N, int K, int packed, const w8_cfg& c);
+size_t moe_ws_bytes(int fmt, int E, int max_m, int N, int K, const w8_cfg& c);
+w8_cfg moe_fallback_cfg(int fmt, int E, int T, int max_m, int N, int K, int packed);
+w8_status launch_moe_call(const MoeCall& call, const w8_cfg& c, hipStream_t s);
 
 constexpr const char* kArch = "gfx950";
 

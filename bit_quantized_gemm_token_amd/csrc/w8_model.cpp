@@ -99,7 +99,7 @@ double predict_us(int fmt, int op, int M, int N, int K, const w8_cfg& c) {
 }
 
 std::vector<w8_cfg> enumerate_configs(int fmt, int op, int M, int N, int K, int packed,
-                                      int max_split_k, int stream_k) {
+                                      int max_split_k, int stream_k, bool prune_waves) {
   (void)packed;
   const int T = ksteps_of(fmt, K);
   const long long wbytes = (long long)N * ((K + 15) / 16 * 16);
@@ -153,7 +153,7 @@ std::vector<w8_cfg> enumerate_configs(int fmt, int op, int M, int N, int K, int 
             consider(c);
           }
         }
-  const long long min_waves = std::min<long long>(256, most_waves);
+  const long long min_waves = prune_waves ? std::min<long long>(256, most_waves) : 0;
   std::vector<w8_cfg> out;
   for (const w8_cfg& c : all)
     if (total_waves(c) >= min_waves) out.push_back(c);

@@ -54,6 +54,8 @@ size_t part_stride(int fmt, int max_m, int N, int K, const w8_cfg& c) {
                                    c.waves_n * c.tile_n / 16, (max_m + 15) / 16));
 }
 
+}  // namespace
+
 // A config of the GEMM family (its rules at M = max_m) that has a compiled
 // grouped instance, and whose shared tiles fit the counter region.
 w8_status check_moe_cfg(int fmt, int E, int max_m, int N, int K, int packed, const w8_cfg& c) {
@@ -83,7 +85,7 @@ size_t moe_ws_bytes(int fmt, int E, int max_m, int N, int K, const w8_cfg& c) {
 // invalid for the shape, the cost model's fastest valid config for a GEMM
 // whose N spans the experts a call can reach -- min(E, 8 T) of them -- is
 // used.
-w8_cfg moe_default_cfg(int fmt, int E, int T, int max_m, int N, int K, int packed) {
+w8_cfg moe_fallback_cfg(int fmt, int E, int T, int max_m, int N, int K, int packed) {
   w8_cfg d;
   std::memset(&d, 0, sizeof d);
   d.abi_version = W8_ABI_VERSION;
@@ -108,6 +110,22 @@ w8_cfg moe_default_cfg(int fmt, int E, int T, int max_m, int N, int K, int packe
   return c;
 }
 
+namespace {
+
+// The config for cfg == NULL: the table entry for (fmt, moe, layout, T, N,
+// K) if valid here, else the fallback.
+w8_cfg moe_default_cfg(int fmt, int E, int T, int max_m, int N, int K, int packed,
+                       int* from_table) {
+  w8_cfg c;
+  if (from_table) *from_table = 0;
+  if (w8_lookup_config((w8_fmt)fmt, W8_OP_MOE, T, N, K, packed, &c, nullptr) == W8_OK &&
+      check_moe_cfg(fmt, E, max_m, N, K, packed, c) == W8_OK) {
+    if (from_table) *from_table = 1;
+    return c;
+  }
+  return moe_fallback_cfg(fmt, E, T, max_m, N, K, packed);
+}
+
 w8_status check_moe_shape(int fmt, int E, int T, int N, int K, int max_m) {
   w8_status st = check_gemm_shape(fmt, max_m, N, K);
   if (st) return st;
@@ -123,22 +141,70 @@ w8_status resolve_moe(int fmt, int E, int T, int N, int K, int max_m, int packed
     if (st) return st;
     *out = *cfg;
   } else {
-    *out = moe_default_cfg(fmt, E, T, max_m, N, K, packed);
+    *out = moe_default_cfg(fmt, E, T, max_m, N, K, packed, nullptr);
   }
   return W8_OK;
 }
 
 }  // namespace
+
+w8_status launch_moe_call(const MoeCall& g, const w8_cfg& c, hipStream_t s) {
+  const int fmt = g.fmt, E = g.E, T = g.T, N = g.N, K = g.K, max_m = g.max_m;
+  const int packed = g.ldw == 0;
+  const size_t need = moe_ws_bytes(fmt, E, max_m, N, K, c);
+  const int ntiles = tiles_of(N, c);
+  GemmArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.xq = static_cast<const uint8_t*>(g.xq);
+  a.sx = g.sx;
+  a.wq = static_cast<const uint8_t*>(g.wq);
+  a.sw = g.sw;
+  a.out = g.y;
+  a.ldq = g.ldq;
+  a.ldw = g.ldw;
+  a.ldo = g.ldy;
+  a.M = max_m;  // per expert: its routed count (at most max_m rows are computed)
+  a.N = N;
+  a.K = K;
+  a.ksteps = ksteps_of(fmt, K);
+  a.kfull = K / kstep_of(fmt);
+  a.split_k = c.split_k;
+  a.split_shift = __builtin_ctz((unsigned)c.split_k);
+  a.grid = c.grid;
+  a.slots = partial_slots(fmt, N, K, c);
+  a.ntiles = ntiles;
+  a.sgroups = fmt == W8_BLOCK_FP8 ? K / W8_GROUP : 0;
+  a.out_mode = 0;
+  MoeArgs m;
+  m.offsets = g.offsets;
+  m.rows = g.rows;
+  m.w_stride = g.w_stride;
+  m.sw_stride = g.sw_stride;
+  m.part_stride = (long long)part_stride(fmt, max_m, N, K, c);
+  m.xrow_max = T - 1;
+  m.n_rows = g.n_rows;
+  if (need > 0) {
+    a.counters = static_cast<unsigned int*>(g.ws);
+    a.part = static_cast<char*>(g.ws) + ws_counter_bytes(ntiles);
+  }
+  const unsigned wgs = c.grid > 0 ? (unsigned)c.grid : (unsigned)(ntiles * c.split_k);
+  hipError_t e = moe_fn(fmt, max_m, packed, c)(a, m, dim3(wgs, (unsigned)E),
+                                              dim3(64 * c.waves_k * c.waves_n),
+                                              s);
+  if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("MoE GEMM launch", e));
+  return W8_OK;
+}
+
 }  // namespace w8
 
 using namespace w8;
 
 extern "C" w8_status w8_moe_config(w8_fmt fmt, int E, int T, int N, int K, int max_m, int packed,
-                                   w8_cfg* out) {
+                                   w8_cfg* out, int* from_table) {
   w8_status st = check_moe_shape(fmt, E, T, N, K, max_m);
   if (st) return st;
   if (!out) return fail(W8_E_INVALID, "null output pointer");
-  *out = moe_default_cfg(fmt, E, T, max_m, N, K, packed ? 1 : 0);
+  *out = moe_default_cfg(fmt, E, T, max_m, N, K, packed ? 1 : 0, from_table);
   return ok();
 }
 
@@ -207,45 +273,9 @@ extern "C" w8_status w8_moe_gemm(w8_fmt fmt, int E, int T, int N, int K, int max
   }
   st = check_device();
   if (st) return st;
-  const int ntiles = tiles_of(N, c);
-  GemmArgs a;
-  std::memset(&a, 0, sizeof a);
-  a.xq = static_cast<const uint8_t*>(xq);
-  a.sx = sx;
-  a.wq = static_cast<const uint8_t*>(wq);
-  a.sw = sw;
-  a.out = y;
-  a.ldq = ldq;
-  a.ldw = ldw;
-  a.ldo = ldy;
-  a.M = max_m;  // per expert: its routed count (at most max_m rows are computed)
-  a.N = N;
-  a.K = K;
-  a.ksteps = ksteps_of(fmt, K);
-  a.kfull = K / kstep_of(fmt);
-  a.split_k = c.split_k;
-  a.split_shift = __builtin_ctz((unsigned)c.split_k);
-  a.grid = c.grid;
-  a.slots = partial_slots(fmt, N, K, c);
-  a.ntiles = ntiles;
-  a.sgroups = fmt == W8_BLOCK_FP8 ? K / W8_GROUP : 0;
-  a.out_mode = 0;
-  MoeArgs m;
-  m.offsets = offsets;
-  m.rows = rows;
-  m.w_stride = w_stride;
-  m.sw_stride = sw_stride;
-  m.part_stride = (long long)part_stride(fmt, max_m, N, K, c);
-  m.xrow_max = T - 1;
-  m.n_rows = n_rows;
-  if (need > 0) {
-    a.counters = static_cast<unsigned int*>(ws);
-    a.part = static_cast<char*>(ws) + ws_counter_bytes(ntiles);
-  }
-  const unsigned wgs = c.grid > 0 ? (unsigned)c.grid : (unsigned)(ntiles * c.split_k);
-  hipError_t e = moe_fn(fmt, max_m, packed, c)(a, m, dim3(wgs, (unsigned)E),
-                                              dim3(64 * c.waves_k * c.waves_n),
-                                              static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("MoE GEMM launch", e));
+  MoeCall call{fmt, E, T, N, K, max_m, xq, ldq, sx, offsets, rows, n_rows, wq, ldw, w_stride,
+               sw, sw_stride, y, ldy, ws, ws_bytes};
+  st = launch_moe_call(call, c, static_cast<hipStream_t>(stream));
+  if (st) return st;
   return ok();
 }

@@ -31,7 +31,9 @@ struct Entry {
 typedef std::tuple<int, int, int, int, int, int> Key;  // fmt, op, packed, M, N, K
 
 const char* layout_name(int packed) { return packed ? "packed" : "row"; }
-const char* op_name(int op) { return op == W8_OP_LINEAR ? "linear" : "gemm"; }
+const char* op_name(int op) {
+  return op == W8_OP_LINEAR ? "linear" : op == W8_OP_MOE ? "moe" : "gemm";
+}
 
 struct Table {
   std::mutex mu;
@@ -98,7 +100,8 @@ w8_status parse_table(const std::string& text, std::map<Key, Entry>* native,
     int op = -1;
     if (tok[3] == "gemm") op = W8_OP_GEMM;
     if (tok[3] == "linear") op = W8_OP_LINEAR;
-    if (op < 0) return fail(W8_E_TABLE_FORMAT, where + "op must be gemm or linear");
+    if (tok[3] == "moe") op = W8_OP_MOE;
+    if (op < 0) return fail(W8_E_TABLE_FORMAT, where + "op must be gemm, linear or moe");
     int packed = -1;
     if (tok[4] == "row") packed = 0;
     if (tok[4] == "packed") packed = 1;
@@ -301,7 +304,8 @@ w8_status w8_lookup_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!out) return fail(W8_E_INVALID, "null output pointer");
-  if (op != W8_OP_GEMM && op != W8_OP_LINEAR) return fail(W8_E_INVALID, "unknown op");
+  if (op != W8_OP_GEMM && op != W8_OP_LINEAR && op != W8_OP_MOE)
+    return fail(W8_E_INVALID, "unknown op");
   Table& t = table();
   std::lock_guard<std::mutex> lk(t.mu);
   maybe_load_env(t);

@@ -80,17 +80,19 @@ struct Buffers {
   uint16_t* x = nullptr;     // bf16 activations (fused linear op)
   float* sw = nullptr;
   uint16_t* y = nullptr;
+  int* route = nullptr;      // MoE routings: per routing E + 1 offsets, then the rows
   void* ws = nullptr;
   size_t ws_bytes = 0;
   ~Buffers() {
-    hipFree(wrow);
-    hipFree(wpool);
-    hipFree(xq);
-    hipFree(sx);
-    hipFree(x);
-    hipFree(sw);
-    hipFree(y);
-    hipFree(ws);
+    (void)hipFree(route);
+    (void)hipFree(wrow);
+    (void)hipFree(wpool);
+    (void)hipFree(xq);
+    (void)hipFree(sx);
+    (void)hipFree(x);
+    (void)hipFree(sw);
+    (void)hipFree(y);
+    (void)hipFree(ws);
   }
 };
 
@@ -114,6 +116,63 @@ struct Cand {
     if (e_ != hipSuccess) return fail(W8_E_HIP, hip_msg(#expr, e_));        \
   } while (0)
 
+// Median us per call of a graph of R calls, launch(r) recording call r.
+template <class Launch>
+w8_status time_graph(hipStream_t stream, size_t R, int warmup, int replays, Launch&& launch,
+                     double* us) {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  TRY_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal));
+  w8_status s2 = W8_OK;
+  for (size_t r = 0; r < R && s2 == W8_OK; ++r) s2 = launch(r);
+  hipError_t e = hipStreamEndCapture(stream, &graph);
+  if (s2) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return s2;
+  }
+  if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("hipStreamEndCapture", e));
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("hipGraphInstantiate", e));
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  std::vector<float> ms;
+  for (int i = 0; i < warmup + replays && e == hipSuccess; ++i) {
+    e = hipEventRecord(e0, stream);
+    if (e == hipSuccess) e = hipGraphLaunch(exec, stream);
+    if (e == hipSuccess) e = hipEventRecord(e1, stream);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    float t = 0;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, e0, e1);
+    if (i >= warmup) ms.push_back(t);
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  (void)hipGraphExecDestroy(exec);
+  if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("timing replay", e));
+  std::sort(ms.begin(), ms.end());
+  *us = ms[ms.size() / 2] * 1000.0 / (double)R;
+  return W8_OK;
+}
+
+// Candidate output ycur against the reference yref: bit-exact for INT8
+// (exact int32 sums), else within fp32 reassociation error.
+bool outputs_match(bool exact, const std::vector<uint16_t>& ycur,
+                   const std::vector<uint16_t>& yref, float ref_max) {
+  for (size_t i = 0; i < ycur.size(); ++i) {
+    if (exact) {
+      if (ycur[i] != yref[i]) return false;
+    } else {
+      const float a = bf16_to_float(ycur[i]), r = bf16_to_float(yref[i]);
+      // fp32 sums in another order: relative 1e-2, plus a floor tied to the
+      // output's scale for entries that cancel to near zero
+      if (!(std::fabs(a - r) <= 1e-2f * (1.0f + std::fabs(r)) + 1e-3f * ref_max)) return false;
+    }
+  }
+  return true;
+}
+
 // The timing and validation harness shared by the tuner and the profiler:
 // device buffers for (fmt, M, N, K) and one op and weight layout, the
 // reference output of the default GEMM config, and graph timing over R
@@ -132,7 +191,7 @@ struct Harness {
   float ref_max = 0.0f;
 
   ~Harness() {
-    if (stream) hipStreamDestroy(stream);
+    if (stream) (void)hipStreamDestroy(stream);
   }
 
   w8_status launch(const GemmCall& g, const w8_cfg& c) {
@@ -223,61 +282,177 @@ struct Harness {
     if (s2) return s2;
     TRY_HIP(hipStreamSynchronize(stream));
     TRY_HIP(hipMemcpy(ycur.data(), b.y, ycur.size() * 2, hipMemcpyDeviceToHost));
-    *good = true;
-    for (size_t i = 0; i < ycur.size() && *good; ++i) {
-      if (is_int8) {
-        *good = ycur[i] == yref[i];
-      } else {
-        const float a = bf16_to_float(ycur[i]), r = bf16_to_float(yref[i]);
-        // fp32 sums in another order: relative 1e-2, plus a floor tied to the
-        // output's scale for entries that cancel to near zero
-        *good = std::fabs(a - r) <= 1e-2f * (1.0f + std::fabs(r)) + 1e-3f * ref_max;
-      }
-    }
+    *good = outputs_match(is_int8, ycur, yref, ref_max);
     return W8_OK;
   }
 
   // Median us per call of the graph of R calls over rotating weight copies
   // (every call of the graph reads its own copy of the weights).
   w8_status time(const w8_cfg& c, double* us) {
-    hipGraph_t graph = nullptr;
-    hipGraphExec_t exec = nullptr;
-    TRY_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal));
-    w8_status s2 = W8_OK;
-    for (size_t r = 0; r < R && s2 == W8_OK; ++r) {
-      GemmCall cr = call;
-      cr.wq = b.wpool + r * wbytes;
-      s2 = launch(cr, c);
+    return time_graph(
+        stream, R, o.warmup, o.replays,
+        [&](size_t r) {
+          GemmCall cr = call;
+          cr.wq = b.wpool + r * wbytes;
+          return launch(cr, c);
+        },
+        us);
+  }
+};
+
+// Seeded uniform top-k routing of T tokens over E experts (each token to
+// topk distinct experts, drawn by xorshift64 rejection), as w8_moe_gemm's
+// (offsets, rows) lists: E + 1 offsets, then T * topk token ids grouped by
+// expert in token order.
+std::vector<int> make_routing(int E, int T, int topk, uint64_t seed) {
+  std::vector<std::vector<int>> per(E);
+  uint64_t s = seed * 0x9E3779B97F4A7C15ULL + 0x2545F4914F6CDD1DULL;
+  std::vector<int> pick;
+  for (int t = 0; t < T; ++t) {
+    pick.clear();
+    while ((int)pick.size() < topk) {
+      s ^= s << 13;
+      s ^= s >> 7;
+      s ^= s << 17;
+      const int e = (int)(s % (uint64_t)E);
+      if (std::find(pick.begin(), pick.end(), e) == pick.end()) pick.push_back(e);
     }
-    hipError_t e = hipStreamEndCapture(stream, &graph);
-    if (s2) {
-      if (graph) hipGraphDestroy(graph);
-      return s2;
+    for (int e : pick) per[e].push_back(t);
+  }
+  std::vector<int> out(E + 1, 0);
+  for (int e = 0; e < E; ++e) {
+    out[e + 1] = out[e] + (int)per[e].size();
+  }
+  for (int e = 0; e < E; ++e) out.insert(out.end(), per[e].begin(), per[e].end());
+  return out;
+}
+
+// The MoE tuner's harness: E experts of (N, K) in R rotating copies (R * E
+// experts' weights span at least rotate_bytes) and G routings of T tokens
+// top-k, call g of a graph on copy g % R with routing g.  G is large enough
+// that the experts the calls of one graph reach span rotate_bytes too (at
+// most 64, at least R), so neither the last-level cache nor the graph
+// launch's own cost, spread over G calls, flatters small T.  The reference
+// output: the fallback config on row-major copy 0 with routing 0.
+struct MoeHarness {
+  int fmt, E, T, N, K, topk, packed;
+  w8_tune_opts o;
+  long long ld = 0;
+  size_t wexp = 0, wrow_exp = 0, R = 0, G = 0, nsx = 0, nsw = 0, n_rows = 0, route_len = 0;
+  double active_mean = 0;  // experts with routed rows, mean over the routings
+  bool is_int8 = false;
+  Buffers b;
+  hipStream_t stream = nullptr;
+  MoeCall call{};
+  std::vector<uint16_t> yref, ycur;
+  float ref_max = 0.0f;
+
+  ~MoeHarness() {
+    if (stream) (void)hipStreamDestroy(stream);
+  }
+
+  MoeCall call_g(size_t g) const {
+    MoeCall c = call;
+    c.wq = b.wpool + (g % R) * (size_t)E * wexp;
+    c.offsets = b.route + g * route_len;
+    c.rows = c.offsets + E + 1;
+    return c;
+  }
+
+  w8_status setup(size_t max_ws) {
+    ld = (K + 15) / 16 * 16;
+    wrow_exp = (size_t)N * ld;
+    wexp = packed ? packed_weight_bytes(fmt, N, K) : wrow_exp;
+    const size_t set = (size_t)E * wexp;
+    R = (size_t)((o.rotate_bytes + (long long)set - 1) / (long long)set);
+    R = std::min<size_t>(std::max<size_t>(R, 2), 4096);
+    const bool block = fmt == W8_BLOCK_FP8;
+    const int groups = K / W8_GROUP;
+    nsx = block ? (size_t)T * groups : (size_t)T;
+    nsw = block ? (size_t)((N + 127) / 128) * groups : (size_t)N;
+    n_rows = (size_t)T * topk;
+    route_len = (size_t)E + 1 + n_rows;
+    const double reach = (double)std::min<long long>(E, (long long)T * topk) * (double)wexp;
+    G = std::max<size_t>(R, std::min<size_t>(64, (size_t)std::ceil((double)o.rotate_bytes / reach)));
+    is_int8 = fmt == W8_W8A8_INT8;
+    const w8_cfg dflt = moe_fallback_cfg(fmt, E, T, T, N, K, 0);  // reference
+    max_ws = std::max(max_ws, moe_ws_bytes(fmt, E, T, N, K, dflt));
+    TRY_HIP(hipStreamCreate(&stream));
+    TRY_HIP(hipMalloc(&b.wrow, wrow_exp * E));
+    TRY_HIP(hipMalloc(&b.wpool, set * R));
+    TRY_HIP(hipMalloc(&b.xq, (size_t)T * ld));
+    TRY_HIP(hipMalloc(&b.sx, nsx * 4));
+    TRY_HIP(hipMalloc(&b.sw, nsw * E * 4));
+    TRY_HIP(hipMalloc(&b.y, n_rows * N * 2));
+    TRY_HIP(hipMalloc(&b.route, route_len * G * 4));
+    b.ws_bytes = max_ws;
+    if (max_ws) {
+      TRY_HIP(hipMalloc(&b.ws, max_ws));
+      TRY_HIP(hipMemsetAsync(b.ws, 0, max_ws, stream));
     }
-    if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("hipStreamEndCapture", e));
-    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-    hipGraphDestroy(graph);
-    if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("hipGraphInstantiate", e));
-    hipEvent_t e0, e1;
-    hipEventCreate(&e0);
-    hipEventCreate(&e1);
-    std::vector<float> ms;
-    for (int i = 0; i < o.warmup + o.replays && e == hipSuccess; ++i) {
-      e = hipEventRecord(e0, stream);
-      if (e == hipSuccess) e = hipGraphLaunch(exec, stream);
-      if (e == hipSuccess) e = hipEventRecord(e1, stream);
-      if (e == hipSuccess) e = hipEventSynchronize(e1);
-      float t = 0;
-      if (e == hipSuccess) e = hipEventElapsedTime(&t, e0, e1);
-      if (i >= o.warmup) ms.push_back(t);
+    std::vector<int> routes;
+    double active = 0;
+    for (size_t g = 0; g < G; ++g) {
+      const std::vector<int> one = make_routing(E, T, topk, 1000003ULL * (g + 1));
+      for (int e = 0; e < E; ++e) active += one[e + 1] > one[e];
+      routes.insert(routes.end(), one.begin(), one.end());
     }
-    hipEventDestroy(e0);
-    hipEventDestroy(e1);
-    hipGraphExecDestroy(exec);
-    if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("timing replay", e));
-    std::sort(ms.begin(), ms.end());
-    *us = ms[ms.size() / 2] * 1000.0 / (double)R;
+    active_mean = active / (double)G;
+    TRY_HIP(hipMemcpyAsync(b.route, routes.data(), routes.size() * 4, hipMemcpyHostToDevice,
+                           stream));
+    hipLaunchKernelGGL(fill_codes_kernel, dim3(4096), dim3(256), 0, stream, b.wpool, set * R,
+                       0x1234u, (int)is_int8);
+    hipLaunchKernelGGL(fill_codes_kernel, dim3(4096), dim3(256), 0, stream, b.wrow, wrow_exp * E,
+                       0x4321u, (int)is_int8);
+    for (int e = 0; e < E; ++e) {  // copy 0 holds the reference weights, in the tuned layout
+      if (packed) {
+        TRY_HIP(launch_pack_weight(fmt, b.wrow + e * wrow_exp, ld, N, K, b.wpool + e * wexp,
+                                   stream));
+      }
+    }
+    if (!packed)
+      TRY_HIP(hipMemcpyAsync(b.wpool, b.wrow, set, hipMemcpyDeviceToDevice, stream));
+    hipLaunchKernelGGL(fill_codes_kernel, dim3(64), dim3(256), 0, stream, b.xq, (size_t)T * ld,
+                       0x9876u, (int)is_int8);
+    hipLaunchKernelGGL(fill_scales_kernel, dim3(64), dim3(256), 0, stream, b.sx, nsx, 0x55u,
+                       0.01f, 0.1f);
+    hipLaunchKernelGGL(fill_scales_kernel, dim3(256), dim3(256), 0, stream, b.sw, nsw * E, 0x77u,
+                       0.001f, 0.01f);
+    TRY_HIP(hipGetLastError());
+    TRY_HIP(hipStreamSynchronize(stream));
+
+    call = MoeCall{fmt,     E,      T,        N,    K,         T,    b.xq,
+                   ld,      b.sx,   b.route,  b.route + E + 1, (int)n_rows, b.wpool,
+                   packed ? 0 : ld, (long long)wexp, b.sw, (long long)nsw, b.y,
+                   N,       b.ws,   b.ws_bytes};
+    yref.resize(n_rows * N);
+    ycur.resize(n_rows * N);
+    MoeCall ref = call;
+    ref.wq = b.wrow;
+    ref.ldw = ld;
+    ref.w_stride = (long long)wrow_exp;
+    w8_status st = launch_moe_call(ref, dflt, stream);
+    if (st) return st;
+    TRY_HIP(hipStreamSynchronize(stream));
+    TRY_HIP(hipMemcpy(yref.data(), b.y, yref.size() * 2, hipMemcpyDeviceToHost));
+    for (uint16_t v : yref) ref_max = std::max(ref_max, std::fabs(bf16_to_float(v)));
     return W8_OK;
+  }
+
+  w8_status validate(const w8_cfg& c, bool* good) {
+    TRY_HIP(hipMemsetAsync(b.y, 0xFF, yref.size() * 2, stream));  // NaN: every row must be written
+    w8_status s2 = launch_moe_call(call, c, stream);
+    if (s2) return s2;
+    TRY_HIP(hipStreamSynchronize(stream));
+    TRY_HIP(hipMemcpy(ycur.data(), b.y, ycur.size() * 2, hipMemcpyDeviceToHost));
+    *good = outputs_match(is_int8, ycur, yref, ref_max);
+    return W8_OK;
+  }
+
+  w8_status time(const w8_cfg& c, double* us) {
+    return time_graph(
+        stream, G, o.warmup, o.replays,
+        [&](size_t g) { return launch_moe_call(call_g(g), c, stream); }, us);
   }
 };
 
@@ -485,6 +660,122 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
     const double bytes = block ? (double)N * K + (double)M * K + 2.0 * M * N +
                                      4.0 * ((N + 127) / 128) * G + 4.0 * M * G
                                : (double)N * K + (double)M * K + 2.0 * M * N + 4.0 * N + 4.0 * M;
+    stats->best_gbps = bytes / (win->us2 * 1e3);
+    stats->tune_seconds =
+        std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
+  }
+  return ok();
+}
+
+extern "C" w8_status w8_moe_tune(w8_fmt fmt, int E, int T, int N, int K, int topk,
+                                 const w8_tune_opts* opts, w8_cfg* best, w8_tune_stats* stats) {
+  const auto t_start = std::chrono::steady_clock::now();
+  w8_status st = check_gemm_shape(fmt, T, N, K);
+  if (st) return st;
+  if (E < 1 || E > 65535) return fail(W8_E_INVALID, "E must be in [1, 65535]");
+  if (topk < 1 || topk > E) return fail(W8_E_INVALID, "topk must be in [1, E]");
+  if (!best) return fail(W8_E_INVALID, "null best");
+  w8_tune_opts o;
+  st = read_opts(opts, &o);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  const int packed = o.packed ? 1 : 0;
+
+  // Candidates: the GEMM family's feasible set at M = T (an expert holds at
+  // most T rows), without the minimum-waves pruning (the experts multiply
+  // the workgroups), that the grouped kernel runs, and whose workspace stays
+  // within 1 GiB.
+  constexpr size_t kMaxWs = (size_t)1 << 30;
+  std::vector<Cand> cands;
+  for (const w8_cfg& c :
+       enumerate_configs(fmt, W8_OP_GEMM, T, N, K, packed, o.max_split_k, 0, false)) {
+    if (check_moe_cfg(fmt, E, T, N, K, packed, c) != W8_OK) continue;
+    if (moe_ws_bytes(fmt, E, T, N, K, c) > kMaxWs) continue;
+    Cand cd;
+    cd.cfg = c;
+    cd.index = (int)cands.size();
+    cands.push_back(cd);
+  }
+  if (cands.empty()) return fail(W8_E_VALIDATION, "no feasible candidate");
+  const w8_cfg dflt = moe_fallback_cfg(fmt, E, T, T, N, K, packed);  // reported baseline
+  size_t max_ws = moe_ws_bytes(fmt, E, T, N, K, dflt);
+  for (const Cand& cd : cands) max_ws = std::max(max_ws, moe_ws_bytes(fmt, E, T, N, K, cd.cfg));
+
+  MoeHarness h;
+  h.fmt = fmt;
+  h.E = E;
+  h.T = T;
+  h.N = N;
+  h.K = K;
+  h.topk = topk;
+  h.packed = packed;
+  h.o = o;
+  st = h.setup(max_ws);
+  if (st) return st;
+
+  int nvalid = 0, nrej = 0;
+  for (Cand& cd : cands) {
+    bool good = false;
+    st = h.validate(cd.cfg, &good);
+    if (st) return st;
+    if (cd.index == o.fail_candidate) good = false;
+    if (!good) {
+      ++nrej;
+      continue;
+    }
+    cd.valid = true;
+    ++nvalid;
+    st = h.time(cd.cfg, &cd.us1);
+    if (st) return st;
+  }
+  if (nvalid == 0) return fail(W8_E_VALIDATION, "no candidate passed validation");
+
+  std::vector<Cand*> order;
+  for (Cand& cd : cands)
+    if (cd.valid) order.push_back(&cd);
+  std::sort(order.begin(), order.end(), [](const Cand* a, const Cand* c) { return a->us1 < c->us1; });
+  const size_t top = std::min<size_t>(order.size(), (size_t)o.bank2_top);
+  for (size_t i = 0; i < top; ++i) {
+    st = h.time(order[i]->cfg, &order[i]->us2);
+    if (st) return st;
+  }
+  double dflt_us2 = 0;
+  st = h.time(dflt, &dflt_us2);
+  if (st) return st;
+
+  // Bank-2 winner; within 1% prefer no shared tiles, then fewer waves.
+  Cand* win = order[0];
+  for (size_t i = 1; i < top; ++i) {
+    Cand* c = order[i];
+    const double a = c->us2, w = win->us2;
+    const auto rank = [](const w8_cfg& x) {
+      return std::make_tuple(x.split_k == 1 && x.grid == 0 ? 0 : 1, x.swap_ab,
+                             x.waves_k * x.waves_n);
+    };
+    if (a < w * 0.99 || (a <= w * 1.01 && rank(c->cfg) < rank(win->cfg))) win = c;
+  }
+  *best = win->cfg;
+  if (o.insert) {
+    st = w8_set_config(fmt, W8_OP_MOE, T, N, K, packed, &win->cfg, win->us2);
+    if (st) return st;
+  }
+  if (stats) {
+    std::memset(stats, 0, sizeof *stats);
+    stats->candidates = (int)cands.size();
+    stats->validated = nvalid;
+    stats->rejected = nrej;
+    stats->best_index = win->index;
+    stats->best_us_bank1 = win->us1;
+    stats->best_us_bank2 = win->us2;
+    stats->default_us_bank2 = dflt_us2;
+    // algorithmic bytes of one call: the active experts' weights and scales,
+    // the T activation rows and scales, the T * topk output rows
+    const bool block = fmt == W8_BLOCK_FP8;
+    const int G = K / W8_GROUP;
+    const double sw_exp = block ? 4.0 * ((N + 127) / 128) * G : 4.0 * N;
+    const double bytes = h.active_mean * ((double)N * K + sw_exp) + (double)T * K +
+                         4.0 * (block ? (double)T * G : (double)T) + 2.0 * T * topk * N;
     stats->best_gbps = bytes / (win->us2 * 1e3);
     stats->tune_seconds =
         std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();

@@ -3,11 +3,14 @@
     python -m bit_quantized_gemm_token_amd.tune_sweep --out TABLE [--formats ...]
            [--ops gemm,linear] [--layouts row,packed] [--shapes M,N,K;M,N,K...]
            [--no-resume] [--max-split-k 256] [--top-n N]
+           [--moe-shapes E,topk,T,N,K;...]
 
 Default shapes: the 24-shape M <= 32 sweep of synthetic.SWEEP plus the shapes
 the tests and benchmarks name (N=K=4096 at M in {1, 4, 16, 32}; N=4608,
 K=7168 at M in {1, 8, 32}; N=512, K=7168 at M in {1, 2, 4, 8, 16, 32};
-16 x 896 x 1024).
+16 x 896 x 1024).  Op "moe" tunes the MoE grouped GEMM (moe_tune) on its own
+shapes, packed layout only: by default the 128-expert top-8 layers of
+synthetic.MOE_SHAPES at the token counts synthetic.MOE_TOKENS.
 
 Tuning is the expensive offline step the page describes (ai-radar.it,
 "Helion nel backend vLLM", paragraph 6: ahead-of-time tuning can take hours
@@ -38,13 +41,21 @@ def default_shapes():
     return out
 
 
+def default_moe_shapes():
+    sys.path.insert(0, ROOT)
+    import synthetic
+    return [(synthetic.MOE_E, synthetic.MOE_TOPK, T, N, K)
+            for _, N, K in synthetic.MOE_SHAPES for T in synthetic.MOE_TOKENS]
+
+
 def main(argv=None):
     import bit_quantized_gemm_token_amd as w8
     p = argparse.ArgumentParser()
     p.add_argument("--out", required=True)
     p.add_argument("--formats", default="FP8_Dynamic,W8A8_INT8,Block_FP8")
     p.add_argument("--layouts", default="row,packed")
-    p.add_argument("--ops", default="gemm", help="gemm, linear or gemm,linear")
+    p.add_argument("--ops", default="gemm", help="comma list of gemm, linear, moe")
+    p.add_argument("--moe-shapes", default=None, help="E,topk,T,N,K;... for op moe")
     p.add_argument("--shapes", default=None)
     p.add_argument("--no-resume", action="store_true")
     p.add_argument("--max-split-k", type=int, default=w8.MAX_SPLIT_K)
@@ -66,9 +77,18 @@ def main(argv=None):
     t0 = time.time()
     done = skipped = 0
     layouts = [{"row": False, "packed": True}[v] for v in a.layouts.split(",")]
-    jobs = [(op, fmt, s, packed) for op in a.ops.split(",") for fmt in a.formats.split(",")
-            for s in shapes for packed in layouts]
-    for op, fmt, (M, N, K), packed in jobs:
+    if a.moe_shapes:
+        moe_shapes = [tuple(int(v) for v in s.split(",")) for s in a.moe_shapes.split(";") if s]
+    else:
+        moe_shapes = default_moe_shapes()
+    jobs = []
+    for op in a.ops.split(","):
+        for fmt in a.formats.split(","):
+            if op == "moe":  # (T, N, K) keys the entry; E and topk set the routing
+                jobs += [(op, fmt, (T, N, K), True, (E, k)) for E, k, T, N, K in moe_shapes]
+            else:
+                jobs += [(op, fmt, s, packed, None) for s in shapes for packed in layouts]
+    for op, fmt, (M, N, K), packed, moe in jobs:
         if w8.lookup_config(fmt, M, N, K, packed=packed, op=op) is not None:
             skipped += 1
             continue
@@ -76,9 +96,14 @@ def main(argv=None):
             print(f"[tune] time budget reached after {done} shapes", flush=True)
             print(f"[tune] tuned {done}, kept {skipped}, table {a.out}", flush=True)
             return 0
-        best, st = w8.tune_shape(fmt, M, N, K, rotate_bytes=a.rotate_mib << 20,
-                                 replays=a.replays, max_split_k=a.max_split_k, insert=True,
-                                 packed=packed, stream_k=a.stream_k, op=op, top_n=a.top_n)
+        if moe:
+            best, st = w8.moe_tune(fmt, moe[0], M, N, K, moe[1], rotate_bytes=a.rotate_mib << 20,
+                                   replays=a.replays, max_split_k=a.max_split_k, insert=True,
+                                   packed=True)
+        else:
+            best, st = w8.tune_shape(fmt, M, N, K, rotate_bytes=a.rotate_mib << 20,
+                                     replays=a.replays, max_split_k=a.max_split_k, insert=True,
+                                     packed=packed, stream_k=a.stream_k, op=op, top_n=a.top_n)
         w8.save_config_table(a.out)
         done += 1
         print(f"[tune] {op} {fmt} {'packed' if packed else 'row'} {M}x{N}x{K}: {best} "

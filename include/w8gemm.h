@@ -67,12 +67,14 @@ extern "C" {
 
 typedef void *w8_stream; /* hipStream_t */
 
-/* The two operations configs are tuned for: the GEMM on quantized
- * activations (w8_gemm_w8a8), and the whole linear layer with activation
- * quantization fused into the GEMM (w8_linear).                            */
+/* The operations configs are tuned for: the GEMM on quantized activations
+ * (w8_gemm_w8a8), the whole linear layer (w8_linear), and the MoE grouped
+ * GEMM (w8_moe_gemm; its table entries hold the token count T in the M
+ * field, and take w8_moe_tune, not w8_tune_shape).                          */
 typedef enum {
     W8_OP_GEMM = 0,
-    W8_OP_LINEAR = 1
+    W8_OP_LINEAR = 1,
+    W8_OP_MOE = 2
 } w8_op;
 
 typedef enum {
@@ -294,8 +296,9 @@ w8_status w8_linear(w8_fmt fmt, int M, int N, int K, const void *x, int64_t ldx,
                     void *ws, size_t ws_bytes, w8_stream stream);
 
 /* ---------------------------------------------------------------- config -- */
-/* W8_OK if cfg is a valid configuration of operation op for (fmt, M, N, K),
- * else W8_E_INVALID (with the reason in w8_last_error()).                   */
+/* W8_OK if cfg is a valid configuration of operation op (GEMM or LINEAR;
+ * grouped configs take w8_moe_validate_config) for (fmt, M, N, K), else
+ * W8_E_INVALID (with the reason in w8_last_error()).                        */
 w8_status w8_validate_config(w8_fmt fmt, w8_op op, int M, int N, int K, const w8_cfg *cfg);
 
 /* The built-in rule-of-thumb configuration of op for (fmt, M, N, K): fixed
@@ -337,7 +340,9 @@ void w8_clear_config_table(void);
 int w8_config_table_size(void);
 /* Entries of the last load that were skipped for a foreign arch or abi. */
 int w8_config_table_foreign(void);
-/* Insert or replace one entry for this device (validated first). */
+/* Insert or replace one entry for this device (validated first; a MOE
+ * entry against the GEMM rules at M = T, and again against the grouped
+ * kernel's rules when w8_moe_config reads it). */
 w8_status w8_set_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed,
                         const w8_cfg *cfg, double us_per_call);
 /* Exact lookup for this device: W8_OK on a hit (with the entry's time per
@@ -438,13 +443,28 @@ w8_status w8_moe_workspace_size(w8_fmt fmt, int E, int T, int N, int K, int max_
 /* W8_OK if cfg is valid for w8_moe_gemm with these sizes and layout.       */
 w8_status w8_moe_validate_config(w8_fmt fmt, int E, int N, int K, int max_m, int packed,
                                  const w8_cfg *cfg);
-/* The config w8_moe_gemm uses for cfg == NULL: tile_n 32, one K-wave
- * (two, with unroll 2, for T <= 2), no split, no x_lds -- the fastest on
- * 128-expert top-8 layers measured at 1..32 tokens -- or, where that is
- * invalid, the cost model's fastest valid config for a GEMM of
- * N x min(E, 8 T) columns (the experts T tokens reach with up to 8 each).  */
+/* The config w8_moe_gemm uses for cfg == NULL: the table entry for
+ * (fmt, W8_OP_MOE, layout, T, N, K) if it is valid for E and max_m; else
+ * tile_n 32, one K-wave (two, with unroll 2, for T <= 2), no split, no
+ * x_lds -- the fastest on 128-expert top-8 layers measured at 1..32
+ * tokens -- or, where that is invalid, the cost model's fastest valid config
+ * for a GEMM of N x min(E, 8 T) columns (the experts T tokens reach with up
+ * to 8 each).  *from_table (may be NULL) is 1 for a table entry.           */
 w8_status w8_moe_config(w8_fmt fmt, int E, int T, int N, int K, int max_m, int packed,
-                        w8_cfg *out);
+                        w8_cfg *out, int *from_table);
+
+/* Ahead-of-time tuning of the MoE grouped GEMM for E experts of (N, K) at T
+ * tokens routed top-k (1 <= topk <= E): the grouped GEMM's configs
+ * (w8_moe_validate_config with max_m = T), each checked against the default
+ * config's output and timed like w8_tune_shape's candidates, as graphs of
+ * calls over rotating weight copies and seeded uniform top-k routings (up
+ * to 64 calls, each with its own routing, so that the experts one graph
+ * reaches span opts->rotate_bytes);
+ * opts as for w8_tune_shape (op, stream_k and top_n ignored).  The winner is
+ * inserted as the (fmt, W8_OP_MOE, layout, T, N, K) entry when
+ * opts->insert.  Allocates and synchronizes.                              */
+w8_status w8_moe_tune(w8_fmt fmt, int E, int T, int N, int K, int topk,
+                      const w8_tune_opts *opts, w8_cfg *best, w8_tune_stats *stats);
 
 #ifdef __cplusplus
 }

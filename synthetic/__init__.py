@@ -81,6 +81,15 @@ SWEEP = (
 )
 
 
+# MoE layers of the Qwen3 family's MoE models (the pages measure Qwen3
+# models): 128 experts, top-8 routing, hidden size 2048 and expert width 768,
+# i.e. the experts' gate/up projection (N = 1536, K = 2048) and down
+# projection (N = 2048, K = 768), at decode token counts.
+MOE_E, MOE_TOPK = 128, 8
+MOE_SHAPES = (("gate_up", 1536, 2048), ("down", 2048, 768))
+MOE_TOKENS = (1, 4, 16, 32)
+
+
 def activations_extreme(fmt: str, M: int, K: int) -> np.ndarray:
     """bf16 X [M, K] whose rows span the magnitudes an activation quantizer
     meets at the edges of bf16: row r is N(0, 1) scaled by 2^e with e cycling

@@ -539,10 +539,52 @@ def test_moe_workspace_and_default(w8):
     for fmt in w8.FORMATS:
         for (E, T, N, K, m) in ((128, 16, 1536, 2048, 32), (8, 1, 4096, 4096, 1),
                                 (64, 32, 2048, 768, 16)):
-            c = w8.moe_config(fmt, E, T, N, K, m, packed=True)
-            assert lib_ok(w8, fmt, E, N, K, m, c)
+            c, hit = w8.moe_config(fmt, E, T, N, K, m, packed=True)
+            assert lib_ok(w8, fmt, E, N, K, m, c) and hit in (0, 1)
 
 
 def lib_ok(w8, fmt, E, N, K, m, c):
     st = w8._lib.w8_moe_validate_config(w8.FORMATS[fmt], E, N, K, m, 1, ctypes.byref(c))
     return st == 0
+
+
+def test_moe_table_entries(w8, tmp_path):
+    """A "moe" entry keyed by the token count T is what moe_config returns
+    when the grouped kernel runs it; otherwise the fallback is used."""
+    fmt, E, T, N, K = "FP8_Dynamic", 128, 4, 1536, 2048
+    base, hit = w8.moe_config(fmt, E, T, N, K, T, packed=True)
+    assert hit == 0
+    c = w8.Config.make(tile_n=16, waves_k=4, unroll=2, split_k=1)
+    assert c != base
+    w8.set_config(fmt, T, N, K, c, 9.5, packed=True, op="moe")
+    assert w8.lookup_config(fmt, T, N, K, packed=True, op="moe") == c
+    assert w8.lookup_config(fmt, T, N, K, packed=True) is None        # not a GEMM entry
+    got, hit = w8.moe_config(fmt, E, T, N, K, T, packed=True)
+    assert hit == 1 and got == c
+    assert w8.moe_config(fmt, E, T, N, K, T, packed=False)[1] == 0     # other layout
+    assert w8.moe_config(fmt, E, 8, N, K, 8, packed=True)[1] == 0      # other T: exact keys only
+    # an entry the grouped kernel does not compile (waves_k 16) is passed over
+    bad = w8.Config.make(tile_n=16, waves_k=16, unroll=1, split_k=1)
+    w8.set_config(fmt, T, N, K, bad, 9.0, packed=True, op="moe")
+    got, hit = w8.moe_config(fmt, E, T, N, K, T, packed=True)
+    assert hit == 0 and got == base
+    w8.set_config(fmt, T, N, K, c, 9.5, packed=True, op="moe")
+    p = tmp_path / "m.tbl"
+    w8.save_config_table(str(p))
+    assert " moe packed 4 1536 2048 " in p.read_text()
+    w8.clear_config_table()
+    w8.load_config_table(str(p))
+    assert w8.moe_config(fmt, E, T, N, K, T, packed=True) == (c, 1)
+    with pytest.raises(w8.W8Error):   # grouped configs are checked by the grouped rules
+        w8.validate_config(fmt, T, N, K, c, op="moe")
+    assert w8._lib.w8_moe_validate_config(w8.FORMATS[fmt], E, N, K, T, 1, ctypes.byref(c)) == 0
+
+
+def test_moe_tune_argument_errors(w8, lib):
+    best, stats = w8.Config(), w8._capi.TuneStats()
+    t = lib.w8_moe_tune
+    assert t(0, 0, 4, 1536, 2048, 1, None, ctypes.byref(best), ctypes.byref(stats)) == 1   # E
+    assert t(0, 8, 4, 1536, 2048, 9, None, ctypes.byref(best), ctypes.byref(stats)) == 1   # topk > E
+    assert t(0, 8, 4, 1536, 2048, 0, None, ctypes.byref(best), ctypes.byref(stats)) == 1   # topk
+    assert t(0, 8, 33, 1536, 2048, 2, None, ctypes.byref(best), ctypes.byref(stats)) != 0  # T > 32
+    assert t(0, 8, 4, 1536, 2048, 2, None, None, ctypes.byref(stats)) == 1                # best

@@ -185,3 +185,56 @@ def test_moe_many_experts_and_graph_replay(w8):
         g.replay()
         torch.cuda.synchronize()
         assert same_bits(y, eager), f"replay {i}"
+
+
+@pytest.mark.parametrize("proj,N,K", [("gate_up", 1536, 2048), ("down", 2048, 768)])
+def test_moe_bench_size_sampled(w8, proj, N, K):
+    """The benchmark's MoE layers at full size (128 experts, top-8 of 32
+    tokens, packed weights, the default config): W8A8_INT8, whose weight codes
+    are given, against the oracle on a sample of routed entries (every entry
+    of 6 experts)."""
+    fmt, T, E = "W8A8_INT8", 32, 128
+    print(f"[moe] bench size {proj} {N}x{K}", flush=True)
+    g = np.random.Generator(np.random.PCG64(77))
+    wq = g.integers(-127, 128, size=(E, N, K), dtype=np.int8)
+    sw = g.uniform(0.001, 0.01, size=(E, N)).astype(np.float32)
+    bits = synthetic.activations(fmt, T, N, K)
+    xq, sx = w8.quantize_act(fmt, to_bf16_tensor(bits))
+    xq_ref, sx_ref = oracle.quantize_act(fmt, bits)
+    offsets, rows = synthetic.moe_routing(T, E, 8, seed=3)
+    packed = w8.pack_experts(fmt, torch.from_numpy(wq).to(DEV))
+    y = w8.moe_gemm(fmt, xq, sx, torch.from_numpy(offsets).to(DEV),
+                    torch.from_numpy(rows).to(DEV), packed, torch.from_numpy(sw).to(DEV))
+    torch.cuda.synchronize()
+    got = y.float().cpu().numpy()
+    active = [e for e in range(E) if offsets[e + 1] > offsets[e]]
+    for e in active[::max(1, len(active) // 6)][:6]:
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        r = rows[a:b]
+        Y = oracle.gemm(fmt, xq_ref[r], sx_ref[r], wq[e].view(np.uint8), sw[e])
+        assert_bf16_close(torch.from_numpy(got[a:b]), Y, f"moe bench size expert {e}")
+
+
+def test_moe_tune_inserts_a_validated_entry(w8):
+    """The grouped GEMM's tuner: candidates validated against the fallback
+    config (one forced to fail is dropped), the winner inserted as the "moe"
+    entry for (T, N, K), and picked up by moe_gemm's cfg=None path, whose
+    output then matches the oracle."""
+    fmt, E, T, N, K, topk = "FP8_Dynamic", 16, 4, 512, 1024, 2
+    w8.clear_config_table()
+    try:
+        best, stats = w8.moe_tune(fmt, E, T, N, K, topk, warmup=1, replays=3,
+                                  rotate_bytes=64 << 20, packed=True, fail_candidate=0)
+        print(f"[moe] tune: {stats}", flush=True)
+        assert stats["candidates"] > 10 and stats["rejected"] >= 1
+        assert stats["validated"] + stats["rejected"] == stats["candidates"]
+        assert stats["best_index"] != 0 and stats["best_us_bank2"] > 0
+        cfg, hit = w8.moe_config(fmt, E, T, N, K, T, packed=True)
+        assert hit == 1 and cfg == best
+        cs = MoeCase(w8, fmt, T=T, E=E, N=N, K=K, topk=topk, seed=9, max_m=T)
+        y = w8.moe_gemm(fmt, cs.xq, cs.sx, cs.offsets, cs.rows, cs.packed, cs.sw, max_m=T)
+        torch.cuda.synchronize()
+        assert_bf16_close(y, cs.Y, "moe with the tuned entry")
+    finally:
+        w8.clear_config_table()
+        w8.load_default_table()
