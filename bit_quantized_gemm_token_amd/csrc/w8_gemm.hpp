@@ -720,15 +720,52 @@ __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
   gemm_body<FMT, MB, NB, WK, WN, U, SWAP, PACKED, XL, false>(a, nullptr, 0);
 }
 
-// MoE grouped GEMM: blockIdx.y is the expert; its rows are entries
-// [offsets[e], offsets[e+1]) of the routing (at most 16 * MB of them are
-// computed), its weights, weight scales and shared-tile workspace are at the
-// expert's strides, and its outputs are rows offsets[e].. of Y.
+// An expert's entry count with its offsets clamped to the row list (so bad
+// routing reads and writes nothing outside it).
+__device__ __forceinline__ int moe_count(const MoeArgs& m, int e) {
+  return min(m.offsets[e + 1], m.n_rows) - min(max(m.offsets[e], 0), m.n_rows);
+}
+
+// Compact grid: the slot-th expert, in expert order, with a positive count,
+// or -1 if fewer experts have entries.  Every lane reads the offsets of
+// four experts at once (E <= 256), so the search costs one round trip; the
+// ballots make the result wave-uniform, and every wave of the workgroup
+// computes the same value.
+__device__ __forceinline__ int moe_active_expert(const MoeArgs& m, int slot) {
+  const int lane = threadIdx.x & 63;
+  bool act[kMoeCompactMaxE / 64];
+#pragma unroll
+  for (int i = 0; i < kMoeCompactMaxE / 64; ++i) {
+    const int e = 64 * i + lane;
+    act[i] = e < m.n_experts && moe_count(m, e) > 0;
+  }
+  int j = slot;
+#pragma unroll
+  for (int i = 0; i < kMoeCompactMaxE / 64; ++i) {
+    const unsigned long long b = __ballot(act[i]);
+    const int c = __popcll(b);
+    if (j < c) {
+      const unsigned long long below = b & ((1ull << lane) - 1ull);
+      const unsigned long long hit = __ballot(act[i] && __popcll(below) == j);
+      return 64 * i + __builtin_ctzll(hit);
+    }
+    j -= c;
+  }
+  return -1;
+}
+
+// MoE grouped GEMM: blockIdx.y is the expert (compact grid: the
+// blockIdx.y-th expert with entries); its rows are entries [offsets[e],
+// offsets[e+1]) of the routing (at most 16 * MB of them are computed), its
+// weights, weight scales and shared-tile workspace are at the expert's
+// strides, and its outputs are rows offsets[e].. of Y.
 template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL>
 __global__ __launch_bounds__(64 * WK * WN) void moe_gemm_kernel(GemmArgs a, MoeArgs m) {
-  const int e = blockIdx.y;
-  // (offsets clamped to the row list, so bad routing reads and writes nothing
-  // outside it)
+  int e = blockIdx.y;
+  if (m.compact) {
+    e = moe_active_expert(m, e);
+    if (e < 0) return;
+  }
   const int off = min(max(m.offsets[e], 0), m.n_rows);
   const int rows = min(min(m.offsets[e + 1], m.n_rows) - off, 16 * MB);
   if (rows <= 0) return;  // an expert no token was routed to

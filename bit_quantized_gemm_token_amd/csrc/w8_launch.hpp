@@ -70,7 +70,13 @@ struct MoeArgs {
   long long part_stride;   // bytes between two experts' partials in the workspace
   int xrow_max;            // activation rows - 1 (row ids are clamped to [0, xrow_max])
   int n_rows;              // entries in `rows` (offsets are clamped to [0, n_rows])
+  int n_experts;           // E
+  int compact;             // 1: grid.y < E slots, slot j runs the j-th expert with entries
 };
+
+// Largest E for the compact grid (each lane of a wave reads the offsets of
+// kMoeCompactMaxE / 64 experts at once).
+constexpr int kMoeCompactMaxE = 256;
 
 typedef hipError_t (*MoeLaunchFn)(const GemmArgs&, const MoeArgs&, dim3 grid, dim3 block,
                                   hipStream_t);

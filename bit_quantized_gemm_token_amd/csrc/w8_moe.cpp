@@ -183,12 +183,17 @@ w8_status launch_moe_call(const MoeCall& g, const w8_cfg& c, hipStream_t s) {
   m.part_stride = (long long)part_stride(fmt, max_m, N, K, c);
   m.xrow_max = T - 1;
   m.n_rows = g.n_rows;
+  m.n_experts = E;
+  // With ascending offsets at most n_rows experts have entries: below E, a
+  // grid of n_rows expert slots replaces one of E experts that mostly exit.
+  m.compact = E <= kMoeCompactMaxE && g.n_rows > 0 && g.n_rows < E;
+  const unsigned gy = m.compact ? (unsigned)g.n_rows : (unsigned)E;
   if (need > 0) {
     a.counters = static_cast<unsigned int*>(g.ws);
     a.part = static_cast<char*>(g.ws) + ws_counter_bytes(ntiles);
   }
   const unsigned wgs = c.grid > 0 ? (unsigned)c.grid : (unsigned)(ntiles * c.split_k);
-  hipError_t e = moe_fn(fmt, max_m, packed, c)(a, m, dim3(wgs, (unsigned)E),
+  hipError_t e = moe_fn(fmt, max_m, packed, c)(a, m, dim3(wgs, gy),
                                               dim3(64 * c.waves_k * c.waves_n),
                                               s);
   if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("MoE GEMM launch", e));

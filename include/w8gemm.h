@@ -411,12 +411,16 @@ w8_status w8_profile_configs(w8_fmt fmt, int M, int N, int K, const w8_tune_opts
  * with expert e's weight codes Wq_e and scales sw_e in the format's
  * layout -- the GEMM of w8_gemm_w8a8 on the gathered rows, per expert.  One
  * kernel launch covers all experts (no host synchronization: the routing is
- * read on the device); an expert with no entry reads no weights.
+ * read on the device); an expert with no entry reads no weights.  When
+ * 0 < n_rows < E <= 256 the launch holds n_rows expert slots instead of E
+ * (ascending offsets leave at most n_rows experts with entries), slot j
+ * running the j-th expert that has entries.
  *   offsets  int32 [E + 1] (device), ascending, offsets[0] = 0,
  *            offsets[E] = n_rows; each expert's count offsets[e+1] -
  *            offsets[e] must be <= max_m (rows past 16 ceil(max_m/16) of an
  *            expert are not computed).  Offsets are clamped to [0, n_rows],
- *            so bad routing never reads or writes outside rows and y.
+ *            so bad routing never reads or writes outside rows and y (it
+ *            may leave entries unwritten).
  *   rows     int32 [n_rows] (device), each in [0, T) (clamped if not)
  *   max_m    bound on any expert's count, 1..32 (else W8_E_UNSUPPORTED);
  *            kernels for ceil(max_m / 16) row blocks run

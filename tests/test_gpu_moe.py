@@ -238,3 +238,36 @@ def test_moe_tune_inserts_a_validated_entry(w8):
     finally:
         w8.clear_config_table()
         w8.load_default_table()
+
+
+@pytest.mark.parametrize("fmt", ["W8A8_INT8", "Block_FP8"])
+def test_moe_compact_expert_grid(w8, fmt):
+    """Fewer routed entries than experts (E <= 256): the launch holds one slot
+    per entry and slot j runs the j-th expert with entries.  Routings that put
+    entries at the edges of every 64-expert chunk of E = 256, a single entry
+    among 200 experts, and E = 300 (above the compact bound: one slot per
+    expert) all equal the per-expert GEMM bit for bit and the oracle."""
+    N, K = 160, 512
+    experts = [0, 63, 64, 127, 128, 191, 192, 255]
+    per = {e: [i % 3] for i, e in enumerate(experts)}      # 8 entries of 3 tokens
+    per[64].append(2)
+    off = np.zeros(257, np.int32)
+    for e in range(256):
+        off[e + 1] = off[e] + len(per.get(e, []))
+    rows = np.array([t for e in range(256) for t in per.get(e, [])], np.int32)
+    cases = [dict(T=3, E=256, routing=(off, rows)),
+             dict(T=1, E=200, routing=(np.r_[np.zeros(138, np.int32),
+                                             np.ones(63, np.int32)], np.zeros(1, np.int32))),
+             dict(T=2, E=300, topk=2, seed=4)]
+    for kw in cases:
+        cs = MoeCase(w8, fmt, N=N, K=K, **kw)
+        assert len(cs.rows_np) < cs.E
+        for packed in (False, True):
+            for ckw in (CFGS[0], CFGS[1], CFGS[2]):
+                cfg = w8.Config.make(**ckw)
+                y = w8.moe_gemm(fmt, cs.xq, cs.sx, cs.offsets, cs.rows, cs.weights(packed),
+                                cs.sw, max_m=cs.T, cfg=cfg)
+                ref = cs.per_expert(w8, cfg, packed)
+                torch.cuda.synchronize()
+                assert same_bits(y, ref), f"{fmt} E={cs.E} {ckw} packed={packed}"
+                assert_bf16_close(y, cs.Y, f"compact {fmt} E={cs.E} {ckw}")
