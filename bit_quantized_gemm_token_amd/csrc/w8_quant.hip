@@ -4,9 +4,11 @@
 // guadagni fino al 10%", paragraph 1 (the formats) and paragraph 8
 // (quantization as an auxiliary kernel beside the GEMM).  Every group uses
 // s = amax / Qmax (an all-zero group takes s = 1) and codes
-// round-to-nearest-even(x / s) with saturation; the division is the
-// correctly rounded fp32 division (the library is built with
-// -fhip-fp32-correctly-rounded-divide-sqrt and without fast-math).
+// round-to-nearest-even(x / s) with saturation.  s is the correctly rounded
+// fp32 division (the library is built with
+// -fhip-fp32-correctly-rounded-divide-sqrt and without fast-math); x / s
+// takes the reciprocal-and-correction form of encode8, which gives the
+// codes of the correctly rounded quotient.
 #include "w8_device.hpp"
 #include "w8_launch.hpp"
 

@@ -1,11 +1,13 @@
 // Per-shape config table (ai-radar.it, "Helion nel backend vLLM", paragraphs
 // 6-7: tuned configs are shipped per shape, with a default config for shapes
-// that have none).  Lookup is exact on (arch, abi, fmt, weight layout, M, N,
-// K); a miss, or an entry written for another arch or ABI (kept in the file,
-// never used), falls back to the default config
-// (the hard-fallback cases of TensorRT-LLM issue 16363, "Suggested
-// direction", that apply to a table: cache miss and backend identity
-// mismatch).
+// that have none).  Entries are keyed by (arch, abi, fmt, op, weight layout,
+// M, N, K), M being the token count T for the MoE op.  A GEMM or linear
+// lookup that misses, or finds only entries written for another arch or ABI
+// (kept in the file, never used), falls back to an entry of the same
+// floor(log2 M) bucket and then to the cost model's pick (the hard-fallback
+// cases of TensorRT-LLM issue 16363, "Suggested direction", that apply to a
+// table: cache miss and backend identity mismatch); the MoE op reads exact
+// entries only.
 #include <cerrno>
 #include <cstdio>
 #include <cstdlib>

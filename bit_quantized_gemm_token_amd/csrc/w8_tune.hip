@@ -301,23 +301,23 @@ struct Harness {
 };
 
 // Seeded uniform top-k routing of T tokens over E experts (each token to
-// topk distinct experts, drawn by xorshift64 rejection), as w8_moe_gemm's
-// (offsets, rows) lists: E + 1 offsets, then T * topk token ids grouped by
-// expert in token order.
+// topk distinct experts: a partial Fisher-Yates shuffle of the expert ids
+// driven by xorshift64), as w8_moe_gemm's (offsets, rows) lists: E + 1
+// offsets, then T * topk token ids grouped by expert in token order.
 std::vector<int> make_routing(int E, int T, int topk, uint64_t seed) {
   std::vector<std::vector<int>> per(E);
   uint64_t s = seed * 0x9E3779B97F4A7C15ULL + 0x2545F4914F6CDD1DULL;
-  std::vector<int> pick;
+  std::vector<int> ids(E);
   for (int t = 0; t < T; ++t) {
-    pick.clear();
-    while ((int)pick.size() < topk) {
+    for (int e = 0; e < E; ++e) ids[e] = e;
+    for (int k = 0; k < topk; ++k) {
       s ^= s << 13;
       s ^= s >> 7;
       s ^= s << 17;
-      const int e = (int)(s % (uint64_t)E);
-      if (std::find(pick.begin(), pick.end(), e) == pick.end()) pick.push_back(e);
+      const int j = k + (int)(s % (uint64_t)(E - k));
+      std::swap(ids[k], ids[j]);
+      per[ids[k]].push_back(t);
     }
-    for (int e : pick) per[e].push_back(t);
   }
   std::vector<int> out(E + 1, 0);
   for (int e = 0; e < E; ++e) {
