@@ -296,7 +296,8 @@ def moe_bench(w8, dev, rotate_bytes, warmup, reps):
     call j on weight copy j % R with routing seed j, so the distinct expert
     weights a graph reads exceed the last-level cache; beside it the same
     calls as one dense GEMM launch per active expert (rows gathered
-    beforehand).  us per call = median graph time / G."""
+    beforehand), and from the bf16 tokens: moe_linear (quantization fused)
+    and quantize_act + moe_gemm.  us per call = median graph time / G."""
     gen = torch.Generator(device=dev)
     gen.manual_seed(1234)
     rows_out = []
@@ -322,8 +323,11 @@ def moe_bench(w8, dev, rotate_bytes, warmup, reps):
                                   torch.from_numpy(rows).to(dev), off, rows))
                 # an expert holds at most T rows (top-k picks distinct experts)
                 cfg, from_table = w8.moe_config(fmt, MOE_E, T, N, K, T, packed=True)
+                cfg_l, from_table_l = w8.moe_linear_config(fmt, MOE_E, T, N, K, T, packed=True)
                 ws = w8.Workspace(dev, max(256, w8.moe_workspace_size(fmt, MOE_E, T, N, K, T, cfg,
-                                                                      packed=True)))
+                                                                      packed=True),
+                                           w8.moe_workspace_size(fmt, MOE_E, T, N, K, T, cfg_l,
+                                                                 packed=True)))
                 y = torch.empty((T * MOE_TOPK, N), dtype=torch.bfloat16, device=dev)
                 # per-expert dense launches: gathered rows and configs prepared up front
                 dense = []
@@ -342,17 +346,29 @@ def moe_bench(w8, dev, rotate_bytes, warmup, reps):
                 stream = torch.cuda.Stream(dev)
                 stream.wait_stream(torch.cuda.current_stream(dev))
                 g_moe, g_dense = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+                g_lin, g_qm = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g_moe, stream=stream):
                     for wt, offt, rowst, _, _ in calls:
                         w8.moe_gemm(fmt, xq, sx, offt, rowst, wt, sw, max_m=T, cfg=cfg, y=y,
                                     workspace=ws)
+                # from bf16 tokens: fused (moe_linear), and quantize_act + moe_gemm
+                with torch.cuda.graph(g_lin, stream=stream):
+                    for wt, offt, rowst, _, _ in calls:
+                        w8.moe_linear(fmt, x, offt, rowst, wt, sw, max_m=T, cfg=cfg_l, y=y,
+                                      workspace=ws)
+                with torch.cuda.graph(g_qm, stream=stream):
+                    for wt, offt, rowst, _, _ in calls:
+                        xq2, sx2 = w8.quantize_act(fmt, x)
+                        w8.moe_gemm(fmt, xq2, sx2, offt, rowst, wt, sw, max_m=T, cfg=cfg, y=y,
+                                    workspace=ws)
                 with torch.cuda.graph(g_dense, stream=stream):
                     for d in dense:
                         w8.gemm_w8a8(fmt, d[0], d[1], d[2], d[3], cfg=d[5], y=d[4], workspace=wsd)
-                t = {"moe": [], "dense": []}
+                t = {"moe": [], "dense": [], "linear": [], "quant_moe": []}
                 with torch.cuda.stream(stream):
                     for i in range(warmup + reps):
-                        for key, gr in (("moe", g_moe), ("dense", g_dense)):
+                        for key, gr in (("moe", g_moe), ("dense", g_dense), ("linear", g_lin),
+                                        ("quant_moe", g_qm)):
                             e0 = torch.cuda.Event(enable_timing=True)
                             e1 = torch.cuda.Event(enable_timing=True)
                             e0.record(stream)
@@ -361,19 +377,23 @@ def moe_bench(w8, dev, rotate_bytes, warmup, reps):
                             e1.synchronize()
                             if i >= warmup:
                                 t[key].append(e0.elapsed_time(e1) * 1e3 / G)
-                us = sorted(t["moe"])[len(t["moe"]) // 2]
-                us_d = sorted(t["dense"])[len(t["dense"]) // 2]
+                us, us_d, us_l, us_qm = (sorted(t[k])[len(t[k]) // 2]
+                                         for k in ("moe", "dense", "linear", "quant_moe"))
                 n_act = np.mean([int((np.diff(c[3]) > 0).sum()) for c in calls])
                 byts = n_act * (N * K + 4 * nsw) + T * K + T * MOE_TOPK * N * 2
                 rows_out.append({"fmt": fmt, "proj": name, "N": N, "K": K, "T": T,
                                  "active_experts": float(n_act), "calls": G, "copies": R,
                                  "cfg": cfg.as_dict(), "cfg_from_table": bool(from_table),
-                                 "us": round(us, 3),
+                                 "cfg_linear": cfg_l.as_dict(),
+                                 "cfg_linear_from_table": bool(from_table_l),
+                                 "us": round(us, 3), "us_linear": round(us_l, 3),
+                                 "us_quant_plus_moe": round(us_qm, 3),
                                  "us_per_expert_launches": round(us_d, 3),
                                  "gbps": round(byts / (us * 1e3), 1)})
                 log(f"[moe] {fmt} {name} T={T}: {us:.2f} us ({byts / (us * 1e3):.0f} GB/s), "
-                    f"per-expert launches {us_d:.2f} us, {n_act:.0f} experts active")
-                del g_moe, g_dense, dense
+                    f"per-expert launches {us_d:.2f} us, {n_act:.0f} experts active; from bf16: "
+                    f"fused {us_l:.2f} us, quantize + grouped {us_qm:.2f} us")
+                del g_moe, g_dense, g_lin, g_qm, dense
             del weights
             torch.cuda.empty_cache()
     return {"workload": f"{MOE_E} experts, top-{MOE_TOPK}, gate_up 1536x2048 and down 2048x768, "
@@ -383,6 +403,9 @@ def moe_bench(w8, dev, rotate_bytes, warmup, reps):
             "geomean_gbps": round(geomean([r["gbps"] for r in rows_out]), 1),
             "geomean_speedup_vs_per_expert_launches": round(
                 geomean([r["us_per_expert_launches"] / r["us"] for r in rows_out]), 3),
+            "geomean_us_linear_fused": round(geomean([r["us_linear"] for r in rows_out]), 3),
+            "geomean_us_quant_plus_moe": round(
+                geomean([r["us_quant_plus_moe"] for r in rows_out]), 3),
             "rows": rows_out}
 
 

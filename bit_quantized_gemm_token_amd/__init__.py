@@ -33,7 +33,8 @@ __all__ = ["Config", "W8Error", "UnsupportedShape", "Workspace", "PackedWeight",
            "validate_config", "default_config", "resolve_config", "lookup_config",
            "set_config", "load_config_table", "save_config_table", "clear_config_table",
            "config_table_size", "config_table_foreign", "tune_shape", "rank_configs",
-           "profile_configs", "model_config", "moe_gemm", "moe_config", "moe_tune", "moe_workspace_size",
+           "profile_configs", "model_config", "moe_gemm", "moe_config", "moe_tune",
+           "moe_workspace_size", "moe_linear", "moe_linear_config",
            "pack_experts", "PackedExperts", "FORMATS", "MAX_M",
            "MAX_SPLIT_K", "GROUP", "ABI_VERSION"]
 
@@ -359,14 +360,25 @@ def moe_config(fmt, E, T, N, K, max_m=32, packed=False):
     return c, hit.value
 
 
+def moe_linear_config(fmt, E, T, N, K, max_m=32, packed=False):
+    """(config moe_linear uses when cfg is None, 1 if it is the table's
+    "moe_linear" entry for (T, N, K) else 0)."""
+    c = Config()
+    hit = ctypes.c_int(0)
+    _check(_lib.w8_moe_linear_config(_fmt(fmt), E, T, N, K, max_m, int(bool(packed)),
+                                     ctypes.byref(c), ctypes.byref(hit)))
+    return c, hit.value
+
+
 def moe_tune(fmt, E, T, N, K, topk, warmup=2, replays=5, bank2_top=5, rotate_bytes=512 << 20,
-             max_split_k=MAX_SPLIT_K, insert=True, fail_candidate=-1, packed=False):
+             max_split_k=MAX_SPLIT_K, insert=True, fail_candidate=-1, packed=False, fused=False):
     """Ahead-of-time tuning of the grouped GEMM for E experts of (N, K) at T
-    tokens routed top-k (seeded uniform routings); the winner becomes the
-    table's "moe" entry for (T, N, K) when insert.  Returns (Config, stats
-    dict).  Synchronizes the device."""
+    tokens routed top-k (seeded uniform routings); fused=True tunes
+    moe_linear (quantization fused) instead of moe_gemm.  The winner becomes
+    the table's "moe" (or "moe_linear") entry for (T, N, K) when insert.
+    Returns (Config, stats dict).  Synchronizes the device."""
     o = _tune_opts(warmup, replays, bank2_top, rotate_bytes, max_split_k, insert,
-                   fail_candidate, packed, False, "gemm", 0)
+                   fail_candidate, packed, False, "linear" if fused else "gemm", 0)
     best = Config()
     stats = TuneStats()
     _check(_lib.w8_moe_tune(_fmt(fmt), E, T, N, K, topk, ctypes.byref(o), ctypes.byref(best),
@@ -420,6 +432,49 @@ def moe_gemm(fmt, xq, sx, offsets, rows, wq, sw, max_m=32, cfg=None, y=None, wor
                             _dev_ptr(sw, "sw", torch.float32), sw.stride(0),
                             _dev_ptr(y, "y"), _row_major(y, "y"), _cfg_ptr(cfg), ws_ptr, ws_bytes,
                             _stream(stream, xq.device)))
+    return y
+
+
+def moe_linear(fmt, x, offsets, rows, wq, sw, max_m=32, cfg=None, y=None, workspace=None,
+               stream=None):
+    """MoE grouped GEMM on bf16 tokens x [T, K] with the activation
+    quantization fused into the grouped kernel: equals quantize_act(x) then
+    moe_gemm with the same config, bit for bit.  cfg: a grouped config with
+    x_lds=1 and waves_k <= 4, or None (moe_linear_config).  Other arguments as
+    for moe_gemm.  One launch, no host sync."""
+    f = _fmt(fmt)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    ldx = _row_major(x, "x")
+    T, K = x.shape
+    E, N, wk, ldw, w_stride, wptr, packed = _experts(f, wq)
+    if wk != K:
+        raise ValueError(f"K mismatch: x {tuple(x.shape)} vs experts' K {wk}")
+    if offsets.numel() != E + 1:
+        raise ValueError("offsets must hold E + 1 entries")
+    if sw.shape[0] != E or not sw.is_contiguous():
+        raise ValueError("sw must be a contiguous [E, ...] tensor")
+    if y is None:
+        y = torch.empty((rows.numel(), N), dtype=torch.bfloat16, device=x.device)
+    elif y.dtype != torch.bfloat16:
+        raise TypeError("y must be bfloat16")
+    elif y.shape[0] < rows.numel() or y.shape[1] != N:
+        raise ValueError(f"y must be [{rows.numel()}, {N}]")
+    if cfg is None:
+        cfg = moe_linear_config(f, E, T, N, K, max_m, packed)[0]
+    if workspace is None:
+        workspace = _default_workspace(x.device)
+    need = moe_workspace_size(f, E, T, N, K, max_m, cfg, packed)
+    ws_ptr, ws_bytes = (None, 0)
+    if need:
+        buf = workspace.reserve(need)
+        ws_ptr, ws_bytes = ctypes.c_void_p(buf.data_ptr()), buf.numel()
+    _check(_lib.w8_moe_linear(f, E, T, N, K, max_m, _dev_ptr(x, "x"), ldx,
+                              _dev_ptr(offsets, "offsets", torch.int32),
+                              _dev_ptr(rows, "rows", torch.int32), rows.numel(), wptr, ldw,
+                              w_stride, _dev_ptr(sw, "sw", torch.float32), sw.stride(0),
+                              _dev_ptr(y, "y"), _row_major(y, "y"), _cfg_ptr(cfg), ws_ptr,
+                              ws_bytes, _stream(stream, x.device)))
     return y
 
 

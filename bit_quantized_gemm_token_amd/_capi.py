@@ -11,7 +11,7 @@ MAX_SPLIT_K = 256
 GROUP = 128
 
 FORMATS = {"FP8_Dynamic": 0, "W8A8_INT8": 1, "Block_FP8": 2}
-OPS = {"gemm": 0, "linear": 1, "moe": 2}
+OPS = {"gemm": 0, "linear": 1, "moe": 2, "moe_linear": 3}
 FORMAT_NAMES = {v: k for k, v in FORMATS.items()}
 
 STATUS = {0: "W8_OK", 1: "W8_E_INVALID", 2: "W8_E_UNSUPPORTED", 3: "W8_E_WORKSPACE",
@@ -27,7 +27,8 @@ EXPORTS = ("w8_abi_version", "w8_status_string", "w8_last_error", "w8_quantize_a
            "w8_config_table_size", "w8_config_table_foreign", "w8_set_config",
            "w8_lookup_config", "w8_tune_shape", "w8_tune_default_opts", "w8_model_config",
            "w8_rank_configs", "w8_profile_configs", "w8_moe_gemm", "w8_moe_workspace_size",
-           "w8_moe_validate_config", "w8_moe_config", "w8_moe_tune")
+           "w8_moe_validate_config", "w8_moe_config", "w8_moe_tune", "w8_moe_linear",
+           "w8_moe_linear_config")
 
 
 class Config(ctypes.Structure):
@@ -161,4 +162,11 @@ def load():
     lib.w8_moe_tune.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int,
                                 ctypes.POINTER(TuneOpts), cfgp, ctypes.POINTER(TuneStats)]
     lib.w8_moe_tune.restype = st
+    lib.w8_moe_linear.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, vp, i64, vp, vp,
+                                  c_int, vp, i64, i64, f32p, i64, vp, i64, cfgp, vp,
+                                  ctypes.c_size_t, vp]
+    lib.w8_moe_linear.restype = st
+    lib.w8_moe_linear_config.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int, cfgp,
+                                         ctypes.POINTER(c_int)]
+    lib.w8_moe_linear_config.restype = st
     return lib

@@ -107,15 +107,16 @@ w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c) {
   if (c.x_lds != 0 && c.x_lds != 1) return fail(W8_E_INVALID, "cfg.x_lds must be 0 or 1");
   if (c.waves_n > 1 && !c.x_lds) return fail(W8_E_INVALID, "cfg: waves_n > 1 needs x_lds == 1");
   if (c.x_lds && c.waves_k > 8) return fail(W8_E_INVALID, "cfg: x_lds needs waves_k <= 8");
-  if (op != W8_OP_GEMM && op != W8_OP_LINEAR && op != W8_OP_MOE)
+  if (op != W8_OP_GEMM && op != W8_OP_LINEAR && op != W8_OP_MOE && op != W8_OP_MOE_LINEAR)
     return fail(W8_E_INVALID, "unknown op");
   if (c.quant_launch != 0 && c.quant_launch != 1)
     return fail(W8_E_INVALID, "cfg.quant_launch must be 0 or 1");
-  if (op != W8_OP_LINEAR && c.quant_launch)
-    return fail(W8_E_INVALID, "cfg.quant_launch is for the linear op only");
-  if (op == W8_OP_LINEAR && !c.quant_launch && (!c.x_lds || c.waves_k > 4))
+  if (op != W8_OP_LINEAR && op != W8_OP_MOE_LINEAR && c.quant_launch)
+    return fail(W8_E_INVALID, "cfg.quant_launch is for the linear ops only");
+  if ((op == W8_OP_LINEAR || op == W8_OP_MOE_LINEAR) && !c.quant_launch &&
+      (!c.x_lds || c.waves_k > 4))
     return fail(W8_E_INVALID,
-                "cfg: the fused linear op (quant_launch == 0) needs x_lds == 1 and waves_k <= 4");
+                "cfg: fused quantization (quant_launch == 0) needs x_lds == 1 and waves_k <= 4");
   if (u_index(c.unroll) < 0) return fail(W8_E_INVALID, "cfg.unroll must be 1, 2 or 4");
   if ((c.tile_n / 16) * c.unroll > 4)
     return fail(W8_E_INVALID, "cfg: tile_n/16 * unroll must be at most 4");
@@ -505,7 +506,8 @@ w8_status w8_validate_config(w8_fmt fmt, w8_op op, int M, int N, int K, const w8
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!cfg) return fail(W8_E_INVALID, "null cfg");
-  if (op == W8_OP_MOE) return fail(W8_E_INVALID, "grouped configs: w8_moe_validate_config");
+  if (op == W8_OP_MOE || op == W8_OP_MOE_LINEAR)
+    return fail(W8_E_INVALID, "grouped configs: w8_moe_validate_config");
   st = check_cfg(fmt, op, M, N, K, *cfg);
   if (st) return st;
   return ok();

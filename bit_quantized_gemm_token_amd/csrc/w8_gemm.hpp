@@ -150,7 +150,8 @@ __device__ __forceinline__ typename Traits<FMT>::Acc mma(typename Traits<FMT>::F
 
 // The body of one GEMM workgroup.  GROUPED (the MoE grouped GEMM): activation
 // row m of this call is row xrows[m] (clamped to [0, xrow_max]) of the
-// activation codes and scales; everything else is per call in `a`.
+// activation codes and scales (XL == 2: of the bf16 activations); everything
+// else is per call in `a`.
 template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL,
           bool GROUPED>
 __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xrows,
@@ -161,8 +162,8 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
   constexpr bool BLOCK = (FMT == BLOCK_FP8);
   static_assert(WN == 1 || WK == 1, "the waves of a workgroup split either K or N");
   static_assert(WN == 1 || XL, "waves side by side along N share activations through LDS");
-  static_assert(!GROUPED || XL != 2, "the grouped GEMM takes quantized activations");
-  // activation row (codes and scales) of row m of this call
+  // activation row (codes and scales, or XL == 2 the bf16 row) of row m of
+  // this call
   auto xr = [&](int m) -> long long {
     if constexpr (GROUPED)
       return min(max(xrows[m], 0), xrow_max);
@@ -409,7 +410,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
             const int e = (ka + kk) * KSTEP + 64 * jj + 16 * (lane >> 4);  // first element
             raw[q][jj][0] = raw[q][jj][1] = v4u{0u, 0u, 0u, 0u};
             if (u < nunits && e < a.K) {  // (K % 16 == 0: a chunk is wholly inside K or past it)
-              const uint16_t* src = xb + (long long)row * a.ldq + e;
+              const uint16_t* src = xb + xr(row) * a.ldq + e;
               raw[q][jj][0] = *reinterpret_cast<const v4u*>(src);
               raw[q][jj][1] = *reinterpret_cast<const v4u*>(src + 8);
             }
@@ -462,7 +463,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
           const int step = 64 * wpr;
           for (int slot = wave; slot < a.M * wpr; slot += nw) {
             const int m = slot / wpr, part = slot - m * wpr;
-            const uint16_t* rowp = xb + (long long)m * a.ldq;
+            const uint16_t* rowp = xb + xr(m) * a.ldq;
             float mx = 0.0f;
             constexpr int QA = WK * WN >= 8 ? 2 : 4;  // loads in flight per lane (registers)
             for (int c0 = part * 64 + lane; c0 < cpr; c0 += QA * step) {

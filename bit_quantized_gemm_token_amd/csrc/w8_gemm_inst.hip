@@ -33,7 +33,10 @@
   W8_U(MB, 1, 4, 2) W8_U(MB, 1, 8, 2)
 
 // The MoE grouped GEMM: the same (MB, NB, UNROLL, PACKED) and (WK, WN, XL) in
-// {(1, 1, 0), (2, 1, 0), (4, 1, 0), (8, 1, 0), (1, 2, 1), (1, 4, 1), (1, 8, 1)}.
+// {(1, 1, 0), (2, 1, 0), (4, 1, 0), (8, 1, 0), (1, 2, 1), (1, 4, 1), (1, 8, 1)}
+// on quantized activations, and with fused quantization (XL 2) in
+// {(1, 4, 2), (1, 8, 2)} (the only fused shapes that ever beat a quantize
+// launch + the unfused kernel on the MoE layers measured).
 #define W8_MOE_TABLE_FN W8_CAT(moe_instances_f, W8_FMT, W8_SWAP)
 #define W8_MI(MB, NB, WK, WN, U, P, XL)                                      \
   {W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL,                                 \
@@ -44,7 +47,8 @@
   W8_MP(MB, 2, WK, WN, 1, XL) W8_MP(MB, 2, WK, WN, 2, XL) W8_MP(MB, 4, WK, WN, 1, XL)
 #define W8_MW(MB)                                                                      \
   W8_MU(MB, 1, 1, 0) W8_MU(MB, 2, 1, 0) W8_MU(MB, 4, 1, 0) W8_MU(MB, 8, 1, 0)         \
-  W8_MU(MB, 1, 2, 1) W8_MU(MB, 1, 4, 1) W8_MU(MB, 1, 8, 1)
+  W8_MU(MB, 1, 2, 1) W8_MU(MB, 1, 4, 1) W8_MU(MB, 1, 8, 1)                            \
+  W8_MU(MB, 1, 4, 2) W8_MU(MB, 1, 8, 2)
 
 namespace w8 {
 

@@ -96,10 +96,14 @@ struct MoeCall {
   long long ldy;
   void* ws;
   size_t ws_bytes;
+  const void* x;  // non-null: bf16 activations, quantization fused (xq, sx unused)
+  long long ldx;  // elements
 };
-w8_status check_moe_cfg(int fmt, int E, int max_m, int N, int K, int packed, const w8_cfg& c);
-size_t moe_ws_bytes(int fmt, int E, int max_m, int N, int K, const w8_cfg& c);
-w8_cfg moe_fallback_cfg(int fmt, int E, int T, int max_m, int N, int K, int packed);
+// fused: the rules of the fused grouped kernel (w8_moe_linear).
+w8_status check_moe_cfg(int fmt, int E, int max_m, int N, int K, int packed, const w8_cfg& c,
+                        bool fused);
+size_t moe_ws_bytes(int fmt, int E, int T, int max_m, int N, int K, const w8_cfg& c);
+w8_cfg moe_fallback_cfg(int fmt, int E, int T, int max_m, int N, int K, int packed, bool fused);
 w8_status launch_moe_call(const MoeCall& call, const w8_cfg& c, hipStream_t s);
 
 constexpr const char* kArch = "gfx950";

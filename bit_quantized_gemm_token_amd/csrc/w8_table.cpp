@@ -1,12 +1,12 @@
 // Per-shape config table (ai-radar.it, "Helion nel backend vLLM", paragraphs
 // 6-7: tuned configs are shipped per shape, with a default config for shapes
 // that have none).  Entries are keyed by (arch, abi, fmt, op, weight layout,
-// M, N, K), M being the token count T for the MoE op.  A GEMM or linear
+// M, N, K), M being the token count T for the MoE ops.  A GEMM or linear
 // lookup that misses, or finds only entries written for another arch or ABI
 // (kept in the file, never used), falls back to an entry of the same
 // floor(log2 M) bucket and then to the cost model's pick (the hard-fallback
 // cases of TensorRT-LLM issue 16363, "Suggested direction", that apply to a
-// table: cache miss and backend identity mismatch); the MoE op reads exact
+// table: cache miss and backend identity mismatch); the MoE ops read exact
 // entries only.
 #include <cerrno>
 #include <cstdio>
@@ -34,7 +34,10 @@ typedef std::tuple<int, int, int, int, int, int> Key;  // fmt, op, packed, M, N,
 
 const char* layout_name(int packed) { return packed ? "packed" : "row"; }
 const char* op_name(int op) {
-  return op == W8_OP_LINEAR ? "linear" : op == W8_OP_MOE ? "moe" : "gemm";
+  return op == W8_OP_LINEAR       ? "linear"
+         : op == W8_OP_MOE        ? "moe"
+         : op == W8_OP_MOE_LINEAR ? "moe_linear"
+                                  : "gemm";
 }
 
 struct Table {
@@ -103,7 +106,9 @@ w8_status parse_table(const std::string& text, std::map<Key, Entry>* native,
     if (tok[3] == "gemm") op = W8_OP_GEMM;
     if (tok[3] == "linear") op = W8_OP_LINEAR;
     if (tok[3] == "moe") op = W8_OP_MOE;
-    if (op < 0) return fail(W8_E_TABLE_FORMAT, where + "op must be gemm, linear or moe");
+    if (tok[3] == "moe_linear") op = W8_OP_MOE_LINEAR;
+    if (op < 0)
+      return fail(W8_E_TABLE_FORMAT, where + "op must be gemm, linear, moe or moe_linear");
     int packed = -1;
     if (tok[4] == "row") packed = 0;
     if (tok[4] == "packed") packed = 1;
@@ -306,7 +311,7 @@ w8_status w8_lookup_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!out) return fail(W8_E_INVALID, "null output pointer");
-  if (op != W8_OP_GEMM && op != W8_OP_LINEAR && op != W8_OP_MOE)
+  if (op != W8_OP_GEMM && op != W8_OP_LINEAR && op != W8_OP_MOE && op != W8_OP_MOE_LINEAR)
     return fail(W8_E_INVALID, "unknown op");
   Table& t = table();
   std::lock_guard<std::mutex> lk(t.mu);

@@ -333,9 +333,12 @@ std::vector<int> make_routing(int E, int T, int topk, uint64_t seed) {
 // that the experts the calls of one graph reach span rotate_bytes too (at
 // most 64, at least R), so neither the last-level cache nor the graph
 // launch's own cost, spread over G calls, flatters small T.  The reference
-// output: the fallback config on row-major copy 0 with routing 0.
+// output: the fallback config on row-major copy 0 with routing 0.  fused
+// (w8_moe_linear): the calls take bf16 activations, and the reference runs
+// the standalone quantizer on them first.
 struct MoeHarness {
   int fmt, E, T, N, K, topk, packed;
+  bool fused = false;
   w8_tune_opts o;
   long long ld = 0;
   size_t wexp = 0, wrow_exp = 0, R = 0, G = 0, nsx = 0, nsw = 0, n_rows = 0, route_len = 0;
@@ -375,12 +378,13 @@ struct MoeHarness {
     const double reach = (double)std::min<long long>(E, (long long)T * topk) * (double)wexp;
     G = std::max<size_t>(R, std::min<size_t>(64, (size_t)std::ceil((double)o.rotate_bytes / reach)));
     is_int8 = fmt == W8_W8A8_INT8;
-    const w8_cfg dflt = moe_fallback_cfg(fmt, E, T, T, N, K, 0);  // reference
-    max_ws = std::max(max_ws, moe_ws_bytes(fmt, E, T, N, K, dflt));
+    const w8_cfg dflt = moe_fallback_cfg(fmt, E, T, T, N, K, 0, false);  // reference
+    max_ws = std::max(max_ws, moe_ws_bytes(fmt, E, T, T, N, K, dflt));
     TRY_HIP(hipStreamCreate(&stream));
     TRY_HIP(hipMalloc(&b.wrow, wrow_exp * E));
     TRY_HIP(hipMalloc(&b.wpool, set * R));
     TRY_HIP(hipMalloc(&b.xq, (size_t)T * ld));
+    if (fused) TRY_HIP(hipMalloc(&b.x, (size_t)T * ld * 2));
     TRY_HIP(hipMalloc(&b.sx, nsx * 4));
     TRY_HIP(hipMalloc(&b.sw, nsw * E * 4));
     TRY_HIP(hipMalloc(&b.y, n_rows * N * 2));
@@ -412,10 +416,19 @@ struct MoeHarness {
     }
     if (!packed)
       TRY_HIP(hipMemcpyAsync(b.wpool, b.wrow, set, hipMemcpyDeviceToDevice, stream));
-    hipLaunchKernelGGL(fill_codes_kernel, dim3(64), dim3(256), 0, stream, b.xq, (size_t)T * ld,
-                       0x9876u, (int)is_int8);
-    hipLaunchKernelGGL(fill_scales_kernel, dim3(64), dim3(256), 0, stream, b.sx, nsx, 0x55u,
-                       0.01f, 0.1f);
+    if (fused) {
+      // bf16 activations, quantized by the standalone quantizer for the reference
+      hipLaunchKernelGGL(fill_bf16_kernel, dim3(64), dim3(256), 0, stream, b.x, (size_t)T * ld,
+                         0x9876u);
+      TRY_HIP(hipGetLastError());
+      QuantActArgs qa{b.x, b.xq, b.sx, ld, ld, T, K};
+      TRY_HIP(launch_quantize_act(fmt, qa, stream));
+    } else {
+      hipLaunchKernelGGL(fill_codes_kernel, dim3(64), dim3(256), 0, stream, b.xq, (size_t)T * ld,
+                         0x9876u, (int)is_int8);
+      hipLaunchKernelGGL(fill_scales_kernel, dim3(64), dim3(256), 0, stream, b.sx, nsx, 0x55u,
+                         0.01f, 0.1f);
+    }
     hipLaunchKernelGGL(fill_scales_kernel, dim3(256), dim3(256), 0, stream, b.sw, nsw * E, 0x77u,
                        0.001f, 0.01f);
     TRY_HIP(hipGetLastError());
@@ -427,7 +440,7 @@ struct MoeHarness {
                    N,       b.ws,   b.ws_bytes};
     yref.resize(n_rows * N);
     ycur.resize(n_rows * N);
-    MoeCall ref = call;
+    MoeCall ref = call;  // on the quantized activations
     ref.wq = b.wrow;
     ref.ldw = ld;
     ref.w_stride = (long long)wrow_exp;
@@ -436,6 +449,12 @@ struct MoeHarness {
     TRY_HIP(hipStreamSynchronize(stream));
     TRY_HIP(hipMemcpy(yref.data(), b.y, yref.size() * 2, hipMemcpyDeviceToHost));
     for (uint16_t v : yref) ref_max = std::max(ref_max, std::fabs(bf16_to_float(v)));
+    if (fused) {  // the tuned calls read the bf16 activations
+      call.xq = nullptr;
+      call.sx = nullptr;
+      call.x = b.x;
+      call.ldx = ld;
+    }
     return W8_OK;
   }
 
@@ -685,22 +704,42 @@ extern "C" w8_status w8_moe_tune(w8_fmt fmt, int E, int T, int N, int K, int top
   // Candidates: the GEMM family's feasible set at M = T (an expert holds at
   // most T rows), without the minimum-waves pruning (the experts multiply
   // the workgroups), that the grouped kernel runs, and whose workspace stays
-  // within 1 GiB.
+  // within 1 GiB.  op LINEAR (w8_moe_linear): the configs of the fused
+  // grouped kernel, plus quantize launch + the grouped kernel (quant_launch
+  // 1) with the "moe" table entry for the shape and with the fallback.
+  const bool fused = o.op == W8_OP_LINEAR;
   constexpr size_t kMaxWs = (size_t)1 << 30;
+  std::vector<w8_cfg> list;
+  for (const w8_cfg& c : enumerate_configs(fmt, fused ? W8_OP_LINEAR : W8_OP_GEMM, T, N, K, packed,
+                                           o.max_split_k, 0, false))
+    if (!c.quant_launch) list.push_back(c);
+  if (fused) {
+    w8_cfg q;
+    if (w8_lookup_config(fmt, W8_OP_MOE, T, N, K, packed, &q, nullptr) == W8_OK) {
+      q.quant_launch = 1;
+      list.push_back(q);
+    }
+    q = moe_fallback_cfg(fmt, E, T, T, N, K, packed, true);  // quant_launch 1
+    list.push_back(q);
+  }
   std::vector<Cand> cands;
-  for (const w8_cfg& c :
-       enumerate_configs(fmt, W8_OP_GEMM, T, N, K, packed, o.max_split_k, 0, false)) {
-    if (check_moe_cfg(fmt, E, T, N, K, packed, c) != W8_OK) continue;
-    if (moe_ws_bytes(fmt, E, T, N, K, c) > kMaxWs) continue;
+  for (const w8_cfg& c : list) {
+    if (check_moe_cfg(fmt, E, T, N, K, packed, c, fused) != W8_OK) continue;
+    if (moe_ws_bytes(fmt, E, T, T, N, K, c) > kMaxWs) continue;
+    bool dup = false;
+    for (const Cand& o2 : cands) dup = dup || std::memcmp(&o2.cfg, &c, sizeof c) == 0;
+    if (dup) continue;
     Cand cd;
     cd.cfg = c;
     cd.index = (int)cands.size();
     cands.push_back(cd);
   }
   if (cands.empty()) return fail(W8_E_VALIDATION, "no feasible candidate");
-  const w8_cfg dflt = moe_fallback_cfg(fmt, E, T, T, N, K, packed);  // reported baseline
-  size_t max_ws = moe_ws_bytes(fmt, E, T, N, K, dflt);
-  for (const Cand& cd : cands) max_ws = std::max(max_ws, moe_ws_bytes(fmt, E, T, N, K, cd.cfg));
+  const w8_cfg dflt = moe_fallback_cfg(fmt, E, T, T, N, K, packed, fused);  // reported baseline
+  if (check_moe_cfg(fmt, E, T, N, K, packed, dflt, fused) != W8_OK)
+    return fail(W8_E_VALIDATION, "no valid fallback config for this shape");
+  size_t max_ws = moe_ws_bytes(fmt, E, T, T, N, K, dflt);
+  for (const Cand& cd : cands) max_ws = std::max(max_ws, moe_ws_bytes(fmt, E, T, T, N, K, cd.cfg));
 
   MoeHarness h;
   h.fmt = fmt;
@@ -710,6 +749,7 @@ extern "C" w8_status w8_moe_tune(w8_fmt fmt, int E, int T, int N, int K, int top
   h.K = K;
   h.topk = topk;
   h.packed = packed;
+  h.fused = fused;
   h.o = o;
   st = h.setup(max_ws);
   if (st) return st;
@@ -757,7 +797,8 @@ extern "C" w8_status w8_moe_tune(w8_fmt fmt, int E, int T, int N, int K, int top
   }
   *best = win->cfg;
   if (o.insert) {
-    st = w8_set_config(fmt, W8_OP_MOE, T, N, K, packed, &win->cfg, win->us2);
+    st = w8_set_config(fmt, fused ? W8_OP_MOE_LINEAR : W8_OP_MOE, T, N, K, packed, &win->cfg,
+                       win->us2);
     if (st) return st;
   }
   if (stats) {
@@ -774,8 +815,9 @@ extern "C" w8_status w8_moe_tune(w8_fmt fmt, int E, int T, int N, int K, int top
     const bool block = fmt == W8_BLOCK_FP8;
     const int G = K / W8_GROUP;
     const double sw_exp = block ? 4.0 * ((N + 127) / 128) * G : 4.0 * N;
-    const double bytes = h.active_mean * ((double)N * K + sw_exp) + (double)T * K +
-                         4.0 * (block ? (double)T * G : (double)T) + 2.0 * T * topk * N;
+    // (fused: the tokens as bf16, no activation scales)
+    const double act = fused ? 2.0 * T * K : (double)T * K + 4.0 * (block ? (double)T * G : T);
+    const double bytes = h.active_mean * ((double)N * K + sw_exp) + act + 2.0 * T * topk * N;
     stats->best_gbps = bytes / (win->us2 * 1e3);
     stats->tune_seconds =
         std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();

@@ -8,9 +8,10 @@
 Default shapes: the 24-shape M <= 32 sweep of synthetic.SWEEP plus the shapes
 the tests and benchmarks name (N=K=4096 at M in {1, 4, 16, 32}; N=4608,
 K=7168 at M in {1, 8, 32}; N=512, K=7168 at M in {1, 2, 4, 8, 16, 32};
-16 x 896 x 1024).  Op "moe" tunes the MoE grouped GEMM (moe_tune) on its own
-shapes, packed layout only: by default the 128-expert top-8 layers of
-synthetic.MOE_SHAPES at the token counts synthetic.MOE_TOKENS.
+16 x 896 x 1024).  Ops "moe" and "moe_linear" tune the MoE grouped GEMM on
+quantized tokens and on bf16 tokens with the quantization fused (moe_tune) on
+their own shapes, packed layout only: by default the 128-expert top-8 layers
+of synthetic.MOE_SHAPES at the token counts synthetic.MOE_TOKENS.
 
 Tuning is the expensive offline step the page describes (ai-radar.it,
 "Helion nel backend vLLM", paragraph 6: ahead-of-time tuning can take hours
@@ -54,8 +55,8 @@ def main(argv=None):
     p.add_argument("--out", required=True)
     p.add_argument("--formats", default="FP8_Dynamic,W8A8_INT8,Block_FP8")
     p.add_argument("--layouts", default="row,packed")
-    p.add_argument("--ops", default="gemm", help="comma list of gemm, linear, moe")
-    p.add_argument("--moe-shapes", default=None, help="E,topk,T,N,K;... for op moe")
+    p.add_argument("--ops", default="gemm", help="comma list of gemm, linear, moe, moe_linear")
+    p.add_argument("--moe-shapes", default=None, help="E,topk,T,N,K;... for the MoE ops")
     p.add_argument("--shapes", default=None)
     p.add_argument("--no-resume", action="store_true")
     p.add_argument("--max-split-k", type=int, default=w8.MAX_SPLIT_K)
@@ -84,7 +85,7 @@ def main(argv=None):
     jobs = []
     for op in a.ops.split(","):
         for fmt in a.formats.split(","):
-            if op == "moe":  # (T, N, K) keys the entry; E and topk set the routing
+            if op in ("moe", "moe_linear"):  # (T, N, K) keys the entry; E, topk: routing
                 jobs += [(op, fmt, (T, N, K), True, (E, k)) for E, k, T, N, K in moe_shapes]
             else:
                 jobs += [(op, fmt, s, packed, None) for s in shapes for packed in layouts]
@@ -99,7 +100,7 @@ def main(argv=None):
         if moe:
             best, st = w8.moe_tune(fmt, moe[0], M, N, K, moe[1], rotate_bytes=a.rotate_mib << 20,
                                    replays=a.replays, max_split_k=a.max_split_k, insert=True,
-                                   packed=True)
+                                   packed=True, fused=op == "moe_linear")
         else:
             best, st = w8.tune_shape(fmt, M, N, K, rotate_bytes=a.rotate_mib << 20,
                                      replays=a.replays, max_split_k=a.max_split_k, insert=True,

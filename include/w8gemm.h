@@ -69,12 +69,15 @@ typedef void *w8_stream; /* hipStream_t */
 
 /* The operations configs are tuned for: the GEMM on quantized activations
  * (w8_gemm_w8a8), the whole linear layer (w8_linear), and the MoE grouped
- * GEMM (w8_moe_gemm; its table entries hold the token count T in the M
- * field, and take w8_moe_tune, not w8_tune_shape).                          */
+ * GEMM on quantized activations (w8_moe_gemm) and on bf16 activations with
+ * the quantization fused (w8_moe_linear).  The two MoE ops' table entries
+ * hold the token count T in the M field and take w8_moe_tune, not
+ * w8_tune_shape.                                                           */
 typedef enum {
     W8_OP_GEMM = 0,
     W8_OP_LINEAR = 1,
-    W8_OP_MOE = 2
+    W8_OP_MOE = 2,
+    W8_OP_MOE_LINEAR = 3
 } w8_op;
 
 typedef enum {
@@ -124,9 +127,9 @@ typedef enum {
  *            most tiles x K-steps.
  *   swap_ab  0: MFMA A operand = activations, B = weights^T.
  *            1: Swap-AB, Y^T = Wq . Xq^T: A = weights, B = activations^T.
- *   quant_launch  W8_OP_LINEAR only (0 for W8_OP_GEMM).  0: the activations
- *            are quantized inside the GEMM (needs x_lds == 1 and
- *            waves_k <= 4).  1: they are quantized by a launch of their own
+ *   quant_launch  W8_OP_LINEAR and W8_OP_MOE_LINEAR only (0 for the other
+ *            ops).  0: the activations are quantized inside the GEMM (needs
+ *            x_lds == 1 and waves_k <= 4).  1: they are quantized by a launch of their own
  *            (w8_quantize_act's kernel) into the workspace, and the GEMM
  *            runs with this config under the W8_OP_GEMM rules.  The tuner
  *            tries both for the linear op and keeps the faster.
@@ -430,9 +433,9 @@ w8_status w8_profile_configs(w8_fmt fmt, int M, int N, int K, const w8_tune_opts
  *   sw       expert e's scales at sw + e * sw_stride floats
  *   y        bf16 [n_rows, N], row stride ldy (device), entry i's row i
  *   cfg      a GEMM-family config valid at M = max_m whose (waves_k, waves_n,
- *            x_lds) is one of (1|2|4|8, 1, 0) or (1, 2|4|8, 1); NULL = the
- *            cost model's pick (w8_moe_config).  Shared tiles (split_k > 1
- *            or grid > 0) need E x tiles <= 16384.
+ *            x_lds) is one of (1|2|4|8, 1, 0) or (1, 2|4|8, 1); NULL =
+ *            w8_moe_config's.  Shared tiles (split_k > 1 or grid > 0) need
+ *            E x tiles <= 16384.
  *   ws       w8_moe_workspace_size bytes: the 2 MiB counter region, then
  *            each expert's partials; zero-filled before first use.
  * Same allocation, ordering and error rules as w8_gemm_w8a8.               */
@@ -442,6 +445,9 @@ w8_status w8_moe_gemm(w8_fmt fmt, int E, int T, int N, int K, int max_m,
                       const void *wq, int64_t ldw, int64_t w_stride,
                       const float *sw, int64_t sw_stride, void *y, int64_t ldy,
                       const w8_cfg *cfg, void *ws, size_t ws_bytes, w8_stream stream);
+/* Workspace bytes of w8_moe_gemm or w8_moe_linear with cfg (a config of
+ * either; NULL = w8_moe_config's): the shared-tile region, and with
+ * quant_launch the T tokens' codes and scales after it.                    */
 w8_status w8_moe_workspace_size(w8_fmt fmt, int E, int T, int N, int K, int max_m, int packed,
                                 const w8_cfg *cfg, size_t *bytes);
 /* W8_OK if cfg is valid for w8_moe_gemm with these sizes and layout.       */
@@ -457,6 +463,34 @@ w8_status w8_moe_validate_config(w8_fmt fmt, int E, int N, int K, int max_m, int
 w8_status w8_moe_config(w8_fmt fmt, int E, int T, int N, int K, int max_m, int packed,
                         w8_cfg *out, int *from_table);
 
+/* The MoE grouped GEMM on bf16 activations x [T, K] (row stride ldx,
+ * 16-byte aligned, ldx % 8 == 0): the whole MoE expert layer from the
+ * tokens.  With cfg->quant_launch == 0 the activation quantization is fused
+ * into the grouped kernel: each expert's workgroups quantize the token rows
+ * routed to it while their weights load, per token (FP8_Dynamic,
+ * W8A8_INT8: the row's maximum over the whole of K) or per 1x128 group
+ * (Block_FP8), with the codes and scales of w8_quantize_act; the config
+ * needs x_lds == 1 and (waves_k, waves_n) in {(1, 4), (1, 8)}.
+ * With quant_launch == 1 the tokens are quantized by a launch of their own
+ * into the workspace (after its shared-tile region), then the grouped
+ * kernel runs with the config under w8_moe_gemm's rules.  Either way Y
+ * equals w8_quantize_act followed by w8_moe_gemm with the same tiling, bit
+ * for bit.  NULL cfg = w8_moe_linear_config.  All other arguments, rules
+ * and the workspace (w8_moe_workspace_size with the resolved cfg) as for
+ * w8_moe_gemm.                                                           */
+w8_status w8_moe_linear(w8_fmt fmt, int E, int T, int N, int K, int max_m,
+                        const void *x, int64_t ldx,
+                        const int32_t *offsets, const int32_t *rows, int n_rows,
+                        const void *wq, int64_t ldw, int64_t w_stride,
+                        const float *sw, int64_t sw_stride, void *y, int64_t ldy,
+                        const w8_cfg *cfg, void *ws, size_t ws_bytes, w8_stream stream);
+/* The config w8_moe_linear uses for cfg == NULL: the table entry for
+ * (fmt, W8_OP_MOE_LINEAR, layout, T, N, K) if it is valid for E and max_m;
+ * else w8_moe_config's config with quant_launch = 1.  *from_table (may be
+ * NULL) is 1 for a table entry.                                           */
+w8_status w8_moe_linear_config(w8_fmt fmt, int E, int T, int N, int K, int max_m, int packed,
+                               w8_cfg *out, int *from_table);
+
 /* Ahead-of-time tuning of the MoE grouped GEMM for E experts of (N, K) at T
  * tokens routed top-k (1 <= topk <= E): the grouped GEMM's configs
  * (w8_moe_validate_config with max_m = T), each checked against the default
@@ -464,9 +498,11 @@ w8_status w8_moe_config(w8_fmt fmt, int E, int T, int N, int K, int max_m, int p
  * calls over rotating weight copies and seeded uniform top-k routings (up
  * to 64 calls, each with its own routing, so that the experts one graph
  * reaches span opts->rotate_bytes);
- * opts as for w8_tune_shape (op, stream_k and top_n ignored).  The winner is
- * inserted as the (fmt, W8_OP_MOE, layout, T, N, K) entry when
- * opts->insert.  Allocates and synchronizes.                              */
+ * opts as for w8_tune_shape (stream_k and top_n ignored); opts->op =
+ * W8_OP_GEMM tunes w8_moe_gemm, W8_OP_LINEAR tunes w8_moe_linear (fused
+ * quantization, checked against w8_quantize_act + the fallback config).
+ * The winner is inserted as the (fmt, W8_OP_MOE or W8_OP_MOE_LINEAR,
+ * layout, T, N, K) entry when opts->insert.  Allocates and synchronizes.  */
 w8_status w8_moe_tune(w8_fmt fmt, int E, int T, int N, int K, int topk,
                       const w8_tune_opts *opts, w8_cfg *best, w8_tune_stats *stats);
 

@@ -588,3 +588,61 @@ def test_moe_tune_argument_errors(w8, lib):
     assert t(0, 8, 4, 1536, 2048, 0, None, ctypes.byref(best), ctypes.byref(stats)) == 1   # topk
     assert t(0, 8, 33, 1536, 2048, 2, None, ctypes.byref(best), ctypes.byref(stats)) != 0  # T > 32
     assert t(0, 8, 4, 1536, 2048, 2, None, None, ctypes.byref(stats)) == 1                # best
+
+
+def test_moe_linear_argument_errors_and_config(w8, lib):
+    """w8_moe_linear validates its bf16 activations and takes only configs of
+    the fused grouped kernel; its default config is valid for every format at
+    the benchmark's MoE layers and at a deep K that needs split-K to stage."""
+    L = lib.w8_moe_linear
+    cfg = w8.Config.make(waves_k=1, waves_n=4, unroll=1, x_lds=1)
+
+    def call(fmt=0, E=8, T=16, N=64, K=256, max_m=32, x=FAKE, ldx=256, cfgp=ctypes.byref(cfg),
+             ws=None, wsb=0):
+        return L(fmt, E, T, N, K, max_m, x, ldx, FAKE, FAKE, 64, FAKE, 256, 64 * 256, FAKE, 64,
+                 FAKE, 64, cfgp, ws, wsb, None)
+
+    assert call(max_m=33) == 2
+    assert call(x=None) == 1
+    assert call(ldx=250) == 1                        # ldx % 8
+    assert call(ldx=248) == 1                        # ldx < K
+    for bad in (w8.Config.make(waves_k=1, unroll=1, x_lds=0),     # x_lds 0
+                w8.Config.make(waves_k=8, unroll=1, x_lds=1),     # fused: waves_k <= 4
+                w8.Config.make(waves_k=2, unroll=1, x_lds=1),     # fused: waves along N only
+                # quantize launch: the unfused grouped kernel stages activations
+                # only with waves along N
+                w8.Config.make(waves_k=2, unroll=1, x_lds=1, quant_launch=1)):
+        assert call(cfgp=ctypes.byref(bad)) == 1
+    ql = w8.Config.make(waves_k=2, unroll=1, quant_launch=1)
+    assert call(cfgp=ctypes.byref(ql)) == 3          # the codes need a workspace
+    with pytest.raises(w8.W8Error):                  # quant_launch is no moe_gemm config
+        w8.moe_workspace_size("FP8_Dynamic", 8, 16, 64, 256, 32,
+                              w8.Config.make(waves_k=2, unroll=1, quant_launch=1, x_lds=2))
+    sk = w8.Config.make(waves_k=1, waves_n=4, unroll=1, x_lds=1, split_k=4)
+    assert call(cfgp=ctypes.byref(sk)) == 3          # workspace missing
+    # workspace sizing accepts a config of either grouped op
+    assert w8.moe_workspace_size("FP8_Dynamic", 8, 16, 64, 256, 32, sk) > 0
+    for fmt in w8.FORMATS:
+        for (E, T, N, K, m) in ((128, 1, 1536, 2048, 1), (128, 32, 2048, 768, 32),
+                                (64, 8, 512, 16384, 8)):
+            # no table entry: quantize launch + the grouped kernel's own default
+            c, hit = w8.moe_linear_config(fmt, E, T, N, K, m, packed=True)
+            d, _ = w8.moe_config(fmt, E, T, N, K, m, packed=True)
+            assert hit == 0 and c.quant_launch == 1 and c == w8.Config.make(
+                **dict(d.as_dict(), quant_launch=1))
+            # its workspace holds the T tokens' codes and scales past the counters
+            ws = w8.moe_workspace_size(fmt, E, T, N, K, m, c, packed=True)
+            ldq = (K + 15) // 16 * 16
+            nsx = T * (K // 128) if fmt == "Block_FP8" else T
+            r256 = lambda b: (b + 255) // 256 * 256
+            shared = w8.moe_workspace_size(fmt, E, T, N, K, m, d, packed=True)
+            assert ws == r256(max(shared, COUNTERS)) + r256(T * ldq) + r256(4 * nsx)
+    # moe_linear table entries: their own key, the fused rules
+    fmt, E, T, N, K = "W8A8_INT8", 128, 4, 1536, 2048
+    good = w8.Config.make(tile_n=32, waves_k=1, waves_n=4, unroll=1, x_lds=1)
+    w8.set_config(fmt, T, N, K, good, 7.0, packed=True, op="moe_linear")
+    assert w8.moe_linear_config(fmt, E, T, N, K, T, packed=True) == (good, 1)
+    assert w8.moe_config(fmt, E, T, N, K, T, packed=True)[1] == 0
+    with pytest.raises(w8.W8Error):                  # fused entries need x_lds = 1
+        w8.set_config(fmt, T, N, K, w8.Config.make(waves_k=2, unroll=1), 7.0, packed=True,
+                      op="moe_linear")

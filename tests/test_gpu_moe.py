@@ -271,3 +271,127 @@ def test_moe_compact_expert_grid(w8, fmt):
                 torch.cuda.synchronize()
                 assert same_bits(y, ref), f"{fmt} E={cs.E} {ckw} packed={packed}"
                 assert_bf16_close(y, cs.Y, f"compact {fmt} E={cs.E} {ckw}")
+
+
+FUSED_CFGS = (dict(tile_n=16, waves_k=1, waves_n=8, unroll=2, split_k=1, x_lds=1),
+              dict(tile_n=32, waves_k=1, waves_n=4, unroll=1, split_k=4, swap_ab=1, x_lds=1),
+              dict(tile_n=16, waves_k=1, waves_n=8, unroll=1, split_k=2, x_lds=1),
+              dict(tile_n=64, waves_k=1, waves_n=4, unroll=1, split_k=1, x_lds=1),
+              dict(tile_n=16, waves_k=1, waves_n=4, unroll=4, grid=40, x_lds=1))
+
+
+def unfused_twin(w8, kw):
+    """The grouped config on quantized activations that runs the same MFMA
+    sequence: the unfused kernel stages activations in LDS only with waves
+    along N, and reads them in the K loop (same fragments, same order)
+    otherwise."""
+    return w8.Config.make(**dict(kw, x_lds=1 if kw.get("waves_n", 1) > 1 else 0))
+
+
+@pytest.mark.parametrize("fmt", ["W8A8_INT8", "FP8_Dynamic", "Block_FP8"])
+def test_moe_linear_equals_quantize_then_moe_gemm(w8, fmt):
+    """moe_linear, fused quantization in the grouped kernel and quantize
+    launch + grouped kernel: bit-identical to quantize_act followed by
+    moe_gemm with the same tiling (every format, both layouts,
+    split-K, stream-K, waves along N, Swap-AB, an empty expert, experts above
+    16 tokens), within the bar of the oracle, and the compact grid with one
+    token among 200 experts."""
+    off9, rows = synthetic.moe_routing(24, 9, 6, 5)
+    offsets = np.insert(off9, 3, off9[3]).astype(np.int32)
+    N, K = 300, 1280 if fmt != "Block_FP8" else 1024
+    cs = MoeCase(w8, fmt, T=24, E=10, N=N, K=K, routing=(offsets, rows))
+    x = to_bf16_tensor(synthetic.activations(fmt, 24, N, K))
+    for packed in (False, True):
+        y = w8.moe_linear(fmt, x, cs.offsets, cs.rows, cs.weights(packed), cs.sw)
+        torch.cuda.synchronize()
+        assert_bf16_close(y, cs.Y, f"moe_linear default {fmt} packed={packed}")
+        for kw in FUSED_CFGS:
+            cfg = w8.Config.make(**kw)
+            y = w8.moe_linear(fmt, x, cs.offsets, cs.rows, cs.weights(packed), cs.sw, cfg=cfg)
+            ref = w8.moe_gemm(fmt, cs.xq, cs.sx, cs.offsets, cs.rows, cs.weights(packed), cs.sw,
+                              cfg=unfused_twin(w8, kw))
+            torch.cuda.synchronize()
+            assert same_bits(y, ref), f"{fmt} {kw} packed={packed}"
+            assert_bf16_close(y, cs.Y, f"moe_linear {fmt} {kw} packed={packed}")
+        # quantize launch + the grouped kernel (codes in the workspace, after
+        # the shared tiles of split-K / stream-K configs)
+        for kw in CFGS[:3] + CFGS[5:]:
+            cfg = w8.Config.make(**dict(kw, quant_launch=1))
+            y = w8.moe_linear(fmt, x, cs.offsets, cs.rows, cs.weights(packed), cs.sw, cfg=cfg)
+            ref = w8.moe_gemm(fmt, cs.xq, cs.sx, cs.offsets, cs.rows, cs.weights(packed), cs.sw,
+                              cfg=w8.Config.make(**kw))
+            torch.cuda.synchronize()
+            assert same_bits(y, ref), f"quant_launch {fmt} {kw} packed={packed}"
+    # one token among 200 experts (compact grid), max_m = 1
+    one = MoeCase(w8, fmt, T=1, E=200, N=N, K=K,
+                  routing=(np.r_[np.zeros(138, np.int32), np.ones(63, np.int32)],
+                           np.zeros(1, np.int32)))
+    x1 = to_bf16_tensor(synthetic.activations(fmt, 1, N, K))
+    for kw in FUSED_CFGS[:3]:
+        cfg = w8.Config.make(**kw)
+        y = w8.moe_linear(fmt, x1, one.offsets, one.rows, one.packed, one.sw, max_m=1, cfg=cfg)
+        ref = w8.moe_gemm(fmt, one.xq, one.sx, one.offsets, one.rows, one.packed, one.sw,
+                          max_m=1, cfg=unfused_twin(w8, kw))
+        torch.cuda.synchronize()
+        assert same_bits(y, ref), f"compact {fmt} {kw}"
+
+
+def test_moe_linear_extreme_rows_and_graph(w8):
+    """Token rows at the edges of bf16 (subnormal, -0, 2^120 magnitudes)
+    quantized inside the grouped kernel give the standalone quantizer's
+    codes (outputs bit-identical to quantize_act + moe_gemm); replayed from a
+    HIP graph with a split-K workspace, every replay equals the eager call."""
+    fmt, T, E, N, K = "W8A8_INT8", 14, 6, 128, 512
+    cs = MoeCase(w8, fmt, T=T, E=E, N=N, K=K, topk=3, seed=21, max_m=16)
+    x = to_bf16_tensor(synthetic.activations_extreme(fmt, T, K))
+    xq, sx = w8.quantize_act(fmt, x)
+    kw = dict(tile_n=16, waves_k=1, waves_n=4, unroll=1, split_k=4, x_lds=1)
+    cfg = w8.Config.make(**kw)
+    ws = w8.Workspace(DEV, w8.moe_workspace_size(fmt, E, T, N, K, 16, cfg, packed=True))
+    ref = w8.moe_gemm(fmt, xq, sx, cs.offsets, cs.rows, cs.packed, cs.sw, max_m=16,
+                      cfg=unfused_twin(w8, kw), workspace=ws)
+    eager = w8.moe_linear(fmt, x, cs.offsets, cs.rows, cs.packed, cs.sw, max_m=16, cfg=cfg,
+                          workspace=ws).clone()
+    torch.cuda.synchronize()
+    assert same_bits(eager, ref)
+    y = torch.empty_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        w8.moe_linear(fmt, x, cs.offsets, cs.rows, cs.packed, cs.sw, max_m=16, cfg=cfg, y=y,
+                      workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w8.moe_linear(fmt, x, cs.offsets, cs.rows, cs.packed, cs.sw, max_m=16, cfg=cfg, y=y,
+                      workspace=ws)
+    for i in range(3):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert same_bits(y, eager), f"replay {i}"
+
+
+def test_moe_linear_tune(w8):
+    """The fused grouped GEMM's tuner inserts a "moe_linear" entry that
+    moe_linear then uses; output within the bar of the oracle."""
+    fmt, E, T, N, K, topk = "Block_FP8", 16, 4, 512, 1024, 2
+    w8.clear_config_table()
+    try:
+        best, stats = w8.moe_tune(fmt, E, T, N, K, topk, warmup=1, replays=3,
+                                  rotate_bytes=64 << 20, packed=True, fused=True)
+        print(f"[moe] fused tune: {stats}", flush=True)
+        assert stats["validated"] >= 1
+        assert best.quant_launch == 1 or (best.x_lds == 1 and best.waves_k <= 4)
+        cfg, hit = w8.moe_linear_config(fmt, E, T, N, K, T, packed=True)
+        assert hit == 1 and cfg == best
+        assert w8.moe_config(fmt, E, T, N, K, T, packed=True)[1] == 0   # the unfused op's key
+        cs = MoeCase(w8, fmt, T=T, E=E, N=N, K=K, topk=topk, seed=9, max_m=T)
+        x = to_bf16_tensor(synthetic.activations(fmt, T, N, K))
+        y = w8.moe_linear(fmt, x, cs.offsets, cs.rows, cs.packed, cs.sw, max_m=T)
+        torch.cuda.synchronize()
+        assert_bf16_close(y, cs.Y, "moe_linear with the tuned entry")
+    finally:
+        w8.clear_config_table()
+        w8.load_default_table()
