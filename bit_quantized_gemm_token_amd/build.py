@@ -2,7 +2,7 @@
 
 Compiles every translation unit under csrc/ with hipcc in parallel and links
 them into bit_quantized_gemm_token_amd/libw8gemm.so.  The GEMM instance file is
-compiled once per (format, swap_ab) pair.  Flags:
+compiled once per (format, swap_ab, part).  Flags:
   -fhip-fp32-correctly-rounded-divide-sqrt  the quantizer's x / s is the IEEE
                                             correctly rounded division
   -Xclang -target-feature -Xclang -packed-fp32-ops
@@ -39,11 +39,12 @@ def _units():
              ("w8_model.cpp", ["-x", "hip"], "w8_model.o"),
              ("w8_moe.cpp", ["-x", "hip"], "w8_moe.o"),
              ("w8_registry.cpp", ["-x", "hip"], "w8_registry.o")]
-    for fmt in (0, 1, 2):
-        for swap in (0, 1):
-            units.append(("w8_gemm_inst.hip", [f"-DW8_FMT={fmt}", f"-DW8_SWAP={swap}"],
-                          f"w8_gemm_f{fmt}_s{swap}.o"))
-    return units
+    # the instance file in 24 parts (the GEMM parts, the largest, first so
+    # the pool stays busy), then the small units
+    inst = [("w8_gemm_inst.hip", [f"-DW8_FMT={fmt}", f"-DW8_SWAP={swap}", f"-DW8_PART={part}"],
+             f"w8_gemm_f{fmt}_s{swap}_p{part}.o")
+            for part in (0, 1, 2, 3) for fmt in (0, 1, 2) for swap in (0, 1)]
+    return inst + units
 
 
 def _compile(unit, verbose):

@@ -1,6 +1,8 @@
-// Explicit instances of the GEMM family for one format and one Swap-AB
-// setting.  The build compiles this file once per (W8_FMT, W8_SWAP) pair so
-// the instances compile in parallel.
+// Explicit instances of the GEMM family for one format, one Swap-AB setting
+// and one part: W8_PART 0 and 1 are the GEMM instances with MB = 1 and 2,
+// 2 and 3 the MoE grouped instances with MB = 1 and 2.  The build compiles
+// this file once per (W8_FMT, W8_SWAP, W8_PART) so the instances compile in
+// parallel.
 #include "w8_gemm.hpp"
 
 #ifndef W8_FMT
@@ -9,10 +11,13 @@
 #ifndef W8_SWAP
 #error "W8_SWAP must be defined"
 #endif
+#ifndef W8_PART
+#error "W8_PART must be defined"
+#endif
 
-#define W8_CAT2(a, b, c) a##b##_##c
-#define W8_CAT(a, b, c) W8_CAT2(a, b, c)
-#define W8_TABLE_FN W8_CAT(gemm_instances_f, W8_FMT, W8_SWAP)
+#define W8_CAT2(a, b, c, d) a##b##_##c##_##d
+#define W8_CAT(a, b, c, d) W8_CAT2(a, b, c, d)
+#define W8_MB (W8_PART % 2 + 1)
 
 // One entry per (MB, NB, WK, WN, UNROLL, PACKED, XL): MB in {1, 2}; (NB,
 // UNROLL) with NB * UNROLL <= 4 (the weight registers of one stage);
@@ -37,7 +42,6 @@
 // on quantized activations, and with fused quantization (XL 2) in
 // {(1, 4, 2), (1, 8, 2)} (the only fused shapes that ever beat a quantize
 // launch + the unfused kernel on the MoE layers measured).
-#define W8_MOE_TABLE_FN W8_CAT(moe_instances_f, W8_FMT, W8_SWAP)
 #define W8_MI(MB, NB, WK, WN, U, P, XL)                                      \
   {W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL,                                 \
    &launch_moe_gemm<W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL>},
@@ -52,17 +56,20 @@
 
 namespace w8 {
 
-static const GemmInstance kInstances[] = {W8_W(1) W8_W(2)};
-static const MoeInstance kMoeInstances[] = {W8_MW(1) W8_MW(2)};
+#if W8_PART < 2
+static const GemmInstance kInstances[] = {W8_W(W8_MB)};
 
-const GemmInstance* W8_TABLE_FN(int* count) {
+const GemmInstance* W8_CAT(gemm_instances_f, W8_FMT, W8_SWAP, W8_PART)(int* count) {
   *count = (int)(sizeof(kInstances) / sizeof(kInstances[0]));
   return kInstances;
 }
+#else
+static const MoeInstance kMoeInstances[] = {W8_MW(W8_MB)};
 
-const MoeInstance* W8_MOE_TABLE_FN(int* count) {
+const MoeInstance* W8_CAT(moe_instances_f, W8_FMT, W8_SWAP, W8_PART)(int* count) {
   *count = (int)(sizeof(kMoeInstances) / sizeof(kMoeInstances[0]));
   return kMoeInstances;
 }
+#endif
 
 }  // namespace w8

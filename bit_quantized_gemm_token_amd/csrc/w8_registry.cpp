@@ -1,37 +1,45 @@
-// Gathers the GEMM instances compiled in the per-(format, swap) translation
-// units into one table.
+// Gathers the GEMM instances compiled in the per-(format, swap, part)
+// translation units into one table.
 #include <vector>
 
 #include "w8_launch.hpp"
 
 namespace w8 {
 
-const GemmInstance* gemm_instances_f0_0(int*);
-const GemmInstance* gemm_instances_f0_1(int*);
-const GemmInstance* gemm_instances_f1_0(int*);
-const GemmInstance* gemm_instances_f1_1(int*);
-const GemmInstance* gemm_instances_f2_0(int*);
-const GemmInstance* gemm_instances_f2_1(int*);
+#define W8_DECL_PARTS(F, S)                                \
+  const GemmInstance* gemm_instances_f##F##_##S##_0(int*); \
+  const GemmInstance* gemm_instances_f##F##_##S##_1(int*); \
+  const MoeInstance* moe_instances_f##F##_##S##_2(int*);   \
+  const MoeInstance* moe_instances_f##F##_##S##_3(int*);
+W8_DECL_PARTS(0, 0)
+W8_DECL_PARTS(0, 1)
+W8_DECL_PARTS(1, 0)
+W8_DECL_PARTS(1, 1)
+W8_DECL_PARTS(2, 0)
+W8_DECL_PARTS(2, 1)
 
-const MoeInstance* moe_instances_f0_0(int*);
-const MoeInstance* moe_instances_f0_1(int*);
-const MoeInstance* moe_instances_f1_0(int*);
-const MoeInstance* moe_instances_f1_1(int*);
-const MoeInstance* moe_instances_f2_0(int*);
-const MoeInstance* moe_instances_f2_1(int*);
+namespace {
+template <class I>
+std::vector<I> gather(const I* (*const* parts)(int*), int n) {
+  std::vector<I> v;
+  for (int i = 0; i < n; ++i) {
+    int c = 0;
+    const I* p = parts[i](&c);
+    v.insert(v.end(), p, p + c);
+  }
+  return v;
+}
+}  // namespace
+
+#define W8_GEMM_PARTS(F, S) gemm_instances_f##F##_##S##_0, gemm_instances_f##F##_##S##_1
+#define W8_MOE_PARTS(F, S) moe_instances_f##F##_##S##_2, moe_instances_f##F##_##S##_3
 
 const MoeInstance* moe_instances(int* count) {
   static const std::vector<MoeInstance> all = [] {
-    std::vector<MoeInstance> v;
-    const MoeInstance* (*parts[])(int*) = {moe_instances_f0_0, moe_instances_f0_1,
-                                           moe_instances_f1_0, moe_instances_f1_1,
-                                           moe_instances_f2_0, moe_instances_f2_1};
-    for (auto part : parts) {
-      int n = 0;
-      const MoeInstance* p = part(&n);
-      v.insert(v.end(), p, p + n);
-    }
-    return v;
+    const MoeInstance* (*const parts[])(int*) = {W8_MOE_PARTS(0, 0), W8_MOE_PARTS(0, 1),
+                                                 W8_MOE_PARTS(1, 0), W8_MOE_PARTS(1, 1),
+                                                 W8_MOE_PARTS(2, 0), W8_MOE_PARTS(2, 1)};
+    return gather<MoeInstance>(parts, 12);
   }();
   *count = (int)all.size();
   return all.data();
@@ -39,16 +47,10 @@ const MoeInstance* moe_instances(int* count) {
 
 const GemmInstance* gemm_instances(int* count) {
   static const std::vector<GemmInstance> all = [] {
-    std::vector<GemmInstance> v;
-    const GemmInstance* (*parts[])(int*) = {gemm_instances_f0_0, gemm_instances_f0_1,
-                                            gemm_instances_f1_0, gemm_instances_f1_1,
-                                            gemm_instances_f2_0, gemm_instances_f2_1};
-    for (auto part : parts) {
-      int n = 0;
-      const GemmInstance* p = part(&n);
-      v.insert(v.end(), p, p + n);
-    }
-    return v;
+    const GemmInstance* (*const parts[])(int*) = {W8_GEMM_PARTS(0, 0), W8_GEMM_PARTS(0, 1),
+                                                  W8_GEMM_PARTS(1, 0), W8_GEMM_PARTS(1, 1),
+                                                  W8_GEMM_PARTS(2, 0), W8_GEMM_PARTS(2, 1)};
+    return gather<GemmInstance>(parts, 12);
   }();
   *count = (int)all.size();
   return all.data();
