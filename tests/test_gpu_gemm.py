@@ -300,3 +300,59 @@ def test_graph_capture_replay(w8, kind):
         junk = torch.randn(1024, 1024, device=DEV) @ torch.randn(1024, 1024, device=DEV)
         del junk
     assert_bf16_close(y_static, cs.Y, "graph replay")
+
+
+@pytest.mark.parametrize("fmt", ["W8A8_INT8", "FP8_Dynamic"])
+def test_deepest_k_accumulators(w8, fmt):
+    """K = 131072, the deepest K whose all-max int8 sum fits int32 with room
+    (131072 x 127^2 = 2 114 060 288 < 2^31 - 1): rows of all +max and all
+    -max codes against all-max weight rows give +-K Qmax^2 (E4M3FN: 448^2 K =
+    49 x 2^29, a value every partial sum of which fp32 holds exactly), and
+    random rows the oracle's exact sums -- under Standard, split-K 16 and
+    256, Swap-AB, staged activations with waves along N, and stream-K, with
+    unit scales."""
+    M, N, K = 4, 48, 131072
+    int8 = fmt == "W8A8_INT8"
+    g = np.random.Generator(np.random.PCG64(5))
+    if int8:
+        pos, neg = 0x7F, 0x81                               # +127, -127
+        rnd = lambda shape: g.integers(-127, 128, size=shape, dtype=np.int8).view(np.uint8)
+        qmax = 127
+    else:
+        pos, neg = 0x7E, 0xFE                               # +448, -448
+        def rnd(shape):
+            c = g.integers(0, 256, size=shape, dtype=np.int64).astype(np.uint8)
+            c[(c & 0x7F) == 0x7F] = 0x38                     # no NaN codes
+            return c
+        qmax = 448
+    xq = np.empty((M, K), np.uint8)
+    xq[0], xq[1] = pos, neg
+    xq[2:] = rnd((M - 2, K))
+    wq = np.empty((N, K), np.uint8)
+    wq[:16] = pos
+    wq[16:] = rnd((N - 16, K))
+    dt = torch.int8 if int8 else torch.float8_e4m3fn
+    xt = torch.from_numpy(xq).to(DEV).view(dt)
+    wt = torch.from_numpy(wq).to(DEV).view(dt)
+    ones_m = torch.ones(M, dtype=torch.float32, device=DEV)
+    ones_n = torch.ones(N, dtype=torch.float32, device=DEV)
+    ref = oracle.acc_int8(xq, wq) if int8 else oracle.acc_fp8(xq, wq)
+    closed = K * qmax * qmax
+    assert np.all(ref[0, :16] == closed) and np.all(ref[1, :16] == -closed)
+    if not int8:  # magnitude bound of the E4M3FN accumulation (see Case.acc_bound)
+        dec = oracle.e4m3_decode(xq).astype(np.float64)
+        decw = oracle.e4m3_decode(wq).astype(np.float64)
+        bound = 2.0 ** -14 * (np.abs(dec) @ np.abs(decw).T)
+    for kw in (dict(tile_n=16, waves_k=4, unroll=2, split_k=1),
+               dict(tile_n=16, waves_k=8, unroll=1, split_k=256),
+               dict(tile_n=32, waves_k=2, unroll=2, split_k=16, swap_ab=1),
+               dict(tile_n=16, waves_k=1, waves_n=2, unroll=1, split_k=64, x_lds=1),
+               dict(tile_n=16, waves_k=4, unroll=1, grid=100)):
+        print(f"[deep K] {fmt} {kw}", flush=True)
+        acc = w8.gemm_w8a8_acc(fmt, xt, ones_m, wt, ones_n, cfg=C(w8, **kw))
+        torch.cuda.synchronize()
+        got = acc.cpu().numpy()
+        if int8:
+            assert np.array_equal(got.astype(np.int64), ref), f"{kw}"
+        else:
+            assert np.all(np.abs(got.astype(np.float64) - ref) <= bound), f"{kw}"
