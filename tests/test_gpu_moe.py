@@ -395,3 +395,34 @@ def test_moe_linear_tune(w8):
     finally:
         w8.clear_config_table()
         w8.load_default_table()
+
+
+@pytest.mark.parametrize("T", [4, 32])
+@pytest.mark.parametrize("proj,N,K", [("gate_up", 1536, 2048), ("down", 2048, 768)])
+def test_moe_linear_bench_size(w8, proj, N, K, T):
+    """The benchmark's MoE layers at full size from bf16 tokens (128 experts,
+    top-8, packed weights, the shipped moe_linear entries -- the fused kernel
+    at 4 tokens on the down projection, a quantize launch elsewhere): bit for
+    bit the quantize_act + moe_gemm result with the same tiling."""
+    fmt, E = "Block_FP8", 128
+    print(f"[moe] linear bench size {proj} {N}x{K} T={T}", flush=True)
+    g = np.random.Generator(np.random.PCG64(91))
+    codes = g.integers(0, 256, size=(E, N, K), dtype=np.int64).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38
+    wq = torch.from_numpy(codes).to(DEV).view(torch.float8_e4m3fn)
+    sw = torch.from_numpy(g.uniform(0.5, 2.0, size=(E, (N + 127) // 128, K // 128))
+                          .astype(np.float32)).to(DEV)
+    packed = w8.pack_experts(fmt, wq)
+    offsets, rows = synthetic.moe_routing(T, E, 8, seed=7)
+    off_t, rows_t = torch.from_numpy(offsets).to(DEV), torch.from_numpy(rows).to(DEV)
+    x = to_bf16_tensor(synthetic.activations(fmt, T, N, K))
+    cfg, hit = w8.moe_linear_config(fmt, E, T, N, K, T, packed=True)
+    assert hit == 1
+    y = w8.moe_linear(fmt, x, off_t, rows_t, packed, sw, max_m=T)
+    xq, sx = w8.quantize_act(fmt, x)
+    twin = cfg.as_dict()
+    fused = not twin.pop("quant_launch")
+    ref = w8.moe_gemm(fmt, xq, sx, off_t, rows_t, packed, sw, max_m=T,
+                      cfg=unfused_twin(w8, twin) if fused else w8.Config.make(**twin))
+    torch.cuda.synchronize()
+    assert same_bits(y, ref), f"{proj} T={T} {cfg}"
