@@ -195,9 +195,10 @@ w8_status resolve_moe(int fmt, int E, int T, int N, int K, int max_m, int packed
 // checked by the caller), then the launch.
 w8_status moe_entry(MoeCall call, const w8_cfg* cfg, bool fused, w8_stream stream) {
   const int fmt = call.fmt, E = call.E, T = call.T, N = call.N, K = call.K, max_m = call.max_m;
-  if (!call.offsets || !call.rows || !call.wq || !call.sw || !call.y)
-    return fail(W8_E_INVALID, "null device pointer");
   if (call.n_rows < 0) return fail(W8_E_INVALID, "n_rows must be >= 0");
+  const bool empty = call.n_rows == 0;  // no routed entry: nothing to compute
+  if (!call.offsets || !call.wq || !call.sw || (!empty && (!call.rows || !call.y)))
+    return fail(W8_E_INVALID, "null device pointer");
   const int packed = call.ldw == 0;
   if (!aligned(call.wq, 16) || call.w_stride % 16)
     return fail(W8_E_INVALID, "wq and w_stride must be 16-byte aligned");
@@ -222,7 +223,7 @@ w8_status moe_entry(MoeCall call, const w8_cfg* cfg, bool fused, w8_stream strea
   w8_status st = resolve_moe(fmt, E, T, N, K, max_m, packed, fused, cfg, &c);
   if (st) return st;
   const size_t need = moe_ws_bytes(fmt, E, T, max_m, N, K, c);
-  if (need > 0) {
+  if (need > 0 && !empty) {
     if (!call.ws || call.ws_bytes < need)
       return fail(W8_E_WORKSPACE, "workspace of " + std::to_string(need) + " bytes needed, got " +
                                       std::to_string(call.ws ? call.ws_bytes : 0));
@@ -230,8 +231,10 @@ w8_status moe_entry(MoeCall call, const w8_cfg* cfg, bool fused, w8_stream strea
   }
   st = check_device();
   if (st) return st;
-  st = launch_moe_call(call, c, static_cast<hipStream_t>(stream));
-  if (st) return st;
+  if (!empty) {
+    st = launch_moe_call(call, c, static_cast<hipStream_t>(stream));
+    if (st) return st;
+  }
   return ok();
 }
 

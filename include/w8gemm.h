@@ -424,7 +424,9 @@ w8_status w8_profile_configs(w8_fmt fmt, int M, int N, int K, const w8_tune_opts
  *            expert are not computed).  Offsets are clamped to [0, n_rows],
  *            so bad routing never reads or writes outside rows and y (it
  *            may leave entries unwritten).
- *   rows     int32 [n_rows] (device), each in [0, T) (clamped if not)
+ *   rows     int32 [n_rows] (device), each in [0, T) (clamped if not);
+ *            n_rows = 0: nothing is computed or launched (rows, y and ws
+ *            may be NULL)
  *   max_m    bound on any expert's count, 1..32 (else W8_E_UNSUPPORTED);
  *            kernels for ceil(max_m / 16) row blocks run
  *   wq       expert e's codes at wq + e * w_stride bytes: row-major [N, K]

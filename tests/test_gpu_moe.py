@@ -426,3 +426,21 @@ def test_moe_linear_bench_size(w8, proj, N, K, T):
                       cfg=unfused_twin(w8, twin) if fused else w8.Config.make(**twin))
     torch.cuda.synchronize()
     assert same_bits(y, ref), f"{proj} T={T} {cfg}"
+
+
+def test_moe_empty_routing(w8):
+    """No routed entry (all offsets 0, an empty row list): both grouped entry
+    points return an empty output without launching, with the default and a
+    split-K config."""
+    fmt, T, E, N, K = "FP8_Dynamic", 3, 8, 64, 256
+    cs = MoeCase(w8, fmt, T=T, E=E, N=N, K=K, routing=(np.zeros(E + 1, np.int32),
+                                                       np.zeros(0, np.int32)))
+    x = to_bf16_tensor(synthetic.activations(fmt, T, N, K))
+    sk = w8.Config.make(tile_n=16, waves_k=4, unroll=1, split_k=4)
+    for packed in (False, True):
+        y = w8.moe_gemm(fmt, cs.xq, cs.sx, cs.offsets, cs.rows, cs.weights(packed), cs.sw)
+        y2 = w8.moe_gemm(fmt, cs.xq, cs.sx, cs.offsets, cs.rows, cs.weights(packed), cs.sw,
+                         cfg=sk, workspace=w8.Workspace(DEV, 256))
+        y3 = w8.moe_linear(fmt, x, cs.offsets, cs.rows, cs.weights(packed), cs.sw)
+        torch.cuda.synchronize()
+        assert y.shape == y2.shape == y3.shape == (0, N)
