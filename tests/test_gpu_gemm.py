@@ -356,3 +356,46 @@ def test_deepest_k_accumulators(w8, fmt):
             assert np.array_equal(got.astype(np.int64), ref), f"{kw}"
         else:
             assert np.all(np.abs(got.astype(np.float64) - ref) <= bound), f"{kw}"
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [("W8A8_INT8", 2, (1 << 24) - 7, 16),
+                                       ("W8A8_INT8", 3, 16, 1 << 22),
+                                       ("FP8_Dynamic", 2, 40, 1 << 22)])
+def test_largest_n_and_k(w8, fmt, M, N, K):
+    """The largest N (2^24, here with a ragged last tile) and K (2^22) the
+    library accepts, with random codes and unit scales: the default config
+    and an explicit one, accumulators against the oracle's exact sums (all
+    of them, or for the 2^24 columns a sample with the ragged tail)."""
+    g = np.random.Generator(np.random.PCG64(K + N))
+    int8 = fmt == "W8A8_INT8"
+    def rnd(shape):
+        if int8:
+            return g.integers(-127, 128, size=shape, dtype=np.int8).view(np.uint8)
+        c = g.integers(0, 256, size=shape, dtype=np.int64).astype(np.uint8)
+        c[(c & 0x7F) == 0x7F] = 0x38
+        return c
+    xq, wq = rnd((M, K)), rnd((N, K))
+    dt = torch.int8 if int8 else torch.float8_e4m3fn
+    xt = torch.from_numpy(xq).to(DEV).view(dt)
+    wt = torch.from_numpy(wq).to(DEV).view(dt)
+    ones_m = torch.ones(M, dtype=torch.float32, device=DEV)
+    ones_n = torch.ones(N, dtype=torch.float32, device=DEV)
+    cols = np.arange(N) if N <= 4096 else np.unique(np.r_[g.integers(0, N, 4096),
+                                                          np.arange(N - 80, N)])
+    if int8:
+        ref = oracle.acc_int8(xq, wq[cols])
+    else:
+        ref = oracle.acc_fp8(xq, wq[cols])
+        dec = np.abs(oracle.e4m3_decode(xq)).astype(np.float32)  # a bound: fp32 suffices
+        decw = np.abs(oracle.e4m3_decode(wq[cols])).astype(np.float32)
+        bound = 2.0 ** -14 * (dec @ decw.T).astype(np.float64) * 1.001
+    for cfg in (None, C(w8, tile_n=64, waves_k=1, unroll=1, split_k=1),
+                C(w8, tile_n=16, waves_k=8, unroll=1, split_k=1)):
+        print(f"[largest] {fmt} M={M} N={N} K={K} {cfg}", flush=True)
+        acc = w8.gemm_w8a8_acc(fmt, xt, ones_m, wt, ones_n, cfg=cfg)
+        torch.cuda.synchronize()
+        got = acc[:, torch.from_numpy(cols).to(DEV)].cpu().numpy()
+        if int8:
+            assert np.array_equal(got.astype(np.int64), ref), f"{cfg}"
+        else:
+            assert np.all(np.abs(got.astype(np.float64) - ref) <= bound), f"{cfg}"
