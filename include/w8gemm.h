@@ -20,7 +20,9 @@
  *                weights: E4M3FN codes, fp32 sw[N] (one per output channel);
  *                fp32 accumulation.
  *   W8A8_INT8    activations: per-token int8 codes, fp32 sx[M];
- *                weights: int8 codes, fp32 sw[N]; exact int32 accumulation.
+ *                weights: int8 codes, fp32 sw[N]; exact int32 accumulation
+ *                (exact for any codes up to K = 133144, where K * 127^2
+ *                reaches 2^31; beyond it, as far as the sums stay in int32).
  *   Block_FP8    activations: E4M3FN, fp32 sx[M, K/128] (1x128 groups);
  *                weights: E4M3FN, fp32 sw[ceil(N/128), K/128] (128x128
  *                blocks); each 128-wide K group's partial dot product is
