@@ -29,7 +29,7 @@ int u_index(int u) { return u == 1 ? 0 : u == 2 ? 1 : u == 4 ? 2 : -1; }
 
 // [fmt][mb-1][nb][wk][wn][unroll][swap][packed][xl] -> launcher
 struct InstanceIndex {
-  GemmLaunchFn fn[3][2][3][5][4][3][2][2][3] = {};
+  GemmLaunchFn fn[3][2][3][5][4][3][2][2][4] = {};
   InstanceIndex() {
     int n = 0;
     const GemmInstance* p = gemm_instances(&n);
@@ -113,10 +113,16 @@ w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c) {
     return fail(W8_E_INVALID, "cfg.quant_launch must be 0 or 1");
   if (op != W8_OP_LINEAR && op != W8_OP_MOE_LINEAR && c.quant_launch)
     return fail(W8_E_INVALID, "cfg.quant_launch is for the linear ops only");
+  // fused quantization: staged in LDS (x_lds 1), or for the Block_FP8
+  // linear op also in the K loop (x_lds 0: each wave quantizes the 1x128
+  // groups it loads)
   if ((op == W8_OP_LINEAR || op == W8_OP_MOE_LINEAR) && !c.quant_launch &&
-      (!c.x_lds || c.waves_k > 4))
+      (c.x_lds ? c.waves_k > 4
+               : (op != W8_OP_LINEAR || fmt != W8_BLOCK_FP8 || c.unroll > 2 || c.waves_k > 8)))
     return fail(W8_E_INVALID,
-                "cfg: fused quantization (quant_launch == 0) needs x_lds == 1 and waves_k <= 4");
+                "cfg: fused quantization (quant_launch == 0) needs x_lds == 1 and waves_k <= 4, "
+                "or for the Block_FP8 linear op x_lds == 0 (quantized in the K loop) with "
+                "waves_k <= 8 and unroll <= 2");
   if (u_index(c.unroll) < 0) return fail(W8_E_INVALID, "cfg.unroll must be 1, 2 or 4");
   if ((c.tile_n / 16) * c.unroll > 4)
     return fail(W8_E_INVALID, "cfg: tile_n/16 * unroll must be at most 4");
@@ -248,7 +254,8 @@ w8_status launch_gemm_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
   const int nb = c.tile_n / 16;
   GemmLaunchFn fn =
       instance_index().fn[g.fmt][mb - 1][nb_index(nb)][wk_index(c.waves_k)][wn_index(c.waves_n)]
-                         [u_index(c.unroll)][c.swap_ab][g.packed ? 1 : 0][g.x ? 2 : c.x_lds];
+                         [u_index(c.unroll)][c.swap_ab][g.packed ? 1 : 0]
+                         [g.x ? (c.x_lds ? 2 : 3) : c.x_lds];
   if (!fn) return fail(W8_E_INVALID, "no compiled kernel for this config");
   const int ntiles = tiles_of(g.N, c);
   GemmArgs a;

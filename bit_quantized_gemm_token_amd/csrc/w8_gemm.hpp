@@ -162,6 +162,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
   constexpr bool BLOCK = (FMT == BLOCK_FP8);
   static_assert(WN == 1 || WK == 1, "the waves of a workgroup split either K or N");
   static_assert(WN == 1 || XL, "waves side by side along N share activations through LDS");
+  static_assert(XL != 3 || (BLOCK && WN == 1), "quantization in the K loop: Block_FP8, WN == 1");
   // activation row (codes and scales, or XL == 2 the bf16 row) of row m of
   // this call
   auto xr = [&](int m) -> long long {
@@ -170,7 +171,10 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
     else
       return m;
   };
-  // XL: the segment's activation fragments are staged in LDS up front, one
+  // XL 3 (Block_FP8 linear): no staging; each wave loads the bf16
+  // activations of its K-steps in its stages and quantizes every 1x128
+  // group in the K loop.
+  // XL 1, 2: the segment's activation fragments are staged in LDS up front, one
   // 1 KiB chunk (16 bytes per lane) per (K-step, M block, 16-byte load):
   // chunk ((k - ka) * MB + b) * CH + jj.  XL == 1 copies the codes; XL == 2
   // (fused quantization) quantizes bf16 activations into them.
@@ -187,6 +191,13 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
   const uint8_t* xrow[MB];
 #pragma unroll
   for (int b = 0; b < MB; ++b) xrow[b] = a.xq + xr(min(16 * b + r, a.M - 1)) * a.ldq + 16 * g;
+  // XL == 3: the lane's bf16 activations (row stride ldq in elements), the
+  // same 2 x 16 elements of each K-step whose codes it feeds to the MFMA.
+  const uint16_t* xrow16[MB];
+#pragma unroll
+  for (int b = 0; b < MB; ++b)
+    xrow16[b] = reinterpret_cast<const uint16_t*>(a.xq) + xr(min(16 * b + r, a.M - 1)) * a.ldq +
+                16 * g;
 
   // Block_FP8 sx rows of the accumulator elements this lane holds (SWAP: one
   // m per lane; else four), and the per-token formats' epilogue sx, loaded
@@ -194,7 +205,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
   constexpr int SXN = SWAP ? 1 : 4;
   const int nthreads = 64 * WK * WN;
   __shared__ Acc red[WK > 1 ? (WK - 1) * MB * NB * 64 : 1];
-  __shared__ v4i xl[XL ? kXlChunks * 64 : 1];
+  __shared__ v4i xl[(XL == 1 || XL == 2) ? kXlChunks * 64 : 1];
   // XL == 2: activation scales computed here -- per row for the per-token
   // formats, per (staged group, row) for Block_FP8.
   __shared__ float sxl[XL == 2 ? (BLOCK ? kXlMaxGroups * 32 : 32) : 1];
@@ -217,7 +228,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
       const int m = min(SWAP ? 16 * b + r : 16 * b + 4 * g + i, a.M - 1);
       sxm[b][i] = m;
       if constexpr (BLOCK) {
-        sxrow[b][i] = XL == 2 ? nullptr : a.sx + xr(m) * a.sgroups;
+        sxrow[b][i] = XL >= 2 ? nullptr : a.sx + xr(m) * a.sgroups;
         ep_sx[b][i] = 0.0f;
       } else {
         sxrow[b][i] = nullptr;
@@ -280,6 +291,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
     struct Stage {
       Frag w[U][NB];
       Frag x[XL ? 1 : U][MB];  // !XL: the wave's own activation fragments
+      v4u xb[XL == 3 ? U : 1][XL == 3 ? MB : 1][2][2];  // XL == 3: bf16, quantized in run_stage
       float sw[BLOCK ? U : 1];
       float sx[BLOCK ? U : 1][MB][SXN];
     };
@@ -293,9 +305,19 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
 #pragma unroll
           for (int b = 0; b < MB; ++b) st.x[u][b] = load_frag<FMT>(xrow[b], k);
         }
+        if constexpr (XL == 3) {
+#pragma unroll
+          for (int b = 0; b < MB; ++b)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+              const uint16_t* src = xrow16[b] + (long long)k * KSTEP + 64 * jj;
+              st.xb[u][b][jj][0] = *reinterpret_cast<const v4u*>(src);
+              st.xb[u][b][jj][1] = *reinterpret_cast<const v4u*>(src + 8);
+            }
+        }
         if constexpr (BLOCK) {
           st.sw[u] = swrow[k];
-          if constexpr (XL != 2) {  // XL == 2: staged scales, read from LDS in run_stage
+          if constexpr (XL < 2) {  // XL >= 2: scales computed here (LDS or registers)
 #pragma unroll
             for (int b = 0; b < MB; ++b)
 #pragma unroll
@@ -329,7 +351,36 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
           const Frag zero = {};
           w[j] = (decltype(mask)::value && k0 + u < la) ? zero : st.w[u][j];
         }
-        if constexpr (XL) {
+        if constexpr (XL == 3) {
+          // Quantize the loaded 1x128 groups (the standalone quantizer's
+          // steps): the four lanes l, l^16, l^32, l^48 hold one row's group,
+          // so two shuffles give its maximum; SWAP = 0 accumulator lanes get
+          // their rows' scales from lane 4g + i.
+          Frag x[MB];
+          float sx[MB][SXN];
+#pragma unroll
+          for (int b = 0; b < MB; ++b) {
+            float gm = 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+              gm = fmaxf(gm, fmaxf(absmax8(st.xb[u][b][jj][0]), absmax8(st.xb[u][b][jj][1])));
+            gm = fmaxf(gm, __shfl_xor(gm, 16, 64));
+            gm = fmaxf(gm, __shfl_xor(gm, 32, 64));
+            const float sc = act_scale<false>(gm);
+            const float rs = act_recip(sc);
+            v4i q[2];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+              const v2u ql = encode8<false>(st.xb[u][b][jj][0], sc, rs),
+                        qh = encode8<false>(st.xb[u][b][jj][1], sc, rs);
+              q[jj] = v4i{(int)ql[0], (int)ql[1], (int)qh[0], (int)qh[1]};
+            }
+            x[b] = __builtin_shufflevector(q[0], q[1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int i = 0; i < SXN; ++i) sx[b][i] = SWAP ? sc : __shfl(sc, 4 * g + i, 64);
+          }
+          step(w, x, st.sw[u], sx);
+        } else if constexpr (XL) {
           const int k = max(k0 + u, la);
           Frag x[MB];
 #pragma unroll
@@ -495,7 +546,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
         put(u0);
       }
     }
-    if constexpr (XL) {
+    if constexpr (XL == 1 || XL == 2) {
       // the copies (and the first weight stages) have landed in every wave
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();

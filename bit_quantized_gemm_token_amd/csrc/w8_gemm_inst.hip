@@ -37,6 +37,18 @@
   W8_U(MB, 1, 1, 2) W8_U(MB, 2, 1, 2) W8_U(MB, 4, 1, 2) W8_U(MB, 1, 2, 2)             \
   W8_U(MB, 1, 4, 2) W8_U(MB, 1, 8, 2)
 
+// Block_FP8 also has the linear op's in-K-loop quantization (XL 3): WN 1,
+// WK in {1, 2, 4, 8}, UNROLL <= 2 (the bf16 activations of a stage double
+// its activation registers).
+#define W8_U3(MB, WK)                                                          \
+  W8_P(MB, 1, WK, 1, 1, 3) W8_P(MB, 1, WK, 1, 2, 3) W8_P(MB, 2, WK, 1, 1, 3)   \
+  W8_P(MB, 2, WK, 1, 2, 3) W8_P(MB, 4, WK, 1, 1, 3)
+#if W8_FMT == 2
+#define W8_W3(MB) W8_U3(MB, 1) W8_U3(MB, 2) W8_U3(MB, 4) W8_U3(MB, 8)
+#else
+#define W8_W3(MB)
+#endif
+
 // The MoE grouped GEMM: the same (MB, NB, UNROLL, PACKED) and (WK, WN, XL) in
 // {(1, 1, 0), (2, 1, 0), (4, 1, 0), (8, 1, 0), (1, 2, 1), (1, 4, 1), (1, 8, 1)}
 // on quantized activations, and with fused quantization (XL 2) in
@@ -57,7 +69,7 @@
 namespace w8 {
 
 #if W8_PART < 2
-static const GemmInstance kInstances[] = {W8_W(W8_MB)};
+static const GemmInstance kInstances[] = {W8_W(W8_MB) W8_W3(W8_MB)};
 
 const GemmInstance* W8_CAT(gemm_instances_f, W8_FMT, W8_SWAP, W8_PART)(int* count) {
   *count = (int)(sizeof(kInstances) / sizeof(kInstances[0]));

@@ -166,7 +166,10 @@ def test_default_config_is_valid_everywhere(w8):
             cl = w8.default_config(fmt, M, N, K, op="linear")
             w8.validate_config(fmt, M, N, K, cl, op="linear")
             assert cl.x_lds == 1
-            assert not _valid_op(w8, fmt, M, N, K, c, "linear")      # the GEMM default has no x_lds
+            # the GEMM default has no x_lds: a linear config only where the
+            # Block_FP8 linear op quantizes in the K loop (unroll <= 2)
+            assert _valid_op(w8, fmt, M, N, K, c, "linear") == (
+                fmt == "Block_FP8" and c.unroll <= 2 and c.waves_k <= 8)
 
 
 def _valid_op(w8, fmt, M, N, K, cfg, op):
@@ -186,6 +189,16 @@ def test_linear_config_rules(w8):
                      w8.Config.make(waves_k=1, waves_n=8, x_lds=1), "linear")
     with pytest.raises(ValueError):
         w8.validate_config("FP8_Dynamic", 4, 512, 1024, ok, op="fused")
+    # Block_FP8 linear may quantize in the K loop (x_lds 0): waves along K
+    # only, at most 8 of them, unroll <= 2; not the per-token formats
+    inloop = w8.Config.make(waves_k=8, unroll=2, x_lds=0, split_k=2)
+    assert _valid_op(w8, "Block_FP8", 4, 512, 1024, inloop, "linear")
+    assert not _valid_op(w8, "FP8_Dynamic", 4, 512, 1024, inloop, "linear")
+    assert not _valid_op(w8, "W8A8_INT8", 4, 512, 1024, inloop, "linear")
+    for bad in (w8.Config.make(waves_k=8, unroll=4, tile_n=16, x_lds=0),
+                w8.Config.make(waves_k=16, unroll=1, x_lds=0)):
+        assert not _valid_op(w8, "Block_FP8", 4, 512, 1024, bad, "linear")
+    assert not _valid_op(w8, "Block_FP8", 4, 512, 1024, inloop, "moe_linear")
 
 
 def test_quant_launch_rules_and_workspace(w8):
@@ -338,7 +351,8 @@ def test_table_roundtrip_and_lookup(w8, tmp_path):
     got, hit = w8.resolve_config("Block_FP8", 32, 4608, 7168, op="linear")
     assert hit == 0 and got == w8.model_config("Block_FP8", 32, 4608, 7168, op="linear")
     with pytest.raises(w8.W8Error):                                  # a GEMM config is no linear one
-        w8.set_config("Block_FP8", 32, 4608, 7168, c2, 5.5, packed=True, op="linear")
+        w8.set_config("Block_FP8", 32, 4608, 7168, w8.Config.make(tile_n=16, waves_k=16, unroll=1),
+                      5.5, packed=True, op="linear")
     p = tmp_path / "t.tbl"
     w8.save_config_table(str(p))
     assert " linear packed 32 4608 7168 " in p.read_text()

@@ -258,3 +258,54 @@ def test_fused_rejects_gemm_config(w8):
     cs = case("W8A8_INT8", 4, 64, 256)
     with pytest.raises(w8.W8Error, match="x_lds"):
         fused(w8, cs, w8.Config.make(waves_k=4), False)
+
+
+@pytest.mark.parametrize("M", [17, 3])
+def test_every_block_fp8_k_loop_instance(w8, M):
+    """Block_FP8 linear quantizing in the K loop (x_lds = 0: each wave
+    quantizes the 1x128 groups it loads): every instance (tile_n x waves_k x
+    unroll x swap_ab x layout) with whole tiles, split-K and stream-K, at
+    M = 17 (two row blocks) and M = 3, bit-identical to the two-launch path
+    with the same config, and within the bar of the oracle."""
+    fmt, N, K = "Block_FP8", 200, 1280
+    cs = case(fmt, M, N, K)
+    n = 0
+    for tn, wk, u, swap, (s, grid), packed in itertools.product(
+            (16, 32, 64), (1, 2, 4, 8), (1, 2), (0, 1), ((1, 0), (4, 0), (1, 3)), (False, True)):
+        if (tn // 16) * u > 4:
+            continue
+        cfg = w8.Config.make(tile_n=tn, waves_k=wk, waves_n=1, unroll=u, split_k=s, grid=grid,
+                             swap_ab=swap, x_lds=0)
+        y1 = fused(w8, cs, cfg, packed)
+        y2 = two_launch(w8, cs, cfg, packed)
+        torch.cuda.synchronize()
+        assert same_bits(y1, y2), f"{cfg} packed={packed}: K-loop quantization != two-launch"
+        n += 1
+    assert n == 5 * 4 * 2 * 3 * 2
+    assert_bf16_close(y1, cs.Y, f"K-loop fused M={M}")
+
+
+def test_block_fp8_k_loop_large_and_extreme(w8):
+    """The K-loop quantization at 4608 x 7168 (M = 1, 8, 32) and on rows of
+    extreme magnitude (subnormal, -0, 2^120 scales): bit-identical to the
+    two-launch path."""
+    import synthetic
+    from tests.gpu_cases import to_bf16_tensor
+    fmt = "Block_FP8"
+    for M in (1, 8, 32):
+        cs = case(fmt, M, 4608, 7168)
+        for cfg in (w8.Config.make(tile_n=16, waves_k=4, unroll=1, split_k=1),
+                    w8.Config.make(tile_n=32, waves_k=2, unroll=2, split_k=4, swap_ab=1)):
+            y1 = fused(w8, cs, cfg, True)
+            y2 = two_launch(w8, cs, cfg, True)
+            torch.cuda.synchronize()
+            assert same_bits(y1, y2), f"M={M} {cfg}"
+        assert_bf16_close(y1, cs.Y, f"K-loop fused 4608x7168 M={M}")
+    cs = case(fmt, 21, 256, 1024)
+    x = to_bf16_tensor(synthetic.activations_extreme(fmt, 21, 1024))
+    cfg = w8.Config.make(tile_n=16, waves_k=8, unroll=1, split_k=2)
+    xq, sx = w8.quantize_act(fmt, x)
+    ref = w8.gemm_w8a8(fmt, xq, sx, cs.weights(True), cs.sw, cfg=cfg)
+    y = fused(w8, cs, cfg, True, x=x)
+    torch.cuda.synchronize()
+    assert same_bits(y, ref)
