@@ -130,8 +130,10 @@ typedef enum {
  *   swap_ab  0: MFMA A operand = activations, B = weights^T.
  *            1: Swap-AB, Y^T = Wq . Xq^T: A = weights, B = activations^T.
  *   quant_launch  W8_OP_LINEAR and W8_OP_MOE_LINEAR only (0 for the other
- *            ops).  0: the activations are quantized inside the GEMM (needs
- *            x_lds == 1 and waves_k <= 4).  1: they are quantized by a launch of their own
+ *            ops).  0: the activations are quantized inside the GEMM: staged
+ *            in LDS (x_lds == 1, waves_k <= 4), or for the Block_FP8 linear
+ *            op also in the K loop (x_lds == 0, waves_n == 1, waves_k <= 8,
+ *            unroll <= 2).  1: they are quantized by a launch of their own
  *            (w8_quantize_act's kernel) into the workspace, and the GEMM
  *            runs with this config under the W8_OP_GEMM rules.  The tuner
  *            tries both for the linear op and keeps the faster.
@@ -283,11 +285,13 @@ w8_status w8_gemm_w8a8_acc(w8_fmt fmt, int M, int N, int K,
 
 /* The whole linear layer on bf16 activations.  With quant_launch == 0, one
  * kernel launch: activation quantization (the w8_quantize_act rules, giving
- * the same codes and scales) fused into the GEMM.  Each workgroup quantizes
- * the activations of its K range into LDS: per 1x128 group for Block_FP8;
- * per token for the other formats, after a pass over the whole row for its
- * absolute maximum.  Either way Y equals w8_quantize_act followed by
- * w8_gemm_w8a8 with the same tile config, bit for bit.
+ * the same codes and scales) fused into the GEMM.  With x_lds == 1 each
+ * workgroup quantizes the activations of its K range into LDS: per 1x128
+ * group for Block_FP8; per token for the other formats, after a pass over
+ * the whole row for its absolute maximum.  With x_lds == 0 (Block_FP8 only)
+ * each wave quantizes the 1x128 groups it loads inside the K loop.  Either
+ * way Y equals w8_quantize_act followed by w8_gemm_w8a8 with the same tile
+ * config, bit for bit.
  *   x       bf16 [M, K], row stride ldx elements (device), 16-byte aligned,
  *           ldx % 8 == 0
  *   wq, sw, y, ws, stream  as for w8_gemm_w8a8
