@@ -39,11 +39,13 @@ def _units():
              ("w8_model.cpp", ["-x", "hip"], "w8_model.o"),
              ("w8_moe.cpp", ["-x", "hip"], "w8_moe.o"),
              ("w8_registry.cpp", ["-x", "hip"], "w8_registry.o")]
-    # the instance file in 24 parts (the GEMM parts, the largest, first so
-    # the pool stays busy), then the small units
+    # the instance file in 28 parts (the GEMM parts, the largest, first so
+    # the pool stays busy; parts 4 and 5 exist for Block_FP8 only), then the
+    # small units
     inst = [("w8_gemm_inst.hip", [f"-DW8_FMT={fmt}", f"-DW8_SWAP={swap}", f"-DW8_PART={part}"],
              f"w8_gemm_f{fmt}_s{swap}_p{part}.o")
-            for part in (0, 1, 2, 3) for fmt in (0, 1, 2) for swap in (0, 1)]
+            for part in (0, 1, 2, 3, 4, 5) for fmt in (0, 1, 2) for swap in (0, 1)
+            if part < 4 or fmt == 2]
     return inst + units
 
 

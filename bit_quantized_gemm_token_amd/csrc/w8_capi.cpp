@@ -118,11 +118,12 @@ w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c) {
   // groups it loads)
   if ((op == W8_OP_LINEAR || op == W8_OP_MOE_LINEAR) && !c.quant_launch &&
       (c.x_lds ? c.waves_k > 4
-               : (op != W8_OP_LINEAR || fmt != W8_BLOCK_FP8 || c.unroll > 2 || c.waves_k > 8)))
+               : (op != W8_OP_LINEAR || fmt != W8_BLOCK_FP8 || c.unroll != 1 ||
+                  c.tile_n > 32 || c.waves_k < 2 || c.waves_k > 8)))
     return fail(W8_E_INVALID,
                 "cfg: fused quantization (quant_launch == 0) needs x_lds == 1 and waves_k <= 4, "
                 "or for the Block_FP8 linear op x_lds == 0 (quantized in the K loop) with "
-                "waves_k <= 8 and unroll <= 2");
+                "tile_n 16 or 32, unroll 1 and waves_k 2, 4 or 8");
   if (u_index(c.unroll) < 0) return fail(W8_E_INVALID, "cfg.unroll must be 1, 2 or 4");
   if ((c.tile_n / 16) * c.unroll > 4)
     return fail(W8_E_INVALID, "cfg: tile_n/16 * unroll must be at most 4");

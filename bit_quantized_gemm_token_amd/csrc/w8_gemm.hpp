@@ -173,7 +173,10 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
   };
   // XL 3 (Block_FP8 linear): no staging; each wave loads the bf16
   // activations of its K-steps in its stages and quantizes every 1x128
-  // group in the K loop.
+  // group in the K loop.  (Not for the per-token formats: a wave quantizes
+  // all 16 rows of its MFMA tile at every K-step whatever M is, and every
+  // workgroup repeats it, so the quantization's ALU work outweighs the
+  // separate launch it saves -- measured 3-4x slower.)
   // XL 1, 2: the segment's activation fragments are staged in LDS up front, one
   // 1 KiB chunk (16 bytes per lane) per (K-step, M block, 16-byte load):
   // chunk ((k - ka) * MB + b) * CH + jj.  XL == 1 copies the codes; XL == 2
@@ -236,6 +239,45 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
       }
     }
 
+  // Per-token formats, XL == 2: row absolute maxima over the whole of K.
+  // Each row is split over max(1, waves / M) waves, each lane keeps a
+  // running maximum of its chunks (two or four loads in flight), one wave
+  // reduction per (row, part), folded into the row's word (|x| >= 0: its
+  // float bits order as unsigned integers); then the epilogue's row scales.
+  auto row_pass = [&]() {
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(a.xq);
+    unsigned* amx = reinterpret_cast<unsigned*>(sxl);
+    const int nw = WK * WN;
+    const int wpr = max(1, nw / a.M);  // waves per row
+    const int cpr = a.K / 8;           // 16-byte chunks per row
+    const int step = 64 * wpr;
+    for (int slot = wave; slot < a.M * wpr; slot += nw) {
+      const int m = slot / wpr, part = slot - m * wpr;
+      const uint16_t* rowp = xb + xr(m) * a.ldq;
+      float mx = 0.0f;
+      constexpr int QA = WK * WN >= 8 ? 2 : 4;  // loads in flight per lane (registers)
+      for (int c0 = part * 64 + lane; c0 < cpr; c0 += QA * step) {
+        v4u v[QA];
+#pragma unroll
+        for (int q = 0; q < QA; ++q) {
+          const int c = c0 + q * step;
+          v[q] = v4u{0u, 0u, 0u, 0u};
+          if (c < cpr) v[q] = *reinterpret_cast<const v4u*>(rowp + 8 * c);
+        }
+#pragma unroll
+        for (int q = 0; q < QA; ++q) mx = fmaxf(mx, absmax8(v[q]));
+      }
+      mx = wave_max(mx);
+      if (lane == 0) atomicMax(&amx[m], __float_as_uint(mx));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int i = 0; i < SXN; ++i) ep_sx[b][i] = act_scale<INT8>(__uint_as_float(amx[sxm[b][i]]));
+    rows_done = true;
+  };
+
   // One segment: K-steps [ka, kb) of output tile `tile` (WN*NB blocks of 16
   // weight rows).  The segment is contributor `slot` of the `count`
   // workgroups that cover the tile; count == 1 writes Y directly.
@@ -291,7 +333,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
     struct Stage {
       Frag w[U][NB];
       Frag x[XL ? 1 : U][MB];  // !XL: the wave's own activation fragments
-      v4u xb[XL == 3 ? U : 1][XL == 3 ? MB : 1][2][2];  // XL == 3: bf16, quantized in run_stage
+      v4u xb[XL == 3 ? U : 1][XL == 3 ? MB : 1][CH][2];  // XL == 3: bf16, quantized in run_stage
       float sw[BLOCK ? U : 1];
       float sx[BLOCK ? U : 1][MB][SXN];
     };
@@ -309,7 +351,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
 #pragma unroll
           for (int b = 0; b < MB; ++b)
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
+            for (int jj = 0; jj < CH; ++jj) {
               const uint16_t* src = xrow16[b] + (long long)k * KSTEP + 64 * jj;
               st.xb[u][b][jj][0] = *reinterpret_cast<const v4u*>(src);
               st.xb[u][b][jj][1] = *reinterpret_cast<const v4u*>(src + 8);
@@ -501,44 +543,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
       };
       fetch(threadIdx.x);
       if constexpr (!BLOCK) {
-        if (!rows_done) {
-          // Row absolute maxima over the whole of K: each row is split over
-          // max(1, waves / M) waves, each lane keeps a running maximum of its
-          // chunks (two or four loads in flight), one wave reduction per (row,
-          // part), folded into the row's word (|x| >= 0: its float bits
-          // order as unsigned integers).
-          unsigned* amx = reinterpret_cast<unsigned*>(sxl);
-          const int nw = WK * WN;
-          const int wpr = max(1, nw / a.M);  // waves per row
-          const int cpr = a.K / 8;           // 16-byte chunks per row
-          const int step = 64 * wpr;
-          for (int slot = wave; slot < a.M * wpr; slot += nw) {
-            const int m = slot / wpr, part = slot - m * wpr;
-            const uint16_t* rowp = xb + xr(m) * a.ldq;
-            float mx = 0.0f;
-            constexpr int QA = WK * WN >= 8 ? 2 : 4;  // loads in flight per lane (registers)
-            for (int c0 = part * 64 + lane; c0 < cpr; c0 += QA * step) {
-              v4u v[QA];
-#pragma unroll
-              for (int q = 0; q < QA; ++q) {
-                const int c = c0 + q * step;
-                v[q] = v4u{0u, 0u, 0u, 0u};
-                if (c < cpr) v[q] = *reinterpret_cast<const v4u*>(rowp + 8 * c);
-              }
-#pragma unroll
-              for (int q = 0; q < QA; ++q) mx = fmaxf(mx, absmax8(v[q]));
-            }
-            mx = wave_max(mx);
-            if (lane == 0) atomicMax(&amx[m], __float_as_uint(mx));
-          }
-          __syncthreads();
-#pragma unroll
-          for (int b = 0; b < MB; ++b)
-#pragma unroll
-            for (int i = 0; i < SXN; ++i)
-              ep_sx[b][i] = act_scale<INT8>(__uint_as_float(amx[sxm[b][i]]));
-          rows_done = true;
-        }
+        if (!rows_done) row_pass();
       }
       put(threadIdx.x);
       for (int u0 = threadIdx.x + QB * nthreads; u0 < nunits; u0 += QB * nthreads) {

@@ -1,8 +1,9 @@
 // Explicit instances of the GEMM family for one format, one Swap-AB setting
 // and one part: W8_PART 0 and 1 are the GEMM instances with MB = 1 and 2,
-// 2 and 3 the MoE grouped instances with MB = 1 and 2.  The build compiles
-// this file once per (W8_FMT, W8_SWAP, W8_PART) so the instances compile in
-// parallel.
+// 2 and 3 the MoE grouped instances with MB = 1 and 2, 4 and 5 the Block_FP8
+// linear op's instances that quantize in the K loop (XL 3) with MB = 1 and 2.  The
+// build compiles this file once per (W8_FMT, W8_SWAP, W8_PART) so the
+// instances compile in parallel.
 #include "w8_gemm.hpp"
 
 #ifndef W8_FMT
@@ -37,17 +38,12 @@
   W8_U(MB, 1, 1, 2) W8_U(MB, 2, 1, 2) W8_U(MB, 4, 1, 2) W8_U(MB, 1, 2, 2)             \
   W8_U(MB, 1, 4, 2) W8_U(MB, 1, 8, 2)
 
-// Block_FP8 also has the linear op's in-K-loop quantization (XL 3): WN 1,
-// WK in {1, 2, 4, 8}, UNROLL <= 2 (the bf16 activations of a stage double
-// its activation registers).
-#define W8_U3(MB, WK)                                                          \
-  W8_P(MB, 1, WK, 1, 1, 3) W8_P(MB, 1, WK, 1, 2, 3) W8_P(MB, 2, WK, 1, 1, 3)   \
-  W8_P(MB, 2, WK, 1, 2, 3) W8_P(MB, 4, WK, 1, 1, 3)
-#if W8_FMT == 2
-#define W8_W3(MB) W8_U3(MB, 1) W8_U3(MB, 2) W8_U3(MB, 4) W8_U3(MB, 8)
-#else
-#define W8_W3(MB)
-#endif
+// Block_FP8's linear op quantizing in the K loop (XL 3): WN 1, WK in {2, 4,
+// 8}, tile_n 16 or 32, UNROLL 1 (the shapes it wins on; the bf16
+// activations of a stage double its activation registers).  Parts 4 and 5
+// hold them (Block_FP8 only).
+#define W8_U3(MB, WK) W8_P(MB, 1, WK, 1, 1, 3) W8_P(MB, 2, WK, 1, 1, 3)
+#define W8_W3(MB) W8_U3(MB, 2) W8_U3(MB, 4) W8_U3(MB, 8)
 
 // The MoE grouped GEMM: the same (MB, NB, UNROLL, PACKED) and (WK, WN, XL) in
 // {(1, 1, 0), (2, 1, 0), (4, 1, 0), (8, 1, 0), (1, 2, 1), (1, 4, 1), (1, 8, 1)}
@@ -68,8 +64,14 @@
 
 namespace w8 {
 
+#if W8_PART > 3 && W8_FMT != 2
+#error "parts 4 and 5 exist for Block_FP8 only"
+#elif W8_PART < 2 || W8_PART > 3
 #if W8_PART < 2
-static const GemmInstance kInstances[] = {W8_W(W8_MB) W8_W3(W8_MB)};
+static const GemmInstance kInstances[] = {W8_W(W8_MB)};
+#else
+static const GemmInstance kInstances[] = {W8_W3(W8_MB)};
+#endif
 
 const GemmInstance* W8_CAT(gemm_instances_f, W8_FMT, W8_SWAP, W8_PART)(int* count) {
   *count = (int)(sizeof(kInstances) / sizeof(kInstances[0]));

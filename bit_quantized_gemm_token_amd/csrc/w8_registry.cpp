@@ -1,5 +1,6 @@
 // Gathers the GEMM instances compiled in the per-(format, swap, part)
-// translation units into one table.
+// translation units into one table (parts 0, 1 and, for Block_FP8, 4, 5:
+// GEMM; 2, 3: MoE).
 #include <vector>
 
 #include "w8_launch.hpp"
@@ -11,6 +12,11 @@ namespace w8 {
   const GemmInstance* gemm_instances_f##F##_##S##_1(int*); \
   const MoeInstance* moe_instances_f##F##_##S##_2(int*);   \
   const MoeInstance* moe_instances_f##F##_##S##_3(int*);
+// Block_FP8's K-loop quantization instances
+const GemmInstance* gemm_instances_f2_0_4(int*);
+const GemmInstance* gemm_instances_f2_0_5(int*);
+const GemmInstance* gemm_instances_f2_1_4(int*);
+const GemmInstance* gemm_instances_f2_1_5(int*);
 W8_DECL_PARTS(0, 0)
 W8_DECL_PARTS(0, 1)
 W8_DECL_PARTS(1, 0)
@@ -25,7 +31,7 @@ std::vector<I> gather(const I* (*const* parts)(int*), int n) {
   for (int i = 0; i < n; ++i) {
     int c = 0;
     const I* p = parts[i](&c);
-    v.insert(v.end(), p, p + c);
+    if (c > 0) v.insert(v.end(), p, p + c);
   }
   return v;
 }
@@ -47,10 +53,12 @@ const MoeInstance* moe_instances(int* count) {
 
 const GemmInstance* gemm_instances(int* count) {
   static const std::vector<GemmInstance> all = [] {
-    const GemmInstance* (*const parts[])(int*) = {W8_GEMM_PARTS(0, 0), W8_GEMM_PARTS(0, 1),
-                                                  W8_GEMM_PARTS(1, 0), W8_GEMM_PARTS(1, 1),
-                                                  W8_GEMM_PARTS(2, 0), W8_GEMM_PARTS(2, 1)};
-    return gather<GemmInstance>(parts, 12);
+    const GemmInstance* (*const parts[])(int*) = {
+        W8_GEMM_PARTS(0, 0),   W8_GEMM_PARTS(0, 1),   W8_GEMM_PARTS(1, 0),
+        W8_GEMM_PARTS(1, 1),   W8_GEMM_PARTS(2, 0),   W8_GEMM_PARTS(2, 1),
+        gemm_instances_f2_0_4, gemm_instances_f2_0_5, gemm_instances_f2_1_4,
+        gemm_instances_f2_1_5};
+    return gather<GemmInstance>(parts, (int)(sizeof(parts) / sizeof(parts[0])));
   }();
   *count = (int)all.size();
   return all.data();

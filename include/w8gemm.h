@@ -132,8 +132,9 @@ typedef enum {
  *   quant_launch  W8_OP_LINEAR and W8_OP_MOE_LINEAR only (0 for the other
  *            ops).  0: the activations are quantized inside the GEMM: staged
  *            in LDS (x_lds == 1, waves_k <= 4), or for the Block_FP8 linear
- *            op also in the K loop (x_lds == 0, waves_n == 1, waves_k <= 8,
- *            unroll <= 2).  1: they are quantized by a launch of their own
+ *            op also in the K loop (x_lds == 0, tile_n 16 or 32, waves_n 1,
+ *            waves_k 2, 4 or 8, unroll 1).  1: they are quantized by a
+ *            launch of their own
  *            (w8_quantize_act's kernel) into the workspace, and the GEMM
  *            runs with this config under the W8_OP_GEMM rules.  The tuner
  *            tries both for the linear op and keeps the faster.

@@ -166,10 +166,8 @@ def test_default_config_is_valid_everywhere(w8):
             cl = w8.default_config(fmt, M, N, K, op="linear")
             w8.validate_config(fmt, M, N, K, cl, op="linear")
             assert cl.x_lds == 1
-            # the GEMM default has no x_lds: a linear config only where the
-            # Block_FP8 linear op quantizes in the K loop (unroll <= 2)
-            assert _valid_op(w8, fmt, M, N, K, c, "linear") == (
-                fmt == "Block_FP8" and c.unroll <= 2 and c.waves_k <= 8)
+            # the GEMM default (no x_lds, unroll 2) is no linear config
+            assert not _valid_op(w8, fmt, M, N, K, c, "linear")
 
 
 def _valid_op(w8, fmt, M, N, K, cfg, op):
@@ -190,13 +188,16 @@ def test_linear_config_rules(w8):
     with pytest.raises(ValueError):
         w8.validate_config("FP8_Dynamic", 4, 512, 1024, ok, op="fused")
     # Block_FP8 linear may quantize in the K loop (x_lds 0): waves along K
-    # only, at most 8 of them, unroll <= 2; not the per-token formats
-    inloop = w8.Config.make(waves_k=8, unroll=2, x_lds=0, split_k=2)
+    # only, at most 8 of them, unroll <= 2; not the per-token formats (their
+    # row scale needs the whole row), not the grouped op
+    inloop = w8.Config.make(waves_k=8, unroll=1, x_lds=0, split_k=2)
     assert _valid_op(w8, "Block_FP8", 4, 512, 1024, inloop, "linear")
     assert not _valid_op(w8, "FP8_Dynamic", 4, 512, 1024, inloop, "linear")
     assert not _valid_op(w8, "W8A8_INT8", 4, 512, 1024, inloop, "linear")
-    for bad in (w8.Config.make(waves_k=8, unroll=4, tile_n=16, x_lds=0),
-                w8.Config.make(waves_k=16, unroll=1, x_lds=0)):
+    for bad in (w8.Config.make(waves_k=8, unroll=2, tile_n=16, x_lds=0),
+                w8.Config.make(waves_k=16, unroll=1, x_lds=0),
+                w8.Config.make(waves_k=1, unroll=1, x_lds=0),
+                w8.Config.make(waves_k=4, unroll=1, tile_n=64, x_lds=0)):
         assert not _valid_op(w8, "Block_FP8", 4, 512, 1024, bad, "linear")
     assert not _valid_op(w8, "Block_FP8", 4, 512, 1024, inloop, "moe_linear")
 

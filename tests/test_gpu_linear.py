@@ -255,6 +255,8 @@ def test_quant_launch_shares_workspace_with_split_k(w8):
 
 
 def test_fused_rejects_gemm_config(w8):
+    """A GEMM config (no x_lds) is no per-token linear config: refused
+    before any launch."""
     cs = case("W8A8_INT8", 4, 64, 256)
     with pytest.raises(w8.W8Error, match="x_lds"):
         fused(w8, cs, w8.Config.make(waves_k=4), False)
@@ -264,25 +266,23 @@ def test_fused_rejects_gemm_config(w8):
 def test_every_block_fp8_k_loop_instance(w8, M):
     """Block_FP8 linear quantizing in the K loop (x_lds = 0: each wave
     quantizes the 1x128 groups it loads): every instance (tile_n x waves_k x
-    unroll x swap_ab x layout) with whole tiles, split-K and stream-K, at
+    swap_ab x layout) with whole tiles, split-K and stream-K, at
     M = 17 (two row blocks) and M = 3, bit-identical to the two-launch path
     with the same config, and within the bar of the oracle."""
     fmt, N, K = "Block_FP8", 200, 1280
     cs = case(fmt, M, N, K)
     n = 0
-    for tn, wk, u, swap, (s, grid), packed in itertools.product(
-            (16, 32, 64), (1, 2, 4, 8), (1, 2), (0, 1), ((1, 0), (4, 0), (1, 3)), (False, True)):
-        if (tn // 16) * u > 4:
-            continue
-        cfg = w8.Config.make(tile_n=tn, waves_k=wk, waves_n=1, unroll=u, split_k=s, grid=grid,
+    for tn, wk, swap, (s, grid), packed in itertools.product(
+            (16, 32), (2, 4, 8), (0, 1), ((1, 0), (4, 0), (1, 3)), (False, True)):
+        cfg = w8.Config.make(tile_n=tn, waves_k=wk, waves_n=1, unroll=1, split_k=s, grid=grid,
                              swap_ab=swap, x_lds=0)
         y1 = fused(w8, cs, cfg, packed)
         y2 = two_launch(w8, cs, cfg, packed)
         torch.cuda.synchronize()
-        assert same_bits(y1, y2), f"{cfg} packed={packed}: K-loop quantization != two-launch"
+        assert same_bits(y1, y2), f"{fmt} {cfg} packed={packed}: K-loop != two-launch"
         n += 1
-    assert n == 5 * 4 * 2 * 3 * 2
-    assert_bf16_close(y1, cs.Y, f"K-loop fused M={M}")
+    assert n == 2 * 3 * 2 * 3 * 2
+    assert_bf16_close(y1, cs.Y, f"K-loop fused {fmt} M={M}")
 
 
 def test_block_fp8_k_loop_large_and_extreme(w8):
@@ -295,7 +295,7 @@ def test_block_fp8_k_loop_large_and_extreme(w8):
     for M in (1, 8, 32):
         cs = case(fmt, M, 4608, 7168)
         for cfg in (w8.Config.make(tile_n=16, waves_k=4, unroll=1, split_k=1),
-                    w8.Config.make(tile_n=32, waves_k=2, unroll=2, split_k=4, swap_ab=1)):
+                    w8.Config.make(tile_n=32, waves_k=2, unroll=1, split_k=4, swap_ab=1)):
             y1 = fused(w8, cs, cfg, True)
             y2 = two_launch(w8, cs, cfg, True)
             torch.cuda.synchronize()
