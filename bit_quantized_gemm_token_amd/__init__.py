@@ -35,7 +35,7 @@ __all__ = ["Config", "W8Error", "UnsupportedShape", "Workspace", "PackedWeight",
            "config_table_size", "config_table_foreign", "tune_shape", "rank_configs",
            "profile_configs", "model_config", "moe_gemm", "moe_config", "moe_tune",
            "moe_workspace_size", "moe_linear", "moe_linear_config",
-           "pack_experts", "PackedExperts", "FORMATS", "MAX_M",
+           "pack_experts", "PackedExperts", "read_floor", "FORMATS", "MAX_M",
            "MAX_SPLIT_K", "GROUP", "ABI_VERSION"]
 
 
@@ -106,6 +106,30 @@ def _codes_dtype(fmt):
     return torch.int8 if _fmt(fmt) == FORMATS["W8A8_INT8"] else torch.float8_e4m3fn
 
 
+def _act_scales(f, M, K):
+    """Element count of the activation scales: [M] or, Block_FP8, [M, K/128]."""
+    return M * (K // GROUP) if f == FORMATS["Block_FP8"] else M
+
+
+def _weight_scales(f, N, K):
+    """Element count of the weight scales: [N] or, Block_FP8, [ceil(N/128), ceil(K/128)]."""
+    if f == FORMATS["Block_FP8"]:
+        return ((N + GROUP - 1) // GROUP) * ((K + GROUP - 1) // GROUP)
+    return N
+
+
+def _check_scales(t, n, name):
+    """The kernels read n contiguous fp32 scales from t's first element."""
+    if not t.is_contiguous() or t.numel() != n:
+        raise ValueError(f"{name} must be a contiguous tensor of {n} elements, got shape "
+                         f"{tuple(t.shape)}")
+
+
+def _check_out(t, M, N, name):
+    if t.dim() != 2 or t.shape[0] != M or t.shape[1] != N:
+        raise ValueError(f"{name} must be [{M}, {N}], got {tuple(t.shape)}")
+
+
 # ----------------------------------------------------------------- quantize --
 def quantize_act(fmt, x, xq=None, sx=None, stream=None):
     """Dynamic activation quantization of bf16 x [M, K] on the GPU.
@@ -121,6 +145,10 @@ def quantize_act(fmt, x, xq=None, sx=None, stream=None):
     if sx is None:
         shape = (M, K // GROUP) if f == FORMATS["Block_FP8"] else (M,)
         sx = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _check_out(xq, M, K, "xq")
+    if xq.element_size() != 1:
+        raise TypeError("xq must hold 1-byte codes")
+    _check_scales(sx, _act_scales(f, M, K), "sx")
     ldq = _row_major(xq, "xq")
     _check(_lib.w8_quantize_act(f, M, K, _dev_ptr(x, "x", torch.bfloat16), ldx,
                                 _dev_ptr(xq, "xq"), ldq * xq.element_size(),
@@ -189,41 +217,71 @@ def workspace_size(fmt, M, N, K, cfg=None, packed=False, op="gemm"):
 
 
 class Workspace:
-    """Device workspace for split-K, zero-filled once when (re)allocated.
+    """Device workspace for split-K and the linear op's quantize launch.
 
-    The GEMM leaves its counters at zero after each call, so one Workspace can
-    serve any sequence of calls on one stream (not concurrent calls).
+    Zero-filled when (re)allocated; the GEMM leaves its counters at zero after
+    each call, so one Workspace can serve any sequence of calls on one stream
+    (calls that overlap on several streams race).
+
+    Under HIP graph capture the workspace cannot grow: the fill would be
+    recorded into the graph and a buffer given back to the allocator could
+    be handed out again while the graph still writes to it.  Size it
+    beforehand (Workspace(device, nbytes), or call reserve() before the
+    capture).  A buffer that a larger one replaces is kept alive for the
+    Workspace's lifetime, because a graph captured earlier may still use it;
+    release_retired() drops those once no such graph remains.
     """
 
     def __init__(self, device=None, nbytes=0):
         self.device = torch.device(device or "cuda")
         self.buf = None
+        self._retired = []
         if nbytes:
             self.reserve(nbytes)
 
-    def reserve(self, nbytes):
-        if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
+    def reserve(self, nbytes, stream=None):
+        """The buffer, grown to at least nbytes (zero-filled on `stream`,
+        default the current stream, before any later work on it)."""
+        if self.buf is not None and self.buf.numel() >= nbytes:
+            return self.buf
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError(
+                f"the workspace would grow to {int(nbytes)} bytes during graph capture; "
+                f"size it before capturing (Workspace(device, nbytes) or reserve())")
+        if self.buf is not None:
+            self._retired.append(self.buf)
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        if not isinstance(s, torch.cuda.Stream):
+            s = torch.cuda.ExternalStream(int(s), device=self.device)
+        with torch.cuda.stream(s):
+            buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
+            buf.zero_()
+        self.buf = buf
         return self.buf
 
-    def for_call(self, fmt, M, N, K, cfg=None, packed=False, op="gemm"):
+    def release_retired(self):
+        """Drops the buffers that larger ones replaced (call only when no
+        captured graph that used them will be replayed)."""
+        self._retired.clear()
+
+    def for_call(self, fmt, M, N, K, cfg=None, packed=False, op="gemm", stream=None):
         need = workspace_size(fmt, M, N, K, cfg, packed, op)
         if need == 0:
             return None, 0
-        buf = self.reserve(need)
+        buf = self.reserve(need, stream)
         return ctypes.c_void_p(buf.data_ptr()), buf.numel()
 
 
 def _weights(f, wq):
-    """(N, K, ldw, pointer, packed) of row-major codes or a PackedWeight."""
+    """(N, K, ldw, device tensor, packed) of row-major codes or a PackedWeight."""
     if isinstance(wq, PackedWeight):
         if wq.fmt != f:
             raise ValueError("packed weights were packed for another format")
-        return wq.N, wq.K, 0, _dev_ptr(wq.data, "wq"), True
+        return wq.N, wq.K, 0, wq.data, True
     if wq.element_size() != 1:
         raise TypeError("wq must hold 1-byte codes")
     N, wk = wq.shape
-    return N, wk, _row_major(wq, "wq") * wq.element_size(), _dev_ptr(wq, "wq"), False
+    return N, wk, _row_major(wq, "wq") * wq.element_size(), wq, False
 
 
 def _gemm(entry, fmt, xq, sx, wq, sw, out, cfg, workspace, stream):
@@ -236,11 +294,14 @@ def _gemm(entry, fmt, xq, sx, wq, sw, out, cfg, workspace, stream):
         raise ValueError(f"K mismatch: xq {tuple(xq.shape)} vs weights {(N, wk)}")
     if xq.element_size() != 1:
         raise TypeError("xq must hold 1-byte codes")
+    _check_scales(sx, _act_scales(f, M, K), "sx")
+    _check_scales(sw, _weight_scales(f, N, K), "sw")
+    _check_out(out, M, N, "out")
     if workspace is None:
         workspace = _default_workspace(xq.device)
-    ws_ptr, ws_bytes = workspace.for_call(f, M, N, K, cfg, packed, "gemm")
+    ws_ptr, ws_bytes = workspace.for_call(f, M, N, K, cfg, packed, "gemm", stream)
     _check(entry(f, M, N, K, _dev_ptr(xq, "xq"), ldq, _dev_ptr(sx, "sx", torch.float32),
-                 wptr, ldw, _dev_ptr(sw, "sw", torch.float32),
+                 _dev_ptr(wptr, "wq"), ldw, _dev_ptr(sw, "sw", torch.float32),
                  _dev_ptr(out, "out"), ldo, _cfg_ptr(cfg), ws_ptr, ws_bytes,
                  _stream(stream, xq.device)))
     return out
@@ -306,10 +367,12 @@ def linear(fmt, x, wq, sw, cfg=None, y=None, workspace=None, stream=None, fused=
         y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     elif y.dtype != torch.bfloat16:
         raise TypeError("y must be bfloat16")
+    _check_out(y, M, N, "y")
+    _check_scales(sw, _weight_scales(f, N, K), "sw")
     if workspace is None:
         workspace = _default_workspace(x.device)
-    ws_ptr, ws_bytes = workspace.for_call(f, M, N, K, cfg, packed, "linear")
-    _check(_lib.w8_linear(f, M, N, K, _dev_ptr(x, "x"), ldx, wptr, ldw,
+    ws_ptr, ws_bytes = workspace.for_call(f, M, N, K, cfg, packed, "linear", stream)
+    _check(_lib.w8_linear(f, M, N, K, _dev_ptr(x, "x"), ldx, _dev_ptr(wptr, "wq"), ldw,
                           _dev_ptr(sw, "sw", torch.float32), _dev_ptr(y, "y"), _row_major(y, "y"),
                           _cfg_ptr(cfg), ws_ptr, ws_bytes, _stream(stream, x.device)))
     return y
@@ -409,8 +472,9 @@ def moe_gemm(fmt, xq, sx, offsets, rows, wq, sw, max_m=32, cfg=None, y=None, wor
         raise ValueError(f"K mismatch: xq {tuple(xq.shape)} vs experts' K {wk}")
     if offsets.numel() != E + 1:
         raise ValueError("offsets must hold E + 1 entries")
-    if sw.shape[0] != E or not sw.is_contiguous():
-        raise ValueError("sw must be a contiguous [E, ...] tensor")
+    if sw.shape[0] != E or not sw.is_contiguous() or sw.numel() != E * _weight_scales(f, N, K):
+        raise ValueError(f"sw must be a contiguous [E, {_weight_scales(f, N, K)}] tensor")
+    _check_scales(sx, _act_scales(f, T, K), "sx")
     if y is None:
         y = torch.empty((rows.numel(), N), dtype=torch.bfloat16, device=xq.device)
     elif y.dtype != torch.bfloat16:
@@ -422,7 +486,7 @@ def moe_gemm(fmt, xq, sx, offsets, rows, wq, sw, max_m=32, cfg=None, y=None, wor
     need = moe_workspace_size(f, E, T, N, K, max_m, cfg, packed)
     ws_ptr, ws_bytes = (None, 0)
     if need:
-        buf = workspace.reserve(need)
+        buf = workspace.reserve(need, stream)
         ws_ptr, ws_bytes = ctypes.c_void_p(buf.data_ptr()), buf.numel()
     _check(_lib.w8_moe_gemm(f, E, T, N, K, max_m, _dev_ptr(xq, "xq"), ldq,
                             _dev_ptr(sx, "sx", torch.float32),
@@ -452,8 +516,8 @@ def moe_linear(fmt, x, offsets, rows, wq, sw, max_m=32, cfg=None, y=None, worksp
         raise ValueError(f"K mismatch: x {tuple(x.shape)} vs experts' K {wk}")
     if offsets.numel() != E + 1:
         raise ValueError("offsets must hold E + 1 entries")
-    if sw.shape[0] != E or not sw.is_contiguous():
-        raise ValueError("sw must be a contiguous [E, ...] tensor")
+    if sw.shape[0] != E or not sw.is_contiguous() or sw.numel() != E * _weight_scales(f, N, K):
+        raise ValueError(f"sw must be a contiguous [E, {_weight_scales(f, N, K)}] tensor")
     if y is None:
         y = torch.empty((rows.numel(), N), dtype=torch.bfloat16, device=x.device)
     elif y.dtype != torch.bfloat16:
@@ -467,7 +531,7 @@ def moe_linear(fmt, x, offsets, rows, wq, sw, max_m=32, cfg=None, y=None, worksp
     need = moe_workspace_size(f, E, T, N, K, max_m, cfg, packed)
     ws_ptr, ws_bytes = (None, 0)
     if need:
-        buf = workspace.reserve(need)
+        buf = workspace.reserve(need, stream)
         ws_ptr, ws_bytes = ctypes.c_void_p(buf.data_ptr()), buf.numel()
     _check(_lib.w8_moe_linear(f, E, T, N, K, max_m, _dev_ptr(x, "x"), ldx,
                               _dev_ptr(offsets, "offsets", torch.int32),
@@ -580,6 +644,10 @@ def _tune_opts(warmup=2, replays=5, bank2_top=5, rotate_bytes=512 << 20,
     o.stream_k = int(bool(stream_k))
     o.op = _op(op)
     o.top_n = int(top_n)
+    # the caller's current stream: the tuners refuse to run while it is being
+    # captured into a graph
+    if torch.cuda.is_available():
+        o.stream = torch.cuda.current_stream().cuda_stream
     return o
 
 
@@ -638,3 +706,15 @@ def algorithmic_bytes(fmt, M, N, K):
 
 
 load_default_table()
+
+
+# -------------------------------------------------------------- measurement --
+def read_floor(src, nbytes, sink, grid=512, waves=4, depth=4, stream=None):
+    """One launch of the read-floor kernel: streams nbytes (a multiple of
+    1024) of the device tensor src once, writing grid * waves words to the
+    uint32/int32 device tensor sink.  Measurement only (w8_read_floor)."""
+    if src.numel() * src.element_size() < nbytes:
+        raise ValueError("src holds fewer than nbytes bytes")
+    _check(_lib.w8_read_floor(_dev_ptr(src, "src"), nbytes, _dev_ptr(sink, "sink"),
+                              sink.numel() * sink.element_size(), grid, waves, depth,
+                              _stream(stream, src.device)))
