@@ -27,16 +27,16 @@ int wk_index(int wk) {
 int wn_index(int wn) { return wn == 1 ? 0 : wn == 2 ? 1 : wn == 4 ? 2 : wn == 8 ? 3 : -1; }
 int u_index(int u) { return u == 1 ? 0 : u == 2 ? 1 : u == 4 ? 2 : -1; }
 
-// [fmt][mb-1][nb][wk][wn][unroll][swap][packed][xl] -> launcher
+// [fmt][mb-1][nb][wk][wn][unroll][swap][packed][xl][sk] -> launcher
 struct InstanceIndex {
-  GemmLaunchFn fn[3][2][3][5][4][3][2][2][4] = {};
+  GemmLaunchFn fn[3][2][3][5][4][3][2][2][4][2] = {};
   InstanceIndex() {
     int n = 0;
     const GemmInstance* p = gemm_instances(&n);
     for (int i = 0; i < n; ++i) {
       const GemmInstance& g = p[i];
       fn[g.fmt][g.mb - 1][nb_index(g.nb)][wk_index(g.wk)][wn_index(g.wn)][u_index(g.unroll)]
-        [g.swap][g.packed][g.xl] = g.fn;
+        [g.swap][g.packed][g.xl][g.sk] = g.fn;
     }
   }
 };
@@ -136,6 +136,9 @@ w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c) {
   if (c.grid < 0) return fail(W8_E_INVALID, "cfg.grid must be >= 0");
   if (c.grid > 0) {
     if (c.split_k != 1) return fail(W8_E_INVALID, "cfg: stream-K (grid > 0) needs split_k == 1");
+    if (c.tile_n != 16 || c.unroll > 2)
+      return fail(W8_E_INVALID, "cfg: stream-K (grid > 0) is compiled for tile_n 16 with "
+                                "unroll 1 or 2 only");
     if (c.grid > iters)
       return fail(W8_E_INVALID, "cfg.grid " + std::to_string(c.grid) +
                                     " exceeds the (tile, K-step) iterations (" +
@@ -256,7 +259,7 @@ w8_status launch_gemm_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
   GemmLaunchFn fn =
       instance_index().fn[g.fmt][mb - 1][nb_index(nb)][wk_index(c.waves_k)][wn_index(c.waves_n)]
                          [u_index(c.unroll)][c.swap_ab][g.packed ? 1 : 0]
-                         [g.x ? (c.x_lds ? 2 : 3) : c.x_lds];
+                         [g.x ? (c.x_lds ? 2 : 3) : c.x_lds][c.grid > 0 ? 1 : 0];
   if (!fn) return fail(W8_E_INVALID, "no compiled kernel for this config");
   const int ntiles = tiles_of(g.N, c);
   GemmArgs a;

@@ -16,11 +16,13 @@
 //          the 8 XCDs, each with its own L2, so with split_k a power of two
 //          an XCD sees only split_k/8 K ranges (split_k >= 8) or one (split_k
 //          < 8), and fetches only those activation columns instead of all K.
-//          grid > 0 (stream-K): exactly `grid` workgroups share the ntiles x
-//          ksteps (tile, K-step) iterations in equal contiguous ranges, so the
-//          weight stream is spread evenly over the compute units whatever the
-//          tile count; a tile split between workgroups is summed like a
-//          split-K tile.
+//          grid > 0 (stream-K, instances compiled with SK = 1): exactly
+//          `grid` workgroups share the ntiles x ksteps (tile, K-step)
+//          iterations in equal contiguous ranges, so the weight stream is
+//          spread evenly over the compute units whatever the tile count; a
+//          tile split between workgroups is summed like a split-K tile.  The
+//          split-K instances (SK = 0) carry none of its code: its loop and
+//          64-bit range arithmetic would cost the common path registers.
 //   K loop one MFMA per K-step, row block and 16-row block of M (64 bytes of K
 //          for int8, 128 for E4M3FN); each lane streams its weight bytes
 //          straight from HBM into MFMA operand registers with 16-byte loads
@@ -152,7 +154,7 @@ __device__ __forceinline__ typename Traits<FMT>::Acc mma(typename Traits<FMT>::F
 // row m of this call is row xrows[m] (clamped to [0, xrow_max]) of the
 // activation codes and scales (XL == 2: of the bf16 activations); everything
 // else is per call in `a`.
-template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL,
+template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL, int SK,
           bool GROUPED>
 __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xrows,
                                           int xrow_max) {
@@ -203,8 +205,8 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
                 16 * g;
 
   // Block_FP8 sx rows of the accumulator elements this lane holds (SWAP: one
-  // m per lane; else four), and the per-token formats' epilogue sx, loaded
-  // now so their latency hides under the K loop.
+  // m per lane; else four); the per-token formats' epilogue sx are loaded in
+  // the segment, after its first weight stages (see there).
   constexpr int SXN = SWAP ? 1 : 4;
   const int nthreads = 64 * WK * WN;
   __shared__ Acc red[WK > 1 ? (WK - 1) * MB * NB * 64 : 1];
@@ -235,7 +237,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
         ep_sx[b][i] = 0.0f;
       } else {
         sxrow[b][i] = nullptr;
-        ep_sx[b][i] = XL == 2 ? 0.0f : a.sx[xr(m)];  // XL == 2: set once the row scales exist
+        ep_sx[b][i] = 0.0f;  // loaded in the segment, or (XL == 2) computed by the row pass
       }
     }
 
@@ -304,15 +306,25 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
     // straddle two blocks); the per-token formats' epilogue sw.
     const float* swrow = nullptr;
     float ep_sw[NB][4 / SXN];
-    if constexpr (BLOCK) {
-      swrow = a.sw + (long long)(min(n0, a.N - 1) / kGroup) * a.sgroups;
-    } else {
+    if constexpr (BLOCK) swrow = a.sw + (long long)(min(n0, a.N - 1) / kGroup) * a.sgroups;
+    // The per-token formats' epilogue scales, issued after the first weight
+    // stages: vector-memory loads complete in issue order, so a scale load
+    // issued first would hold up the first MFMA behind its own latency.
+    auto load_epilogue_scales = [&]() {
+      if constexpr (!BLOCK) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int i = 0; i < 4 / SXN; ++i)
-          ep_sw[j][i] = a.sw[min(SWAP ? n0 + 16 * j + 4 * g + i : n0 + 16 * j + r, a.N - 1)];
-    }
+          for (int i = 0; i < 4 / SXN; ++i)
+            ep_sw[j][i] = a.sw[min(SWAP ? n0 + 16 * j + 4 * g + i : n0 + 16 * j + r, a.N - 1)];
+        if constexpr (XL != 2) {
+#pragma unroll
+          for (int b = 0; b < MB; ++b)
+#pragma unroll
+            for (int i = 0; i < SXN; ++i) ep_sx[b][i] = a.sx[xr(sxm[b][i])];
+        }
+      }
+    };
 
     // K-steps of this wave: its WK-th of the segment.
     const int la = ka + (kb - ka) * wk / WK;
@@ -475,6 +487,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
     Stage A, B;
     if (ns > 0) load_stage(A, k0);
     if (ns > 1) load_stage(B, k0 + U);
+    load_epilogue_scales();
     // XL == 2: quantize the segment's activations into the LDS stage.  The
     // raw bf16 slice is fetched while the first weight stages are in flight
     // (and, for the per-token formats, together with the row pass), so one
@@ -630,9 +643,11 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
     // acknowledged before the workgroup counts itself in; the last workgroup
     // to arrive reads the partials with agent-scope atomic loads, which are
     // served from the device-coherent level, so it sees every slot's data.
-    // Partial layout: fragment f = ((tile*slots + slot)*WN*NB + wn*NB + j)*MB
-    // + b holds 4 x 64 words, word (f*4 + i)*64 + lane, so each of the four
-    // stores of a wave writes 256 contiguous bytes.
+    // (An agent-scope release on the count and acquire in the last arriver
+    // would write back and invalidate whole L2s: measured 1.5 to 9 us more
+    // per launch.)  Partial layout: fragment f = ((tile*slots + slot)*WN*NB +
+    // wn*NB + j)*MB + b holds 4 x 64 words, word (f*4 + i)*64 + lane, so each
+    // of the four stores of a wave writes 256 contiguous bytes.
     bool store = true;
     if (count > 1) {
       typedef decltype(acc[0][0][0]) Elem;
@@ -650,7 +665,13 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
                   part + (((f0 + (long long)slot * WN * NB + j) * MB + b) * 4 + i) * 64 + lane,
                   acc[b][j][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      // The compiler may not move memory operations across the wait (the
+      // signal fences); the hardware keeps the order: s_waitcnt vmcnt(0)
+      // returns only when every store above has been acknowledged by the
+      // level it was written through to, and the count is issued after it.
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_waitcnt(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __syncthreads();
       if (threadIdx.x == 0) {
         const unsigned prev = __hip_atomic_fetch_add(&a.counters[tile * kCounterWords], 1u,
@@ -659,6 +680,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
       }
       __syncthreads();
       store = is_last;
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the partial loads stay after the count
       if (store) {
         if (wk == 0) {
 #pragma unroll
@@ -739,7 +761,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
         }
   };
 
-  if (a.grid == 0) {
+  if constexpr (!SK) {
     // One workgroup per (tile, split); the split index varies fastest.
     const int split = (int)(blockIdx.x & (unsigned)(a.split_k - 1));
     const int tile = (int)(blockIdx.x >> a.split_shift);
@@ -772,9 +794,9 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
   }
 }
 
-template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL>
+template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL, int SK>
 __global__ __launch_bounds__(64 * WK * WN) void gemm_kernel(GemmArgs a) {
-  gemm_body<FMT, MB, NB, WK, WN, U, SWAP, PACKED, XL, false>(a, nullptr, 0);
+  gemm_body<FMT, MB, NB, WK, WN, U, SWAP, PACKED, XL, SK, false>(a, nullptr, 0);
 }
 
 // An expert's entry count with its offsets clamped to the row list (so bad
@@ -816,7 +838,7 @@ __device__ __forceinline__ int moe_active_expert(const MoeArgs& m, int slot) {
 // offsets[e+1]) of the routing (at most 16 * MB of them are computed), its
 // weights, weight scales and shared-tile workspace are at the expert's
 // strides, and its outputs are rows offsets[e].. of Y.
-template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL>
+template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL, int SK>
 __global__ __launch_bounds__(64 * WK * WN) void moe_gemm_kernel(GemmArgs a, MoeArgs m) {
   int e = blockIdx.y;
   if (m.compact) {
@@ -834,20 +856,21 @@ __global__ __launch_bounds__(64 * WK * WN) void moe_gemm_kernel(GemmArgs a, MoeA
     a.counters += (long long)e * a.ntiles * kCounterWords;
     a.part = static_cast<char*>(a.part) + e * m.part_stride;
   }
-  gemm_body<FMT, MB, NB, WK, WN, U, SWAP, PACKED, XL, true>(a, m.rows + off, m.xrow_max);
+  gemm_body<FMT, MB, NB, WK, WN, U, SWAP, PACKED, XL, SK, true>(a, m.rows + off, m.xrow_max);
 }
 
-template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL>
+template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL, int SK>
 hipError_t launch_gemm(const GemmArgs& a, dim3 grid, dim3 block, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, WK, WN, U, SWAP, PACKED, XL>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<FMT, MB, NB, WK, WN, U, SWAP, PACKED, XL, SK>), grid, block, 0, s,
+                     a);
   return hipGetLastError();
 }
 
-template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL>
+template <int FMT, int MB, int NB, int WK, int WN, int U, int SWAP, int PACKED, int XL, int SK>
 hipError_t launch_moe_gemm(const GemmArgs& a, const MoeArgs& m, dim3 grid, dim3 block,
                            hipStream_t s) {
-  hipLaunchKernelGGL((moe_gemm_kernel<FMT, MB, NB, WK, WN, U, SWAP, PACKED, XL>), grid, block, 0,
-                     s, a, m);
+  hipLaunchKernelGGL((moe_gemm_kernel<FMT, MB, NB, WK, WN, U, SWAP, PACKED, XL, SK>), grid, block,
+                     0, s, a, m);
   return hipGetLastError();
 }
 

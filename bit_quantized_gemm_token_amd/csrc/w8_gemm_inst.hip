@@ -20,17 +20,22 @@
 #define W8_CAT(a, b, c, d) W8_CAT2(a, b, c, d)
 #define W8_MB (W8_PART % 2 + 1)
 
-// One entry per (MB, NB, WK, WN, UNROLL, PACKED, XL): MB in {1, 2}; (NB,
+// One entry per (MB, NB, WK, WN, UNROLL, PACKED, XL, SK): MB in {1, 2}; (NB,
 // UNROLL) with NB * UNROLL <= 4 (the weight registers of one stage);
 // (WK, WN, XL) in {(1..16, 1, 0), (1..8, 1, 1), (1, 2..8, 1), (1..4, 1, 2),
-// (1, 2..8, 2)} (XL 2: fused quantization); PACKED in {0, 1}.
-#define W8_I(MB, NB, WK, WN, U, P, XL)                                       \
-  {W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL,                                 \
-   &launch_gemm<W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL>},
-#define W8_P(MB, NB, WK, WN, U, XL) W8_I(MB, NB, WK, WN, U, 0, XL) W8_I(MB, NB, WK, WN, U, 1, XL)
-#define W8_U(MB, WK, WN, XL)                                                           \
-  W8_P(MB, 1, WK, WN, 1, XL) W8_P(MB, 1, WK, WN, 2, XL) W8_P(MB, 1, WK, WN, 4, XL)    \
-  W8_P(MB, 2, WK, WN, 1, XL) W8_P(MB, 2, WK, WN, 2, XL) W8_P(MB, 4, WK, WN, 1, XL)
+// (1, 2..8, 2)} (XL 2: fused quantization); PACKED in {0, 1}; SK 0 (one
+// workgroup per tile and split) for all of them, SK 1 (stream-K) for NB 1
+// with UNROLL 1 or 2 (stream-K never won a tuning, so only the narrowest
+// tiles carry it).
+#define W8_I(MB, NB, WK, WN, U, P, XL, SK)                                   \
+  {W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL, SK,                             \
+   &launch_gemm<W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL, SK>},
+#define W8_P(MB, NB, WK, WN, U, XL, SK) \
+  W8_I(MB, NB, WK, WN, U, 0, XL, SK) W8_I(MB, NB, WK, WN, U, 1, XL, SK)
+#define W8_U(MB, WK, WN, XL)                                                                    \
+  W8_P(MB, 1, WK, WN, 1, XL, 0) W8_P(MB, 1, WK, WN, 2, XL, 0) W8_P(MB, 1, WK, WN, 4, XL, 0)    \
+  W8_P(MB, 2, WK, WN, 1, XL, 0) W8_P(MB, 2, WK, WN, 2, XL, 0) W8_P(MB, 4, WK, WN, 1, XL, 0)    \
+  W8_P(MB, 1, WK, WN, 1, XL, 1) W8_P(MB, 1, WK, WN, 2, XL, 1)
 #define W8_W(MB)                                                                       \
   W8_U(MB, 1, 1, 0) W8_U(MB, 2, 1, 0) W8_U(MB, 4, 1, 0) W8_U(MB, 8, 1, 0)             \
   W8_U(MB, 16, 1, 0) W8_U(MB, 1, 1, 1) W8_U(MB, 2, 1, 1) W8_U(MB, 4, 1, 1)            \
@@ -42,21 +47,23 @@
 // 8}, tile_n 16 or 32, UNROLL 1 (the shapes it wins on; the bf16
 // activations of a stage double its activation registers).  Parts 4 and 5
 // hold them (Block_FP8 only).
-#define W8_U3(MB, WK) W8_P(MB, 1, WK, 1, 1, 3) W8_P(MB, 2, WK, 1, 1, 3)
+#define W8_U3(MB, WK) W8_P(MB, 1, WK, 1, 1, 3, 0) W8_P(MB, 2, WK, 1, 1, 3, 0) W8_P(MB, 1, WK, 1, 1, 3, 1)
 #define W8_W3(MB) W8_U3(MB, 2) W8_U3(MB, 4) W8_U3(MB, 8)
 
-// The MoE grouped GEMM: the same (MB, NB, UNROLL, PACKED) and (WK, WN, XL) in
-// {(1, 1, 0), (2, 1, 0), (4, 1, 0), (8, 1, 0), (1, 2, 1), (1, 4, 1), (1, 8, 1)}
-// on quantized activations, and with fused quantization (XL 2) in
+// The MoE grouped GEMM: the same (MB, NB, UNROLL, PACKED, SK) and (WK, WN, XL)
+// in {(1, 1, 0), (2, 1, 0), (4, 1, 0), (8, 1, 0), (1, 2, 1), (1, 4, 1),
+// (1, 8, 1)} on quantized activations, and with fused quantization (XL 2) in
 // {(1, 4, 2), (1, 8, 2)} (the only fused shapes that ever beat a quantize
 // launch + the unfused kernel on the MoE layers measured).
-#define W8_MI(MB, NB, WK, WN, U, P, XL)                                      \
-  {W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL,                                 \
-   &launch_moe_gemm<W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL>},
-#define W8_MP(MB, NB, WK, WN, U, XL) W8_MI(MB, NB, WK, WN, U, 0, XL) W8_MI(MB, NB, WK, WN, U, 1, XL)
-#define W8_MU(MB, WK, WN, XL)                                                          \
-  W8_MP(MB, 1, WK, WN, 1, XL) W8_MP(MB, 1, WK, WN, 2, XL) W8_MP(MB, 1, WK, WN, 4, XL) \
-  W8_MP(MB, 2, WK, WN, 1, XL) W8_MP(MB, 2, WK, WN, 2, XL) W8_MP(MB, 4, WK, WN, 1, XL)
+#define W8_MI(MB, NB, WK, WN, U, P, XL, SK)                                  \
+  {W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL, SK,                             \
+   &launch_moe_gemm<W8_FMT, MB, NB, WK, WN, U, W8_SWAP, P, XL, SK>},
+#define W8_MP(MB, NB, WK, WN, U, XL, SK) \
+  W8_MI(MB, NB, WK, WN, U, 0, XL, SK) W8_MI(MB, NB, WK, WN, U, 1, XL, SK)
+#define W8_MU(MB, WK, WN, XL)                                                                      \
+  W8_MP(MB, 1, WK, WN, 1, XL, 0) W8_MP(MB, 1, WK, WN, 2, XL, 0) W8_MP(MB, 1, WK, WN, 4, XL, 0)    \
+  W8_MP(MB, 2, WK, WN, 1, XL, 0) W8_MP(MB, 2, WK, WN, 2, XL, 0) W8_MP(MB, 4, WK, WN, 1, XL, 0)    \
+  W8_MP(MB, 1, WK, WN, 1, XL, 1) W8_MP(MB, 1, WK, WN, 2, XL, 1)
 #define W8_MW(MB)                                                                      \
   W8_MU(MB, 1, 1, 0) W8_MU(MB, 2, 1, 0) W8_MU(MB, 4, 1, 0) W8_MU(MB, 8, 1, 0)         \
   W8_MU(MB, 1, 2, 1) W8_MU(MB, 1, 4, 1) W8_MU(MB, 1, 8, 1)                            \

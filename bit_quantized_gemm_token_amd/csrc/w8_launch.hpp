@@ -58,6 +58,7 @@ typedef hipError_t (*GemmLaunchFn)(const GemmArgs&, dim3 grid, dim3 block, hipSt
 
 struct GemmInstance {
   int fmt, mb, nb, wk, wn, unroll, swap, packed, xl;
+  int sk;  // 1: the stream-K variant (cfg.grid > 0)
   GemmLaunchFn fn;
 };
 
@@ -83,6 +84,7 @@ typedef hipError_t (*MoeLaunchFn)(const GemmArgs&, const MoeArgs&, dim3 grid, di
 
 struct MoeInstance {
   int fmt, mb, nb, wk, wn, unroll, swap, packed, xl;
+  int sk;  // 1: the stream-K variant (cfg.grid > 0)
   MoeLaunchFn fn;
 };
 

@@ -22,14 +22,14 @@ int wn_index(int wn) { return wn == 1 ? 0 : wn == 2 ? 1 : wn == 4 ? 2 : wn == 8 
 int u_index(int u) { return u == 1 ? 0 : u == 2 ? 1 : u == 4 ? 2 : -1; }
 
 struct MoeIndex {
-  MoeLaunchFn fn[3][2][3][5][4][3][2][2][3] = {};
+  MoeLaunchFn fn[3][2][3][5][4][3][2][2][3][2] = {};
   MoeIndex() {
     int n = 0;
     const MoeInstance* p = moe_instances(&n);
     for (int i = 0; i < n; ++i) {
       const MoeInstance& g = p[i];
       fn[g.fmt][g.mb - 1][nb_index(g.nb)][wk_index(g.wk)][wn_index(g.wn)][u_index(g.unroll)]
-        [g.swap][g.packed][g.xl] = g.fn;
+        [g.swap][g.packed][g.xl][g.sk] = g.fn;
     }
   }
 };
@@ -45,7 +45,7 @@ MoeLaunchFn moe_fn(int fmt, int max_m, int packed, const w8_cfg& c, bool in_kern
   if (c.x_lds > 1 || (in_kernel && !c.x_lds)) return nullptr;
   return moe_index().fn[fmt][(max_m + 15) / 16 - 1][nb_index(c.tile_n / 16)][wk_index(c.waves_k)]
                        [wn_index(c.waves_n)][u_index(c.unroll)][c.swap_ab][packed]
-                       [in_kernel ? 2 : c.x_lds];
+                       [in_kernel ? 2 : c.x_lds][c.grid > 0 ? 1 : 0];
 }
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }

@@ -134,8 +134,9 @@ WAVE_SHAPES = ((1, 1, 0), (2, 1, 0), (4, 1, 0), (8, 1, 0), (16, 1, 0), (1, 1, 1)
 def test_every_tile_config(w8, fmt):
     """Every (tile_n, waves_k x waves_n, x_lds, unroll, swap_ab, layout)
     instance at one ragged shape (M = 17 needs both 16-row blocks of M),
-    whole tiles, split-K and stream-K (3 and 7 workgroups: several tiles and
-    partial tiles per workgroup)."""
+    whole tiles and split-K; the stream-K instances (tile_n 16, unroll 1 or
+    2) with grids of 3 and 7 workgroups (several tiles and partial tiles per
+    workgroup)."""
     M, N, K = (17, 200, 1280)
     cs = case(fmt, M, N, K)
     xq, sx = cs.gpu_act()
@@ -143,13 +144,13 @@ def test_every_tile_config(w8, fmt):
     for tn, (wk, wn, xl), u, swap, (s, grid), packed in itertools.product(
             (16, 32, 64), WAVE_SHAPES, (1, 2, 4), (0, 1), ((1, 0), (4, 0), (1, 3), (1, 7)),
             (0, 1)):
-        if (tn // 16) * u > 4:
+        if (tn // 16) * u > 4 or (grid and (tn != 16 or u > 2)):
             continue
         cfg = C(w8, tile_n=tn, waves_k=wk, waves_n=wn, unroll=u, split_k=s, grid=grid,
                 swap_ab=swap, x_lds=xl)
         acc_check(w8, cs, xq, sx, cfg, f"{fmt} {cfg} packed={packed}", bool(packed))
         n += 1
-    assert n == 6 * 12 * 2 * 4 * 2
+    assert n == (6 * 12 * 2 * 2 + 2 * 12 * 2 * 2) * 2
 
 
 @pytest.mark.parametrize("fmt,M", [("W8A8_INT8", 32), ("FP8_Dynamic", 16), ("Block_FP8", 1),
@@ -162,8 +163,8 @@ def test_stream_k_and_shared_activations_large(w8, fmt, M):
     cs = case(fmt, M, 4608, 7168)
     xq, sx = cs.gpu_act()
     for tn, wk, wn, u, s, grid, swap, xl in (
-            (16, 1, 8, 2, 1, 256, 0, 1), (16, 1, 4, 1, 1, 512, 1, 1), (32, 2, 1, 2, 1, 1024, 0, 0),
-            (16, 1, 2, 4, 1, 1024, 1, 1), (64, 1, 8, 1, 4, 0, 0, 1), (16, 4, 1, 2, 1, 512, 1, 0),
+            (16, 1, 8, 2, 1, 256, 0, 1), (16, 1, 4, 1, 1, 512, 1, 1), (16, 2, 1, 2, 1, 1024, 0, 0),
+            (16, 1, 2, 2, 1, 1024, 1, 1), (64, 1, 8, 1, 4, 0, 0, 1), (16, 4, 1, 2, 1, 512, 1, 0),
             (16, 2, 1, 2, 4, 0, 0, 1), (32, 1, 1, 1, 8, 0, 1, 1)):
         cfg = C(w8, tile_n=tn, waves_k=wk, waves_n=wn, unroll=u, split_k=s, grid=grid,
                 swap_ab=swap, x_lds=xl)

@@ -277,7 +277,7 @@ FUSED_CFGS = (dict(tile_n=16, waves_k=1, waves_n=8, unroll=2, split_k=1, x_lds=1
               dict(tile_n=32, waves_k=1, waves_n=4, unroll=1, split_k=4, swap_ab=1, x_lds=1),
               dict(tile_n=16, waves_k=1, waves_n=8, unroll=1, split_k=2, x_lds=1),
               dict(tile_n=64, waves_k=1, waves_n=4, unroll=1, split_k=1, x_lds=1),
-              dict(tile_n=16, waves_k=1, waves_n=4, unroll=4, grid=40, x_lds=1))
+              dict(tile_n=16, waves_k=1, waves_n=4, unroll=2, grid=40, x_lds=1))
 
 
 def unfused_twin(w8, kw):
