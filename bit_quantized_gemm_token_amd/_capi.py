@@ -5,7 +5,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw8gemm.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 MAX_M = 32
 MAX_SPLIT_K = 256
 GROUP = 128
@@ -28,7 +28,7 @@ EXPORTS = ("w8_abi_version", "w8_status_string", "w8_last_error", "w8_quantize_a
            "w8_lookup_config", "w8_tune_shape", "w8_tune_default_opts", "w8_model_config",
            "w8_rank_configs", "w8_profile_configs", "w8_moe_gemm", "w8_moe_workspace_size",
            "w8_moe_validate_config", "w8_moe_config", "w8_moe_tune", "w8_moe_linear",
-           "w8_moe_linear_config")
+           "w8_moe_linear_config", "w8_read_floor")
 
 
 class Config(ctypes.Structure):
@@ -67,7 +67,7 @@ class TuneOpts(ctypes.Structure):
                 ("rotate_bytes", ctypes.c_int64), ("max_split_k", ctypes.c_int32),
                 ("insert", ctypes.c_int32), ("fail_candidate", ctypes.c_int32),
                 ("packed", ctypes.c_int32), ("stream_k", ctypes.c_int32),
-                ("op", ctypes.c_int32), ("top_n", ctypes.c_int32)]
+                ("op", ctypes.c_int32), ("top_n", ctypes.c_int32), ("stream", ctypes.c_void_p)]
 
 
 class TuneStats(ctypes.Structure):
@@ -75,7 +75,8 @@ class TuneStats(ctypes.Structure):
                 ("rejected", ctypes.c_int32), ("best_index", ctypes.c_int32),
                 ("best_us_bank1", ctypes.c_double), ("best_us_bank2", ctypes.c_double),
                 ("default_us_bank2", ctypes.c_double), ("best_gbps", ctypes.c_double),
-                ("tune_seconds", ctypes.c_double)]
+                ("tune_seconds", ctypes.c_double), ("best_us_bank2_min", ctypes.c_double),
+                ("best_us_bank2_p90", ctypes.c_double)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -91,6 +92,9 @@ def load():
     cfgp = ctypes.POINTER(Config)
     st = ctypes.c_int
     lib.w8_abi_version.restype = c_int
+    lib.w8_read_floor.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, c_int, c_int, c_int,
+                                  vp]
+    lib.w8_read_floor.restype = st
     lib.w8_status_string.argtypes = [st]
     lib.w8_status_string.restype = ctypes.c_char_p
     lib.w8_last_error.restype = ctypes.c_char_p

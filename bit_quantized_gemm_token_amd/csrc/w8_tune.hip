@@ -107,7 +107,13 @@ struct Cand {
   w8_cfg cfg;
   int index;
   double us1 = 1e30, us2 = 1e30;
+  double us2_min = 0, us2_p90 = 0;  // bank-2 spread (fastest, 90th-percentile replay)
   bool valid = false;
+};
+
+// us per call of one graph replay series: median, fastest and 90th percentile.
+struct Timing {
+  double med = 0, min = 0, p90 = 0;
 };
 
 #define TRY_HIP(expr)                                                       \
@@ -116,10 +122,11 @@ struct Cand {
     if (e_ != hipSuccess) return fail(W8_E_HIP, hip_msg(#expr, e_));        \
   } while (0)
 
-// Median us per call of a graph of R calls, launch(r) recording call r.
+// us per call of a graph of R calls (median, min and p90 over the replays),
+// launch(r) recording call r.
 template <class Launch>
 w8_status time_graph(hipStream_t stream, size_t R, int warmup, int replays, Launch&& launch,
-                     double* us) {
+                     Timing* us) {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
   TRY_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeThreadLocal));
@@ -152,7 +159,10 @@ w8_status time_graph(hipStream_t stream, size_t R, int warmup, int replays, Laun
   (void)hipGraphExecDestroy(exec);
   if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("timing replay", e));
   std::sort(ms.begin(), ms.end());
-  *us = ms[ms.size() / 2] * 1000.0 / (double)R;
+  const double per = 1000.0 / (double)R;
+  us->med = ms[ms.size() / 2] * per;
+  us->min = ms.front() * per;
+  us->p90 = ms[std::min(ms.size() - 1, (size_t)std::ceil(0.9 * (double)ms.size()) - 1)] * per;
   return W8_OK;
 }
 
@@ -286,9 +296,9 @@ struct Harness {
     return W8_OK;
   }
 
-  // Median us per call of the graph of R calls over rotating weight copies
-  // (every call of the graph reads its own copy of the weights).
-  w8_status time(const w8_cfg& c, double* us) {
+  // us per call of the graph of R calls over rotating weight copies (every
+  // call of the graph reads its own copy of the weights).
+  w8_status time(const w8_cfg& c, Timing* us) {
     return time_graph(
         stream, R, o.warmup, o.replays,
         [&](size_t r) {
@@ -297,6 +307,12 @@ struct Harness {
           return launch(cr, c);
         },
         us);
+  }
+  w8_status time(const w8_cfg& c, double* us) {
+    Timing t;
+    w8_status st = time(c, &t);
+    *us = t.med;
+    return st;
   }
 };
 
@@ -468,10 +484,16 @@ struct MoeHarness {
     return W8_OK;
   }
 
-  w8_status time(const w8_cfg& c, double* us) {
+  w8_status time(const w8_cfg& c, Timing* us) {
     return time_graph(
         stream, G, o.warmup, o.replays,
         [&](size_t g) { return launch_moe_call(call_g(g), c, stream); }, us);
+  }
+  w8_status time(const w8_cfg& c, double* us) {
+    Timing t;
+    w8_status st = time(c, &t);
+    *us = t.med;
+    return st;
   }
 };
 
@@ -485,6 +507,24 @@ w8_status read_opts(const w8_tune_opts* opts, w8_tune_opts* o) {
       o->max_split_k < 1 || o->max_split_k > W8_MAX_SPLIT_K || o->top_n < 0 ||
       (o->op != W8_OP_GEMM && o->op != W8_OP_LINEAR))
     return fail(W8_E_INVALID, "bad tuner options");
+  return W8_OK;
+}
+
+// The tuners allocate device memory and synchronize, which a graph capture
+// in progress on the caller's stream (or on the null stream, which every
+// blocking stream's capture involves) would forbid and be invalidated by:
+// refuse before doing anything.
+w8_status refuse_under_capture(const w8_tune_opts& o) {
+  hipStream_t streams[2] = {static_cast<hipStream_t>(o.stream), nullptr};
+  for (int i = o.stream ? 0 : 1; i < 2; ++i) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(streams[i], &cs);
+    if (e == hipErrorStreamCaptureImplicit || (e == hipSuccess && cs != hipStreamCaptureStatusNone))
+      return fail(W8_E_INVALID, std::string("the tuner cannot run while ") +
+                                    (i == 0 ? "the caller's stream" : "the null stream") +
+                                    " is being captured into a graph");
+    if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("hipStreamIsCapturing", e));
+  }
   return W8_OK;
 }
 
@@ -536,6 +576,8 @@ extern "C" w8_status w8_profile_configs(w8_fmt fmt, int M, int N, int K,
   w8_tune_opts o;
   st = read_opts(opts, &o);
   if (st) return st;
+  st = refuse_under_capture(o);
+  if (st) return st;
   for (int i = 0; i < n; ++i) {
     st = check_cfg(fmt, o.op, M, N, K, cfgs[i]);
     if (st) return st;
@@ -575,6 +617,8 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   if (!best) return fail(W8_E_INVALID, "null best");
   w8_tune_opts o;
   st = read_opts(opts, &o);
+  if (st) return st;
+  st = refuse_under_capture(o);
   if (st) return st;
   const int op = o.op;
   st = check_device();
@@ -636,13 +680,18 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
     if (cd.valid) order.push_back(&cd);
   std::sort(order.begin(), order.end(), [](const Cand* a, const Cand* c) { return a->us1 < c->us1; });
   const size_t top = std::min<size_t>(order.size(), (size_t)o.bank2_top);
+  auto time_bank2 = [&](Cand* c) {
+    Timing t;
+    w8_status s2 = h.time(c->cfg, &t);
+    c->us2 = t.med;
+    c->us2_min = t.min;
+    c->us2_p90 = t.p90;
+    return s2;
+  };
   for (size_t i = 0; i < top; ++i) {
-    st = h.time(order[i]->cfg, &order[i]->us2);
+    st = time_bank2(order[i]);
     if (st) return st;
   }
-  double dflt_us2 = 0;
-  st = h.time(dflt_op, &dflt_us2);  // the op's default config on the tuned layout
-  if (st) return st;
 
   // Bank-2 winner; within 1% prefer no shared tiles (split_k = 1, grid = 0),
   // then swap_ab = 0, then fewer waves per workgroup.
@@ -660,6 +709,27 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
       if (rank(c->cfg) < rank(win->cfg)) win = c;
     }
   }
+  // The op's default config on the tuned layout competes on bank 2 too: it
+  // is validated like any candidate (and is one when it is in the candidate
+  // set) and wins unless the winner is strictly faster, so the entry written
+  // is never slower than the default on bank 2.
+  Cand dflt;
+  dflt.cfg = dflt_op;
+  dflt.index = -1;
+  Cand* dc = &dflt;
+  for (Cand& cd : cands)
+    if (std::memcmp(&cd.cfg, &dflt_op, sizeof dflt_op) == 0) dc = &cd;
+  if (dc == &dflt) {
+    st = h.validate(dflt.cfg, &dflt.valid);
+    if (st) return st;
+  }
+  if (dc->valid && dc->us2 >= 1e29) {
+    st = time_bank2(dc);
+    if (st) return st;
+    if (dc->us1 >= 1e29) dc->us1 = dc->us2;  // not a candidate: timed on bank 2 only
+  }
+  const double dflt_us2 = dc->valid ? dc->us2 : 0.0;
+  if (dc->valid && !(win->us2 < dc->us2)) win = dc;
   *best = win->cfg;
   if (o.insert) {
     st = w8_set_config(fmt, (w8_op)op, M, N, K, packed, &win->cfg, win->us2);
@@ -673,6 +743,8 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
     stats->best_index = win->index;
     stats->best_us_bank1 = win->us1;
     stats->best_us_bank2 = win->us2;
+    stats->best_us_bank2_min = win->us2_min;
+    stats->best_us_bank2_p90 = win->us2_p90;
     stats->default_us_bank2 = dflt_us2;
     const int G = K / W8_GROUP;
     const bool block = fmt == W8_BLOCK_FP8;
@@ -696,6 +768,8 @@ extern "C" w8_status w8_moe_tune(w8_fmt fmt, int E, int T, int N, int K, int top
   if (!best) return fail(W8_E_INVALID, "null best");
   w8_tune_opts o;
   st = read_opts(opts, &o);
+  if (st) return st;
+  st = refuse_under_capture(o);
   if (st) return st;
   st = check_device();
   if (st) return st;
@@ -776,13 +850,18 @@ extern "C" w8_status w8_moe_tune(w8_fmt fmt, int E, int T, int N, int K, int top
     if (cd.valid) order.push_back(&cd);
   std::sort(order.begin(), order.end(), [](const Cand* a, const Cand* c) { return a->us1 < c->us1; });
   const size_t top = std::min<size_t>(order.size(), (size_t)o.bank2_top);
+  auto time_bank2 = [&](Cand* c) {
+    Timing t;
+    w8_status s2 = h.time(c->cfg, &t);
+    c->us2 = t.med;
+    c->us2_min = t.min;
+    c->us2_p90 = t.p90;
+    return s2;
+  };
   for (size_t i = 0; i < top; ++i) {
-    st = h.time(order[i]->cfg, &order[i]->us2);
+    st = time_bank2(order[i]);
     if (st) return st;
   }
-  double dflt_us2 = 0;
-  st = h.time(dflt, &dflt_us2);
-  if (st) return st;
 
   // Bank-2 winner; within 1% prefer no shared tiles, then fewer waves.
   Cand* win = order[0];
@@ -795,6 +874,25 @@ extern "C" w8_status w8_moe_tune(w8_fmt fmt, int E, int T, int N, int K, int top
     };
     if (a < w * 0.99 || (a <= w * 1.01 && rank(c->cfg) < rank(win->cfg))) win = c;
   }
+  // The fallback config competes on bank 2 as in the dense tuner: the entry
+  // written is never slower than it.
+  Cand dfl;
+  dfl.cfg = dflt;
+  dfl.index = -1;
+  Cand* dc = &dfl;
+  for (Cand& cd : cands)
+    if (std::memcmp(&cd.cfg, &dflt, sizeof dflt) == 0) dc = &cd;
+  if (dc == &dfl) {
+    st = h.validate(dfl.cfg, &dfl.valid);
+    if (st) return st;
+  }
+  if (dc->valid && dc->us2 >= 1e29) {
+    st = time_bank2(dc);
+    if (st) return st;
+    if (dc->us1 >= 1e29) dc->us1 = dc->us2;  // not a candidate: timed on bank 2 only
+  }
+  const double dflt_us2 = dc->valid ? dc->us2 : 0.0;
+  if (dc->valid && !(win->us2 < dc->us2)) win = dc;
   *best = win->cfg;
   if (o.insert) {
     st = w8_set_config(fmt, fused ? W8_OP_MOE_LINEAR : W8_OP_MOE, T, N, K, packed, &win->cfg,
@@ -809,6 +907,8 @@ extern "C" w8_status w8_moe_tune(w8_fmt fmt, int E, int T, int N, int K, int top
     stats->best_index = win->index;
     stats->best_us_bank1 = win->us1;
     stats->best_us_bank2 = win->us2;
+    stats->best_us_bank2_min = win->us2_min;
+    stats->best_us_bank2_p90 = win->us2_p90;
     stats->default_us_bank2 = dflt_us2;
     // algorithmic bytes of one call: the active experts' weights and scales,
     // the T activation rows and scales, the T * topk output rows

@@ -40,8 +40,9 @@
  * w8_gemm_w8a8 and w8_gemm_w8a8_acc never allocate, free or synchronize; they
  * only enqueue kernels on the caller's stream, so they can be captured into a
  * HIP graph.  The config table is owned by the library (process-global,
- * guarded by a mutex).  w8_tune_shape allocates, synchronizes and must not be
- * called while the stream is capturing.
+ * guarded by a mutex).  The tuners (w8_tune_shape, w8_moe_tune,
+ * w8_profile_configs) allocate and synchronize: they return W8_E_INVALID,
+ * having done nothing, when opts->stream or the null stream is capturing.
  *
  * Errors: every entry point returns a w8_status.  All argument checks run
  * before anything is enqueued, and nothing throws or aborts across the ABI.
@@ -62,7 +63,7 @@
 extern "C" {
 #endif
 
-#define W8_ABI_VERSION 3
+#define W8_ABI_VERSION 4
 #define W8_MAX_M 32         /* token-count window of the tuned path (paragraph 4) */
 #define W8_MAX_SPLIT_K 256  /* split_k is a power of two up to 256 (paragraph 3) */
 #define W8_GROUP 128        /* Block_FP8 group / block edge */
@@ -173,18 +174,27 @@ typedef struct {
     int32_t op;               /* w8_op tuned (default W8_OP_GEMM) */
     int32_t top_n;            /* > 0: time only the top_n candidates of the cost
                                  model's ranking (w8_rank_configs); 0: all */
+    w8_stream stream;         /* the caller's stream: the tuners allocate and
+                                 synchronize, so they refuse to run (W8_E_INVALID,
+                                 nothing done) while this stream or the null stream
+                                 is being captured into a graph (default NULL: the
+                                 null stream only) */
 } w8_tune_opts;
 
 typedef struct {
     int32_t candidates;       /* feasible candidates enumerated */
     int32_t validated;        /* of which passed validation against the default config */
     int32_t rejected;         /* of which failed validation */
-    int32_t best_index;       /* index of the winner in enumeration order */
+    int32_t best_index;       /* index of the winner in enumeration order; -1: the
+                                 default config, not a candidate, won on bank 2 */
     double best_us_bank1;     /* winner, median us per GEMM on timing bank 1 */
     double best_us_bank2;     /* winner, median us per GEMM on bank 2 (reported figure) */
-    double default_us_bank2;  /* default config on bank 2 */
+    double default_us_bank2;  /* default config on bank 2 (it competes there: the
+                                 winner is never slower; 0 if it failed validation) */
     double best_gbps;         /* algorithmic bytes / best_us_bank2 */
     double tune_seconds;      /* wall-clock time of the whole tuning call */
+    double best_us_bank2_min; /* winner on bank 2: fastest replay, us per GEMM */
+    double best_us_bank2_p90; /* winner on bank 2: 90th-percentile replay */
 } w8_tune_stats;
 
 /* ---------------------------------------------------------------- info -- */
@@ -381,9 +391,12 @@ w8_status w8_lookup_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed
  * standalone quantizer; bit-equal for W8A8_INT8, within 1e-2 relative for
  * the FP8 formats) and times it as HIP graph replays over
  * rotating weight copies; the best on timing bank 1 are re-timed on bank 2,
- * and the bank-2 winner is returned (and inserted into the table when
- * opts->insert).  opts NULL = defaults.  Synchronizes the device; not
- * callable during stream capture.                                          */
+ * together with the op's default config (validated like a candidate), and
+ * the bank-2 winner is returned (and inserted into the table when
+ * opts->insert): the default unless a candidate is strictly faster, so the
+ * entry is never slower than the default on bank 2.  opts NULL = defaults.
+ * Synchronizes the device; W8_E_INVALID (nothing done) while opts->stream or
+ * the null stream is capturing.                                            */
 w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tune_opts *opts,
                         w8_cfg *best, w8_tune_stats *stats);
 void w8_tune_default_opts(w8_tune_opts *opts);
@@ -514,6 +527,24 @@ w8_status w8_moe_linear_config(w8_fmt fmt, int E, int T, int N, int K, int max_m
  * layout, T, N, K) entry when opts->insert.  Allocates and synchronizes.  */
 w8_status w8_moe_tune(w8_fmt fmt, int E, int T, int N, int K, int topk,
                       const w8_tune_opts *opts, w8_cfg *best, w8_tune_stats *stats);
+
+/* -------------------------------------------------------- measurement -- */
+/* The read floor the GEMM is measured against: one kernel launch on `stream`
+ * that reads `bytes` of device memory from `src` once (16-byte non-temporal
+ * loads, 1 KiB per wave instruction, the chunks dealt to the grid's waves
+ * interleaved, `depth` chunks per wave in flight) and writes one word per
+ * wave to `sink`.  A GEMM that streams the same bytes in one launch cannot
+ * take less time; the benchmark graph-replays it over the same rotating
+ * weight buffers as the GEMM and reports each GEMM's time against the best
+ * of a few launch shapes.  Not part of the GEMM path.
+ *   src   device, 16-byte aligned, at least `bytes` readable
+ *   bytes a positive multiple of 1024
+ *   sink  device, 4-byte aligned, sink_bytes >= grid * waves * 4
+ *   grid in [1, 65535] workgroups of 64 * waves threads, waves in
+ *   {1, 2, 4, 8, 16}, depth in {1, 2, 4, 8}
+ * Errors: W8_E_INVALID for any other argument; W8_E_HIP if the launch fails. */
+w8_status w8_read_floor(const void *src, size_t bytes, void *sink, size_t sink_bytes, int grid,
+                        int waves, int depth, w8_stream stream);
 
 #ifdef __cplusplus
 }

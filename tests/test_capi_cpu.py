@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_and_status_strings(lib):
-    assert lib.w8_abi_version() == 3
+    assert lib.w8_abi_version() == 4
     assert lib.w8_status_string(2) == b"W8_E_UNSUPPORTED"
     assert lib.w8_status_string(99) == b"W8_E_UNKNOWN"
 
@@ -113,6 +113,10 @@ def test_config_rejects_wave_shapes_and_grids(w8):
                                                               grid=iters))
     assert not _valid(w8, "FP8_Dynamic", M, N, K, w8.Config.make(tile_n=16, waves_k=1,
                                                                   waves_n=4, grid=iters + 1))
+    # stream-K is compiled for tile_n 16 with unroll 1 or 2 only
+    for kw in (dict(tile_n=32, unroll=1), dict(tile_n=64, unroll=1), dict(tile_n=16, unroll=4)):
+        assert not _valid(w8, "FP8_Dynamic", M, N, K,
+                          w8.Config.make(**dict(dict(waves_k=1, grid=8), **kw))), kw
     # x_lds: the workgroup's K range of activations must fit in 64 KiB
     # (ceil(M/16) x K-steps x K-step/64 chunks of 1 KiB)
     K2 = 7168                                    # FP8: 56 K-steps, 2 chunks each
@@ -137,12 +141,12 @@ def _max_contributors(I, G, KS, T):
                                       (896, 1024, 256), (896, 1024, 448), (5120, 640, 512),
                                       (272, 640, 7), (80, 256, 3)])
 def test_stream_k_workspace_covers_every_tile(w8, N, K, grid):
-    cfg = w8.Config.make(tile_n=32, waves_k=1, waves_n=1, unroll=1, grid=grid)
+    cfg = w8.Config.make(tile_n=16, waves_k=1, waves_n=1, unroll=1, grid=grid)
     KS = K // 64                                 # W8A8_INT8 K-steps
-    T = -(-N // 32)
+    T = -(-N // 16)
     need = w8.workspace_size("W8A8_INT8", 20, N, K, cfg)
-    slots = (need - COUNTERS) // (T * 2 * 2 * 1024)  # 2 row blocks per tile, 2 blocks of M
-    assert need == COUNTERS + T * slots * 2 * 2 * 1024
+    slots = (need - COUNTERS) // (T * 1 * 2 * 1024)  # 1 row block per tile, 2 blocks of M
+    assert need == COUNTERS + T * slots * 1 * 2 * 1024
     assert slots >= _max_contributors(T * KS, grid, KS, T)
 
 
@@ -418,23 +422,23 @@ def test_model_ranking(w8):
 def test_table_malformed_keeps_old_table(w8, tmp_path):
     w8.set_config("W8A8_INT8", 16, 896, 1024, w8.Config.make(), 1.0)
     bad_files = [
-        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 1.0\n",          # too few fields
-        "gfx950 3 INT4 gemm row 16 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",               # unknown format
-        "gfx950 3 W8A8_INT8 gemm tiled 16 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",        # unknown layout
-        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 3 0 0 0 0 1.0\n",          # split_k 3
-        "gfx950 3 W8A8_INT8 gemm row 40 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",          # M above 32
-        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 4 1 x 1 0 0 0 0 1.0\n",          # not an integer
-        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 0 fast\n",         # bad time
-        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 64 4 1 2 1 0 0 0 0 1.0\n",          # tile 64 x unroll 2
-        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 2 2 2 1 0 0 0 0 1.0\n",          # waves_k and waves_n
-        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 1 1 2 2 256 0 0 0 1.0\n",        # grid with split_k
-        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 1 1 2 1 100000 0 0 0 1.0\n",     # grid > iterations
-        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 16 1 2 1 0 0 1 0 1.0\n",        # x_lds, 16 waves
-        "gfx950 3 W8A8_INT8 fused row 16 896 1024 16 4 1 2 1 0 0 1 0 1.0\n",       # unknown op
-        "gfx950 3 W8A8_INT8 linear row 16 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",      # linear without x_lds
-        "gfx950 3 W8A8_INT8 linear row 16 896 1024 16 8 1 2 1 0 0 1 0 1.0\n",      # linear, 8 waves_k
-        "gfx950 3 W8A8_INT8 linear row 16 896 1024 16 8 1 2 1 0 0 1 2 1.0\n",      # quant_launch 2
-        "gfx950 3 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 1 1.0\n",        # gemm, quant_launch
+        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 1.0\n",          # too few fields
+        "gfx950 4 INT4 gemm row 16 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",               # unknown format
+        "gfx950 4 W8A8_INT8 gemm tiled 16 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",        # unknown layout
+        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 3 0 0 0 0 1.0\n",          # split_k 3
+        "gfx950 4 W8A8_INT8 gemm row 40 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",          # M above 32
+        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 4 1 x 1 0 0 0 0 1.0\n",          # not an integer
+        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 0 fast\n",         # bad time
+        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 64 4 1 2 1 0 0 0 0 1.0\n",          # tile 64 x unroll 2
+        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 2 2 2 1 0 0 0 0 1.0\n",          # waves_k and waves_n
+        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 1 1 2 2 256 0 0 0 1.0\n",        # grid with split_k
+        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 1 1 2 1 100000 0 0 0 1.0\n",     # grid > iterations
+        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 16 1 2 1 0 0 1 0 1.0\n",        # x_lds, 16 waves
+        "gfx950 4 W8A8_INT8 fused row 16 896 1024 16 4 1 2 1 0 0 1 0 1.0\n",       # unknown op
+        "gfx950 4 W8A8_INT8 linear row 16 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",      # linear without x_lds
+        "gfx950 4 W8A8_INT8 linear row 16 896 1024 16 8 1 2 1 0 0 1 0 1.0\n",      # linear, 8 waves_k
+        "gfx950 4 W8A8_INT8 linear row 16 896 1024 16 8 1 2 1 0 0 1 2 1.0\n",      # quant_launch 2
+        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 1 1.0\n",        # gemm, quant_launch
     ]
     for i, text in enumerate(bad_files):
         p = tmp_path / f"bad{i}.tbl"
@@ -454,9 +458,10 @@ def test_table_foreign_entries_ignored_and_kept(w8, tmp_path):
                  "gfx950 9 FP8_Dynamic row 4 4096 4096 64 2 1 4 1 0 1 2.0\n"
                  "gfx950 1 FP8_Dynamic row 4 4096 4096 32 2 2 4 0 2.5\n"
                  "gfx950 2 FP8_Dynamic gemm row 4 4096 4096 32 2 1 2 4 0 0 0 2.5\n"
-                 "gfx950 3 FP8_Dynamic gemm row 4 4096 4096 32 2 1 2 4 0 0 0 0 2.5  # native\n")
+                 "gfx950 3 FP8_Dynamic gemm row 4 4096 4096 64 2 1 1 4 0 0 0 0 2.5\n"
+                 "gfx950 4 FP8_Dynamic gemm row 4 4096 4096 32 2 1 2 4 0 0 0 0 2.5  # native\n")
     w8.load_config_table(str(p))
-    assert w8.config_table_size() == 1 and w8.config_table_foreign() == 4
+    assert w8.config_table_size() == 1 and w8.config_table_foreign() == 5
     assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096) == \
         w8.Config.make(tile_n=32, waves_k=2, unroll=2, split_k=4, swap_ab=0)
     q = tmp_path / "out.tbl"
@@ -464,11 +469,12 @@ def test_table_foreign_entries_ignored_and_kept(w8, tmp_path):
     text = q.read_text()
     assert "gfx942 2 FP8_Dynamic gemm row" in text and "gfx950 9 FP8_Dynamic row" in text
     assert "gfx950 1 FP8_Dynamic row 4 4096 4096 32 2 2 4 0 2.5" in text   # older ABI, kept
+    assert "gfx950 3 FP8_Dynamic gemm row 4 4096 4096 64 2 1 1 4" in text
 
 
 def test_table_from_environment(tmp_path):
     p = tmp_path / "env.tbl"
-    p.write_text("gfx950 3 W8A8_INT8 gemm row 16 896 1024 32 2 1 2 8 0 1 0 0 0.5\n")
+    p.write_text("gfx950 4 W8A8_INT8 gemm row 16 896 1024 32 2 1 2 8 0 1 0 0 0.5\n")
     code = ("import bit_quantized_gemm_token_amd as w8;"
             "c = w8.lookup_config('W8A8_INT8', 16, 896, 1024);"
             "print(c.as_dict() if c else None)")
@@ -484,7 +490,7 @@ def test_table_from_environment(tmp_path):
 
 def test_env_table_loaded_by_the_c_library_alone(tmp_path):
     p = tmp_path / "env.tbl"
-    p.write_text("gfx950 3 W8A8_INT8 gemm row 16 896 1024 32 2 1 2 8 0 1 0 0 0.5\n")
+    p.write_text("gfx950 4 W8A8_INT8 gemm row 16 896 1024 32 2 1 2 8 0 1 0 0 0.5\n")
     from bit_quantized_gemm_token_amd import _capi
     # load _capi.py on its own (the package __init__ would load the shipped table)
     code = (
