@@ -99,7 +99,7 @@ def counter_pass(problems, w8, manifest_path, copy_mib, launches=2):
     order = []
     for i, p in enumerate(problems):
         for r in range(launches):
-            w8.gemm_w8a8(p.fmt, p.xq, p.sx, p.weights[r % p.R], p.sw, cfg=p.cfg, y=p.y,
+            w8.gemm_w8a8(p.fmt, p.xq, p.sx, p.weights[r % p.R], p.sw, cfg=p.cfg, y=p.y_gemm,
                          workspace=p.ws)
             torch.cuda.synchronize()
             order.append(i)
@@ -172,6 +172,122 @@ def ingest_counters(manifest_path, fetch_csv, write_csv, out_path, command):
         f"{len(probs)} problems")
 
 
+def _cfg_str(c):
+    return (f"tn{c['tile_n']} wk{c['waves_k']} wn{c['waves_n']} u{c['unroll']} s{c['split_k']} "
+            f"sw{c['swap_ab']} xl{c['x_lds']}" + (f" g{c['grid']}" if c.get("grid") else ""))
+
+
+def summarize_trace(stats_csv, out_md, command):
+    """profiles/*.md from a rocprofv3 kernel_stats.csv: per kernel, calls,
+    total, average, min and max duration and share of the kernel time."""
+    import csv
+    rows = []
+    with open(stats_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            ns = lambda k: float(r.get(k) or 0)
+            rows.append((r["Name"], int(r["Calls"]), ns("TotalDurationNs"), ns("AverageNs"),
+                         ns("MinNs"), ns("MaxNs"), float(r.get("Percentage") or 0)))
+    rows.sort(key=lambda t: -t[2])
+    lines = ["# rocprofv3 kernel trace: " + os.path.basename(out_md)[:-3].replace("_", " "), "",
+             "Command (run from /tmp on the MI355X box, repository at $R):", "", "```", command,
+             "```", "",
+             "Kernel durations in microseconds, start to end of each dispatch, over every call "
+             "in the run.  Under the kernel trace the dispatches of a graph are serialized, so "
+             "averages include no overlap of consecutive launches.", "",
+             "| kernel | calls | total ms | avg us | min us | max us | % |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for name, calls, tot, avg, mn, mx, pct in rows[:40]:
+        short = name if len(name) <= 90 else name[:87] + "..."
+        lines.append(f"| `{short}` | {calls} | {tot / 1e6:.2f} | {avg / 1e3:.3f} | "
+                     f"{mn / 1e3:.3f} | {mx / 1e3:.3f} | {pct:.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log(f"[bench] wrote {out_md} ({len(rows)} kernels)")
+
+
+def summarize_traffic(out_md):
+    """The HBM-traffic table from the counter file that measured_traffic() reads."""
+    import bit_quantized_gemm_token_amd as w8
+    with open(PMC_FILE) as f:
+        d = json.load(f)
+    lines = ["# HBM traffic per GEMM launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             "Two counter runs of `bench.py --counter-pass` (each problem's GEMM launched twice, "
+             "one weight copy each, synchronized after every launch; then a plain float32 "
+             "negation copy three times).  FETCH_SIZE counts the L2's requests to the fabric "
+             "(reads served by the last-level cache included), so it bounds HBM reads from "
+             "above.  Both counters are scaled by what they read for the copy of known size: "
+             f"FETCH_SIZE x {d['fetch_scale']}, WRITE_SIZE x {d['write_scale']} "
+             f"(the copy moves {d['copy_bytes'] // 1024} KiB each way).  Kernel sources hash "
+             f"{d['source_hash']}.", "", "Commands (from /tmp on the MI355X box, repository at "
+             "$R):", "", "```", d.get("command", ""), "```", "",
+             "| format | M | N | K | layout | config | HBM bytes (scaled) | algorithmic bytes | "
+             "ratio |", "|---|---:|---:|---:|---|---|---:|---:|---:|"]
+    ratios = []
+    for r in d["problems"]:
+        hbm = r["fetch_kib"] * d["fetch_scale"] * 1024 + r["write_kib"] * d["write_scale"] * 1024
+        alg = w8.algorithmic_bytes(r["fmt"], r["M"], r["N"], r["K"])
+        ratios.append(hbm / alg)
+        lines.append(f"| {r['fmt']} | {r['M']} | {r['N']} | {r['K']} | {r['layout']} | "
+                     f"{_cfg_str(r['cfg'])} | {hbm:,.0f} | {alg:,} | {hbm / alg:.3f} |")
+    lines += ["", f"Geomean ratio {geomean(ratios):.3f} over {len(ratios)} problems."]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log(f"[bench] wrote {out_md}")
+
+
+def summarize_mfma(manifest_path, counter_csv, out_md, command):
+    """MFMA utilisation per problem from one counter pass: busy cycles over the
+    dispatch time, executed MFMA ops against the algorithmic 2MNK."""
+    import csv
+    with open(manifest_path) as f:
+        man = json.load(f)
+    per = {}
+    with open(counter_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            if "gemm_kernel<" not in r["Kernel_Name"]:
+                continue
+            key = int(r.get("Dispatch_Id") or r.get("Correlation_Id") or 0)
+            e = per.setdefault(key, {})
+            e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                e["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    disp = [per[k] for k in sorted(per)]
+    if len(disp) != len(man["gemm_dispatch_order"]):
+        raise SystemExit(f"{counter_csv}: {len(disp)} GEMM dispatches, expected "
+                         f"{len(man['gemm_dispatch_order'])}")
+    acc = {}
+    for i, e in zip(man["gemm_dispatch_order"], disp):
+        acc.setdefault(i, []).append(e)
+    lines = ["# MFMA utilisation per GEMM launch (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES, "
+             "SQ_INSTS_VALU_MFMA_MOPS_F8/_I8)", "",
+             "One counter run of `bench.py --counter-pass` (each problem's GEMM launched twice, "
+             "synchronized after every launch).  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (summed over "
+             "the SIMDs) / (dispatch duration x 2.4 GHz x 1024 SIMDs).  Executed MFMA ops = MOPS "
+             "x 512 against the algorithmic 2MNK (an MFMA tile has 16 rows of M, so M < 16 pads), "
+             "and their rate against the dense fp8 / int8 MFMA peak (5.0 POP/s).", "",
+             "Command (from /tmp on the MI355X box, repository at $R):", "", "```", command, "```",
+             "", "| format | M | N | K | config | dispatch us | MFMA busy % | executed MFMA ops | "
+             "2MNK | executed / 2MNK | TOP/s | % of peak |",
+             "|---|---:|---:|---:|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for i, pr in enumerate(man["problems"]):
+        es = acc.get(i, [])
+        if not es:
+            continue
+        ns = sum(e.get("ns", 0.0) for e in es) / len(es)
+        busy = sum(e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for e in es) / len(es)
+        mops = sum(e.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0) + e.get("SQ_INSTS_VALU_MFMA_MOPS_I8", 0.0)
+                   for e in es) / len(es) * 512
+        alg = 2 * pr["M"] * pr["N"] * pr["K"]
+        busy_pct = 100 * busy / (ns * 2.4 * 1024) if ns else 0.0
+        tops = mops / ns / 1e3 if ns else 0.0
+        lines.append(f"| {pr['fmt']} | {pr['M']} | {pr['N']} | {pr['K']} | {_cfg_str(pr['cfg'])} | "
+                     f"{ns / 1e3:.2f} | {busy_pct:.2f} | {mops:,.0f} | {alg:,} | {mops / alg:.2f} | "
+                     f"{tops:.1f} | {100 * tops / 5000:.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log(f"[bench] wrote {out_md}")
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -197,6 +313,17 @@ def parse():
                         "FETCH_SIZE and WRITE_SIZE counter-collection CSVs, then exit")
     p.add_argument("--ingest-command", default="",
                    help="the commands that made the counter runs, recorded with them")
+    p.add_argument("--summarize-trace", nargs=2, default=None, metavar=("STATS_CSV", "OUT_MD"),
+                   help="write the kernel-trace summary (profiles/*.md) from a rocprofv3 "
+                        "--kernel-trace --stats kernel_stats.csv, then exit")
+    p.add_argument("--summarize-traffic", default=None, metavar="OUT_MD",
+                   help="write the HBM-traffic summary from the counter file, then exit")
+    p.add_argument("--summarize-mfma", nargs=3, default=None,
+                   metavar=("MANIFEST", "COUNTER_CSV", "OUT_MD"),
+                   help="write the MFMA-utilisation summary from a counter pass with "
+                        "SQ_VALU_MFMA_BUSY_CYCLES and SQ_INSTS_VALU_MFMA_MOPS_F8/_I8, then exit")
+    p.add_argument("--summary-command", default="",
+                   help="the command that made the profile, recorded in the summary")
     return p.parse_args()
 
 
@@ -222,6 +349,7 @@ class Problem:
             wq, self.sw = w8.quantize_weight(fmt, w)
             del w
         self.R = max(2, math.ceil(rotate_bytes / (N * K)))
+        self.wbytes = w8.packed_weight_size(fmt, N, K) if self.packed else N * K
         if self.packed:
             pk = w8.pack_weight(fmt, wq)
             self.pool = torch.empty((self.R, pk.data.numel()), dtype=torch.uint8, device=dev)
@@ -233,7 +361,10 @@ class Problem:
             self.weights = [self.pool[r] for r in range(self.R)]
         self.wq = self.weights[0]
         self.xq, self.sx = w8.quantize_act(fmt, self.x)
-        self.y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        # one output per graph, so each graph's replayed result can be checked
+        self.y_gemm = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        self.y_path = torch.empty_like(self.y_gemm)
+        self.y_linear = torch.empty_like(self.y_gemm)
         self.ws = w8.Workspace(dev, max(w8.workspace_size(fmt, M, N, K, self.cfg), 256))
         # the linear layer through w8_linear, with its own table entry for the
         # same weight layout (fused kernel or quantize launch + GEMM)
@@ -249,17 +380,17 @@ class Problem:
     def run_gemm(self, w8):
         for r in range(self.R):
             w8.gemm_w8a8(self.fmt, self.xq, self.sx, self.weights[r], self.sw, cfg=self.cfg,
-                         y=self.y, workspace=self.ws)
+                         y=self.y_gemm, workspace=self.ws)
 
     def run_path(self, w8):
         for r in range(self.R):
             xq, sx = w8.quantize_act(self.fmt, self.x, xq=self.xq, sx=self.sx)
-            w8.gemm_w8a8(self.fmt, xq, sx, self.weights[r], self.sw, cfg=self.cfg, y=self.y,
+            w8.gemm_w8a8(self.fmt, xq, sx, self.weights[r], self.sw, cfg=self.cfg, y=self.y_path,
                          workspace=self.ws)
 
     def run_linear(self, w8):
         for r in range(self.R):
-            w8.linear(self.fmt, self.x, self.weights[r], self.sw, cfg=self.cfg_l, y=self.y,
+            w8.linear(self.fmt, self.x, self.weights[r], self.sw, cfg=self.cfg_l, y=self.y_linear,
                       workspace=self.ws_l, fused=True)
 
     def capture(self, w8, stream):
@@ -409,6 +540,63 @@ def moe_bench(w8, dev, rotate_bytes, warmup, reps):
             "rows": rows_out}
 
 
+# Launch shapes tried for the read floor (grid, waves per workgroup, chunks
+# in flight per wave); the fastest counts.
+FLOOR_SHAPES = ((128, 8, 2), (256, 4, 2), (256, 8, 2), (512, 4, 2), (512, 4, 4), (512, 8, 2),
+                (1024, 4, 2), (1024, 4, 4))
+
+
+def read_floors(w8, problems, stream, reps=7):
+    """Per distinct weight size B: the time of one launch of the library's
+    read-floor kernel (w8_read_floor) streaming B bytes, graph-replayed over
+    the same rotating weight copies the GEMM reads (R launches per graph,
+    launch r on copy r), median over replays, fastest of FLOOR_SHAPES."""
+    sink = torch.empty(1024 * 16, dtype=torch.int32, device=problems[0].x.device)
+    out = {}
+    for p in problems:
+        if p.wbytes in out:
+            continue
+        flat = p.pool.view(-1)
+        best = None
+        for grid, waves, depth in FLOOR_SHAPES:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for r in range(p.R):
+                    w8.read_floor(flat[r * p.wbytes:(r + 1) * p.wbytes], p.wbytes, sink, grid,
+                                  waves, depth)
+            ts = []
+            with torch.cuda.stream(stream):
+                for i in range(reps + 2):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    g.replay()
+                    e1.record(stream)
+                    e1.synchronize()
+                    if i >= 2:
+                        ts.append(e0.elapsed_time(e1) * 1e3 / p.R)
+            us = sorted(ts)[len(ts) // 2]
+            if best is None or us < best["us"]:
+                best = {"us": us, "grid": grid, "waves": waves, "depth": depth}
+            del g
+        out[p.wbytes] = best
+        log(f"[bench] read floor {p.wbytes} B: {best['us']:.3f} us "
+            f"(grid {best['grid']}, {best['waves']} waves, depth {best['depth']})")
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def context_floors(dev, nbytes):
     """Two device figures the small-shape results are read against: the cost
     of one launch of a one-element kernel under graph replay, and the rate of
@@ -449,12 +637,15 @@ def geomean(v):
     return math.exp(sum(math.log(x) for x in v) / len(v)) if v else 0.0
 
 
-def cpu_baseline(problems, budget_s):
+def cpu_baseline(problems, budget_s, threads=None, refcheck=True):
     """The oracle, timed on the host: passes over the problems (quantize + GEMM
     of each) until `budget_s` seconds of oracle time are spent; per problem the
-    fastest run counts."""
+    fastest run counts.  threads: the oracle's OpenMP thread count (None: all
+    it would use)."""
     import oracle
     oracle._load()
+    if threads:
+        oracle.set_threads(threads)
     inputs = []
     for p in problems:
         x_bits = synthetic.activations(p.fmt, p.M, p.N, p.K)
@@ -468,22 +659,22 @@ def cpu_baseline(problems, budget_s):
     done, t_total, passes = set(), 0.0, 0
     while t_total < budget_s and (passes == 0 or len(done) == len(problems)):
         for i, (p, (x_bits, wq, sw)) in enumerate(zip(problems, inputs)):
-            if t_total >= budget_s and passes > 0:
+            if t_total >= budget_s and (passes > 0 or not refcheck):
                 break
             t0 = time.perf_counter()
             Y, _, _ = oracle.forward(p.fmt, x_bits, wq, sw)
             dt = time.perf_counter() - t0
             t_total += dt
             best[i] = min(best[i], dt)
-            if i not in done:
-                # refcheck: the GPU outputs of this problem (two-launch and
-                # fused paths) against the oracle
+            if i not in done and refcheck:
+                # refcheck: the GPU outputs of this problem's three replayed
+                # graphs (GEMM, quantize + GEMM, linear layer) against the oracle
                 ok = True
-                for y in (p.y_check, p.y_check_linear):
+                for y in (p.y_gemm, p.y_path, p.y_linear):
                     got = y.float().cpu().numpy().astype(np.float64)
                     ok = ok and bool((np.abs(got - Y) <= 1e-2 + 1e-2 * np.abs(Y)).all())
                 p.refcheck = ok
-                done.add(i)
+            done.add(i)
         passes += 1
     checked = [problems[i] for i in sorted(done)]
     gbps = [problems[i].bytes / (best[i] * 1e9) for i in sorted(done)]
@@ -491,6 +682,7 @@ def cpu_baseline(problems, budget_s):
         "value": round(geomean(gbps), 4),
         "unit": "GB/s",
         "cores": oracle.num_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"{len(checked)} of {len(problems)} problems "
                    f"({', '.join(sorted(set(p.fmt for p in checked)))}), quantize + GEMM, "
@@ -503,6 +695,15 @@ def main():
     args = parse()
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters, PMC_FILE, args.ingest_command)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.summary_command)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma, args.summary_command)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
@@ -577,11 +778,37 @@ def main():
         p.gbps = p.bytes / (p.us_gemm * 1e3)
         p.gbps_path = p.bytes / (p.us_path * 1e3)
         p.us_gemm_min = g[0] * 1e3 / p.R
-        p.us_gemm_p90 = g[min(len(g) - 1, int(0.9 * len(g)))] * 1e3 / p.R
-        # one eager run of each path for the refcheck
-        p.y_check = w8.linear(p.fmt, p.x, p.wq, p.sw, cfg=p.cfg)
-        p.y_check_linear = w8.linear(p.fmt, p.x, p.wq, p.sw, cfg=p.cfg_l, fused=True)
+        p.us_gemm_p90 = g[min(len(g) - 1, math.ceil(0.9 * len(g)) - 1)] * 1e3 / p.R
     torch.cuda.synchronize()
+
+    # refcheck of the timed graphs themselves: each output cleared to NaN, each
+    # graph replayed once, and its result compared bit for bit with an eager
+    # call of the same config (and, below, with the oracle)
+    graph_equal = 0
+    with torch.cuda.stream(stream):
+        for p in problems:
+            for y in (p.y_gemm, p.y_path, p.y_linear):
+                y.fill_(float("nan"))
+            p.g_gemm.replay()
+            p.g_path.replay()
+            p.g_linear.replay()
+    torch.cuda.synchronize()
+    for p in problems:
+        eager = w8.linear(p.fmt, p.x, p.wq, p.sw, cfg=p.cfg)
+        eager_l = w8.linear(p.fmt, p.x, p.wq, p.sw, cfg=p.cfg_l, fused=True)
+        torch.cuda.synchronize()
+        same = lambda a, b: torch.equal(a.view(torch.int16), b.view(torch.int16))
+        p.graph_equal = (same(p.y_gemm, eager) and same(p.y_path, eager) and
+                         same(p.y_linear, eager_l))
+        graph_equal += p.graph_equal
+        if not p.graph_equal:
+            log(f"[bench] graph replay differs from eager: {p.fmt} {p.M}x{p.N}x{p.K}")
+    log(f"[bench] graph-replayed outputs equal to eager: {graph_equal}/{len(problems)}")
+
+    floors = read_floors(w8, problems, stream)
+    for p in problems:
+        p.floor_us = floors[p.wbytes]["us"]
+        p.frac_of_floor = p.floor_us / p.us_gemm
 
     # dominant kernel instance
     by_kernel = {}
@@ -622,17 +849,24 @@ def main():
         log(f"[bench] MoE measured in {time.time() - t0:.1f} s")
 
     cpu = None
+    refcheck = {"graph_replay_equals_eager": f"{graph_equal}/{len(problems)}"}
     if not args.no_cpu:
+        import oracle
         cpu, checked = cpu_baseline(problems, args.cpu_budget_s)
-        refcheck = f"{sum(p.refcheck for p in checked)}/{len(checked)} pass"
+        refcheck["graph_outputs_vs_oracle"] = f"{sum(p.refcheck for p in checked)}/{len(checked)} pass"
+        # one thread, on the FP8_Dynamic problems (a third of the sweep)
+        one, _ = cpu_baseline([p for p in problems if p.fmt == fmts[0]], args.cpu_budget_s / 2,
+                              threads=1, refcheck=False)
+        cpu["one_thread"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
     else:
-        refcheck = "skipped"
+        refcheck["graph_outputs_vs_oracle"] = "skipped"
 
     per_fmt = {}
     for fmt in fmts:
         ps = [p for p in problems if p.fmt == fmt]
         per_fmt[fmt] = {"geomean_us_per_gemm": round(geomean([p.us_gemm for p in ps]), 4),
                         "geomean_gbps": round(geomean([p.gbps for p in ps]), 2),
+                        "geomean_frac_of_floor": round(geomean([p.frac_of_floor for p in ps]), 4),
                         "geomean_us_quant_plus_gemm": round(geomean([p.us_path for p in ps]), 4),
                         "geomean_us_linear": round(geomean([p.us_linear for p in ps]), 4)}
     value = geomean([p.gbps for p in problems])
@@ -657,6 +891,8 @@ def main():
                    "bucket_hits": sum(p.from_table == 2 for p in problems),
                    "packed_layout": sum(bool(p.packed) for p in problems)},
         "geomean_us_per_gemm": round(geomean([p.us_gemm for p in problems]), 4),
+        "geomean_us_per_gemm_min": round(geomean([p.us_gemm_min for p in problems]), 4),
+        "geomean_us_per_gemm_p90": round(geomean([p.us_gemm_p90 for p in problems]), 4),
         "geomean_us_quant_plus_gemm": round(geomean([p.us_path for p in problems]), 4),
         "geomean_gbps_quant_plus_gemm": round(geomean([p.gbps_path for p in problems]), 2),
         "geomean_us_linear": round(geomean([p.us_linear for p in problems]), 4),
@@ -665,6 +901,13 @@ def main():
         "linear_fused_problems": sum(p.cfg_l.quant_launch == 0 for p in problems),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "context": dict(floors, frac_of_copy_bw=round(value / floors["copy_gbps"], 4)),
+        "read_floor": {
+            "what": "w8_read_floor: one launch streaming the problem's weight bytes, graph-replayed "
+                    "over the same rotating copies; fastest of the launch shapes tried",
+            "geomean_us": round(geomean([p.floor_us for p in problems]), 4),
+            "geomean_frac_of_floor": round(geomean([p.frac_of_floor for p in problems]), 4),
+            "worst_frac_of_floor": round(min(p.frac_of_floor for p in problems), 4),
+            "problems_within_1_25x": sum(p.frac_of_floor >= 0.8 for p in problems)},
         "per_format": per_fmt,
         "refcheck": refcheck,
         "roofline": roofline,
@@ -678,6 +921,8 @@ def main():
                  "from_table": p.from_table, "R": p.R, "bytes": p.bytes,
                  "us_gemm": round(p.us_gemm, 4), "us_gemm_min": round(p.us_gemm_min, 4),
                  "us_gemm_p90": round(p.us_gemm_p90, 4), "us_quant_plus_gemm": round(p.us_path, 4),
+                 "floor_us": round(p.floor_us, 4), "frac_of_floor": round(p.frac_of_floor, 4),
+                 "graph_equal": bool(p.graph_equal),
                  "us_linear": round(p.us_linear, 4), "cfg_linear": p.cfg_l.as_dict(),
                  "linear_from_table": p.from_table_l,
                  "gbps": round(p.gbps, 1), "frac": round(p.gbps / HBM_PEAK_GBPS, 4),

@@ -33,6 +33,7 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
 def _units():
     units = [("w8_quant.hip", [], "w8_quant.o"),
              ("w8_pack.hip", [], "w8_pack.o"),
+             ("w8_floor.hip", [], "w8_floor.o"),
              ("w8_tune.hip", [], "w8_tune.o"),
              ("w8_capi.cpp", ["-x", "hip"], "w8_capi.o"),
              ("w8_table.cpp", ["-x", "hip"], "w8_table.o"),

@@ -76,6 +76,8 @@ def _load():
     lib.or_gemm.restype = c_int
     lib.or_num_threads.argtypes = []
     lib.or_num_threads.restype = c_int
+    lib.or_set_threads.argtypes = [c_int]
+    lib.or_set_threads.restype = None
     _lib = lib
     return lib
 
@@ -95,6 +97,12 @@ def _fmt(fmt):
 
 def num_threads() -> int:
     return _load().or_num_threads()
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of the oracle's loops (timing only: results do not
+    depend on it)."""
+    _load().or_set_threads(int(n))
 
 
 # ---------------------------------------------------------------- codecs ----

@@ -435,3 +435,15 @@ int or_num_threads(void)
     return 1;
 #endif
 }
+
+/* Sets the OpenMP thread count of the loops above (n >= 1; ignored without
+ * OpenMP).  Timing only: the results do not depend on it, since each thread
+ * computes whole, independent rows or blocks. */
+void or_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
