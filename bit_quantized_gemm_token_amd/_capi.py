@@ -28,7 +28,7 @@ EXPORTS = ("w8_abi_version", "w8_status_string", "w8_last_error", "w8_quantize_a
            "w8_lookup_config", "w8_tune_shape", "w8_tune_default_opts", "w8_model_config",
            "w8_rank_configs", "w8_profile_configs", "w8_moe_gemm", "w8_moe_workspace_size",
            "w8_moe_validate_config", "w8_moe_config", "w8_moe_tune", "w8_moe_linear",
-           "w8_moe_linear_config", "w8_read_floor")
+           "w8_moe_linear_config", "w8_read_floor", "w8_gemm_w8a8_noalloc")
 
 
 class Config(ctypes.Structure):
@@ -115,6 +115,9 @@ def load():
     lib.w8_gemm_w8a8.restype = st
     lib.w8_gemm_w8a8_acc.argtypes = gemm_args
     lib.w8_gemm_w8a8_acc.restype = st
+    lib.w8_gemm_w8a8_noalloc.argtypes = [c_int, c_int, c_int, c_int, vp, i64, f32p, vp, i64, f32p,
+                                         vp, i64, cfgp, vp]
+    lib.w8_gemm_w8a8_noalloc.restype = st
     lib.w8_linear.argtypes = [c_int, c_int, c_int, c_int, vp, i64, vp, i64, f32p, vp, i64, cfgp,
                               vp, ctypes.c_size_t, vp]
     lib.w8_linear.restype = st

@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "w8_internal.hpp"
@@ -362,6 +363,36 @@ w8_status gemm_entry(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ld
   return ok();
 }
 
+// ------------------------------------------------ the no-allocation entry --
+// w8_gemm_w8a8_noalloc keeps the split-K workspace (arrival counters, then
+// partials) in this file-scope device array instead of a caller's buffer.
+// The loader zero-fills it on each device; every call leaves its counters at
+// zero again, and the partials are written before they are read, so nothing
+// needs clearing between calls.  Its host-side name is not a device
+// address: the address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = (size_t)16 << 20;  // 2 MiB of counters + 14 MiB of partials
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+w8_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("hipGetDevice", e));
+  if (dev < 0 || dev >= 64) return fail(W8_E_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(W8_E_HIP, hip_msg("hipGetSymbolAddress(scratch)", e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return W8_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -465,6 +496,37 @@ w8_status w8_gemm_w8a8(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t 
                        int64_t ldy, const w8_cfg* cfg, void* ws, size_t ws_bytes,
                        w8_stream stream) {
   return gemm_entry(fmt, M, N, K, xq, ldq, sx, wq, ldw, sw, y, ldy, cfg, ws, ws_bytes, stream, 0);
+}
+
+w8_status w8_gemm_w8a8_noalloc(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ldq,
+                               const float* sx, const void* wq, int64_t ldw, const float* sw,
+                               void* y, int64_t ldy, const w8_cfg* cfg, w8_stream stream) {
+  w8_status st = check_gemm_shape(fmt, M, N, K);
+  if (st) return st;
+  w8_cfg c;
+  if (cfg) {
+    c = *cfg;
+    st = check_cfg(fmt, W8_OP_GEMM, M, N, K, c);
+    if (st) return st;
+  } else {
+    c = resolve_cfg(fmt, W8_OP_GEMM, M, N, K, ldw == 0, nullptr);
+  }
+  const size_t need = workspace_bytes(fmt, W8_OP_GEMM, M, N, K, c);
+  if (need > kScratchBytes)
+    return fail(W8_E_WORKSPACE, "the config needs " + std::to_string(need) +
+                                    " bytes of workspace; the no-allocation entry point has " +
+                                    std::to_string(kScratchBytes) +
+                                    " (use w8_gemm_w8a8 with a workspace, or a config with less "
+                                    "split_k)");
+  st = check_device();
+  if (st) return st;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_address(&ws);
+    if (st) return st;
+  }
+  return gemm_entry(fmt, M, N, K, xq, ldq, sx, wq, ldw, sw, y, ldy, &c, ws,
+                    need > 0 ? kScratchBytes : 0, stream, 0);
 }
 
 w8_status w8_gemm_w8a8_acc(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ldq,

@@ -294,6 +294,22 @@ w8_status w8_gemm_w8a8_acc(w8_fmt fmt, int M, int N, int K,
                            void *acc, int64_t ldacc, const w8_cfg *cfg,
                            void *ws, size_t ws_bytes, w8_stream stream);
 
+/* w8_gemm_w8a8 for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without a workspace, the same kernels and results.  A config
+ * that shares output tiles (split_k > 1 or grid > 0) keeps its arrival
+ * counters and partials in a 16 MiB device array of the library's own (2
+ * MiB of counters, then up to 14 MiB of partials), which each GPU the
+ * library runs on holds until the process ends; a config that needs more
+ * returns W8_E_WORKSPACE before anything is launched.  It allocates
+ * nothing, frees nothing and never synchronizes.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (on several
+ * streams) race and must not be made. */
+w8_status w8_gemm_w8a8_noalloc(w8_fmt fmt, int M, int N, int K,
+                               const void *xq, int64_t ldq, const float *sx,
+                               const void *wq, int64_t ldw, const float *sw,
+                               void *y, int64_t ldy, const w8_cfg *cfg, w8_stream stream);
+
 /* The whole linear layer on bf16 activations.  With quant_launch == 0, one
  * kernel launch: activation quantization (the w8_quantize_act rules, giving
  * the same codes and scales) fused into the GEMM.  With x_lds == 1 each
