@@ -178,40 +178,62 @@ def quantize_weight(fmt, w, wq=None, sw=None, stream=None):
 
 
 # ------------------------------------------------------------- weight layout --
+# Weight layout codes: 0 row-major, 1 packed (MFMA-native, 16-row blocks),
+# 2/4/8 K-segmented packed (that many K-steps per MFMA, 16/T-row blocks).
+LAYOUTS = {"row": 0, "packed": 1, "seg2": 2, "seg4": 4, "seg8": 8}
+LAYOUT_NAMES = {v: k for k, v in LAYOUTS.items()}
+
+
+def _layout(packed):
+    """Layout code of a `packed` argument: False/True, 0/1/2/4/8 or a name."""
+    if isinstance(packed, str):
+        if packed not in LAYOUTS:
+            raise ValueError(f"unknown weight layout {packed!r}")
+        return LAYOUTS[packed]
+    v = int(packed)
+    if v not in LAYOUT_NAMES:
+        raise ValueError(f"weight layout must be one of {sorted(LAYOUT_NAMES)}, got {packed!r}")
+    return v
+
+
 class PackedWeight:
-    """Weight codes in the GEMM's packed (MFMA-native) layout.
+    """Weight codes in a packed layout (1: MFMA-native; 2, 4, 8: K-segmented).
 
     Produced by pack_weight(); pass it to gemm_w8a8() in place of the
     row-major [N, K] code tensor.  `data` is the 1-D uint8 device buffer.
     """
 
-    def __init__(self, fmt, N, K, data):
+    def __init__(self, fmt, N, K, data, layout=1):
         self.fmt, self.N, self.K, self.data = _fmt(fmt), int(N), int(K), data
+        self.layout = _layout(layout)
+        if self.layout == 0:
+            raise ValueError("a PackedWeight holds a packed layout (1, 2, 4 or 8)")
         self.shape = (self.N, self.K)
         self.device = data.device
 
 
-def packed_weight_size(fmt, N, K):
+def packed_weight_size(fmt, N, K, layout=1):
     n = ctypes.c_size_t(0)
-    _check(_lib.w8_packed_weight_size(_fmt(fmt), N, K, ctypes.byref(n)))
+    _check(_lib.w8_packed_weight_size(_fmt(fmt), N, K, _layout(layout), ctypes.byref(n)))
     return n.value
 
 
-def pack_weight(fmt, wq, stream=None):
-    """Pack row-major codes [N, K] into the packed layout (offline, on the GPU)."""
+def pack_weight(fmt, wq, stream=None, layout=1):
+    """Pack row-major codes [N, K] into packed layout `layout` (offline, on the GPU)."""
     f = _fmt(fmt)
+    lay = _layout(layout)
     ldw = _row_major(wq, "wq") * wq.element_size()
     N, K = wq.shape
-    out = torch.empty(packed_weight_size(f, N, K), dtype=torch.uint8, device=wq.device)
-    _check(_lib.w8_pack_weight(f, N, K, _dev_ptr(wq, "wq"), ldw, _dev_ptr(out, "out"),
+    out = torch.empty(packed_weight_size(f, N, K, lay), dtype=torch.uint8, device=wq.device)
+    _check(_lib.w8_pack_weight(f, N, K, _dev_ptr(wq, "wq"), ldw, _dev_ptr(out, "out"), lay,
                                _stream(stream, wq.device)))
-    return PackedWeight(f, N, K, out)
+    return PackedWeight(f, N, K, out, lay)
 
 
 # --------------------------------------------------------------------- GEMM --
 def workspace_size(fmt, M, N, K, cfg=None, packed=False, op="gemm"):
     n = ctypes.c_size_t(0)
-    _check(_lib.w8_workspace_size(_fmt(fmt), _op(op), M, N, K, int(bool(packed)), _cfg_ptr(cfg),
+    _check(_lib.w8_workspace_size(_fmt(fmt), _op(op), M, N, K, _layout(packed), _cfg_ptr(cfg),
                                   ctypes.byref(n)))
     return n.value
 
@@ -273,15 +295,16 @@ class Workspace:
 
 
 def _weights(f, wq):
-    """(N, K, ldw, device tensor, packed) of row-major codes or a PackedWeight."""
+    """(N, K, ldw, device tensor, layout) of row-major codes or a PackedWeight
+    (ldw 0 for layout 1, -T for the K-segmented layouts)."""
     if isinstance(wq, PackedWeight):
         if wq.fmt != f:
             raise ValueError("packed weights were packed for another format")
-        return wq.N, wq.K, 0, wq.data, True
+        return wq.N, wq.K, (0 if wq.layout == 1 else -wq.layout), wq.data, wq.layout
     if wq.element_size() != 1:
         raise TypeError("wq must hold 1-byte codes")
     N, wk = wq.shape
-    return N, wk, _row_major(wq, "wq") * wq.element_size(), wq, False
+    return N, wk, _row_major(wq, "wq") * wq.element_size(), wq, 0
 
 
 def _gemm(entry, fmt, xq, sx, wq, sw, out, cfg, workspace, stream):
@@ -397,7 +420,7 @@ def pack_experts(fmt, wq, stream=None):
     for e in range(E):
         w = wq[e]
         _check(_lib.w8_pack_weight(f, N, K, _dev_ptr(w, "wq"), _row_major(w, "wq"),
-                                   _dev_ptr(out[e], "out"), _stream(stream, wq.device)))
+                                   _dev_ptr(out[e], "out"), 1, _stream(stream, wq.device)))
     return PackedExperts(f, N, K, out)
 
 
@@ -418,7 +441,7 @@ def moe_config(fmt, E, T, N, K, max_m=32, packed=False):
     entry for (T, N, K) else 0)."""
     c = Config()
     hit = ctypes.c_int(0)
-    _check(_lib.w8_moe_config(_fmt(fmt), E, T, N, K, max_m, int(bool(packed)), ctypes.byref(c),
+    _check(_lib.w8_moe_config(_fmt(fmt), E, T, N, K, max_m, _layout(packed), ctypes.byref(c),
                               ctypes.byref(hit)))
     return c, hit.value
 
@@ -428,7 +451,7 @@ def moe_linear_config(fmt, E, T, N, K, max_m=32, packed=False):
     "moe_linear" entry for (T, N, K) else 0)."""
     c = Config()
     hit = ctypes.c_int(0)
-    _check(_lib.w8_moe_linear_config(_fmt(fmt), E, T, N, K, max_m, int(bool(packed)),
+    _check(_lib.w8_moe_linear_config(_fmt(fmt), E, T, N, K, max_m, _layout(packed),
                                      ctypes.byref(c), ctypes.byref(hit)))
     return c, hit.value
 
@@ -451,7 +474,7 @@ def moe_tune(fmt, E, T, N, K, topk, warmup=2, replays=5, bank2_top=5, rotate_byt
 
 def moe_workspace_size(fmt, E, T, N, K, max_m=32, cfg=None, packed=False):
     n = ctypes.c_size_t(0)
-    _check(_lib.w8_moe_workspace_size(_fmt(fmt), E, T, N, K, max_m, int(bool(packed)),
+    _check(_lib.w8_moe_workspace_size(_fmt(fmt), E, T, N, K, max_m, _layout(packed),
                                       _cfg_ptr(cfg), ctypes.byref(n)))
     return n.value
 
@@ -544,13 +567,15 @@ def moe_linear(fmt, x, offsets, rows, wq, sw, max_m=32, cfg=None, y=None, worksp
 
 # ------------------------------------------------------------------- config --
 # op: "gemm" (gemm_w8a8) or "linear" (linear(..., fused=True)).
-def validate_config(fmt, M, N, K, cfg, op="gemm"):
-    _check(_lib.w8_validate_config(_fmt(fmt), _op(op), M, N, K, _cfg_ptr(cfg)))
+def validate_config(fmt, M, N, K, cfg, op="gemm", packed=False):
+    """Raises W8Error unless cfg is valid for op and the shape on weights of
+    layout `packed` (False/True, 0/1/2/4/8 or a LAYOUTS name)."""
+    _check(_lib.w8_validate_config(_fmt(fmt), _op(op), M, N, K, _layout(packed), _cfg_ptr(cfg)))
 
 
-def default_config(fmt, M, N, K, op="gemm"):
+def default_config(fmt, M, N, K, op="gemm", packed=False):
     c = Config()
-    _check(_lib.w8_default_config(_fmt(fmt), _op(op), M, N, K, ctypes.byref(c)))
+    _check(_lib.w8_default_config(_fmt(fmt), _op(op), M, N, K, _layout(packed), ctypes.byref(c)))
     return c
 
 
@@ -560,7 +585,7 @@ def resolve_config(fmt, M, N, K, packed=False, op="gemm"):
     floor(log2 M) bucket, 0 for the cost model's pick."""
     c = Config()
     hit = ctypes.c_int(0)
-    _check(_lib.w8_resolve_config(_fmt(fmt), _op(op), M, N, K, int(bool(packed)),
+    _check(_lib.w8_resolve_config(_fmt(fmt), _op(op), M, N, K, _layout(packed),
                                   ctypes.byref(c), ctypes.byref(hit)))
     return c, hit.value
 
@@ -568,8 +593,46 @@ def resolve_config(fmt, M, N, K, packed=False, op="gemm"):
 def model_config(fmt, M, N, K, packed=False, op="gemm"):
     """The cost model's top-1 config (what an untuned shape runs)."""
     c = Config()
-    _check(_lib.w8_model_config(_fmt(fmt), _op(op), M, N, K, int(bool(packed)), ctypes.byref(c)))
+    _check(_lib.w8_model_config(_fmt(fmt), _op(op), M, N, K, _layout(packed), ctypes.byref(c)))
     return c
+
+
+class PredictBatch:
+    """Rows (fmt, op, layout, M, N, K, cfg) packed once for the library's
+    cost model (w8_predict_us); run(params) returns the predicted us per call
+    of every row as a numpy array, with the compiled constants (params None)
+    or 13 trial constants.  Host only."""
+
+    def __init__(self, rows):
+        import numpy as np
+        n = len(rows)
+        self.n = n
+        arr = lambda vals: (ctypes.c_int * max(n, 1))(*vals)
+        self._fmt = arr([_fmt(r[0]) for r in rows])
+        self._op = arr([_op(r[1]) for r in rows])
+        self._layout = arr([_layout(r[2]) for r in rows])
+        self._M, self._N, self._K = (arr([int(r[i]) for r in rows]) for i in (3, 4, 5))
+        self._cfgs = (Config * max(n, 1))(*[c if isinstance(c, Config) else Config.make(**c)
+                                            for c in (r[6] for r in rows)])
+        self._out = np.zeros(max(n, 1), dtype=np.float64)
+
+    def run(self, params=None):
+        dp = ctypes.POINTER(ctypes.c_double)
+        if params is None:
+            pp, npar = None, 0
+        else:
+            pv = (ctypes.c_double * len(params))(*[float(v) for v in params])
+            pp, npar = ctypes.cast(pv, dp), len(params)
+        _check(_lib.w8_predict_us(self.n, self._fmt, self._op, self._layout, self._M, self._N,
+                                  self._K, self._cfgs, pp, npar,
+                                  self._out.ctypes.data_as(dp)))
+        return self._out[:self.n].copy()
+
+
+def predict_us(rows, params=None):
+    """The cost model's predicted us per call of each (fmt, op, layout, M, N,
+    K, cfg) row (cfg a Config or a dict of its fields)."""
+    return list(PredictBatch(rows).run(params))
 
 
 def lookup_config(fmt, M, N, K, packed=False, with_time=False, op="gemm"):
@@ -579,7 +642,7 @@ def lookup_config(fmt, M, N, K, packed=False, with_time=False, op="gemm"):
     """
     c = Config()
     us = ctypes.c_double(0.0)
-    st = _lib.w8_lookup_config(_fmt(fmt), _op(op), M, N, K, int(bool(packed)), ctypes.byref(c),
+    st = _lib.w8_lookup_config(_fmt(fmt), _op(op), M, N, K, _layout(packed), ctypes.byref(c),
                                ctypes.byref(us))
     if st == 8:
         return None
@@ -587,19 +650,21 @@ def lookup_config(fmt, M, N, K, packed=False, with_time=False, op="gemm"):
     return (c, us.value) if with_time else c
 
 
-def best_layout(fmt, M, N, K, op="gemm"):
-    """True if the table says packed weights are faster for this shape."""
-    row = lookup_config(fmt, M, N, K, packed=False, with_time=True, op=op)
-    pk = lookup_config(fmt, M, N, K, packed=True, with_time=True, op=op)
-    if pk is None:
-        return False
-    return row is None or pk[1] < row[1]
+def best_layout(fmt, M, N, K, op="gemm", layouts=(0, 1, 2, 4, 8)):
+    """The layout code (of `layouts`) whose table entry for this op and
+    shape has the lowest time per call; 0 (row-major) when none has one."""
+    best, best_us = 0, None
+    for lay in layouts:
+        e = lookup_config(fmt, M, N, K, packed=lay, with_time=True, op=op)
+        if e is not None and (best_us is None or e[1] < best_us):
+            best, best_us = _layout(lay), e[1]
+    return best
 
 
 def set_config(fmt, M, N, K, cfg, us_per_gemm=0.0, packed=False, op="gemm"):
     if isinstance(cfg, dict):
         cfg = Config.make(**cfg)
-    _check(_lib.w8_set_config(_fmt(fmt), _op(op), M, N, K, int(bool(packed)), ctypes.byref(cfg),
+    _check(_lib.w8_set_config(_fmt(fmt), _op(op), M, N, K, _layout(packed), ctypes.byref(cfg),
                               float(us_per_gemm)))
 
 
@@ -640,7 +705,7 @@ def _tune_opts(warmup=2, replays=5, bank2_top=5, rotate_bytes=512 << 20,
     o.warmup, o.replays, o.bank2_top = warmup, replays, bank2_top
     o.rotate_bytes, o.max_split_k = rotate_bytes, max_split_k
     o.insert, o.fail_candidate = int(bool(insert)), fail_candidate
-    o.packed = int(bool(packed))
+    o.packed = _layout(packed)
     o.stream_k = int(bool(stream_k))
     o.op = _op(op)
     o.top_n = int(top_n)

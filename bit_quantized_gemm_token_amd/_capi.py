@@ -5,7 +5,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw8gemm.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 MAX_M = 32
 MAX_SPLIT_K = 256
 GROUP = 128
@@ -28,7 +28,7 @@ EXPORTS = ("w8_abi_version", "w8_status_string", "w8_last_error", "w8_quantize_a
            "w8_lookup_config", "w8_tune_shape", "w8_tune_default_opts", "w8_model_config",
            "w8_rank_configs", "w8_profile_configs", "w8_moe_gemm", "w8_moe_workspace_size",
            "w8_moe_validate_config", "w8_moe_config", "w8_moe_tune", "w8_moe_linear",
-           "w8_moe_linear_config", "w8_read_floor", "w8_gemm_w8a8_noalloc")
+           "w8_moe_linear_config", "w8_read_floor", "w8_gemm_w8a8_noalloc", "w8_predict_us")
 
 
 class Config(ctypes.Structure):
@@ -105,9 +105,10 @@ def load():
     lib.w8_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, cfgp,
                                       ctypes.POINTER(ctypes.c_size_t)]
     lib.w8_workspace_size.restype = st
-    lib.w8_packed_weight_size.argtypes = [c_int, c_int, c_int, ctypes.POINTER(ctypes.c_size_t)]
+    lib.w8_packed_weight_size.argtypes = [c_int, c_int, c_int, c_int,
+                                          ctypes.POINTER(ctypes.c_size_t)]
     lib.w8_packed_weight_size.restype = st
-    lib.w8_pack_weight.argtypes = [c_int, c_int, c_int, vp, i64, vp, vp]
+    lib.w8_pack_weight.argtypes = [c_int, c_int, c_int, vp, i64, vp, c_int, vp]
     lib.w8_pack_weight.restype = st
     gemm_args = [c_int, c_int, c_int, c_int, vp, i64, f32p, vp, i64, f32p, vp, i64, cfgp, vp,
                  ctypes.c_size_t, vp]
@@ -121,9 +122,9 @@ def load():
     lib.w8_linear.argtypes = [c_int, c_int, c_int, c_int, vp, i64, vp, i64, f32p, vp, i64, cfgp,
                               vp, ctypes.c_size_t, vp]
     lib.w8_linear.restype = st
-    lib.w8_validate_config.argtypes = [c_int, c_int, c_int, c_int, c_int, cfgp]
+    lib.w8_validate_config.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, cfgp]
     lib.w8_validate_config.restype = st
-    lib.w8_default_config.argtypes = [c_int, c_int, c_int, c_int, c_int, cfgp]
+    lib.w8_default_config.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, cfgp]
     lib.w8_default_config.restype = st
     lib.w8_resolve_config.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, cfgp,
                                       ctypes.POINTER(c_int)]
@@ -147,6 +148,11 @@ def load():
     lib.w8_tune_default_opts.restype = None
     lib.w8_model_config.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, cfgp]
     lib.w8_model_config.restype = st
+    ip = ctypes.POINTER(c_int)
+    lib.w8_predict_us.argtypes = [c_int, ip, ip, ip, ip, ip, ip, cfgp,
+                                  ctypes.POINTER(ctypes.c_double), c_int,
+                                  ctypes.POINTER(ctypes.c_double)]
+    lib.w8_predict_us.restype = st
     dp = ctypes.POINTER(ctypes.c_double)
     lib.w8_rank_configs.argtypes = [c_int, c_int, c_int, c_int, ctypes.POINTER(TuneOpts), cfgp,
                                     dp, c_int, ctypes.POINTER(c_int)]

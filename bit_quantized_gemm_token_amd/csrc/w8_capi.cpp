@@ -27,17 +27,19 @@ int wk_index(int wk) {
 }
 int wn_index(int wn) { return wn == 1 ? 0 : wn == 2 ? 1 : wn == 4 ? 2 : wn == 8 ? 3 : -1; }
 int u_index(int u) { return u == 1 ? 0 : u == 2 ? 1 : u == 4 ? 2 : -1; }
+// weight layout 0 (row-major), 1, 2, 4, 8 (packed, K-steps per MFMA)
+int lay_index(int l) { return l == 0 ? 0 : l == 1 ? 1 : l == 2 ? 2 : l == 4 ? 3 : l == 8 ? 4 : -1; }
 
-// [fmt][mb-1][nb][wk][wn][unroll][swap][packed][xl][sk] -> launcher
+// [fmt][mb-1][nb][wk][wn][unroll][swap][layout][xl][sk] -> launcher
 struct InstanceIndex {
-  GemmLaunchFn fn[3][2][3][5][4][3][2][2][4][2] = {};
+  GemmLaunchFn fn[3][2][3][5][4][3][2][5][4][2] = {};
   InstanceIndex() {
     int n = 0;
     const GemmInstance* p = gemm_instances(&n);
     for (int i = 0; i < n; ++i) {
       const GemmInstance& g = p[i];
       fn[g.fmt][g.mb - 1][nb_index(g.nb)][wk_index(g.wk)][wn_index(g.wn)][u_index(g.unroll)]
-        [g.swap][g.packed][g.xl][g.sk] = g.fn;
+        [g.swap][lay_index(g.packed)][g.xl][g.sk] = g.fn;
     }
   }
 };
@@ -79,6 +81,18 @@ int fmt_from_name(const std::string& s) {
 
 int ksteps_of(int fmt, int K) { return (K + kstep_of(fmt) - 1) / kstep_of(fmt); }
 
+int layout_from_ldw(long long ldw) {
+  if (ldw > 0) return 0;
+  if (ldw == 0 || ldw == -1) return 1;
+  if (ldw == -2 || ldw == -4 || ldw == -8) return (int)-ldw;
+  return -1;
+}
+
+// Token rows one launch covers: 16 per MFMA block (two blocks) for row-major
+// and plain packed weights, R = 16/T per group (two groups) for the
+// K-segmented layouts; larger M runs as consecutive launches.
+int launch_rows(int layout) { return 2 * layout_rows(layout); }
+
 w8_status check_gemm_shape(int fmt, int M, int N, int K) {
   if (fmt < 0 || fmt > 2) return fail(W8_E_INVALID, "unknown format " + std::to_string(fmt));
   if (M < 1 || N < 1 || K < 1)
@@ -94,13 +108,30 @@ w8_status check_gemm_shape(int fmt, int M, int N, int K) {
   return W8_OK;
 }
 
-w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c) {
+GemmLaunchFn find_instance(int fmt, int mb, const w8_cfg& c, int layout, int xl);
+static int launch_mb(int M, int layout);
+
+w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c, int layout) {
   if (c.abi_version != W8_ABI_VERSION)
     return fail(W8_E_INVALID, "cfg.abi_version " + std::to_string(c.abi_version) + " != " +
                                   std::to_string(W8_ABI_VERSION));
   if (c.reserved[0]) return fail(W8_E_INVALID, "cfg.reserved must be zero");
-  if (nb_index(c.tile_n / 16) < 0 || c.tile_n % 16)
-    return fail(W8_E_INVALID, "cfg.tile_n must be 16, 32 or 64");
+  if (!layout_valid(layout)) return fail(W8_E_INVALID, "weight layout must be 0, 1, 2, 4 or 8");
+  const int R = layout_rows(layout);
+  if (nb_index(c.tile_n / R) < 0 || c.tile_n % R)
+    return fail(W8_E_INVALID, layout > 1 ? "cfg.tile_n must be 1, 2 or 4 times the layout's " +
+                                               std::to_string(R) + "-row block"
+                                         : std::string("cfg.tile_n must be 16, 32 or 64"));
+  if (layout > 1) {
+    // K-segmented layouts: plain activation loads, one wave along N, split-K
+    if (c.x_lds || c.waves_n != 1 || c.grid != 0)
+      return fail(W8_E_INVALID, "cfg: the K-segmented layouts run with x_lds 0, waves_n 1 and "
+                                "grid 0");
+    if ((op == W8_OP_LINEAR || op == W8_OP_MOE_LINEAR) && !c.quant_launch)
+      return fail(W8_E_INVALID, "cfg: the linear op on K-segmented layouts needs quant_launch 1");
+    if (op == W8_OP_MOE || op == W8_OP_MOE_LINEAR)
+      return fail(W8_E_INVALID, "the grouped GEMM runs on row-major and plain packed weights");
+  }
   if (wk_index(c.waves_k) < 0) return fail(W8_E_INVALID, "cfg.waves_k must be 1, 2, 4, 8 or 16");
   if (wn_index(c.waves_n) < 0) return fail(W8_E_INVALID, "cfg.waves_n must be 1, 2, 4 or 8");
   if (c.waves_n > 1 && c.waves_k != 1)
@@ -126,14 +157,14 @@ w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c) {
                 "or for the Block_FP8 linear op x_lds == 0 (quantized in the K loop) with "
                 "tile_n 16 or 32, unroll 1 and waves_k 2, 4 or 8");
   if (u_index(c.unroll) < 0) return fail(W8_E_INVALID, "cfg.unroll must be 1, 2 or 4");
-  if ((c.tile_n / 16) * c.unroll > 4)
-    return fail(W8_E_INVALID, "cfg: tile_n/16 * unroll must be at most 4");
+  if ((c.tile_n / R) * c.unroll > 4)
+    return fail(W8_E_INVALID, "cfg: (blocks per wave) * unroll must be at most 4");
   if (!is_pow2(c.split_k) || c.split_k > W8_MAX_SPLIT_K)
     return fail(W8_E_INVALID, "cfg.split_k must be a power of two in [1, 256], got " +
                                   std::to_string(c.split_k));
   if (c.swap_ab != 0 && c.swap_ab != 1) return fail(W8_E_INVALID, "cfg.swap_ab must be 0 or 1");
   const long long ntiles = tiles_of(N, c);
-  const long long iters = ntiles * ksteps_of(fmt, K);
+  const long long iters = ntiles * layout_spans(fmt, K, layout);
   if (c.grid < 0) return fail(W8_E_INVALID, "cfg.grid must be >= 0");
   if (c.grid > 0) {
     if (c.split_k != 1) return fail(W8_E_INVALID, "cfg: stream-K (grid > 0) needs split_k == 1");
@@ -164,6 +195,16 @@ w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c) {
   const long long threads = wgs * 64 * c.waves_k * c.waves_n;
   if (threads > 0xFFFFFFFFLL)
     return fail(W8_E_INVALID, "cfg: (workgroups x waves x 64) threads exceed 2^32 - 1");
+  if (op == W8_OP_GEMM || op == W8_OP_LINEAR) {
+    // a compiled kernel for each launch of the call (all of `rows` token
+    // rows but a shorter last one)
+    const int xl = (op == W8_OP_LINEAR && !c.quant_launch) ? (c.x_lds ? 2 : 3) : c.x_lds;
+    const int rows = launch_rows(layout);
+    const int last = M % rows ? M % rows : rows;
+    if (!find_instance(fmt, launch_mb(std::min(M, rows), layout), c, layout, xl) ||
+        !find_instance(fmt, launch_mb(last, layout), c, layout, xl))
+      return fail(W8_E_INVALID, "no compiled kernel for this config and weight layout");
+  }
   return W8_OK;
 }
 
@@ -177,31 +218,37 @@ int partial_slots(int fmt, int N, int K, const w8_cfg& c) {
   return c.split_k;
 }
 
-static size_t gemm_ws_bytes(int fmt, int M, int N, int K, const w8_cfg& c) {
+// Blocks of token rows in one launch (the kernel's MB).
+static int launch_mb(int M, int layout) {
+  const int R = layout_rows(layout);
+  return std::min(2, (M + R - 1) / R);
+}
+
+static size_t gemm_ws_bytes(int fmt, int M, int N, int K, const w8_cfg& c, int layout) {
   if (c.split_k <= 1 && c.grid <= 0) return 0;
   const int ntiles = tiles_of(N, c);
-  const int mb = (M + 15) / 16;
-  return ws_counter_bytes(ntiles) + ws_partial_bytes(ntiles, partial_slots(fmt, N, K, c),
-                                                     c.waves_n * c.tile_n / 16, mb);
+  return ws_counter_bytes(ntiles) +
+         ws_partial_bytes(ntiles, partial_slots(fmt, N, K, c),
+                          c.waves_n * c.tile_n / layout_rows(layout), launch_mb(M, layout));
 }
 
 static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
-LinearWs linear_ws(int fmt, int M, int N, int K, const w8_cfg& c) {
+LinearWs linear_ws(int fmt, int M, int N, int K, const w8_cfg& c, int layout) {
   LinearWs w;
   w.ldq = (K + 15) / 16 * 16;
   // past the arrival counters even when this config shares no tile: another
   // call on the same workspace may need them at zero
-  w.codes = round256(std::max(gemm_ws_bytes(fmt, M, N, K, c), ws_counter_bytes(0)));
+  w.codes = round256(std::max(gemm_ws_bytes(fmt, M, N, K, c, layout), ws_counter_bytes(0)));
   w.scales = w.codes + round256((size_t)M * w.ldq);
   const size_t nsx = fmt == W8_BLOCK_FP8 ? (size_t)M * (K / W8_GROUP) : (size_t)M;
   w.total = w.scales + round256(nsx * 4);
   return w;
 }
 
-size_t workspace_bytes(int fmt, int op, int M, int N, int K, const w8_cfg& c) {
-  if (op == W8_OP_LINEAR && c.quant_launch) return linear_ws(fmt, M, N, K, c).total;
-  return gemm_ws_bytes(fmt, M, N, K, c);
+size_t workspace_bytes(int fmt, int op, int M, int N, int K, const w8_cfg& c, int layout) {
+  if (op == W8_OP_LINEAR && c.quant_launch) return linear_ws(fmt, M, N, K, c, layout).total;
+  return gemm_ws_bytes(fmt, M, N, K, c, layout);
 }
 
 // Default config (used when the table has no entry for the shape).  It
@@ -210,8 +257,9 @@ size_t workspace_bytes(int fmt, int op, int M, int N, int K, const w8_cfg& c) {
 // split_k that gives at least two workgroups per compute unit while every
 // wave keeps at least one full stage of K-steps.  The fused linear op stages
 // activations in LDS (x_lds), so it doubles split_k further until a
-// workgroup's K range of activations fits.
-w8_cfg make_default_cfg(int fmt, int op, int M, int N, int K) {
+// workgroup's K range of activations fits.  The K-segmented layouts take one
+// block per wave, two K-waves, and the linear op a quantize launch.
+w8_cfg make_default_cfg(int fmt, int op, int M, int N, int K, int layout) {
   w8_cfg c;
   std::memset(&c, 0, sizeof c);
   c.abi_version = W8_ABI_VERSION;
@@ -220,6 +268,20 @@ w8_cfg make_default_cfg(int fmt, int op, int M, int N, int K) {
   c.waves_n = 1;
   c.unroll = 2;
   c.swap_ab = M < 32 ? 1 : 0;
+  if (layout > 1) {
+    const int R = layout_rows(layout);
+    const int spans = layout_spans(fmt, K, layout);
+    c.tile_n = R;
+    c.waves_k = 2;
+    c.swap_ab = 1;
+    int s = 1;
+    while (s < W8_MAX_SPLIT_K && (long long)((N + R - 1) / R) * s < 256 &&
+           spans / (2 * s) >= c.waves_k * c.unroll)
+      s *= 2;
+    c.split_k = s;
+    if (op == W8_OP_LINEAR) c.quant_launch = 1;
+    return c;
+  }
   const int ntiles = (N + 15) / 16;
   const int T = ksteps_of(fmt, K);
   int s = 1;
@@ -254,15 +316,38 @@ w8_status check_device() {
   return W8_OK;
 }
 
+GemmLaunchFn find_instance(int fmt, int mb, const w8_cfg& c, int layout, int xl) {
+  const int nb = c.tile_n / layout_rows(layout);
+  if (mb < 1 || mb > 2 || nb_index(nb) < 0 || wk_index(c.waves_k) < 0 ||
+      wn_index(c.waves_n) < 0 || u_index(c.unroll) < 0 || lay_index(layout) < 0 ||
+      c.swap_ab < 0 || c.swap_ab > 1 || xl < 0 || xl > 3)
+    return nullptr;
+  return instance_index().fn[fmt][mb - 1][nb_index(nb)][wk_index(c.waves_k)][wn_index(c.waves_n)]
+                            [u_index(c.unroll)][c.swap_ab][lay_index(layout)][xl]
+                            [c.grid > 0 ? 1 : 0];
+}
+
 w8_status launch_gemm_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
-  const int mb = (g.M + 15) / 16;
-  const int nb = c.tile_n / 16;
-  GemmLaunchFn fn =
-      instance_index().fn[g.fmt][mb - 1][nb_index(nb)][wk_index(c.waves_k)][wn_index(c.waves_n)]
-                         [u_index(c.unroll)][c.swap_ab][g.packed ? 1 : 0]
-                         [g.x ? (c.x_lds ? 2 : 3) : c.x_lds][c.grid > 0 ? 1 : 0];
+  const int rows = launch_rows(g.layout);
+  if (g.M > rows) {
+    // consecutive launches of `rows` token rows each (K-segmented layouts;
+    // they share the workspace, in stream order)
+    for (int m0 = 0; m0 < g.M; m0 += rows) {
+      GemmCall p = g;
+      p.M = std::min(rows, g.M - m0);
+      p.xq = static_cast<const uint8_t*>(g.xq) + (long long)m0 * g.ldq;
+      p.sx = g.sx + (long long)m0 * (g.fmt == W8_BLOCK_FP8 ? g.K / W8_GROUP : 1);
+      p.out = static_cast<char*>(g.out) + (long long)m0 * g.ldo * (g.out_mode ? 4 : 2);
+      const w8_status st = launch_gemm_call(p, c, s);
+      if (st) return st;
+    }
+    return W8_OK;
+  }
+  const int mb = launch_mb(g.M, g.layout);
+  GemmLaunchFn fn = find_instance(g.fmt, mb, c, g.layout, g.x ? (c.x_lds ? 2 : 3) : c.x_lds);
   if (!fn) return fail(W8_E_INVALID, "no compiled kernel for this config");
   const int ntiles = tiles_of(g.N, c);
+  const int T = layout_segments(g.layout);
   GemmArgs a;
   a.xq = static_cast<const uint8_t*>(g.x ? g.x : g.xq);  // fused: bf16 activations
   a.sx = g.sx;
@@ -270,13 +355,14 @@ w8_status launch_gemm_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
   a.sw = g.sw;
   a.out = g.out;
   a.ldq = g.x ? g.ldx : g.ldq;
-  a.ldw = g.ldw;
+  a.ldw = g.layout ? 0 : g.ldw;
   a.ldo = g.ldo;
   a.M = g.M;
   a.N = g.N;
   a.K = g.K;
-  a.ksteps = ksteps_of(g.fmt, g.K);
-  a.kfull = g.K / kstep_of(g.fmt);
+  // the K loop's steps: K-steps, or spans of T of them
+  a.ksteps = layout_spans(g.fmt, g.K, g.layout);
+  a.kfull = g.K / kstep_of(g.fmt) / T;
   a.split_k = c.split_k;
   a.split_shift = __builtin_ctz((unsigned)c.split_k);
   a.grid = c.grid;
@@ -299,7 +385,7 @@ w8_status launch_gemm_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
 w8_status launch_linear_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
   if (!c.quant_launch) return launch_gemm_call(g, c, s);
   // quantize into the workspace, then the GEMM on the codes
-  const LinearWs w = linear_ws(g.fmt, g.M, g.N, g.K, c);
+  const LinearWs w = linear_ws(g.fmt, g.M, g.N, g.K, c, g.layout);
   char* base = static_cast<char*>(g.ws);
   uint8_t* xq = reinterpret_cast<uint8_t*>(base + w.codes);
   float* sx = reinterpret_cast<float*>(base + w.scales);
@@ -331,23 +417,23 @@ w8_status gemm_entry(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ld
   if (!xq || !sx || !wq || !sw || !out) return fail(W8_E_INVALID, "null device pointer");
   if (!aligned(xq, 16) || !aligned(wq, 16))
     return fail(W8_E_INVALID, "xq and wq must be 16-byte aligned");
-  const int packed = ldw == 0;  // ldw == 0: weights in the packed layout
-  if (ldq < K || ldq % 16 || (!packed && (ldw < K || ldw % 16)))
+  const int layout = layout_from_ldw(ldw);  // ldw <= 0: packed weights
+  if (ldq < K || ldq % 16 || layout < 0 || (!layout && (ldw < K || ldw % 16)))
     return fail(W8_E_INVALID,
-                "ldq must be >= K and a multiple of 16; ldw must be 0 (packed weights) or "
-                ">= K and a multiple of 16");
+                "ldq must be >= K and a multiple of 16; ldw must be >= K and a multiple of 16 "
+                "(row-major weights), 0 (packed) or -2, -4, -8 (K-segmented packed)");
   if (ldo < N) return fail(W8_E_INVALID, "output leading dimension must be >= N");
   if (!aligned(sx, 4) || !aligned(sw, 4) || !aligned(out, out_mode ? 4 : 2))
     return fail(W8_E_INVALID, "misaligned scale or output pointer");
   w8_cfg c;
   if (cfg) {
     c = *cfg;
-    st = check_cfg(fmt, W8_OP_GEMM, M, N, K, c);
+    st = check_cfg(fmt, W8_OP_GEMM, M, N, K, c, layout);
     if (st) return st;
   } else {
-    c = resolve_cfg(fmt, W8_OP_GEMM, M, N, K, packed, nullptr);
+    c = resolve_cfg(fmt, W8_OP_GEMM, M, N, K, layout, nullptr);
   }
-  const size_t need = workspace_bytes(fmt, W8_OP_GEMM, M, N, K, c);
+  const size_t need = workspace_bytes(fmt, W8_OP_GEMM, M, N, K, c, layout);
   if (need > 0) {
     if (!ws || ws_bytes < need)
       return fail(W8_E_WORKSPACE, "workspace of " + std::to_string(need) + " bytes needed, got " +
@@ -356,7 +442,7 @@ w8_status gemm_entry(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ld
   }
   st = check_device();
   if (st) return st;
-  GemmCall g{fmt, M, N, K, xq, ldq, sx, wq, ldw, sw, out, ldo, out_mode, ws, ws_bytes, packed,
+  GemmCall g{fmt, M, N, K, xq, ldq, sx, wq, ldw, sw, out, ldo, out_mode, ws, ws_bytes, layout,
              nullptr, 0};
   st = launch_gemm_call(g, c, static_cast<hipStream_t>(stream));
   if (st) return st;
@@ -450,43 +536,49 @@ w8_status w8_quantize_weight(w8_fmt fmt, int N, int K, const float* w, int64_t l
   return ok();
 }
 
-w8_status w8_workspace_size(w8_fmt fmt, w8_op op, int M, int N, int K, int packed,
+w8_status w8_workspace_size(w8_fmt fmt, w8_op op, int M, int N, int K, int layout,
                             const w8_cfg* cfg, size_t* bytes) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!bytes) return fail(W8_E_INVALID, "null output pointer");
   if (op != W8_OP_GEMM && op != W8_OP_LINEAR) return fail(W8_E_INVALID, "unknown op");
+  if (!layout_valid(layout)) return fail(W8_E_INVALID, "weight layout must be 0, 1, 2, 4 or 8");
   w8_cfg c;
   if (cfg) {
     c = *cfg;
-    st = check_cfg(fmt, op, M, N, K, c);
+    st = check_cfg(fmt, op, M, N, K, c, layout);
     if (st) return st;
   } else {
-    c = resolve_cfg(fmt, op, M, N, K, packed != 0, nullptr);
+    c = resolve_cfg(fmt, op, M, N, K, layout, nullptr);
   }
-  *bytes = workspace_bytes(fmt, op, M, N, K, c);
+  *bytes = workspace_bytes(fmt, op, M, N, K, c, layout);
   return ok();
 }
 
-w8_status w8_packed_weight_size(w8_fmt fmt, int N, int K, size_t* bytes) {
+w8_status w8_packed_weight_size(w8_fmt fmt, int N, int K, int layout, size_t* bytes) {
   w8_status st = check_gemm_shape(fmt, 1, N, K);
   if (st) return st;
   if (!bytes) return fail(W8_E_INVALID, "null output pointer");
-  *bytes = packed_weight_bytes(fmt, N, K);
+  if (layout != 1 && layout != 2 && layout != 4 && layout != 8)
+    return fail(W8_E_INVALID, "packed layout must be 1, 2, 4 or 8");
+  *bytes = packed_weight_bytes(fmt, N, K, layout);
   return ok();
 }
 
 w8_status w8_pack_weight(w8_fmt fmt, int N, int K, const void* wq, int64_t ldw, void* wp,
-                         w8_stream stream) {
+                         int layout, w8_stream stream) {
   w8_status st = check_gemm_shape(fmt, 1, N, K);
   if (st) return st;
+  if (layout != 1 && layout != 2 && layout != 4 && layout != 8)
+    return fail(W8_E_INVALID, "packed layout must be 1, 2, 4 or 8");
   if (!wq || !wp) return fail(W8_E_INVALID, "null device pointer");
   if (!aligned(wq, 16) || !aligned(wp, 16) || ldw < K || ldw % 16)
     return fail(W8_E_INVALID, "wq and wp must be 16-byte aligned, ldw >= K and ldw % 16 == 0");
   st = check_device();
   if (st) return st;
   hipError_t e = launch_pack_weight(fmt, static_cast<const uint8_t*>(wq), ldw, N, K,
-                                    static_cast<uint8_t*>(wp), static_cast<hipStream_t>(stream));
+                                    static_cast<uint8_t*>(wp), layout,
+                                    static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(W8_E_HIP, hip_msg("pack_weight launch", e));
   return ok();
 }
@@ -503,15 +595,17 @@ w8_status w8_gemm_w8a8_noalloc(w8_fmt fmt, int M, int N, int K, const void* xq, 
                                void* y, int64_t ldy, const w8_cfg* cfg, w8_stream stream) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
+  const int layout = layout_from_ldw(ldw);
+  if (layout < 0) return fail(W8_E_INVALID, "ldw must be > 0, 0, -2, -4 or -8");
   w8_cfg c;
   if (cfg) {
     c = *cfg;
-    st = check_cfg(fmt, W8_OP_GEMM, M, N, K, c);
+    st = check_cfg(fmt, W8_OP_GEMM, M, N, K, c, layout);
     if (st) return st;
   } else {
-    c = resolve_cfg(fmt, W8_OP_GEMM, M, N, K, ldw == 0, nullptr);
+    c = resolve_cfg(fmt, W8_OP_GEMM, M, N, K, layout, nullptr);
   }
-  const size_t need = workspace_bytes(fmt, W8_OP_GEMM, M, N, K, c);
+  const size_t need = workspace_bytes(fmt, W8_OP_GEMM, M, N, K, c, layout);
   if (need > kScratchBytes)
     return fail(W8_E_WORKSPACE, "the config needs " + std::to_string(need) +
                                     " bytes of workspace; the no-allocation entry point has " +
@@ -546,20 +640,21 @@ w8_status w8_linear(w8_fmt fmt, int M, int N, int K, const void* x, int64_t ldx,
   if (!aligned(x, 16) || ldx % 8 || ldx < K)
     return fail(W8_E_INVALID, "x must be 16-byte aligned with ldx >= K and ldx % 8 == 0");
   if (!aligned(wq, 16)) return fail(W8_E_INVALID, "wq must be 16-byte aligned");
-  const int packed = ldw == 0;
-  if (!packed && (ldw < K || ldw % 16))
-    return fail(W8_E_INVALID, "ldw must be 0 (packed weights) or >= K and a multiple of 16");
+  const int layout = layout_from_ldw(ldw);
+  if (layout < 0 || (!layout && (ldw < K || ldw % 16)))
+    return fail(W8_E_INVALID, "ldw must be >= K and a multiple of 16 (row-major weights), 0 "
+                              "(packed) or -2, -4, -8 (K-segmented packed)");
   if (ldy < N) return fail(W8_E_INVALID, "output leading dimension must be >= N");
   if (!aligned(sw, 4) || !aligned(y, 2)) return fail(W8_E_INVALID, "misaligned sw or y");
   w8_cfg c;
   if (cfg) {
     c = *cfg;
-    st = check_cfg(fmt, W8_OP_LINEAR, M, N, K, c);
+    st = check_cfg(fmt, W8_OP_LINEAR, M, N, K, c, layout);
     if (st) return st;
   } else {
-    c = resolve_cfg(fmt, W8_OP_LINEAR, M, N, K, packed, nullptr);
+    c = resolve_cfg(fmt, W8_OP_LINEAR, M, N, K, layout, nullptr);
   }
-  const size_t need = workspace_bytes(fmt, W8_OP_LINEAR, M, N, K, c);
+  const size_t need = workspace_bytes(fmt, W8_OP_LINEAR, M, N, K, c, layout);
   if (need > 0) {
     if (!ws || ws_bytes < need)
       return fail(W8_E_WORKSPACE, "workspace of " + std::to_string(need) + " bytes needed, got " +
@@ -568,41 +663,44 @@ w8_status w8_linear(w8_fmt fmt, int M, int N, int K, const void* x, int64_t ldx,
   }
   st = check_device();
   if (st) return st;
-  GemmCall g{fmt, M, N, K, nullptr, 0, nullptr, wq, ldw, sw, y, ldy, 0, ws, ws_bytes, packed,
+  GemmCall g{fmt, M, N, K, nullptr, 0, nullptr, wq, ldw, sw, y, ldy, 0, ws, ws_bytes, layout,
              x, ldx};
   st = launch_linear_call(g, c, static_cast<hipStream_t>(stream));
   if (st) return st;
   return ok();
 }
 
-w8_status w8_validate_config(w8_fmt fmt, w8_op op, int M, int N, int K, const w8_cfg* cfg) {
+w8_status w8_validate_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layout,
+                             const w8_cfg* cfg) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!cfg) return fail(W8_E_INVALID, "null cfg");
   if (op == W8_OP_MOE || op == W8_OP_MOE_LINEAR)
     return fail(W8_E_INVALID, "grouped configs: w8_moe_validate_config");
-  st = check_cfg(fmt, op, M, N, K, *cfg);
+  st = check_cfg(fmt, op, M, N, K, *cfg, layout);
   if (st) return st;
   return ok();
 }
 
-w8_status w8_default_config(w8_fmt fmt, w8_op op, int M, int N, int K, w8_cfg* out) {
+w8_status w8_default_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layout, w8_cfg* out) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!out) return fail(W8_E_INVALID, "null output pointer");
   if (op != W8_OP_GEMM && op != W8_OP_LINEAR) return fail(W8_E_INVALID, "unknown op");
-  *out = make_default_cfg(fmt, op, M, N, K);
+  if (!layout_valid(layout)) return fail(W8_E_INVALID, "weight layout must be 0, 1, 2, 4 or 8");
+  *out = make_default_cfg(fmt, op, M, N, K, layout);
   return ok();
 }
 
-w8_status w8_resolve_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed, w8_cfg* out,
+w8_status w8_resolve_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layout, w8_cfg* out,
                             int* from_table) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!out) return fail(W8_E_INVALID, "null output pointer");
   if (op != W8_OP_GEMM && op != W8_OP_LINEAR) return fail(W8_E_INVALID, "unknown op");
+  if (!layout_valid(layout)) return fail(W8_E_INVALID, "weight layout must be 0, 1, 2, 4 or 8");
   int hit = 0;
-  *out = resolve_cfg(fmt, op, M, N, K, packed != 0, &hit);
+  *out = resolve_cfg(fmt, op, M, N, K, layout, &hit);
   if (from_table) *from_table = hit;
   return ok();
 }

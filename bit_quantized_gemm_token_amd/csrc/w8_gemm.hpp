@@ -45,6 +45,19 @@
 //          load instruction reads 1 KiB contiguous and a wave's whole K range
 //          is one contiguous run; rows and K are zero-padded to whole
 //          fragments.  Packed loads are non-temporal (each line is read once).
+//   K-segmented layouts PACKED = T in {2, 4, 8}: one MFMA takes R = 16/T
+//          weight rows times T consecutive K-steps (a "span"): operand index
+//          p = lane % 16 is split as p = t*R + r (K-step t of the span, row
+//          r), and the activation operand likewise as p = t*R + m (token m
+//          of a group of R tokens).  Of the 16 x 16 products only the blocks
+//          with equal t are wanted; they are summed over t at the end.  A
+//          fragment (R rows, one span) is again 16 x KSTEP bytes in lane
+//          order, so the loads are as contiguous as with PACKED=1, but a row
+//          block is R rows instead of 16: at M <= R tokens the same weight
+//          bytes make 16/R times as many output tiles, which spreads a
+//          narrow N over the compute units without splitting K (and without
+//          the split-K hand-off).  The K loop runs over spans; a span that
+//          reaches past K is masked like the ragged K-step.
 //   Swap-AB SWAP=0: A = activations, B = weights^T, C[m][n];
 //          SWAP=1: A = weights, B = activations^T, C[n][m] = (Wq . Xq^T)^T.
 //          The MFMA work is identical (square 16x16 tiles); what changes is
@@ -165,6 +178,13 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
   static_assert(WN == 1 || WK == 1, "the waves of a workgroup split either K or N");
   static_assert(WN == 1 || XL, "waves side by side along N share activations through LDS");
   static_assert(XL != 3 || (BLOCK && WN == 1), "quantization in the K loop: Block_FP8, WN == 1");
+  // K-segmented layouts: T K-steps per MFMA, row blocks of R = 16/T weight
+  // rows, token groups of R rows (T = 1: the plain 16 x 16 tile).
+  constexpr int T = PACKED > 1 ? PACKED : 1;
+  constexpr int R = 16 / T;
+  static_assert(T == 1 || T == 2 || T == 4 || T == 8, "segments per MFMA: 1, 2, 4 or 8");
+  static_assert(T == 1 || (XL == 0 && WN == 1 && SK == 0 && !GROUPED),
+                "K-segmented layouts: plain activation loads, one wave along N, split-K only");
   // activation row (codes and scales, or XL == 2 the bf16 row) of row m of
   // this call
   auto xr = [&](int m) -> long long {
@@ -190,12 +210,16 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wk = wave % WK, wn = wave / WK;
   const int r = lane & 15, g = lane >> 4;
+  // The lane's operand index r = tl*R + mr: K-step tl of the span and row mr
+  // of its block (T = 1: tl = 0, mr = r).
+  const int tl = r / R, mr = r % R;
 
-  // Activation rows of this lane (padding rows of the 16-row MFMA tile read
-  // a clamped valid row; their outputs are never stored).
+  // Activation rows of this lane (padding rows of the MFMA tile read a
+  // clamped valid row; their outputs are never stored).
   const uint8_t* xrow[MB];
 #pragma unroll
-  for (int b = 0; b < MB; ++b) xrow[b] = a.xq + xr(min(16 * b + r, a.M - 1)) * a.ldq + 16 * g;
+  for (int b = 0; b < MB; ++b)
+    xrow[b] = a.xq + xr(min(R * b + mr, a.M - 1)) * a.ldq + tl * KSTEP + 16 * g;
   // XL == 3: the lane's bf16 activations (row stride ldq in elements), the
   // same 2 x 16 elements of each K-step whose codes it feeds to the MFMA.
   const uint16_t* xrow16[MB];
@@ -215,6 +239,9 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
   // formats, per (staged group, row) for Block_FP8.
   __shared__ float sxl[XL == 2 ? (BLOCK ? kXlMaxGroups * 32 : 32) : 1];
   __shared__ int is_last;
+  // K-segmented layouts: the wave's accumulator tiles for the epilogue's
+  // sums over t (WN == 1: one region).
+  __shared__ Acc dgl[T > 1 ? NB * MB * 64 : 1];
 
   if constexpr (XL == 2 && !BLOCK) {
     // Row absolute maxima (float bits), folded in by the first segment.
@@ -230,7 +257,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
   for (int b = 0; b < MB; ++b)
 #pragma unroll
     for (int i = 0; i < SXN; ++i) {
-      const int m = min(SWAP ? 16 * b + r : 16 * b + 4 * g + i, a.M - 1);
+      const int m = min(SWAP ? R * b + mr : R * b + (4 * g + i) % R, a.M - 1);
       sxm[b][i] = m;
       if constexpr (BLOCK) {
         sxrow[b][i] = XL >= 2 ? nullptr : a.sx + xr(m) * a.sgroups;
@@ -280,17 +307,25 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
     rows_done = true;
   };
 
-  // One segment: K-steps [ka, kb) of output tile `tile` (WN*NB blocks of 16
-  // weight rows).  The segment is contributor `slot` of the `count`
-  // workgroups that cover the tile; count == 1 writes Y directly.
+  // K-segmented layouts: the wave's NB x MB blocks give NB*MB*R*R outputs,
+  // dealt to the lanes OPL at a time in the epilogue: output o = lane + 64q
+  // is (block j, token group b, token m, row rr) with rr varying fastest, so
+  // neighbouring lanes store neighbouring columns of Y.
+  constexpr int NOUT = NB * MB * R * R;
+  constexpr int OPL = T > 1 ? (NOUT + 63) / 64 : 1;
+
+  // One segment: K-steps [ka, kb) (spans for the K-segmented layouts) of
+  // output tile `tile` (WN*NB blocks of 16, or R, weight rows).  The segment
+  // is contributor `slot` of the `count` workgroups that cover the tile;
+  // count == 1 writes Y directly.
   auto segment = [&](int tile, int ka, int kb, int slot, int count) {
-    const int n0 = (tile * WN + wn) * 16 * NB;  // first weight row of this wave
+    const int n0 = (tile * WN + wn) * R * NB;  // first weight row of this wave
 
     const uint8_t* wptr[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if constexpr (PACKED) {
-        const int nb = min((tile * WN + wn) * NB + j, (a.N + 15) / 16 - 1);
+        const int nb = min((tile * WN + wn) * NB + j, (a.N + R - 1) / R - 1);
         wptr[j] = a.wq + (long long)nb * a.ksteps * (16 * KSTEP) + 16 * lane;
       } else {
         wptr[j] = a.wq + (long long)min(n0 + 16 * j + r, a.N - 1) * a.ldw + 16 * g;
@@ -302,16 +337,25 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
       else
         return load_frag<FMT>(wptr[j], kk);
     };
-    // Block_FP8 sw row of the wave's 128-row block (its 16*NB rows never
+    // Block_FP8 sw row of the wave's 128-row block (its R*NB rows never
     // straddle two blocks); the per-token formats' epilogue sw.
     const float* swrow = nullptr;
     float ep_sw[NB][4 / SXN];
+    float ep2_sw[OPL], ep2_sx[OPL];  // K-segmented layouts: per output of the lane
     if constexpr (BLOCK) swrow = a.sw + (long long)(min(n0, a.N - 1) / kGroup) * a.sgroups;
     // The per-token formats' epilogue scales, issued after the first weight
     // stages: vector-memory loads complete in issue order, so a scale load
     // issued first would hold up the first MFMA behind its own latency.
     auto load_epilogue_scales = [&]() {
-      if constexpr (!BLOCK) {
+      if constexpr (!BLOCK && T > 1) {
+#pragma unroll
+        for (int q = 0; q < OPL; ++q) {
+          const int o = min(lane + 64 * q, NOUT - 1);
+          const int jb = o / (R * R), m = (o / R) % R, rr = o % R;
+          ep2_sw[q] = a.sw[min(n0 + R * (jb / MB) + rr, a.N - 1)];
+          ep2_sx[q] = a.sx[xr(min(R * (jb % MB) + m, a.M - 1))];
+        }
+      } else if constexpr (!BLOCK) {
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -355,9 +399,9 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
         const int k = max(k0 + u, la);
 #pragma unroll
         for (int j = 0; j < NB; ++j) st.w[u][j] = load_w(j, k);
-        if constexpr (!XL) {
+        if constexpr (!XL) {  // (K-segmented: span k starts at K-step k*T)
 #pragma unroll
-          for (int b = 0; b < MB; ++b) st.x[u][b] = load_frag<FMT>(xrow[b], k);
+          for (int b = 0; b < MB; ++b) st.x[u][b] = load_frag<FMT>(xrow[b], k * T);
         }
         if constexpr (XL == 3) {
 #pragma unroll
@@ -370,12 +414,15 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
             }
         }
         if constexpr (BLOCK) {
-          st.sw[u] = swrow[k];
+          // group of the lane's own K-step (K-segmented: the group of the
+          // products the lane keeps, K-step k*T + tl)
+          const int kg = k * T + tl;
+          st.sw[u] = swrow[kg];
           if constexpr (XL < 2) {  // XL >= 2: scales computed here (LDS or registers)
 #pragma unroll
             for (int b = 0; b < MB; ++b)
 #pragma unroll
-              for (int i = 0; i < SXN; ++i) st.sx[u][b][i] = sxrow[b][i][k];
+              for (int i = 0; i < SXN; ++i) st.sx[u][b][i] = sxrow[b][i][kg];
           }
         }
       }
@@ -588,12 +635,24 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
         run_stage(B, k0 + s * U, whole);
       }
     }
-    // The ragged K tail (K % KSTEP != 0; never for Block_FP8, whose K is a
-    // multiple of its 128-byte K-step) belongs to the wave that owns step
-    // kfull.  Packed weights are zero-padded there; activations are masked.
-    if constexpr (!BLOCK) {
+    // The ragged K tail (K % KSTEP != 0; for the K-segmented layouts, a
+    // span reaching past K) belongs to the wave that owns step (span) kfull.
+    // Packed weights are zero-padded there; activations are masked by byte.
+    // (Block_FP8's K is a multiple of its 128-byte K-step: only a span can
+    // reach past K; its groups past K have zero codes, and their scale reads
+    // are clamped to the last group.)
+    if constexpr (!BLOCK || T > 1) {
       if (lb > a.kfull && la < lb) {
         Frag wt[NB], xt[MB];
+        float tsw = 0.0f, tsx[MB][SXN] = {};
+        if constexpr (BLOCK) {
+          const int kg = min(a.kfull * T + tl, a.sgroups - 1);
+          tsw = swrow[kg];
+#pragma unroll
+          for (int b = 0; b < MB; ++b)
+#pragma unroll
+            for (int i = 0; i < SXN; ++i) tsx[b][i] = sxrow[b][i][kg];
+        }
 #pragma unroll
         for (int j = 0; j < NB; ++j)
           wt[j] = PACKED ? load_w(j, a.kfull) : load_frag_tail<FMT>(wptr[j], a.kfull, 16 * g, a.K);
@@ -609,11 +668,10 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
               xt[b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
           } else {
-            xt[b] = load_frag_tail<FMT>(xrow[b], a.kfull, 16 * g, a.K);
+            xt[b] = load_frag_tail<FMT>(xrow[b], a.kfull * T, tl * KSTEP + 16 * g, a.K);
           }
         }
-        const float no_sx[MB][SXN] = {};
-        step(wt, xt, 0.0f, no_sx);
+        step(wt, xt, tsw, tsx);
       }
     }
 
@@ -724,6 +782,51 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
       }
     }
     if (!store || wk != 0) return;
+
+    if constexpr (T > 1) {
+      // K-segmented epilogue: the wave writes its 16 x 16 tiles to LDS as
+      // [block][column][row] and each output sums its T wanted products in
+      // t order: SWAP = 1, rows are weight rows (t, rr), columns tokens
+      // (t, m); SWAP = 0 the other way round.  (The LDS region is the
+      // wave's own and a wave's LDS accesses complete in order; the signal
+      // fences keep the compiler from moving the reads above the writes.)
+      typedef decltype(acc[0][0][0]) Elem;
+      typedef typename std::remove_cv<typename std::remove_reference<Elem>::type>::type Word;
+      Word* d = reinterpret_cast<Word*>(dgl);
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+          *reinterpret_cast<Acc*>(d + ((j * MB + b) * 16 + r) * 16 + 4 * g) = acc[b][j];
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+      for (int q = 0; q < OPL; ++q) {
+        const int o = lane + 64 * q;
+        if (o < NOUT) {
+          const int jb = o / (R * R), m = (o / R) % R, rr = o % R;
+          Word v = 0;
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+            v += SWAP ? d[(jb * 16 + t * R + m) * 16 + t * R + rr]
+                      : d[(jb * 16 + t * R + rr) * 16 + t * R + m];
+          const int mm = R * (jb % MB) + m, n = n0 + R * (jb / MB) + rr;
+          if (mm < a.M && n < a.N) {
+            const long long off = (long long)mm * a.ldo + n;
+            if (a.out_mode) {
+              reinterpret_cast<Word*>(a.out)[off] = v;
+            } else {
+              float y;
+              if constexpr (BLOCK)
+                y = v;
+              else
+                y = (float)v * ep2_sx[q] * ep2_sw[q];
+              reinterpret_cast<uint16_t*>(a.out)[off] = bf16_rne(y);
+            }
+          }
+        }
+      }
+      return;
+    }
 
     // Epilogue.
 #pragma unroll
@@ -875,24 +978,29 @@ hipError_t launch_moe_gemm(const GemmArgs& a, const MoeArgs& m, dim3 grid, dim3 
 }
 
 // Packs row-major codes [N, K] (row stride ldw) into the MFMA-native layout
-// (see the kernel header): one thread per 16-byte chunk, zero padding for
-// rows >= N and bytes >= K.
-template <int KSTEP>
+// with T K-steps per MFMA (see the kernel header; T = 1 is the plain packed
+// layout): one thread per 16-byte chunk, zero padding for rows >= N and bytes
+// >= K.  Fragment f = (row block of R = 16/T rows, span of T K-steps) holds
+// 16 x KSTEP bytes; its chunk (instruction jj, lane l) is the 16 bytes that
+// lane l loads: row r = (l % 16) % R of the block, K-step t = (l % 16) / R of
+// the span, bytes 64*jj + 16*(l / 16) of that K-step.
+template <int KSTEP, int T>
 __global__ __launch_bounds__(256) void pack_weight_kernel(const uint8_t* __restrict__ w,
                                                           long long ldw, int N, int K,
-                                                          int ksteps, uint8_t* __restrict__ out,
+                                                          int spans, uint8_t* __restrict__ out,
                                                           long long chunks) {
+  constexpr int R = 16 / T;
   const long long c = blockIdx.x * 256LL + threadIdx.x;
   if (c >= chunks) return;
-  // chunk c: fragment f = c / (KSTEP), within it instruction jj and lane l
   constexpr int CHUNKS_PER_FRAG = 16 * KSTEP / 16;  // = KSTEP
   const long long f = c / CHUNKS_PER_FRAG;
   const int within = (int)(c % CHUNKS_PER_FRAG);
   const int jj = within / 64, l = within % 64;
-  const long long nb = f / ksteps;
-  const int kk = (int)(f % ksteps);
-  const long long row = nb * 16 + (l & 15);
-  const long long k = (long long)kk * KSTEP + 64 * jj + 16 * (l >> 4);
+  const long long nb = f / spans;
+  const int sp = (int)(f % spans);
+  const int p = l & 15;
+  const long long row = nb * R + p % R;
+  const long long k = (long long)(sp * T + p / R) * KSTEP + 64 * jj + 16 * (l >> 4);
   // (K % 16 == 0, so a chunk is either wholly inside K or wholly outside.)
   v4i v = {0, 0, 0, 0};
   if (row < N && k < K) v = *reinterpret_cast<const v4i*>(w + row * ldw + k);

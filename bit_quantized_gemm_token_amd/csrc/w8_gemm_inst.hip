@@ -1,7 +1,8 @@
 // Explicit instances of the GEMM family for one format, one Swap-AB setting
 // and one part: W8_PART 0 and 1 are the GEMM instances with MB = 1 and 2,
 // 2 and 3 the MoE grouped instances with MB = 1 and 2, 4 and 5 the Block_FP8
-// linear op's instances that quantize in the K loop (XL 3) with MB = 1 and 2.  The
+// linear op's instances that quantize in the K loop (XL 3) with MB = 1 and 2,
+// 6 and 7 the K-segmented layouts' instances with MB = 1 and 2.  The
 // build compiles this file once per (W8_FMT, W8_SWAP, W8_PART) so the
 // instances compile in parallel.
 #include "w8_gemm.hpp"
@@ -43,6 +44,16 @@
   W8_U(MB, 1, 1, 2) W8_U(MB, 2, 1, 2) W8_U(MB, 4, 1, 2) W8_U(MB, 1, 2, 2)             \
   W8_U(MB, 1, 4, 2) W8_U(MB, 1, 8, 2)
 
+// The K-segmented layouts (PACKED = T in {2, 4, 8}): WN 1, XL 0, SK 0, and
+// (NB, WK, UNROLL) in the set below (single blocks with every K-wave count,
+// and two blocks with few K-waves).
+#define W8_ST(MB, T)                                                                            \
+  W8_I(MB, 1, 1, 1, 2, T, 0, 0) W8_I(MB, 1, 1, 1, 4, T, 0, 0) W8_I(MB, 1, 2, 1, 1, T, 0, 0)    \
+  W8_I(MB, 1, 2, 1, 2, T, 0, 0) W8_I(MB, 1, 4, 1, 1, T, 0, 0) W8_I(MB, 1, 4, 1, 2, T, 0, 0)    \
+  W8_I(MB, 1, 8, 1, 1, T, 0, 0) W8_I(MB, 1, 16, 1, 1, T, 0, 0) W8_I(MB, 2, 1, 1, 2, T, 0, 0)   \
+  W8_I(MB, 2, 2, 1, 1, T, 0, 0) W8_I(MB, 2, 4, 1, 1, T, 0, 0)
+#define W8_S(MB) W8_ST(MB, 2) W8_ST(MB, 4) W8_ST(MB, 8)
+
 // Block_FP8's linear op quantizing in the K loop (XL 3): WN 1, WK in {2, 4,
 // 8}, tile_n 16 or 32, UNROLL 1 (the shapes it wins on; the bf16
 // activations of a stage double its activation registers).  Parts 4 and 5
@@ -71,13 +82,15 @@
 
 namespace w8 {
 
-#if W8_PART > 3 && W8_FMT != 2
+#if (W8_PART == 4 || W8_PART == 5) && W8_FMT != 2
 #error "parts 4 and 5 exist for Block_FP8 only"
 #elif W8_PART < 2 || W8_PART > 3
 #if W8_PART < 2
 static const GemmInstance kInstances[] = {W8_W(W8_MB)};
-#else
+#elif W8_PART < 6
 static const GemmInstance kInstances[] = {W8_W3(W8_MB)};
+#else
+static const GemmInstance kInstances[] = {W8_S(W8_MB)};
 #endif
 
 const GemmInstance* W8_CAT(gemm_instances_f, W8_FMT, W8_SWAP, W8_PART)(int* count) {

@@ -21,17 +21,22 @@ int fmt_from_name(const std::string& s);  // -1 if unknown
 
 // Shape checks shared by the GEMM, the quantizer and the tuner.
 w8_status check_gemm_shape(int fmt, int M, int N, int K);
-// Config checks (shape-independent and shape-dependent) for operation op.
-w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c);
-w8_cfg make_default_cfg(int fmt, int op, int M, int N, int K);
-size_t workspace_bytes(int fmt, int op, int M, int N, int K, const w8_cfg& c);
+// Config checks (shape-independent and shape-dependent) for operation op on
+// weights of layout `layout` (0 row-major; 1, 2, 4, 8 packed with that many
+// K-steps per MFMA).
+w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c, int layout);
+w8_cfg make_default_cfg(int fmt, int op, int M, int N, int K, int layout);
+size_t workspace_bytes(int fmt, int op, int M, int N, int K, const w8_cfg& c, int layout);
+// The layout of a GEMM call's ldw (-1 if invalid): > 0 row-major, 0 (or -1)
+// plain packed, -2/-4/-8 K-segmented packed.
+int layout_from_ldw(long long ldw);
 // Workspace regions of the linear op with quant_launch == 1 (byte offsets):
 // the GEMM's part at 0, the activation codes (row stride ldq) and scales.
 struct LinearWs {
   size_t codes, scales, total;
   long long ldq;
 };
-LinearWs linear_ws(int fmt, int M, int N, int K, const w8_cfg& c);
+LinearWs linear_ws(int fmt, int M, int N, int K, const w8_cfg& c, int layout);
 int tiles_of(int N, const w8_cfg& c);                       // output tiles along N
 int partial_slots(int fmt, int N, int K, const w8_cfg& c);  // workspace slots per tile
 int ksteps_of(int fmt, int K);
@@ -39,18 +44,18 @@ int ksteps_of(int fmt, int K);
 // Resolve cfg == NULL: the table entry for the shape (*from_table = 1), else
 // one for the same N, K and an M of the same floor(log2 M) bucket that is
 // valid for this M (2), else the cost model's pick (0).
-w8_cfg resolve_cfg(int fmt, int op, int M, int N, int K, int packed, int* from_table);
+w8_cfg resolve_cfg(int fmt, int op, int M, int N, int K, int layout, int* from_table);
 
 // The config family's feasible set for the tuner (its pruning rules, and for
 // the linear op the quantize-launch variants), the cost model's predicted
 // time per call of a config, the set ranked by it (ascending), and the
 // model's top-1 pick.
-std::vector<w8_cfg> enumerate_configs(int fmt, int op, int M, int N, int K, int packed,
+std::vector<w8_cfg> enumerate_configs(int fmt, int op, int M, int N, int K, int layout,
                                       int max_split_k, int stream_k, bool prune_waves = true);
-double predict_us(int fmt, int op, int M, int N, int K, const w8_cfg& c);
+double predict_us(int fmt, int op, int M, int N, int K, const w8_cfg& c, int layout);
 std::vector<std::pair<double, w8_cfg>> rank_configs(int fmt, int op, int M, int N, int K,
-                                                    int packed, int max_split_k, int stream_k);
-w8_cfg model_cfg(int fmt, int op, int M, int N, int K, int packed);
+                                                    int layout, int max_split_k, int stream_k);
+w8_cfg model_cfg(int fmt, int op, int M, int N, int K, int layout);
 
 // The device must be gfx950 (checked once per device).
 w8_status check_device();
@@ -69,7 +74,7 @@ struct GemmCall {
   int out_mode;
   void* ws;
   size_t ws_bytes;
-  int packed;         // weights in the packed (MFMA-native) layout
+  int layout;         // weight layout: 0 row-major, 1/2/4/8 packed
   const void* x;      // fused quantization (w8_linear): bf16 activations, else null
   long long ldx;
 };

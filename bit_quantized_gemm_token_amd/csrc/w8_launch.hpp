@@ -88,12 +88,29 @@ struct MoeInstance {
   MoeLaunchFn fn;
 };
 
-// Packs row-major weight codes into the MFMA-native layout of fmt.
+// Weight layouts: 0 row-major; T in {1, 2, 4, 8} the packed layout with T
+// K-steps per MFMA (1: blocks of 16 rows, the plain packed layout; 2, 4, 8:
+// K-segmented, blocks of 16/T rows).
+inline bool layout_valid(int layout) {
+  return layout == 0 || layout == 1 || layout == 2 || layout == 4 || layout == 8;
+}
+inline int layout_segments(int layout) { return layout > 1 ? layout : 1; }
+// Weight rows per block of the layout (row-major: the 16 of an MFMA).
+inline int layout_rows(int layout) { return 16 / layout_segments(layout); }
+
+// Packs row-major weight codes into packed layout `layout` (1, 2, 4 or 8).
 hipError_t launch_pack_weight(int fmt, const uint8_t* w, long long ldw, int N, int K,
-                              uint8_t* out, hipStream_t s);
-inline size_t packed_weight_bytes(int fmt, int N, int K) {
+                              uint8_t* out, int layout, hipStream_t s);
+// Spans (K-steps per MFMA of the layout) that cover K.
+inline int layout_spans(int fmt, int K, int layout) {
   const int kstep = fmt == 1 ? 64 : 128;
-  return (size_t)((N + 15) / 16) * ((K + kstep - 1) / kstep) * 16 * kstep;
+  const int T = layout_segments(layout);
+  return ((K + kstep - 1) / kstep + T - 1) / T;
+}
+inline size_t packed_weight_bytes(int fmt, int N, int K, int layout) {
+  const int kstep = fmt == 1 ? 64 : 128;
+  const int R = layout_rows(layout);
+  return (size_t)((N + R - 1) / R) * layout_spans(fmt, K, layout) * 16 * kstep;
 }
 
 // Every compiled instance, gathered from the per-format translation units.

@@ -6,7 +6,8 @@
 //
 // The model predicts the time of one call from the quantities that bound
 // this kernel on MI355X, with constants fitted to the tuner's measured
-// timings (fit_model.py beside this package):
+// timings (fit_model.py beside this package fits them through
+// w8_predict_us, so the fit and the library evaluate one model):
 //   - a fixed cost per launch (graph-replayed kernel start and drain);
 //   - the busiest compute unit's bytes through its vector memory path, at a
 //     rate set by Little's law -- the bytes its resident waves keep in
@@ -23,6 +24,7 @@
 #include <cmath>
 #include <cstring>
 #include <map>
+#include <string>
 #include <mutex>
 #include <tuple>
 #include <vector>
@@ -33,8 +35,9 @@ namespace w8 {
 
 namespace {
 
-// Fitted constants (us, bytes/us).  fit_model.py prints these from a dump
-// of measured candidate timings.
+// Fitted constants (us, bytes/us), in this order in w8_predict_us's
+// params.  fit_model.py prints these from a dump of measured candidate
+// timings.
 struct ModelParams {
   double t0;          // fixed cost per launch
   double cu_bw;       // per-CU vector-memory peak
@@ -53,16 +56,26 @@ struct ModelParams {
 
 constexpr ModelParams kParams = {1.6537, 56705.2, 1.0003, 4.54169e6, 2.608, 1.2018, 1.5197,
                                  0.43, 0.1419, 0.0146, 0.051, 0.225973, 20816.5};
+constexpr int kParamCount = (int)(sizeof(ModelParams) / sizeof(double));
+static_assert(kParamCount == 13, "w8_predict_us documents 13 constants");
 
 int kstep_bytes(int fmt) { return fmt == W8_W8A8_INT8 ? 64 : 128; }
 
-}  // namespace
-
-double predict_us(int fmt, int op, int M, int N, int K, const w8_cfg& c) {
-  const ModelParams& p = kParams;
-  const int T = ksteps_of(fmt, K);
+double predict_with(const ModelParams& p, int fmt, int op, int M, int N, int K, const w8_cfg& c,
+                    int layout) {
+  // The K-segmented layouts fit the same terms: a K-loop step is a span of
+  // layout K-steps, a block R = 16/layout weight rows (still one fragment of
+  // 16 x K-step bytes per load), and M runs as launches of at most 2R rows.
+  const int R = layout_rows(layout);
+  const int launches = (M + 2 * R - 1) / (2 * R);
+  if (launches > 1) {
+    const int rows = 2 * R, last = M - (launches - 1) * rows;
+    return (launches - 1) * predict_with(p, fmt, op, rows, N, K, c, layout) +
+           predict_with(p, fmt, op, last, N, K, c, layout);
+  }
+  const int T = layout_spans(fmt, K, layout);
   const double KS = kstep_bytes(fmt);
-  const int MB = (M + 15) / 16, NB = c.tile_n / 16, W = c.waves_k * c.waves_n;
+  const int MB = (M + R - 1) / R, NB = c.tile_n / R, W = c.waves_k * c.waves_n;
   const long long ntiles = tiles_of(N, c);
   const long long G = c.grid > 0 ? c.grid : ntiles * c.split_k;
   const double seg = c.grid > 0 ? std::ceil((double)ntiles * T / c.grid)
@@ -98,12 +111,18 @@ double predict_us(int fmt, int op, int M, int N, int K, const w8_cfg& c) {
   return t;
 }
 
-std::vector<w8_cfg> enumerate_configs(int fmt, int op, int M, int N, int K, int packed,
+}  // namespace
+
+double predict_us(int fmt, int op, int M, int N, int K, const w8_cfg& c, int layout) {
+  return predict_with(kParams, fmt, op, M, N, K, c, layout);
+}
+
+std::vector<w8_cfg> enumerate_configs(int fmt, int op, int M, int N, int K, int layout,
                                       int max_split_k, int stream_k, bool prune_waves) {
-  (void)packed;
-  const int T = ksteps_of(fmt, K);
+  const int T = layout_spans(fmt, K, layout);
+  const int R = layout_rows(layout);
   const long long wbytes = (long long)N * ((K + 15) / 16 * 16);
-  const int tiles_n[] = {16, 32, 64};
+  const int tiles_n[] = {R, 2 * R, 4 * R};
   // (waves_k, waves_n, x_lds)
   const int wave_shapes[][3] = {{1, 1, 0}, {2, 1, 0}, {4, 1, 0}, {8, 1, 0}, {16, 1, 0},
                                 {1, 1, 1}, {2, 1, 1}, {4, 1, 1}, {8, 1, 1},
@@ -117,12 +136,12 @@ std::vector<w8_cfg> enumerate_configs(int fmt, int op, int M, int N, int K, int 
   std::vector<w8_cfg> all;
   long long most_waves = 0;
   auto consider = [&](const w8_cfg& c) {
-    if (check_cfg(fmt, op, M, N, K, c) != W8_OK) return;
+    if (check_cfg(fmt, op, M, N, K, c, layout) != W8_OK) return;
     const long long per_wave = c.grid > 0 ? (long long)tiles_of(N, c) * T / (c.grid * c.waves_k)
                                           : (long long)T / (c.split_k * c.waves_k);
     if (per_wave < 1) return;
     if (c.unroll > 1 && per_wave < c.unroll) return;
-    if ((long long)workspace_bytes(fmt, op, M, N, K, c) >
+    if ((long long)workspace_bytes(fmt, op, M, N, K, c, layout) >
         2 * wbytes + (long long)ws_counter_bytes(0))
       return;
     all.push_back(c);
@@ -162,11 +181,11 @@ std::vector<w8_cfg> enumerate_configs(int fmt, int op, int M, int N, int K, int 
   // entry when the GEMM was tuned first) and with the GEMM's default.
   if (op == W8_OP_LINEAR) {
     int hit = 0;
-    std::vector<w8_cfg> gemm_cfgs = {resolve_cfg(fmt, W8_OP_GEMM, M, N, K, packed, &hit)};
-    gemm_cfgs.push_back(make_default_cfg(fmt, W8_OP_GEMM, M, N, K));
+    std::vector<w8_cfg> gemm_cfgs = {resolve_cfg(fmt, W8_OP_GEMM, M, N, K, layout, &hit)};
+    gemm_cfgs.push_back(make_default_cfg(fmt, W8_OP_GEMM, M, N, K, layout));
     for (w8_cfg c : gemm_cfgs) {
       c.quant_launch = 1;
-      if (check_cfg(fmt, op, M, N, K, c) != W8_OK) continue;
+      if (check_cfg(fmt, op, M, N, K, c, layout) != W8_OK) continue;
       bool dup = false;
       for (const w8_cfg& e : out) dup = dup || std::memcmp(&e, &c, sizeof c) == 0;
       if (!dup) out.push_back(c);
@@ -176,10 +195,10 @@ std::vector<w8_cfg> enumerate_configs(int fmt, int op, int M, int N, int K, int 
 }
 
 std::vector<std::pair<double, w8_cfg>> rank_configs(int fmt, int op, int M, int N, int K,
-                                                    int packed, int max_split_k, int stream_k) {
+                                                    int layout, int max_split_k, int stream_k) {
   std::vector<std::pair<double, w8_cfg>> r;
-  for (const w8_cfg& c : enumerate_configs(fmt, op, M, N, K, packed, max_split_k, stream_k))
-    r.emplace_back(predict_us(fmt, op, M, N, K, c), c);
+  for (const w8_cfg& c : enumerate_configs(fmt, op, M, N, K, layout, max_split_k, stream_k))
+    r.emplace_back(predict_us(fmt, op, M, N, K, c, layout), c);
   // stable: equal predictions keep enumeration order
   std::stable_sort(r.begin(), r.end(),
                    [](const auto& a, const auto& b) { return a.first < b.first; });
@@ -188,17 +207,17 @@ std::vector<std::pair<double, w8_cfg>> rank_configs(int fmt, int op, int M, int 
 
 // The GEMM's picks are memoized per shape (they depend on nothing else); the
 // linear op's depend on the table's GEMM entry, so they are recomputed.
-w8_cfg model_cfg(int fmt, int op, int M, int N, int K, int packed) {
+w8_cfg model_cfg(int fmt, int op, int M, int N, int K, int layout) {
   static std::mutex mu;
   static std::map<std::tuple<int, int, int, int, int>, w8_cfg> memo;
-  const auto key = std::make_tuple(fmt, packed, M, N, K);
+  const auto key = std::make_tuple(fmt, layout, M, N, K);
   if (op == W8_OP_GEMM) {
     std::lock_guard<std::mutex> lk(mu);
     auto it = memo.find(key);
     if (it != memo.end()) return it->second;
   }
-  const auto r = rank_configs(fmt, op, M, N, K, packed, W8_MAX_SPLIT_K, 0);
-  const w8_cfg c = r.empty() ? make_default_cfg(fmt, op, M, N, K) : r.front().second;
+  const auto r = rank_configs(fmt, op, M, N, K, layout, W8_MAX_SPLIT_K, 0);
+  const w8_cfg c = r.empty() ? make_default_cfg(fmt, op, M, N, K, layout) : r.front().second;
   if (op == W8_OP_GEMM) {
     std::lock_guard<std::mutex> lk(mu);
     memo[key] = c;
@@ -208,12 +227,37 @@ w8_cfg model_cfg(int fmt, int op, int M, int N, int K, int packed) {
 
 }  // namespace w8
 
-extern "C" w8_status w8_model_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed,
+extern "C" w8_status w8_predict_us(int n, const int* fmt, const int* op, const int* layout,
+                                   const int* M, const int* N, const int* K, const w8_cfg* cfgs,
+                                   const double* params, int nparams, double* us) {
+  if (n < 0 || (n > 0 && (!fmt || !op || !layout || !M || !N || !K || !cfgs || !us)))
+    return w8::fail(W8_E_INVALID, "bad arguments");
+  w8::ModelParams p = w8::kParams;
+  if (params) {
+    if (nparams != w8::kParamCount)
+      return w8::fail(W8_E_INVALID, "params must hold the model's 13 constants");
+    std::memcpy(&p, params, sizeof p);
+  }
+  for (int i = 0; i < n; ++i) {
+    const w8_cfg& c = cfgs[i];
+    // what the arithmetic divides by or indexes with
+    if (fmt[i] < 0 || fmt[i] > 2 || M[i] < 1 || N[i] < 1 || K[i] < 1 ||
+        !w8::layout_valid(layout[i]) || c.tile_n < 1 || c.waves_k < 1 || c.waves_n < 1 ||
+        c.unroll < 1 || c.split_k < 1 || c.grid < 0)
+      return w8::fail(W8_E_INVALID, "row " + std::to_string(i) + ": bad shape, layout or config");
+    us[i] = w8::predict_with(p, fmt[i], op[i], M[i], N[i], K[i], c, layout[i]);
+  }
+  return w8::ok();
+}
+
+extern "C" w8_status w8_model_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layout,
                                      w8_cfg* out) {
   w8_status st = w8::check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!out) return w8::fail(W8_E_INVALID, "null output pointer");
   if (op != W8_OP_GEMM && op != W8_OP_LINEAR) return w8::fail(W8_E_INVALID, "unknown op");
-  *out = w8::model_cfg(fmt, op, M, N, K, packed ? 1 : 0);
+  if (!w8::layout_valid(layout))
+    return w8::fail(W8_E_INVALID, "weight layout must be 0, 1, 2, 4 or 8");
+  *out = w8::model_cfg(fmt, op, M, N, K, layout);
   return w8::ok();
 }

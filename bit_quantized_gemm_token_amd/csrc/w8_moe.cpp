@@ -87,7 +87,9 @@ size_t shared_ws_bytes(int fmt, int E, int max_m, int N, int K, const w8_cfg& c)
 // whose shared tiles fit the counter region.
 w8_status check_moe_cfg(int fmt, int E, int max_m, int N, int K, int packed, const w8_cfg& c,
                         bool fused) {
-  w8_status st = check_cfg(fmt, fused ? W8_OP_MOE_LINEAR : W8_OP_GEMM, max_m, N, K, c);
+  if (packed != 0 && packed != 1)
+    return fail(W8_E_INVALID, "the grouped GEMM runs on row-major and plain packed weights");
+  w8_status st = check_cfg(fmt, fused ? W8_OP_MOE_LINEAR : W8_OP_GEMM, max_m, N, K, c, packed);
   if (st) return st;
   const bool in_kernel = fused && !c.quant_launch;
   if (!moe_fn(fmt, max_m, packed, c, in_kernel))
@@ -203,7 +205,7 @@ w8_status moe_entry(MoeCall call, const w8_cfg* cfg, bool fused, w8_stream strea
   if (!aligned(call.wq, 16) || call.w_stride % 16)
     return fail(W8_E_INVALID, "wq and w_stride must be 16-byte aligned");
   if (packed) {
-    if (call.w_stride < (long long)packed_weight_bytes(fmt, N, K))
+    if (call.w_stride < (long long)packed_weight_bytes(fmt, N, K, 1))
       return fail(W8_E_INVALID, "w_stride below one expert's packed weights");
   } else {
     if (call.ldw < K || call.ldw % 16)

@@ -1,6 +1,6 @@
 // Gathers the GEMM instances compiled in the per-(format, swap, part)
-// translation units into one table (parts 0, 1 and, for Block_FP8, 4, 5:
-// GEMM; 2, 3: MoE).
+// translation units into one table (parts 0, 1, 6, 7 and, for Block_FP8, 4,
+// 5: GEMM; 2, 3: MoE).
 #include <vector>
 
 #include "w8_launch.hpp"
@@ -11,7 +11,9 @@ namespace w8 {
   const GemmInstance* gemm_instances_f##F##_##S##_0(int*); \
   const GemmInstance* gemm_instances_f##F##_##S##_1(int*); \
   const MoeInstance* moe_instances_f##F##_##S##_2(int*);   \
-  const MoeInstance* moe_instances_f##F##_##S##_3(int*);
+  const MoeInstance* moe_instances_f##F##_##S##_3(int*);   \
+  const GemmInstance* gemm_instances_f##F##_##S##_6(int*); \
+  const GemmInstance* gemm_instances_f##F##_##S##_7(int*);
 // Block_FP8's K-loop quantization instances
 const GemmInstance* gemm_instances_f2_0_4(int*);
 const GemmInstance* gemm_instances_f2_0_5(int*);
@@ -37,7 +39,9 @@ std::vector<I> gather(const I* (*const* parts)(int*), int n) {
 }
 }  // namespace
 
-#define W8_GEMM_PARTS(F, S) gemm_instances_f##F##_##S##_0, gemm_instances_f##F##_##S##_1
+#define W8_GEMM_PARTS(F, S)                                                      \
+  gemm_instances_f##F##_##S##_0, gemm_instances_f##F##_##S##_1,                 \
+      gemm_instances_f##F##_##S##_6, gemm_instances_f##F##_##S##_7
 #define W8_MOE_PARTS(F, S) moe_instances_f##F##_##S##_2, moe_instances_f##F##_##S##_3
 
 const MoeInstance* moe_instances(int* count) {

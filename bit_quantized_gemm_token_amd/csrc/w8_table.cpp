@@ -30,9 +30,18 @@ struct Entry {
   double us;
 };
 
-typedef std::tuple<int, int, int, int, int, int> Key;  // fmt, op, packed, M, N, K
+typedef std::tuple<int, int, int, int, int, int> Key;  // fmt, op, layout, M, N, K
 
-const char* layout_name(int packed) { return packed ? "packed" : "row"; }
+const char* layout_name(int layout) {
+  switch (layout) {
+    case 0: return "row";
+    case 1: return "packed";
+    case 2: return "seg2";
+    case 4: return "seg4";
+    case 8: return "seg8";
+  }
+  return "?";
+}
 const char* op_name(int op) {
   return op == W8_OP_LINEAR       ? "linear"
          : op == W8_OP_MOE        ? "moe"
@@ -109,10 +118,11 @@ w8_status parse_table(const std::string& text, std::map<Key, Entry>* native,
     if (tok[3] == "moe_linear") op = W8_OP_MOE_LINEAR;
     if (op < 0)
       return fail(W8_E_TABLE_FORMAT, where + "op must be gemm, linear, moe or moe_linear");
-    int packed = -1;
-    if (tok[4] == "row") packed = 0;
-    if (tok[4] == "packed") packed = 1;
-    if (packed < 0) return fail(W8_E_TABLE_FORMAT, where + "layout must be row or packed");
+    int packed = -1;  // the weight layout
+    for (int l : {0, 1, 2, 4, 8})
+      if (tok[4] == layout_name(l)) packed = l;
+    if (packed < 0)
+      return fail(W8_E_TABLE_FORMAT, where + "layout must be row, packed, seg2, seg4 or seg8");
     int v[12];  // M N K tile_n waves_k waves_n unroll split_k grid swap_ab x_lds quant_launch
     for (int i = 0; i < 12; ++i)
       if (!parse_int(tok[5 + i], &v[i]))
@@ -132,7 +142,7 @@ w8_status parse_table(const std::string& text, std::map<Key, Entry>* native,
     c.x_lds = v[10];
     c.quant_launch = v[11];
     if (check_gemm_shape(fmt, v[0], v[1], v[2]) != W8_OK ||
-        check_cfg(fmt, op, v[0], v[1], v[2], c) != W8_OK)
+        check_cfg(fmt, op, v[0], v[1], v[2], c, packed) != W8_OK)
       return fail(W8_E_TABLE_FORMAT, where + "invalid entry (" + std::string(w8_last_error()) + ")");
     (*native)[Key(fmt, op, packed, v[0], v[1], v[2])] = Entry{c, us};
   }
@@ -183,12 +193,12 @@ void maybe_load_env(Table& t) {
 
 static int m_bucket(int M) { return 31 - __builtin_clz((unsigned)M); }  // floor(log2 M)
 
-w8_cfg resolve_cfg(int fmt, int op, int M, int N, int K, int packed, int* from_table) {
+w8_cfg resolve_cfg(int fmt, int op, int M, int N, int K, int layout, int* from_table) {
   Table& t = table();
   {
     std::lock_guard<std::mutex> lk(t.mu);
     maybe_load_env(t);
-    const int pk = packed ? 1 : 0;
+    const int pk = layout;
     auto it = t.native.find(Key(fmt, op, pk, M, N, K));
     if (it != t.native.end()) {
       if (from_table) *from_table = 1;
@@ -207,7 +217,7 @@ w8_cfg resolve_cfg(int fmt, int op, int M, int N, int K, int packed, int* from_t
       const int d = m > M ? m - M : M - m;
       if (d < pick_dist || (d == pick_dist && m > pick_m)) {
         w8_cfg c = e->second.cfg;
-        if (check_cfg(fmt, op, M, N, K, c) != W8_OK) continue;
+        if (check_cfg(fmt, op, M, N, K, c, layout) != W8_OK) continue;
         pick = &e->second.cfg;
         pick_dist = d;
         pick_m = m;
@@ -219,7 +229,7 @@ w8_cfg resolve_cfg(int fmt, int op, int M, int N, int K, int packed, int* from_t
     }
   }
   if (from_table) *from_table = 0;
-  return model_cfg(fmt, op, M, N, K, packed ? 1 : 0);
+  return model_cfg(fmt, op, M, N, K, layout);
 }
 
 }  // namespace w8
@@ -292,21 +302,22 @@ int w8_config_table_foreign(void) {
   return t.foreign_count;
 }
 
-w8_status w8_set_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed,
+w8_status w8_set_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layout,
                         const w8_cfg* cfg, double us_per_call) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!cfg) return fail(W8_E_INVALID, "null cfg");
-  st = check_cfg(fmt, op, M, N, K, *cfg);
+  if (!layout_valid(layout)) return fail(W8_E_INVALID, "weight layout must be 0, 1, 2, 4 or 8");
+  st = check_cfg(fmt, op, M, N, K, *cfg, layout);
   if (st) return st;
   Table& t = table();
   std::lock_guard<std::mutex> lk(t.mu);
   maybe_load_env(t);
-  t.native[Key(fmt, op, packed ? 1 : 0, M, N, K)] = Entry{*cfg, us_per_call};
+  t.native[Key(fmt, op, layout, M, N, K)] = Entry{*cfg, us_per_call};
   return ok();
 }
 
-w8_status w8_lookup_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed, w8_cfg* out,
+w8_status w8_lookup_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layout, w8_cfg* out,
                            double* us_per_call) {
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
@@ -316,7 +327,7 @@ w8_status w8_lookup_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed
   Table& t = table();
   std::lock_guard<std::mutex> lk(t.mu);
   maybe_load_env(t);
-  auto it = t.native.find(Key(fmt, op, packed ? 1 : 0, M, N, K));
+  auto it = t.native.find(Key(fmt, op, layout, M, N, K));
   if (it == t.native.end()) return fail(W8_E_NOT_FOUND, "no table entry for this shape and layout");
   *out = it->second.cfg;
   if (us_per_call) *us_per_call = it->second.us;

@@ -188,7 +188,7 @@ bool outputs_match(bool exact, const std::vector<uint16_t>& ycur,
 // reference output of the default GEMM config, and graph timing over R
 // rotating weight copies.
 struct Harness {
-  int fmt, op, M, N, K, packed;
+  int fmt, op, M, N, K, packed;  // packed: the weight layout (0 row-major, 1/2/4/8 packed)
   w8_tune_opts o;
   long long ld = 0;
   size_t wbytes = 0, wrow_bytes = 0, R = 0, nsx = 0, nsw = 0;
@@ -213,7 +213,7 @@ struct Harness {
   w8_status setup(size_t max_ws) {
     ld = (K + 15) / 16 * 16;
     wrow_bytes = (size_t)N * ld;
-    wbytes = packed ? packed_weight_bytes(fmt, N, K) : wrow_bytes;
+    wbytes = packed ? packed_weight_bytes(fmt, N, K, packed) : wrow_bytes;
     R = wbytes ? (size_t)((o.rotate_bytes + (long long)wbytes - 1) / (long long)wbytes) : 1;
     R = std::max<size_t>(R, 2);
     R = std::min<size_t>(R, 4096);
@@ -221,8 +221,8 @@ struct Harness {
     const int G = K / W8_GROUP;
     nsx = block ? (size_t)M * G : (size_t)M;
     nsw = block ? (size_t)((N + 127) / 128) * G : (size_t)N;
-    const w8_cfg dflt = make_default_cfg(fmt, W8_OP_GEMM, M, N, K);  // reference
-    max_ws = std::max(max_ws, workspace_bytes(fmt, W8_OP_GEMM, M, N, K, dflt));
+    const w8_cfg dflt = make_default_cfg(fmt, W8_OP_GEMM, M, N, K, 0);  // reference
+    max_ws = std::max(max_ws, workspace_bytes(fmt, W8_OP_GEMM, M, N, K, dflt, 0));
     TRY_HIP(hipStreamCreate(&stream));
     TRY_HIP(hipMalloc(&b.wrow, wrow_bytes));
     TRY_HIP(hipMalloc(&b.wpool, wbytes * R));
@@ -243,7 +243,7 @@ struct Harness {
                        0x4321u, is_int8);
     // copy 0 of the pool holds the same weights as the reference, in the tuned layout
     if (packed) {
-      TRY_HIP(launch_pack_weight(fmt, b.wrow, ld, N, K, b.wpool, stream));
+      TRY_HIP(launch_pack_weight(fmt, b.wrow, ld, N, K, b.wpool, packed, stream));
     } else {
       TRY_HIP(hipMemcpyAsync(b.wpool, b.wrow, wrow_bytes, hipMemcpyDeviceToDevice, stream));
     }
@@ -381,7 +381,7 @@ struct MoeHarness {
   w8_status setup(size_t max_ws) {
     ld = (K + 15) / 16 * 16;
     wrow_exp = (size_t)N * ld;
-    wexp = packed ? packed_weight_bytes(fmt, N, K) : wrow_exp;
+    wexp = packed ? packed_weight_bytes(fmt, N, K, 1) : wrow_exp;
     const size_t set = (size_t)E * wexp;
     R = (size_t)((o.rotate_bytes + (long long)set - 1) / (long long)set);
     R = std::min<size_t>(std::max<size_t>(R, 2), 4096);
@@ -426,7 +426,7 @@ struct MoeHarness {
                        0x4321u, (int)is_int8);
     for (int e = 0; e < E; ++e) {  // copy 0 holds the reference weights, in the tuned layout
       if (packed) {
-        TRY_HIP(launch_pack_weight(fmt, b.wrow + e * wrow_exp, ld, N, K, b.wpool + e * wexp,
+        TRY_HIP(launch_pack_weight(fmt, b.wrow + e * wrow_exp, ld, N, K, b.wpool + e * wexp, 1,
                                    stream));
       }
     }
@@ -505,7 +505,7 @@ w8_status read_opts(const w8_tune_opts* opts, w8_tune_opts* o) {
   }
   if (o->warmup < 0 || o->replays < 1 || o->bank2_top < 1 || o->rotate_bytes < 0 ||
       o->max_split_k < 1 || o->max_split_k > W8_MAX_SPLIT_K || o->top_n < 0 ||
-      (o->op != W8_OP_GEMM && o->op != W8_OP_LINEAR))
+      (o->op != W8_OP_GEMM && o->op != W8_OP_LINEAR) || !layout_valid(o->packed))
     return fail(W8_E_INVALID, "bad tuner options");
   return W8_OK;
 }
@@ -558,7 +558,7 @@ extern "C" w8_status w8_rank_configs(w8_fmt fmt, int M, int N, int K, const w8_t
   w8_tune_opts o;
   st = read_opts(opts, &o);
   if (st) return st;
-  const auto r = rank_configs(fmt, o.op, M, N, K, o.packed ? 1 : 0, o.max_split_k, o.stream_k);
+  const auto r = rank_configs(fmt, o.op, M, N, K, o.packed, o.max_split_k, o.stream_k);
   *count = (int)r.size();
   for (int i = 0; i < cap && i < (int)r.size(); ++i) {
     out[i] = r[i].second;
@@ -579,7 +579,7 @@ extern "C" w8_status w8_profile_configs(w8_fmt fmt, int M, int N, int K,
   st = refuse_under_capture(o);
   if (st) return st;
   for (int i = 0; i < n; ++i) {
-    st = check_cfg(fmt, o.op, M, N, K, cfgs[i]);
+    st = check_cfg(fmt, o.op, M, N, K, cfgs[i], o.packed);
     if (st) return st;
   }
   st = check_device();
@@ -590,10 +590,11 @@ extern "C" w8_status w8_profile_configs(w8_fmt fmt, int M, int N, int K,
   h.M = M;
   h.N = N;
   h.K = K;
-  h.packed = o.packed ? 1 : 0;
+  h.packed = o.packed;
   h.o = o;
   size_t max_ws = 0;
-  for (int i = 0; i < n; ++i) max_ws = std::max(max_ws, workspace_bytes(fmt, o.op, M, N, K, cfgs[i]));
+  for (int i = 0; i < n; ++i)
+    max_ws = std::max(max_ws, workspace_bytes(fmt, o.op, M, N, K, cfgs[i], o.packed));
   st = h.setup(max_ws);
   if (st) return st;
   for (int i = 0; i < n; ++i) {
@@ -623,7 +624,7 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   const int op = o.op;
   st = check_device();
   if (st) return st;
-  const int packed = o.packed ? 1 : 0;
+  const int packed = o.packed;  // the weight layout
 
   // Candidates: the feasible set of the family (enumerate_configs), in
   // enumeration order, or with top_n > 0 the top_n of the cost model's
@@ -643,9 +644,10 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
     cd.index = (int)cands.size();
     cands.push_back(cd);
   }
-  const w8_cfg dflt_op = make_default_cfg(fmt, op, M, N, K);  // reported baseline
-  size_t max_ws = workspace_bytes(fmt, op, M, N, K, dflt_op);
-  for (const Cand& cd : cands) max_ws = std::max(max_ws, workspace_bytes(fmt, op, M, N, K, cd.cfg));
+  const w8_cfg dflt_op = make_default_cfg(fmt, op, M, N, K, packed);  // reported baseline
+  size_t max_ws = workspace_bytes(fmt, op, M, N, K, dflt_op, packed);
+  for (const Cand& cd : cands)
+    max_ws = std::max(max_ws, workspace_bytes(fmt, op, M, N, K, cd.cfg, packed));
 
   Harness h;
   h.fmt = fmt;
@@ -773,7 +775,9 @@ extern "C" w8_status w8_moe_tune(w8_fmt fmt, int E, int T, int N, int K, int top
   if (st) return st;
   st = check_device();
   if (st) return st;
-  const int packed = o.packed ? 1 : 0;
+  if (o.packed != 0 && o.packed != 1)
+    return fail(W8_E_INVALID, "the grouped GEMM is tuned on row-major or plain packed weights");
+  const int packed = o.packed;
 
   // Candidates: the GEMM family's feasible set at M = T (an expert holds at
   // most T rows), without the minimum-waves pruning (the experts multiply

@@ -17,9 +17,10 @@ timings (a ranking loss plus a weighted log-time error, Nelder-Mead over the
 constants, which enter the model non-linearly) and reports how good the model's
 top-1 and the best of its top-N are against the measured best -- the two
 quantities the flashinfer-ai/flashinfer pull 3948 discussion weighs (top-1
-geomean, and the loss of autotuning only a top-N ranked list).  The Python
-model below mirrors predict_us() in w8_model.cpp term by term; the printed
-constants go into kParams there.
+geomean, and the loss of autotuning only a top-N ranked list).  Every
+prediction comes from the library's own model (w8_predict_us, with the trial
+constants passed in), so the fit tunes exactly the model the library ships;
+the printed constants go into kParams in csrc/w8_model.cpp.
 
 bucket-eval (GPU): for shapes whose M has no table entry but whose
 floor(log2 M) bucket has one, times the bucket entry's config, the model's
@@ -54,7 +55,7 @@ def collect(a):
             wr.writerow(("fmt", "op", "layout", "M", "N", "K") + CFG_KEYS + ("us", "pred"))
         for op in a.ops.split(","):
             for fmt in a.formats.split(","):
-                for packed in [{"row": False, "packed": True}[v] for v in a.layouts.split(",")]:
+                for packed in [w8.LAYOUTS[v] for v in a.layouts.split(",")]:
                     for (M, N, K) in shapes:
                         if a.time_budget_s and time.time() - t0 > a.time_budget_s:
                             print("[collect] time budget reached", flush=True)
@@ -77,59 +78,15 @@ def collect(a):
 
 
 # ------------------------------------------------------------------ model --
-def ksteps(fmt, K):
-    ks = 64 if fmt == "W8A8_INT8" else 128
-    return (K + ks - 1) // ks, ks
+def _library():
+    import bit_quantized_gemm_token_amd as w8
+    return w8
 
 
-def partial_slots(fmt, N, K, c, ntiles):
-    if c["grid"] > 0:
-        T, _ = ksteps(fmt, K)
-        I = ntiles * T
-        lmin = I // c["grid"]
-        return 1 if T <= 1 else (T - 2) // lmin + 2
-    return c["split_k"]
-
-
-def predict(p, fmt, op, M, N, K, c):
-    """predict_us() of csrc/w8_model.cpp."""
-    (t0, cu_bw, lat, hbm_bw, slots, sk_base, sk_slot, xl_stage, wg_cost, mfma, reduce,
-     q_launch, q_row_bw) = p
-    T, KS = ksteps(fmt, K)
-    MB, NB, W = (M + 15) // 16, c["tile_n"] // 16, c["waves_k"] * c["waves_n"]
-    cols = c["tile_n"] * c["waves_n"]
-    ntiles = (N + cols - 1) // cols
-    G = c["grid"] if c["grid"] > 0 else ntiles * c["split_k"]
-    seg = math.ceil(ntiles * T / c["grid"]) if c["grid"] > 0 else math.ceil(T / c["split_k"])
-    fused = op == "linear" and not c["quant_launch"]
-    wbytes = 16.0 * NB * c["waves_n"] * seg * KS
-    abytes = (1.0 if c["x_lds"] else c["waves_n"]) * 16.0 * MB * seg * KS
-    if fused:
-        abytes *= 2.0
-    shared = c["split_k"] > 1 or c["grid"] > 0
-    pbytes = 16.0 * NB * c["waves_n"] * 16.0 * MB * 4.0 if shared else 0.0
-    per_wg = wbytes + abytes + pbytes
-    per_cu_wgs = math.ceil(G / 256.0)
-    resident = min(per_cu_wgs, slots)
-    frag = 64.0 * 16.0 * (KS / 64.0)
-    inflight = resident * W * 2.0 * c["unroll"] * (NB + (0.0 if c["x_lds"] else MB)) * frag
-    rate = min(cu_bw, inflight / lat)
-    t_cu = per_cu_wgs * per_wg / rate
-    t_hbm = N * K / hbm_bw
-    t = t0 + max(t_cu, t_hbm)
-    t += per_cu_wgs * wg_cost
-    t += mfma * per_cu_wgs * seg * NB * MB * (KS / 64.0) / max(1, min(W, 4))
-    t += reduce * (c["waves_k"] - 1) * NB * MB
-    if shared:
-        ns = partial_slots(fmt, N, K, c, ntiles)
-        t += sk_base + sk_slot * ns * 16.0 * NB * c["waves_n"] * 16.0 * MB * 4.0 / cu_bw
-    if c["x_lds"]:
-        t += xl_stage
-    if fused and fmt != "Block_FP8":
-        t += 2.0 * M * K / q_row_bw
-    if op == "linear" and c["quant_launch"]:
-        t += q_launch
-    return t
+def predict(p, fmt, op, M, N, K, c, layout=1):
+    """The library model's prediction (us per call) with constants p."""
+    w8 = _library()
+    return w8.predict_us([(fmt, op, layout, M, N, K, c)], params=p)[0]
 
 
 # the constants compiled into csrc/w8_model.cpp (kParams); the fit starts here
@@ -138,8 +95,10 @@ CURRENT = (1.6537, 56705.2, 1.0003, 4.54169e6, 2.608, 1.2018, 1.5197, 0.43, 0.14
 
 
 def load(path):
-    """Timed rows of a collect CSV as numpy arrays, grouped by problem."""
+    """Timed rows of a collect CSV as numpy arrays, grouped by problem, plus
+    the rows packed once for the library's batch prediction."""
     import numpy as np
+    w8 = _library()
     with open(path) as f:
         rows = [r for r in csv.DictReader(f) if r["us"]]
     d = {k: np.array([int(r[k]) for r in rows]) for k in ("M", "N", "K") + CFG_KEYS}
@@ -149,42 +108,15 @@ def load(path):
     key = np.array([f"{r['fmt']} {r['op']} {r['layout']} {r['M']}x{r['N']}x{r['K']}"
                     for r in rows])
     d["keys"], d["group"] = np.unique(key, return_inverse=True)
+    d["batch"] = w8.PredictBatch([
+        (r["fmt"], r["op"], w8.LAYOUTS[r["layout"]], int(r["M"]), int(r["N"]), int(r["K"]),
+         {k: int(r[k]) for k in CFG_KEYS}) for r in rows])
     return d
 
 
 def predict_arrays(p, d):
-    """predict() over the arrays of load()."""
-    import numpy as np
-    (t0, cu_bw, lat, hbm_bw, slots, sk_base, sk_slot, xl_stage, wg_cost, mfma, reduce,
-     q_launch, q_row_bw) = p
-    KS = np.where(d["fmt"] == "W8A8_INT8", 64.0, 128.0)
-    T = np.ceil(d["K"] / KS)
-    MB, NB = (d["M"] + 15) // 16, d["tile_n"] // 16
-    wk, wn, S, grid, xl, ql = (d[k] for k in ("waves_k", "waves_n", "split_k", "grid", "x_lds",
-                                             "quant_launch"))
-    W = wk * wn
-    ntiles = np.ceil(d["N"] / (d["tile_n"] * wn))
-    G = np.where(grid > 0, grid, ntiles * S)
-    seg = np.where(grid > 0, np.ceil(ntiles * T / np.maximum(grid, 1)), np.ceil(T / S))
-    fused = (d["op"] == "linear") & (ql == 0)
-    abytes = np.where(xl > 0, 1.0, wn) * 16.0 * MB * seg * KS * np.where(fused, 2.0, 1.0)
-    shared = (S > 1) | (grid > 0)
-    tile_p = 16.0 * NB * wn * 16.0 * MB * 4.0
-    per_wg = 16.0 * NB * wn * seg * KS + abytes + np.where(shared, tile_p, 0.0)
-    pcw = np.ceil(G / 256.0)
-    inflight = (np.minimum(pcw, slots) * W * 2.0 * d["unroll"] *
-                (NB + np.where(xl > 0, 0.0, MB)) * 64.0 * 16.0 * (KS / 64.0))
-    t_cu = pcw * per_wg / np.minimum(cu_bw, inflight / lat)
-    t = t0 + np.maximum(t_cu, d["N"] * d["K"] / hbm_bw)
-    t = t + pcw * wg_cost + mfma * pcw * seg * NB * MB * (KS / 64.0) / np.clip(W, 1, 4)
-    t = t + reduce * (wk - 1) * NB * MB
-    lmin = np.maximum(ntiles * T // np.maximum(grid, 1), 1)
-    slots_n = np.where(grid > 0, np.where(T <= 1, 1, (T - 2) // lmin + 2), S)
-    t = t + np.where(shared, sk_base + sk_slot * slots_n * tile_p / cu_bw, 0.0)
-    t = t + np.where(xl > 0, xl_stage, 0.0)
-    t = t + np.where(fused & (d["fmt"] != "Block_FP8"), 2.0 * d["M"] * d["K"] / q_row_bw, 0.0)
-    t = t + np.where((d["op"] == "linear") & (ql > 0), q_launch, 0.0)
-    return t
+    """The library model's predictions for every row of load(), constants p."""
+    return d["batch"].run(p)
 
 
 def evaluate(p, d, top_n):

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define W8_ABI_VERSION 4
+#define W8_ABI_VERSION 5
 #define W8_MAX_M 32         /* token-count window of the tuned path (paragraph 4) */
 #define W8_MAX_SPLIT_K 256  /* split_k is a power of two up to 256 (paragraph 3) */
 #define W8_GROUP 128        /* Block_FP8 group / block edge */
@@ -104,7 +104,10 @@ typedef enum {
 /* One kernel configuration of the GEMM family (paragraphs 2-3 of the page:
  * the algorithmic variants are parameters, not separate kernels).
  *   tile_n   output columns (= weight rows) each wave owns: 16, 32 or 64
- *            (one activation fragment feeds tile_n/16 MFMAs per K-step).
+ *            (one activation fragment feeds tile_n/16 MFMAs per K-step);
+ *            on the K-segmented layouts (below) 1, 2 or 4 blocks of the
+ *            layout's 16/T rows: T = 2: 8, 16, 32; T = 4: 4, 8, 16;
+ *            T = 8: 2, 4, 8.
  *   waves_k  wavefronts of a workgroup that split its K range and are
  *            reduced through LDS: 1, 2, 4, 8 or 16.
  *   waves_n  wavefronts of a workgroup side by side along N, which share
@@ -140,8 +143,10 @@ typedef enum {
  *            runs with this config under the W8_OP_GEMM rules.  The tuner
  *            tries both for the linear op and keeps the faster.
  * Set abi_version to W8_ABI_VERSION and reserved[] to 0.  The weight layout
- * (row-major or packed, below) is a property of the weight buffer, not of
- * the config: it is given by the ldw argument of the GEMM.                 */
+ * (row-major, packed or K-segmented packed, below) is a property of the
+ * weight buffer, not of the config: it is given by the ldw argument of the
+ * GEMM.  On the K-segmented layouts a config has x_lds 0, waves_n 1, grid 0
+ * and, for the linear op, quant_launch 1.                                  */
 typedef struct {
     int32_t abi_version;
     int32_t tile_n;
@@ -168,7 +173,8 @@ typedef struct {
     int32_t insert;           /* 1: insert the winner into the config table */
     int32_t fail_candidate;   /* test hook: candidate with this index fails validation
                                  (-1 = none) */
-    int32_t packed;           /* weight layout tuned: 0 row-major, 1 packed */
+    int32_t packed;           /* weight layout tuned: 0 row-major, 1 packed, 2/4/8
+                                 K-segmented packed (the grouped GEMM: 0 or 1) */
     int32_t stream_k;         /* 1: also try stream-K grids (default 0: on the
                                  shapes measured so far they never won) */
     int32_t op;               /* w8_op tuned (default W8_OP_GEMM) */
@@ -227,27 +233,41 @@ w8_status w8_quantize_weight(w8_fmt fmt, int N, int K, const float *w, int64_t l
                              void *wq, int64_t ldq, float *sw, w8_stream stream);
 
 /* ------------------------------------------------------------------ GEMM -- */
-/* Weight layouts.  Row-major: codes [N, K], row stride ldw bytes (ldw >= K,
- * ldw % 16 == 0).  Packed: the MFMA-native layout written by w8_pack_weight
- * (the "memory layout" choice the page puts in the tuner's search space,
- * paragraph 3): for each block of 16 rows and each K-step (64 bytes of K for
- * W8A8_INT8, 128 for the FP8 formats), the 16 x K-step bytes are stored in
- * the order the kernel's lanes load them, so every load instruction reads
- * 1 KiB contiguous; rows and K are zero-padded to whole fragments.  A GEMM
- * call passes ldw = 0 for packed weights.  Configs are tuned per layout.     */
+/* Weight layouts (the "memory layout" choice the page puts in the tuner's
+ * search space, paragraph 3), each with a code used by the config, table
+ * and tuner functions:
+ *   0  row-major: codes [N, K], row stride ldw bytes (ldw >= K,
+ *      ldw % 16 == 0).
+ *   1  packed: the MFMA-native layout written by w8_pack_weight: for each
+ *      block of 16 rows and each K-step (64 bytes of K for W8A8_INT8, 128
+ *      for the FP8 formats), the 16 x K-step bytes are stored in the order
+ *      the kernel's lanes load them, so every load instruction reads 1 KiB
+ *      contiguous; rows and K are zero-padded to whole fragments.  GEMM
+ *      calls pass ldw = 0.
+ *   T = 2, 4, 8  K-segmented packed: one MFMA takes 16/T weight rows times
+ *      T consecutive K-steps (and 16/T tokens times the same K-steps); of
+ *      its products only the T diagonal blocks are kept and summed.  The
+ *      fragments (16/T rows, T K-steps) are stored like layout 1's, rows
+ *      zero-padded to multiples of 16/T and K to multiples of T K-steps.  At
+ *      M <= 16/T tokens the same weight bytes make T times as many output
+ *      tiles, which fills the GPU on narrow N without splitting K.  Larger M
+ *      runs as consecutive launches of 2 x 16/T tokens.  GEMM calls pass
+ *      ldw = -T.
+ * Configs are tuned per layout.                                            */
 
-/* Bytes of the packed layout for an N x K weight of fmt. */
-w8_status w8_packed_weight_size(w8_fmt fmt, int N, int K, size_t *bytes);
+/* Bytes of packed layout `layout` (1, 2, 4 or 8) for an N x K weight of fmt. */
+w8_status w8_packed_weight_size(w8_fmt fmt, int N, int K, int layout, size_t *bytes);
 
 /* Packs row-major codes (device, 16-byte aligned, ldw >= K, ldw % 16 == 0)
- * into wp (device, 16-byte aligned, w8_packed_weight_size bytes).  Offline;
- * one kernel launch on stream.  Same preconditions on N and K as the GEMM. */
+ * into wp (device, 16-byte aligned, w8_packed_weight_size bytes) in layout
+ * 1, 2, 4 or 8.  Offline; one kernel launch on stream.  Same preconditions
+ * on N and K as the GEMM. */
 w8_status w8_pack_weight(w8_fmt fmt, int N, int K, const void *wq, int64_t ldw, void *wp,
-                         w8_stream stream);
+                         int layout, w8_stream stream);
 
 /* Bytes of device workspace operation op needs for (fmt, M, N, K) under cfg
- * (cfg NULL: the config w8_resolve_config picks for op and that weight
- * layout; packed = 1 for packed weights).  The GEMM needs none when no tile
+ * on weights of layout `packed` (0, 1, 2, 4 or 8; cfg NULL: the config
+ * w8_resolve_config picks for op and that layout).  The GEMM needs none when no tile
  * is shared between workgroups (split_k == 1 and grid == 0); otherwise a
  * fixed 2 MiB region of arrival counters, then the partials of shared
  * tiles, so split_k > 1 and grid > 0 support at most 16384 output tiles
@@ -263,9 +283,9 @@ w8_status w8_workspace_size(w8_fmt fmt, w8_op op, int M, int N, int K, int packe
  * runs inside it: the last workgroup of each output tile to finish sums the
  * partials in split order, so results are run-to-run deterministic).
  *   xq, sx  activations as written by w8_quantize_act
- *   wq, sw  weights: codes in the row-major layout (row stride ldw bytes) or,
- *           with ldw = 0, in the packed layout; scales in the layout given
- *           above for fmt
+ *   wq, sw  weights: codes in the row-major layout (row stride ldw bytes),
+ *           with ldw = 0 in the packed layout, with ldw = -2, -4 or -8 in
+ *           that K-segmented layout; scales in the layout given above for fmt
  *   y       bf16 [M, N], row stride ldy elements (device)
  *   cfg     kernel configuration; NULL = w8_resolve_config's pick for
  *           (fmt, weight layout, M, N, K): table entry, M-bucket entry or
@@ -333,23 +353,41 @@ w8_status w8_linear(w8_fmt fmt, int M, int N, int K, const void *x, int64_t ldx,
 
 /* ---------------------------------------------------------------- config -- */
 /* W8_OK if cfg is a valid configuration of operation op (GEMM or LINEAR;
- * grouped configs take w8_moe_validate_config) for (fmt, M, N, K), else
+ * grouped configs take w8_moe_validate_config) for (fmt, M, N, K) on
+ * weights of layout `layout` (0, 1, 2, 4 or 8), else
  * W8_E_INVALID (with the reason in w8_last_error()).                        */
-w8_status w8_validate_config(w8_fmt fmt, w8_op op, int M, int N, int K, const w8_cfg *cfg);
+w8_status w8_validate_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layout,
+                             const w8_cfg *cfg);
 
 /* The built-in rule-of-thumb configuration of op for (fmt, M, N, K): fixed
  * tile and waves, Swap-AB below 32 tokens, the smallest split_k that fills
  * the machine (paragraph 7 of the page: a default config serves untuned
- * shapes).  The tuner validates every candidate against its output.       */
-w8_status w8_default_config(w8_fmt fmt, w8_op op, int M, int N, int K, w8_cfg *out);
+ * shapes); on the K-segmented layouts one block per wave and two K-waves.
+ * The tuner validates every candidate against its output.                 */
+w8_status w8_default_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layout,
+                            w8_cfg *out);
 
 /* The cost model's pick (the top-1 of w8_rank_configs with the default
  * options for op and layout): what an untuned shape runs
  * (flashinfer-ai/flashinfer pull 3948: a heuristic top-1 without tuning). */
 w8_status w8_model_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packed, w8_cfg *out);
 
+/* The cost model's predicted microseconds per call, us[i], of config
+ * cfgs[i] for operation op[i] (W8_OP_GEMM or W8_OP_LINEAR) on
+ * (fmt[i], M[i], N[i], K[i]) with weights of layout layout[i], for i < n.
+ * params NULL: the compiled constants; else nparams = 13 constants in the
+ * order t0, cu_bw, latency, hbm_bw, slots, sk_base, sk_slot, xl_stage,
+ * wg_cost, mfma, reduce, q_launch, q_row_bw (the model's fitter passes its
+ * trial values here, so fit and library evaluate the same model).  Host
+ * only; the configs are not validated beyond what the arithmetic needs
+ * (positive shape and config fields, a known layout: else W8_E_INVALID). */
+w8_status w8_predict_us(int n, const int *fmt, const int *op, const int *layout,
+                        const int *M, const int *N, const int *K, const w8_cfg *cfgs,
+                        const double *params, int nparams, double *us);
+
 /* The config op uses when called with cfg == NULL for weights in the given
- * layout (packed = 0 row-major, 1 packed), looked up for this device's arch
+ * layout (packed = 0 row-major, 1 packed, 2/4/8 K-segmented), looked up for
+ * this device's arch
  * and W8_ABI_VERSION: the table entry for (fmt, op, layout, M, N, K)
  * (*from_table = 1); else the entry for the same (fmt, op, layout, N, K)
  * whose M is nearest in the same floor(log2 M) bucket (the larger on a tie)
@@ -363,7 +401,8 @@ w8_status w8_resolve_config(w8_fmt fmt, w8_op op, int M, int N, int K, int packe
  * per line:
  *   arch abi fmt op layout M N K tile_n waves_k waves_n unroll split_k grid
  *   swap_ab x_lds quant_launch us_per_call
- * with op "gemm" or "linear" and layout "row" or "packed"; '#' starts a
+ * with op "gemm", "linear", "moe" or "moe_linear" and layout "row",
+ * "packed", "seg2", "seg4" or "seg8" (codes 0, 1, 2, 4, 8); '#' starts a
  * comment.  Entries whose arch or
  * abi differ from this build and device are kept in the file but never used.
  * w8_load_config_table replaces the in-memory table atomically: on any parse

@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_and_status_strings(lib):
-    assert lib.w8_abi_version() == 4
+    assert lib.w8_abi_version() == 5
     assert lib.w8_status_string(2) == b"W8_E_UNSUPPORTED"
     assert lib.w8_status_string(99) == b"W8_E_UNKNOWN"
 
@@ -276,15 +276,26 @@ def test_gemm_workspace_errors(w8, lib):
 def test_pack_argument_errors(w8, lib):
     # every call here fails validation before anything touches a device
     p = lib.w8_pack_weight
-    assert p(0, 64, 256, FAKE, 248, FAKE, None) == 1            # ldw < K
-    assert p(0, 64, 200, FAKE, 256, FAKE, None) == 1            # K % 16
-    assert p(2, 64, 192, FAKE, 256, FAKE, None) == 1            # Block_FP8 K % 128
-    assert p(0, 64, 256, None, 256, FAKE, None) == 1
-    assert p(0, 64, 256, FAKE, 256, ctypes.c_void_p(0x100008), None) == 1
+    assert p(0, 64, 256, FAKE, 248, FAKE, 1, None) == 1            # ldw < K
+    assert p(0, 64, 200, FAKE, 256, FAKE, 1, None) == 1            # K % 16
+    assert p(2, 64, 192, FAKE, 256, FAKE, 1, None) == 1            # Block_FP8 K % 128
+    assert p(0, 64, 256, None, 256, FAKE, 1, None) == 1
+    assert p(0, 64, 256, FAKE, 256, ctypes.c_void_p(0x100008), 1, None) == 1
+    for bad_layout in (0, 3, 16, -1):
+        assert p(0, 64, 256, FAKE, 256, FAKE, bad_layout, None) == 1
     # 16-row blocks x K-steps x (16 x K-step) bytes, zero padded
     assert w8.packed_weight_size("W8A8_INT8", 17, 80) == 2 * 2 * 16 * 64
     assert w8.packed_weight_size("FP8_Dynamic", 200, 208) == 13 * 2 * 16 * 128
     assert w8.packed_weight_size("Block_FP8", 4608, 7168) == 4608 * 7168
+    # K-segmented: (16/T)-row blocks x spans of T K-steps x (16 x K-step) bytes
+    assert w8.packed_weight_size("FP8_Dynamic", 200, 208, layout=2) == 25 * 1 * 16 * 128
+    assert w8.packed_weight_size("FP8_Dynamic", 200, 1040, layout=8) == 100 * 2 * 16 * 128
+    assert w8.packed_weight_size("W8A8_INT8", 17, 80, layout="seg4") == 5 * 1 * 16 * 64
+    assert w8.packed_weight_size("Block_FP8", 4608, 7168, layout=8) == 4608 * 7168
+    with pytest.raises(w8.W8Error):
+        w8.packed_weight_size("FP8_Dynamic", 64, 256, layout=0)
+    with pytest.raises(ValueError):
+        w8.packed_weight_size("FP8_Dynamic", 64, 256, layout=3)
 
 
 def test_linear_argument_errors(w8, lib):
@@ -344,8 +355,8 @@ def test_table_roundtrip_and_lookup(w8, tmp_path):
     assert hit == 0 and got == w8.model_config("Block_FP8", 32, 4608, 7168)
     got, hit = w8.resolve_config("Block_FP8", 16, 4608, 7168)       # other bucket -> model
     assert hit == 0 and got == w8.model_config("Block_FP8", 16, 4608, 7168)
-    assert w8.best_layout("Block_FP8", 32, 4608, 7168) is True
-    assert w8.best_layout("FP8_Dynamic", 4, 4096, 4096) is False
+    assert w8.best_layout("Block_FP8", 32, 4608, 7168) == 1
+    assert w8.best_layout("FP8_Dynamic", 4, 4096, 4096) == 0
     # the fused linear op has entries of its own
     c3 = w8.Config.make(tile_n=16, waves_k=1, waves_n=8, unroll=1, split_k=4, x_lds=1)
     w8.set_config("Block_FP8", 32, 4608, 7168, c3, 7.5, packed=True, op="linear")
@@ -422,23 +433,23 @@ def test_model_ranking(w8):
 def test_table_malformed_keeps_old_table(w8, tmp_path):
     w8.set_config("W8A8_INT8", 16, 896, 1024, w8.Config.make(), 1.0)
     bad_files = [
-        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 1.0\n",          # too few fields
-        "gfx950 4 INT4 gemm row 16 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",               # unknown format
-        "gfx950 4 W8A8_INT8 gemm tiled 16 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",        # unknown layout
-        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 3 0 0 0 0 1.0\n",          # split_k 3
-        "gfx950 4 W8A8_INT8 gemm row 40 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",          # M above 32
-        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 4 1 x 1 0 0 0 0 1.0\n",          # not an integer
-        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 0 fast\n",         # bad time
-        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 64 4 1 2 1 0 0 0 0 1.0\n",          # tile 64 x unroll 2
-        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 2 2 2 1 0 0 0 0 1.0\n",          # waves_k and waves_n
-        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 1 1 2 2 256 0 0 0 1.0\n",        # grid with split_k
-        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 1 1 2 1 100000 0 0 0 1.0\n",     # grid > iterations
-        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 16 1 2 1 0 0 1 0 1.0\n",        # x_lds, 16 waves
-        "gfx950 4 W8A8_INT8 fused row 16 896 1024 16 4 1 2 1 0 0 1 0 1.0\n",       # unknown op
-        "gfx950 4 W8A8_INT8 linear row 16 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",      # linear without x_lds
-        "gfx950 4 W8A8_INT8 linear row 16 896 1024 16 8 1 2 1 0 0 1 0 1.0\n",      # linear, 8 waves_k
-        "gfx950 4 W8A8_INT8 linear row 16 896 1024 16 8 1 2 1 0 0 1 2 1.0\n",      # quant_launch 2
-        "gfx950 4 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 1 1.0\n",        # gemm, quant_launch
+        "gfx950 5 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 1.0\n",          # too few fields
+        "gfx950 5 INT4 gemm row 16 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",               # unknown format
+        "gfx950 5 W8A8_INT8 gemm tiled 16 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",        # unknown layout
+        "gfx950 5 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 3 0 0 0 0 1.0\n",          # split_k 3
+        "gfx950 5 W8A8_INT8 gemm row 40 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",          # M above 32
+        "gfx950 5 W8A8_INT8 gemm row 16 896 1024 16 4 1 x 1 0 0 0 0 1.0\n",          # not an integer
+        "gfx950 5 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 0 fast\n",         # bad time
+        "gfx950 5 W8A8_INT8 gemm row 16 896 1024 64 4 1 2 1 0 0 0 0 1.0\n",          # tile 64 x unroll 2
+        "gfx950 5 W8A8_INT8 gemm row 16 896 1024 16 2 2 2 1 0 0 0 0 1.0\n",          # waves_k and waves_n
+        "gfx950 5 W8A8_INT8 gemm row 16 896 1024 16 1 1 2 2 256 0 0 0 1.0\n",        # grid with split_k
+        "gfx950 5 W8A8_INT8 gemm row 16 896 1024 16 1 1 2 1 100000 0 0 0 1.0\n",     # grid > iterations
+        "gfx950 5 W8A8_INT8 gemm row 16 896 1024 16 16 1 2 1 0 0 1 0 1.0\n",        # x_lds, 16 waves
+        "gfx950 5 W8A8_INT8 fused row 16 896 1024 16 4 1 2 1 0 0 1 0 1.0\n",       # unknown op
+        "gfx950 5 W8A8_INT8 linear row 16 896 1024 16 4 1 2 1 0 0 0 0 1.0\n",      # linear without x_lds
+        "gfx950 5 W8A8_INT8 linear row 16 896 1024 16 8 1 2 1 0 0 1 0 1.0\n",      # linear, 8 waves_k
+        "gfx950 5 W8A8_INT8 linear row 16 896 1024 16 8 1 2 1 0 0 1 2 1.0\n",      # quant_launch 2
+        "gfx950 5 W8A8_INT8 gemm row 16 896 1024 16 4 1 2 1 0 0 0 1 1.0\n",        # gemm, quant_launch
     ]
     for i, text in enumerate(bad_files):
         p = tmp_path / f"bad{i}.tbl"
@@ -459,7 +470,7 @@ def test_table_foreign_entries_ignored_and_kept(w8, tmp_path):
                  "gfx950 1 FP8_Dynamic row 4 4096 4096 32 2 2 4 0 2.5\n"
                  "gfx950 2 FP8_Dynamic gemm row 4 4096 4096 32 2 1 2 4 0 0 0 2.5\n"
                  "gfx950 3 FP8_Dynamic gemm row 4 4096 4096 64 2 1 1 4 0 0 0 0 2.5\n"
-                 "gfx950 4 FP8_Dynamic gemm row 4 4096 4096 32 2 1 2 4 0 0 0 0 2.5  # native\n")
+                 "gfx950 5 FP8_Dynamic gemm row 4 4096 4096 32 2 1 2 4 0 0 0 0 2.5  # native\n")
     w8.load_config_table(str(p))
     assert w8.config_table_size() == 1 and w8.config_table_foreign() == 5
     assert w8.lookup_config("FP8_Dynamic", 4, 4096, 4096) == \
@@ -474,7 +485,7 @@ def test_table_foreign_entries_ignored_and_kept(w8, tmp_path):
 
 def test_table_from_environment(tmp_path):
     p = tmp_path / "env.tbl"
-    p.write_text("gfx950 4 W8A8_INT8 gemm row 16 896 1024 32 2 1 2 8 0 1 0 0 0.5\n")
+    p.write_text("gfx950 5 W8A8_INT8 gemm row 16 896 1024 32 2 1 2 8 0 1 0 0 0.5\n")
     code = ("import bit_quantized_gemm_token_amd as w8;"
             "c = w8.lookup_config('W8A8_INT8', 16, 896, 1024);"
             "print(c.as_dict() if c else None)")
@@ -490,7 +501,7 @@ def test_table_from_environment(tmp_path):
 
 def test_env_table_loaded_by_the_c_library_alone(tmp_path):
     p = tmp_path / "env.tbl"
-    p.write_text("gfx950 4 W8A8_INT8 gemm row 16 896 1024 32 2 1 2 8 0 1 0 0 0.5\n")
+    p.write_text("gfx950 5 W8A8_INT8 gemm row 16 896 1024 32 2 1 2 8 0 1 0 0 0.5\n")
     from bit_quantized_gemm_token_amd import _capi
     # load _capi.py on its own (the package __init__ would load the shipped table)
     code = (
@@ -507,18 +518,34 @@ def test_env_table_loaded_by_the_c_library_alone(tmp_path):
     assert out == ["0", "8", "32"]
 
 
-def test_model_mirror_matches_library(w8):
-    """fit_model.predict with the compiled constants reproduces the library's
-    predictions term by term (the fit tunes the same model it ships)."""
+def test_model_fit_uses_library_model(w8):
+    """The fitter evaluates the library's own model (w8_predict_us): with its
+    starting constants it reproduces the tuner's ranking predictions, so
+    those constants are the compiled ones, on every layout; a change of one
+    constant moves the prediction; bad rows are refused."""
     from bit_quantized_gemm_token_amd import fit_model as fm
-    for fmt, M, N, K, op in (("FP8_Dynamic", 1, 4096, 4096, "gemm"),
-                             ("W8A8_INT8", 32, 896, 1040, "gemm"),
-                             ("Block_FP8", 17, 4608, 7168, "linear"),
-                             ("FP8_Dynamic", 8, 512, 7168, "linear")):
-        for us, c in w8.rank_configs(fmt, M, N, K, op=op, stream_k=True):
-            want = fm.predict(fm.CURRENT, fmt, op, M, N, K, c.as_dict())
-            assert abs(us - want) <= 1e-9 * want, (fmt, M, N, K, op, c, us, want)
-
+    for fmt, M, N, K, op, lay in (("FP8_Dynamic", 1, 4096, 4096, "gemm", 1),
+                                  ("W8A8_INT8", 32, 896, 1040, "gemm", 0),
+                                  ("Block_FP8", 17, 4608, 7168, "linear", 1),
+                                  ("FP8_Dynamic", 8, 512, 7168, "linear", 0),
+                                  ("FP8_Dynamic", 1, 512, 7168, "gemm", 8),
+                                  ("W8A8_INT8", 4, 896, 1040, "gemm", 4),
+                                  ("Block_FP8", 12, 1792, 5120, "linear", 2)):
+        ranked = w8.rank_configs(fmt, M, N, K, op=op, packed=lay, stream_k=True)
+        assert ranked, (fmt, M, N, K, op, lay)
+        batch = w8.PredictBatch([(fmt, op, lay, M, N, K, c) for _, c in ranked])
+        got = batch.run(fm.CURRENT)
+        for (us, c), want in zip(ranked, got):
+            assert abs(us - want) <= 1e-9 * want, (fmt, M, N, K, op, lay, c, us, want)
+        assert list(batch.run()) == [u for u, _ in ranked]
+        slower = list(fm.CURRENT)
+        slower[0] += 1.0                                   # t0, the fixed launch cost
+        assert all(abs(a - b - 1.0) < 1e-9 for a, b in zip(batch.run(slower), got))
+    with pytest.raises(w8.W8Error):
+        w8.predict_us([("FP8_Dynamic", "gemm", 1, 1, 512, 7168, w8.Config.make(split_k=0))])
+    with pytest.raises(w8.W8Error):
+        w8.predict_us([("FP8_Dynamic", "gemm", 1, 1, 512, 7168, w8.Config.make())],
+                      params=fm.CURRENT[:12])
 
 def test_moe_argument_errors(w8, lib):
     """Validation of the MoE entry point before anything touches a device."""
@@ -667,3 +694,84 @@ def test_moe_linear_argument_errors_and_config(w8, lib):
     with pytest.raises(w8.W8Error):                  # fused entries need x_lds = 1
         w8.set_config(fmt, T, N, K, w8.Config.make(waves_k=2, unroll=1), 7.0, packed=True,
                       op="moe_linear")
+
+
+def test_segmented_rules(w8):
+    """What the K-segmented layouts refuse: staged activations, waves along N,
+    stream-K, tiles that are not 1, 2 or 4 blocks of 16/T rows, a fused
+    linear op, and the grouped GEMM."""
+    ok = w8.Config.make(tile_n=2, waves_k=2, unroll=2, split_k=1, swap_ab=1)
+    w8.validate_config("FP8_Dynamic", 1, 512, 7168, ok, packed=8)
+    for bad in (dict(x_lds=1), dict(waves_n=2, x_lds=1, waves_k=1), dict(grid=64, split_k=1),
+                dict(tile_n=16), dict(tile_n=3), dict(tile_n=16 * 4)):
+        c = w8.Config.make(**{**ok.as_dict(), **bad})
+        with pytest.raises(w8.W8Error):
+            w8.validate_config("FP8_Dynamic", 1, 512, 7168, c, packed=8)
+    with pytest.raises(w8.W8Error):
+        w8.validate_config("FP8_Dynamic", 1, 512, 7168, ok, op="linear", packed=8)
+    w8.validate_config("FP8_Dynamic", 1, 512, 7168, w8.Config.make(**{**ok.as_dict(), "quant_launch": 1}),
+                       op="linear", packed=8)
+    with pytest.raises(w8.W8Error):
+        w8.validate_config("FP8_Dynamic", 4, 512, 7168, ok, op="moe", packed=8)
+
+
+def test_segmented_defaults_models_and_table(w8, tmp_path):
+    """On every K-segmented layout: the default config and the cost model's
+    pick are valid configs of the layout at every sweep shape and M up to 32
+    (several launches), their workspaces are sized for one launch's token
+    groups, entries round-trip through the table file under their layout
+    names, and the layout's entries never answer a lookup for another."""
+    import synthetic
+    for T in (2, 4, 8):
+        R = 16 // T
+        for fmt in w8.FORMATS:
+            for (M, N, K) in synthetic.SWEEP[:6] + ((32, 512, 7168), (3, 530, 1040)):
+                if fmt == "Block_FP8" and K % 128:
+                    continue
+                for op in ("gemm", "linear"):
+                    c = w8.default_config(fmt, M, N, K, op=op, packed=T)
+                    w8.validate_config(fmt, M, N, K, c, op=op, packed=T)
+                    assert c.tile_n == R and c.x_lds == 0 and c.quant_launch == (op == "linear")
+                    m = w8.model_config(fmt, M, N, K, packed=T, op=op)
+                    w8.validate_config(fmt, M, N, K, m, op=op, packed=T)
+                    assert m.tile_n % R == 0 and m.waves_n == 1 and m.grid == 0
+        # a split-K config's workspace: counters, then one 1 KiB fragment per
+        # (tile, split, block of rows, token group of one launch)
+        cfg = w8.Config.make(tile_n=2 * R, waves_k=1, unroll=2, split_k=4, swap_ab=1)
+        tiles = -(-512 // (2 * R))
+        assert w8.workspace_size("FP8_Dynamic", 32, 512, 7168, cfg, packed=T) == \
+            16384 * 128 + tiles * 4 * 2 * 2 * 1024
+        assert w8.workspace_size("FP8_Dynamic", 1, 512, 7168, cfg, packed=T) == \
+            16384 * 128 + tiles * 4 * 2 * 1 * 1024
+    w8.clear_config_table()
+    try:
+        c8 = w8.Config.make(tile_n=2, waves_k=1, unroll=4, split_k=1, swap_ab=1)
+        c2 = w8.Config.make(tile_n=8, waves_k=8, unroll=1, split_k=1, swap_ab=1)
+        w8.set_config("FP8_Dynamic", 1, 512, 7168, c8, 2.8, packed=8)
+        w8.set_config("FP8_Dynamic", 8, 896, 5120, c2, 4.3, packed="seg2")
+        w8.set_config("FP8_Dynamic", 1, 512, 7168, w8.Config.make(split_k=8), 4.1, packed=True)
+        with pytest.raises(w8.W8Error):            # a plain config is no layout-8 config
+            w8.set_config("FP8_Dynamic", 1, 512, 7168, w8.Config.make(split_k=8), 4.1, packed=8)
+        p = tmp_path / "seg.tbl"
+        w8.save_config_table(str(p))
+        text = p.read_text()
+        assert " FP8_Dynamic gemm seg8 1 512 7168 2 1 1 4 1 0 1 0 0 " in text
+        assert " FP8_Dynamic gemm seg2 8 896 5120 8 8 1 1 1 0 1 0 0 " in text
+        w8.clear_config_table()
+        w8.load_config_table(str(p))
+        assert w8.lookup_config("FP8_Dynamic", 1, 512, 7168, packed=8) == c8
+        assert w8.lookup_config("FP8_Dynamic", 8, 896, 5120, packed=2) == c2
+        assert w8.lookup_config("FP8_Dynamic", 8, 896, 5120, packed=4) is None
+        assert w8.resolve_config("FP8_Dynamic", 1, 512, 7168, packed=8) == (c8, 1)
+        assert w8.best_layout("FP8_Dynamic", 1, 512, 7168) == 8
+        bad = tmp_path / "bad.tbl"
+        bad.write_text("gfx950 5 FP8_Dynamic gemm seg8 1 512 7168 2 1 1 4 1 0 1 1 0 1.0\n")
+        with pytest.raises(w8.W8Error):             # x_lds on a K-segmented layout
+            w8.load_config_table(str(bad))
+        bad.write_text("gfx950 5 FP8_Dynamic gemm seg3 1 512 7168 2 1 1 4 1 0 1 0 0 1.0\n")
+        with pytest.raises(w8.W8Error):
+            w8.load_config_table(str(bad))
+        assert w8.lookup_config("FP8_Dynamic", 1, 512, 7168, packed=8) == c8   # old table kept
+    finally:
+        w8.clear_config_table()
+        w8.load_default_table()
