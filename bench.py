@@ -80,7 +80,7 @@ def measured_traffic(kernel, problems):
             for r in d.get("problems", [])}
     total = launches = 0.0
     for p in problems:
-        r = rows.get((p.fmt, p.M, p.N, p.K, "packed" if p.packed else "row",
+        r = rows.get((p.fmt, p.M, p.N, p.K, p.layout_name,
                       json.dumps(p.cfg.as_dict(), sort_keys=True)))
         if r is None or r.get("kernel") != kernel:
             return None
@@ -111,7 +111,7 @@ def counter_pass(problems, w8, manifest_path, copy_mib, launches=2):
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
     manifest = {"problems": [{"fmt": p.fmt, "M": p.M, "N": p.N, "K": p.K,
-                              "layout": "packed" if p.packed else "row", "cfg": p.cfg.as_dict(),
+                              "layout": p.layout_name, "cfg": p.cfg.as_dict(),
                               "kernel": p.kernel} for p in problems],
                 "gemm_dispatch_order": order, "copy_bytes_read": n * 4, "copy_bytes_written": n * 4,
                 "copies": 3, "source_hash": kernel_source_hash()}
@@ -298,8 +298,9 @@ def parse():
     p.add_argument("--cpu-budget-s", type=float, default=20.0)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--table", default=None, help="config table to load instead of the shipped one")
-    p.add_argument("--layout", choices=("table", "row", "packed"), default="table",
-                   help="weight layout: the faster one per the table (default), or forced")
+    p.add_argument("--layout", choices=("table", "row", "packed", "seg2", "seg4", "seg8"),
+                   default="table",
+                   help="weight layout: the fastest one per the table (default), or forced")
     p.add_argument("--report", default=None, help="write per-problem results (JSON) here")
     p.add_argument("--no-moe", action="store_true", help="skip the MoE grouped GEMM measurement")
     p.add_argument("--counter-pass", default=None, metavar="MANIFEST",
@@ -334,8 +335,10 @@ def log(*a):
 class Problem:
     def __init__(self, w8, fmt, M, N, K, rotate_bytes, dev, layout="table"):
         self.fmt, self.M, self.N, self.K = fmt, M, N, K
-        # the weight layout the table times best for this shape (row-major if none)
-        self.packed = w8.best_layout(fmt, M, N, K) if layout == "table" else layout == "packed"
+        # the weight layout the table times best for this shape (row-major if
+        # none): 0 row-major, 1 packed, 2/4/8 K-segmented packed
+        self.packed = w8.best_layout(fmt, M, N, K) if layout == "table" else w8.LAYOUTS[layout]
+        self.layout_name = w8.LAYOUT_NAMES[self.packed]
         self.cfg, self.from_table = w8.resolve_config(fmt, M, N, K, packed=self.packed)
         self.bytes = w8.algorithmic_bytes(fmt, M, N, K)
         x_bits = synthetic.activations(fmt, M, N, K)
@@ -349,12 +352,13 @@ class Problem:
             wq, self.sw = w8.quantize_weight(fmt, w)
             del w
         self.R = max(2, math.ceil(rotate_bytes / (N * K)))
-        self.wbytes = w8.packed_weight_size(fmt, N, K) if self.packed else N * K
+        self.wbytes = w8.packed_weight_size(fmt, N, K, self.packed) if self.packed else N * K
         if self.packed:
-            pk = w8.pack_weight(fmt, wq)
+            pk = w8.pack_weight(fmt, wq, layout=self.packed)
             self.pool = torch.empty((self.R, pk.data.numel()), dtype=torch.uint8, device=dev)
             self.pool.copy_(pk.data.unsqueeze(0).expand(self.R, -1))
-            self.weights = [w8.PackedWeight(fmt, N, K, self.pool[r]) for r in range(self.R)]
+            self.weights = [w8.PackedWeight(fmt, N, K, self.pool[r], self.packed)
+                            for r in range(self.R)]
         else:
             self.pool = torch.empty((self.R, N, K), dtype=wq.dtype, device=dev)
             self.pool.copy_(wq.unsqueeze(0).expand(self.R, N, K))
@@ -365,17 +369,22 @@ class Problem:
         self.y_gemm = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         self.y_path = torch.empty_like(self.y_gemm)
         self.y_linear = torch.empty_like(self.y_gemm)
-        self.ws = w8.Workspace(dev, max(w8.workspace_size(fmt, M, N, K, self.cfg), 256))
+        self.ws = w8.Workspace(dev, max(w8.workspace_size(fmt, M, N, K, self.cfg,
+                                                          packed=self.packed), 256))
         # the linear layer through w8_linear, with its own table entry for the
         # same weight layout (fused kernel or quantize launch + GEMM)
         self.cfg_l, self.from_table_l = w8.resolve_config(fmt, M, N, K, packed=self.packed,
                                                           op="linear")
         self.ws_l = w8.Workspace(dev, max(w8.workspace_size(fmt, M, N, K, self.cfg_l,
                                                             packed=self.packed, op="linear"), 256))
-        mb = (M + 15) // 16
+        # the kernel instance (its name in a rocprofv3 trace): token blocks of
+        # 16 rows, or of 16/T on the K-segmented layouts (one launch's)
+        rows = 16 // max(self.packed, 1)
+        mb = min(2, -(-M // rows))
         c = self.cfg
-        self.kernel = (f"gemm_kernel<{w8.FORMATS[fmt]}, {mb}, {c.tile_n // 16}, {c.waves_k}, "
-                       f"{c.waves_n}, {c.unroll}, {c.swap_ab}, {int(self.packed)}, {c.x_lds}>")
+        self.kernel = (f"gemm_kernel<{w8.FORMATS[fmt]}, {mb}, {c.tile_n // rows}, {c.waves_k}, "
+                       f"{c.waves_n}, {c.unroll}, {c.swap_ab}, {self.packed}, {c.x_lds}, "
+                       f"{1 if c.grid > 0 else 0}>")
 
     def run_gemm(self, w8):
         for r in range(self.R):
@@ -889,7 +898,9 @@ def main():
                    "problems": len(problems),
                    "table_hits": sum(p.from_table == 1 for p in problems),
                    "bucket_hits": sum(p.from_table == 2 for p in problems),
-                   "packed_layout": sum(bool(p.packed) for p in problems)},
+                   "packed_layout": sum(bool(p.packed) for p in problems),
+                   "layouts": {n: sum(p.layout_name == n for p in problems)
+                               for n in ("row", "packed", "seg2", "seg4", "seg8")}},
         "geomean_us_per_gemm": round(geomean([p.us_gemm for p in problems]), 4),
         "geomean_us_per_gemm_min": round(geomean([p.us_gemm_min for p in problems]), 4),
         "geomean_us_per_gemm_p90": round(geomean([p.us_gemm_p90 for p in problems]), 4),
@@ -917,7 +928,7 @@ def main():
         out["moe"] = {k: v for k, v in moe.items() if k != "rows"}
     if args.report:
         rows = [{"fmt": p.fmt, "M": p.M, "N": p.N, "K": p.K, "cfg": p.cfg.as_dict(),
-                 "layout": "packed" if p.packed else "row",
+                 "layout": p.layout_name,
                  "from_table": p.from_table, "R": p.R, "bytes": p.bytes,
                  "us_gemm": round(p.us_gemm, 4), "us_gemm_min": round(p.us_gemm_min, 4),
                  "us_gemm_p90": round(p.us_gemm_p90, 4), "us_quant_plus_gemm": round(p.us_path, 4),

@@ -48,10 +48,11 @@
 // (NB, WK, UNROLL) in the set below (single blocks with every K-wave count,
 // and two blocks with few K-waves).
 #define W8_ST(MB, T)                                                                            \
-  W8_I(MB, 1, 1, 1, 2, T, 0, 0) W8_I(MB, 1, 1, 1, 4, T, 0, 0) W8_I(MB, 1, 2, 1, 1, T, 0, 0)    \
-  W8_I(MB, 1, 2, 1, 2, T, 0, 0) W8_I(MB, 1, 4, 1, 1, T, 0, 0) W8_I(MB, 1, 4, 1, 2, T, 0, 0)    \
-  W8_I(MB, 1, 8, 1, 1, T, 0, 0) W8_I(MB, 1, 16, 1, 1, T, 0, 0) W8_I(MB, 2, 1, 1, 2, T, 0, 0)   \
-  W8_I(MB, 2, 2, 1, 1, T, 0, 0) W8_I(MB, 2, 4, 1, 1, T, 0, 0)
+  W8_I(MB, 1, 1, 1, 1, T, 0, 0) W8_I(MB, 1, 1, 1, 2, T, 0, 0) W8_I(MB, 1, 1, 1, 4, T, 0, 0)    \
+  W8_I(MB, 1, 2, 1, 1, T, 0, 0) W8_I(MB, 1, 2, 1, 2, T, 0, 0) W8_I(MB, 1, 4, 1, 1, T, 0, 0)    \
+  W8_I(MB, 1, 4, 1, 2, T, 0, 0) W8_I(MB, 1, 8, 1, 1, T, 0, 0) W8_I(MB, 1, 16, 1, 1, T, 0, 0)   \
+  W8_I(MB, 2, 1, 1, 1, T, 0, 0) W8_I(MB, 2, 1, 1, 2, T, 0, 0) W8_I(MB, 2, 2, 1, 1, T, 0, 0)    \
+  W8_I(MB, 2, 4, 1, 1, T, 0, 0)
 #define W8_S(MB) W8_ST(MB, 2) W8_ST(MB, 4) W8_ST(MB, 8)
 
 // Block_FP8's linear op quantizing in the K loop (XL 3): WN 1, WK in {2, 4,

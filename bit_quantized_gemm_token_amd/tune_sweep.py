@@ -1,7 +1,8 @@
 """Ahead-of-time tuning of a list of shapes into a config table file.
 
     python -m bit_quantized_gemm_token_amd.tune_sweep --out TABLE [--formats ...]
-           [--ops gemm,linear] [--layouts row,packed] [--shapes M,N,K;M,N,K...]
+           [--ops gemm,linear] [--layouts row,packed,seg2,seg4,seg8]
+           [--shapes M,N,K;M,N,K...]
            [--no-resume] [--max-split-k 256] [--top-n N]
            [--moe-shapes E,topk,T,N,K;...]
 
@@ -11,7 +12,10 @@ K=7168 at M in {1, 8, 32}; N=512, K=7168 at M in {1, 2, 4, 8, 16, 32};
 16 x 896 x 1024).  Ops "moe" and "moe_linear" tune the MoE grouped GEMM on
 quantized tokens and on bf16 tokens with the quantization fused (moe_tune) on
 their own shapes, packed layout only: by default the 128-expert top-8 layers
-of synthetic.MOE_SHAPES at the token counts synthetic.MOE_TOKENS.
+of synthetic.MOE_SHAPES at the token counts synthetic.MOE_TOKENS.  The
+K-segmented layouts (seg2, seg4, seg8: 16/T-row blocks) are tuned only for
+the M one launch covers, M <= 2 x 16/T (beyond it a call runs as several
+launches and the plain packed layout is the better one), unless --all-m.
 
 Tuning is the expensive offline step the page describes (ai-radar.it,
 "Helion nel backend vLLM", paragraph 6: ahead-of-time tuning can take hours
@@ -55,6 +59,8 @@ def main(argv=None):
     p.add_argument("--out", required=True)
     p.add_argument("--formats", default="FP8_Dynamic,W8A8_INT8,Block_FP8")
     p.add_argument("--layouts", default="row,packed")
+    p.add_argument("--all-m", action="store_true",
+                   help="tune the K-segmented layouts at every M, not only M <= 32/T")
     p.add_argument("--ops", default="gemm", help="comma list of gemm, linear, moe, moe_linear")
     p.add_argument("--moe-shapes", default=None, help="E,topk,T,N,K;... for the MoE ops")
     p.add_argument("--shapes", default=None)
@@ -77,7 +83,7 @@ def main(argv=None):
         w8.load_config_table(a.out)
     t0 = time.time()
     done = skipped = 0
-    layouts = [{"row": False, "packed": True}[v] for v in a.layouts.split(",")]
+    layouts = [w8.LAYOUTS[v] for v in a.layouts.split(",")]
     if a.moe_shapes:
         moe_shapes = [tuple(int(v) for v in s.split(",")) for s in a.moe_shapes.split(";") if s]
     else:
@@ -88,7 +94,8 @@ def main(argv=None):
             if op in ("moe", "moe_linear"):  # (T, N, K) keys the entry; E, topk: routing
                 jobs += [(op, fmt, (T, N, K), True, (E, k)) for E, k, T, N, K in moe_shapes]
             else:
-                jobs += [(op, fmt, s, packed, None) for s in shapes for packed in layouts]
+                jobs += [(op, fmt, s, packed, None) for s in shapes for packed in layouts
+                         if a.all_m or packed < 2 or s[0] <= 32 // packed]
     for op, fmt, (M, N, K), packed, moe in jobs:
         if w8.lookup_config(fmt, M, N, K, packed=packed, op=op) is not None:
             skipped += 1
@@ -102,12 +109,18 @@ def main(argv=None):
                                    replays=a.replays, max_split_k=a.max_split_k, insert=True,
                                    packed=True, fused=op == "moe_linear")
         else:
-            best, st = w8.tune_shape(fmt, M, N, K, rotate_bytes=a.rotate_mib << 20,
-                                     replays=a.replays, max_split_k=a.max_split_k, insert=True,
-                                     packed=packed, stream_k=a.stream_k, op=op, top_n=a.top_n)
+            try:
+                best, st = w8.tune_shape(fmt, M, N, K, rotate_bytes=a.rotate_mib << 20,
+                                         replays=a.replays, max_split_k=a.max_split_k,
+                                         insert=True, packed=packed, stream_k=a.stream_k, op=op,
+                                         top_n=a.top_n)
+            except w8.W8Error as e:          # e.g. no candidate of this layout fits the shape
+                print(f"[tune] {op} {fmt} {w8.LAYOUT_NAMES[int(packed)]} {M}x{N}x{K}: "
+                      f"not tuned ({e})", flush=True)
+                continue
         w8.save_config_table(a.out)
         done += 1
-        print(f"[tune] {op} {fmt} {'packed' if packed else 'row'} {M}x{N}x{K}: {best} "
+        print(f"[tune] {op} {fmt} {w8.LAYOUT_NAMES[int(packed)]} {M}x{N}x{K}: {best} "
               f"{st['best_us_bank2']:.3f} us "
               f"({st['best_gbps']:.0f} GB/s; default {st['default_us_bank2']:.3f} us; "
               f"{st['validated']}/{st['candidates']} validated; {st['tune_seconds']:.1f} s)",

@@ -3,7 +3,8 @@
 for small token counts under graph replay), checked output by output.
 
 For every (format, shape) of the 24-shape sweep, for the GEMM and the linear
-op, and for both weight layouts, with the config the library resolves from
+op, and for the row-major, the packed and the fastest layout of the table
+(K-segmented at small M), with the config the library resolves from
 its shipped table: two calls on two distinct copies of the weights, each into
 its own output, are captured into one HIP graph; the graph is replayed twice
 (outputs cleared before each replay, eager work in between), and every
@@ -34,10 +35,15 @@ def _bits(t):
 def test_sweep_graph_replay(w8, fmt, M, N, K):
     cs = Case(fmt, M, N, K)
     xq, sx = cs.gpu_act()
-    for packed in (False, True):
-        w0 = cs.weights(packed)
+    # row-major, packed, and the layout the table times best (a K-segmented
+    # one at small M)
+    for packed in sorted({0, 1, w8.best_layout(fmt, M, N, K)}):
+        if packed > 1:
+            w0 = cs.memo(("seg", packed), lambda: w8.pack_weight(fmt, cs.wq, layout=packed))
+        else:
+            w0 = cs.weights(bool(packed))
         if packed:
-            w1 = w8.PackedWeight(fmt, N, K, w0.data.clone())
+            w1 = w8.PackedWeight(fmt, N, K, w0.data.clone(), packed)
         else:
             w1 = w0.clone()
         for op in ("gemm", "linear"):

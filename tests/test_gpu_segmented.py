@@ -100,8 +100,8 @@ def test_pack_segmented_layout(w8, fmt, N, K, T):
 
 
 # (blocks per wave, waves_k, unroll) of the compiled K-segmented instances
-SEG_TILES = ((1, 1, 2), (1, 1, 4), (1, 2, 1), (1, 2, 2), (1, 4, 1), (1, 4, 2), (1, 8, 1),
-             (1, 16, 1), (2, 1, 2), (2, 2, 1), (2, 4, 1))
+SEG_TILES = ((1, 1, 1), (1, 1, 2), (1, 1, 4), (1, 2, 1), (1, 2, 2), (1, 4, 1), (1, 4, 2),
+             (1, 8, 1), (1, 16, 1), (2, 1, 1), (2, 1, 2), (2, 2, 1), (2, 4, 1))
 
 
 @pytest.mark.parametrize("fmt", ["W8A8_INT8", "FP8_Dynamic", "Block_FP8"])
