@@ -26,9 +26,12 @@ the same pair for the whole path (quantize + GEMM, two calls) and the time
 of the linear layer through w8_linear (with the count of problems whose
 table entry is the fused kernel).
 
-roofline: the dominant GEMM kernel instance (largest summed time over the
-problems that use it), achieved = its algorithmic bytes per launch / its
-average launch time from the HIP events, against the 8 TB/s HBM peak.
+roofline: the dominant GEMM kernel instance -- the largest sum, over the
+problems that use it, of one GEMM's time per problem (the headline weighs
+every problem once; the graphs' launch counts only follow from rotating
+1 GiB of weight copies, so they would favour the smallest shapes) --
+achieved = its algorithmic bytes per launch / its average launch time from
+the HIP events, against the 8 TB/s HBM peak.
 
 cpu_baseline: the oracle (oracle/, plain C, fp64/int64) run on the host on a
 bounded sample of the same problems (quantize + GEMM), in the same unit.
@@ -823,8 +826,8 @@ def main():
     by_kernel = {}
     for p in problems:
         by_kernel.setdefault(p.kernel, []).append(p)
-    # the instance with the largest share of the timed GEMM work (launches x time)
-    dom = max(by_kernel, key=lambda k: sum(p.us_gemm * p.R for p in by_kernel[k]))
+    # the instance with the largest summed time of one GEMM per problem
+    dom = max(by_kernel, key=lambda k: sum(p.us_gemm for p in by_kernel[k]))
     dp = by_kernel[dom]
     launches = sum(p.R for p in dp)
     achieved = sum(p.bytes * p.R for p in dp) / sum(p.us_gemm * 1e3 * p.R for p in dp)

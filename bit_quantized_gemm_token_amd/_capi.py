@@ -3,7 +3,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libw8gemm.so")
+# W8_LIBRARY: another build of the library to load (the host-sanitizer
+# build of build.build_sanitized(), for the CPU tests)
+LIB_PATH = os.environ.get("W8_LIBRARY") or os.path.join(_HERE, "libw8gemm.so")
 
 ABI_VERSION = 5
 MAX_M = 32

@@ -408,7 +408,7 @@ using namespace w8;
 
 namespace {
 
-w8_status gemm_entry(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ldq,
+w8_status gemm_entry(int fmt, int M, int N, int K, const void* xq, int64_t ldq,
                      const float* sx, const void* wq, int64_t ldw, const float* sw, void* out,
                      int64_t ldo, const w8_cfg* cfg, void* ws, size_t ws_bytes,
                      w8_stream stream, int out_mode) {
@@ -485,7 +485,8 @@ extern "C" {
 
 int w8_abi_version(void) { return W8_ABI_VERSION; }
 
-const char* w8_status_string(w8_status s) {
+const char* w8_status_string(w8_status s_in) {
+  const int s = raw_enum(s_in);
   switch (s) {
     case W8_OK: return "W8_OK";
     case W8_E_INVALID: return "W8_E_INVALID";
@@ -502,8 +503,9 @@ const char* w8_status_string(w8_status s) {
 
 const char* w8_last_error(void) { return g_err.c_str(); }
 
-w8_status w8_quantize_act(w8_fmt fmt, int M, int K, const void* x, int64_t ldx, void* xq,
+w8_status w8_quantize_act(w8_fmt fmt_in, int M, int K, const void* x, int64_t ldx, void* xq,
                           int64_t ldq, float* sx, w8_stream stream) {
+  const int fmt = raw_enum(fmt_in);
   w8_status st = check_gemm_shape(fmt, M, 1, K);
   if (st) return st;
   if (!x || !xq || !sx) return fail(W8_E_INVALID, "null device pointer");
@@ -520,8 +522,9 @@ w8_status w8_quantize_act(w8_fmt fmt, int M, int K, const void* x, int64_t ldx, 
   return ok();
 }
 
-w8_status w8_quantize_weight(w8_fmt fmt, int N, int K, const float* w, int64_t ldw, void* wq,
+w8_status w8_quantize_weight(w8_fmt fmt_in, int N, int K, const float* w, int64_t ldw, void* wq,
                              int64_t ldq, float* sw, w8_stream stream) {
+  const int fmt = raw_enum(fmt_in);
   if (fmt != W8_FP8_DYNAMIC && fmt != W8_BLOCK_FP8)
     return fail(W8_E_INVALID, "weight quantization is defined for FP8_Dynamic and Block_FP8");
   if (N < 1 || K < 1 || N > kMaxN || K > kMaxK) return fail(W8_E_INVALID, "bad N or K");
@@ -536,8 +539,10 @@ w8_status w8_quantize_weight(w8_fmt fmt, int N, int K, const float* w, int64_t l
   return ok();
 }
 
-w8_status w8_workspace_size(w8_fmt fmt, w8_op op, int M, int N, int K, int layout,
+w8_status w8_workspace_size(w8_fmt fmt_in, w8_op op_in, int M, int N, int K, int layout,
                             const w8_cfg* cfg, size_t* bytes) {
+  const int fmt = raw_enum(fmt_in);
+  const int op = raw_enum(op_in);
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!bytes) return fail(W8_E_INVALID, "null output pointer");
@@ -555,7 +560,8 @@ w8_status w8_workspace_size(w8_fmt fmt, w8_op op, int M, int N, int K, int layou
   return ok();
 }
 
-w8_status w8_packed_weight_size(w8_fmt fmt, int N, int K, int layout, size_t* bytes) {
+w8_status w8_packed_weight_size(w8_fmt fmt_in, int N, int K, int layout, size_t* bytes) {
+  const int fmt = raw_enum(fmt_in);
   w8_status st = check_gemm_shape(fmt, 1, N, K);
   if (st) return st;
   if (!bytes) return fail(W8_E_INVALID, "null output pointer");
@@ -565,8 +571,9 @@ w8_status w8_packed_weight_size(w8_fmt fmt, int N, int K, int layout, size_t* by
   return ok();
 }
 
-w8_status w8_pack_weight(w8_fmt fmt, int N, int K, const void* wq, int64_t ldw, void* wp,
+w8_status w8_pack_weight(w8_fmt fmt_in, int N, int K, const void* wq, int64_t ldw, void* wp,
                          int layout, w8_stream stream) {
+  const int fmt = raw_enum(fmt_in);
   w8_status st = check_gemm_shape(fmt, 1, N, K);
   if (st) return st;
   if (layout != 1 && layout != 2 && layout != 4 && layout != 8)
@@ -583,16 +590,18 @@ w8_status w8_pack_weight(w8_fmt fmt, int N, int K, const void* wq, int64_t ldw, 
   return ok();
 }
 
-w8_status w8_gemm_w8a8(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ldq,
+w8_status w8_gemm_w8a8(w8_fmt fmt_in, int M, int N, int K, const void* xq, int64_t ldq,
                        const float* sx, const void* wq, int64_t ldw, const float* sw, void* y,
                        int64_t ldy, const w8_cfg* cfg, void* ws, size_t ws_bytes,
                        w8_stream stream) {
+  const int fmt = raw_enum(fmt_in);
   return gemm_entry(fmt, M, N, K, xq, ldq, sx, wq, ldw, sw, y, ldy, cfg, ws, ws_bytes, stream, 0);
 }
 
-w8_status w8_gemm_w8a8_noalloc(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ldq,
+w8_status w8_gemm_w8a8_noalloc(w8_fmt fmt_in, int M, int N, int K, const void* xq, int64_t ldq,
                                const float* sx, const void* wq, int64_t ldw, const float* sw,
                                void* y, int64_t ldy, const w8_cfg* cfg, w8_stream stream) {
+  const int fmt = raw_enum(fmt_in);
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   const int layout = layout_from_ldw(ldw);
@@ -623,17 +632,19 @@ w8_status w8_gemm_w8a8_noalloc(w8_fmt fmt, int M, int N, int K, const void* xq, 
                     need > 0 ? kScratchBytes : 0, stream, 0);
 }
 
-w8_status w8_gemm_w8a8_acc(w8_fmt fmt, int M, int N, int K, const void* xq, int64_t ldq,
+w8_status w8_gemm_w8a8_acc(w8_fmt fmt_in, int M, int N, int K, const void* xq, int64_t ldq,
                            const float* sx, const void* wq, int64_t ldw, const float* sw,
                            void* acc, int64_t ldacc, const w8_cfg* cfg, void* ws,
                            size_t ws_bytes, w8_stream stream) {
+  const int fmt = raw_enum(fmt_in);
   return gemm_entry(fmt, M, N, K, xq, ldq, sx, wq, ldw, sw, acc, ldacc, cfg, ws, ws_bytes, stream,
                     1);
 }
 
-w8_status w8_linear(w8_fmt fmt, int M, int N, int K, const void* x, int64_t ldx, const void* wq,
+w8_status w8_linear(w8_fmt fmt_in, int M, int N, int K, const void* x, int64_t ldx, const void* wq,
                     int64_t ldw, const float* sw, void* y, int64_t ldy, const w8_cfg* cfg,
                     void* ws, size_t ws_bytes, w8_stream stream) {
+  const int fmt = raw_enum(fmt_in);
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!x || !wq || !sw || !y) return fail(W8_E_INVALID, "null device pointer");
@@ -670,8 +681,10 @@ w8_status w8_linear(w8_fmt fmt, int M, int N, int K, const void* x, int64_t ldx,
   return ok();
 }
 
-w8_status w8_validate_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layout,
+w8_status w8_validate_config(w8_fmt fmt_in, w8_op op_in, int M, int N, int K, int layout,
                              const w8_cfg* cfg) {
+  const int fmt = raw_enum(fmt_in);
+  const int op = raw_enum(op_in);
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!cfg) return fail(W8_E_INVALID, "null cfg");
@@ -682,7 +695,9 @@ w8_status w8_validate_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layo
   return ok();
 }
 
-w8_status w8_default_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layout, w8_cfg* out) {
+w8_status w8_default_config(w8_fmt fmt_in, w8_op op_in, int M, int N, int K, int layout, w8_cfg* out) {
+  const int fmt = raw_enum(fmt_in);
+  const int op = raw_enum(op_in);
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!out) return fail(W8_E_INVALID, "null output pointer");
@@ -692,8 +707,10 @@ w8_status w8_default_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layou
   return ok();
 }
 
-w8_status w8_resolve_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layout, w8_cfg* out,
+w8_status w8_resolve_config(w8_fmt fmt_in, w8_op op_in, int M, int N, int K, int layout, w8_cfg* out,
                             int* from_table) {
+  const int fmt = raw_enum(fmt_in);
+  const int op = raw_enum(op_in);
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!out) return fail(W8_E_INVALID, "null output pointer");

@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include <cstring>
 #include <string>
 #include <utility>
 #include <vector>
@@ -10,6 +11,19 @@
 #include "w8_launch.hpp"
 
 namespace w8 {
+
+// The integer a C caller passed for an enum-typed argument.  The C-ABI's
+// enums have no fixed underlying type, so in C++ a value outside their range
+// may not be loaded as the enum; the entry points copy the argument's bytes
+// into an int and validate that instead.
+// (By reference: passing the argument by value would load it as the enum.)
+template <class E>
+inline int raw_enum(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized here");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
 
 // Thread-local error text behind w8_last_error().
 w8_status fail(w8_status s, const std::string& msg);

@@ -250,8 +250,10 @@ extern "C" w8_status w8_predict_us(int n, const int* fmt, const int* op, const i
   return w8::ok();
 }
 
-extern "C" w8_status w8_model_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layout,
+extern "C" w8_status w8_model_config(w8_fmt fmt_in, w8_op op_in, int M, int N, int K, int layout,
                                      w8_cfg* out) {
+  const int fmt = w8::raw_enum(fmt_in);
+  const int op = w8::raw_enum(op_in);
   w8_status st = w8::check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!out) return w8::fail(W8_E_INVALID, "null output pointer");

@@ -318,8 +318,9 @@ w8_status launch_moe_call(const MoeCall& g, const w8_cfg& c, hipStream_t s) {
 
 using namespace w8;
 
-extern "C" w8_status w8_moe_config(w8_fmt fmt, int E, int T, int N, int K, int max_m, int packed,
+extern "C" w8_status w8_moe_config(w8_fmt fmt_in, int E, int T, int N, int K, int max_m, int packed,
                                    w8_cfg* out, int* from_table) {
+  const int fmt = raw_enum(fmt_in);
   w8_status st = check_moe_shape(fmt, E, T, N, K, max_m);
   if (st) return st;
   if (!out) return fail(W8_E_INVALID, "null output pointer");
@@ -327,8 +328,9 @@ extern "C" w8_status w8_moe_config(w8_fmt fmt, int E, int T, int N, int K, int m
   return ok();
 }
 
-extern "C" w8_status w8_moe_linear_config(w8_fmt fmt, int E, int T, int N, int K, int max_m,
+extern "C" w8_status w8_moe_linear_config(w8_fmt fmt_in, int E, int T, int N, int K, int max_m,
                                           int packed, w8_cfg* out, int* from_table) {
+  const int fmt = raw_enum(fmt_in);
   w8_status st = check_moe_shape(fmt, E, T, N, K, max_m);
   if (st) return st;
   if (!out) return fail(W8_E_INVALID, "null output pointer");
@@ -336,8 +338,9 @@ extern "C" w8_status w8_moe_linear_config(w8_fmt fmt, int E, int T, int N, int K
   return ok();
 }
 
-extern "C" w8_status w8_moe_validate_config(w8_fmt fmt, int E, int N, int K, int max_m,
+extern "C" w8_status w8_moe_validate_config(w8_fmt fmt_in, int E, int N, int K, int max_m,
                                             int packed, const w8_cfg* cfg) {
+  const int fmt = raw_enum(fmt_in);
   w8_status st = check_moe_shape(fmt, E, 1, N, K, max_m);
   if (st) return st;
   if (!cfg) return fail(W8_E_INVALID, "null cfg");
@@ -346,8 +349,9 @@ extern "C" w8_status w8_moe_validate_config(w8_fmt fmt, int E, int N, int K, int
   return ok();
 }
 
-extern "C" w8_status w8_moe_workspace_size(w8_fmt fmt, int E, int T, int N, int K, int max_m,
+extern "C" w8_status w8_moe_workspace_size(w8_fmt fmt_in, int E, int T, int N, int K, int max_m,
                                            int packed, const w8_cfg* cfg, size_t* bytes) {
+  const int fmt = raw_enum(fmt_in);
   w8_status st = check_moe_shape(fmt, E, T, N, K, max_m);
   if (st) return st;
   if (!bytes) return fail(W8_E_INVALID, "null output pointer");
@@ -365,12 +369,13 @@ extern "C" w8_status w8_moe_workspace_size(w8_fmt fmt, int E, int T, int N, int 
   return ok();
 }
 
-extern "C" w8_status w8_moe_gemm(w8_fmt fmt, int E, int T, int N, int K, int max_m,
+extern "C" w8_status w8_moe_gemm(w8_fmt fmt_in, int E, int T, int N, int K, int max_m,
                                  const void* xq, int64_t ldq, const float* sx,
                                  const int32_t* offsets, const int32_t* rows, int n_rows,
                                  const void* wq, int64_t ldw, int64_t w_stride, const float* sw,
                                  int64_t sw_stride, void* y, int64_t ldy, const w8_cfg* cfg,
                                  void* ws, size_t ws_bytes, w8_stream stream) {
+  const int fmt = raw_enum(fmt_in);
   w8_status st = check_moe_shape(fmt, E, T, N, K, max_m);
   if (st) return st;
   if (!xq || !sx) return fail(W8_E_INVALID, "null device pointer");
@@ -382,12 +387,13 @@ extern "C" w8_status w8_moe_gemm(w8_fmt fmt, int E, int T, int N, int K, int max
   return moe_entry(call, cfg, false, stream);
 }
 
-extern "C" w8_status w8_moe_linear(w8_fmt fmt, int E, int T, int N, int K, int max_m,
+extern "C" w8_status w8_moe_linear(w8_fmt fmt_in, int E, int T, int N, int K, int max_m,
                                    const void* x, int64_t ldx, const int32_t* offsets,
                                    const int32_t* rows, int n_rows, const void* wq, int64_t ldw,
                                    int64_t w_stride, const float* sw, int64_t sw_stride, void* y,
                                    int64_t ldy, const w8_cfg* cfg, void* ws, size_t ws_bytes,
                                    w8_stream stream) {
+  const int fmt = raw_enum(fmt_in);
   w8_status st = check_moe_shape(fmt, E, T, N, K, max_m);
   if (st) return st;
   if (!x) return fail(W8_E_INVALID, "null device pointer");

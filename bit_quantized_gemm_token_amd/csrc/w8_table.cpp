@@ -302,8 +302,10 @@ int w8_config_table_foreign(void) {
   return t.foreign_count;
 }
 
-w8_status w8_set_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layout,
+w8_status w8_set_config(w8_fmt fmt_in, w8_op op_in, int M, int N, int K, int layout,
                         const w8_cfg* cfg, double us_per_call) {
+  const int fmt = raw_enum(fmt_in);
+  const int op = raw_enum(op_in);
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!cfg) return fail(W8_E_INVALID, "null cfg");
@@ -317,8 +319,10 @@ w8_status w8_set_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layout,
   return ok();
 }
 
-w8_status w8_lookup_config(w8_fmt fmt, w8_op op, int M, int N, int K, int layout, w8_cfg* out,
+w8_status w8_lookup_config(w8_fmt fmt_in, w8_op op_in, int M, int N, int K, int layout, w8_cfg* out,
                            double* us_per_call) {
+  const int fmt = raw_enum(fmt_in);
+  const int op = raw_enum(op_in);
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!out) return fail(W8_E_INVALID, "null output pointer");

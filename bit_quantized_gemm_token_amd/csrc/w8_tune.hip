@@ -550,8 +550,9 @@ extern "C" void w8_tune_default_opts(w8_tune_opts* o) {
   o->top_n = 0;
 }
 
-extern "C" w8_status w8_rank_configs(w8_fmt fmt, int M, int N, int K, const w8_tune_opts* opts,
+extern "C" w8_status w8_rank_configs(w8_fmt fmt_in, int M, int N, int K, const w8_tune_opts* opts,
                                      w8_cfg* out, double* predicted_us, int cap, int* count) {
+  const int fmt = raw_enum(fmt_in);
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (!count || cap < 0 || (cap > 0 && !out)) return fail(W8_E_INVALID, "bad output arguments");
@@ -567,9 +568,10 @@ extern "C" w8_status w8_rank_configs(w8_fmt fmt, int M, int N, int K, const w8_t
   return ok();
 }
 
-extern "C" w8_status w8_profile_configs(w8_fmt fmt, int M, int N, int K,
+extern "C" w8_status w8_profile_configs(w8_fmt fmt_in, int M, int N, int K,
                                         const w8_tune_opts* opts, const w8_cfg* cfgs, int n,
                                         double* us, int* valid) {
+  const int fmt = raw_enum(fmt_in);
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
   if (n < 0 || (n > 0 && (!cfgs || !us || !valid))) return fail(W8_E_INVALID, "bad arguments");
@@ -610,8 +612,9 @@ extern "C" w8_status w8_profile_configs(w8_fmt fmt, int M, int N, int K,
   return ok();
 }
 
-extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tune_opts* opts,
+extern "C" w8_status w8_tune_shape(w8_fmt fmt_in, int M, int N, int K, const w8_tune_opts* opts,
                                    w8_cfg* best, w8_tune_stats* stats) {
+  const int fmt = raw_enum(fmt_in);
   const auto t_start = std::chrono::steady_clock::now();
   w8_status st = check_gemm_shape(fmt, M, N, K);
   if (st) return st;
@@ -734,7 +737,7 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   if (dc->valid && !(win->us2 < dc->us2)) win = dc;
   *best = win->cfg;
   if (o.insert) {
-    st = w8_set_config(fmt, (w8_op)op, M, N, K, packed, &win->cfg, win->us2);
+    st = w8_set_config((w8_fmt)fmt, (w8_op)op, M, N, K, packed, &win->cfg, win->us2);
     if (st) return st;
   }
   if (stats) {
@@ -760,8 +763,9 @@ extern "C" w8_status w8_tune_shape(w8_fmt fmt, int M, int N, int K, const w8_tun
   return ok();
 }
 
-extern "C" w8_status w8_moe_tune(w8_fmt fmt, int E, int T, int N, int K, int topk,
+extern "C" w8_status w8_moe_tune(w8_fmt fmt_in, int E, int T, int N, int K, int topk,
                                  const w8_tune_opts* opts, w8_cfg* best, w8_tune_stats* stats) {
+  const int fmt = raw_enum(fmt_in);
   const auto t_start = std::chrono::steady_clock::now();
   w8_status st = check_gemm_shape(fmt, T, N, K);
   if (st) return st;
@@ -793,7 +797,7 @@ extern "C" w8_status w8_moe_tune(w8_fmt fmt, int E, int T, int N, int K, int top
     if (!c.quant_launch) list.push_back(c);
   if (fused) {
     w8_cfg q;
-    if (w8_lookup_config(fmt, W8_OP_MOE, T, N, K, packed, &q, nullptr) == W8_OK) {
+    if (w8_lookup_config((w8_fmt)fmt, W8_OP_MOE, T, N, K, packed, &q, nullptr) == W8_OK) {
       q.quant_launch = 1;
       list.push_back(q);
     }
@@ -899,7 +903,7 @@ extern "C" w8_status w8_moe_tune(w8_fmt fmt, int E, int T, int N, int K, int top
   if (dc->valid && !(win->us2 < dc->us2)) win = dc;
   *best = win->cfg;
   if (o.insert) {
-    st = w8_set_config(fmt, fused ? W8_OP_MOE_LINEAR : W8_OP_MOE, T, N, K, packed, &win->cfg,
+    st = w8_set_config((w8_fmt)fmt, fused ? W8_OP_MOE_LINEAR : W8_OP_MOE, T, N, K, packed, &win->cfg,
                        win->us2);
     if (st) return st;
   }

@@ -28,7 +28,9 @@ FORMATS = {"FP8_Dynamic": FP8_DYNAMIC, "W8A8_INT8": W8A8_INT8, "Block_FP8": BLOC
 GROUP = 128
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "_build", "libw8oracle.so")
+# W8_ORACLE_LIBRARY: another build of the oracle to load (the host-sanitizer
+# build of build.build_sanitized(), for the CPU tests)
+_LIB_PATH = os.environ.get("W8_ORACLE_LIBRARY") or os.path.join(_HERE, "_build", "libw8oracle.so")
 _lib = None
 
 

@@ -32,6 +32,7 @@ class Cfg:
 class P:
     def __init__(self, fmt, M, N, K, packed, cfg, R):
         self.fmt, self.M, self.N, self.K, self.packed, self.cfg, self.R = fmt, M, N, K, packed, cfg, R
+        self.layout_name = {0: "row", 1: "packed", 2: "seg2", 4: "seg4", 8: "seg8"}[int(packed)]
 
 
 def write_csv(path, counter, rows):
