@@ -123,12 +123,14 @@ w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c, int l
                                                std::to_string(R) + "-row block"
                                          : std::string("cfg.tile_n must be 16, 32 or 64"));
   if (layout > 1) {
-    // K-segmented layouts: plain activation loads, one wave along N, split-K
-    if (c.x_lds || c.waves_n != 1 || c.grid != 0)
-      return fail(W8_E_INVALID, "cfg: the K-segmented layouts run with x_lds 0, waves_n 1 and "
-                                "grid 0");
-    if ((op == W8_OP_LINEAR || op == W8_OP_MOE_LINEAR) && !c.quant_launch)
-      return fail(W8_E_INVALID, "cfg: the linear op on K-segmented layouts needs quant_launch 1");
+    // K-segmented layouts: one wave along N, split-K; activations loaded by
+    // each wave, or (the fused linear op) quantized into LDS by the kernel
+    if (c.waves_n != 1 || c.grid != 0)
+      return fail(W8_E_INVALID, "cfg: the K-segmented layouts run with waves_n 1 and grid 0");
+    const bool fused = op == W8_OP_LINEAR && !c.quant_launch;
+    if (c.x_lds != (fused ? 1 : 0))
+      return fail(W8_E_INVALID, "cfg: on the K-segmented layouts x_lds is 1 exactly for the "
+                                "fused linear op (quant_launch 0)");
     if (op == W8_OP_MOE || op == W8_OP_MOE_LINEAR)
       return fail(W8_E_INVALID, "the grouped GEMM runs on row-major and plain packed weights");
   }
@@ -177,10 +179,12 @@ w8_status check_cfg(int fmt, int op, int M, int N, int K, const w8_cfg& c, int l
                                     std::to_string(iters) + ")");
   }
   if (c.x_lds) {
-    const long long ks = ksteps_of(fmt, K);
+    // K-steps (spans) of a workgroup x token blocks of one launch x 1 KiB chunks
+    const long long ks = layout_spans(fmt, K, layout);
     const long long seg = c.grid > 0 ? std::min(ks, (iters + c.grid - 1) / c.grid)
                                      : (ks + c.split_k - 1) / c.split_k;
-    const long long chunks = seg * ((M + 15) / 16) * (kstep_of(fmt) / 64);
+    const long long chunks =
+        seg * launch_mb(std::min(M, launch_rows(layout)), layout) * (kstep_of(fmt) / 64);
     if (chunks > kXlChunks)
       return fail(W8_E_INVALID, "cfg: x_lds needs the activations of a workgroup's K range in "
                                 "64 KiB (" + std::to_string(chunks) + " KiB here)");
@@ -335,8 +339,12 @@ w8_status launch_gemm_call(const GemmCall& g, const w8_cfg& c, hipStream_t s) {
     for (int m0 = 0; m0 < g.M; m0 += rows) {
       GemmCall p = g;
       p.M = std::min(rows, g.M - m0);
-      p.xq = static_cast<const uint8_t*>(g.xq) + (long long)m0 * g.ldq;
-      p.sx = g.sx + (long long)m0 * (g.fmt == W8_BLOCK_FP8 ? g.K / W8_GROUP : 1);
+      if (g.x) {  // fused quantization: bf16 rows, scales computed by the kernel
+        p.x = static_cast<const uint16_t*>(g.x) + (long long)m0 * g.ldx;
+      } else {
+        p.xq = static_cast<const uint8_t*>(g.xq) + (long long)m0 * g.ldq;
+        p.sx = g.sx + (long long)m0 * (g.fmt == W8_BLOCK_FP8 ? g.K / W8_GROUP : 1);
+      }
       p.out = static_cast<char*>(g.out) + (long long)m0 * g.ldo * (g.out_mode ? 4 : 2);
       const w8_status st = launch_gemm_call(p, c, s);
       if (st) return st;

@@ -183,8 +183,9 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
   constexpr int T = PACKED > 1 ? PACKED : 1;
   constexpr int R = 16 / T;
   static_assert(T == 1 || T == 2 || T == 4 || T == 8, "segments per MFMA: 1, 2, 4 or 8");
-  static_assert(T == 1 || (XL == 0 && WN == 1 && SK == 0 && !GROUPED),
-                "K-segmented layouts: plain activation loads, one wave along N, split-K only");
+  static_assert(T == 1 || ((XL == 0 || XL == 2) && WN == 1 && SK == 0 && !GROUPED),
+                "K-segmented layouts: plain activation loads or fused quantization, one wave "
+                "along N, split-K only");
   // activation row (codes and scales, or XL == 2 the bf16 row) of row m of
   // this call
   auto xr = [&](int m) -> long long {
@@ -353,7 +354,8 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
           const int o = min(lane + 64 * q, NOUT - 1);
           const int jb = o / (R * R), m = (o / R) % R, rr = o % R;
           ep2_sw[q] = a.sw[min(n0 + R * (jb / MB) + rr, a.N - 1)];
-          ep2_sx[q] = a.sx[xr(min(R * (jb % MB) + m, a.M - 1))];
+          // (XL == 2: the row scales are computed by the row pass instead)
+          if constexpr (XL != 2) ep2_sx[q] = a.sx[xr(min(R * (jb % MB) + m, a.M - 1))];
         }
       } else if constexpr (!BLOCK) {
 #pragma unroll
@@ -500,7 +502,8 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
 #pragma unroll
             for (int b = 0; b < MB; ++b)
 #pragma unroll
-              for (int i = 0; i < SXN; ++i) sx[b][i] = sxl[(k - ka) * 32 + sxm[b][i]];
+              for (int i = 0; i < SXN; ++i)
+                sx[b][i] = sxl[((k - ka) * MB + b) * 16 + (SWAP ? r : tl * R + (4 * g + i) % R)];
             step(w, x, st.sw[u], sx);
           } else {
             step(w, x, st.sw[BLOCK ? u : 0], st.sx[BLOCK ? u : 0]);
@@ -546,7 +549,11 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
     // 16-byte chunks lane l of that MFMA operand reads; a wave's 64 units
     // share one K-step and row block, so the four lanes l, l^16, l^32, l^48
     // hold one row's whole K-step, a Block_FP8 group.  The ragged K tail step
-    // is staged too, its bytes past K as zero codes.
+    // is staged too, its bytes past K as zero codes.  (K-segmented layouts:
+    // a unit is (span, token group, lane), lane l holding row (l%16)%R of the
+    // group at K-step (l%16)/R of the span; the four lanes still share one
+    // row's K-step.)  Block_FP8 group scales go to sxl[(kk*MB + b)*16 + p]
+    // for the unit's K-step kk of the segment, group b and operand index p.
     if constexpr (XL == 2) {
       const uint16_t* xb = reinterpret_cast<const uint16_t*>(a.xq);
       constexpr int QB = WK * WN >= 8 ? 1 : 2;  // units per thread per batch (registers)
@@ -557,10 +564,11 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
         for (int q = 0; q < QB; ++q) {
           const int u = u0 + q * nthreads;
           const int kk = u / (MB * 64), b = (u >> 6) % MB;
-          const int row = min(16 * b + (lane & 15), a.M - 1);
+          const int row = min(R * b + mr, a.M - 1);
 #pragma unroll
           for (int jj = 0; jj < CH; ++jj) {
-            const int e = (ka + kk) * KSTEP + 64 * jj + 16 * (lane >> 4);  // first element
+            // first element
+            const int e = ((ka + kk) * T + tl) * KSTEP + 64 * jj + 16 * (lane >> 4);
             raw[q][jj][0] = raw[q][jj][1] = v4u{0u, 0u, 0u, 0u};
             if (u < nunits && e < a.K) {  // (K % 16 == 0: a chunk is wholly inside K or past it)
               const uint16_t* src = xb + xr(row) * a.ldq + e;
@@ -575,7 +583,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
         for (int q = 0; q < QB; ++q) {
           const int u = u0 + q * nthreads;  // wave-uniform validity (nunits % 64 == 0)
           const int kk = u / (MB * 64), b = (u >> 6) % MB;
-          const int row = min(16 * b + (lane & 15), a.M - 1);
+          const int row = min(R * b + mr, a.M - 1);
           float s;
           if constexpr (BLOCK) {
             float gm = 0.0f;
@@ -585,7 +593,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
             gm = fmaxf(gm, __shfl_xor(gm, 16, 64));
             gm = fmaxf(gm, __shfl_xor(gm, 32, 64));
             s = act_scale<false>(gm);
-            if (u < nunits && lane < 16 && 16 * b + lane < a.M) sxl[kk * 32 + 16 * b + lane] = s;
+            if (u < nunits && lane < 16) sxl[(kk * MB + b) * 16 + lane] = s;
           } else {
             s = act_scale<INT8>(__uint_as_float(reinterpret_cast<const unsigned*>(sxl)[row]));
           }
@@ -651,7 +659,13 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
 #pragma unroll
           for (int b = 0; b < MB; ++b)
 #pragma unroll
-            for (int i = 0; i < SXN; ++i) tsx[b][i] = sxrow[b][i][kg];
+            for (int i = 0; i < SXN; ++i) {
+              if constexpr (XL == 2)  // the staged span's group scales
+                tsx[b][i] = sxl[((a.kfull - ka) * MB + b) * 16 +
+                                (SWAP ? r : tl * R + (4 * g + i) % R)];
+              else
+                tsx[b][i] = sxrow[b][i][kg];
+            }
         }
 #pragma unroll
         for (int j = 0; j < NB; ++j)
@@ -816,10 +830,16 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
               reinterpret_cast<Word*>(a.out)[off] = v;
             } else {
               float y;
-              if constexpr (BLOCK)
+              if constexpr (BLOCK) {
                 y = v;
-              else
-                y = (float)v * ep2_sx[q] * ep2_sw[q];
+              } else {
+                float sxv;
+                if constexpr (XL == 2)  // from the row pass's absolute maximum of row mm
+                  sxv = act_scale<INT8>(__uint_as_float(reinterpret_cast<const unsigned*>(sxl)[mm]));
+                else
+                  sxv = ep2_sx[q];
+                y = (float)v * sxv * ep2_sw[q];
+              }
               reinterpret_cast<uint16_t*>(a.out)[off] = bf16_rne(y);
             }
           }

@@ -44,7 +44,7 @@
   W8_U(MB, 1, 1, 2) W8_U(MB, 2, 1, 2) W8_U(MB, 4, 1, 2) W8_U(MB, 1, 2, 2)             \
   W8_U(MB, 1, 4, 2) W8_U(MB, 1, 8, 2)
 
-// The K-segmented layouts (PACKED = T in {2, 4, 8}): WN 1, XL 0, SK 0, and
+// The K-segmented layouts (PACKED = T in {2, 4, 8}): WN 1, SK 0, XL 0 and
 // (NB, WK, UNROLL) in the set below (single blocks with every K-wave count,
 // and two blocks with few K-waves).
 #define W8_ST(MB, T)                                                                            \
@@ -53,7 +53,14 @@
   W8_I(MB, 1, 4, 1, 2, T, 0, 0) W8_I(MB, 1, 8, 1, 1, T, 0, 0) W8_I(MB, 1, 16, 1, 1, T, 0, 0)   \
   W8_I(MB, 2, 1, 1, 1, T, 0, 0) W8_I(MB, 2, 1, 1, 2, T, 0, 0) W8_I(MB, 2, 2, 1, 1, T, 0, 0)    \
   W8_I(MB, 2, 4, 1, 1, T, 0, 0)
-#define W8_S(MB) W8_ST(MB, 2) W8_ST(MB, 4) W8_ST(MB, 8)
+// and with the activations quantized into LDS by the kernel (XL 2, the fused
+// linear op): waves_k <= 4.
+#define W8_SQ(MB, T)                                                                            \
+  W8_I(MB, 1, 1, 1, 1, T, 2, 0) W8_I(MB, 1, 1, 1, 2, T, 2, 0) W8_I(MB, 1, 2, 1, 1, T, 2, 0)    \
+  W8_I(MB, 1, 2, 1, 2, T, 2, 0) W8_I(MB, 1, 4, 1, 1, T, 2, 0) W8_I(MB, 2, 1, 1, 1, T, 2, 0)    \
+  W8_I(MB, 2, 2, 1, 1, T, 2, 0)
+#define W8_S(MB) \
+  W8_ST(MB, 2) W8_ST(MB, 4) W8_ST(MB, 8) W8_SQ(MB, 2) W8_SQ(MB, 4) W8_SQ(MB, 8)
 
 // Block_FP8's linear op quantizing in the K loop (XL 3): WN 1, WK in {2, 4,
 // 8}, tile_n 16 or 32, UNROLL 1 (the shapes it wins on; the bf16

@@ -3,7 +3,7 @@
     python -m bit_quantized_gemm_token_amd.tune_sweep --out TABLE [--formats ...]
            [--ops gemm,linear] [--layouts row,packed,seg2,seg4,seg8]
            [--shapes M,N,K;M,N,K...]
-           [--no-resume] [--max-split-k 256] [--top-n N]
+           [--no-resume] [--retune] [--max-split-k 256] [--top-n N]
            [--moe-shapes E,topk,T,N,K;...]
 
 Default shapes: the 24-shape M <= 32 sweep of synthetic.SWEEP plus the shapes
@@ -65,6 +65,9 @@ def main(argv=None):
     p.add_argument("--moe-shapes", default=None, help="E,topk,T,N,K;... for the MoE ops")
     p.add_argument("--shapes", default=None)
     p.add_argument("--no-resume", action="store_true")
+    p.add_argument("--retune", action="store_true",
+                   help="tune the selected ops, layouts and shapes again even where the table "
+                        "has an entry (the other entries are kept)")
     p.add_argument("--max-split-k", type=int, default=w8.MAX_SPLIT_K)
     p.add_argument("--rotate-mib", type=int, default=512)
     p.add_argument("--replays", type=int, default=5)
@@ -97,7 +100,7 @@ def main(argv=None):
                 jobs += [(op, fmt, s, packed, None) for s in shapes for packed in layouts
                          if a.all_m or packed < 2 or s[0] <= 32 // packed]
     for op, fmt, (M, N, K), packed, moe in jobs:
-        if w8.lookup_config(fmt, M, N, K, packed=packed, op=op) is not None:
+        if not a.retune and w8.lookup_config(fmt, M, N, K, packed=packed, op=op) is not None:
             skipped += 1
             continue
         if a.time_budget_s and time.time() - t0 > a.time_budget_s:

@@ -697,9 +697,10 @@ def test_moe_linear_argument_errors_and_config(w8, lib):
 
 
 def test_segmented_rules(w8):
-    """What the K-segmented layouts refuse: staged activations, waves along N,
-    stream-K, tiles that are not 1, 2 or 4 blocks of 16/T rows, a fused
-    linear op, and the grouped GEMM."""
+    """What the K-segmented layouts refuse: staged activation codes, waves
+    along N, stream-K, tiles that are not 1, 2 or 4 blocks of 16/T rows, a
+    linear op neither fused into LDS nor with a quantize launch, and the
+    grouped GEMM."""
     ok = w8.Config.make(tile_n=2, waves_k=2, unroll=2, split_k=1, swap_ab=1)
     w8.validate_config("FP8_Dynamic", 1, 512, 7168, ok, packed=8)
     for bad in (dict(x_lds=1), dict(waves_n=2, x_lds=1, waves_k=1), dict(grid=64, split_k=1),
@@ -707,10 +708,20 @@ def test_segmented_rules(w8):
         c = w8.Config.make(**{**ok.as_dict(), **bad})
         with pytest.raises(w8.W8Error):
             w8.validate_config("FP8_Dynamic", 1, 512, 7168, c, packed=8)
-    with pytest.raises(w8.W8Error):
+    with pytest.raises(w8.W8Error):    # fused linear: the activations quantized into LDS
         w8.validate_config("FP8_Dynamic", 1, 512, 7168, ok, op="linear", packed=8)
+    w8.validate_config("FP8_Dynamic", 1, 512, 7168, w8.Config.make(**{**ok.as_dict(), "x_lds": 1}),
+                       op="linear", packed=8)
+    with pytest.raises(w8.W8Error):    # ... with at most 4 K-waves
+        w8.validate_config("FP8_Dynamic", 1, 512, 7168,
+                           w8.Config.make(**{**ok.as_dict(), "x_lds": 1, "waves_k": 8}),
+                           op="linear", packed=8)
     w8.validate_config("FP8_Dynamic", 1, 512, 7168, w8.Config.make(**{**ok.as_dict(), "quant_launch": 1}),
                        op="linear", packed=8)
+    with pytest.raises(w8.W8Error):    # a quantize launch's GEMM loads its codes
+        w8.validate_config("FP8_Dynamic", 1, 512, 7168,
+                           w8.Config.make(**{**ok.as_dict(), "quant_launch": 1, "x_lds": 1}),
+                           op="linear", packed=8)
     with pytest.raises(w8.W8Error):
         w8.validate_config("FP8_Dynamic", 4, 512, 7168, ok, op="moe", packed=8)
 

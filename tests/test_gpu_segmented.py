@@ -9,8 +9,9 @@ oracle.
 - M beyond one launch (two token groups of 16/T rows) runs as consecutive
   launches, ragged N, K and spans reaching past K are masked;
 - the whole path (quantize + GEMM, and the linear op with a quantize
-  launch) within rtol = atol = 1e-2 of the fp64 oracle, also under graph
-  replay.
+  launch or with the quantization fused into the kernel, bit-identical to
+  the two calls) within rtol = atol = 1e-2 of the fp64 oracle, also under
+  graph replay.
 """
 import itertools
 
@@ -161,6 +162,52 @@ def test_segmented_ragged_and_chunked(w8, fmt, M, N, K, T):
             assert_bf16_close(yl, cs.Y, f"{fmt} T={T} linear")
         else:                                  # quantize launch + this GEMM config
             assert torch.equal(yl.view(torch.int16), y.view(torch.int16)), f"linear {cfg}"
+
+
+# (blocks per wave, waves_k, unroll) of the fused-quantization instances
+SEG_FUSED = ((1, 1, 1), (1, 1, 2), (1, 2, 1), (1, 2, 2), (1, 4, 1), (2, 1, 1), (2, 2, 1))
+
+
+@pytest.mark.parametrize("fmt", ["W8A8_INT8", "FP8_Dynamic", "Block_FP8"])
+@pytest.mark.parametrize("T", LAYOUTS)
+def test_segmented_fused_linear(w8, fmt, T):
+    """The linear op with the quantization fused (x_lds 1) on layout T: every
+    fused instance, whole tiles and split-K, at the ragged shape of
+    test_every_segmented_instance with M = 1 and M = 16/T + 1, and at M = 2 x
+    16/T + 3 (two launches plus a third of 3 rows); Y bit-identical to
+    quantize_act + gemm_w8a8 with the same tiles (x_lds 0), within the bar
+    of the oracle; rows of extreme magnitude too."""
+    import synthetic
+    from tests.gpu_cases import to_bf16_tensor
+    R = 16 // T
+    N, K = 193, (1152 if fmt == "Block_FP8" else 1040)
+    for M in (1, R + 1, 2 * R + 3):
+        cs = case(fmt, M, N, K)
+        wp = packed(w8, cs, T)
+        n = 0
+        for (nb, wk, u), swap, s in itertools.product(SEG_FUSED, (0, 1), (1, 4)):
+            if M > R + 1 and (nb, wk, u, s) != (1, 2, 1, 4):
+                continue                     # the multi-launch case: one config
+            kw = dict(tile_n=nb * R, waves_k=wk, unroll=u, split_k=s, swap_ab=swap)
+            cfg = C(w8, **kw, x_lds=1)
+            w8.validate_config(fmt, M, N, K, cfg, op="linear", packed=T)
+            y1 = w8.linear(fmt, cs.x, wp, cs.sw, cfg=cfg, fused=True)
+            xq, sx = w8.quantize_act(fmt, cs.x)
+            y2 = w8.gemm_w8a8(fmt, xq, sx, wp, cs.sw, cfg=C(w8, **kw))
+            torch.cuda.synchronize()
+            assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), f"{fmt} T={T} M={M} {cfg}"
+            n += 1
+        assert_bf16_close(y1, cs.Y, f"{fmt} T={T} M={M} fused")
+        assert n == (len(SEG_FUSED) * 4 if M <= R + 1 else 2)
+    x = to_bf16_tensor(synthetic.activations_extreme(fmt, R + 1, K))
+    cs = case(fmt, R + 1, N, K)
+    wp = packed(w8, cs, T)
+    kw = dict(tile_n=R, waves_k=2, unroll=2, split_k=2, swap_ab=1)
+    y1 = w8.linear(fmt, x, wp, cs.sw, cfg=C(w8, **kw, x_lds=1), fused=True)
+    xq, sx = w8.quantize_act(fmt, x)
+    y2 = w8.gemm_w8a8(fmt, xq, sx, wp, cs.sw, cfg=C(w8, **kw))
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), f"{fmt} T={T} extreme rows"
 
 
 def test_segmented_graph_replay(w8):
