@@ -180,9 +180,11 @@ def _cfg_str(c):
             f"sw{c['swap_ab']} xl{c['x_lds']}" + (f" g{c['grid']}" if c.get("grid") else ""))
 
 
-def summarize_trace(stats_csv, out_md, command):
+def summarize_trace(stats_csv, out_md, command, bench_json=None):
     """profiles/*.md from a rocprofv3 kernel_stats.csv: per kernel, calls,
-    total, average, min and max duration and share of the kernel time."""
+    total, average, min and max duration and share of the kernel time; with
+    the JSON line of an unprofiled bench run, its dominant kernel's trace
+    figures beside the bench's own average launch time."""
     import csv
     rows = []
     with open(stats_csv, newline="") as f:
@@ -203,6 +205,22 @@ def summarize_trace(stats_csv, out_md, command):
         short = name if len(name) <= 90 else name[:87] + "..."
         lines.append(f"| `{short}` | {calls} | {tot / 1e6:.2f} | {avg / 1e3:.3f} | "
                      f"{mn / 1e3:.3f} | {mx / 1e3:.3f} | {pct:.2f} |")
+    if bench_json:
+        with open(bench_json) as f:
+            line = json.loads(f.read().strip().splitlines()[-1])
+        rf = line["roofline"]
+        # rocprofv3 names it "void w8::gemm_kernel<...>(w8::GemmArgs)"
+        hit = [r for r in rows if "::" + rf["kernel"] + "(" in r[0]]
+        lines += ["", f"Dominant kernel of the bench line (`{rf['kernel']}`, "
+                  f"{len(rf['problems'])} problems: {', '.join(rf['problems'])}): "]
+        if hit:
+            name, calls, tot, avg, mn, mx, pct = hit[0]
+            lines[-1] += (f"rocprofv3 average {avg / 1e3:.3f} us over {calls} calls (min "
+                          f"{mn / 1e3:.3f}, max {mx / 1e3:.3f}); the unprofiled bench reports "
+                          f"avg_launch_us = {rf['avg_launch_us']} for it (graph replay, where "
+                          f"consecutive launches overlap head and tail).")
+        else:
+            lines[-1] += "not in this trace."
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     log(f"[bench] wrote {out_md} ({len(rows)} kernels)")
@@ -266,12 +284,15 @@ def summarize_mfma(manifest_path, counter_csv, out_md, command):
              "One counter run of `bench.py --counter-pass` (each problem's GEMM launched twice, "
              "synchronized after every launch).  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES (summed over "
              "the SIMDs) / (dispatch duration x 2.4 GHz x 1024 SIMDs).  Executed MFMA ops = MOPS "
-             "x 512 against the algorithmic 2MNK (an MFMA tile has 16 rows of M, so M < 16 pads), "
-             "and their rate against the dense fp8 / int8 MFMA peak (5.0 POP/s).", "",
+             "x 512 against the algorithmic 2MNK: one MFMA serves a group of token rows (16, "
+             "or 16/T on the K-segmented layout segT, whose MFMA keeps only T diagonal blocks of "
+             "its products), so executed / 2MNK = 16 x (token groups) / M, 16 at M = 1 on any "
+             "layout, more where a stage's first steps run masked; and their rate against the "
+             "dense fp8 / int8 MFMA peak (5.0 POP/s).", "",
              "Command (from /tmp on the MI355X box, repository at $R):", "", "```", command, "```",
-             "", "| format | M | N | K | config | dispatch us | MFMA busy % | executed MFMA ops | "
-             "2MNK | executed / 2MNK | TOP/s | % of peak |",
-             "|---|---:|---:|---:|---|---:|---:|---:|---:|---:|---:|---:|"]
+             "", "| format | M | N | K | layout | config | dispatch us | MFMA busy % | "
+             "executed MFMA ops | 2MNK | executed / 2MNK | TOP/s | % of peak |",
+             "|---|---:|---:|---:|---|---|---:|---:|---:|---:|---:|---:|---:|"]
     for i, pr in enumerate(man["problems"]):
         es = acc.get(i, [])
         if not es:
@@ -283,7 +304,8 @@ def summarize_mfma(manifest_path, counter_csv, out_md, command):
         alg = 2 * pr["M"] * pr["N"] * pr["K"]
         busy_pct = 100 * busy / (ns * 2.4 * 1024) if ns else 0.0
         tops = mops / ns / 1e3 if ns else 0.0
-        lines.append(f"| {pr['fmt']} | {pr['M']} | {pr['N']} | {pr['K']} | {_cfg_str(pr['cfg'])} | "
+        lines.append(f"| {pr['fmt']} | {pr['M']} | {pr['N']} | {pr['K']} | "
+                     f"{pr.get('layout', '')} | {_cfg_str(pr['cfg'])} | "
                      f"{ns / 1e3:.2f} | {busy_pct:.2f} | {mops:,.0f} | {alg:,} | {mops / alg:.2f} | "
                      f"{tops:.1f} | {100 * tops / 5000:.2f} |")
     with open(out_md, "w") as f:
@@ -326,6 +348,9 @@ def parse():
                    metavar=("MANIFEST", "COUNTER_CSV", "OUT_MD"),
                    help="write the MFMA-utilisation summary from a counter pass with "
                         "SQ_VALU_MFMA_BUSY_CYCLES and SQ_INSTS_VALU_MFMA_MOPS_F8/_I8, then exit")
+    p.add_argument("--bench-line", default=None, metavar="JSON",
+                   help="with --summarize-trace: an unprofiled bench run's output line, whose "
+                        "dominant kernel the summary reports")
     p.add_argument("--summary-command", default="",
                    help="the command that made the profile, recorded in the summary")
     return p.parse_args()
@@ -709,7 +734,7 @@ def main():
         ingest_counters(*args.ingest_counters, PMC_FILE, args.ingest_command)
         return
     if args.summarize_trace:
-        summarize_trace(*args.summarize_trace, args.summary_command)
+        summarize_trace(*args.summarize_trace, args.summary_command, args.bench_line)
         return
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic)
