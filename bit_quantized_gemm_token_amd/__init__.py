@@ -241,8 +241,9 @@ def workspace_size(fmt, M, N, K, cfg=None, packed=False, op="gemm"):
 class Workspace:
     """Device workspace for split-K and the linear op's quantize launch.
 
-    Zero-filled when (re)allocated; the GEMM leaves its counters at zero after
-    each call, so one Workspace can serve any sequence of calls on one stream
+    Zero-filled when (re)allocated; the GEMM leaves its arrival counters at
+    multiples of 256 after each call (which is all a call needs of them), so
+    one Workspace can serve any sequence of calls on one stream
     (calls that overlap on several streams race).
 
     Under HIP graph capture the workspace cannot grow: the fill would be

@@ -242,7 +242,7 @@ LinearWs linear_ws(int fmt, int M, int N, int K, const w8_cfg& c, int layout) {
   LinearWs w;
   w.ldq = (K + 15) / 16 * 16;
   // past the arrival counters even when this config shares no tile: another
-  // call on the same workspace may need them at zero
+  // call on the same workspace relies on their values
   w.codes = round256(std::max(gemm_ws_bytes(fmt, M, N, K, c, layout), ws_counter_bytes(0)));
   w.scales = w.codes + round256((size_t)M * w.ldq);
   const size_t nsx = fmt == W8_BLOCK_FP8 ? (size_t)M * (K / W8_GROUP) : (size_t)M;
@@ -460,9 +460,10 @@ w8_status gemm_entry(int fmt, int M, int N, int K, const void* xq, int64_t ldq,
 // ------------------------------------------------ the no-allocation entry --
 // w8_gemm_w8a8_noalloc keeps the split-K workspace (arrival counters, then
 // partials) in this file-scope device array instead of a caller's buffer.
-// The loader zero-fills it on each device; every call leaves its counters at
-// zero again, and the partials are written before they are read, so nothing
-// needs clearing between calls.  Its host-side name is not a device
+// The loader zero-fills it on each device; every call leaves its arrival
+// counters at multiples of 256 (the split-K counters rise by 256 a launch,
+// the stream-K ones return to zero), and the partials are written before
+// they are read, so nothing needs clearing between calls.  Its host-side name is not a device
 // address: the address comes from hipGetSymbolAddress, once per device.
 constexpr size_t kScratchBytes = (size_t)16 << 20;  // 2 MiB of counters + 14 MiB of partials
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];

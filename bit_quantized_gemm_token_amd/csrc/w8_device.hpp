@@ -134,6 +134,25 @@ __device__ __forceinline__ float seg16_max(float v) {
   return v;
 }
 
+// ------------------------------------------------- device-coherent I/O --
+// Buffer loads and stores of 16 bytes a lane with the agent-scope cache
+// policy (SC1): the same bits the compiler sets on agent-scope atomic loads
+// and stores, so a store is written through to the level the whole device
+// shares and a load is served from it, whichever XCD the other side ran on.
+// One instruction moves 1 KiB of a wave where the 4-byte atomic forms would
+// take four.  `base` must be 4-byte aligned and the offsets below `bytes`.
+constexpr int kCpolAgent = 16;  // SC1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ v4i coherent_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolAgent);
+}
+__device__ __forceinline__ void coherent_store16(__amdgpu_buffer_rsrc_t r, int off, v4i v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolAgent);
+}
+
 // ------------------------------------------------------------------- MFMA --
 // 16x16 output tile; lane l holds column l%16, rows 4*(l/16) .. 4*(l/16)+3.
 // A and B operands: lane l supplies row (A) / column (B) l%16 and one slice

@@ -64,8 +64,7 @@
 //          the accumulator-to-lane map and so the epilogue's store pattern.
 //   Split-K / shared tiles  each contributing workgroup writes its partial
 //          tile to the workspace; the last one of the tile to arrive (arrival
-//          counter) sums the partials in K order, runs the epilogue and
-//          resets the counter.  The fixed order makes results run-to-run
+//          counter) sums the partials in K order and runs the epilogue.  The fixed order makes results run-to-run
 //          deterministic; empty splits (split_k > number of K-steps)
 //          contribute zeros.
 //   Block_FP8  K-step = one 128-wide group: each group's MFMA starts from
@@ -710,32 +709,33 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
     // Several workgroups cover this tile: publish the partial; the last
     // workgroup to arrive sums them in slot (= K) order.
     // Protocol (no L2 writeback or invalidate): the partials are written with
-    // agent-scope atomic stores, which write through this XCD's L2 to the
+    // agent-scope (SC1) stores, which write through this XCD's L2 to the
     // device-coherent level; s_waitcnt waits until every one of them is
     // acknowledged before the workgroup counts itself in; the last workgroup
-    // to arrive reads the partials with agent-scope atomic loads, which are
+    // to arrive reads the partials with agent-scope (SC1) loads, which are
     // served from the device-coherent level, so it sees every slot's data.
     // (An agent-scope release on the count and acquire in the last arriver
     // would write back and invalidate whole L2s: measured 1.5 to 9 us more
-    // per launch.)  Partial layout: fragment f = ((tile*slots + slot)*WN*NB +
-    // wn*NB + j)*MB + b holds 4 x 64 words, word (f*4 + i)*64 + lane, so each
-    // of the four stores of a wave writes 256 contiguous bytes.
+    // per launch.)  Partial layout: the tile's slots * WN * NB * MB fragments
+    // of 1 KiB, fragment ((slot * WN + wn) * NB + j) * MB + b holding lane
+    // l's four accumulator words at 16 l, so one store or load instruction
+    // of a wave moves 1 KiB contiguous.
     bool store = true;
     if (count > 1) {
-      typedef decltype(acc[0][0][0]) Elem;
-      typedef typename std::remove_cv<typename std::remove_reference<Elem>::type>::type Word;
-      Word* part = reinterpret_cast<Word*>(a.part);
-      const long long f0 = ((long long)tile * a.slots * WN + wn) * NB;  // + slot*WN*NB + j
+      // fragments per tile: slots <= 256 (split-K) or <= K-steps <= 2^16
+      // (stream-K, WN * NB * MB <= 16 there), so byte offsets fit in 31 bits
+      const int tfrags = a.slots * WN * NB * MB;
+      const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(
+          static_cast<char*>(a.part) + (long long)tile * tfrags * 1024, tfrags * 1024);
+      auto foff = [&](int sl, int j, int b) {
+        return (((sl * WN + wn) * NB + j) * MB + b) * 1024 + 16 * lane;
+      };
       if (wk == 0) {
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
           for (int b = 0; b < MB; ++b)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              __hip_atomic_store(
-                  part + (((f0 + (long long)slot * WN * NB + j) * MB + b) * 4 + i) * 64 + lane,
-                  acc[b][j][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            coherent_store16(prs, foff(slot, j, b), __builtin_bit_cast(v4i, acc[b][j]));
       }
       // The compiler may not move memory operations across the wait (the
       // signal fences); the hardware keeps the order: s_waitcnt vmcnt(0)
@@ -745,10 +745,19 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
       __builtin_amdgcn_s_waitcnt(0);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __syncthreads();
+      // Arrival counting.  Split-K (count = split_k, a power of two <= 256):
+      // each contributor adds 256 / count to word 0 of the tile's counter
+      // line, so a launch raises it by exactly 256 and the counter is never
+      // reset (it stays a multiple of 256 between launches; a zero-filled
+      // workspace starts it so); the contributor that completes a multiple
+      // of 256 is the last.  Stream-K (any count): word 1 counts from zero
+      // and the last contributor resets it.
+      unsigned* ctr = a.counters + (long long)tile * kCounterWords + (SK ? 1 : 0);
       if (threadIdx.x == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(&a.counters[tile * kCounterWords], 1u,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        is_last = (prev == (unsigned)(count - 1));
+        const unsigned inc = SK ? 1u : 256u / (unsigned)count;
+        const unsigned prev =
+            __hip_atomic_fetch_add(ctr, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = SK ? prev == (unsigned)(count - 1) : ((prev + inc) & 255u) == 0u;
       }
       __syncthreads();
       store = is_last;
@@ -759,40 +768,33 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
           for (int b = 0; b < MB; ++b)
 #pragma unroll
             for (int j = 0; j < NB; ++j) acc[b][j] = Acc{0, 0, 0, 0};
-          // Slots are read in batches of Q, all loads of a batch in flight
-          // at once (a slot past the end rereads the last one and adds 0),
-          // then added in slot order.
-          constexpr int Q = (NB * MB >= 8) ? 1 : 8 / (NB * MB);
+          // Slots are read in batches of up to Q (at most 16 fragments, all
+          // loads of a batch in flight at once), then added in slot order.
+          constexpr int Q = (NB * MB >= 16) ? 1 : 16 / (NB * MB);
           for (int s0 = 0; s0 < count; s0 += Q) {
-            Word v[Q][NB][MB][4];
+            v4i v[Q][NB][MB];
 #pragma unroll
             for (int q = 0; q < Q; ++q) {
-              const long long sl = min(s0 + q, count - 1);
+              if (s0 + q < count) {  // (wave-uniform)
 #pragma unroll
-              for (int j = 0; j < NB; ++j)
+                for (int j = 0; j < NB; ++j)
 #pragma unroll
-                for (int b = 0; b < MB; ++b)
-#pragma unroll
-                  for (int i = 0; i < 4; ++i)
-                    v[q][j][b][i] = __hip_atomic_load(
-                        part + (((f0 + sl * WN * NB + j) * MB + b) * 4 + i) * 64 + lane,
-                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                  for (int b = 0; b < MB; ++b) v[q][j][b] = coherent_load16(prs, foff(s0 + q, j, b));
+              }
             }
 #pragma unroll
             for (int q = 0; q < Q; ++q) {
-              const bool in = s0 + q < count;
+              if (s0 + q < count) {
 #pragma unroll
-              for (int j = 0; j < NB; ++j)
+                for (int j = 0; j < NB; ++j)
 #pragma unroll
-                for (int b = 0; b < MB; ++b)
-#pragma unroll
-                  for (int i = 0; i < 4; ++i) acc[b][j][i] += in ? v[q][j][b][i] : Word(0);
+                  for (int b = 0; b < MB; ++b) acc[b][j] += __builtin_bit_cast(Acc, v[q][j][b]);
+              }
             }
           }
         }
-        if (threadIdx.x == 0)
-          __hip_atomic_store(&a.counters[tile * kCounterWords], 0u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+        if (SK && threadIdx.x == 0)
+          __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     if (!store || wk != 0) return;

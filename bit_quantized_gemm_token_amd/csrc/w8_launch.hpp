@@ -136,7 +136,9 @@ constexpr int kXlMaxGroups = kXlChunks / 2;
 // split_k slots per tile for Split-K and stream_k_slots() for stream-K.  The
 // counter region has the same size for every shape, so the partials of one
 // call never overlap the counters of another call that shares the
-// workspace: counters left at zero stay zero.
+// workspace, which keeps every counter at a multiple of 256 between calls
+// (a Split-K launch adds exactly 256 to each of its tiles' counters; a
+// stream-K launch counts in the line's second word and resets it).
 constexpr int kSplitKMaxTiles = 16384;
 constexpr int kCounterWords = 32;  // counter stride, 128 bytes
 inline size_t ws_counter_bytes(int ntiles) {

@@ -59,7 +59,7 @@ size_t part_stride(int fmt, int max_m, int N, int K, const w8_cfg& c) {
 
 // w8_moe_linear with quant_launch: the T tokens' codes and scales follow the
 // shared-tile region of the workspace (past the arrival counters even when
-// no tile is shared: another call on the workspace may need them at zero).
+// no tile is shared: another call on the workspace relies on their values).
 struct MoeQuantWs {
   size_t codes, scales, total;
   long long ldq;

@@ -273,7 +273,7 @@ w8_status w8_pack_weight(w8_fmt fmt, int N, int K, const void *wq, int64_t ldw, 
  * tiles, so split_k > 1 and grid > 0 support at most 16384 output tiles
  * (N <= 16384 * tile_n * waves_n).  The linear op with quant_launch == 1
  * adds, after the GEMM's part and never below the 2 MiB counter region (so a
- * workspace shared by any sequence of calls keeps its counters at zero),
+ * workspace shared by any sequence of calls keeps its counters intact),
  * the codes (M rows of K rounded up to 16 bytes) and the scales of the
  * activations, each region 256-byte aligned.                               */
 w8_status w8_workspace_size(w8_fmt fmt, w8_op op, int M, int N, int K, int packed,
@@ -291,8 +291,11 @@ w8_status w8_workspace_size(w8_fmt fmt, w8_op op, int M, int N, int K, int packe
  *           (fmt, weight layout, M, N, K): table entry, M-bucket entry or
  *           the cost model's pick
  *   ws      workspace of at least w8_workspace_size() bytes, zero-filled
- *           before its first use; every completed call leaves its counters
- *           at zero again.  May be NULL when the size is 0.  Calls that share
+ *           before its first use; every completed call leaves its arrival
+ *           counters at multiples of 256 (split-K adds 256 to each of its
+ *           tiles' counters per call, stream-K returns its own to zero), the
+ *           state the next call needs, so it is never cleared again.  May be
+ *           NULL when the size is 0.  Calls that share
  *           a workspace must not run concurrently.
  * Requires 1 <= M <= 32 (else W8_E_UNSUPPORTED), N >= 1, K >= 16,
  * K % 16 == 0 (Block_FP8: K % 128 == 0), ldq >= K, ldy >= N, xq/wq 16-byte

@@ -239,4 +239,5 @@ def test_segmented_graph_replay(w8):
         junk = torch.randn(256, 256, device=DEV) @ torch.randn(256, 256, device=DEV)
         del junk
     assert_bf16_close(y, cs.Y, "segmented graph replay")
-    assert (ws.buf[:16384 * 128].cpu() == 0).all()
+    # split-K arrival counters: multiples of 256 after every call
+    assert (ws.buf[:16384 * 128].view(torch.int32).cpu() % 256 == 0).all()
