@@ -235,6 +235,10 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
   const int nthreads = 64 * WK * WN;
   __shared__ Acc red[WK > 1 ? (WK - 1) * MB * NB * 64 : 1];
   __shared__ v4i xl[(XL == 1 || XL == 2) ? kXlChunks * 64 : 1];
+  // XL == 1, Block_FP8: the segment's activation scales, group-major
+  // (entry kk * 16 * MB + row for K-step ka + kk), staged with the codes
+  // (at most kXlChunks / 2 K-steps of 32 rows, plus a partial last copy).
+  __shared__ float sxs[(XL == 1 && BLOCK) ? kXlMaxGroups * 32 + 64 : 1];
   // XL == 2: activation scales computed here -- per row for the per-token
   // formats, per (staged group, row) for Block_FP8.
   __shared__ float sxl[XL == 2 ? (BLOCK ? kXlMaxGroups * 32 : 32) : 1];
@@ -391,8 +395,11 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
       Frag w[U][NB];
       Frag x[XL ? 1 : U][MB];  // !XL: the wave's own activation fragments
       v4u xb[XL == 3 ? U : 1][XL == 3 ? MB : 1][CH][2];  // XL == 3: bf16, quantized in run_stage
+      // Block_FP8 scales of each K-step: the weight scale, and for XL == 0
+      // the activation scale of each accumulator row (XL == 1 stages them in
+      // LDS with the codes, XL >= 2 computes them in the kernel).
       float sw[BLOCK ? U : 1];
-      float sx[BLOCK ? U : 1][MB][SXN];
+      float sx[BLOCK && XL == 0 ? U : 1][MB][SXN];
     };
     auto load_stage = [&](Stage& st, int k0) {
 #pragma unroll
@@ -418,8 +425,14 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
           // group of the lane's own K-step (K-segmented: the group of the
           // products the lane keeps, K-step k*T + tl)
           const int kg = k * T + tl;
-          st.sw[u] = swrow[kg];
-          if constexpr (XL < 2) {  // XL >= 2: scales computed here (LDS or registers)
+          if constexpr (T == 1) {
+            // one value for the whole wave (its rows lie in one 128-row
+            // block): a scalar load, off the vector-memory path
+            st.sw[u] = *(const __attribute__((address_space(4))) float*)(swrow + kg);
+          } else {
+            st.sw[u] = swrow[kg];
+          }
+          if constexpr (XL == 0) {
 #pragma unroll
             for (int b = 0; b < MB; ++b)
 #pragma unroll
@@ -428,8 +441,9 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
         }
       }
     };
-    auto step = [&](const Frag (&w)[NB], const Frag (&x)[MB], float sw,
-                    const float (&sx)[MB][SXN]) {
+
+    // sc: Block_FP8's sx * sw of each accumulator element (ignored otherwise)
+    auto step = [&](const Frag (&w)[NB], const Frag (&x)[MB], const float (&sc)[MB][SXN]) {
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
@@ -437,7 +451,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
           if constexpr (BLOCK) {
             const Acc p = mma<FMT, SWAP>(w[j], x[b], Acc{0, 0, 0, 0});
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[b][j][i] += p[i] * (sx[b][SWAP ? 0 : i] * sw);
+            for (int i = 0; i < 4; ++i) acc[b][j][i] += p[i] * sc[b][SWAP ? 0 : i];
           } else {
             acc[b][j] = mma<FMT, SWAP>(w[j], x[b], acc[b][j]);
           }
@@ -479,9 +493,10 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
             }
             x[b] = __builtin_shufflevector(q[0], q[1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-            for (int i = 0; i < SXN; ++i) sx[b][i] = SWAP ? sc : __shfl(sc, 4 * g + i, 64);
+            for (int i = 0; i < SXN; ++i)
+              sx[b][i] = (SWAP ? sc : __shfl(sc, 4 * g + i, 64)) * st.sw[u];
           }
-          step(w, x, st.sw[u], sx);
+          step(w, x, sx);
         } else if constexpr (XL) {
           const int k = max(k0 + u, la);
           Frag x[MB];
@@ -496,19 +511,37 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
               x[b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
           }
+          float sc[MB][SXN] = {};
           if constexpr (XL == 2 && BLOCK) {
-            float sx[MB][SXN];
 #pragma unroll
             for (int b = 0; b < MB; ++b)
 #pragma unroll
               for (int i = 0; i < SXN; ++i)
-                sx[b][i] = sxl[((k - ka) * MB + b) * 16 + (SWAP ? r : tl * R + (4 * g + i) % R)];
-            step(w, x, st.sw[u], sx);
-          } else {
-            step(w, x, st.sw[BLOCK ? u : 0], st.sx[BLOCK ? u : 0]);
+                sc[b][i] =
+                    sxl[((k - ka) * MB + b) * 16 + (SWAP ? r : tl * R + (4 * g + i) % R)] * st.sw[u];
+          } else if constexpr (BLOCK) {  // XL == 1 (T == 1): the staged scales
+#pragma unroll
+            for (int b = 0; b < MB; ++b) {
+              const int e = (k - ka) * 16 * MB + 16 * b;
+              if constexpr (SWAP) {
+                sc[b][0] = sxs[e + r] * st.sw[u];
+              } else {
+                const v4f v = *reinterpret_cast<const v4f*>(&sxs[e + 4 * g]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sc[b][i] = v[i] * st.sw[u];
+              }
+            }
           }
+          step(w, x, sc);
         } else {
-          step(w, st.x[u], st.sw[BLOCK ? u : 0], st.sx[BLOCK ? u : 0]);
+          float sc[MB][SXN] = {};
+          if constexpr (BLOCK) {
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+#pragma unroll
+              for (int i = 0; i < SXN; ++i) sc[b][i] = st.sx[u][b][i] * st.sw[u];
+          }
+          step(w, st.x[u], sc);
         }
       }
     };
@@ -526,6 +559,19 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
                              (long long)(ka + kk) * KSTEP + 64 * jj;
         __builtin_amdgcn_global_load_lds(
             src, (__attribute__((address_space(3))) void*)(xl + c * 64), 16, 0, 0);
+      }
+      if constexpr (BLOCK) {
+        // and the scales of the segment's rows and groups, 64 a load
+        // (Block_FP8: K % 128 == 0, so every K-step is whole; the entries
+        // past the end of the last copy reread the last one)
+        const int nsx = (kb - ka) * 16 * MB;
+        for (int c = wave * 64; c < nsx; c += 64 * WK * WN) {
+          const int e = min(c + lane, nsx - 1);
+          const int kk = e / (16 * MB), row = e % (16 * MB);
+          const float* src = a.sx + xr(min(row, a.M - 1)) * a.sgroups + ka + kk;
+          __builtin_amdgcn_global_load_lds(
+              src, (__attribute__((address_space(3))) void*)(sxs + c), 4, 0, 0);
+        }
       }
     }
 
@@ -684,7 +730,12 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
             xt[b] = load_frag_tail<FMT>(xrow[b], a.kfull * T, tl * KSTEP + 16 * g, a.K);
           }
         }
-        step(wt, xt, tsw, tsx);
+        float tsc[MB][SXN];
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+#pragma unroll
+          for (int i = 0; i < SXN; ++i) tsc[b][i] = tsx[b][i] * tsw;
+        step(wt, xt, tsc);
       }
     }
 
@@ -815,42 +866,76 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
         for (int b = 0; b < MB; ++b)
           *reinterpret_cast<Acc*>(d + ((j * MB + b) * 16 + r) * 16 + 4 * g) = acc[b][j];
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      // Every value first, then the stores (see the plain epilogue below).
+      Word vv[OPL];
+      uint16_t yb[OPL];
+#pragma unroll
+      for (int q = 0; q < OPL; ++q) {
+        const int o = min(lane + 64 * q, NOUT - 1);
+        const int jb = o / (R * R), m = (o / R) % R, rr = o % R;
+        Word v = 0;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          v += SWAP ? d[(jb * 16 + t * R + m) * 16 + t * R + rr]
+                    : d[(jb * 16 + t * R + rr) * 16 + t * R + m];
+        vv[q] = v;
+        float y;
+        if constexpr (BLOCK) {
+          y = v;
+        } else {
+          float sxv;
+          if constexpr (XL == 2)  // from the row pass's absolute maximum of row mm
+            sxv = act_scale<INT8>(__uint_as_float(
+                reinterpret_cast<const unsigned*>(sxl)[min(R * (jb % MB) + m, a.M - 1)]));
+          else
+            sxv = ep2_sx[q];
+          y = (float)v * sxv * ep2_sw[q];
+        }
+        yb[q] = bf16_rne(y);
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // (see the plain epilogue below)
 #pragma unroll
       for (int q = 0; q < OPL; ++q) {
         const int o = lane + 64 * q;
-        if (o < NOUT) {
-          const int jb = o / (R * R), m = (o / R) % R, rr = o % R;
-          Word v = 0;
-#pragma unroll
-          for (int t = 0; t < T; ++t)
-            v += SWAP ? d[(jb * 16 + t * R + m) * 16 + t * R + rr]
-                      : d[(jb * 16 + t * R + rr) * 16 + t * R + m];
-          const int mm = R * (jb % MB) + m, n = n0 + R * (jb / MB) + rr;
-          if (mm < a.M && n < a.N) {
-            const long long off = (long long)mm * a.ldo + n;
-            if (a.out_mode) {
-              reinterpret_cast<Word*>(a.out)[off] = v;
-            } else {
-              float y;
-              if constexpr (BLOCK) {
-                y = v;
-              } else {
-                float sxv;
-                if constexpr (XL == 2)  // from the row pass's absolute maximum of row mm
-                  sxv = act_scale<INT8>(__uint_as_float(reinterpret_cast<const unsigned*>(sxl)[mm]));
-                else
-                  sxv = ep2_sx[q];
-                y = (float)v * sxv * ep2_sw[q];
-              }
-              reinterpret_cast<uint16_t*>(a.out)[off] = bf16_rne(y);
-            }
-          }
+        const int jb = o / (R * R), m = (o / R) % R, rr = o % R;
+        const int mm = R * (jb % MB) + m, n = n0 + R * (jb / MB) + rr;
+        if (o < NOUT && mm < a.M && n < a.N) {
+          const long long off = (long long)mm * a.ldo + n;
+          if (a.out_mode)
+            reinterpret_cast<Word*>(a.out)[off] = vv[q];
+          else
+            reinterpret_cast<uint16_t*>(a.out)[off] = yb[q];
         }
       }
       return;
     }
 
-    // Epilogue.
+    // Epilogue: every value first, then one wait for all outstanding loads,
+    // then the stores.  (Without the explicit wait the compiler re-waited
+    // vmcnt(0) at the top of every guarded store: a lane-empty branch may
+    // skip a block, so at each join it still counts earlier loads as
+    // pending, and on gfx9 vmcnt(0) also waits for the stores issued
+    // before -- the stores went out one at a time, ~0.6 us for eight.)
+    uint16_t yb[MB][NB][4];
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float y;
+          if constexpr (BLOCK) {
+            y = acc[b][j][i];
+          } else {
+            const float sxm = ep_sx[b][SWAP ? 0 : i], swn = ep_sw[j][SWAP ? i : 0];
+            if constexpr (FMT == W8A8_INT8)
+              y = (float)acc[b][j][i] * sxm * swn;
+            else
+              y = acc[b][j][i] * sxm * swn;
+          }
+          yb[b][j][i] = bf16_rne(y);
+        }
+    __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
     for (int b = 0; b < MB; ++b)
 #pragma unroll
@@ -870,17 +955,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
               else
                 reinterpret_cast<float*>(a.out)[o] = acc[b][j][i];
             } else {
-              float y;
-              if constexpr (BLOCK) {
-                y = acc[b][j][i];
-              } else {
-                const float sxm = ep_sx[b][SWAP ? 0 : i], swn = ep_sw[j][SWAP ? i : 0];
-                if constexpr (FMT == W8A8_INT8)
-                  y = (float)acc[b][j][i] * sxm * swn;
-                else
-                  y = acc[b][j][i] * sxm * swn;
-              }
-              reinterpret_cast<uint16_t*>(a.out)[o] = bf16_rne(y);
+              reinterpret_cast<uint16_t*>(a.out)[o] = yb[b][j][i];
             }
           }
         }
