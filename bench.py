@@ -226,6 +226,62 @@ def summarize_trace(stats_csv, out_md, command, bench_json=None):
     log(f"[bench] wrote {out_md} ({len(rows)} kernels)")
 
 
+PHASE_PROBE = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                           "bit_quantized_gemm_token_amd", "w8_phase_probe")
+
+
+def phase_study(out_md, command, only=None):
+    """profiles/*.md from the phase probe (built beside the library from
+    csrc/w8_phase_probe.hip): per configuration, the per-launch time of a
+    graph replay and where it goes, from s_memrealtime stamps the probe's
+    build of the kernel records at its phase boundaries."""
+    import subprocess
+    if not os.path.exists(PHASE_PROBE):
+        raise SystemExit(f"{PHASE_PROBE} is missing: build the package first")
+    cmd = [PHASE_PROBE] + ([only] if only else [])
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        raise SystemExit(f"phase probe failed ({r.returncode}):\n{r.stderr}")
+    rows = [json.loads(l) for l in r.stdout.splitlines() if l.startswith("{")]
+    lines = ["# Where one GEMM launch's time goes (phase probe)", "",
+             "Command (on the MI355X box, repository at $R):", "", "```", command, "```", "",
+             "`w8_phase_probe` replays each configuration from a HIP graph as the benchmark does "
+             "(R launches on R weight copies spanning >= 1 GiB) and times the graph with HIP "
+             "events (`us/launch`).  Its build of the GEMM kernel records `s_memrealtime` "
+             "(100 MHz, common to the whole device) at the phase boundaries of every workgroup "
+             "(`W8_PHASE_STAMPS`, see `csrc/w8_gemm.hpp`); from one more replay, averaged over "
+             "the launches:", "",
+             "- `gap`: from the previous launch's last workgroup finishing to this launch's "
+             "first workgroup starting (the launch cost under graph replay);",
+             "- `in-kernel`: first workgroup start to last workgroup end; `start spread`: first "
+             "to last workgroup start;",
+             "- `loop w0` / `loop max`: K loop of wave 0 / of the workgroup's slowest wave, from "
+             "the workgroup's start; `K-sum`: summing the K-waves through LDS after the slowest "
+             "wave (workgroups whose waves split K);",
+             "- shared tiles (split-K): `ack` the partial stores acknowledged, `count` the "
+             "arrival counter's round trip, `last` the last arriver's partial reads, epilogue "
+             "and stores;",
+             "- owned tiles: `epilogue` from the K-sum to the stores completed.", "",
+             "Stamps of the phases that end in a wait (`last`, `epilogue`) are taken after the "
+             "wave's outstanding memory operations complete; the kernels of the library have "
+             "no stamps.", "",
+             "| configuration | grid | block | us/launch | gap | in-kernel | start spread | "
+             "loop w0 | loop max | K-sum | ack | count | last | epilogue |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for q in rows:
+        split = q["ack_us"] > 0
+        f = lambda k, on=True: f"{q[k]:.2f}" if on else "-"
+        lines.append(f"| {q['name']} | {q['grid']} | {q['block']} | {q['us_per_launch']:.2f} | "
+                     f"{f('gap_us')} | {f('in_kernel_us')} | {f('start_spread_us')} | "
+                     f"{f('loop_wave0_us')} | {f('loop_slowest_wave_us')} | "
+                     f"{f('kwave_sum_us', q['waves_k'] > 1)} | "
+                     f"{f('ack_us', split)} | {f('count_us', split)} | "
+                     f"{f('last_arriver_us', split)} | {f('epilogue_us', not split)} |")
+    with open(out_md, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    log(f"[bench] wrote {out_md} ({len(rows)} configurations)")
+
+
 def summarize_traffic(out_md):
     """The HBM-traffic table from the counter file that measured_traffic() reads."""
     import bit_quantized_gemm_token_amd as w8
@@ -348,6 +404,8 @@ def parse():
                    metavar=("MANIFEST", "COUNTER_CSV", "OUT_MD"),
                    help="write the MFMA-utilisation summary from a counter pass with "
                         "SQ_VALU_MFMA_BUSY_CYCLES and SQ_INSTS_VALU_MFMA_MOPS_F8/_I8, then exit")
+    p.add_argument("--phases", default=None, metavar="OUT_MD",
+                   help="run the phase probe (w8_phase_probe) and write its summary, then exit")
     p.add_argument("--bench-line", default=None, metavar="JSON",
                    help="with --summarize-trace: an unprofiled bench run's output line, whose "
                         "dominant kernel the summary reports")
@@ -741,6 +799,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma, args.summary_command)
+        return
+    if args.phases:
+        phase_study(args.phases, args.summary_command)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "

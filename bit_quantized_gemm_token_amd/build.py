@@ -2,7 +2,9 @@
 
 Compiles every translation unit under csrc/ with hipcc in parallel and links
 them into bit_quantized_gemm_token_amd/libw8gemm.so.  The GEMM instance file is
-compiled once per (format, swap_ab, part).  Flags:
+compiled once per (format, swap_ab, part).  Beside it, the phase probe
+(csrc/w8_phase_probe.hip: the GEMM kernel with timing stamps, a timing-study
+executable, not part of the library) is built as w8_phase_probe.  Flags:
   -fhip-fp32-correctly-rounded-divide-sqrt  the quantizer's x / s is the IEEE
                                             correctly rounded division
   -Xclang -target-feature -Xclang -packed-fp32-ops
@@ -19,6 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libw8gemm.so")
+PROBE = os.path.join(HERE, "w8_phase_probe")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 ARCH = "gfx950"
@@ -63,14 +66,28 @@ def _compile(unit, verbose):
     return out
 
 
+def _build_probe(verbose):
+    tmp = PROBE + ".tmp"
+    cmd = [HIPCC, *[f for f in FLAGS if f != "-fPIC"], os.path.join(CSRC, "w8_phase_probe.hip"),
+           "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on w8_phase_probe.hip:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, PROBE)
+
+
 def build(verbose: bool = False, jobs: int = 0) -> str:
     os.makedirs(OBJ, exist_ok=True)
     units = _units()
     jobs = jobs or min(len(units), max(1, min(os.cpu_count() or 4, 8)))
     with cf.ThreadPoolExecutor(jobs) as ex:
+        probe = ex.submit(_build_probe, verbose)
         for msg in ex.map(lambda u: _compile(u, verbose), units):
             if msg and verbose:
                 print(msg, flush=True)
+        probe.result()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
            f"-Wl,--version-script={os.path.join(CSRC, 'w8gemm.map')}",

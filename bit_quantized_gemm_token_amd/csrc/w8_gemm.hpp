@@ -82,6 +82,51 @@
 #include "w8_device.hpp"
 #include "w8_launch.hpp"
 
+// Phase stamps, for timing studies only: unless W8_PHASE_STAMPS is defined
+// (the library never defines it; csrc/w8_phase_probe.hip does) they compile
+// to nothing.  Defined, thread 0 of each workgroup -- and lane 0 of each
+// wave for the end of its K loop -- records s_memrealtime (a 100 MHz
+// counter common to the whole device) into a record of 32 words per
+// workgroup that starts W8_PHASE_STAMPS bytes past the output: word 0 the
+// segment's start, 1 wave 0's K loop done, 2 the K-waves summed, 3 the
+// partials acknowledged, 4 the arrival count returned, 6 the output stored
+// (the workgroup that owns its tile or is the last to arrive), 7 done
+// without storing, 8 + w the end of wave w's K loop.  Words 6 and 7 are
+// taken after the stores and loads in flight have completed.
+#ifdef W8_PHASE_STAMPS
+#define W8_STAMP_AT(slot)                                                              \
+  do {                                                                                 \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);                                           \
+    reinterpret_cast<unsigned long long*>(static_cast<char*>(a.out) +                  \
+                                          W8_PHASE_STAMPS)[blockIdx.x * 32 + (slot)] = \
+        __builtin_amdgcn_s_memrealtime();                                              \
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);                                           \
+  } while (0)
+#define W8_STAMP(i)                        \
+  do {                                     \
+    if (threadIdx.x == 0) W8_STAMP_AT(i); \
+  } while (0)
+#define W8_STAMP_DONE(i)                 \
+  do {                                   \
+    __builtin_amdgcn_s_waitcnt(0);       \
+    W8_STAMP(i);                         \
+  } while (0)
+#define W8_STAMP_WAVE()                                                   \
+  do {                                                                    \
+    if ((threadIdx.x & 63) == 0) W8_STAMP_AT(8 + (int)(threadIdx.x >> 6)); \
+  } while (0)
+#else
+#define W8_STAMP(i) \
+  do {              \
+  } while (0)
+#define W8_STAMP_DONE(i) \
+  do {                   \
+  } while (0)
+#define W8_STAMP_WAVE() \
+  do {                  \
+  } while (0)
+#endif
+
 namespace w8 {
 
 template <int FMT>
@@ -323,6 +368,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
   // is contributor `slot` of the `count` workgroups that cover the tile;
   // count == 1 writes Y directly.
   auto segment = [&](int tile, int ka, int kb, int slot, int count) {
+    W8_STAMP(0);
     const int n0 = (tile * WN + wn) * R * NB;  // first weight row of this wave
 
     const uint8_t* wptr[NB];
@@ -688,6 +734,8 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
         run_stage(B, k0 + s * U, whole);
       }
     }
+    W8_STAMP(1);
+    W8_STAMP_WAVE();
     // The ragged K tail (K % KSTEP != 0; for the K-segmented layouts, a
     // span reaching past K) belongs to the wave that owns step (span) kfull.
     // Packed weights are zero-padded there; activations are masked by byte.
@@ -757,6 +805,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
       }
     }
 
+    W8_STAMP(2);
     // Several workgroups cover this tile: publish the partial; the last
     // workgroup to arrive sums them in slot (= K) order.
     // Protocol (no L2 writeback or invalidate): the partials are written with
@@ -796,6 +845,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
       __builtin_amdgcn_s_waitcnt(0);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __syncthreads();
+      W8_STAMP(3);
       // Arrival counting.  Split-K (count = split_k, a power of two <= 256):
       // each contributor adds 256 / count to word 0 of the tile's counter
       // line, so a launch raises it by exactly 256 and the counter is never
@@ -812,6 +862,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
       }
       __syncthreads();
       store = is_last;
+      W8_STAMP(4);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the partial loads stay after the count
       if (store) {
         if (wk == 0) {
@@ -848,7 +899,10 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
           __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    if (!store || wk != 0) return;
+    if (!store || wk != 0) {
+      if (!store) W8_STAMP_DONE(7);
+      return;
+    }
 
     if constexpr (T > 1) {
       // K-segmented epilogue: the wave writes its 16 x 16 tiles to LDS as
@@ -907,6 +961,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
             reinterpret_cast<uint16_t*>(a.out)[off] = yb[q];
         }
       }
+      W8_STAMP_DONE(6);
       return;
     }
 
@@ -959,6 +1014,7 @@ __device__ __forceinline__ void gemm_body(GemmArgs a, const int* __restrict__ xr
             }
           }
         }
+    W8_STAMP_DONE(6);
   };
 
   if constexpr (!SK) {
