@@ -120,18 +120,52 @@ __device__ __forceinline__ v2u encode8(v4u v, float s, float r) {
 }
 
 // ------------------------------------------------------------- reductions --
-// Max over the 64 lanes of a wavefront (every lane gets the result).
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+// Lane moves within a row of 16 lanes by DPP (a VALU operand modifier: no
+// LDS round trip, unlike a lane shuffle).  gfx9 DPP controls: quad_perm
+// [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141
+// (lane i <-> 7 - i within each 8), row_mirror = 0x140 (i <-> 15 - i).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over aligned segments of 16 lanes (every lane gets its segment's max):
+// pairs, then quads, then halves, then the row.
+__device__ __forceinline__ float seg16_max(float v) {
+  v = fmaxf(v, dpp_move<0xB1>(v));
+  v = fmaxf(v, dpp_move<0x4E>(v));
+  v = fmaxf(v, dpp_move<0x141>(v));
+  v = fmaxf(v, dpp_move<0x140>(v));
   return v;
 }
 
-// Max over aligned segments of 16 lanes.
-__device__ __forceinline__ float seg16_max(float v) {
-#pragma unroll
-  for (int off = 8; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+// Max over the 64 lanes of a wavefront (every lane gets the result): the
+// four rows' maxima, read from one lane of each row.
+__device__ __forceinline__ float wave_max(float v) {
+  v = seg16_max(v);
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// ------------------------------------------------------- launch identity --
+// The HSA dispatch packet id of the running launch (a per-queue counter that
+// every dispatch, graph replays included, advances), read through the LLVM
+// intrinsic that exposes the dispatch-id kernel argument.
+extern "C" __device__ unsigned long long w8_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
+// A 64-bit key of the running launch: its packet id, its queue's address and
+// a number the host draws per call, mixed by odd multipliers, so launches on
+// different queues and calls captured in different graphs get different
+// keys; odd, so never the 0 of a zero-filled flag.
+__device__ __forceinline__ unsigned long long inq_key(unsigned long long epoch) {
+  const unsigned long long q = (unsigned long long)(uintptr_t)__builtin_amdgcn_queue_ptr();
+  return ((w8_dispatch_id() + 1ull) * 0x9E3779B97F4A7C15ull ^ q * 0xC2B2AE3D27D4EB4Full ^
+          epoch * 0x165667B19E3779F9ull) | 1ull;
 }
 
 // ------------------------------------------------- device-coherent I/O --

@@ -10,7 +10,7 @@
 // wave w reads chunks w, w + W, w + 2W, ... (W waves in all) -- so the waves
 // of one moment read neighbouring memory; DEPTH chunks per wave in flight.
 // Each wave XORs what it read and writes one word of `sink`, so no load is
-// dead code.
+// dead code and, like a GEMM, the launch ends with a store.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,10 +38,16 @@ __global__ void read_floor_kernel(const u4* __restrict__ src, long long nchunks,
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) acc ^= v[d];
   }
-  unsigned x = acc.x ^ acc.y ^ acc.z ^ acc.w;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off, 64);
-  if (lane == 0) sink[w] = x;
+  // the wave's XOR: within each row of 16 lanes by DPP moves, then across
+  // the four rows by lane reads (no LDS round trips)
+  int x = (int)(acc.x ^ acc.y ^ acc.z ^ acc.w);
+  x ^= __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  x ^= __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  x ^= __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  x ^= __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);  // row_mirror
+  x = __builtin_amdgcn_readlane(x, 0) ^ __builtin_amdgcn_readlane(x, 16) ^
+      __builtin_amdgcn_readlane(x, 32) ^ __builtin_amdgcn_readlane(x, 48);
+  if (lane == 0) sink[w] = (unsigned)x;
 }
 
 }  // namespace
