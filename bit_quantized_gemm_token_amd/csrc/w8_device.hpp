@@ -152,22 +152,6 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-// ------------------------------------------------------- launch identity --
-// The HSA dispatch packet id of the running launch (a per-queue counter that
-// every dispatch, graph replays included, advances), read through the LLVM
-// intrinsic that exposes the dispatch-id kernel argument.
-extern "C" __device__ unsigned long long w8_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
-
-// A 64-bit key of the running launch: its packet id, its queue's address and
-// a number the host draws per call, mixed by odd multipliers, so launches on
-// different queues and calls captured in different graphs get different
-// keys; odd, so never the 0 of a zero-filled flag.
-__device__ __forceinline__ unsigned long long inq_key(unsigned long long epoch) {
-  const unsigned long long q = (unsigned long long)(uintptr_t)__builtin_amdgcn_queue_ptr();
-  return ((w8_dispatch_id() + 1ull) * 0x9E3779B97F4A7C15ull ^ q * 0xC2B2AE3D27D4EB4Full ^
-          epoch * 0x165667B19E3779F9ull) | 1ull;
-}
-
 // ------------------------------------------------- device-coherent I/O --
 // Buffer loads and stores of 16 bytes a lane with the agent-scope cache
 // policy (SC1): the same bits the compiler sets on agent-scope atomic loads
