@@ -403,3 +403,18 @@ def test_largest_n_and_k(w8, fmt, M, N, K):
             assert np.array_equal(got.astype(np.int64), ref), f"{cfg}"
         else:
             assert np.all(np.abs(got.astype(np.float64) - ref) <= bound), f"{cfg}"
+
+
+@pytest.mark.parametrize("M", [5, 20])
+def test_block_fp8_long_segments(w8, M):
+    """Block_FP8 at a K longer than the sweep's (16384: 128 groups, each
+    K-step's products scaled by its own pair of group scales): split_k 1, 2
+    and 4, one and four K-waves, both Swap-AB settings, one and two 16-row
+    blocks of M, row-major and packed weights; accumulators against the
+    oracle within the fp32 summation bound."""
+    cs = case("Block_FP8", M, 160, 16384)
+    xq, sx = cs.gpu_act()
+    for s, wk, swap, packed in itertools.product((1, 2, 4), (1, 4), (0, 1), (0, 1)):
+        cfg = C(w8, tile_n=16, waves_k=wk, unroll=2, split_k=s, swap_ab=swap)
+        acc_check(w8, cs, xq, sx, cfg, f"Block_FP8 M={M} K=16384 {cfg} packed={packed}",
+                  bool(packed))
