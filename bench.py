@@ -369,6 +369,70 @@ def summarize_mfma(manifest_path, counter_csv, out_md, command):
     log(f"[bench] wrote {out_md}")
 
 
+def summarize_counters(manifest_path, counter_csv, out_md, command):
+    """Per-problem memory-pipeline counters from one counter pass (rocprofv3
+    --pmc with TA_BUSY_avr, TCC_HIT_sum, TCC_MISS_sum, SQ_WAVES,
+    SQ_INSTS_VMEM_RD): how busy the vector-memory path of a compute unit is
+    during a launch, and how many L2 requests hit."""
+    import csv
+    with open(manifest_path) as f:
+        man = json.load(f)
+    per = {}
+    with open(counter_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            if "gemm_kernel<" not in r["Kernel_Name"]:
+                continue
+            key = int(r.get("Dispatch_Id") or r.get("Correlation_Id") or 0)
+            e = per.setdefault(key, {})
+            e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                e["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    disp = [per[k] for k in sorted(per)]
+    if len(disp) != len(man["gemm_dispatch_order"]):
+        raise SystemExit(f"{counter_csv}: {len(disp)} GEMM dispatches, expected "
+                         f"{len(man['gemm_dispatch_order'])}")
+    acc = {}
+    for i, e in zip(man["gemm_dispatch_order"], disp):
+        acc.setdefault(i, []).append(e)
+
+    def mean(es, c):
+        return sum(e.get(c, 0.0) for e in es) / len(es)
+
+    lines = ["# Vector-memory path and L2 per GEMM launch (rocprofv3 TA_BUSY, TCC_HIT/MISS, "
+             "SQ_WAVES, SQ_INSTS_VMEM_RD)", "",
+             "One counter run of `bench.py --counter-pass` (each problem's GEMM launched twice on "
+             "two weight copies, synchronized after every launch; averages of the two).  "
+             "Dispatch us: the counter run's dispatch time (the profiler serializes and "
+             "instruments each launch, so it is longer than under graph replay).  TA busy = "
+             "TA_BUSY_avr, the busy cycles of the texture-address unit (one per compute unit) "
+             "averaged over the units; TA busy % = that over the dispatch time at 2.4 GHz, the "
+             "share of the launch in which an average compute unit's vector-memory path is "
+             "issuing addresses.  VMEM rd = vector-memory read instructions issued in the whole "
+             "launch (SQ_INSTS_VMEM_RD), waves = SQ_WAVES.  L2 hit % = TCC_HIT / (TCC_HIT + "
+             "TCC_MISS) over all L2 requests of the launch (weights stream past the L2 and miss; "
+             "activations, scales and split-K partials re-read by many workgroups hit).", "",
+             "Command (from /tmp on the MI355X box, repository at $R):", "", "```", command, "```",
+             "", "| format | M | N | K | layout | config | dispatch us | waves | VMEM rd | "
+             "TA busy cycles | TA busy % | L2 hit % |",
+             "|---|---:|---:|---:|---|---|---:|---:|---:|---:|---:|---:|"]
+    for i, pr in enumerate(man["problems"]):
+        es = acc.get(i, [])
+        if not es:
+            continue
+        ns = mean(es, "ns")
+        ta = mean(es, "TA_BUSY_avr")
+        hit, miss = mean(es, "TCC_HIT_sum"), mean(es, "TCC_MISS_sum")
+        lines.append(
+            f"| {pr['fmt']} | {pr['M']} | {pr['N']} | {pr['K']} | {pr.get('layout', '')} | "
+            f"{_cfg_str(pr['cfg'])} | {ns / 1e3:.2f} | {mean(es, 'SQ_WAVES'):,.0f} | "
+            f"{mean(es, 'SQ_INSTS_VMEM_RD'):,.0f} | {ta:,.0f} | "
+            f"{100 * ta / (ns * 2.4) if ns else 0:.1f} | "
+            f"{100 * hit / (hit + miss) if hit + miss else 0:.1f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log(f"[bench] wrote {out_md}")
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -404,6 +468,11 @@ def parse():
                    metavar=("MANIFEST", "COUNTER_CSV", "OUT_MD"),
                    help="write the MFMA-utilisation summary from a counter pass with "
                         "SQ_VALU_MFMA_BUSY_CYCLES and SQ_INSTS_VALU_MFMA_MOPS_F8/_I8, then exit")
+    p.add_argument("--summarize-counters", nargs=3, default=None,
+                   metavar=("MANIFEST", "COUNTER_CSV", "OUT_MD"),
+                   help="write the vector-memory and L2 counter summary from a counter pass with "
+                        "TA_BUSY_avr, TCC_HIT_sum, TCC_MISS_sum, SQ_WAVES, SQ_INSTS_VMEM_RD, "
+                        "then exit")
     p.add_argument("--phases", default=None, metavar="OUT_MD",
                    help="run the phase probe (w8_phase_probe) and write its summary, then exit")
     p.add_argument("--bench-line", default=None, metavar="JSON",
@@ -799,6 +868,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma, args.summary_command)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.summary_command)
         return
     if args.phases:
         phase_study(args.phases, args.summary_command)
