@@ -111,3 +111,53 @@ def test_bench_refuses_several_gpus():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_summarize_counters(tmp_path):
+    """The counter summary averages each problem's dispatches (matched to the
+    manifest's dispatch order) and derives TA busy % over the dispatch time at
+    2.4 GHz and the L2 hit rate."""
+    def full_manifest(order):
+        mp, _, _, _, _ = make_run(tmp_path, [], [], order)
+        man = json.loads(mp.read_text())
+        for pr in man["problems"]:
+            for k in ("waves_n", "x_lds", "grid"):
+                pr["cfg"].setdefault(k, 1 if k == "waves_n" else 0)
+        mp.write_text(json.dumps(man))
+        return mp
+
+    mp = full_manifest([0, 1, 0, 1])
+    gemm = "void w8::gemm_kernel<0, 1, 1, 1, 1, 4, 0, 8, 0, 0>(w8::GemmArgs)"
+    vals = [  # dispatch: (ns, TA_BUSY_avr, TCC_HIT_sum, TCC_MISS_sum, SQ_WAVES, SQ_INSTS_VMEM_RD)
+        (4000, 2400, 60, 40, 256, 1000), (2000, 960, 30, 70, 448, 500),
+        (4000, 4800, 20, 80, 256, 3000), (2000, 960, 50, 50, 448, 700)]
+    path = tmp_path / "pmc.csv"
+    names = ("TA_BUSY_avr", "TCC_HIT_sum", "TCC_MISS_sum", "SQ_WAVES", "SQ_INSTS_VMEM_RD")
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        # a copy kernel first: not a GEMM, ignored
+        r = {k: 0 for k in FIELDS}
+        r.update(Dispatch_Id=1, Kernel_Name=COPY, Counter_Name="TA_BUSY_avr", Counter_Value=5)
+        w.writerow(r)
+        for d, (ns, *cs) in enumerate(vals):
+            for name, v in zip(names, cs):
+                r = {k: 0 for k in FIELDS}
+                r.update(Dispatch_Id=d + 2, Kernel_Name=gemm, Counter_Name=name, Counter_Value=v,
+                         Start_Timestamp=1000, End_Timestamp=1000 + ns)
+                w.writerow(r)
+    out = tmp_path / "out.md"
+    bench.summarize_counters(str(mp), str(path), str(out), "cmd")
+    rows = [l.split("|")[1:-1] for l in out.read_text().splitlines()
+            if l.startswith("| FP8") or l.startswith("| W8A8")]
+    rows = [[c.strip() for c in r] for r in rows]
+    # problem 0: dispatches 0 and 2; ns 4000, TA (2400 + 4800) / 2 = 3600 cycles of 9600
+    assert rows[0][6] == "4.00" and rows[0][9] == "3,600" and rows[0][10] == "37.5"
+    assert rows[0][11] == "40.0"  # hits 40 of 100 on average
+    assert rows[0][8] == "2,000" and rows[0][7] == "256"
+    # problem 1: TA 960 of 4800 cycles, hits 40 of 100
+    assert rows[1][10] == "20.0" and rows[1][11] == "40.0" and rows[1][8] == "600"
+    # a dispatch count that does not match the manifest is refused
+    mp2 = full_manifest([0, 1, 0])
+    with pytest.raises(SystemExit):
+        bench.summarize_counters(str(mp2), str(path), str(out), "cmd")
